@@ -1,0 +1,11 @@
+"""Exact tiled attention for MI355X (gfx950): online-softmax forward and
+recompute backward as hand-written HIP kernels behind a C ABI (libfa.so).
+
+The Python layer only marshals arguments; see ``_lib`` for the entry points
+(fa_fwd, fa_bwd, fa_bwd_workspace_bytes, fa_strerror) and the torch-tensor
+conveniences ``forward`` / ``backward``.
+"""
+from ._lib import (  # noqa: F401
+    FA_BF16, FA_FP32, FAError, LIB_PATH, backward, fa_bwd, fa_bwd_workspace_bytes, fa_fwd,
+    fa_strerror, forward, load, workspace,
+)

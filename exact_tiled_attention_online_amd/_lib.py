@@ -1,0 +1,133 @@
+"""ctypes binding of libfa.so: the C entry points under the same names, plus
+torch-tensor conveniences that only marshal arguments.
+
+Every step of the computation runs in the library's HIP kernels; this module
+allocates outputs with torch and passes device pointers and the current HIP
+stream.  If the library has not been built, loading fails loudly: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
+FA_BF16, FA_FP32 = 0, 1
+
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_strerror(status)} (status {status})")
+
+
+def load():
+    """Load libfa.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m exact_tiled_attention_online_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---- the C entry points, same names, raw integer pointers ------------------
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype) -> int:
+    return load().fa_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream, dtype)
+
+
+def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes,
+           stream, dtype) -> int:
+    return load().fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
+                         workspace, workspace_bytes, stream, dtype)
+
+
+def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
+    return load().fa_bwd_workspace_bytes(B, H, N, d, dtype)
+
+
+def fa_strerror(status: int) -> str:
+    return load().fa_strerror(status).decode()
+
+
+# ---- torch conveniences ------------------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(ts, shape):
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+            raise ValueError("expected contiguous device tensors of shape [B,H,N,d]")
+        if t.dtype != ts[0].dtype:
+            raise ValueError("q, k, v (and o, dO) must share one dtype")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def forward(q, k, v, causal: bool, scale: float, out=None, lse=None, stream=None):
+    """O, LSE = attention forward on [B,H,N,d] device tensors (bf16 or fp32)."""
+    import torch
+    B, H, N, d = q.shape
+    _check((q, k, v), q.shape)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                B, H, N, d, causal, scale, _stream(stream), _dtype_code(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return o, l
+
+
+def workspace(q):
+    """A device byte buffer large enough for fa_bwd on q's shape and dtype."""
+    import torch
+    B, H, N, d = q.shape
+    n = fa_bwd_workspace_bytes(B, H, N, d, _dtype_code(q))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def backward(q, k, v, o, do, lse, causal: bool, scale: float, ws=None, grads=None, stream=None):
+    """dQ, dK, dV of attention on [B,H,N,d] device tensors, given O and LSE."""
+    import torch
+    B, H, N, d = q.shape
+    _check((q, k, v, o, do), q.shape)
+    if ws is None:
+        ws = workspace(q)
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(q),
+                                                  torch.empty_like(q))
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
+                ws.data_ptr(), ws.numel(), _stream(stream), _dtype_code(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,0 +1,123 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument checks, workspace
+// carving and the kernel sequence.  No allocation, no synchronisation.
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Common shape / flag checks; returns FA_OK or an error status.
+int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID;
+  if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const long long elems = (long long)B * H * N * d;
+  if (elems >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+struct Workspace {
+  float* drow;
+  float* lse2;
+  float* dq_acc;  // bf16 only
+  size_t bytes;
+};
+
+Workspace carve(void* base, int B, int H, int N, int d, int dtype) {
+  const size_t rows = (size_t)B * H * N;
+  Workspace w{};
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  w.drow = reinterpret_cast<float*>(p + off);
+  off += round_up(rows * sizeof(float));
+  w.lse2 = reinterpret_cast<float*>(p + off);
+  off += round_up(rows * sizeof(float));
+  w.dq_acc = nullptr;
+  if (dtype == FA_BF16) {
+    w.dq_acc = reinterpret_cast<float*>(p + off);
+    off += round_up(rows * d * sizeof(float));
+  }
+  w.bytes = off;
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           int causal, float scale, void* stream, int dtype) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == FA_BF16)
+    return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, s));
+  return hip_status(fa::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                       static_cast<const float*>(v), static_cast<float*>(o), lse, B * H, N, d,
+                                       causal != 0, scale, s));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128) || (dtype != FA_BF16 && dtype != FA_FP32)) return 0;
+  return carve(nullptr, B, H, N, d, dtype).bytes;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
+           size_t workspace_bytes, void* stream, int dtype) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d, dtype);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return FA_ERR_WORKSPACE;
+  const Workspace w = carve(workspace, B, H, N, d, dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  const bool fp32 = dtype == FA_FP32;
+  hipError_t e = fa::launch_bwd_pre(o, dO, lse, w.drow, w.lse2, w.dq_acc, BH, N, d, fp32, s);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  if (fp32) {
+    e = fa::launch_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                           static_cast<const float*>(v), static_cast<const float*>(dO), lse, w.drow,
+                           static_cast<float*>(dq), static_cast<float*>(dk), static_cast<float*>(dv), BH, N, d,
+                           causal != 0, scale, s);
+    return hip_status(e);
+  }
+  e = fa::launch_bwd_bf16(q, k, v, dO, w.lse2, w.drow, w.dq_acc, dk, dv, BH, N, d, causal != 0, scale, s);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  return hip_status(fa::launch_dq_convert(w.dq_acc, dq, (size_t)BH * N * d, scale, s));
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad size, flag or scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dim, dtype or size";
+    case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "HIP runtime reported a launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

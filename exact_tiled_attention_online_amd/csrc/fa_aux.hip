@@ -1,0 +1,104 @@
+// fa_aux.hip -- the memory-bound kernels around the backward product kernel.
+//
+// bwd_pre: D_i = sum_c dO_ic * O_ic for every query row (page
+// "flash-attention-backpropagation" (aiqz.cc), section Softmax梯度: the row
+// term the softmax normalisation adds to dP), plus the ledger rescaled to base
+// 2 (LSE * log2 e) for the backward's exp2, plus the clear of the fp32 dQ
+// accumulator (a fill kernel, so the whole backward can be captured in a graph).
+// Each row of d elements is read by d/8 lanes with 16-byte (bf16) or 32-byte
+// (fp32) loads, reduced across those lanes with xor-shuffles.
+//
+// dq_convert: dQ = bf16(scale * acc), 8 elements per thread, 16-byte stores.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
+                                                      const float* __restrict__ lse,
+                                                      float* __restrict__ drow, float* __restrict__ lse2,
+                                                      float* __restrict__ dq_acc, size_t rows) {
+  constexpr int LPR = D / 8;            // lanes per row, 8 elements each
+  constexpr int RPB = 256 / LPR;        // rows per block
+  const int tid = threadIdx.x;
+  const size_t row = (size_t)blockIdx.x * RPB + tid / LPR;
+  const int part = tid % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const size_t base = row * D + part * 8;
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(O + base);
+      const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(dO + base);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)o8[e], (float)g8[e], acc);
+    } else {
+      const f32x4* o4 = reinterpret_cast<const f32x4*>(O + base);
+      const f32x4* g4 = reinterpret_cast<const f32x4*>(dO + base);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 a = o4[h], b = g4[h];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf(a[e], b[e], acc);
+      }
+    }
+    if (dq_acc) {
+      f32x4* z = reinterpret_cast<f32x4*>(dq_acc + base);
+      z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (row < rows && part == 0) {
+    drow[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
+}
+
+hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* drow, float* lse2,
+                          float* dq_acc, int BH, int N, int d, bool fp32, hipStream_t stream) {
+  const size_t rows = (size_t)BH * N;
+  const int rpb = 256 / (d / 8);
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
+  if (fp32) {
+    if (d == 128)
+      hipLaunchKernelGGL((bwd_pre_kernel<128, float>), grid, block, 0, stream, (const float*)o,
+                         (const float*)dO, lse, drow, lse2, dq_acc, rows);
+    else
+      hipLaunchKernelGGL((bwd_pre_kernel<64, float>), grid, block, 0, stream, (const float*)o,
+                         (const float*)dO, lse, drow, lse2, dq_acc, rows);
+  } else {
+    if (d == 128)
+      hipLaunchKernelGGL((bwd_pre_kernel<128, bf16>), grid, block, 0, stream, (const bf16*)o,
+                         (const bf16*)dO, lse, drow, lse2, dq_acc, rows);
+    else
+      hipLaunchKernelGGL((bwd_pre_kernel<64, bf16>), grid, block, 0, stream, (const bf16*)o,
+                         (const bf16*)dO, lse, drow, lse2, dq_acc, rows);
+  }
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
+                                                         size_t n8, float scale) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4* a = reinterpret_cast<const f32x4*>(acc) + 2 * i;
+  const f32x4 x = a[0], y = a[1];
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (bf16)(x[e] * scale);
+    r[4 + e] = (bf16)(y[e] * scale);
+  }
+  reinterpret_cast<bf16x8*>(dq)[i] = r;
+}
+
+hipError_t launch_dq_convert(const float* dq_acc, void* dq, size_t n, float scale, hipStream_t stream) {
+  const size_t n8 = n / 8;   // n = B*H*N*d, a multiple of 64
+  const dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
+  hipLaunchKernelGGL(dq_convert_kernel, grid, block, 0, stream, dq_acc, (bf16*)dq, n8, scale);
+  return hipGetLastError();
+}
+
+}  // namespace fa

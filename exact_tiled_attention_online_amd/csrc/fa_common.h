@@ -1,0 +1,117 @@
+// fa_common.h -- gfx950 building blocks shared by the attention kernels:
+// MFMA wrappers, the swizzled LDS tile layout, transposing LDS reads and
+// wave-half exchanges.  CDNA4 only (wave64, v_mfma_*_bf16 with K=16/32,
+// ds_read_b64_tr_b16, v_permlane32_swap).
+//
+// Register layouts (checked on the device against a host matmul):
+//   v_mfma_f32_32x32x16_bf16  A: lane l holds row m = l%32, k = 8*(l/32)+r
+//                             B: lane l holds col n = l%32, k = 8*(l/32)+r
+//                             C: lane l, reg 4*i+j holds row 8*i+4*(l/32)+j,
+//                                col l%32  (i, j in 0..3)
+// The contraction index k may be permuted freely as long as A and B agree,
+// which is how C tiles are reused as the next product's operand without a
+// round trip: a C tile holds its N index across lanes and its M index in
+// registers, exactly what an A or B operand wants for (lane = M or N,
+// registers = K).
+//
+// ds_read_b64_tr_b16: within each 16-lane group, if lane s points at the
+// 4-element row segment M[k0 + s/4][n0 + 4*(s%4) .. +3] of a row-major bf16
+// tile, lane i receives the column slice M[k0 .. k0+3][n0 + i].  This gives
+// an operand whose registers run down a row-major tile's rows (the
+// transposed read every K-major operand needs).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS __attribute__((address_space(3)))
+#define FA_DEV __device__ __forceinline__
+
+namespace fa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+FA_DEV f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+FA_DEV float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+FA_DEV float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Combine a per-lane value with the value of lane l^32 (the other wave half).
+FA_DEV float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+FA_DEV float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---- swizzled row-major tiles in LDS -----------------------------------
+// A tile of rows of ROWB bytes (ROWB = 128 or 256) stored as 16-byte chunks;
+// chunk c of row r lives at chunk position c ^ swz(r).  With
+// swz(r) = 2*(r%4) + (r/4)%2:
+//  * 8 consecutive rows read at the same logical chunk (ds_read_b128 of an
+//    operand row) land on 8 distinct chunk positions;
+//  * 4 consecutive rows (first row a multiple of 4) read as 32-byte spans at
+//    an even logical chunk (ds_read_b64_tr_b16) also land on 8 distinct
+//    positions.
+FA_DEV int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int ROWB>
+FA_DEV int tile_off(int row, int chunk) {
+  return row * ROWB + ((chunk ^ swz(row)) << 4);
+}
+// byte offset of element (row, col) (bf16 columns) in the swizzled tile
+template <int ROWB>
+FA_DEV int tile_off_elem(int row, int col) {
+  return tile_off<ROWB>(row, col >> 3) + ((col & 7) << 1);
+}
+
+FA_DEV bf16x8 lds_read_b128(const char* base, int off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+
+FA_DEV bf16x4 lds_read_tr(const char* base, int off) {
+  typedef FA_LDS i16x4 lds_i16x4;
+  // generic -> LDS address-space cast of a pointer into a __shared__ array
+  lds_i16x4* p = (lds_i16x4*)(base + off);
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+FA_DEV bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Transposed operand (8 K-values per lane) from a swizzled row-major tile
+// whose rows are the K index: two 4-row tr reads, rows k0..k0+3 and
+// k1..k1+3, at the 16-column group n0 (lane group g = lane/16 supplies the
+// columns n0 .. n0+15, the caller folds g into n0).
+template <int ROWB>
+FA_DEV bf16x8 tr_operand(const char* tile, int k0, int k1, int n0, int lane) {
+  const int s = lane & 15;
+  const int col = n0 + 4 * (s & 3);
+  const bf16x4 lo = lds_read_tr(tile, tile_off_elem<ROWB>(k0 + (s >> 2), col));
+  const bf16x4 hi = lds_read_tr(tile, tile_off_elem<ROWB>(k1 + (s >> 2), col));
+  return cat(lo, hi);
+}
+
+FA_DEV bf16x8 pack8(float a0, float a1, float a2, float a3, float b0, float b1, float b2, float b3) {
+  bf16x8 r;
+  r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+  r[4] = (bf16)b0; r[5] = (bf16)b1; r[6] = (bf16)b2; r[7] = (bf16)b3;
+  return r;
+}
+
+}  // namespace fa

@@ -1,0 +1,251 @@
+// fa_fp32.hip -- fp32 path: the same tiled method in exact fp32 VALU
+// arithmetic (no MFMA rounding of operands), for fp32 callers.
+//
+// Work split: a pair of lanes owns one row (query row in the forward and in
+// the dQ kernel, key row in the dK/dV kernel), each lane half of d; a dot
+// product is the two halves' partial sums combined with one xor-shuffle.
+// The streamed operand rows sit in LDS and every lane reads the same element
+// (broadcast).
+//
+// forward   : online softmax over 32-key tiles (page
+//             "flash-attention-v2-sram-tiling" (aiqz.cc), section 5), deferred
+//             normalisation, ledger LSE = m + ln l.
+// backward  : key-row-outer kernel for dK, dV and query-row-outer kernel for
+//             dQ, both recomputing P^ = exp(S - LSE) (page
+//             "flash-attention-backpropagation" (aiqz.cc), sections 数值稳定,
+//             Softmax梯度, QKV梯度); no atomics.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+constexpr int F32_ROWS = 64;   // rows per workgroup (128 lanes)
+constexpr int F32_TILE = 32;   // streamed rows per LDS tile
+
+template <int D>
+FA_DEV void load_rows_f32(float* dst, const float* src, int row0, int nrows, int N, int tid) {
+  // dst: [F32_TILE][D] floats; src rows row0.. of one head
+  constexpr int V4 = D / 4;
+  for (int e = tid; e < F32_TILE * V4; e += 128) {
+    const int r = e / V4, c4 = e % V4;
+    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (r < nrows && row0 + r < N) x = reinterpret_cast<const f32x4*>(src + (size_t)(row0 + r) * D)[c4];
+    reinterpret_cast<f32x4*>(dst + r * D)[c4] = x;
+  }
+}
+
+template <int D>
+FA_DEV float half_dot(const float* a, const float* b) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 2; ++c) s = fmaf(a[c], b[c], s);
+  return s + __shfl_xor(s, 1);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                      const float* __restrict__ V, float* __restrict__ O,
+                                                      float* __restrict__ LSE, int BH, int N, float scale) {
+  constexpr int DH = D / 2;
+  __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
+  __shared__ __attribute__((aligned(16))) float sv[F32_TILE * D];
+  const int tid = threadIdx.x, half = tid & 1;
+  const int head = blockIdx.y;
+  const int row0 = blockIdx.x * F32_ROWS;
+  const int qrow = row0 + (tid >> 1);
+  const size_t hoff = (size_t)head * N * D;
+  float qh[DH], oh[DH];
+#pragma unroll
+  for (int c = 0; c < DH; ++c) {
+    qh[c] = qrow < N ? Q[hoff + (size_t)qrow * D + half * DH + c] : 0.f;
+    oh[c] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kv_end = CAUSAL ? min(N, row0 + F32_ROWS) : N;
+  for (int t0 = 0; t0 < kv_end; t0 += F32_TILE) {
+    __syncthreads();
+    load_rows_f32<D>(sk, K + hoff, t0, F32_TILE, N, tid);
+    load_rows_f32<D>(sv, V + hoff, t0, F32_TILE, N, tid);
+    __syncthreads();
+    float s[F32_TILE];
+    float mx = m;
+#pragma unroll
+    for (int j = 0; j < F32_TILE; ++j) {
+      const int kv = t0 + j;
+      float x = half_dot<D>(qh, sk + j * D + half * DH) * scale;
+      if (kv >= N || (CAUSAL && kv > qrow)) x = -INFINITY;
+      s[j] = x;
+      mx = fmaxf(mx, x);
+    }
+    // key 0 is never masked, so mx is finite from the first tile on
+    const float alpha = expf(m - mx);
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < F32_TILE; ++j) {
+      s[j] = expf(s[j] - mx);
+      rs += s[j];
+    }
+    l = l * alpha + rs;
+    m = mx;
+#pragma unroll
+    for (int c = 0; c < DH; ++c) {
+      float acc = oh[c] * alpha;
+#pragma unroll
+      for (int j = 0; j < F32_TILE; ++j) acc = fmaf(s[j], sv[j * D + half * DH + c], acc);
+      oh[c] = acc;
+    }
+  }
+  if (qrow < N) {
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int c = 0; c < DH; ++c) O[hoff + (size_t)qrow * D + half * DH + c] = oh[c] * inv;
+    if (half == 0) LSE[(size_t)head * N + qrow] = m + logf(l);
+  }
+}
+
+// dK, dV: a lane pair per key row; query rows stream through LDS.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                         const float* __restrict__ V, const float* __restrict__ dO,
+                                                         const float* __restrict__ LSE, const float* __restrict__ DR,
+                                                         float* __restrict__ dK, float* __restrict__ dV, int N,
+                                                         float scale) {
+  constexpr int DH = D / 2;
+  __shared__ __attribute__((aligned(16))) float sq[F32_TILE * D];
+  __shared__ __attribute__((aligned(16))) float sg[F32_TILE * D];
+  __shared__ float sl[F32_TILE], sd[F32_TILE];
+  const int tid = threadIdx.x, half = tid & 1;
+  const int head = blockIdx.y;
+  const int row0 = blockIdx.x * F32_ROWS;
+  const int kvrow = row0 + (tid >> 1);
+  const size_t hoff = (size_t)head * N * D;
+  float kh[DH], vh[DH], dkh[DH], dvh[DH];
+#pragma unroll
+  for (int c = 0; c < DH; ++c) {
+    kh[c] = kvrow < N ? K[hoff + (size_t)kvrow * D + half * DH + c] : 0.f;
+    vh[c] = kvrow < N ? V[hoff + (size_t)kvrow * D + half * DH + c] : 0.f;
+    dkh[c] = 0.f;
+    dvh[c] = 0.f;
+  }
+  const int q_begin = CAUSAL ? (row0 / F32_TILE) * F32_TILE : 0;
+  for (int t0 = q_begin; t0 < N; t0 += F32_TILE) {
+    __syncthreads();
+    load_rows_f32<D>(sq, Q + hoff, t0, F32_TILE, N, tid);
+    load_rows_f32<D>(sg, dO + hoff, t0, F32_TILE, N, tid);
+    if (tid < F32_TILE) {
+      const int q = t0 + tid;
+      sl[tid] = q < N ? LSE[(size_t)head * N + q] : 0.f;
+      sd[tid] = q < N ? DR[(size_t)head * N + q] : 0.f;
+    }
+    __syncthreads();
+    for (int j = 0; j < F32_TILE; ++j) {
+      const int q = t0 + j;
+      const float sc = half_dot<D>(sq + j * D + half * DH, kh) * scale;
+      float p = expf(sc - sl[j]);
+      if (q >= N || kvrow >= N || (CAUSAL && kvrow > q)) p = 0.f;
+      const float dp = half_dot<D>(sg + j * D + half * DH, vh);
+      const float ds = p * (dp - sd[j]);
+#pragma unroll
+      for (int c = 0; c < DH; ++c) {
+        dvh[c] = fmaf(p, sg[j * D + half * DH + c], dvh[c]);
+        dkh[c] = fmaf(ds, sq[j * D + half * DH + c], dkh[c]);
+      }
+    }
+  }
+  if (kvrow < N) {
+#pragma unroll
+    for (int c = 0; c < DH; ++c) {
+      dK[hoff + (size_t)kvrow * D + half * DH + c] = dkh[c] * scale;
+      dV[hoff + (size_t)kvrow * D + half * DH + c] = dvh[c];
+    }
+  }
+}
+
+// dQ: a lane pair per query row; key and value rows stream through LDS.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                        const float* __restrict__ V, const float* __restrict__ dO,
+                                                        const float* __restrict__ LSE, const float* __restrict__ DR,
+                                                        float* __restrict__ dQ, int N, float scale) {
+  constexpr int DH = D / 2;
+  __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
+  __shared__ __attribute__((aligned(16))) float sv[F32_TILE * D];
+  const int tid = threadIdx.x, half = tid & 1;
+  const int head = blockIdx.y;
+  const int row0 = blockIdx.x * F32_ROWS;
+  const int qrow = row0 + (tid >> 1);
+  const size_t hoff = (size_t)head * N * D;
+  float qh[DH], gh[DH], dqh[DH];
+#pragma unroll
+  for (int c = 0; c < DH; ++c) {
+    qh[c] = qrow < N ? Q[hoff + (size_t)qrow * D + half * DH + c] : 0.f;
+    gh[c] = qrow < N ? dO[hoff + (size_t)qrow * D + half * DH + c] : 0.f;
+    dqh[c] = 0.f;
+  }
+  const float lse = qrow < N ? LSE[(size_t)head * N + qrow] : 0.f;
+  const float drow = qrow < N ? DR[(size_t)head * N + qrow] : 0.f;
+  const int kv_end = CAUSAL ? min(N, row0 + F32_ROWS) : N;
+  for (int t0 = 0; t0 < kv_end; t0 += F32_TILE) {
+    __syncthreads();
+    load_rows_f32<D>(sk, K + hoff, t0, F32_TILE, N, tid);
+    load_rows_f32<D>(sv, V + hoff, t0, F32_TILE, N, tid);
+    __syncthreads();
+    for (int j = 0; j < F32_TILE; ++j) {
+      const int kv = t0 + j;
+      const float sc = half_dot<D>(qh, sk + j * D + half * DH) * scale;
+      float p = expf(sc - lse);
+      if (qrow >= N || kv >= N || (CAUSAL && kv > qrow)) p = 0.f;
+      const float dp = half_dot<D>(gh, sv + j * D + half * DH);
+      const float ds = p * (dp - drow);
+#pragma unroll
+      for (int c = 0; c < DH; ++c) dqh[c] = fmaf(ds, sk[j * D + half * DH + c], dqh[c]);
+    }
+  }
+  if (qrow < N) {
+#pragma unroll
+    for (int c = 0; c < DH; ++c) dQ[hoff + (size_t)qrow * D + half * DH + c] = dqh[c] * scale;
+  }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t fwd_f32_t(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
+                            int N, float scale, hipStream_t stream) {
+  const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, o, lse, BH, N, scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t bwd_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
+                            const float* drow, float* dq, float* dk, float* dv, int BH, int N, float scale,
+                            hipStream_t stream) {
+  const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
+  hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, drow, dk, dv,
+                     N, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, drow, dq, N,
+                     scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N,
+                          int d, bool causal, float scale, hipStream_t stream) {
+  if (d == 128)
+    return causal ? fwd_f32_t<128, true>(q, k, v, o, lse, BH, N, scale, stream)
+                  : fwd_f32_t<128, false>(q, k, v, o, lse, BH, N, scale, stream);
+  return causal ? fwd_f32_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
+                : fwd_f32_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);
+}
+
+hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dO, const float* lse,
+                          const float* drow, float* dq, float* dk, float* dv, int BH, int N, int d, bool causal,
+                          float scale, hipStream_t stream) {
+  if (d == 128)
+    return causal ? bwd_f32_t<128, true>(q, k, v, dO, lse, drow, dq, dk, dv, BH, N, scale, stream)
+                  : bwd_f32_t<128, false>(q, k, v, dO, lse, drow, dq, dk, dv, BH, N, scale, stream);
+  return causal ? bwd_f32_t<64, true>(q, k, v, dO, lse, drow, dq, dk, dv, BH, N, scale, stream)
+                : bwd_f32_t<64, false>(q, k, v, dO, lse, drow, dq, dk, dv, BH, N, scale, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,223 @@
+// fa_fwd_bf16.hip -- forward kernel, bf16 inputs/outputs, fp32 accumulation.
+//
+// One workgroup (4 waves) owns BR = 128 query rows of one (batch, head); each
+// wave owns 32 of them.  Key/value tiles of BC = 64 rows stream through two
+// LDS buffers (the next tile is fetched while the current one is used).  Per
+// tile and wave:
+//   S^T = K_j Q_w^T            v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
+//                              B = the wave's Q rows held in registers;
+//   online softmax             per lane one query row: running max m and
+//                              running sum l, rescale factor 2^(c(m_old-m_new))
+//                              (page "flash-attention-v2-sram-tiling"
+//                              (aiqz.cc), section 5; the l update uses the full
+//                              block sum as in the derivation on page
+//                              "blog.xiaohack.org/tag/flops", 知识点13 §4);
+//   O^T = a O^T + V_j^T P^T    A = V^T through transposing LDS reads, B = P^T
+//                              straight from the S^T accumulator registers.
+// Normalisation by l is deferred to the end (the NumPy demo of page
+// "flash-attention-backpropagation" (aiqz.cc), section Python 演示), and the
+// ledger LSE = scale*m + ln l is written instead of P.
+// The softmax runs in base 2 with the scale folded into one multiply-add:
+// p = 2^(c*s - c*m) with c = scale*log2(e).
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c) {
+  constexpr int BR = 128, BC = 64;
+  constexpr int ROWB = D * 2;        // bytes per row
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int KS = D / 16;         // K-steps of the S product
+  constexpr int DT = D / 32;         // 32-row tiles of O^T
+  constexpr int TILEB = BC * ROWB;   // bytes of one K or V tile
+  constexpr int LPT = BC * CH / 256; // 16-byte loads per thread per tensor
+
+  __shared__ __attribute__((aligned(16))) char smem[2][2][TILEB];  // [buffer][K, V]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5, g = lane >> 4;
+  const int bid = blockIdx.x;
+  const int head = bid % BH;
+  // causal: the longest query blocks are dispatched first
+  const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
+  const size_t hoff = (size_t)head * N * D;
+  const bf16* Qh = Q + hoff;
+  const bf16* Kh = K + hoff;
+  const bf16* Vh = V + hoff;
+
+  const int q0 = qb * BR + wave * 32;   // first query row of this wave
+  const int qrow = q0 + l32;            // the query row this lane's statistics belong to
+
+  // Q rows as the B operand of S^T = K Q^T: lane (n = l32, half h) holds
+  // d = 16*s + 8*h + r for K-step s.
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (qrow < N)
+      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + 16 * s + 8 * h);
+    else
+      qf[s] = bf16x8{};
+  }
+
+  const int kv_end = CAUSAL ? min(N, qb * BR + BR) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  int wave_tiles = 0;
+  if (q0 < N) {
+    const int wkv_end = CAUSAL ? min(N, q0 + 32) : N;
+    wave_tiles = (wkv_end + BC - 1) / BC;
+  }
+
+  u32x4 stK[LPT], stV[LPT];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int p = 0; p < LPT; ++p) {
+      const int ci = p * 256 + tid;
+      const int row = ci / CH, ch = ci % CH;
+      const int kv = j * BC + row;
+      if (kv < N) {
+        stK[p] = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv * D + ch * 8);
+        stV[p] = *reinterpret_cast<const u32x4*>(Vh + (size_t)kv * D + ch * 8);
+      } else {
+        stK[p] = u32x4{0, 0, 0, 0};
+        stV[p] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < LPT; ++p) {
+      const int ci = p * 256 + tid;
+      const int row = ci / CH, ch = ci % CH;
+      const int off = tile_off<ROWB>(row, ch);
+      *reinterpret_cast<u32x4*>(&smem[buf][0][off]) = stK[p];
+      *reinterpret_cast<u32x4*>(&smem[buf][1][off]) = stV[p];
+    }
+  };
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  float m_run = -INFINITY;   // running max of the raw scores q.k
+  float l_run = 0.f;         // running sum, partial over this lane's half of the keys
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+    if (j < wave_tiles) {
+      const char* Kt = smem[buf][0];
+      const char* Vt = smem[buf][1];
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 a = lds_read_b128(Kt, tile_off<ROWB>(mt * 32 + l32, 2 * ks + h));
+          s[mt] = mfma32(a, qf[ks], s[mt]);
+        }
+      }
+      // s[mt][4*i+jj] = q_qrow . k_kv with kv = j*BC + 32*mt + 8*i + 4*h + jj
+      const int kvb = j * BC;
+      const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0);
+      if (need_mask) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (kv >= N || (CAUSAL && kv > qrow)) s[mt][r] = -INFINITY;
+          }
+      }
+      float mx = m_run;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+      mx = half_max(mx);
+      // key 0 is never masked, so every row has a finite max from its first tile
+      const float alpha = exp2_fast((m_run - mx) * c);
+      const float nb = -mx * c;
+      float rs = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_fast(fmaf(s[mt][r], c, nb));
+          s[mt][r] = p;
+          rs += p;
+        }
+      l_run = fmaf(l_run, alpha, rs);
+      m_run = mx;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+      }
+      // P^T as B operand, K-step st covers keys 16*st .. 16*st+15 of the tile:
+      // registers 0..3 <- keys 16st+4h+jj, 4..7 <- keys 16st+8+4h+jj
+#pragma unroll
+      for (int st = 0; st < BC / 16; ++st) {
+        const int mt = st >> 1, i0 = 2 * (st & 1);
+        const bf16x8 pb = pack8(s[mt][4 * i0 + 0], s[mt][4 * i0 + 1], s[mt][4 * i0 + 2], s[mt][4 * i0 + 3],
+                                s[mt][4 * i0 + 4], s[mt][4 * i0 + 5], s[mt][4 * i0 + 6], s[mt][4 * i0 + 7]);
+        const int k0 = 16 * st + 4 * h;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          const bf16x8 a = tr_operand<ROWB>(Vt, k0, k0 + 8, 32 * t + 16 * (g & 1), lane);
+          oacc[t] = mfma32(a, pb, oacc[t]);
+        }
+      }
+    }
+    if (j + 1 < ntiles) swrite((j + 1) & 1);
+    __syncthreads();
+  }
+
+  if (q0 >= N) return;
+  const float l_tot = half_sum(l_run);
+  if (qrow < N) {
+    const float inv = 1.f / l_tot;
+    bf16* Orow = O + hoff + (size_t)qrow * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bf16x4 v;
+        v[0] = (bf16)(oacc[t][4 * i + 0] * inv);
+        v[1] = (bf16)(oacc[t][4 * i + 1] * inv);
+        v[2] = (bf16)(oacc[t][4 * i + 2] * inv);
+        v[3] = (bf16)(oacc[t][4 * i + 3] * inv);
+        *reinterpret_cast<bf16x4*>(Orow + 32 * t + 8 * i + 4 * h) = v;
+      }
+    if (h == 0) LSE[(size_t)head * N + qrow] = m_run * scale + log2_fast(l_tot) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int BH, int N, float scale, hipStream_t stream) {
+  const int nqb = (N + 127) / 128;
+  const dim3 grid((unsigned)(nqb * BH)), block(256);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), grid, block, 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
+                     scale * kLog2e);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                           int N, int d, bool causal, float scale, hipStream_t stream) {
+  if (d == 128)
+    return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, stream)
+                  : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, stream);
+  return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
+                : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,99 @@
+/*
+ * fa.h -- C ABI of the exact tiled attention library (libfa.so), gfx950.
+ *
+ * Exact softmax attention computed tile by tile on one GPU:
+ *   forward : O = softmax(scale * Q K^T [+ causal mask]) V, computed with an
+ *             online softmax that keeps, per query row, the running maximum m
+ *             and running sum l; only O and the fp32 log-sum-exp ledger
+ *             LSE_i = scale * m_i + ln l_i are written, never the N x N matrix
+ *             (page "flash-attention-backpropagation" (aiqz.cc), section
+ *             前向台账; page "flash-attention-v2-sram-tiling" (aiqz.cc),
+ *             section 5, the running-max / running-sum update).
+ *   backward: P^ = exp(scale * Q K^T - LSE) is recomputed block by block from
+ *             Q, K and the ledger; then dV = P^T dO, dP = dO V^T,
+ *             D_i = rowsum(dO o O), dS = P^ o (dP - D), dQ = scale * dS K,
+ *             dK = scale * dS^T Q (page "flash-attention-backpropagation",
+ *             sections 反向总览, Softmax梯度 and QKV梯度).
+ *
+ * Layout (every tensor): contiguous [B, H, N, d], row-major, d fastest, in
+ * the element type named by `dtype` (FA_BF16: bfloat16, FA_FP32: float).
+ * lse is float [B, H, N], natural log, in units of the scaled score
+ * scale * q_i . k_j.  The causal mask keeps key j for query i iff j <= i
+ * (queries and keys share the index range 0..N-1).
+ *
+ * Supported: d in {64, 128}; N >= 1 (any N, tails are masked); B, H >= 1 with
+ * B*H*N*d < 2^31; scale finite and > 0; causal in {0, 1}.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller.  The
+ * library allocates and frees nothing and never synchronises; each call only
+ * enqueues kernels on `stream` (a hipStream_t; 0 = the null stream) and
+ * returns.  Results are valid once the stream has completed.  Outputs must not
+ * alias inputs.  There is no global mutable state: concurrent calls on
+ * different streams are safe if their buffers are disjoint.
+ *
+ * Errors: every entry point returns an fa_status.  All argument checks run
+ * before any HIP call, so a rejected call has launched nothing.  A launch
+ * failure reported by the HIP runtime returns FA_ERR_HIP.  fa_strerror maps a
+ * status to a static string.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID = -1,      /* null pointer, non-positive size, bad flag, bad scale */
+  FA_ERR_UNSUPPORTED = -2,  /* head dim or dtype this build has no kernel for */
+  FA_ERR_WORKSPACE = -3,    /* backward workspace missing or too small */
+  FA_ERR_HIP = -4           /* the HIP runtime reported a launch error */
+} fa_status;
+
+typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
+
+/*
+ * Forward pass.  Reads q, k, v; writes o ([B,H,N,d], dtype) and
+ * lse ([B,H,N], float).  One workgroup owns a block of query rows and streams
+ * the key/value blocks through LDS, applying the online-softmax update of
+ * page "flash-attention-v2-sram-tiling", section 5, with the normalisation by
+ * l deferred to the end as in the NumPy demo of page
+ * "flash-attention-backpropagation" (section Python 演示).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, int causal, float scale,
+           void* stream, int dtype);
+
+/*
+ * Bytes of device workspace fa_bwd needs for this shape: the fp32 row term
+ * D [B,H,N], a staged copy of the ledger [B,H,N] and, for bf16, an fp32 dQ
+ * accumulator [B,H,N,d].  The caller allocates it (any 256-byte-aligned
+ * device buffer); its contents on entry do not matter.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward pass.  Reads q, k, v, o, dO and the ledger lse written by fa_fwd
+ * with the same q, k, v, causal and scale (the recompute of P^ is exact only
+ * for the ledger of that forward: page "flash-attention-backpropagation",
+ * section 数值稳定).  Writes dq, dk, dv ([B,H,N,d], dtype).  Uses `workspace`
+ * (at least fa_bwd_workspace_bytes bytes) as scratch; it is fully overwritten.
+ * Kernels, in stream order: D = rowsum(dO o O) (which also clears the dQ
+ * accumulator), the key/value-block-outer gradient kernel, the dQ conversion.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const void* dO, const float* lse, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, int causal, float scale,
+           void* workspace, size_t workspace_bytes, void* stream, int dtype);
+
+/* Static, human-readable text for a status code. */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,109 @@
+"""The C-ABI library: it loads, exports every entry point include/fa.h
+declares, and rejects bad arguments before any HIP call (so these checks run
+on a host without a GPU; no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_online_amd as fa
+from exact_tiled_attention_online_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libfa.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert header_functions() == sorted(_lib.EXPORTS)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    names = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    for name in header_functions():
+        assert re.search(rf"\bT {name}$", names, flags=re.M), name
+
+
+@needs_lib
+def test_strerror():
+    for st in (0, -1, -2, -3, -4):
+        assert isinstance(fa.fa_strerror(st), str) and fa.fa_strerror(st)
+    assert fa.fa_strerror(12345) == "unknown status"
+
+
+@needs_lib
+def test_workspace_size():
+    rows = 1 * 32 * 8192
+    bf = fa.fa_bwd_workspace_bytes(1, 32, 8192, 128, fa.FA_BF16)
+    assert bf == 2 * rows * 4 + rows * 128 * 4
+    f32 = fa.fa_bwd_workspace_bytes(1, 1, 128, 64, fa.FA_FP32)
+    assert f32 == 2 * 512
+    assert fa.fa_bwd_workspace_bytes(1, 1, 100, 64, fa.FA_BF16) % 256 == 0
+    assert fa.fa_bwd_workspace_bytes(0, 1, 128, 64, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 128, 96, fa.FA_BF16) == 0
+
+
+P = 0x10000  # a non-null, 256-byte aligned stand-in address; never dereferenced
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, causal=0, scale=0.125, stream=None,
+             dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.fa_fwd(**a)
+
+
+def bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, dO=P, lse=P, dq=P, dk=P, dv=P, B=1, H=1, N=128, d=64, causal=0,
+             scale=0.125, workspace=P, workspace_bytes=1 << 30, stream=None, dtype=fa.FA_BF16)
+    a.update(kw)
+    return fa.fa_bwd(**a)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1), (dict(causal=2), -1),
+    (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1), (dict(scale=0.0), -1),
+    (dict(scale=-0.1), -1), (dict(d=96), -2), (dict(d=256), -2), (dict(dtype=7), -2),
+    (dict(q=P + 8), -1), (dict(lse=P + 2), -1),
+    (dict(B=1024, H=1024, N=4096, d=128), -2),
+])
+def test_fwd_rejects(kw, status):
+    assert fwd(**kw) == status
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), -1), (dict(dq=None), -1), (dict(dk=None), -1), (dict(dv=None), -1),
+    (dict(N=-5), -1), (dict(d=32), -2), (dict(scale=float("-inf")), -1),
+    (dict(workspace=None), -3), (dict(workspace_bytes=1000), -3), (dict(workspace=P + 16), -3),
+    (dict(dv=P + 4), -1),
+])
+def test_bwd_rejects(kw, status):
+    assert bwd(**kw) == status
+
+
+@needs_lib
+def test_bwd_workspace_boundary():
+    need = fa.fa_bwd_workspace_bytes(1, 1, 128, 64, fa.FA_BF16)
+    assert bwd(workspace_bytes=need - 1) == -3
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        _lib.load()

@@ -1,0 +1,189 @@
+"""GPU parity of fa_fwd / fa_bwd (through the C ABI) against the fp64 oracle.
+
+Small and ragged shapes are compared element by element on every head; the
+five workloads run at their full sizes in the same launch configuration the
+benchmark uses, and are compared on whole sampled heads (heads are
+independent, so a head is an output the oracle can compute on its own), plus
+properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import exact_tiled_attention_online_amd as fa
+from exact_tiled_attention_online_amd import inputs as gen
+from gpu_util import compare, log, oracle_heads, run_gpu, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_compare(x, dtype, causal, scale, where):
+    res = run_gpu(x, dtype, causal, scale)
+    B, H = x["q"].shape[:2]
+    want = oracle_heads(x, causal, scale, heads=None)
+    errs = {}
+    for (b, h), w in want.items():
+        got = {n: res[n][b, h] for n in ("o", "lse", "dq", "dk", "dv")}
+        e = compare(got, w, dtype, where=f"{where} head ({b},{h})")
+        for n, v in e.items():
+            errs[n] = max(errs.get(n, 0.0), v)
+    return errs
+
+
+EDGE = [(dtype, d, causal, n)
+        for dtype in ("bf16", "fp32")
+        for d in (64, 128)
+        for causal in (False, True)
+        for n in (1, 17, 64, 129, 300)]
+
+
+@pytest.mark.parametrize("dtype,d,causal,n", EDGE)
+def test_small_and_ragged(dtype, d, causal, n):
+    log(f"[edge] dtype={dtype} d={d} causal={causal} N={n}")
+    w = gen.workload("c2")
+    x = gen.make_inputs(w, shape=(1, 2, n, d), seed=1000 + n + d, dtype=dtype)
+    _full_compare(x, dtype, causal, 1.0 / math.sqrt(d), f"edge {dtype} d{d} c{int(causal)} N{n}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_other_scale_and_spread(dtype, causal):
+    log(f"[scale] dtype={dtype} causal={causal}")
+    w = gen.workload("c2")
+    x = gen.make_inputs(w, shape=(2, 3, 200, 64), seed=77, sigma_qk=2.0, dtype=dtype)
+    _full_compare(x, dtype, causal, 0.3, f"scale0.3 {dtype} c{int(causal)}")
+
+
+def test_workload_c1_fp32():
+    w = gen.workload("c1")
+    log(f"[workload] {w.name}")
+    x = gen.make_inputs(w)
+    errs = _full_compare(x, "fp32", w.causal, w.scale, w.name)
+    log(f"  max errors {errs}")
+
+
+def test_workload_c2_bf16():
+    w = gen.workload("c2")
+    log(f"[workload] {w.name}")
+    x = gen.make_inputs(w)
+    errs = _full_compare(x, "bf16", w.causal, w.scale, w.name)
+    log(f"  max errors {errs}")
+
+
+SAMPLED = {"c3": [(0, 0), (1, 15)], "c4": [(0, 0), (0, 31)], "c5": [(0, 5)]}
+
+
+@pytest.fixture(scope="module")
+def big_runs():
+    cache = {}
+
+    def get(key):
+        if key not in cache:
+            w = gen.workload(key)
+            log(f"[workload] {w.name}: inputs")
+            x = gen.make_inputs(w)
+            log(f"[workload] {w.name}: gpu fwd+bwd")
+            res = run_gpu(x, "bf16", w.causal, w.scale, bwd=True)
+            cache.clear()
+            cache[key] = (w, x, res)
+        return cache[key]
+
+    return get
+
+
+@pytest.mark.parametrize("key", ["c3", "c4", "c5"])
+def test_full_size_sampled_heads(big_runs, key):
+    w, x, res = big_runs(key)
+    for b, h in SAMPLED[key]:
+        log(f"[workload] {w.name}: oracle head ({b},{h})")
+        want = oracle_heads(x, w.causal, w.scale, heads=[(b, h)])[(b, h)]
+        got = {n: res[n][b, h] for n in ("o", "lse", "dq", "dk", "dv")}
+        errs = compare(got, want, "bf16", where=f"{w.name} head ({b},{h})")
+        log(f"  max errors {errs}")
+
+
+@pytest.mark.parametrize("key", ["c3", "c4", "c5"])
+def test_full_size_invariants(big_runs, key):
+    """Sum_j dK_j = 0, Sum_j dV_j = Sum_i dO_i, O inside the box spanned by V,
+    on every head (consequences of sum_j dS_ij = 0 and of stochastic rows)."""
+    w, x, res = big_runs(key)
+    log(f"[invariants] {w.name}")
+    dk_sum = res["dk"].sum(axis=2)
+    dv_sum = res["dv"].sum(axis=2)
+    do_sum = x["do"].astype(np.float64).sum(axis=2)
+    # each row sum is over N bf16-rounded values; allow bf16 rounding per term
+    n = w.N
+    tol_k = 2e-2 * np.abs(res["dk"]).max() * math.sqrt(n)
+    tol_v = 2e-2 * np.abs(res["dv"]).max() * math.sqrt(n)
+    assert np.abs(dk_sum).max() <= tol_k, (np.abs(dk_sum).max(), tol_k)
+    assert np.abs(dv_sum - do_sum).max() <= tol_v, (np.abs(dv_sum - do_sum).max(), tol_v)
+    v = x["v"].astype(np.float64)
+    if not w.causal:
+        hi, lo = v.max(axis=2, keepdims=True), v.min(axis=2, keepdims=True)
+    else:
+        hi = np.maximum.accumulate(v, axis=2)
+        lo = np.minimum.accumulate(v, axis=2)
+    slack = 1e-2 * np.abs(v).max()
+    assert (res["o"] <= hi + slack).all() and (res["o"] >= lo - slack).all()
+    assert np.isfinite(res["lse"]).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_keys_and_constant_values(dtype, causal):
+    log(f"[special] dtype={dtype} causal={causal}")
+    w = gen.workload("c2")
+    x = gen.make_inputs(w, shape=(1, 2, 256, 128), seed=9, dtype=dtype)
+    x0 = dict(x, k=np.zeros_like(x["k"]))
+    _full_compare(x0, dtype, causal, 1 / math.sqrt(128), f"K=0 {dtype}")
+    vc = np.broadcast_to(x["v"][:, :, :1, :], x["v"].shape).copy()
+    xc = dict(x, v=vc)
+    _full_compare(xc, dtype, causal, 1 / math.sqrt(128), f"V const {dtype}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_alone_from_oracle_forward(causal):
+    """fa_bwd fed the oracle's O (rounded to bf16) and LSE: isolates the backward's error."""
+    import torch
+    log(f"[bwd-only] causal={causal}")
+    w = gen.workload("c3")
+    x = gen.make_inputs(w, shape=(1, 2, 1024, 128), seed=31)
+    want = oracle_heads(x, causal, w.scale, heads=None)
+    o = np.stack([want[(0, h)]["o"] for h in range(2)])[None].astype(np.float32)
+    lse = np.stack([want[(0, h)]["lse"] for h in range(2)])[None].astype(np.float32)
+    q, k, v, do = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    od = to_dev(o, "bf16")
+    ld = torch.from_numpy(lse).cuda()
+    dq, dk, dv = fa.backward(q, k, v, od, do, ld, causal, w.scale)
+    torch.cuda.synchronize()
+    for h in range(2):
+        got = {"dq": to_np(dq[0, h]), "dk": to_np(dk[0, h]), "dv": to_np(dv[0, h])}
+        compare(got, want[(0, h)], "bf16", names=("dq", "dk", "dv"), where=f"bwd-only head {h}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_deterministic_outputs(dtype):
+    """O, LSE, dK, dV are bitwise reproducible; dQ (atomic accumulation in
+    bf16 mode) only within tolerance."""
+    log(f"[determinism] {dtype}")
+    w = gen.workload("c2")
+    x = gen.make_inputs(w, shape=(2, 4, 512, 128), seed=5, dtype=dtype)
+    a = run_gpu(x, dtype, True, 1 / math.sqrt(128))
+    b = run_gpu(x, dtype, True, 1 / math.sqrt(128))
+    for n in ("o", "lse", "dk", "dv"):
+        assert np.array_equal(a[n], b[n]), n
+    assert np.abs(a["dq"] - b["dq"]).max() <= 1e-2 * np.abs(a["dq"]).max()
+
+
+def test_non_default_stream():
+    import torch
+    log("[stream] side stream")
+    w = gen.workload("c2")
+    x = gen.make_inputs(w, shape=(1, 2, 384, 64), seed=13)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        res = run_gpu(x, "bf16", True, 0.125, stream=s)
+    want = oracle_heads(x, True, 0.125, heads=None)
+    for (b, h), wv in want.items():
+        compare({n: res[n][b, h] for n in wv}, wv, "bf16", where=f"stream head {h}")
