@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention, forward + backward, on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+fa_fwd (O, LSE), then the backward's three stages fa_bwd_preprocess,
+fa_bwd_main and fa_bwd_finish (together exactly fa_bwd).  Inputs are resident
+in HBM before the timed region; W warm-up steps, then K timed steps between
+two device synchronisations.  HIP events recorded on the launch stream around
+every kernel give each kernel's average duration over the same timed steps.
+
+value = credited FLOPs of a step / step time, with the credited counts
+fwd = 4*B*H*N^2*d and bwd = 10*B*H*N^2*d, both halved for a causal mask.
+
+Prints one JSON line.  Default workload: B=1, H=32, N=8192, d=128, causal,
+bf16 (the headline shape).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak, 1×MI355X, N=8192 d=128"
+COUNTERS = os.path.join(ROOT, "profiles", "bwd_main_c4_counters.json")
+BWD_SOURCES = ["fa_bwd_bf16.hip", "fa_common.h"]
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_tiled_attention_online_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters():
+    """HBM bytes per launch of the backward main kernel, from the committed
+    rocprofv3 counter summary, or None if absent or taken on other sources."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    if c.get("source_digest") != source_digest(BWD_SOURCES):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s=12.0):
+    """Time the fp64 oracle on whole heads of the same workload until the
+    budget is spent (at least one head); credited-FLOP rate in TFLOP/s."""
+    import numpy as np
+    from oracle import ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    fwd1, bwd1 = w.flops()
+    per_head = (fwd1 + bwd1) / (w.B * w.H)
+    done, t0 = 0, time.perf_counter()
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    while done < len(heads):
+        b, h = heads[done]
+        ref.forward_backward(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal, heads=[(b, h)])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(per_head * done / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of the same workload (B=1,H=1,N={w.N},d={w.d}, "
+                      f"causal={w.causal}), fp64 materialised fwd+bwd, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4", help="c1..c5 (default c4, the headline shape)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(heads are independent, see the sharding note in the design document)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import exact_tiled_attention_online_amd as fa
+    from exact_tiled_attention_online_amd import inputs as gen
+
+    w = gen.workload(args.workload)
+    dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP32
+    x = gen.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (torch.from_numpy(x[n]).to(dev).to(dtype) for n in ("q", "k", "v", "do"))
+    B, H, N, d = w.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = fa.workspace(q)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()
+
+    def check(st, what):
+        if st != 0:
+            raise fa.FAError(st, what)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        check(fa.fa_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, N, d, w.causal, w.scale, sp, code), "fa_fwd")
+        if ev is not None:
+            ev[1].record(stream)
+        check(fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, P(ws), ws.numel(), sp, code),
+              "fa_bwd_preprocess")
+        if ev is not None:
+            ev[2].record(stream)
+        check(fa.fa_bwd_main(P(q), P(k), P(v), P(do), P(lse), P(dq), P(dk), P(dv), B, H, N, d, w.causal,
+                             w.scale, P(ws), ws.numel(), sp, code), "fa_bwd_main")
+        if ev is not None:
+            ev[3].record(stream)
+        check(fa.fa_bwd_finish(P(dq), B, H, N, d, w.scale, P(ws), ws.numel(), sp, code), "fa_bwd_finish")
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    def avg(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in events) / len(events)
+
+    fwd_ms, pre_ms, main_ms, fin_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    fwd_fl, bwd_fl = w.flops()
+    value = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
+    bwd_ms = pre_ms + main_ms + fin_ms
+    achieved = bwd_fl / (main_ms * 1e-3) / 1e12
+    elem = 2 if w.dtype == "bf16" else 4
+    T = B * H * N * d
+    pre_bytes = 2 * T * elem + 12 * B * H * N + (4 * T if w.dtype == "bf16" else 0)
+    fin_bytes = 6 * T if w.dtype == "bf16" else 0
+    traffic = traffic_from_counters() if args.workload == "c4" else None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
+                   "scale": w.scale, "inputs": f"N(0,{w.sigma_qk}^2) q,k; N(0,{w.sigma_vdo}^2) v,dO; seed {w.seed}"},
+        "roofline": {"kernel": "bwd_bf16_kernel (fa_bwd_main)", "bound": "mfma",
+                     "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "detail": {
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "bwd_preprocess_ms": round(pre_ms, 4), "bwd_main_ms": round(main_ms, 4),
+            "bwd_finish_ms": round(fin_ms, 4),
+            "fwd_tflops": round(fwd_fl / (fwd_ms * 1e-3) / 1e12, 3),
+            "bwd_tflops": round(bwd_fl / (bwd_ms * 1e-3) / 1e12, 3),
+            "fwd_frac_peak": round(fwd_fl / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bwd_frac_peak": round(bwd_fl / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "preprocess_gbs": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
+            "finish_gbs": round(fin_bytes / (fin_ms * 1e-3) / 1e9, 1) if fin_bytes else None,
+            "gpu": torch.cuda.get_device_name(0),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -89,6 +89,28 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int H, int N, int d, int causal, float scale,
            void* workspace, size_t workspace_bytes, void* stream, int dtype);
 
+/*
+ * The three stages fa_bwd runs, in this order on one stream, for callers that
+ * schedule them themselves (for example to time or overlap them).  Calling
+ * all three with the same arguments is exactly fa_bwd.
+ *
+ * fa_bwd_preprocess: D_i = sum_c dO_ic * O_ic (page
+ *   "flash-attention-backpropagation", section Softmax梯度), the ledger in
+ *   base 2, and the clear of the dQ accumulator; writes only the workspace.
+ * fa_bwd_main: the key/value-block-outer gradient kernel (section QKV梯度):
+ *   writes dk, dv; for bf16 accumulates dQ into the workspace, for fp32 also
+ *   runs the query-row-outer dQ kernel and writes dq.
+ * fa_bwd_finish: bf16 only, dq = bf16(scale * accumulator); no-op for fp32.
+ * Argument meaning, checks and errors are those of fa_bwd.
+ */
+int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
+                      void* workspace, size_t workspace_bytes, void* stream, int dtype);
+int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+                void* workspace, size_t workspace_bytes, void* stream, int dtype);
+int fa_bwd_finish(void* dq, int B, int H, int N, int d, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream, int dtype);
+
 /* Static, human-readable text for a status code. */
 const char* fa_strerror(int status);
 
