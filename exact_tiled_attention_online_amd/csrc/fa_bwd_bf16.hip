@@ -21,6 +21,16 @@
 // The accumulators hold fp32 and are converted once at write-back (page
 // "gsyq.cn news/1372000", 踩坑三).  scale is applied to dK here and to dQ by
 // the conversion kernel.
+//
+// Pipelining: Q/dO/LSE/D of the next query block are fetched straight into
+// the other LDS buffer (global_load_lds) while the current block is used; the
+// dQ product of a block runs at the start of the next iteration so that its
+// atomics drain under the next block's products; one barrier per block.  The
+// loop body is instantiated per buffer so that every LDS buffer is a distinct
+// object (the compiler then knows the prefetch cannot alias the reads).
+// LDS addresses are a few per-lane bases plus compile-time offsets.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -35,6 +45,20 @@ FA_DEV int ds_off(int row, int col) {
   return row * 128 + (slot << 3) + ((col & 3) << 1);
 }
 
+template <int B>
+using IC = std::integral_constant<int, B>;
+
+// wave-wide direct fetch: lane l's 16 (or 4) bytes land at lds_base + 16*l
+// (or 4*l); lds_base must be the same for the whole wave
+FA_DEV void dma16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (FA_LDS void*)lds_base, 16, 0, 0);
+}
+FA_DEV void dma4(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (FA_LDS void*)lds_base, 4, 0, 0);
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -44,18 +68,24 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   constexpr int BC = 128, BR = 64;
   constexpr int ROWB = D * 2, CH = D / 8, KS = D / 16, DT = D / 32;
   constexpr int QTB = BR * ROWB;          // bytes of one Q or dO tile
-  constexpr int LPT = BR * CH / 256;      // 16-byte loads per thread per tile
+  constexpr int RPL = 1024 / ROWB;        // tile rows per 1 KB wave-wide LDS load
+  constexpr int LPW = BR / RPL / 4;       // such loads per wave per tile
   constexpr int NQT = (D == 128) ? 2 : 1; // query tiles of dQ per wave
 
-  __shared__ __attribute__((aligned(16))) char sQ[2][QTB];
-  __shared__ __attribute__((aligned(16))) char sG[2][QTB];   // dO
-  __shared__ __attribute__((aligned(16))) float sL[2][BR];   // LSE * log2 e
-  __shared__ __attribute__((aligned(16))) float sD[2][BR];   // D
-  __shared__ __attribute__((aligned(16))) char sS[BC * BR * 2];  // dS, [key][query]
-  __shared__ __attribute__((aligned(16))) char sK[BC * ROWB];    // K block (start) / output staging
+  __shared__ __attribute__((aligned(1024))) char sQ0[QTB];
+  __shared__ __attribute__((aligned(1024))) char sQ1[QTB];
+  __shared__ __attribute__((aligned(1024))) char sG0[QTB];   // dO
+  __shared__ __attribute__((aligned(1024))) char sG1[QTB];
+  __shared__ __attribute__((aligned(256))) float sL0[BR];    // LSE * log2 e
+  __shared__ __attribute__((aligned(256))) float sL1[BR];
+  __shared__ __attribute__((aligned(256))) float sD0[BR];    // D
+  __shared__ __attribute__((aligned(256))) float sD1[BR];
+  __shared__ __attribute__((aligned(1024))) char sS0[BC * BR * 2];  // dS, [key][query]
+  __shared__ __attribute__((aligned(1024))) char sS1[BC * BR * 2];
+  __shared__ __attribute__((aligned(1024))) char sK[BC * ROWB];     // K block / output staging
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, h = lane >> 5, g = lane >> 4;
+  const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, s16 = lane & 15;
   const int bid = blockIdx.x;
   const int head = bid % BH;
   const int kb = bid / BH;                 // ascending key block = descending causal work
@@ -71,6 +101,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   const int kv0 = kb * BC;
   const int kvw = kv0 + 32 * wave;         // first key row of this wave
   const int kvrow = kvw + l32;             // key row of this lane in the S accumulators
+  const int krow = 32 * wave + l32;        // the same row within the block
 
   // ---- K block into LDS, then the register operands -----------------------
   {
@@ -108,43 +139,59 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   for (int s = 0; s < BC / 16; ++s)
     ktf[s] = tr_operand<ROWB>(sK, 16 * s + 8 * h, 16 * s + 8 * h + 4, 32 * dsl + 16 * (g & 1), lane);
 
+  // ---- per-lane LDS address bases ------------------------------------------
+  // A operand (rows = query, registers = d) of S / dP, from a swizzled tile:
+  // offset(t, ks) = baseA[ks % 4] + 128*(ks / 4) + 32*t*ROWB.
+  const int swA = swz(l32);
+  int baseA[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) baseA[j] = l32 * ROWB + 16 * (h ^ (swA & 1)) + 32 * (j ^ (swA >> 1));
+  // transposed B operand (registers = query rows) of dV / dK, from the same
+  // tiles: offset(st, dt, hi) = baseC[dt % 2] + 64*(dt & ~1) + (16*st + 8*hi)*ROWB.
+  int baseC[2];
+  {
+    const int sw = 2 * (s16 >> 2) + h;
+    const int cc = 2 * (g & 1) + ((s16 & 3) >> 1);
+    const int L = (4 * h + (s16 >> 2)) * ROWB + 16 * (cc ^ (sw & 3)) + 8 * (s16 & 1);
+    const int b = sw >> 2;
+    baseC[0] = L + 64 * b;          // dt even: chunk group dt ^ b = dt + b
+    baseC[1] = L + 64 * (1 - b);    // dt odd:  chunk group dt ^ b = (dt - 1) + (1 - b)
+  }
+  // transposed A operand of dQ (registers = key rows) from the dS tile:
+  // offset(s, u, hi) = baseE[u][hi] + 2048*s.
+  int baseE[NQT][2];
+  {
+    const int a = s16 >> 2;
+    const int E = (4 * (g & 1) + (s16 & 3)) ^ (4 * (a & 1) + 2 * h);
+#pragma unroll
+    for (int u = 0; u < NQT; ++u)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int mt = mt0 + u;
+        baseE[u][hi] = (8 * h + a + 4 * hi) * 128 + 64 * (mt ^ (a >> 1)) + 8 * (E ^ hi);
+      }
+  }
+
   const int i_begin = CAUSAL ? (kv0 / BR) : 0;
 
-  u32x4 stQ[LPT], stG[LPT];
-  float stL = 0.f;
-  auto gload = [&](int i) {
+  // ---- direct global -> LDS fetch of one query block ------------------------
+  // wave w, load j fills LDS bytes [(w*LPW + j) KB, +1 KB): tile rows
+  // (w*LPW + j)*RPL + lane/CH, chunk position lane%CH (logical chunk
+  // position ^ swz(row)).  Rows past N read row N-1 (finite; masked later).
+  auto fetch = [&](int i, char* dQt, char* dGt, float* dL, float* dD) {
+    const int qb0 = i * BR;
 #pragma unroll
-    for (int p = 0; p < LPT; ++p) {
-      const int ci = p * 256 + tid;
-      const int row = ci / CH, ch = ci % CH;
-      const int q = i * BR + row;
-      if (q < N) {
-        stQ[p] = *reinterpret_cast<const u32x4*>(Qh + (size_t)q * D + ch * 8);
-        stG[p] = *reinterpret_cast<const u32x4*>(Gh + (size_t)q * D + ch * 8);
-      } else {
-        stQ[p] = u32x4{0, 0, 0, 0};
-        stG[p] = u32x4{0, 0, 0, 0};
-      }
+    for (int j = 0; j < LPW; ++j) {
+      const int blk = wave * LPW + j;
+      const int row = blk * RPL + lane / CH;
+      const int ch = (lane % CH) ^ swz(row);
+      const int q = min(qb0 + row, N - 1);
+      const size_t go = (size_t)q * D + ch * 8;
+      dma16(Qh + go, dQt + blk * 1024);
+      dma16(Gh + go, dGt + blk * 1024);
     }
-    if (tid < 2 * BR) {
-      const int q = i * BR + (tid & (BR - 1));
-      stL = 0.f;
-      if (q < N) stL = (tid < BR) ? Lh[q] : Dh[q];
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < LPT; ++p) {
-      const int ci = p * 256 + tid;
-      const int row = ci / CH, ch = ci % CH;
-      const int off = tile_off<ROWB>(row, ch);
-      *reinterpret_cast<u32x4*>(&sQ[buf][off]) = stQ[p];
-      *reinterpret_cast<u32x4*>(&sG[buf][off]) = stG[p];
-    }
-    if (tid < BR)
-      sL[buf][tid] = stL;
-    else if (tid < 2 * BR)
-      sD[buf][tid - BR] = stL;
+    if (wave == 0) dma4(Lh + min(qb0 + lane, N - 1), dL);
+    if (wave == 1) dma4(Dh + min(qb0 + lane, N - 1), dD);
   };
 
   f32x16 dk[DT], dv[DT];
@@ -154,119 +201,137 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     dv[t] = f32x16{};
   }
 
-  if (i_begin < nqb) {
-    gload(i_begin);
-    swrite(0);
-  }
-  __syncthreads();
-
-  for (int i = i_begin; i < nqb; ++i) {
-    const int buf = (i - i_begin) & 1;
-    if (i + 1 < nqb) gload(i + 1);
-    const int qb0 = i * BR;
-    const char* Qt = sQ[buf];
-    const char* Gt = sG[buf];
-    // this wave's keys are all later than all queries of the block: P^ = 0
-    const bool skip = (kvw >= N) || (CAUSAL && qb0 + BR - 1 < kvw);
-    if (!skip) {
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-      f32x16 dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int off = tile_off<ROWB>(32 * t + l32, 2 * ks + h);
-          s[t] = mfma32(lds_read_b128(Qt, off), kf[ks], s[t]);
-          dp[t] = mfma32(lds_read_b128(Gt, off), vf[ks], dp[t]);
-        }
-      }
-      // accumulator r of tile t: query qb0 + 32t + 8*(r/4) + 4h + r%4, key kvrow
-      const bool need_mask = (CAUSAL && qb0 < kvw + 31) || (qb0 + BR > N) || (kvw + 32 > N);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int ql = 32 * t + 8 * i4 + 4 * h;
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[buf][ql]);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[buf][ql]);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int r = 4 * i4 + jj;
-            float p = exp2_fast(fmaf(s[t][r], c, -L4[jj]));
-            if (need_mask) {
-              const int q = qb0 + ql + jj;
-              if (q >= N || kvrow >= N || (CAUSAL && kvrow > q)) p = 0.f;
-            }
-            s[t][r] = p;
-            dp[t][r] = p * (dp[t][r] - D4[jj]);
-          }
-        }
-      // P^T and dS^T as A operands (lane = key row), K-step st covers queries
-      // 16st..16st+15: registers 0..3 <- 16st+4h+jj, 4..7 <- 16st+8+4h+jj
-#pragma unroll
-      for (int st = 0; st < BR / 16; ++st) {
-        const int t = st >> 1, i0 = 2 * (st & 1);
-        const bf16x8 pa = pack8(s[t][4 * i0 + 0], s[t][4 * i0 + 1], s[t][4 * i0 + 2], s[t][4 * i0 + 3],
-                                s[t][4 * i0 + 4], s[t][4 * i0 + 5], s[t][4 * i0 + 6], s[t][4 * i0 + 7]);
-        const bf16x8 da = pack8(dp[t][4 * i0 + 0], dp[t][4 * i0 + 1], dp[t][4 * i0 + 2], dp[t][4 * i0 + 3],
-                                dp[t][4 * i0 + 4], dp[t][4 * i0 + 5], dp[t][4 * i0 + 6], dp[t][4 * i0 + 7]);
-        const int k0 = 16 * st + 4 * h;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int n0 = 32 * dt + 16 * (g & 1);
-          dv[dt] = mfma32(pa, tr_operand<ROWB>(Gt, k0, k0 + 8, n0, lane), dv[dt]);
-          dk[dt] = mfma32(da, tr_operand<ROWB>(Qt, k0, k0 + 8, n0, lane), dk[dt]);
-        }
-      }
-      // dS (bf16) to LDS, [key][query]
-      const int krow = 32 * wave + l32;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4 v;
-          v[0] = (bf16)dp[t][4 * i4 + 0];
-          v[1] = (bf16)dp[t][4 * i4 + 1];
-          v[2] = (bf16)dp[t][4 * i4 + 2];
-          v[3] = (bf16)dp[t][4 * i4 + 3];
-          *reinterpret_cast<bf16x4*>(&sS[ds_off(krow, 32 * t + 8 * i4 + 4 * h)]) = v;
-        }
-    } else {
-      const int krow = 32 * wave + l32;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          *reinterpret_cast<u32x2*>(&sS[ds_off(krow, 32 * t + 8 * i4 + 4 * h)]) = u32x2{0, 0};
-    }
-    __syncthreads();
-    // dQ_i += dS K over the whole key block: wave takes d-slice dsl and query
-    // tiles mt0 .. mt0+NQT-1.  A = dS with the query across lanes (transposing
-    // reads of the [key][query] tile), B = K^T slice in registers.
+  // dQ_ip += dS_ip K over the whole key block, from the dS tile St: the wave
+  // takes d-slice dsl and query tiles mt0 .. mt0+NQT-1.  A = dS with the
+  // query across lanes, B = the K^T slice in registers.
+  auto dq_product = [&](int ip, const char* St) {
+    const int qp0 = ip * BR;
 #pragma unroll
     for (int u = 0; u < NQT; ++u) {
       const int mt = mt0 + u;
-      if (qb0 + 32 * mt >= N) continue;
+      if (qp0 + 32 * mt >= N) continue;
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int s = 0; s < BC / 16; ++s) {
-        const int kr = 16 * s + 8 * h;
-        const int scol = lane & 15;
-        const int col = 32 * mt + 16 * (g & 1) + 4 * (scol & 3);
-        const bf16x4 lo = lds_read_tr(sS, ds_off(kr + (scol >> 2), col));
-        const bf16x4 hi = lds_read_tr(sS, ds_off(kr + 4 + (scol >> 2), col));
+        const bf16x4 lo = lds_read_tr(St, baseE[u][0] + 2048 * s);
+        const bf16x4 hi = lds_read_tr(St, baseE[u][1] + 2048 * s);
         acc = mfma32(cat(lo, hi), ktf[s], acc);
       }
       // acc[4*i4+jj] = dQ[query 32mt + 8*i4 + 4h + jj][d 32*dsl + l32]
-      float* dst = dQh + (size_t)(qb0 + 32 * mt) * D + 32 * dsl + l32;
+      const int qrow0 = qp0 + 32 * mt + 4 * h;
+      float* dst = dQh + (size_t)qrow0 * D + 32 * dsl + l32;
+      if (qp0 + 32 * mt + 32 <= N) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ql = 8 * (r >> 2) + 4 * h + (r & 3);
-        if (qb0 + 32 * mt + ql < N) unsafeAtomicAdd(dst + (size_t)ql * D, acc[r]);
+        for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r]);
+      } else {
+        const int nvalid = N - qrow0;   // register r is a valid row iff ql(r) < nvalid
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = 8 * (r >> 2) + (r & 3);
+          if (ql < nvalid) unsafeAtomicAdd(dst + ql * D, acc[r]);
+        }
       }
     }
-    if (i + 1 < nqb) swrite(buf ^ 1);
+  };
+
+  // one query block: products from buffer b, prefetch into buffer b^1
+  auto body = [&](auto bc, int i) {
+    constexpr int b = decltype(bc)::value;
+    char* Qt = b ? sQ1 : sQ0;
+    char* Gt = b ? sG1 : sG0;
+    const float* Lt = b ? sL1 : sL0;
+    const float* Dt = b ? sD1 : sD0;
+    char* St = b ? sS1 : sS0;
+    const int it = i - i_begin;
+    if (i + 1 < nqb) fetch(i + 1, b ? sQ0 : sQ1, b ? sG0 : sG1, b ? sL0 : sL1, b ? sD0 : sD1);
+    if (it > 0) dq_product(i - 1, b ? sS0 : sS1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int qb0 = i * BR;
+    // this wave's keys are all later than all queries of the block: P^ = 0
+    const bool skip = (kvw >= N) || (CAUSAL && qb0 + BR - 1 < kvw);
+    if (!skip) {
+      const bool need_mask = (CAUSAL && qb0 < kvw + 31) || (qb0 + BR > N) || (kvw + 32 > N);
+      // P^T and dS^T as A operands (lane = key row); K-step st covers queries
+      // 16st..16st+15: registers 0..3 <- 16st+4h+jj, 4..7 <- 16st+8+4h+jj
+      bf16x8 pa[BR / 16], da[BR / 16];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int off = baseA[ks & 3] + 128 * (ks >> 2) + 32 * t * ROWB;
+          s = mfma32(lds_read_b128(Qt, off), kf[ks], s);
+          dp = mfma32(lds_read_b128(Gt, off), vf[ks], dp);
+        }
+        // register r: query qb0 + 32t + 8*(r/4) + 4h + r%4, key kvrow
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int ql = 32 * t + 8 * i4 + 4 * h;
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(Lt + ql);
+          const f32x4 D4 = *reinterpret_cast<const f32x4*>(Dt + ql);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int r = 4 * i4 + jj;
+            float p = exp2_fast(fmaf(s[r], c, -L4[jj]));
+            if (need_mask) {
+              const int q = qb0 + ql + jj;
+              const bool dead = (q >= N) | (kvrow >= N) | (CAUSAL & (kvrow > q));
+              p = dead ? 0.f : p;
+            }
+            s[r] = p;
+            dp[r] = p * (dp[r] - D4[jj]);
+          }
+        }
+        pa[2 * t] = pack8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
+        pa[2 * t + 1] = pack8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
+        da[2 * t] = pack8(dp[0], dp[1], dp[2], dp[3], dp[4], dp[5], dp[6], dp[7]);
+        da[2 * t + 1] = pack8(dp[8], dp[9], dp[10], dp[11], dp[12], dp[13], dp[14], dp[15]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // dV += P^T dO, dK += dS^T Q; B = dO / Q rows through transposing reads
+#pragma unroll
+      for (int st = 0; st < BR / 16; ++st) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int o0 = baseC[dt & 1] + 64 * (dt & ~1) + 16 * st * ROWB;
+          const int o1 = o0 + 8 * ROWB;
+          dv[dt] = mfma32(pa[st], cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1)), dv[dt]);
+          dk[dt] = mfma32(da[st], cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1)), dk[dt]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // dS (bf16) to LDS, [key][query]
+#pragma unroll
+      for (int st = 0; st < BR / 16; ++st) {
+        const bf16x4 lo = __builtin_shufflevector(da[st], da[st], 0, 1, 2, 3);
+        const bf16x4 hi = __builtin_shufflevector(da[st], da[st], 4, 5, 6, 7);
+        *reinterpret_cast<bf16x4*>(&St[ds_off(krow, 16 * st + 4 * h)]) = lo;
+        *reinterpret_cast<bf16x4*>(&St[ds_off(krow, 16 * st + 8 + 4 * h)]) = hi;
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < BR / 16; ++st) {
+        *reinterpret_cast<u32x2*>(&St[ds_off(krow, 16 * st + 4 * h)]) = u32x2{0, 0};
+        *reinterpret_cast<u32x2*>(&St[ds_off(krow, 16 * st + 8 + 4 * h)]) = u32x2{0, 0};
+      }
+    }
     __syncthreads();
+  };
+
+  if (i_begin < nqb) {
+    fetch(i_begin, sQ0, sG0, sL0, sD0);
+    __syncthreads();
+    int i = i_begin;
+    while (true) {
+      body(IC<0>{}, i);
+      if (++i >= nqb) break;
+      body(IC<1>{}, i);
+      if (++i >= nqb) break;
+    }
+    if (((nqb - 1 - i_begin) & 1) == 0)
+      dq_product(nqb - 1, sS0);
+    else
+      dq_product(nqb - 1, sS1);
   }
 
   // ---- write-back: dK = scale * acc, dV = acc, staged through LDS ----------
