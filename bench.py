@@ -3,7 +3,7 @@
 
 A step is one pass of the whole path over one batch of synthetic input:
 fa_fwd (O, LSE), then the backward's three stages fa_bwd_preprocess,
-fa_bwd_main and fa_bwd_finish (together exactly fa_bwd).  Inputs are resident
+fa_bwd_dkdv and fa_bwd_dq (together exactly fa_bwd).  Inputs are resident
 in HBM before the timed region; W warm-up steps, then K timed steps between
 two device synchronisations.  HIP events recorded on the launch stream around
 every kernel give each kernel's average duration over the same timed steps.
@@ -29,8 +29,13 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak, 1×MI355X, N=8192 d=128"
-COUNTERS = os.path.join(ROOT, "profiles", "bwd_main_c4_counters.json")
-BWD_SOURCES = ["fa_bwd_bf16.hip", "fa_common.h"]
+COUNTERS = os.path.join(ROOT, "profiles", "counters_c4.json")
+# sources each timed kernel is built from (a counter record is valid only for these)
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": ["fa_fwd_bf16.hip", "fa_common.h"],
+    "bwd_bf16_kernel": ["fa_bwd_bf16.hip", "fa_common.h"],
+    "bwd_dq_kernel": ["fa_bwd_dq.hip", "fa_common.h"],
+}
 
 
 def source_digest(names):
@@ -41,14 +46,14 @@ def source_digest(names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_counters():
-    """HBM bytes per launch of the backward main kernel, from the committed
-    rocprofv3 counter summary, or None if absent or taken on other sources."""
+def traffic_from_counters(kernel):
+    """HBM bytes per launch of `kernel`, from the committed rocprofv3 counter
+    summary, or None if absent or taken on other sources."""
     if not os.path.exists(COUNTERS):
         return None
     with open(COUNTERS) as f:
-        c = json.load(f)
-    if c.get("source_digest") != source_digest(BWD_SOURCES):
+        c = json.load(f).get(kernel)
+    if not c or c.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -127,11 +132,12 @@ def main():
               "fa_bwd_preprocess")
         if ev is not None:
             ev[2].record(stream)
-        check(fa.fa_bwd_main(P(q), P(k), P(v), P(do), P(lse), P(dq), P(dk), P(dv), B, H, N, d, w.causal,
-                             w.scale, P(ws), ws.numel(), sp, code), "fa_bwd_main")
+        check(fa.fa_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, N, d, w.causal,
+                             w.scale, P(ws), ws.numel(), sp, code), "fa_bwd_dkdv")
         if ev is not None:
             ev[3].record(stream)
-        check(fa.fa_bwd_finish(P(dq), B, H, N, d, w.scale, P(ws), ws.numel(), sp, code), "fa_bwd_finish")
+        check(fa.fa_bwd_dq(P(q), P(k), P(v), P(do), P(lse), P(dq), B, H, N, d, w.causal, w.scale,
+                           P(ws), ws.numel(), sp, code), "fa_bwd_dq")
         if ev is not None:
             ev[4].record(stream)
 
@@ -149,16 +155,26 @@ def main():
     def avg(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in events) / len(events)
 
-    fwd_ms, pre_ms, main_ms, fin_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    fwd_ms, pre_ms, kv_ms, dq_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
     fwd_fl, bwd_fl = w.flops()
+    unit = bwd_fl / 5.0             # one N x N x d product: 2*B*H*N^2*d FLOPs (halved if causal)
     value = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
-    bwd_ms = pre_ms + main_ms + fin_ms
-    achieved = bwd_fl / (main_ms * 1e-3) / 1e12
+    bwd_ms = pre_ms + kv_ms + dq_ms
+    atomic = os.environ.get("FA_DQ_MODE") == "atomic"
+    # algorithmic FLOPs per launch of each kernel: the products it computes
+    kernels = {
+        "fwd_bf16_kernel": (fwd_ms, 2 * unit),                       # S, P V
+        "bwd_bf16_kernel": (kv_ms, (5 if atomic else 4) * unit),     # S, dP, dV, dK (+ dQ)
+    }
+    if not atomic:
+        kernels["bwd_dq_kernel"] = (dq_ms, 3 * unit)                 # S, dP, dQ
+    dom = max(kernels, key=lambda k: kernels[k][0])
+    dom_ms, dom_fl = kernels[dom]
+    achieved = dom_fl / (dom_ms * 1e-3) / 1e12
     elem = 2 if w.dtype == "bf16" else 4
     T = B * H * N * d
-    pre_bytes = 2 * T * elem + 12 * B * H * N + (4 * T if w.dtype == "bf16" else 0)
-    fin_bytes = 6 * T if w.dtype == "bf16" else 0
-    traffic = traffic_from_counters() if args.workload == "c4" else None
+    pre_bytes = 2 * T * elem + 12 * B * H * N
+    traffic = traffic_from_counters(dom) if (args.workload == "c4" and not atomic) else None
 
     out = {
         "metric": METRIC,
@@ -175,19 +191,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal,
                    "scale": w.scale, "inputs": f"N(0,{w.sigma_qk}^2) q,k; N(0,{w.sigma_vdo}^2) v,dO; seed {w.seed}"},
-        "roofline": {"kernel": "bwd_bf16_kernel (fa_bwd_main)", "bound": "mfma",
+        "roofline": {"kernel": dom, "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "detail": {
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
-            "bwd_preprocess_ms": round(pre_ms, 4), "bwd_main_ms": round(main_ms, 4),
-            "bwd_finish_ms": round(fin_ms, 4),
+            "bwd_preprocess_ms": round(pre_ms, 4), "bwd_dkdv_ms": round(kv_ms, 4),
+            "bwd_dq_ms": round(dq_ms, 4), "dq_mode": "atomic" if atomic else "query-outer",
             "fwd_tflops": round(fwd_fl / (fwd_ms * 1e-3) / 1e12, 3),
             "bwd_tflops": round(bwd_fl / (bwd_ms * 1e-3) / 1e12, 3),
             "fwd_frac_peak": round(fwd_fl / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "bwd_frac_peak": round(bwd_fl / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernel_tflops": {k: round(f / (t * 1e-3) / 1e12, 3) for k, (t, f) in kernels.items()},
             "preprocess_gbs": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
-            "finish_gbs": round(fin_bytes / (fin_ms * 1e-3) / 1e9, 1) if fin_bytes else None,
             "gpu": torch.cuda.get_device_name(0),
         },
     }

@@ -6,7 +6,7 @@ The Python layer only marshals arguments; see ``_lib`` for the entry points
 conveniences ``forward`` / ``backward``.
 """
 from ._lib import (  # noqa: F401
-    FA_BF16, FA_FP32, FAError, LIB_PATH, backward, fa_bwd, fa_bwd_finish, fa_bwd_main,
+    FA_BF16, FA_FP32, FAError, LIB_PATH, backward, fa_bwd, fa_bwd_dkdv, fa_bwd_dq,
     fa_bwd_preprocess, fa_bwd_workspace_bytes, fa_fwd,
     fa_strerror, forward, load, workspace,
 )

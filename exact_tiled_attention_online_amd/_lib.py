@@ -16,8 +16,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
 FA_BF16, FA_FP32 = 0, 1
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_main",
-           "fa_bwd_finish", "fa_strerror")
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
+           "fa_bwd_dq", "fa_strerror")
 
 _lib = None
 
@@ -46,10 +46,10 @@ def load():
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp, i]
     lib.fa_bwd_preprocess.restype = i
-    lib.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i]
-    lib.fa_bwd_main.restype = i
-    lib.fa_bwd_finish.argtypes = [vp, i, i, i, i, f, vp, sz, vp, i]
-    lib.fa_bwd_finish.restype = i
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i]
+    lib.fa_bwd_dkdv.restype = i
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i]
+    lib.fa_bwd_dq.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -76,14 +76,16 @@ def fa_bwd_preprocess(o, dO, lse, B, H, N, d, workspace, workspace_bytes, stream
     return load().fa_bwd_preprocess(o, dO, lse, B, H, N, d, workspace, workspace_bytes, stream, dtype)
 
 
-def fa_bwd_main(q, k, v, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes,
+def fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes,
                 stream, dtype) -> int:
-    return load().fa_bwd_main(q, k, v, dO, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
+    return load().fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, int(causal), float(scale),
                               workspace, workspace_bytes, stream, dtype)
 
 
-def fa_bwd_finish(dq, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype) -> int:
-    return load().fa_bwd_finish(dq, B, H, N, d, float(scale), workspace, workspace_bytes, stream, dtype)
+def fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, causal, scale, workspace, workspace_bytes,
+              stream, dtype) -> int:
+    return load().fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, int(causal), float(scale),
+                            workspace, workspace_bytes, stream, dtype)
 
 
 def fa_strerror(status: int) -> str:

@@ -6,6 +6,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "fa_launch.h"
 
@@ -56,6 +58,13 @@ Workspace carve(void* base, int B, int H, int N, int d, int dtype) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// dQ path of the bf16 backward: the query-block-outer kernel (default), or
+// fp32 atomics from the key/value-outer kernel when FA_DQ_MODE=atomic.
+bool dq_atomic_mode() {
+  const char* m = std::getenv("FA_DQ_MODE");
+  return m && std::strcmp(m, "atomic") == 0;
+}
+
 bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d, int dtype) {
   return ws && aligned(ws, kAlign) && bytes >= carve(nullptr, B, H, N, d, dtype).bytes;
 }
@@ -92,42 +101,51 @@ int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, in
   if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(lse, 4)) return FA_ERR_INVALID;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
   const Workspace w = carve(workspace, B, H, N, d, dtype);
-  return hip_status(fa::launch_bwd_pre(o, dO, lse, w.drow, w.lse2, w.dq_acc, B * H, N, d, dtype == FA_FP32,
+  float* dq_acc = (dtype == FA_BF16 && dq_atomic_mode()) ? w.dq_acc : nullptr;
+  return hip_status(fa::launch_bwd_pre(o, dO, lse, w.drow, w.lse2, dq_acc, B * H, N, d, dtype == FA_FP32,
                                        static_cast<hipStream_t>(stream)));
 }
 
-int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq,
-                void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dk,
+                void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
                 size_t workspace_bytes, void* stream, int dtype) {
-  if (!q || !k || !v || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID;
+  if (!q || !k || !v || !dO || !lse || !dk || !dv) return FA_ERR_INVALID;
   const int st = check_shape(B, H, N, d, causal, scale, dtype);
   if (st != FA_OK) return st;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dq, 16) ||
-      !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
   const Workspace w = carve(workspace, B, H, N, d, dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == FA_FP32)
-    return hip_status(fa::launch_bwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                                         static_cast<const float*>(v), static_cast<const float*>(dO), lse,
-                                         w.drow, static_cast<float*>(dq), static_cast<float*>(dk),
-                                         static_cast<float*>(dv), B * H, N, d, causal != 0, scale, s));
-  return hip_status(
-      fa::launch_bwd_bf16(q, k, v, dO, w.lse2, w.drow, w.dq_acc, dk, dv, B * H, N, d, causal != 0, scale, s));
+    return hip_status(fa::launch_bwd_kv_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                            static_cast<const float*>(v), static_cast<const float*>(dO), lse,
+                                            w.drow, static_cast<float*>(dk), static_cast<float*>(dv), B * H, N,
+                                            d, causal != 0, scale, s));
+  return hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.lse2, w.drow, w.dq_acc, dk, dv, B * H, N, d,
+                                        causal != 0, scale, dq_atomic_mode(), s));
 }
 
-int fa_bwd_finish(void* dq, int B, int H, int N, int d, float scale, void* workspace, size_t workspace_bytes,
-                  void* stream, int dtype) {
-  if (!dq) return FA_ERR_INVALID;
-  const int st = check_shape(B, H, N, d, 0, scale, dtype);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq, int B,
+              int H, int N, int d, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream,
+              int dtype) {
+  if (!q || !k || !v || !dO || !lse || !dq) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, causal, scale, dtype);
   if (st != FA_OK) return st;
-  if (!aligned(dq, 16)) return FA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dq, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_INVALID;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
-  if (dtype == FA_FP32) return FA_OK;
   const Workspace w = carve(workspace, B, H, N, d, dtype);
-  return hip_status(
-      fa::launch_dq_convert(w.dq_acc, dq, (size_t)B * H * N * d, scale, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == FA_FP32)
+    return hip_status(fa::launch_bwd_q_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                           static_cast<const float*>(v), static_cast<const float*>(dO), lse,
+                                           w.drow, static_cast<float*>(dq), B * H, N, d, causal != 0, scale, s));
+  if (dq_atomic_mode())
+    return hip_status(fa::launch_dq_convert(w.dq_acc, dq, (size_t)B * H * N * d, scale, s));
+  return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.lse2, w.drow, dq, B * H, N, d, causal != 0, scale, s));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
@@ -143,10 +161,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
   int r = fa_bwd_preprocess(o, dO, lse, B, H, N, d, workspace, workspace_bytes, stream, dtype);
   if (r != FA_OK) return r;
-  r = fa_bwd_main(q, k, v, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream,
-                  dtype);
+  r = fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype);
   if (r != FA_OK) return r;
-  return fa_bwd_finish(dq, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype);
+  return fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype);
 }
 
 const char* fa_strerror(int status) {

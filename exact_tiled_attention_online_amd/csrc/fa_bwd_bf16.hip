@@ -59,7 +59,7 @@ FA_DEV void dma4(const void* gsrc, void* lds_base) {
                                    (FA_LDS void*)lds_base, 4, 0, 0);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DQA>
 __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ DR,
@@ -80,15 +80,29 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   __shared__ __attribute__((aligned(256))) float sL1[BR];
   __shared__ __attribute__((aligned(256))) float sD0[BR];    // D
   __shared__ __attribute__((aligned(256))) float sD1[BR];
-  __shared__ __attribute__((aligned(1024))) char sS0[BC * BR * 2];  // dS, [key][query]
-  __shared__ __attribute__((aligned(1024))) char sS1[BC * BR * 2];
-  __shared__ __attribute__((aligned(1024))) char sK[BC * ROWB];     // K block / output staging
+  constexpr int SSB = DQA ? BC * BR * 2 : 16;   // dS tiles exist only with atomic dQ
+  constexpr int SKB = DQA ? BC * ROWB : 16;      // K block for the K^T operand of dQ
+  __shared__ __attribute__((aligned(1024))) char sS0[SSB];  // dS, [key][query]
+  __shared__ __attribute__((aligned(1024))) char sS1[SSB];
+  __shared__ __attribute__((aligned(1024))) char sK[SKB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, s16 = lane & 15;
+  // Work items.  Causal: item c of a head is the key-block pair
+  // (c, nkb-1-c), whose query walks together always cover the same number of
+  // blocks, so every workgroup does the same work; the first block is walked
+  // from the last query block down, the second from its first query block
+  // up, so at any moment the workgroups of a head sit on only two query
+  // blocks (their dQ atomics and Q/dO fetches meet in L2).  Workgroups are
+  // dealt round-robin to the 8 XCDs: the item index is XCD-major so that all
+  // items of a head share one XCD's L2.
+  const int nkb = (N + BC - 1) / BC;
+  const int P = CAUSAL ? (nkb + 1) / 2 : nkb;
+  const int W = P * BH;
   const int bid = blockIdx.x;
-  const int head = bid % BH;
-  const int kb = bid / BH;                 // ascending key block = descending causal work
+  const int item = (W % 8 == 0) ? (bid % 8) * (W / 8) + bid / 8 : bid;
+  const int head = item / P, c_item = item % P;
+  const int nparts = (CAUSAL && 2 * c_item + 1 != nkb) ? 2 : 1;
   const size_t hoff = (size_t)head * N * D;
   const bf16* Qh = Q + hoff;
   const bf16* Kh = K + hoff;
@@ -98,290 +112,317 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   const float* Dh = DR + (size_t)head * N;
   float* dQh = dQacc + hoff;
 
-  const int kv0 = kb * BC;
-  const int kvw = kv0 + 32 * wave;         // first key row of this wave
-  const int kvrow = kvw + l32;             // key row of this lane in the S accumulators
-  const int krow = 32 * wave + l32;        // the same row within the block
+  for (int part = 0; part < nparts; ++part) {
+    const int kb = CAUSAL ? (part == 0 ? c_item : nkb - 1 - c_item) : c_item;
+    const bool ascend = part == 1;
+    const int kv0 = kb * BC;
+    const int kvw = kv0 + 32 * wave;         // first key row of this wave
+    const int kvrow = kvw + l32;             // key row of this lane in the S accumulators
+    const int krow = 32 * wave + l32;        // the same row within the block
 
-  // ---- K block into LDS, then the register operands -----------------------
-  {
-    constexpr int KPT = BC * CH / 256;
+    // ---- K block into LDS (for K^T), then the register operands -------------
+    if constexpr (DQA) {
+      constexpr int KPT = BC * CH / 256;
 #pragma unroll
-    for (int p = 0; p < KPT; ++p) {
-      const int ci = p * 256 + tid;
-      const int row = ci / CH, ch = ci % CH;
-      const int kv = kv0 + row;
-      u32x4 x = u32x4{0, 0, 0, 0};
-      if (kv < N) x = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv * D + ch * 8);
-      *reinterpret_cast<u32x4*>(&sK[tile_off<ROWB>(row, ch)]) = x;
-    }
-  }
-  // K_w, V_w as B operands of S = Q K^T, dP = dO V^T: lane (n = key l32, h),
-  // registers d = 16*s + 8*h + r.
-  bf16x8 kf[KS], vf[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (kvrow < N) {
-      kf[s] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kvrow * D + 16 * s + 8 * h);
-      vf[s] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kvrow * D + 16 * s + 8 * h);
-    } else {
-      kf[s] = bf16x8{};
-      vf[s] = bf16x8{};
-    }
-  }
-  __syncthreads();
-  // K^T slice as the B operand of dQ = dS K: lane (n = d col 32*dsl + l32, h),
-  // registers = key rows 16*s + 8*h + r of the block.
-  const int dsl = (D == 128) ? wave : (wave & 1);
-  const int mt0 = (D == 128) ? 0 : (wave >> 1);
-  bf16x8 ktf[BC / 16];
-#pragma unroll
-  for (int s = 0; s < BC / 16; ++s)
-    ktf[s] = tr_operand<ROWB>(sK, 16 * s + 8 * h, 16 * s + 8 * h + 4, 32 * dsl + 16 * (g & 1), lane);
-
-  // ---- per-lane LDS address bases ------------------------------------------
-  // A operand (rows = query, registers = d) of S / dP, from a swizzled tile:
-  // offset(t, ks) = baseA[ks % 4] + 128*(ks / 4) + 32*t*ROWB.
-  const int swA = swz(l32);
-  int baseA[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) baseA[j] = l32 * ROWB + 16 * (h ^ (swA & 1)) + 32 * (j ^ (swA >> 1));
-  // transposed B operand (registers = query rows) of dV / dK, from the same
-  // tiles: offset(st, dt, hi) = baseC[dt % 2] + 64*(dt & ~1) + (16*st + 8*hi)*ROWB.
-  int baseC[2];
-  {
-    const int sw = 2 * (s16 >> 2) + h;
-    const int cc = 2 * (g & 1) + ((s16 & 3) >> 1);
-    const int L = (4 * h + (s16 >> 2)) * ROWB + 16 * (cc ^ (sw & 3)) + 8 * (s16 & 1);
-    const int b = sw >> 2;
-    baseC[0] = L + 64 * b;          // dt even: chunk group dt ^ b = dt + b
-    baseC[1] = L + 64 * (1 - b);    // dt odd:  chunk group dt ^ b = (dt - 1) + (1 - b)
-  }
-  // transposed A operand of dQ (registers = key rows) from the dS tile:
-  // offset(s, u, hi) = baseE[u][hi] + 2048*s.
-  int baseE[NQT][2];
-  {
-    const int a = s16 >> 2;
-    const int E = (4 * (g & 1) + (s16 & 3)) ^ (4 * (a & 1) + 2 * h);
-#pragma unroll
-    for (int u = 0; u < NQT; ++u)
-#pragma unroll
-      for (int hi = 0; hi < 2; ++hi) {
-        const int mt = mt0 + u;
-        baseE[u][hi] = (8 * h + a + 4 * hi) * 128 + 64 * (mt ^ (a >> 1)) + 8 * (E ^ hi);
+      for (int p = 0; p < KPT; ++p) {
+        const int ci = p * 256 + tid;
+        const int row = ci / CH, ch = ci % CH;
+        const int kv = kv0 + row;
+        u32x4 x = u32x4{0, 0, 0, 0};
+        if (kv < N) x = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv * D + ch * 8);
+        *reinterpret_cast<u32x4*>(&sK[tile_off<ROWB>(row, ch)]) = x;
       }
-  }
-
-  const int i_begin = CAUSAL ? (kv0 / BR) : 0;
-
-  // ---- direct global -> LDS fetch of one query block ------------------------
-  // wave w, load j fills LDS bytes [(w*LPW + j) KB, +1 KB): tile rows
-  // (w*LPW + j)*RPL + lane/CH, chunk position lane%CH (logical chunk
-  // position ^ swz(row)).  Rows past N read row N-1 (finite; masked later).
-  auto fetch = [&](int i, char* dQt, char* dGt, float* dL, float* dD) {
-    const int qb0 = i * BR;
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int blk = wave * LPW + j;
-      const int row = blk * RPL + lane / CH;
-      const int ch = (lane % CH) ^ swz(row);
-      const int q = min(qb0 + row, N - 1);
-      const size_t go = (size_t)q * D + ch * 8;
-      dma16(Qh + go, dQt + blk * 1024);
-      dma16(Gh + go, dGt + blk * 1024);
     }
-    if (wave == 0) dma4(Lh + min(qb0 + lane, N - 1), dL);
-    if (wave == 1) dma4(Dh + min(qb0 + lane, N - 1), dD);
-  };
-
-  f32x16 dk[DT], dv[DT];
+    // K_w, V_w as B operands of S = Q K^T, dP = dO V^T: lane (n = key l32, h),
+    // registers d = 16*s + 8*h + r.
+    bf16x8 kf[KS], vf[KS];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) {
-    dk[t] = f32x16{};
-    dv[t] = f32x16{};
-  }
-
-  // dQ_ip += dS_ip K over the whole key block, from the dS tile St: the wave
-  // takes d-slice dsl and query tiles mt0 .. mt0+NQT-1.  A = dS with the
-  // query across lanes, B = the K^T slice in registers.
-  auto dq_product = [&](int ip, const char* St) {
-    const int qp0 = ip * BR;
-#pragma unroll
-    for (int u = 0; u < NQT; ++u) {
-      const int mt = mt0 + u;
-      if (qp0 + 32 * mt >= N) continue;
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < BC / 16; ++s) {
-        const bf16x4 lo = lds_read_tr(St, baseE[u][0] + 2048 * s);
-        const bf16x4 hi = lds_read_tr(St, baseE[u][1] + 2048 * s);
-        acc = mfma32(cat(lo, hi), ktf[s], acc);
-      }
-      // acc[4*i4+jj] = dQ[query 32mt + 8*i4 + 4h + jj][d 32*dsl + l32]
-      const int qrow0 = qp0 + 32 * mt + 4 * h;
-      float* dst = dQh + (size_t)qrow0 * D + 32 * dsl + l32;
-      if (qp0 + 32 * mt + 32 <= N) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r]);
+    for (int s = 0; s < KS; ++s) {
+      if (kvrow < N) {
+        kf[s] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kvrow * D + 16 * s + 8 * h);
+        vf[s] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kvrow * D + 16 * s + 8 * h);
       } else {
-        const int nvalid = N - qrow0;   // register r is a valid row iff ql(r) < nvalid
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = 8 * (r >> 2) + (r & 3);
-          if (ql < nvalid) unsafeAtomicAdd(dst + ql * D, acc[r]);
-        }
+        kf[s] = bf16x8{};
+        vf[s] = bf16x8{};
       }
     }
-  };
+    __syncthreads();
+    // K^T slice as the B operand of dQ = dS K: lane (n = d col 32*dsl + l32, h),
+    // registers = key rows 16*s + 8*h + r of the block.
+    const int dsl = (D == 128) ? wave : (wave & 1);
+    const int mt0 = (D == 128) ? 0 : (wave >> 1);
+    bf16x8 ktf[DQA ? BC / 16 : 1];
+    if constexpr (DQA) {
+#pragma unroll
+      for (int s = 0; s < BC / 16; ++s)
+        ktf[s] = tr_operand<ROWB>(sK, 16 * s + 8 * h, 16 * s + 8 * h + 4, 32 * dsl + 16 * (g & 1), lane);
+    }
 
-  // one query block: products from buffer b, prefetch into buffer b^1
-  auto body = [&](auto bc, int i) {
-    constexpr int b = decltype(bc)::value;
-    char* Qt = b ? sQ1 : sQ0;
-    char* Gt = b ? sG1 : sG0;
-    const float* Lt = b ? sL1 : sL0;
-    const float* Dt = b ? sD1 : sD0;
-    char* St = b ? sS1 : sS0;
-    const int it = i - i_begin;
-    if (i + 1 < nqb) fetch(i + 1, b ? sQ0 : sQ1, b ? sG0 : sG1, b ? sL0 : sL1, b ? sD0 : sD1);
-    if (it > 0) dq_product(i - 1, b ? sS0 : sS1);
-    __builtin_amdgcn_sched_barrier(0);
-    const int qb0 = i * BR;
-    // this wave's keys are all later than all queries of the block: P^ = 0
-    const bool skip = (kvw >= N) || (CAUSAL && qb0 + BR - 1 < kvw);
-    if (!skip) {
-      const bool need_mask = (CAUSAL && qb0 < kvw + 31) || (qb0 + BR > N) || (kvw + 32 > N);
-      // P^T and dS^T as A operands (lane = key row); K-step st covers queries
-      // 16st..16st+15: registers 0..3 <- 16st+4h+jj, 4..7 <- 16st+8+4h+jj
-      bf16x8 pa[BR / 16], da[BR / 16];
+    // ---- per-lane LDS address bases ------------------------------------------
+    // A operand (rows = query, registers = d) of S / dP, from a swizzled tile:
+    // offset(t, ks) = baseA[ks % 4] + 128*(ks / 4) + 32*t*ROWB.
+    const int swA = swz(l32);
+    int baseA[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+    for (int j = 0; j < 4; ++j) baseA[j] = l32 * ROWB + 16 * (h ^ (swA & 1)) + 32 * (j ^ (swA >> 1));
+    // transposed B operand (registers = query rows) of dV / dK, from the same
+    // tiles: offset(st, dt, hi) = baseC[dt % 2] + 64*(dt & ~1) + (16*st + 8*hi)*ROWB.
+    int baseC[2];
+    {
+      const int sw = 2 * (s16 >> 2) + h;
+      const int cc = 2 * (g & 1) + ((s16 & 3) >> 1);
+      const int L = (4 * h + (s16 >> 2)) * ROWB + 16 * (cc ^ (sw & 3)) + 8 * (s16 & 1);
+      const int b = sw >> 2;
+      baseC[0] = L + 64 * b;          // dt even: chunk group dt ^ b = dt + b
+      baseC[1] = L + 64 * (1 - b);    // dt odd:  chunk group dt ^ b = (dt - 1) + (1 - b)
+    }
+    // transposed A operand of dQ (registers = key rows) from the dS tile:
+    // offset(s, u, hi) = baseE[u][hi] + 2048*s.
+    int baseE[NQT][2];
+    {
+      const int a = s16 >> 2;
+      const int E = (4 * (g & 1) + (s16 & 3)) ^ (4 * (a & 1) + 2 * h);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = baseA[ks & 3] + 128 * (ks >> 2) + 32 * t * ROWB;
-          s = mfma32(lds_read_b128(Qt, off), kf[ks], s);
-          dp = mfma32(lds_read_b128(Gt, off), vf[ks], dp);
+      for (int u = 0; u < NQT; ++u)
+#pragma unroll
+        for (int hi = 0; hi < 2; ++hi) {
+          const int mt = mt0 + u;
+          baseE[u][hi] = (8 * h + a + 4 * hi) * 128 + 64 * (mt ^ (a >> 1)) + 8 * (E ^ hi);
         }
-        // register r: query qb0 + 32t + 8*(r/4) + 4h + r%4, key kvrow
+    }
+
+    const int i_begin = CAUSAL ? (kv0 / BR) : 0;
+
+    // ---- direct global -> LDS fetch of one query block ------------------------
+    // wave w, load j fills LDS bytes [(w*LPW + j) KB, +1 KB): tile rows
+    // (w*LPW + j)*RPL + lane/CH, chunk position lane%CH (logical chunk
+    // position ^ swz(row)).  Rows past N read row N-1 (finite; masked later).
+    auto fetch = [&](int i, char* dQt, char* dGt, float* dL, float* dD) {
+      const int qb0 = i * BR;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int ql = 32 * t + 8 * i4 + 4 * h;
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(Lt + ql);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(Dt + ql);
+      for (int j = 0; j < LPW; ++j) {
+        const int blk = wave * LPW + j;
+        const int row = blk * RPL + lane / CH;
+        const int ch = (lane % CH) ^ swz(row);
+        const int q = min(qb0 + row, N - 1);
+        const size_t go = (size_t)q * D + ch * 8;
+        dma16(Qh + go, dQt + blk * 1024);
+        dma16(Gh + go, dGt + blk * 1024);
+      }
+      if (wave == 0) dma4(Lh + min(qb0 + lane, N - 1), dL);
+      if (wave == 1) dma4(Dh + min(qb0 + lane, N - 1), dD);
+    };
+
+    f32x16 dk[DT], dv[DT];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int r = 4 * i4 + jj;
-            float p = exp2_fast(fmaf(s[r], c, -L4[jj]));
-            if (need_mask) {
-              const int q = qb0 + ql + jj;
-              const bool dead = (q >= N) | (kvrow >= N) | (CAUSAL & (kvrow > q));
-              p = dead ? 0.f : p;
-            }
-            s[r] = p;
-            dp[r] = p * (dp[r] - D4[jj]);
+    for (int t = 0; t < DT; ++t) {
+      dk[t] = f32x16{};
+      dv[t] = f32x16{};
+    }
+
+    // dQ_ip += dS_ip K over the whole key block, from the dS tile St: the wave
+    // takes d-slice dsl and query tiles mt0 .. mt0+NQT-1.  A = dS with the
+    // query across lanes, B = the K^T slice in registers.
+    auto dq_product = [&](int ip, const char* St) {
+      if constexpr (!DQA) return;
+      const int qp0 = ip * BR;
+#pragma unroll
+      for (int u = 0; u < NQT; ++u) {
+        const int mt = mt0 + u;
+        if (qp0 + 32 * mt >= N) continue;
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < BC / 16; ++s) {
+          const bf16x4 lo = lds_read_tr(St, baseE[u][0] + 2048 * s);
+          const bf16x4 hi = lds_read_tr(St, baseE[u][1] + 2048 * s);
+          acc = mfma32(cat(lo, hi), ktf[s], acc);
+        }
+        // acc[4*i4+jj] = dQ[query 32mt + 8*i4 + 4h + jj][d 32*dsl + l32]
+        const int qrow0 = qp0 + 32 * mt + 4 * h;
+        float* dst = dQh + (size_t)qrow0 * D + 32 * dsl + l32;
+        if (qp0 + 32 * mt + 32 <= N) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(dst + (8 * (r >> 2) + (r & 3)) * D, acc[r]);
+        } else {
+          const int nvalid = N - qrow0;   // register r is a valid row iff ql(r) < nvalid
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ql = 8 * (r >> 2) + (r & 3);
+            if (ql < nvalid) unsafeAtomicAdd(dst + ql * D, acc[r]);
           }
         }
-        pa[2 * t] = pack8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
-        pa[2 * t + 1] = pack8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
-        da[2 * t] = pack8(dp[0], dp[1], dp[2], dp[3], dp[4], dp[5], dp[6], dp[7]);
-        da[2 * t + 1] = pack8(dp[8], dp[9], dp[10], dp[11], dp[12], dp[13], dp[14], dp[15]);
       }
+    };
+
+    // Step k handles query block nqb-1-k (first part) or i_begin+k (second).
+    const int nsteps = nqb - i_begin;
+    // one query block: products from buffer b, prefetch into buffer b^1
+    auto body = [&](auto bc, int k) {
+      constexpr int b = decltype(bc)::value;
+      const int i = ascend ? i_begin + k : nqb - 1 - k;
+      char* Qt = b ? sQ1 : sQ0;
+      char* Gt = b ? sG1 : sG0;
+      const float* Lt = b ? sL1 : sL0;
+      const float* Dt = b ? sD1 : sD0;
+      char* St = b ? sS1 : sS0;
+      const int dir = ascend ? 1 : -1;
+      if (k + 1 < nsteps) fetch(i + dir, b ? sQ0 : sQ1, b ? sG0 : sG1, b ? sL0 : sL1, b ? sD0 : sD1);
+      if (k > 0) dq_product(i - dir, b ? sS0 : sS1);
       __builtin_amdgcn_sched_barrier(0);
-      // dV += P^T dO, dK += dS^T Q; B = dO / Q rows through transposing reads
+      const int qb0 = i * BR;
+      // this wave's keys are all later than all queries of the block: P^ = 0
+      const bool skip = (kvw >= N) || (CAUSAL && qb0 + BR - 1 < kvw);
+      if (!skip) {
+        const bool need_mask = (CAUSAL && qb0 < kvw + 31) || (qb0 + BR > N) || (kvw + 32 > N);
+        // P^T and dS^T as A operands (lane = key row); K-step st covers queries
+        // 16st..16st+15: registers 0..3 <- 16st+4h+jj, 4..7 <- 16st+8+4h+jj
+        bf16x8 pa[BR / 16], da[BR / 16];
 #pragma unroll
-      for (int st = 0; st < BR / 16; ++st) {
+        for (int t = 0; t < 2; ++t) {
+          f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int o0 = baseC[dt & 1] + 64 * (dt & ~1) + 16 * st * ROWB;
-          const int o1 = o0 + 8 * ROWB;
-          dv[dt] = mfma32(pa[st], cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1)), dv[dt]);
-          dk[dt] = mfma32(da[st], cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1)), dk[dt]);
+          for (int ks = 0; ks < KS; ++ks) {
+            const int off = baseA[ks & 3] + 128 * (ks >> 2) + 32 * t * ROWB;
+            s = mfma32(lds_read_b128(Qt, off), kf[ks], s);
+            dp = mfma32(lds_read_b128(Gt, off), vf[ks], dp);
+          }
+          // register r: query qb0 + 32t + 8*(r/4) + 4h + r%4, key kvrow
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int ql = 32 * t + 8 * i4 + 4 * h;
+            const f32x4 L4 = *reinterpret_cast<const f32x4*>(Lt + ql);
+            const f32x4 D4 = *reinterpret_cast<const f32x4*>(Dt + ql);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int r = 4 * i4 + jj;
+              float p = exp2_fast(fmaf(s[r], c, -L4[jj]));
+              if (need_mask) {
+                const int q = qb0 + ql + jj;
+                const bool dead = (q >= N) | (kvrow >= N) | (CAUSAL & (kvrow > q));
+                p = dead ? 0.f : p;
+              }
+              s[r] = p;
+              dp[r] = p * (dp[r] - D4[jj]);
+            }
+          }
+          pa[2 * t] = pack8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
+          pa[2 * t + 1] = pack8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
+          da[2 * t] = pack8(dp[0], dp[1], dp[2], dp[3], dp[4], dp[5], dp[6], dp[7]);
+          da[2 * t + 1] = pack8(dp[8], dp[9], dp[10], dp[11], dp[12], dp[13], dp[14], dp[15]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dV += P^T dO, dK += dS^T Q; B = dO / Q rows through transposing reads
+#pragma unroll
+        for (int st = 0; st < BR / 16; ++st) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int o0 = baseC[dt & 1] + 64 * (dt & ~1) + 16 * st * ROWB;
+            const int o1 = o0 + 8 * ROWB;
+            dv[dt] = mfma32(pa[st], cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1)), dv[dt]);
+            dk[dt] = mfma32(da[st], cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1)), dk[dt]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dS (bf16) to LDS, [key][query]
+        if constexpr (DQA) {
+#pragma unroll
+        for (int st = 0; st < BR / 16; ++st) {
+          const bf16x4 lo = __builtin_shufflevector(da[st], da[st], 0, 1, 2, 3);
+          const bf16x4 hi = __builtin_shufflevector(da[st], da[st], 4, 5, 6, 7);
+          *reinterpret_cast<bf16x4*>(&St[ds_off(krow, 16 * st + 4 * h)]) = lo;
+          *reinterpret_cast<bf16x4*>(&St[ds_off(krow, 16 * st + 8 + 4 * h)]) = hi;
+        }
+        }
+      } else if constexpr (DQA) {
+#pragma unroll
+        for (int st = 0; st < BR / 16; ++st) {
+          *reinterpret_cast<u32x2*>(&St[ds_off(krow, 16 * st + 4 * h)]) = u32x2{0, 0};
+          *reinterpret_cast<u32x2*>(&St[ds_off(krow, 16 * st + 8 + 4 * h)]) = u32x2{0, 0};
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // dS (bf16) to LDS, [key][query]
-#pragma unroll
-      for (int st = 0; st < BR / 16; ++st) {
-        const bf16x4 lo = __builtin_shufflevector(da[st], da[st], 0, 1, 2, 3);
-        const bf16x4 hi = __builtin_shufflevector(da[st], da[st], 4, 5, 6, 7);
-        *reinterpret_cast<bf16x4*>(&St[ds_off(krow, 16 * st + 4 * h)]) = lo;
-        *reinterpret_cast<bf16x4*>(&St[ds_off(krow, 16 * st + 8 + 4 * h)]) = hi;
-      }
-    } else {
-#pragma unroll
-      for (int st = 0; st < BR / 16; ++st) {
-        *reinterpret_cast<u32x2*>(&St[ds_off(krow, 16 * st + 4 * h)]) = u32x2{0, 0};
-        *reinterpret_cast<u32x2*>(&St[ds_off(krow, 16 * st + 8 + 4 * h)]) = u32x2{0, 0};
-      }
-    }
-    __syncthreads();
-  };
+      __syncthreads();
+    };
 
-  if (i_begin < nqb) {
-    fetch(i_begin, sQ0, sG0, sL0, sD0);
-    __syncthreads();
-    int i = i_begin;
-    while (true) {
-      body(IC<0>{}, i);
-      if (++i >= nqb) break;
-      body(IC<1>{}, i);
-      if (++i >= nqb) break;
-    }
-    if (((nqb - 1 - i_begin) & 1) == 0)
-      dq_product(nqb - 1, sS0);
-    else
-      dq_product(nqb - 1, sS1);
-  }
-
-  // ---- write-back: dK = scale * acc, dV = acc, staged through LDS ----------
-  // accumulator r of tile dt: key 32*wave + 8*(r/4) + 4h + r%4, d 32*dt + l32
-  bf16* stK = reinterpret_cast<bf16*>(sK);   // [128][D] plain row-major staging
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * wave + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float x = pass == 0 ? dk[dt][r] * scale : dv[dt][r];
-        stK[row * D + 32 * dt + l32] = (bf16)x;
+    if (nsteps > 0) {
+      fetch(ascend ? i_begin : nqb - 1, sQ0, sG0, sL0, sD0);
+      __syncthreads();
+      int k = 0;
+      while (true) {
+        body(IC<0>{}, k);
+        if (++k >= nsteps) break;
+        body(IC<1>{}, k);
+        if (++k >= nsteps) break;
       }
-    __syncthreads();
-    bf16* dst = (pass == 0 ? dK : dV) + hoff;
-    constexpr int OPT = BC * CH / 256;
-#pragma unroll
-    for (int p = 0; p < OPT; ++p) {
-      const int ci = p * 256 + tid;
-      const int row = ci / CH, ch = ci % CH;
-      if (kv0 + row < N)
-        *reinterpret_cast<u32x4*>(dst + (size_t)(kv0 + row) * D + ch * 8) =
-            *reinterpret_cast<const u32x4*>(&stK[row * D + ch * 8]);
+      const int i_last = ascend ? nqb - 1 : i_begin;
+      if (((nsteps - 1) & 1) == 0)
+        dq_product(i_last, sS0);
+      else
+        dq_product(i_last, sS1);
     }
-    __syncthreads();
+
+    // ---- write-back: dK = scale * acc, dV = acc ------------------------------
+    // Each wave stages its own 32 rows through a private 8 KB LDS region (the
+    // query buffers, idle after the walk) to turn the accumulator layout into
+    // 16-byte row stores.  Accumulator r of tile dt: key 32*wave + 8*(r/4) +
+    // 4h + r%4, d 32*dt + l32.
+    {
+      char* region = (wave < 2 ? sQ0 : sG0) + (wave & 1) * (32 * ROWB);
+      bf16* stg = reinterpret_cast<bf16*>(region);   // [32][D] plain row-major
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+            const float x = pass == 0 ? dk[dt][r] * scale : dv[dt][r];
+            stg[row * D + 32 * dt + l32] = (bf16)x;
+          }
+        bf16* dst = (pass == 0 ? dK : dV) + hoff;
+        constexpr int OPW = 32 * CH / 64;   // 16-byte stores per lane
+#pragma unroll
+        for (int p = 0; p < OPW; ++p) {
+          const int ci = p * 64 + lane;
+          const int row = ci / CH, ch = ci % CH;
+          if (kvw + row < N)
+            *reinterpret_cast<u32x4*>(dst + (size_t)(kvw + row) * D + ch * 8) =
+                *reinterpret_cast<const u32x4*>(&stg[row * D + ch * 8]);
+        }
+      }
+      __syncthreads();   // the next part refills the query buffers
+    }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DQA>
 static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v, const void* dO,
                                     const float* lse2, const float* drow, float* dq_acc, void* dk,
                                     void* dv, int BH, int N, float scale, hipStream_t stream) {
   const int nkb = (N + 127) / 128, nqb = (N + 63) / 64;
-  const dim3 grid((unsigned)(nkb * BH)), block(256);
-  hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q,
+  const int items = CAUSAL ? (nkb + 1) / 2 : nkb;
+  const dim3 grid((unsigned)(items * BH)), block(256);
+  hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, DQA>), grid, block, 0, stream, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, drow, dq_acc, (bf16*)dk,
                      (bf16*)dv, BH, N, nqb, scale, scale * kLog2e);
   return hipGetLastError();
 }
 
+template <bool DQA>
+static hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void* dO,
+                                const float* lse2, const float* drow, float* dq_acc, void* dk, void* dv,
+                                int BH, int N, int d, bool causal, float scale, hipStream_t stream) {
+  if (d == 128)
+    return causal ? launch_bwd_bf16_t<128, true, DQA>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream)
+                  : launch_bwd_bf16_t<128, false, DQA>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream);
+  return causal ? launch_bwd_bf16_t<64, true, DQA>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream)
+                : launch_bwd_bf16_t<64, false, DQA>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream);
+}
+
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dO,
                            const float* lse2, const float* drow, float* dq_acc, void* dk, void* dv,
-                           int BH, int N, int d, bool causal, float scale, hipStream_t stream) {
-  if (d == 128)
-    return causal ? launch_bwd_bf16_t<128, true>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream)
-                  : launch_bwd_bf16_t<128, false>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream);
-  return causal ? launch_bwd_bf16_t<64, true>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream)
-                : launch_bwd_bf16_t<64, false>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream);
+                           int BH, int N, int d, bool causal, float scale, bool dq_atomic, hipStream_t stream) {
+  return dq_atomic ? launch_bwd_kv<true>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, d, causal, scale, stream)
+                   : launch_bwd_kv<false>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, d, causal, scale, stream);
 }
 
 }  // namespace fa

@@ -1,0 +1,200 @@
+// fa_bwd_dq.hip -- query-block-outer dQ kernel, bf16 in/out, fp32 accumulation.
+//
+// dQ_i = scale * sum_j dS_ij K_j (page "flash-attention-backpropagation"
+// (aiqz.cc), section QKV梯度), computed without atomics: one workgroup
+// (4 waves) owns BR = 128 query rows of one (batch, head), each wave 32 of
+// them, with the wave's Q and dO rows in registers and dQ accumulated in
+// registers, and walks the key/value tiles of BC = 64 rows (double-buffered
+// through LDS).  Per tile and wave:
+//   S^T  = K_j Q_w^T           MFMA, A = K rows (LDS), B = Q_w (registers)
+//   dP^T = V_j dO_w^T          MFMA, A = V rows (LDS), B = dO_w (registers)
+//   P^   = 2^(c*S - LSE2)      recompute from the ledger (section 数值稳定);
+//                              the lane holds one query row, so LSE and D
+//                              are per-lane scalars
+//   dS   = P^ o (dP - D)       (section Softmax梯度)
+//   dQ^T += K_j^T dS^T         MFMA, A = K^T through transposing LDS reads,
+//                              B = dS^T straight from the accumulators.
+// It repeats the S and dP products of the key/value-outer kernel instead of
+// exchanging dS through fp32 atomics.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ DR,
+    bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c) {
+  constexpr int BR = 128, BC = 64;
+  constexpr int ROWB = D * 2;        // bytes per row
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int KS = D / 16;         // K-steps of the S and dP products
+  constexpr int DT = D / 32;         // 32-row tiles of dQ^T
+  constexpr int TILEB = BC * ROWB;   // bytes of one K or V tile
+  constexpr int LPT = BC * CH / 256; // 16-byte loads per thread per tensor
+
+  __shared__ __attribute__((aligned(16))) char smem[2][2][TILEB];  // [buffer][K, V]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const TileBases<D * 2> tb(lane);
+  const int bid = blockIdx.x;
+  const int head = bid % BH;
+  // causal: the longest query blocks are dispatched first
+  const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
+  const size_t hoff = (size_t)head * N * D;
+  const bf16* Qh = Q + hoff;
+  const bf16* Kh = K + hoff;
+  const bf16* Vh = V + hoff;
+  const bf16* Gh = dO + hoff;
+
+  const int q0 = qb * BR + wave * 32;   // first query row of this wave
+  const int qrow = q0 + l32;            // the query row this lane's statistics belong to
+
+  // Q and dO rows as B operands: lane (n = l32, half h) holds d = 16*s + 8*h + r
+  bf16x8 qf[KS], gf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (qrow < N) {
+      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + 16 * s + 8 * h);
+      gf[s] = *reinterpret_cast<const bf16x8*>(Gh + (size_t)qrow * D + 16 * s + 8 * h);
+    } else {
+      qf[s] = bf16x8{};
+      gf[s] = bf16x8{};
+    }
+  }
+  const float lse2 = qrow < N ? LSE2[(size_t)head * N + qrow] : 0.f;
+  const float drow = qrow < N ? DR[(size_t)head * N + qrow] : 0.f;
+
+  const int kv_end = CAUSAL ? min(N, qb * BR + BR) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  int wave_tiles = 0;
+  if (q0 < N) {
+    const int wkv_end = CAUSAL ? min(N, q0 + 32) : N;
+    wave_tiles = (wkv_end + BC - 1) / BC;
+  }
+
+  u32x4 stK[LPT], stV[LPT];
+  auto gload = [&](int j) {
+#pragma unroll
+    for (int p = 0; p < LPT; ++p) {
+      const int ci = p * 256 + tid;
+      const int row = ci / CH, ch = ci % CH;
+      const int kv = j * BC + row;
+      if (kv < N) {
+        stK[p] = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv * D + ch * 8);
+        stV[p] = *reinterpret_cast<const u32x4*>(Vh + (size_t)kv * D + ch * 8);
+      } else {
+        stK[p] = u32x4{0, 0, 0, 0};
+        stV[p] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < LPT; ++p) {
+      const int ci = p * 256 + tid;
+      const int row = ci / CH, ch = ci % CH;
+      const int off = tile_off<ROWB>(row, ch);
+      *reinterpret_cast<u32x4*>(&smem[buf][0][off]) = stK[p];
+      *reinterpret_cast<u32x4*>(&smem[buf][1][off]) = stV[p];
+    }
+  };
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
+
+  gload(0);
+  swrite(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) gload(j + 1);
+    if (j < wave_tiles) {
+      const char* Kt = smem[buf][0];
+      const char* Vt = smem[buf][1];
+      const int kvb = j * BC;
+      const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0) || (qrow >= N);
+      // the tile's two 32-key halves one after the other (fewer live registers)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int off = tb.nat_off(mt, ks);
+          s = mfma32(lds_read_b128(Kt, off), qf[ks], s);
+          dp = mfma32(lds_read_b128(Vt, off), gf[ks], dp);
+        }
+        // register r: key kvb + 32*mt + 8*(r/4) + 4*h + r%4, query qrow
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = exp2_fast(fmaf(s[r], c, -lse2));
+          if (need_mask) {
+            const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+            const bool dead = (kv >= N) | (qrow >= N) | (CAUSAL & (kv > qrow));
+            p = dead ? 0.f : p;
+          }
+          dp[r] = p * (dp[r] - drow);
+        }
+        // dS^T as B operand; K-step st = 2*mt + half covers keys 16*st ..
+        // 16*st+15 of the tile: registers 0..3 <- keys 16st+4h+jj, 4..7 <-
+        // keys 16st+8+4h+jj
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int i0 = 2 * half;
+          const bf16x8 db = pack8(dp[4 * i0 + 0], dp[4 * i0 + 1], dp[4 * i0 + 2], dp[4 * i0 + 3],
+                                  dp[4 * i0 + 4], dp[4 * i0 + 5], dp[4 * i0 + 6], dp[4 * i0 + 7]);
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            const int st = 2 * mt + half;
+            const bf16x8 a = cat(lds_read_tr(Kt, tb.tr_off(st, t, 0)), lds_read_tr(Kt, tb.tr_off(st, t, 1)));
+            acc[t] = mfma32(a, db, acc[t]);
+          }
+        }
+      }
+    }
+    if (j + 1 < ntiles) swrite((j + 1) & 1);
+    __syncthreads();
+  }
+
+  if (qrow >= N) return;
+  // acc[t][4*i+jj] = dQ^T[d = 32t + 8i + 4h + jj][query qrow]
+  bf16* row = dQ + hoff + (size_t)qrow * D;
+#pragma unroll
+  for (int t = 0; t < DT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x4 v;
+      v[0] = (bf16)(acc[t][4 * i + 0] * scale);
+      v[1] = (bf16)(acc[t][4 * i + 1] * scale);
+      v[2] = (bf16)(acc[t][4 * i + 2] * scale);
+      v[3] = (bf16)(acc[t][4 * i + 3] * scale);
+      *reinterpret_cast<bf16x4*>(row + 32 * t + 8 * i + 4 * h) = v;
+    }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_dq_t(const void* q, const void* k, const void* v, const void* dO,
+                                  const float* lse2, const float* drow, void* dq, int BH, int N, float scale,
+                                  hipStream_t stream) {
+  const int nqb = (N + 127) / 128;
+  const dim3 grid((unsigned)(nqb * BH)), block(256);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
+                     (const bf16*)v, (const bf16*)dO, lse2, drow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                         const float* drow, void* dq, int BH, int N, int d, bool causal, float scale,
+                         hipStream_t stream) {
+  if (d == 128)
+    return causal ? launch_bwd_dq_t<128, true>(q, k, v, dO, lse2, drow, dq, BH, N, scale, stream)
+                  : launch_bwd_dq_t<128, false>(q, k, v, dO, lse2, drow, dq, BH, N, scale, stream);
+  return causal ? launch_bwd_dq_t<64, true>(q, k, v, dO, lse2, drow, dq, BH, N, scale, stream)
+                : launch_bwd_dq_t<64, false>(q, k, v, dO, lse2, drow, dq, BH, N, scale, stream);
+}
+
+}  // namespace fa

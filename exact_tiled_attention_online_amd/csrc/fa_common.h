@@ -107,6 +107,39 @@ FA_DEV bf16x8 tr_operand(const char* tile, int k0, int k1, int n0, int lane) {
   return cat(lo, hi);
 }
 
+// Per-lane bases that turn every operand access of a swizzled tile into
+// base + compile-time offset (so only a handful of address registers stay
+// live).  Derivation: with row = R + r_lane (R a multiple of 8) the swizzle
+// swz(row) depends on the lane only, and the chunk index splits into a
+// compile-time part and a lane part; the XOR then acts on the lane part
+// except for one chunk bit, which two (or four) bases absorb.
+template <int ROWB>
+struct TileBases {
+  // natural operand (lane = row 32*t + l32, registers = 8 elements of chunk
+  // 2*ks + h):  off(t, ks) = nat[ks % 4] + 128*(ks / 4) + 32*t*ROWB
+  int nat[4];
+  // transposed operand (lane = column, registers = rows k0..k0+3 and
+  // k0+8..k0+11 with k0 = 16*st + 4*h), column group 32*t + 16*(g%2):
+  // off(st, t, hi) = tr[t % 2] + 64*(t & ~1) + (16*st + 8*hi)*ROWB
+  int tr[2];
+  FA_DEV TileBases(int lane) {
+    const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, s16 = lane & 15;
+    const int swA = swz(l32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nat[j] = l32 * ROWB + 16 * (h ^ (swA & 1)) + 32 * (j ^ (swA >> 1));
+    const int sw = 2 * (s16 >> 2) + h;
+    const int cc = 2 * (g & 1) + ((s16 & 3) >> 1);
+    const int L = (4 * h + (s16 >> 2)) * ROWB + 16 * (cc ^ (sw & 3)) + 8 * (s16 & 1);
+    const int b = sw >> 2;
+    tr[0] = L + 64 * b;          // t even: chunk group t ^ b = t + b
+    tr[1] = L + 64 * (1 - b);    // t odd:  chunk group t ^ b = (t - 1) + (1 - b)
+  }
+  FA_DEV int nat_off(int t, int ks) const { return nat[ks & 3] + 128 * (ks >> 2) + 32 * t * ROWB; }
+  FA_DEV int tr_off(int st, int t, int hi) const {
+    return tr[t & 1] + 64 * (t & ~1) + (16 * st + 8 * hi) * ROWB;
+  }
+};
+
 FA_DEV bf16x8 pack8(float a0, float a1, float a2, float a3, float b0, float b1, float b2, float b3) {
   bf16x8 r;
   r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;

@@ -216,16 +216,20 @@ static hipError_t fwd_f32_t(const float* q, const float* k, const float* v, floa
 }
 
 template <int D, bool CAUSAL>
-static hipError_t bwd_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
-                            const float* drow, float* dq, float* dk, float* dv, int BH, int N, float scale,
-                            hipStream_t stream) {
+static hipError_t bwd_kv_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
+                               const float* drow, float* dk, float* dv, int BH, int N, float scale,
+                               hipStream_t stream) {
   const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
-  hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, drow, dk, dv,
-                     N, scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, drow, dq, N,
+  hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, drow, dk, dv, N,
                      scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t bwd_q_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
+                              const float* drow, float* dq, int BH, int N, float scale, hipStream_t stream) {
+  const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
+  hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, drow, dq, N, scale);
   return hipGetLastError();
 }
 
@@ -238,14 +242,24 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                 : fwd_f32_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);
 }
 
-hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dO, const float* lse,
-                          const float* drow, float* dq, float* dk, float* dv, int BH, int N, int d, bool causal,
-                          float scale, hipStream_t stream) {
+hipError_t launch_bwd_kv_f32(const float* q, const float* k, const float* v, const float* dO, const float* lse,
+                             const float* drow, float* dk, float* dv, int BH, int N, int d, bool causal,
+                             float scale, hipStream_t stream) {
   if (d == 128)
-    return causal ? bwd_f32_t<128, true>(q, k, v, dO, lse, drow, dq, dk, dv, BH, N, scale, stream)
-                  : bwd_f32_t<128, false>(q, k, v, dO, lse, drow, dq, dk, dv, BH, N, scale, stream);
-  return causal ? bwd_f32_t<64, true>(q, k, v, dO, lse, drow, dq, dk, dv, BH, N, scale, stream)
-                : bwd_f32_t<64, false>(q, k, v, dO, lse, drow, dq, dk, dv, BH, N, scale, stream);
+    return causal ? bwd_kv_f32_t<128, true>(q, k, v, dO, lse, drow, dk, dv, BH, N, scale, stream)
+                  : bwd_kv_f32_t<128, false>(q, k, v, dO, lse, drow, dk, dv, BH, N, scale, stream);
+  return causal ? bwd_kv_f32_t<64, true>(q, k, v, dO, lse, drow, dk, dv, BH, N, scale, stream)
+                : bwd_kv_f32_t<64, false>(q, k, v, dO, lse, drow, dk, dv, BH, N, scale, stream);
+}
+
+hipError_t launch_bwd_q_f32(const float* q, const float* k, const float* v, const float* dO, const float* lse,
+                            const float* drow, float* dq, int BH, int N, int d, bool causal, float scale,
+                            hipStream_t stream) {
+  if (d == 128)
+    return causal ? bwd_q_f32_t<128, true>(q, k, v, dO, lse, drow, dq, BH, N, scale, stream)
+                  : bwd_q_f32_t<128, false>(q, k, v, dO, lse, drow, dq, BH, N, scale, stream);
+  return causal ? bwd_q_f32_t<64, true>(q, k, v, dO, lse, drow, dq, BH, N, scale, stream)
+                : bwd_q_f32_t<64, false>(q, k, v, dO, lse, drow, dq, BH, N, scale, stream);
 }
 
 }  // namespace fa

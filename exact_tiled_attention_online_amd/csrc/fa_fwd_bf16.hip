@@ -39,7 +39,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) char smem[2][2][TILEB];  // [buffer][K, V]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, h = lane >> 5, g = lane >> 4;
+  const int l32 = lane & 31, h = lane >> 5;
+  const TileBases<D * 2> tb(lane);
   const int bid = blockIdx.x;
   const int head = bid % BH;
   // causal: the longest query blocks are dispatched first
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 a = lds_read_b128(Kt, tile_off<ROWB>(mt * 32 + l32, 2 * ks + h));
+          const bf16x8 a = lds_read_b128(Kt, tb.nat_off(mt, ks));
           s[mt] = mfma32(a, qf[ks], s[mt]);
         }
       }
@@ -168,10 +169,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         const int mt = st >> 1, i0 = 2 * (st & 1);
         const bf16x8 pb = pack8(s[mt][4 * i0 + 0], s[mt][4 * i0 + 1], s[mt][4 * i0 + 2], s[mt][4 * i0 + 3],
                                 s[mt][4 * i0 + 4], s[mt][4 * i0 + 5], s[mt][4 * i0 + 6], s[mt][4 * i0 + 7]);
-        const int k0 = 16 * st + 4 * h;
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-          const bf16x8 a = tr_operand<ROWB>(Vt, k0, k0 + 8, 32 * t + 16 * (g & 1), lane);
+          const bf16x8 a = cat(lds_read_tr(Vt, tb.tr_off(st, t, 0)), lds_read_tr(Vt, tb.tr_off(st, t, 1)));
           oacc[t] = mfma32(a, pb, oacc[t]);
         }
       }

@@ -16,11 +16,17 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* drow, float* lse2,
                           float* dq_acc, int BH, int N, int d, bool fp32, hipStream_t stream);
 
-// bf16 key/value-block-outer backward: dK, dV written, dQ accumulated (fp32,
-// unscaled dS K) into dq_acc with atomics.
+// bf16 key/value-block-outer backward: dK, dV written; with dq_atomic, dQ is
+// also accumulated (fp32, unscaled dS K) into dq_acc with atomics.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dO,
                            const float* lse2, const float* drow, float* dq_acc, void* dk, void* dv,
-                           int BH, int N, int d, bool causal, float scale, hipStream_t stream);
+                           int BH, int N, int d, bool causal, float scale, bool dq_atomic,
+                           hipStream_t stream);
+
+// bf16 query-block-outer dQ kernel: dQ = bf16(scale * dS K), no atomics.
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
+                         const float* drow, void* dq, int BH, int N, int d, bool causal, float scale,
+                         hipStream_t stream);
 
 // dQ = bf16(scale * dq_acc).
 hipError_t launch_dq_convert(const float* dq_acc, void* dq, size_t n, float scale, hipStream_t stream);
@@ -28,8 +34,11 @@ hipError_t launch_dq_convert(const float* dq_acc, void* dq, size_t n, float scal
 // fp32 path (plain VALU kernels, exact fp32 arithmetic).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                           int BH, int N, int d, bool causal, float scale, hipStream_t stream);
-hipError_t launch_bwd_f32(const float* q, const float* k, const float* v, const float* dO,
-                          const float* lse, const float* drow, float* dq, float* dk, float* dv,
-                          int BH, int N, int d, bool causal, float scale, hipStream_t stream);
+hipError_t launch_bwd_kv_f32(const float* q, const float* k, const float* v, const float* dO,
+                             const float* lse, const float* drow, float* dk, float* dv, int BH, int N,
+                             int d, bool causal, float scale, hipStream_t stream);
+hipError_t launch_bwd_q_f32(const float* q, const float* k, const float* v, const float* dO,
+                            const float* lse, const float* drow, float* dq, int BH, int N, int d,
+                            bool causal, float scale, hipStream_t stream);
 
 }  // namespace fa

@@ -69,8 +69,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace fa_bwd needs for this shape: the fp32 row term
- * D [B,H,N], a staged copy of the ledger [B,H,N] and, for bf16, an fp32 dQ
- * accumulator [B,H,N,d].  The caller allocates it (any 256-byte-aligned
+ * D [B,H,N], the ledger in base 2 [B,H,N] and, for bf16, room for an fp32
+ * dQ accumulator [B,H,N,d] (used only with FA_DQ_MODE=atomic).  The caller allocates it (any 256-byte-aligned
  * device buffer); its contents on entry do not matter.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
@@ -81,8 +81,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
  * for the ledger of that forward: page "flash-attention-backpropagation",
  * section 数值稳定).  Writes dq, dk, dv ([B,H,N,d], dtype).  Uses `workspace`
  * (at least fa_bwd_workspace_bytes bytes) as scratch; it is fully overwritten.
- * Kernels, in stream order: D = rowsum(dO o O) (which also clears the dQ
- * accumulator), the key/value-block-outer gradient kernel, the dQ conversion.
+ * Kernels, in stream order: D = rowsum(dO o O), the key/value-block-outer
+ * kernel (dK, dV), the query-block-outer kernel (dQ).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dO, const float* lse, void* dq, void* dk, void* dv,
@@ -95,21 +95,26 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * all three with the same arguments is exactly fa_bwd.
  *
  * fa_bwd_preprocess: D_i = sum_c dO_ic * O_ic (page
- *   "flash-attention-backpropagation", section Softmax梯度), the ledger in
- *   base 2, and the clear of the dQ accumulator; writes only the workspace.
- * fa_bwd_main: the key/value-block-outer gradient kernel (section QKV梯度):
- *   writes dk, dv; for bf16 accumulates dQ into the workspace, for fp32 also
- *   runs the query-row-outer dQ kernel and writes dq.
- * fa_bwd_finish: bf16 only, dq = bf16(scale * accumulator); no-op for fp32.
- * Argument meaning, checks and errors are those of fa_bwd.
+ *   "flash-attention-backpropagation", section Softmax梯度) and the ledger in
+ *   base 2, into the workspace.
+ * fa_bwd_dkdv: the key/value-block-outer kernel (section QKV梯度): recomputes
+ *   P^ and dS per pair of blocks and writes dk and dv.
+ * fa_bwd_dq: the query-block-outer kernel: recomputes S, P^, dP, dS per pair
+ *   of blocks and writes dq (no atomics).
+ * Argument meaning, checks and errors are those of fa_bwd.  With the
+ * environment variable FA_DQ_MODE=atomic (bf16 only) the dQ products run
+ * inside fa_bwd_dkdv instead, as fp32 atomic adds into the workspace, and
+ * fa_bwd_dq converts that accumulator; the default is the query-outer kernel,
+ * which measured faster.
  */
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
                       void* workspace, size_t workspace_bytes, void* stream, int dtype);
-int fa_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
                 void* workspace, size_t workspace_bytes, void* stream, int dtype);
-int fa_bwd_finish(void* dq, int B, int H, int N, int d, float scale, void* workspace,
-                  size_t workspace_bytes, void* stream, int dtype);
+int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+              void* dq, int B, int H, int N, int d, int causal, float scale,
+              void* workspace, size_t workspace_bytes, void* stream, int dtype);
 
 /* Static, human-readable text for a status code. */
 const char* fa_strerror(int status);
