@@ -58,6 +58,54 @@ def traffic_from_counters(kernel):
     return c.get("hbm_bytes_per_launch")
 
 
+def _read_counter_csv(path):
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_counters(fetch_csv, write_csv, copy_mib, out_json):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE, with --copy-probe-mib) into HBM bytes per launch per kernel.
+
+    The probe copy converts copy_mib MiB of bf16 into fp32, so it reads
+    copy_mib MiB and writes 2*copy_mib MiB; each counter is scaled by the
+    factor that makes the probe's reading exactly that."""
+    fetch, write = _read_counter_csv(fetch_csv), _read_counter_csv(write_csv)
+    known_read_kib, known_write_kib = copy_mib * 1024.0, 2 * copy_mib * 1024.0
+
+    def mean(d, key):
+        v = d.get(key, [])
+        return sum(v) / len(v) if v else None
+
+    copy = [k for k in fetch if "copy" in k.lower() and "elementwise" in k.lower()]
+    # the probe copy is the largest copy kernel in the run
+    ck = max(copy, key=lambda k: max(fetch[k]["FETCH_SIZE"]))
+    f_fetch = known_read_kib / max(fetch[ck]["FETCH_SIZE"])
+    f_write = known_write_kib / max(write[ck]["WRITE_SIZE"])
+    out = {"copy_probe": {"kernel": ck, "mib": copy_mib, "fetch_factor": round(f_fetch, 4),
+                          "write_factor": round(f_write, 4)}}
+    rows = []
+    for short, srcs in KERNEL_SOURCES.items():
+        key = next((k for k in fetch if short in k), None)
+        if key is None or key not in write:
+            continue
+        fk, wkib = mean(fetch[key], "FETCH_SIZE"), mean(write[key], "WRITE_SIZE")
+        hbm = (fk * f_fetch + wkib * f_write) * 1024.0
+        out[short] = {"fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wkib, 1),
+                      "hbm_bytes_per_launch": int(hbm), "source_digest": source_digest(srcs)}
+        rows.append(f"| {short} | {fk:.0f} | {wkib:.0f} | {hbm / 1e6:.1f} |")
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(f"copy probe {ck}: fetch factor {f_fetch:.4f}, write factor {f_write:.4f}")
+    print("| kernel | FETCH_SIZE KiB/launch | WRITE_SIZE KiB/launch | HBM MB/launch (scaled) |")
+    print("|---|---|---|---|")
+    print("\n".join(rows))
+
+
 def cpu_baseline(w, x, budget_s=12.0):
     """Time the fp64 oracle on whole heads of the same workload until the
     budget is spent (at least one head); credited-FLOP rate in TFLOP/s."""
@@ -92,7 +140,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4", help="c1..c5 (default c4, the headline shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB "
+                         "(the calibration kernel for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
+                    help="write profiles/counters_c4.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        fcsv, wcsv, mib = args.summarize_counters
+        summarize_counters(fcsv, wcsv, float(mib), COUNTERS)
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(heads are independent, see the sharding note in the design document)", file=sys.stderr)
@@ -151,6 +208,14 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty(n, dtype=torch.float32, device=dev)
+        dst.copy_(src)          # reads copy_probe_mib MiB, writes twice that
+        torch.cuda.synchronize()
+        del src, dst
 
     def avg(a, b):
         return sum(e[a].elapsed_time(e[b]) for e in events) / len(events)

@@ -29,8 +29,6 @@
 // loop body is instantiated per buffer so that every LDS buffer is a distinct
 // object (the compiler then knows the prefetch cannot alias the reads).
 // LDS addresses are a few per-lane bases plus compile-time offsets.
-#include <type_traits>
-
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -43,20 +41,6 @@ namespace fa {
 FA_DEV int ds_off(int row, int col) {
   const int slot = (col >> 2) ^ (((row & 3) << 2) | ((row >> 2) & 3));
   return row * 128 + (slot << 3) + ((col & 3) << 1);
-}
-
-template <int B>
-using IC = std::integral_constant<int, B>;
-
-// wave-wide direct fetch: lane l's 16 (or 4) bytes land at lds_base + 16*l
-// (or 4*l); lds_base must be the same for the whole wave
-FA_DEV void dma16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (FA_LDS void*)lds_base, 16, 0, 0);
-}
-FA_DEV void dma4(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (FA_LDS void*)lds_base, 4, 0, 0);
 }
 
 template <int D, bool CAUSAL, bool DQA>
@@ -159,23 +143,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     }
 
     // ---- per-lane LDS address bases ------------------------------------------
-    // A operand (rows = query, registers = d) of S / dP, from a swizzled tile:
-    // offset(t, ks) = baseA[ks % 4] + 128*(ks / 4) + 32*t*ROWB.
-    const int swA = swz(l32);
-    int baseA[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) baseA[j] = l32 * ROWB + 16 * (h ^ (swA & 1)) + 32 * (j ^ (swA >> 1));
-    // transposed B operand (registers = query rows) of dV / dK, from the same
-    // tiles: offset(st, dt, hi) = baseC[dt % 2] + 64*(dt & ~1) + (16*st + 8*hi)*ROWB.
-    int baseC[2];
-    {
-      const int sw = 2 * (s16 >> 2) + h;
-      const int cc = 2 * (g & 1) + ((s16 & 3) >> 1);
-      const int L = (4 * h + (s16 >> 2)) * ROWB + 16 * (cc ^ (sw & 3)) + 8 * (s16 & 1);
-      const int b = sw >> 2;
-      baseC[0] = L + 64 * b;          // dt even: chunk group dt ^ b = dt + b
-      baseC[1] = L + 64 * (1 - b);    // dt odd:  chunk group dt ^ b = (dt - 1) + (1 - b)
-    }
+    const TileBases<ROWB> tb(lane);
     // transposed A operand of dQ (registers = key rows) from the dS tile:
     // offset(s, u, hi) = baseE[u][hi] + 2048*s.
     int baseE[NQT][2];
@@ -203,7 +171,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
       for (int j = 0; j < LPW; ++j) {
         const int blk = wave * LPW + j;
         const int row = blk * RPL + lane / CH;
-        const int ch = (lane % CH) ^ swz(row);
+        const int ch = (lane % CH) ^ swz<ROWB>(row);
         const int q = min(qb0 + row, N - 1);
         const size_t go = (size_t)q * D + ch * 8;
         dma16(Qh + go, dQt + blk * 1024);
@@ -282,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
           f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const int off = baseA[ks & 3] + 128 * (ks >> 2) + 32 * t * ROWB;
+            const int off = tb.nat_off(t, ks);
             s = mfma32(lds_read_b128(Qt, off), kf[ks], s);
             dp = mfma32(lds_read_b128(Gt, off), vf[ks], dp);
           }
@@ -316,8 +284,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
         for (int st = 0; st < BR / 16; ++st) {
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const int o0 = baseC[dt & 1] + 64 * (dt & ~1) + 16 * st * ROWB;
-            const int o1 = o0 + 8 * ROWB;
+            const int o0 = tb.tr_off(st, dt, 0);
+            const int o1 = tb.tr_off(st, dt, 1);
             dv[dt] = mfma32(pa[st], cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1)), dv[dt]);
             dk[dt] = mfma32(da[st], cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1)), dk[dt]);
           }

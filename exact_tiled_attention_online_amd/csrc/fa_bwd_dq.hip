@@ -28,13 +28,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c) {
   constexpr int BR = 128, BC = 64;
   constexpr int ROWB = D * 2;        // bytes per row
-  constexpr int CH = D / 8;          // 16-byte chunks per row
   constexpr int KS = D / 16;         // K-steps of the S and dP products
   constexpr int DT = D / 32;         // 32-row tiles of dQ^T
   constexpr int TILEB = BC * ROWB;   // bytes of one K or V tile
-  constexpr int LPT = BC * CH / 256; // 16-byte loads per thread per tensor
 
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TILEB];  // [buffer][K, V]
+  __shared__ __attribute__((aligned(1024))) char sK0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char sK1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char sV0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char sV1[TILEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
@@ -75,49 +76,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     wave_tiles = (wkv_end + BC - 1) / BC;
   }
 
-  u32x4 stK[LPT], stV[LPT];
-  auto gload = [&](int j) {
-#pragma unroll
-    for (int p = 0; p < LPT; ++p) {
-      const int ci = p * 256 + tid;
-      const int row = ci / CH, ch = ci % CH;
-      const int kv = j * BC + row;
-      if (kv < N) {
-        stK[p] = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv * D + ch * 8);
-        stV[p] = *reinterpret_cast<const u32x4*>(Vh + (size_t)kv * D + ch * 8);
-      } else {
-        stK[p] = u32x4{0, 0, 0, 0};
-        stV[p] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < LPT; ++p) {
-      const int ci = p * 256 + tid;
-      const int row = ci / CH, ch = ci % CH;
-      const int off = tile_off<ROWB>(row, ch);
-      *reinterpret_cast<u32x4*>(&smem[buf][0][off]) = stK[p];
-      *reinterpret_cast<u32x4*>(&smem[buf][1][off]) = stV[p];
-    }
-  };
 
   f32x16 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) gload(j + 1);
+  // one key/value tile: products from buffer b while tile j+1 is fetched
+  // straight into buffer b^1 (distinct LDS objects per buffer, so the fetch
+  // cannot alias the reads)
+  auto body = [&](auto bc, int j) {
+    constexpr int b = decltype(bc)::value;
+    const char* Kt = b ? sK1 : sK0;
+    const char* Vt = b ? sV1 : sV0;
+    if (j + 1 < ntiles) {
+      dma_tile<ROWB, BC>(Kh, (j + 1) * BC, N, b ? sK0 : sK1, wave, lane);
+      dma_tile<ROWB, BC>(Vh, (j + 1) * BC, N, b ? sV0 : sV1, wave, lane);
+    }
     if (j < wave_tiles) {
-      const char* Kt = smem[buf][0];
-      const char* Vt = smem[buf][1];
       const int kvb = j * BC;
-      const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0) || (qrow >= N);
+      const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0) || (q0 + 32 > N);
       // the tile's two 32-key halves one after the other (fewer live registers)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
@@ -156,8 +133,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         }
       }
     }
-    if (j + 1 < ntiles) swrite((j + 1) & 1);
     __syncthreads();
+  };
+
+  dma_tile<ROWB, BC>(Kh, 0, N, sK0, wave, lane);
+  dma_tile<ROWB, BC>(Vh, 0, N, sV0, wave, lane);
+  __syncthreads();
+  for (int j = 0;;) {
+    body(IC<0>{}, j);
+    if (++j >= ntiles) break;
+    body(IC<1>{}, j);
+    if (++j >= ntiles) break;
   }
 
   if (qrow >= N) return;

@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -58,19 +60,26 @@ FA_DEV float half_sum(float x) {
 }
 
 // ---- swizzled row-major tiles in LDS -----------------------------------
-// A tile of rows of ROWB bytes (ROWB = 128 or 256) stored as 16-byte chunks;
-// chunk c of row r lives at chunk position c ^ swz(r).  With
-// swz(r) = 2*(r%4) + (r/4)%2:
-//  * 8 consecutive rows read at the same logical chunk (ds_read_b128 of an
-//    operand row) land on 8 distinct chunk positions;
-//  * 4 consecutive rows (first row a multiple of 4) read as 32-byte spans at
-//    an even logical chunk (ds_read_b64_tr_b16) also land on 8 distinct
-//    positions.
-FA_DEV int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// The LDS of gfx950 serves 256 bytes per clock as 64 four-byte banks: a
+// 16-byte read (ds_read_b128) is served 16 lanes at a time, an 8-byte
+// transposing read 32 lanes at a time (measured with the bank-conflict
+// counter).  A tile of rows of ROWB bytes (ROWB = 256 or 128) is stored as
+// 16-byte chunks, chunk c of row r at chunk position c ^ swz(r):
+//   ROWB = 256: swz(r) = 4*(r%4) + (r/4)%4
+//   ROWB = 128: swz(r) = 4*((r/2)%2) + (r/4)%4
+// so that both the operand reads (16 consecutive rows at one chunk) and the
+// transposing reads (4 consecutive rows, first a multiple of 4, times 4
+// consecutive chunks, first a multiple of 4) touch 16 distinct 16-byte bank
+// groups.  swz(r) depends on r % 16 only.
+template <int ROWB>
+FA_DEV int swz(int r) {
+  if constexpr (ROWB == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 template <int ROWB>
 FA_DEV int tile_off(int row, int chunk) {
-  return row * ROWB + ((chunk ^ swz(row)) << 4);
+  return row * ROWB + ((chunk ^ swz<ROWB>(row)) << 4);
 }
 // byte offset of element (row, col) (bf16 columns) in the swizzled tile
 template <int ROWB>
@@ -108,37 +117,66 @@ FA_DEV bf16x8 tr_operand(const char* tile, int k0, int k1, int n0, int lane) {
 }
 
 // Per-lane bases that turn every operand access of a swizzled tile into
-// base + compile-time offset (so only a handful of address registers stay
-// live).  Derivation: with row = R + r_lane (R a multiple of 8) the swizzle
-// swz(row) depends on the lane only, and the chunk index splits into a
-// compile-time part and a lane part; the XOR then acts on the lane part
-// except for one chunk bit, which two (or four) bases absorb.
+// base + compile-time offset, so that only a handful of address registers
+// stay live.  swz(row) depends on row % 16 only, so moving by a multiple of
+// 16 rows adds a constant; the chunk-dependent parts get one base each.
 template <int ROWB>
 struct TileBases {
+  static constexpr int KS = ROWB / 32;   // 16-wide K-steps per row
+  static constexpr int DT = ROWB / 64;   // 32-column groups per row
   // natural operand (lane = row 32*t + l32, registers = 8 elements of chunk
-  // 2*ks + h):  off(t, ks) = nat[ks % 4] + 128*(ks / 4) + 32*t*ROWB
-  int nat[4];
-  // transposed operand (lane = column, registers = rows k0..k0+3 and
-  // k0+8..k0+11 with k0 = 16*st + 4*h), column group 32*t + 16*(g%2):
-  // off(st, t, hi) = tr[t % 2] + 64*(t & ~1) + (16*st + 8*hi)*ROWB
-  int tr[2];
+  // 2*ks + h):  off(t, ks) = nat[ks] + 32*t*ROWB
+  int nat[KS];
+  // transposed operand (lane = column 32*t + 16*(g%2) + s, registers = rows
+  // k0..k0+3 and k0+8..k0+11 with k0 = 16*st + 4*h):
+  // off(st, t, hi) = tr[t][hi] + 16*st*ROWB
+  int tr[DT][2];
   FA_DEV TileBases(int lane) {
     const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, s16 = lane & 15;
-    const int swA = swz(l32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) nat[j] = l32 * ROWB + 16 * (h ^ (swA & 1)) + 32 * (j ^ (swA >> 1));
-    const int sw = 2 * (s16 >> 2) + h;
-    const int cc = 2 * (g & 1) + ((s16 & 3) >> 1);
-    const int L = (4 * h + (s16 >> 2)) * ROWB + 16 * (cc ^ (sw & 3)) + 8 * (s16 & 1);
-    const int b = sw >> 2;
-    tr[0] = L + 64 * b;          // t even: chunk group t ^ b = t + b
-    tr[1] = L + 64 * (1 - b);    // t odd:  chunk group t ^ b = (t - 1) + (1 - b)
+    for (int ks = 0; ks < KS; ++ks) nat[ks] = tile_off<ROWB>(l32, 2 * ks + h);
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi)
+        tr[t][hi] = tile_off_elem<ROWB>(4 * h + (s16 >> 2) + 8 * hi, 32 * t + 16 * (g & 1) + 4 * (s16 & 3));
   }
-  FA_DEV int nat_off(int t, int ks) const { return nat[ks & 3] + 128 * (ks >> 2) + 32 * t * ROWB; }
-  FA_DEV int tr_off(int st, int t, int hi) const {
-    return tr[t & 1] + 64 * (t & ~1) + (16 * st + 8 * hi) * ROWB;
-  }
+  FA_DEV int nat_off(int t, int ks) const { return nat[ks] + 32 * t * ROWB; }
+  FA_DEV int tr_off(int st, int t, int hi) const { return tr[t][hi] + 16 * st * ROWB; }
 };
+
+template <int B>
+using IC = std::integral_constant<int, B>;
+
+// Wave-wide direct fetch global -> LDS: lane l's 16 (or 4) bytes land at
+// lds_base + 16*l (or 4*l); lds_base must be the same for the whole wave.
+FA_DEV void dma16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (FA_LDS void*)lds_base, 16, 0, 0);
+}
+FA_DEV void dma4(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (FA_LDS void*)lds_base, 4, 0, 0);
+}
+
+// Fetch ROWS rows (ROWB bytes each) starting at row0 of a row-major bf16
+// matrix into a swizzled LDS tile, with the 4 waves of a workgroup.  Wave w,
+// load j fills LDS bytes [(w*LPW + j) KB, +1 KB): tile row blk*RPL + lane/CH
+// at chunk position lane%CH, i.e. logical chunk (lane%CH) ^ swz(row).  Rows at
+// or past nrows read row nrows-1 instead (finite values the caller masks).
+template <int ROWB, int ROWS>
+FA_DEV void dma_tile(const bf16* src, int row0, int nrows, char* dst, int wave, int lane) {
+  constexpr int CH = ROWB / 16, RPL = 1024 / ROWB, LPW = ROWS / RPL / 4;
+  static_assert(LPW * RPL * 4 == ROWS, "tile must split evenly over 4 waves");
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int blk = wave * LPW + j;
+    const int row = blk * RPL + lane / CH;
+    const int ch = (lane % CH) ^ swz<ROWB>(row);
+    const int r = min(row0 + row, nrows - 1);
+    dma16(src + (size_t)r * (ROWB / 2) + ch * 8, dst + blk * 1024);
+  }
+}
 
 FA_DEV bf16x8 pack8(float a0, float a1, float a2, float a3, float b0, float b1, float b2, float b3) {
   bf16x8 r;
