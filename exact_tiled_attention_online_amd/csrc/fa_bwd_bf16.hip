@@ -240,10 +240,14 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
       const int qb0 = i * BR;
       // this wave's keys are all later than all queries of the block: P^ = 0
       const bool skip = (kvw >= N) || (CAUSAL && qb0 + BR - 1 < kvw);
-      if (!skip) {
-        const bool need_mask = (CAUSAL && qb0 < kvw + 31) || (qb0 + BR > N) || (kvw + 32 > N);
+      // one pass over the block; MASK: apply the causal / tail mask (a
+      // compile-time variant, so the common unmasked path carries no mask code)
+      auto compute = [&](auto mc) {
+        constexpr bool MASK = decltype(mc)::value;
         // P^T and dS^T as A operands (lane = key row); K-step st covers queries
-        // 16st..16st+15: registers 0..3 <- 16st+4h+jj, 4..7 <- 16st+8+4h+jj
+        // 16st..16st+15: registers 0..3 <- 16st+4h+jj, 4..7 <- 16st+8+4h+jj.
+        // Each 32-query tile goes S/dP -> P^/dS -> its dV/dK products, so the
+        // products of one tile can overlap the exponentials of the next.
         bf16x8 pa[BR / 16], da[BR / 16];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
             for (int jj = 0; jj < 4; ++jj) {
               const int r = 4 * i4 + jj;
               float p = exp2_fast(fmaf(s[r], c, -L4[jj]));
-              if (need_mask) {
+              if constexpr (MASK) {
                 const int q = qb0 + ql + jj;
                 const bool dead = (q >= N) | (kvrow >= N) | (CAUSAL & (kvrow > q));
                 p = dead ? 0.f : p;
@@ -277,30 +281,36 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
           pa[2 * t + 1] = pack8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
           da[2 * t] = pack8(dp[0], dp[1], dp[2], dp[3], dp[4], dp[5], dp[6], dp[7]);
           da[2 * t + 1] = pack8(dp[8], dp[9], dp[10], dp[11], dp[12], dp[13], dp[14], dp[15]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // dV += P^T dO, dK += dS^T Q; B = dO / Q rows through transposing reads
+          // dV += P^T dO, dK += dS^T Q; B = dO / Q rows through transposing reads
 #pragma unroll
-        for (int st = 0; st < BR / 16; ++st) {
+          for (int sx = 0; sx < 2; ++sx) {
+            const int st = 2 * t + sx;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const int o0 = tb.tr_off(st, dt, 0);
-            const int o1 = tb.tr_off(st, dt, 1);
-            dv[dt] = mfma32(pa[st], cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1)), dv[dt]);
-            dk[dt] = mfma32(da[st], cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1)), dk[dt]);
+            for (int dt = 0; dt < DT; ++dt) {
+              const int o0 = tb.tr_off(st, dt, 0);
+              const int o1 = tb.tr_off(st, dt, 1);
+              dv[dt] = mfma32(pa[st], cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1)), dv[dt]);
+              dk[dt] = mfma32(da[st], cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1)), dk[dt]);
+            }
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
         // dS (bf16) to LDS, [key][query]
         if constexpr (DQA) {
 #pragma unroll
-        for (int st = 0; st < BR / 16; ++st) {
-          const bf16x4 lo = __builtin_shufflevector(da[st], da[st], 0, 1, 2, 3);
-          const bf16x4 hi = __builtin_shufflevector(da[st], da[st], 4, 5, 6, 7);
-          *reinterpret_cast<bf16x4*>(&St[ds_off(krow, 16 * st + 4 * h)]) = lo;
-          *reinterpret_cast<bf16x4*>(&St[ds_off(krow, 16 * st + 8 + 4 * h)]) = hi;
+          for (int st = 0; st < BR / 16; ++st) {
+            const bf16x4 lo = __builtin_shufflevector(da[st], da[st], 0, 1, 2, 3);
+            const bf16x4 hi = __builtin_shufflevector(da[st], da[st], 4, 5, 6, 7);
+            *reinterpret_cast<bf16x4*>(&St[ds_off(krow, 16 * st + 4 * h)]) = lo;
+            *reinterpret_cast<bf16x4*>(&St[ds_off(krow, 16 * st + 8 + 4 * h)]) = hi;
+          }
         }
-        }
+      };
+      if (!skip) {
+        const bool need_mask = (CAUSAL && qb0 < kvw + 31) || (qb0 + BR > N) || (kvw + 32 > N);
+        if (need_mask)
+          compute(IC<1>{});
+        else
+          compute(IC<0>{});
       } else if constexpr (DQA) {
 #pragma unroll
         for (int st = 0; st < BR / 16; ++st) {
