@@ -258,6 +258,16 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
             s = mfma32(lds_read_b128(Qt, off), kf[ks], s);
             dp = mfma32(lds_read_b128(Gt, off), vf[ks], dp);
           }
+          // keep four operand reads in flight ahead of the products
+#pragma unroll
+          for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+          for (int i_ = 0; i_ < 12; ++i_) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+#pragma unroll
+          for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           // register r: query qb0 + 32t + 8*(r/4) + 4h + r%4, key kvrow
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {

@@ -37,7 +37,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char sV0[TILEB];
   __shared__ __attribute__((aligned(1024))) char sV1[TILEB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform across the wave; readfirstlane tells the compiler
+  // so, which keeps the wave-level conditions below scalar branches
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const TileBases<D * 2> tb(lane);
   const int bid = blockIdx.x;
@@ -105,6 +107,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
           s = mfma32(lds_read_b128(Kt, off), qf[ks], s);
           dp = mfma32(lds_read_b128(Vt, off), gf[ks], dp);
         }
+        // keep four operand reads in flight ahead of the products
+#pragma unroll
+        for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int i_ = 0; i_ < 12; ++i_) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         // register r: key kvb + 32*mt + 8*(r/4) + 4*h + r%4, query qrow
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

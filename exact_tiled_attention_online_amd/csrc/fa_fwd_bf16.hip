@@ -39,7 +39,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sV0[TILEB];
   __shared__ __attribute__((aligned(1024))) char sV1[TILEB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform across the wave; readfirstlane tells the compiler
+  // so, which keeps the wave-level conditions below scalar branches
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const TileBases<D * 2> tb(lane);
   const int bid = blockIdx.x;
@@ -101,6 +103,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
           s[mt] = mfma32(a, qf[ks], s[mt]);
         }
       }
+      // keep four operand reads in flight ahead of the products
+#pragma unroll
+      for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i_ = 0; i_ < 12; ++i_) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       // s[mt][4*i+jj] = q_qrow . k_kv with kv = j*BC + 32*mt + 8*i + 4*h + jj
       const int kvb = j * BC;
       const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0);
