@@ -185,7 +185,7 @@ def main():
         check(fa.fa_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, N, d, w.causal, w.scale, sp, code), "fa_fwd")
         if ev is not None:
             ev[1].record(stream)
-        check(fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, P(ws), ws.numel(), sp, code),
+        check(fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, w.scale, P(ws), ws.numel(), sp, code),
               "fa_bwd_preprocess")
         if ev is not None:
             ev[2].record(stream)

@@ -44,7 +44,7 @@ def load():
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
-    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp, sz, vp, i]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, f, vp, sz, vp, i]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i]
     lib.fa_bwd_dkdv.restype = i
@@ -72,8 +72,9 @@ def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
     return load().fa_bwd_workspace_bytes(B, H, N, d, dtype)
 
 
-def fa_bwd_preprocess(o, dO, lse, B, H, N, d, workspace, workspace_bytes, stream, dtype) -> int:
-    return load().fa_bwd_preprocess(o, dO, lse, B, H, N, d, workspace, workspace_bytes, stream, dtype)
+def fa_bwd_preprocess(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype) -> int:
+    return load().fa_bwd_preprocess(o, dO, lse, B, H, N, d, float(scale), workspace, workspace_bytes,
+                                    stream, dtype)
 
 
 def fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes,

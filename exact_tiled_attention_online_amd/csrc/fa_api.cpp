@@ -32,8 +32,8 @@ int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype) 
 }
 
 struct Workspace {
-  float* drow;
-  float* lse2;
+  float* ndrow;   // -D per query row
+  float* nlse;    // -LSE / scale per query row
   float* dq_acc;  // bf16 only
   size_t bytes;
 };
@@ -43,9 +43,9 @@ Workspace carve(void* base, int B, int H, int N, int d, int dtype) {
   Workspace w{};
   char* p = static_cast<char*>(base);
   size_t off = 0;
-  w.drow = reinterpret_cast<float*>(p + off);
+  w.ndrow = reinterpret_cast<float*>(p + off);
   off += round_up(rows * sizeof(float));
-  w.lse2 = reinterpret_cast<float*>(p + off);
+  w.nlse = reinterpret_cast<float*>(p + off);
   off += round_up(rows * sizeof(float));
   w.dq_acc = nullptr;
   if (dtype == FA_BF16) {
@@ -94,16 +94,16 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
 }
 
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
-                      void* workspace, size_t workspace_bytes, void* stream, int dtype) {
+                      float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype) {
   if (!o || !dO || !lse) return FA_ERR_INVALID;
-  const int st = check_shape(B, H, N, d, 0, 1.f, dtype);
+  const int st = check_shape(B, H, N, d, 0, scale, dtype);
   if (st != FA_OK) return st;
   if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(lse, 4)) return FA_ERR_INVALID;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
   const Workspace w = carve(workspace, B, H, N, d, dtype);
   float* dq_acc = (dtype == FA_BF16 && dq_atomic_mode()) ? w.dq_acc : nullptr;
-  return hip_status(fa::launch_bwd_pre(o, dO, lse, w.drow, w.lse2, dq_acc, B * H, N, d, dtype == FA_FP32,
-                                       static_cast<hipStream_t>(stream)));
+  return hip_status(fa::launch_bwd_pre(o, dO, lse, w.ndrow, w.nlse, dq_acc, B * H, N, d, scale,
+                                       dtype == FA_FP32, static_cast<hipStream_t>(stream)));
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dk,
@@ -121,9 +121,9 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, con
   if (dtype == FA_FP32)
     return hip_status(fa::launch_bwd_kv_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                             static_cast<const float*>(v), static_cast<const float*>(dO), lse,
-                                            w.drow, static_cast<float*>(dk), static_cast<float*>(dv), B * H, N,
+                                            w.ndrow, static_cast<float*>(dk), static_cast<float*>(dv), B * H, N,
                                             d, causal != 0, scale, s));
-  return hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.lse2, w.drow, w.dq_acc, dk, dv, B * H, N, d,
+  return hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.nlse, w.ndrow, w.dq_acc, dk, dv, B * H, N, d,
                                         causal != 0, scale, dq_atomic_mode(), s));
 }
 
@@ -142,10 +142,10 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const
   if (dtype == FA_FP32)
     return hip_status(fa::launch_bwd_q_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                            static_cast<const float*>(v), static_cast<const float*>(dO), lse,
-                                           w.drow, static_cast<float*>(dq), B * H, N, d, causal != 0, scale, s));
+                                           w.ndrow, static_cast<float*>(dq), B * H, N, d, causal != 0, scale, s));
   if (dq_atomic_mode())
     return hip_status(fa::launch_dq_convert(w.dq_acc, dq, (size_t)B * H * N * d, scale, s));
-  return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.lse2, w.drow, dq, B * H, N, d, causal != 0, scale, s));
+  return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.nlse, w.ndrow, dq, B * H, N, d, causal != 0, scale, s));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
@@ -159,7 +159,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
-  int r = fa_bwd_preprocess(o, dO, lse, B, H, N, d, workspace, workspace_bytes, stream, dtype);
+  int r = fa_bwd_preprocess(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype);
   if (r != FA_OK) return r;
   r = fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype);
   if (r != FA_OK) return r;

@@ -2,9 +2,11 @@
 //
 // bwd_pre: D_i = sum_c dO_ic * O_ic for every query row (page
 // "flash-attention-backpropagation" (aiqz.cc), section Softmax梯度: the row
-// term the softmax normalisation adds to dP), plus the ledger rescaled to base
-// 2 (LSE * log2 e) for the backward's exp2, plus the clear of the fp32 dQ
-// accumulator (a fill kernel, so the whole backward can be captured in a graph).
+// term the softmax normalisation adds to dP), stored negated, plus the ledger
+// divided by the scale, negated (-LSE / scale): the product kernels start
+// their S and dP accumulators from these, so that the accumulators end as
+// S - LSE/scale and dP - D.  Also the clear of the fp32 dQ accumulator (a fill
+// kernel, so the whole backward can be captured in a graph).
 // Each row of d elements is read by d/8 lanes with 16-byte (bf16) or 32-byte
 // (fp32) loads, reduced across those lanes with xor-shuffles.
 //
@@ -17,8 +19,8 @@ namespace fa {
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                       const float* __restrict__ lse,
-                                                      float* __restrict__ drow, float* __restrict__ lse2,
-                                                      float* __restrict__ dq_acc, size_t rows) {
+                                                      float* __restrict__ ndrow, float* __restrict__ nlse,
+                                                      float* __restrict__ dq_acc, size_t rows, float inv_scale) {
   constexpr int LPR = D / 8;            // lanes per row, 8 elements each
   constexpr int RPB = 256 / LPR;        // rows per block
   const int tid = threadIdx.x;
@@ -51,30 +53,31 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
   if (row < rows && part == 0) {
-    drow[row] = acc;
-    lse2[row] = lse[row] * kLog2e;
+    ndrow[row] = -acc;
+    nlse[row] = -lse[row] * inv_scale;
   }
 }
 
-hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* drow, float* lse2,
-                          float* dq_acc, int BH, int N, int d, bool fp32, hipStream_t stream) {
+hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ndrow, float* nlse,
+                          float* dq_acc, int BH, int N, int d, float scale, bool fp32, hipStream_t stream) {
+  const float inv_scale = 1.f / scale;
   const size_t rows = (size_t)BH * N;
   const int rpb = 256 / (d / 8);
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
   if (fp32) {
     if (d == 128)
       hipLaunchKernelGGL((bwd_pre_kernel<128, float>), grid, block, 0, stream, (const float*)o,
-                         (const float*)dO, lse, drow, lse2, dq_acc, rows);
+                         (const float*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale);
     else
       hipLaunchKernelGGL((bwd_pre_kernel<64, float>), grid, block, 0, stream, (const float*)o,
-                         (const float*)dO, lse, drow, lse2, dq_acc, rows);
+                         (const float*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale);
   } else {
     if (d == 128)
       hipLaunchKernelGGL((bwd_pre_kernel<128, bf16>), grid, block, 0, stream, (const bf16*)o,
-                         (const bf16*)dO, lse, drow, lse2, dq_acc, rows);
+                         (const bf16*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale);
     else
       hipLaunchKernelGGL((bwd_pre_kernel<64, bf16>), grid, block, 0, stream, (const bf16*)o,
-                         (const bf16*)dO, lse, drow, lse2, dq_acc, rows);
+                         (const bf16*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale);
   }
   return hipGetLastError();
 }

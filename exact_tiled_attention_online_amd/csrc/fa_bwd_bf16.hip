@@ -9,7 +9,7 @@
 // news/1372000", 踩坑二: recomputing P once per pair of blocks):
 //   S  = Q_i K_w^T                 MFMA, A = Q rows (LDS), B = K_w (registers)
 //   dP = dO_i V_w^T                MFMA, A = dO rows (LDS), B = V_w (registers)
-//   P^ = 2^(c*S - LSE2)            recompute from the ledger (section 数值稳定)
+//   P^ = 2^(c*(S - LSE/scale))     recompute from the ledger (section 数值稳定)
 //   dS = P^ o (dP - D)             (section Softmax梯度)
 //   dV_w += P^T dO_i               MFMA, A = P^T from the S accumulators,
 //                                  B = dO through transposing LDS reads
@@ -46,7 +46,7 @@ FA_DEV int ds_off(int row, int col) {
 template <int D, bool CAUSAL, bool DQA>
 __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ DR,
+    const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
     float* __restrict__ dQacc, bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb,
     float scale, float c) {
   constexpr int BC = 128, BR = 64;
@@ -60,9 +60,9 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sQ1[QTB];
   __shared__ __attribute__((aligned(1024))) char sG0[QTB];   // dO
   __shared__ __attribute__((aligned(1024))) char sG1[QTB];
-  __shared__ __attribute__((aligned(256))) float sL0[BR];    // LSE * log2 e
+  __shared__ __attribute__((aligned(256))) float sL0[BR];    // -LSE / scale
   __shared__ __attribute__((aligned(256))) float sL1[BR];
-  __shared__ __attribute__((aligned(256))) float sD0[BR];    // D
+  __shared__ __attribute__((aligned(256))) float sD0[BR];    // -D
   __shared__ __attribute__((aligned(256))) float sD1[BR];
   constexpr int SSB = DQA ? BC * BR * 2 : 16;   // dS tiles exist only with atomic dQ
   constexpr int SKB = DQA ? BC * ROWB : 16;      // K block for the K^T operand of dQ
@@ -92,8 +92,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   const bf16* Kh = K + hoff;
   const bf16* Vh = V + hoff;
   const bf16* Gh = dO + hoff;
-  const float* Lh = LSE2 + (size_t)head * N;
-  const float* Dh = DR + (size_t)head * N;
+  const float* Lh = NLSE + (size_t)head * N;   // -LSE / scale
+  const float* Dh = NDR + (size_t)head * N;    // -D
   float* dQh = dQacc + hoff;
 
   for (int part = 0; part < nparts; ++part) {
@@ -246,64 +246,114 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
         constexpr bool MASK = decltype(mc)::value;
         // P^T and dS^T as A operands (lane = key row); K-step st covers queries
         // 16st..16st+15: registers 0..3 <- 16st+4h+jj, 4..7 <- 16st+8+4h+jj.
-        // Each 32-query tile goes S/dP -> P^/dS -> its dV/dK products, so the
-        // products of one tile can overlap the exponentials of the next.
         bf16x8 pa[BR / 16], da[BR / 16];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const int off = tb.nat_off(t, ks);
-            s = mfma32(lds_read_b128(Qt, off), kf[ks], s);
-            dp = mfma32(lds_read_b128(Gt, off), vf[ks], dp);
-          }
-          // keep four operand reads in flight ahead of the products
-#pragma unroll
-          for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-          for (int i_ = 0; i_ < 12; ++i_) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-#pragma unroll
-          for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          // register r: query qb0 + 32t + 8*(r/4) + 4h + r%4, key kvrow
+        // Four phases separated by scheduling fences; each pairs products with
+        // vector work that does not depend on them:
+        //   A: S, dP of query tile 0
+        //   B: S, dP of query tile 1   | exponentials of tile 0
+        //   C: dV, dK of tile 0        | exponentials of tile 1
+        //   D: dV, dK of tile 1
+        // The first operands of a phase are read at the end of the one before.
+        // The S and dP accumulators start from -LSE/scale and -D of their
+        // query rows, so they end as S - LSE/scale and dP - D.
+        f32x16 s[2], dp[2];
+        bf16x8 qa[2][KS], ga[2][KS];
+        bf16x8 tq[2][2 * DT], tg[2][2 * DT];
+        auto rd_s = [&](int t, int ks) {
+          const int off = tb.nat_off(t, ks);
+          qa[t][ks] = lds_read_b128(Qt, off);
+          ga[t][ks] = lds_read_b128(Gt, off);
+        };
+        auto rd_t = [&](int t, int j) {   // j = sx*DT + dt
+          const int st = 2 * t + j / DT, dt = j % DT;
+          const int o0 = tb.tr_off(st, dt, 0), o1 = tb.tr_off(st, dt, 1);
+          tg[t][j] = cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1));
+          tq[t][j] = cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1));
+        };
+        // S = Q_i K_w^T - LSE/scale, dP = dO_i V_w^T - D; register r: query
+        // qb0 + 32t + 8*(r/4) + 4h + r%4, key kvrow
+        auto sdp = [&](int t, int ks_pre) {
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
             const int ql = 32 * t + 8 * i4 + 4 * h;
-            const f32x4 L4 = *reinterpret_cast<const f32x4*>(Lt + ql);
-            const f32x4 D4 = *reinterpret_cast<const f32x4*>(Dt + ql);
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + ql);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Dt + ql);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-              const int r = 4 * i4 + jj;
-              float p = exp2_fast(fmaf(s[r], c, -L4[jj]));
-              if constexpr (MASK) {
-                const int q = qb0 + ql + jj;
-                const bool dead = (q >= N) | (kvrow >= N) | (CAUSAL & (kvrow > q));
-                p = dead ? 0.f : p;
-              }
-              s[r] = p;
-              dp[r] = p * (dp[r] - D4[jj]);
+              s[t][4 * i4 + jj] = l4[jj];
+              dp[t][4 * i4 + jj] = d4[jj];
             }
           }
-          pa[2 * t] = pack8(s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]);
-          pa[2 * t + 1] = pack8(s[8], s[9], s[10], s[11], s[12], s[13], s[14], s[15]);
-          da[2 * t] = pack8(dp[0], dp[1], dp[2], dp[3], dp[4], dp[5], dp[6], dp[7]);
-          da[2 * t + 1] = pack8(dp[8], dp[9], dp[10], dp[11], dp[12], dp[13], dp[14], dp[15]);
-          // dV += P^T dO, dK += dS^T Q; B = dO / Q rows through transposing reads
 #pragma unroll
-          for (int sx = 0; sx < 2; ++sx) {
-            const int st = 2 * t + sx;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-              const int o0 = tb.tr_off(st, dt, 0);
-              const int o1 = tb.tr_off(st, dt, 1);
-              dv[dt] = mfma32(pa[st], cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1)), dv[dt]);
-              dk[dt] = mfma32(da[st], cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1)), dk[dt]);
-            }
+          for (int ks = 0; ks < KS; ++ks) {
+            if (ks >= ks_pre) rd_s(t, ks);
+            s[t] = mfma32(qa[t][ks], kf[ks], s[t]);
+            dp[t] = mfma32(ga[t][ks], vf[ks], dp[t]);
           }
+        };
+        // P^ = 2^(c (S - LSE/scale)), dS = P^ o (dP - D), both to bf16
+        auto elem = [&](int t) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float p = exp2_fast(s[t][r] * c);
+            if constexpr (MASK) {
+              const int q = qb0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+              const bool dead = (q >= N) | (kvrow >= N) | (CAUSAL & (kvrow > q));
+              p = dead ? 0.f : p;
+            }
+            s[t][r] = p;
+            dp[t][r] = p * dp[t][r];
+          }
+          pa[2 * t] = pack8(s[t][0], s[t][1], s[t][2], s[t][3], s[t][4], s[t][5], s[t][6], s[t][7]);
+          pa[2 * t + 1] = pack8(s[t][8], s[t][9], s[t][10], s[t][11], s[t][12], s[t][13], s[t][14], s[t][15]);
+          da[2 * t] = pack8(dp[t][0], dp[t][1], dp[t][2], dp[t][3], dp[t][4], dp[t][5], dp[t][6], dp[t][7]);
+          da[2 * t + 1] = pack8(dp[t][8], dp[t][9], dp[t][10], dp[t][11], dp[t][12], dp[t][13], dp[t][14], dp[t][15]);
+        };
+        // dV += P^T dO, dK += dS^T Q; B = dO / Q rows through transposing reads
+        auto dvdk = [&](int t, int j_pre) {
+#pragma unroll
+          for (int j = 0; j < 2 * DT; ++j) {
+            if (j >= j_pre) rd_t(t, j);
+            const int st = 2 * t + j / DT, dt = j % DT;
+            dv[dt] = mfma32(pa[st], tg[t][j], dv[dt]);
+            dk[dt] = mfma32(da[st], tq[t][j], dk[dt]);
+          }
+        };
+        constexpr int PRE = 2;   // operand pairs read ahead into the next phase
+        constexpr int VPM = 6;   // vector instructions per product in phases B, C
+        // ---- A
+#pragma unroll
+        for (int ks = 0; ks < PRE; ++ks) rd_s(0, ks);
+        sdp(0, PRE);
+#pragma unroll
+        for (int ks = 0; ks < PRE; ++ks) rd_s(1, ks);
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- B
+        sdp(1, PRE);
+        elem(0);
+#pragma unroll
+        for (int j = 0; j < PRE; ++j) rd_t(0, j);
+#pragma unroll
+        for (int i_ = 0; i_ < 2 * KS; ++i_) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0); // VALU
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- C
+        dvdk(0, PRE);
+        elem(1);
+#pragma unroll
+        for (int j = 0; j < PRE; ++j) rd_t(1, j);
+#pragma unroll
+        for (int i_ = 0; i_ < 4 * DT; ++i_) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- D
+        dvdk(1, PRE);
         // dS (bf16) to LDS, [key][query]
         if constexpr (DQA) {
 #pragma unroll
@@ -384,33 +434,33 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 
 template <int D, bool CAUSAL, bool DQA>
 static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v, const void* dO,
-                                    const float* lse2, const float* drow, float* dq_acc, void* dk,
+                                    const float* nlse, const float* ndrow, float* dq_acc, void* dk,
                                     void* dv, int BH, int N, float scale, hipStream_t stream) {
   const int nkb = (N + 127) / 128, nqb = (N + 63) / 64;
   const int items = CAUSAL ? (nkb + 1) / 2 : nkb;
   const dim3 grid((unsigned)(items * BH)), block(256);
   hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, DQA>), grid, block, 0, stream, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, (const bf16*)dO, lse2, drow, dq_acc, (bf16*)dk,
+                     (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, dq_acc, (bf16*)dk,
                      (bf16*)dv, BH, N, nqb, scale, scale * kLog2e);
   return hipGetLastError();
 }
 
 template <bool DQA>
 static hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void* dO,
-                                const float* lse2, const float* drow, float* dq_acc, void* dk, void* dv,
+                                const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
                                 int BH, int N, int d, bool causal, float scale, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_bwd_bf16_t<128, true, DQA>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream)
-                  : launch_bwd_bf16_t<128, false, DQA>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream);
-  return causal ? launch_bwd_bf16_t<64, true, DQA>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream)
-                : launch_bwd_bf16_t<64, false, DQA>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, scale, stream);
+    return causal ? launch_bwd_bf16_t<128, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, stream)
+                  : launch_bwd_bf16_t<128, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, stream);
+  return causal ? launch_bwd_bf16_t<64, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, stream)
+                : launch_bwd_bf16_t<64, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, stream);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dO,
-                           const float* lse2, const float* drow, float* dq_acc, void* dk, void* dv,
+                           const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
                            int BH, int N, int d, bool causal, float scale, bool dq_atomic, hipStream_t stream) {
-  return dq_atomic ? launch_bwd_kv<true>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, d, causal, scale, stream)
-                   : launch_bwd_kv<false>(q, k, v, dO, lse2, drow, dq_acc, dk, dv, BH, N, d, causal, scale, stream);
+  return dq_atomic ? launch_bwd_kv<true>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, d, causal, scale, stream)
+                   : launch_bwd_kv<false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, d, causal, scale, stream);
 }
 
 }  // namespace fa

@@ -8,7 +8,7 @@
 // through LDS).  Per tile and wave:
 //   S^T  = K_j Q_w^T           MFMA, A = K rows (LDS), B = Q_w (registers)
 //   dP^T = V_j dO_w^T          MFMA, A = V rows (LDS), B = dO_w (registers)
-//   P^   = 2^(c*S - LSE2)      recompute from the ledger (section 数值稳定);
+//   P^   = 2^(c*(S - LSE/scale))  recompute from the ledger (section 数值稳定);
 //                              the lane holds one query row, so LSE and D
 //                              are per-lane scalars
 //   dS   = P^ o (dP - D)       (section Softmax梯度)
@@ -24,7 +24,7 @@ namespace fa {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ DR,
+    const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
     bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c) {
   constexpr int BR = 128, BC = 64;
   constexpr int ROWB = D * 2;        // bytes per row
@@ -67,8 +67,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       gf[s] = bf16x8{};
     }
   }
-  const float lse2 = qrow < N ? LSE2[(size_t)head * N + qrow] : 0.f;
-  const float drow = qrow < N ? DR[(size_t)head * N + qrow] : 0.f;
+  // -LSE * log2(e) and -D of this lane's query row
+  const float nl2 = qrow < N ? NLSE[(size_t)head * N + qrow] * c : 0.f;
+  const float ndrow = qrow < N ? NDR[(size_t)head * N + qrow] : 0.f;
 
   const int kv_end = CAUSAL ? min(N, qb * BR + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
@@ -120,13 +121,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         // register r: key kvb + 32*mt + 8*(r/4) + 4*h + r%4, query qrow
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = exp2_fast(fmaf(s[r], c, -lse2));
+          float p = exp2_fast(fmaf(s[r], c, nl2));
           if (need_mask) {
             const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
             const bool dead = (kv >= N) | (qrow >= N) | (CAUSAL & (kv > qrow));
             p = dead ? 0.f : p;
           }
-          dp[r] = p * (dp[r] - drow);
+          dp[r] = p * (dp[r] + ndrow);
         }
         // dS^T as B operand; K-step st = 2*mt + half covers keys 16*st ..
         // 16*st+15 of the tile: registers 0..3 <- keys 16st+4h+jj, 4..7 <-
@@ -176,23 +177,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_dq_t(const void* q, const void* k, const void* v, const void* dO,
-                                  const float* lse2, const float* drow, void* dq, int BH, int N, float scale,
+                                  const float* nlse, const float* ndrow, void* dq, int BH, int N, float scale,
                                   hipStream_t stream) {
   const int nqb = (N + 127) / 128;
   const dim3 grid((unsigned)(nqb * BH)), block(256);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
-                     (const bf16*)v, (const bf16*)dO, lse2, drow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e);
+                     (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse2,
-                         const float* drow, void* dq, int BH, int N, int d, bool causal, float scale,
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
+                         const float* ndrow, void* dq, int BH, int N, int d, bool causal, float scale,
                          hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_bwd_dq_t<128, true>(q, k, v, dO, lse2, drow, dq, BH, N, scale, stream)
-                  : launch_bwd_dq_t<128, false>(q, k, v, dO, lse2, drow, dq, BH, N, scale, stream);
-  return causal ? launch_bwd_dq_t<64, true>(q, k, v, dO, lse2, drow, dq, BH, N, scale, stream)
-                : launch_bwd_dq_t<64, false>(q, k, v, dO, lse2, drow, dq, BH, N, scale, stream);
+    return causal ? launch_bwd_dq_t<128, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, stream)
+                  : launch_bwd_dq_t<128, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, stream);
+  return causal ? launch_bwd_dq_t<64, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, stream)
+                : launch_bwd_dq_t<64, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, stream);
 }
 
 }  // namespace fa

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                          const float* __restrict__ V, const float* __restrict__ dO,
-                                                         const float* __restrict__ LSE, const float* __restrict__ DR,
+                                                         const float* __restrict__ LSE, const float* __restrict__ NDR,
                                                          float* __restrict__ dK, float* __restrict__ dV, int N,
                                                          float scale) {
   constexpr int DH = D / 2;
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
     if (tid < F32_TILE) {
       const int q = t0 + tid;
       sl[tid] = q < N ? LSE[(size_t)head * N + q] : 0.f;
-      sd[tid] = q < N ? DR[(size_t)head * N + q] : 0.f;
+      sd[tid] = q < N ? NDR[(size_t)head * N + q] : 0.f;
     }
     __syncthreads();
     for (int j = 0; j < F32_TILE; ++j) {
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
       float p = expf(sc - sl[j]);
       if (q >= N || kvrow >= N || (CAUSAL && kvrow > q)) p = 0.f;
       const float dp = half_dot<D>(sg + j * D + half * DH, vh);
-      const float ds = p * (dp - sd[j]);
+      const float ds = p * (dp + sd[j]);   // sd holds -D
 #pragma unroll
       for (int c = 0; c < DH; ++c) {
         dvh[c] = fmaf(p, sg[j * D + half * DH + c], dvh[c]);
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                         const float* __restrict__ V, const float* __restrict__ dO,
-                                                        const float* __restrict__ LSE, const float* __restrict__ DR,
+                                                        const float* __restrict__ LSE, const float* __restrict__ NDR,
                                                         float* __restrict__ dQ, int N, float scale) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
     dqh[c] = 0.f;
   }
   const float lse = qrow < N ? LSE[(size_t)head * N + qrow] : 0.f;
-  const float drow = qrow < N ? DR[(size_t)head * N + qrow] : 0.f;
+  const float ndrow = qrow < N ? NDR[(size_t)head * N + qrow] : 0.f;   // -D
   const int kv_end = CAUSAL ? min(N, row0 + F32_ROWS) : N;
   for (int t0 = 0; t0 < kv_end; t0 += F32_TILE) {
     __syncthreads();
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
       float p = expf(sc - lse);
       if (qrow >= N || kv >= N || (CAUSAL && kv > qrow)) p = 0.f;
       const float dp = half_dot<D>(gh, sv + j * D + half * DH);
-      const float ds = p * (dp - drow);
+      const float ds = p * (dp + ndrow);
 #pragma unroll
       for (int c = 0; c < DH; ++c) dqh[c] = fmaf(ds, sk[j * D + half * DH + c], dqh[c]);
     }
@@ -217,19 +217,19 @@ static hipError_t fwd_f32_t(const float* q, const float* k, const float* v, floa
 
 template <int D, bool CAUSAL>
 static hipError_t bwd_kv_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
-                               const float* drow, float* dk, float* dv, int BH, int N, float scale,
+                               const float* ndrow, float* dk, float* dv, int BH, int N, float scale,
                                hipStream_t stream) {
   const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
-  hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, drow, dk, dv, N,
+  hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dk, dv, N,
                      scale);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 static hipError_t bwd_q_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
-                              const float* drow, float* dq, int BH, int N, float scale, hipStream_t stream) {
+                              const float* ndrow, float* dq, int BH, int N, float scale, hipStream_t stream) {
   const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
-  hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, drow, dq, N, scale);
+  hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dq, N, scale);
   return hipGetLastError();
 }
 
@@ -243,23 +243,23 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 }
 
 hipError_t launch_bwd_kv_f32(const float* q, const float* k, const float* v, const float* dO, const float* lse,
-                             const float* drow, float* dk, float* dv, int BH, int N, int d, bool causal,
+                             const float* ndrow, float* dk, float* dv, int BH, int N, int d, bool causal,
                              float scale, hipStream_t stream) {
   if (d == 128)
-    return causal ? bwd_kv_f32_t<128, true>(q, k, v, dO, lse, drow, dk, dv, BH, N, scale, stream)
-                  : bwd_kv_f32_t<128, false>(q, k, v, dO, lse, drow, dk, dv, BH, N, scale, stream);
-  return causal ? bwd_kv_f32_t<64, true>(q, k, v, dO, lse, drow, dk, dv, BH, N, scale, stream)
-                : bwd_kv_f32_t<64, false>(q, k, v, dO, lse, drow, dk, dv, BH, N, scale, stream);
+    return causal ? bwd_kv_f32_t<128, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, stream)
+                  : bwd_kv_f32_t<128, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, stream);
+  return causal ? bwd_kv_f32_t<64, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, stream)
+                : bwd_kv_f32_t<64, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, stream);
 }
 
 hipError_t launch_bwd_q_f32(const float* q, const float* k, const float* v, const float* dO, const float* lse,
-                            const float* drow, float* dq, int BH, int N, int d, bool causal, float scale,
+                            const float* ndrow, float* dq, int BH, int N, int d, bool causal, float scale,
                             hipStream_t stream) {
   if (d == 128)
-    return causal ? bwd_q_f32_t<128, true>(q, k, v, dO, lse, drow, dq, BH, N, scale, stream)
-                  : bwd_q_f32_t<128, false>(q, k, v, dO, lse, drow, dq, BH, N, scale, stream);
-  return causal ? bwd_q_f32_t<64, true>(q, k, v, dO, lse, drow, dq, BH, N, scale, stream)
-                : bwd_q_f32_t<64, false>(q, k, v, dO, lse, drow, dq, BH, N, scale, stream);
+    return causal ? bwd_q_f32_t<128, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, stream)
+                  : bwd_q_f32_t<128, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, stream);
+  return causal ? bwd_q_f32_t<64, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, stream)
+                : bwd_q_f32_t<64, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, stream);
 }
 
 }  // namespace fa

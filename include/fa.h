@@ -95,8 +95,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * all three with the same arguments is exactly fa_bwd.
  *
  * fa_bwd_preprocess: D_i = sum_c dO_ic * O_ic (page
- *   "flash-attention-backpropagation", section Softmax梯度) and the ledger in
- *   base 2, into the workspace.
+ *   "flash-attention-backpropagation", section Softmax梯度) and the ledger
+ *   divided by scale, both negated, into the workspace (the product kernels
+ *   start their S and dP accumulators from these values).  scale must be the
+ *   one later passed to fa_bwd_dkdv and fa_bwd_dq.
  * fa_bwd_dkdv: the key/value-block-outer kernel (section QKV梯度): recomputes
  *   P^ and dS per pair of blocks and writes dk and dv.
  * fa_bwd_dq: the query-block-outer kernel: recomputes S, P^, dP, dS per pair
@@ -108,7 +110,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * which measured faster.
  */
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
-                      void* workspace, size_t workspace_bytes, void* stream, int dtype);
+                      float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype);
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                 void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
                 void* workspace, size_t workspace_bytes, void* stream, int dtype);

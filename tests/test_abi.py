@@ -26,6 +26,41 @@ def test_header_declares_the_boundary():
     assert header_functions() == sorted(_lib.EXPORTS)
 
 
+def header_signatures():
+    """name -> list of C parameter types, from the declarations in include/fa.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    sigs = {}
+    for m in re.finditer(r"^\s*(?:const\s+)?\w+\**\s+\**(fa_\w+)\s*\(([^)]*)\)\s*;", text, flags=re.M):
+        params = [" ".join(p.split()) for p in m.group(2).split(",")]
+        types = []
+        for p in params:
+            p = re.sub(r"\b\w+$", "", p).strip()   # drop the parameter name
+            types.append(p)
+        sigs[m.group(1)] = types
+    return sigs
+
+
+def _ctype_of(c_type):
+    if "*" in c_type:
+        return ctypes.c_void_p
+    return {"int": ctypes.c_int, "float": ctypes.c_float, "size_t": ctypes.c_size_t}[c_type]
+
+
+@needs_lib
+def test_binding_argtypes_match_header():
+    """Every ctypes prototype in the binding has the header's parameter count
+    and kinds (pointer, int, float, size_t), so a change of the C signature
+    cannot be marshalled wrongly."""
+    lib = _lib.load()
+    sigs = header_signatures()
+    assert sorted(sigs) == sorted(_lib.EXPORTS)
+    for name, types in sigs.items():
+        want = [_ctype_of(t) for t in types if t != "void"]
+        got = list(getattr(lib, name).argtypes)
+        assert got == want, (name, got, want)
+
+
 @needs_lib
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(_lib.LIB_PATH)
