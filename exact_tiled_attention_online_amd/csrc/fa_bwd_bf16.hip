@@ -52,8 +52,6 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   constexpr int BC = 128, BR = 64;
   constexpr int ROWB = D * 2, CH = D / 8, KS = D / 16, DT = D / 32;
   constexpr int QTB = BR * ROWB;          // bytes of one Q or dO tile
-  constexpr int RPL = 1024 / ROWB;        // tile rows per 1 KB wave-wide LDS load
-  constexpr int LPW = BR / RPL / 4;       // such loads per wave per tile
   constexpr int NQT = (D == 128) ? 2 : 1; // query tiles of dQ per wave
 
   __shared__ __attribute__((aligned(1024))) char sQ0[QTB];
@@ -72,6 +70,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, s16 = lane & 15;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the same value, known uniform
+  const TileFetch<D * 2, BR> qfetch(wave_u, lane);
   // Work items.  Causal: item c of a head is the key-block pair
   // (c, nkb-1-c), whose query walks together always cover the same number of
   // blocks, so every workgroup does the same work; the first block is walked
@@ -162,23 +162,19 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     const int i_begin = CAUSAL ? (kv0 / BR) : 0;
 
     // ---- direct global -> LDS fetch of one query block ------------------------
-    // wave w, load j fills LDS bytes [(w*LPW + j) KB, +1 KB): tile rows
-    // (w*LPW + j)*RPL + lane/CH, chunk position lane%CH (logical chunk
-    // position ^ swz(row)).  Rows past N read row N-1 (finite; masked later).
+    // Q and dO tiles through TileFetch (rows past N read row N-1: finite,
+    // masked later); the LSE and D rows by waves 0 and 1, 4 bytes per lane.
     auto fetch = [&](int i, char* dQt, char* dGt, float* dL, float* dD) {
       const int qb0 = i * BR;
-#pragma unroll
-      for (int j = 0; j < LPW; ++j) {
-        const int blk = wave * LPW + j;
-        const int row = blk * RPL + lane / CH;
-        const int ch = (lane % CH) ^ swz<ROWB>(row);
-        const int q = min(qb0 + row, N - 1);
-        const size_t go = (size_t)q * D + ch * 8;
-        dma16(Qh + go, dQt + blk * 1024);
-        dma16(Gh + go, dGt + blk * 1024);
+      qfetch(Qh, qb0, N, dQt);
+      qfetch(Gh, qb0, N, dGt);
+      if (qb0 + BR <= N) {
+        if (wave_u == 0) dma4_buf(raw_rsrc(Lh), 4 * lane, 4 * qb0, dL);
+        if (wave_u == 1) dma4_buf(raw_rsrc(Dh), 4 * lane, 4 * qb0, dD);
+      } else {
+        if (wave_u == 0) dma4(Lh + min(qb0 + lane, N - 1), dL);
+        if (wave_u == 1) dma4(Dh + min(qb0 + lane, N - 1), dD);
       }
-      if (wave == 0) dma4(Lh + min(qb0 + lane, N - 1), dL);
-      if (wave == 1) dma4(Dh + min(qb0 + lane, N - 1), dD);
     };
 
     f32x16 dk[DT], dv[DT];

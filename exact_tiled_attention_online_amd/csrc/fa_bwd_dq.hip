@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const TileBases<D * 2> tb(lane);
+  const TileFetch<D * 2, BC> fetch(wave, lane);
   const int bid = blockIdx.x;
   const int head = bid % BH;
   // causal: the longest query blocks are dispatched first
@@ -92,8 +93,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const char* Kt = b ? sK1 : sK0;
     const char* Vt = b ? sV1 : sV0;
     if (j + 1 < ntiles) {
-      dma_tile<ROWB, BC>(Kh, (j + 1) * BC, N, b ? sK0 : sK1, wave, lane);
-      dma_tile<ROWB, BC>(Vh, (j + 1) * BC, N, b ? sV0 : sV1, wave, lane);
+      fetch(Kh, (j + 1) * BC, N, b ? sK0 : sK1);
+      fetch(Vh, (j + 1) * BC, N, b ? sV0 : sV1);
     }
     if (j < wave_tiles) {
       const int kvb = j * BC;
@@ -149,8 +150,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     __syncthreads();
   };
 
-  dma_tile<ROWB, BC>(Kh, 0, N, sK0, wave, lane);
-  dma_tile<ROWB, BC>(Vh, 0, N, sV0, wave, lane);
+  fetch(Kh, 0, N, sK0);
+  fetch(Vh, 0, N, sV0);
   __syncthreads();
   for (int j = 0;;) {
     body(IC<0>{}, j);

@@ -159,24 +159,59 @@ FA_DEV void dma4(const void* gsrc, void* lds_base) {
                                    (FA_LDS void*)lds_base, 4, 0, 0);
 }
 
+// The same through a buffer resource: byte address = base + soffset (uniform)
+// + voffset (per lane), so a uniform block offset costs no vector arithmetic.
+// The resource covers the whole 32-bit range (callers stay in bounds).
+FA_DEV __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
+}
+FA_DEV void dma16_buf(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)lds_base, 16, voff, soff, 0, 0);
+}
+FA_DEV void dma4_buf(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)lds_base, 4, voff, soff, 0, 0);
+}
+
 // Fetch ROWS rows (ROWB bytes each) starting at row0 of a row-major bf16
 // matrix into a swizzled LDS tile, with the 4 waves of a workgroup.  Wave w,
 // load j fills LDS bytes [(w*LPW + j) KB, +1 KB): tile row blk*RPL + lane/CH
 // at chunk position lane%CH, i.e. logical chunk (lane%CH) ^ swz(row).  Rows at
 // or past nrows read row nrows-1 instead (finite values the caller masks).
+// The per-lane byte offsets within a tile do not depend on row0, so they are
+// computed once; a whole tile is then fetched from a uniform base address plus
+// those offsets, and only a ragged last tile takes the clamped per-row path.
 template <int ROWB, int ROWS>
-FA_DEV void dma_tile(const bf16* src, int row0, int nrows, char* dst, int wave, int lane) {
-  constexpr int CH = ROWB / 16, RPL = 1024 / ROWB, LPW = ROWS / RPL / 4;
+struct TileFetch {
+  static constexpr int CH = ROWB / 16, RPL = 1024 / ROWB, LPW = ROWS / RPL / 4;
   static_assert(LPW * RPL * 4 == ROWS, "tile must split evenly over 4 waves");
+  unsigned goff[LPW];   // byte offset of this lane's chunk from the tile's first row
+  int wave, lane;       // wave: uniform across the wave
+  FA_DEV TileFetch(int wave_, int lane_) : wave(wave_), lane(lane_) {
 #pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int blk = wave * LPW + j;
-    const int row = blk * RPL + lane / CH;
-    const int ch = (lane % CH) ^ swz<ROWB>(row);
-    const int r = min(row0 + row, nrows - 1);
-    dma16(src + (size_t)r * (ROWB / 2) + ch * 8, dst + blk * 1024);
+    for (int j = 0; j < LPW; ++j) {
+      const int row = (wave * LPW + j) * RPL + lane / CH;
+      const int ch = (lane % CH) ^ swz<ROWB>(row);
+      goff[j] = (unsigned)(row * ROWB + ch * 16);
+    }
   }
-}
+  FA_DEV void operator()(const bf16* src, int row0, int nrows, char* dst) const {
+    if (row0 + ROWS <= nrows) {
+      const __amdgpu_buffer_rsrc_t rs = raw_rsrc(src);
+      const unsigned soff = (unsigned)row0 * ROWB;
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) dma16_buf(rs, goff[j], soff, dst + (wave * LPW + j) * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const int blk = wave * LPW + j;
+        const int row = blk * RPL + lane / CH;
+        const int ch = (lane % CH) ^ swz<ROWB>(row);
+        const int r = min(row0 + row, nrows - 1);
+        dma16(src + (size_t)r * (ROWB / 2) + ch * 8, dst + blk * 1024);
+      }
+    }
+  }
+};
 
 FA_DEV bf16x8 pack8(float a0, float a1, float a2, float a3, float b0, float b1, float b2, float b3) {
   bf16x8 r;

@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const TileBases<D * 2> tb(lane);
+  const TileFetch<D * 2, BC> fetch(wave, lane);
   const int bid = blockIdx.x;
   const int head = bid % BH;
   // causal: the longest query blocks are dispatched first
@@ -90,8 +91,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const char* Kt = b ? sK1 : sK0;
     const char* Vt = b ? sV1 : sV0;
     if (j + 1 < ntiles) {
-      dma_tile<ROWB, BC>(Kh, (j + 1) * BC, N, b ? sK0 : sK1, wave, lane);
-      dma_tile<ROWB, BC>(Vh, (j + 1) * BC, N, b ? sV0 : sV1, wave, lane);
+      fetch(Kh, (j + 1) * BC, N, b ? sK0 : sK1);
+      fetch(Vh, (j + 1) * BC, N, b ? sV0 : sV1);
     }
     if (j < wave_tiles) {
       f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -168,8 +169,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     __syncthreads();
   };
 
-  dma_tile<ROWB, BC>(Kh, 0, N, sK0, wave, lane);
-  dma_tile<ROWB, BC>(Vh, 0, N, sV0, wave, lane);
+  fetch(Kh, 0, N, sK0);
+  fetch(Vh, 0, N, sV0);
   __syncthreads();
   for (int j = 0;;) {
     body(IC<0>{}, j);
