@@ -106,6 +106,27 @@ def summarize_counters(fetch_csv, write_csv, copy_mib, out_json):
     print("\n".join(rows))
 
 
+def summarize_trace(trace_csv, last):
+    """Markdown table of kernel durations (us) from a rocprofv3 kernel trace:
+    all launches, and the last `last` launches of each kernel, which are the
+    timed steps when the traced command is this script with --steps last."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(trace_csv)):
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), d))
+    print(f"| kernel | launches | avg us (all) | avg us (last {last}) | min us | max us |")
+    print("|---|---|---|---|---|---|")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        ds = [d for _, d in sorted(v)]
+        tail = ds[-last:]
+        short = name.split("(")[0].replace("void ", "")
+        if "at::native" in short:
+            short = "torch " + short.split("::")[2].split("<")[0]
+        print(f"| `{short[:70]}` | {len(ds)} | {sum(ds) / len(ds):.1f} | {sum(tail) / len(tail):.1f} | "
+              f"{min(ds):.1f} | {max(ds):.1f} |")
+
+
 def cpu_baseline(w, x, budget_s=12.0):
     """Time the fp64 oracle on whole heads of the same workload until the
     budget is spent (at least one head); credited-FLOP rate in TFLOP/s."""
@@ -136,8 +157,8 @@ def cpu_baseline(w, x, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4", help="c1..c5 (default c4, the headline shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -145,14 +166,20 @@ def main():
                          "(the calibration kernel for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
                     help="write profiles/counters_c4.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "LAST"),
+                    help="print per-kernel durations from a rocprofv3 --kernel-trace CSV: over all "
+                         "launches and over the last LAST launches (the timed steps) and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace[0], int(args.summarize_trace[1]))
+        return 0
     if args.summarize_counters:
         fcsv, wcsv, mib = args.summarize_counters
         summarize_counters(fcsv, wcsv, float(mib), COUNTERS)
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(heads are independent, see the sharding note in the design document)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported (the (batch, head) "
+              "pairs are independent, so several GPUs would each take a share of them)", file=sys.stderr)
         return 2
 
     import numpy as np
