@@ -118,12 +118,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       const int kvb = j * BC;
       const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0);
       if (need_mask) {
+        // a fence keeps this block a real branch: without it the compiler
+        // turns it into selects executed on every tile
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (kv >= N || (CAUSAL && kv > qrow)) s[mt][r] = -INFINITY;
+            const bool dead = (kv >= N) | (CAUSAL & (kv > qrow));
+            s[mt][r] = dead ? -INFINITY : s[mt][r];
           }
       }
       float mx = m_run;
@@ -132,9 +136,22 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
       mx = half_max(mx);
-      // key 0 is never masked, so every row has a finite max from its first tile
-      const float alpha = exp2_fast((m_run - mx) * c);
-      const float nb = -mx * c;
+      // The reference max m_run is moved (and O, l rescaled) only when some
+      // row of the wave gains more than 2^8 over it; otherwise the tile's
+      // probabilities are taken against the old reference, which keeps them
+      // below 2^8 and changes nothing but the rounding (O and l carry the
+      // same factor, and LSE = scale*m_run + ln l for any reference).  Key 0
+      // is never masked, so the first tile always sets a finite reference.
+      if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 8.f) != 0) {
+        const float alpha = exp2_fast((m_run - mx) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+        m_run = mx;
+      }
+      const float nb = -m_run * c;
       float rs = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -144,14 +161,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
           s[mt][r] = p;
           rs += p;
         }
-      l_run = fmaf(l_run, alpha, rs);
-      m_run = mx;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-      }
+      l_run += rs;
       // P^T as B operand, K-step st covers keys 16*st .. 16*st+15 of the tile:
       // registers 0..3 <- keys 16st+4h+jj, 4..7 <- keys 16st+8+4h+jj
 #pragma unroll
