@@ -119,15 +119,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         }
 #pragma unroll
         for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        // register r: key kvb + 32*mt + 8*(r/4) + 4*h + r%4, query qrow
+        // register r: key kvb + 32*mt + 8*(r/4) + 4*h + r%4, query qrow.
+        // Masked scores become -inf (P^ = 0).  The fence keeps this one
+        // uniform branch: without it the compiler splits the test per element.
+        if (need_mask) {
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = exp2_fast(fmaf(s[r], c, nl2));
-          if (need_mask) {
+          for (int r = 0; r < 16; ++r) {
             const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
             const bool dead = (kv >= N) | (qrow >= N) | (CAUSAL & (kv > qrow));
-            p = dead ? 0.f : p;
+            s[r] = dead ? -INFINITY : s[r];
           }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_fast(fmaf(s[r], c, nl2));
           dp[r] = p * (dp[r] + ndrow);
         }
         // dS^T as B operand; K-step st = 2*mt + half covers keys 16*st ..
