@@ -35,6 +35,7 @@ KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["fa_fwd_bf16.hip", "fa_common.h"],
     "bwd_bf16_kernel": ["fa_bwd_bf16.hip", "fa_common.h"],
     "bwd_dq_kernel": ["fa_bwd_dq.hip", "fa_common.h"],
+    "bwd_pre_kernel": ["fa_aux.hip", "fa_common.h"],
 }
 
 
@@ -129,8 +130,8 @@ def summarize_trace(trace_csv, last):
 
 def cpu_baseline(w, x, budget_s=12.0):
     """Time the fp64 oracle on whole heads of the same workload until the
-    budget is spent (at least one head); credited-FLOP rate in TFLOP/s."""
-    import numpy as np
+    budget is spent (at least one head); credited-FLOP rate in TFLOP/s.
+    Also returns the heads done and the oracle's results for them."""
     from oracle import ref
     try:
         from threadpoolctl import threadpool_info
@@ -141,17 +142,46 @@ def cpu_baseline(w, x, budget_s=12.0):
     per_head = (fwd1 + bwd1) / (w.B * w.H)
     done, t0 = 0, time.perf_counter()
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    results = {}
     while done < len(heads):
         b, h = heads[done]
-        ref.forward_backward(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal, heads=[(b, h)])
+        results.update(ref.forward_backward(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal,
+                                            heads=[(b, h)]))
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(per_head * done / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+    base = {"value": round(per_head * done / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{done} of {len(heads)} heads of the same workload (B=1,H=1,N={w.N},d={w.d}, "
                       f"causal={w.causal}), fp64 materialised fwd+bwd, {dt:.1f} s"}
+    return base, heads[:done], results
+
+
+# the parity bar of the test suite: fp32 max-abs 1e-4; bf16 max-abs 2e-2 * max|ref|
+# (max|ref| taken as at least 1e-2); LSE max-abs 1e-3
+def oracle_check(w, heads, want, got):
+    """Max errors of the timed run's outputs against the oracle on the heads
+    the CPU baseline computed, and whether they meet the parity bar."""
+    import numpy as np
+    errs, ok = {}, True
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        worst = 0.0
+        for (b, h) in heads:
+            g = got[n][b, h].float().cpu().numpy().astype(np.float64)
+            r = want[(b, h)][n]
+            err = float(np.abs(g - r).max())
+            if n == "lse":
+                tol = 1e-3
+            elif w.dtype == "fp32":
+                tol = 1e-4
+            else:
+                tol = 2e-2 * max(1e-2, float(np.abs(r).max()))
+            ok = ok and err <= tol
+            worst = max(worst, err / tol)
+        errs[n] = round(worst, 4)
+    return {"heads": len(heads), "first_head": list(heads[0]), "last_head": list(heads[-1]),
+            "max_err_over_tolerance": errs, "within_tolerance": ok}
 
 
 def main():
@@ -161,6 +191,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4", help="c1..c5 (default c4, the headline shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write a scratch buffer of this many MiB between timed steps (untimed), so "
+                         "that the 256 MB last-level cache holds no inputs; the step time is then the "
+                         "sum of the per-step event intervals instead of the bracketing wall clock")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(the calibration kernel for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -225,16 +259,23 @@ def main():
         if ev is not None:
             ev[4].record(stream)
 
+    scratch = torch.empty(args.flush_mib * (1 << 20), dtype=torch.uint8, device=dev) if args.flush_mib else None
     for _ in range(args.warmup):
         step()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
         step(events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    step_ms = sorted(e[0].elapsed_time(e[4]) for e in events)
+    if scratch is None:
+        ms_step = (t1 - t0) * 1e3 / args.steps
+    else:
+        ms_step = sum(step_ms) / len(step_ms)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2
@@ -267,6 +308,8 @@ def main():
     T = B * H * N * d
     pre_bytes = 2 * T * elem + 12 * B * H * N
     traffic = traffic_from_counters(dom) if (args.workload == "c4" and not atomic) else None
+    pre_traffic = traffic_from_counters("bwd_pre_kernel") if args.workload == "c4" else None
+    props = torch.cuda.get_device_properties(0)
 
     out = {
         "metric": METRIC,
@@ -295,12 +338,24 @@ def main():
             "fwd_frac_peak": round(fwd_fl / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "bwd_frac_peak": round(bwd_fl / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "kernel_tflops": {k: round(f / (t * 1e-3) / 1e12, 3) for k, (t, f) in kernels.items()},
-            "preprocess_gbs": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
+            "preprocess_roofline": {"kernel": "bwd_pre_kernel", "bound": "hbm",
+                                    "achieved": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
+                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(pre_bytes / (pre_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                    "traffic": pre_traffic},
+            "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
+            "step_ms_min": round(step_ms[0], 4),
+            "flush_mib": args.flush_mib,
             "gpu": torch.cuda.get_device_name(0),
+            "compute_units": props.multi_processor_count,
+            "peak_from_cus_at_2p4ghz": round(props.multi_processor_count * 4096 * 2.4e9 / 1e12, 1),
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x)
+        base, heads, ref = cpu_baseline(w, x)
+        out["cpu_baseline"] = base
+        out["detail"]["oracle_check"] = oracle_check(w, heads, ref, {"o": o, "lse": lse, "dq": dq,
+                                                                    "dk": dk, "dv": dv})
     print(json.dumps(out), flush=True)
     return 0
 
