@@ -23,7 +23,7 @@
 // the conversion kernel.
 //
 // Pipelining: Q/dO/LSE/D of the next query block are fetched straight into
-// the other LDS buffer (global_load_lds) while the current block is used; the
+// the other LDS buffer (buffer loads into LDS) while the current block is used; the
 // dQ product of a block runs at the start of the next iteration so that its
 // atomics drain under the next block's products; one barrier per block.  The
 // loop body is instantiated per buffer so that every LDS buffer is a distinct
@@ -172,8 +172,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
         if (wave_u == 0) dma4_buf(raw_rsrc(Lh), 4 * lane, 4 * qb0, dL);
         if (wave_u == 1) dma4_buf(raw_rsrc(Dh), 4 * lane, 4 * qb0, dD);
       } else {
-        if (wave_u == 0) dma4(Lh + min(qb0 + lane, N - 1), dL);
-        if (wave_u == 1) dma4(Dh + min(qb0 + lane, N - 1), dD);
+        if (wave_u == 0) dma4_buf(raw_rsrc(Lh), 4 * min(qb0 + lane, N - 1), 0, dL);
+        if (wave_u == 1) dma4_buf(raw_rsrc(Dh), 4 * min(qb0 + lane, N - 1), 0, dD);
       }
     };
 
@@ -243,32 +243,40 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
         // P^T and dS^T as A operands (lane = key row); K-step st covers queries
         // 16st..16st+15: registers 0..3 <- 16st+4h+jj, 4..7 <- 16st+8+4h+jj.
         bf16x8 pa[BR / 16], da[BR / 16];
-        // Four phases separated by scheduling fences; each pairs products with
-        // vector work that does not depend on them:
-        //   A: S, dP of query tile 0
-        //   B: S, dP of query tile 1   | exponentials of tile 0
-        //   C: dV, dK of tile 0        | exponentials of tile 1
-        //   D: dV, dK of tile 1
-        // The first operands of a phase are read at the end of the one before.
+        // Software pipeline over the step's 32 operand groups, in this order:
+        //   g = 0..7    S, dP of query tile 0, K-step g
+        //   g = 8..15   S, dP of tile 1          | exponentials of tile 0
+        //   g = 16..23  dV, dK of tile 0, j = g-16 | exponentials of tile 1
+        //   g = 24..31  dV, dK of tile 1
+        // Slot g issues the LDS reads of group g + DIST, then the two products
+        // of group g, then its share of the vector work; scheduling fences
+        // between slots keep this order, so each product waits only for reads
+        // issued DIST slots earlier (LDS returns in order).
         // The S and dP accumulators start from -LSE/scale and -D of their
         // query rows, so they end as S - LSE/scale and dP - D.
+#ifndef FA_KV_DIST
+#define FA_KV_DIST 3
+#endif
+        constexpr int DIST = FA_KV_DIST;   // slots between an LDS read and its use
+        constexpr int NG = 4 * KS;                 // groups per step (KS = 2*DT)
         f32x16 s[2], dp[2];
-        bf16x8 qa[2][KS], ga[2][KS];
-        bf16x8 tq[2][2 * DT], tg[2][2 * DT];
-        auto rd_s = [&](int t, int ks) {
-          const int off = tb.nat_off(t, ks);
-          qa[t][ks] = lds_read_b128(Qt, off);
-          ga[t][ks] = lds_read_b128(Gt, off);
+        bf16x8 qa[2][KS], ga[2][KS];               // S/dP operands (Q, dO rows)
+        bf16x8 tq[2][2 * DT], tg[2][2 * DT];       // dV/dK operands (transposed)
+        auto read_group = [&](int g) {
+          if (g < 2 * KS) {
+            const int t = g / KS, ks = g % KS;
+            const int off = tb.nat_off(t, ks);
+            qa[t][ks] = lds_read_b128(Qt, off);
+            ga[t][ks] = lds_read_b128(Gt, off);
+          } else {
+            const int t = (g - 2 * KS) / (2 * DT), j = (g - 2 * KS) % (2 * DT);
+            const int st = 2 * t + j / DT, dt = j % DT;
+            const int o0 = tb.tr_off(st, dt, 0), o1 = tb.tr_off(st, dt, 1);
+            tg[t][j] = cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1));
+            tq[t][j] = cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1));
+          }
         };
-        auto rd_t = [&](int t, int j) {   // j = sx*DT + dt
-          const int st = 2 * t + j / DT, dt = j % DT;
-          const int o0 = tb.tr_off(st, dt, 0), o1 = tb.tr_off(st, dt, 1);
-          tg[t][j] = cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1));
-          tq[t][j] = cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1));
-        };
-        // S = Q_i K_w^T - LSE/scale, dP = dO_i V_w^T - D; register r: query
-        // qb0 + 32t + 8*(r/4) + 4h + r%4, key kvrow
-        auto sdp = [&](int t, int ks_pre) {
+        auto init_acc = [&](int t) {   // register r: query qb0 + 32t + 8*(r/4) + 4h + r%4
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4) {
             const int ql = 32 * t + 8 * i4 + 4 * h;
@@ -280,17 +288,26 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
               dp[t][4 * i4 + jj] = d4[jj];
             }
           }
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            if (ks >= ks_pre) rd_s(t, ks);
+        };
+        auto products = [&](int g) {
+          if (g < 2 * KS) {   // S = Q_i K_w^T - LSE/scale, dP = dO_i V_w^T - D
+            const int t = g / KS, ks = g % KS;
             s[t] = mfma32(qa[t][ks], kf[ks], s[t]);
             dp[t] = mfma32(ga[t][ks], vf[ks], dp[t]);
+          } else {            // dV += P^T dO, dK += dS^T Q
+            const int t = (g - 2 * KS) / (2 * DT), j = (g - 2 * KS) % (2 * DT);
+            const int st = 2 * t + j / DT, dt = j % DT;
+            dv[dt] = mfma32(pa[st], tg[t][j], dv[dt]);
+            dk[dt] = mfma32(da[st], tq[t][j], dk[dt]);
           }
         };
-        // P^ = 2^(c (S - LSE/scale)), dS = P^ o (dP - D), both to bf16
-        auto elem = [&](int t) {
+        // P^ = 2^(c (S - LSE/scale)), dS = P^ o (dP - D) for the RPC registers
+        // of chunk ch of tile t (one chunk per slot of a phase); the bf16
+        // operands are packed once registers 0..7 and 8..15 are done
+        constexpr int RPC = 16 / KS;
+        auto elem_chunk = [&](int t, int ch) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
+          for (int r = RPC * ch; r < RPC * ch + RPC; ++r) {
             float p = exp2_fast(s[t][r] * c);
             if constexpr (MASK) {
               const int q = qb0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -300,57 +317,28 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
             s[t][r] = p;
             dp[t][r] = p * dp[t][r];
           }
-          pa[2 * t] = pack8(s[t][0], s[t][1], s[t][2], s[t][3], s[t][4], s[t][5], s[t][6], s[t][7]);
-          pa[2 * t + 1] = pack8(s[t][8], s[t][9], s[t][10], s[t][11], s[t][12], s[t][13], s[t][14], s[t][15]);
-          da[2 * t] = pack8(dp[t][0], dp[t][1], dp[t][2], dp[t][3], dp[t][4], dp[t][5], dp[t][6], dp[t][7]);
-          da[2 * t + 1] = pack8(dp[t][8], dp[t][9], dp[t][10], dp[t][11], dp[t][12], dp[t][13], dp[t][14], dp[t][15]);
-        };
-        // dV += P^T dO, dK += dS^T Q; B = dO / Q rows through transposing reads
-        auto dvdk = [&](int t, int j_pre) {
-#pragma unroll
-          for (int j = 0; j < 2 * DT; ++j) {
-            if (j >= j_pre) rd_t(t, j);
-            const int st = 2 * t + j / DT, dt = j % DT;
-            dv[dt] = mfma32(pa[st], tg[t][j], dv[dt]);
-            dk[dt] = mfma32(da[st], tq[t][j], dk[dt]);
+          if ((RPC * ch + RPC) % 8 == 0) {
+            const int hi = (RPC * ch + RPC) / 8 - 1, o = 8 * hi;
+            pa[2 * t + hi] = pack8(s[t][o], s[t][o + 1], s[t][o + 2], s[t][o + 3],
+                                   s[t][o + 4], s[t][o + 5], s[t][o + 6], s[t][o + 7]);
+            da[2 * t + hi] = pack8(dp[t][o], dp[t][o + 1], dp[t][o + 2], dp[t][o + 3],
+                                   dp[t][o + 4], dp[t][o + 5], dp[t][o + 6], dp[t][o + 7]);
           }
         };
-        constexpr int PRE = 2;   // operand pairs read ahead into the next phase
-        constexpr int VPM = 6;   // vector instructions per product in phases B, C
-        // ---- A
+        init_acc(0);
 #pragma unroll
-        for (int ks = 0; ks < PRE; ++ks) rd_s(0, ks);
-        sdp(0, PRE);
+        for (int g = 0; g < DIST; ++g) read_group(g);
+        init_acc(1);
 #pragma unroll
-        for (int ks = 0; ks < PRE; ++ks) rd_s(1, ks);
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- B
-        sdp(1, PRE);
-        elem(0);
-#pragma unroll
-        for (int j = 0; j < PRE; ++j) rd_t(0, j);
-#pragma unroll
-        for (int i_ = 0; i_ < 2 * KS; ++i_) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0); // VALU
+        for (int g = 0; g < NG; ++g) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (g + DIST < NG) read_group(g + DIST);
+          products(g);
+          if (g >= KS && g < 2 * KS) elem_chunk(0, g - KS);
+          if (g >= 2 * KS && g < 3 * KS) elem_chunk(1, g - 2 * KS);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // ---- C
-        dvdk(0, PRE);
-        elem(1);
-#pragma unroll
-        for (int j = 0; j < PRE; ++j) rd_t(1, j);
-#pragma unroll
-        for (int i_ = 0; i_ < 4 * DT; ++i_) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // ---- D
-        dvdk(1, PRE);
-        // dS (bf16) to LDS, [key][query]
+        // dS (bf16) to LDS, [key][query], for the dQ product of the atomic variant
         if constexpr (DQA) {
 #pragma unroll
           for (int st = 0; st < BR / 16; ++st) {

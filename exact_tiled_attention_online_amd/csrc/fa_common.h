@@ -148,19 +148,13 @@ struct TileBases {
 template <int B>
 using IC = std::integral_constant<int, B>;
 
-// Wave-wide direct fetch global -> LDS: lane l's 16 (or 4) bytes land at
-// lds_base + 16*l (or 4*l); lds_base must be the same for the whole wave.
-FA_DEV void dma16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (FA_LDS void*)lds_base, 16, 0, 0);
-}
-FA_DEV void dma4(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
-                                   (FA_LDS void*)lds_base, 4, 0, 0);
-}
-
-// The same through a buffer resource: byte address = base + soffset (uniform)
-// + voffset (per lane), so a uniform block offset costs no vector arithmetic.
+// Wave-wide direct fetch global -> LDS through a buffer resource: lane l's 16
+// (or 4) bytes, read from base + soffset (uniform) + voffset (per lane), land
+// at lds_base + 16*l (or 4*l); lds_base must be the same for the whole wave.
+// A uniform block offset thus costs no vector arithmetic.  Only the buffer
+// (MUBUF) form is used: the compiler treats a pending global_load_lds (a FLAT
+// instruction) as possibly out of order with LDS reads and then waits for
+// every outstanding LDS read at each use, which defeats reading operands ahead.
 // The resource covers the whole 32-bit range (callers stay in bounds).
 FA_DEV __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000);
@@ -207,7 +201,7 @@ struct TileFetch {
         const int row = blk * RPL + lane / CH;
         const int ch = (lane % CH) ^ swz<ROWB>(row);
         const int r = min(row0 + row, nrows - 1);
-        dma16(src + (size_t)r * (ROWB / 2) + ch * 8, dst + blk * 1024);
+        dma16_buf(raw_rsrc(src), (unsigned)(r * ROWB + ch * 16), 0, dst + blk * 1024);
       }
     }
   }
