@@ -99,59 +99,77 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     if (j < wave_tiles) {
       const int kvb = j * BC;
       const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0) || (q0 + 32 > N);
-      // the tile's two 32-key halves one after the other (fewer live registers)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = tb.nat_off(mt, ks);
-          s = mfma32(lds_read_b128(Kt, off), qf[ks], s);
-          dp = mfma32(lds_read_b128(Vt, off), gf[ks], dp);
+      // The tile's two 32-key halves one after the other (fewer live
+      // registers), each as: S, dP products (KS slots of two products), the
+      // exponentials, the dQ products (2*DT slots of one product).  Slot i
+      // issues the LDS reads of slot i + DIST before its products, with
+      // scheduling fences between slots, so each product waits only for reads
+      // issued DIST slots earlier (LDS returns in order).
+      constexpr int DIST = 3;
+      constexpr int SPM = KS + 2 * DT;    // slots per 32-key half
+      constexpr int NSL = 2 * SPM;
+      bf16x8 ka[KS], va[KS], kt[2 * DT];
+      auto read_slot = [&](int i) {
+        const int mt = i / SPM, k = i % SPM;
+        if (k < KS) {
+          const int off = tb.nat_off(mt, k);
+          ka[k] = lds_read_b128(Kt, off);
+          va[k] = lds_read_b128(Vt, off);
+        } else {
+          const int u = k - KS, half = u / DT, t = u % DT;
+          const int st = 2 * mt + half;
+          kt[u] = cat(lds_read_tr(Kt, tb.tr_off(st, t, 0)), lds_read_tr(Kt, tb.tr_off(st, t, 1)));
         }
-        // keep four operand reads in flight ahead of the products
+      };
+      f32x16 s, dp;
+      bf16x8 db[2];
 #pragma unroll
-        for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < DIST; ++i) read_slot(i);
 #pragma unroll
-        for (int i_ = 0; i_ < 12; ++i_) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        // register r: key kvb + 32*mt + 8*(r/4) + 4*h + r%4, query qrow.
-        // Masked scores become -inf (P^ = 0).  The fence keeps this one
-        // uniform branch: without it the compiler splits the test per element.
-        if (need_mask) {
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-            const bool dead = (kv >= N) | (qrow >= N) | (CAUSAL & (kv > qrow));
-            s[r] = dead ? -INFINITY : s[r];
+      for (int i = 0; i < NSL; ++i) {
+        const int mt = i / SPM, k = i % SPM;
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + DIST < NSL) read_slot(i + DIST);
+        if (k < KS) {
+          if (k == 0) {
+            s = f32x16{};
+            dp = f32x16{};
           }
-        }
+          s = mfma32(ka[k], qf[k], s);
+          dp = mfma32(va[k], gf[k], dp);
+          if (k == KS - 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            // register r: key kvb + 32*mt + 8*(r/4) + 4*h + r%4, query qrow.
+            // Masked scores become -inf (P^ = 0), behind one uniform branch.
+            if (need_mask) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(fmaf(s[r], c, nl2));
-          dp[r] = p * (dp[r] + ndrow);
-        }
-        // dS^T as B operand; K-step st = 2*mt + half covers keys 16*st ..
-        // 16*st+15 of the tile: registers 0..3 <- keys 16st+4h+jj, 4..7 <-
-        // keys 16st+8+4h+jj
+              for (int r = 0; r < 16; ++r) {
+                const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+                const bool dead = (kv >= N) | (qrow >= N) | (CAUSAL & (kv > qrow));
+                s[r] = dead ? -INFINITY : s[r];
+              }
+            }
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int i0 = 2 * half;
-          const bf16x8 db = pack8(dp[4 * i0 + 0], dp[4 * i0 + 1], dp[4 * i0 + 2], dp[4 * i0 + 3],
-                                  dp[4 * i0 + 4], dp[4 * i0 + 5], dp[4 * i0 + 6], dp[4 * i0 + 7]);
+            for (int r = 0; r < 16; ++r) {
+              const float p = exp2_fast(fmaf(s[r], c, nl2));
+              dp[r] = p * (dp[r] + ndrow);
+            }
+            // dS^T as B operand; K-step st = 2*mt + half covers keys 16*st ..
+            // 16*st+15 of the tile: registers 0..3 <- keys 16st+4h+jj, 4..7 <-
+            // keys 16st+8+4h+jj
 #pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            const int st = 2 * mt + half;
-            const bf16x8 a = cat(lds_read_tr(Kt, tb.tr_off(st, t, 0)), lds_read_tr(Kt, tb.tr_off(st, t, 1)));
-            acc[t] = mfma32(a, db, acc[t]);
+            for (int half = 0; half < 2; ++half) {
+              const int i0 = 2 * half;
+              db[half] = pack8(dp[4 * i0 + 0], dp[4 * i0 + 1], dp[4 * i0 + 2], dp[4 * i0 + 3],
+                               dp[4 * i0 + 4], dp[4 * i0 + 5], dp[4 * i0 + 6], dp[4 * i0 + 7]);
+            }
           }
+        } else {
+          const int u = k - KS, half = u / DT, t = u % DT;
+          acc[t] = mfma32(kt[u], db[half], acc[t]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   };

@@ -95,86 +95,96 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       fetch(Vh, (j + 1) * BC, N, b ? sV0 : sV1);
     }
     if (j < wave_tiles) {
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+      // Slots: KS slots of S products (two 32-key halves per K-step), then
+      // the softmax, then (BC/16)*DT slots of P V products.  Slot i issues the
+      // LDS reads of slot i + DIST before its products, with scheduling fences
+      // between slots, so each product waits only for reads issued DIST slots
+      // earlier (LDS returns in order).
+      constexpr int DIST = 3;
+      constexpr int NPV = (BC / 16) * DT;
+      constexpr int NSL = KS + NPV;
+      bf16x8 ka[KS][2], vt[NPV];
+      auto read_slot = [&](int i) {
+        if (i < KS) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 a = lds_read_b128(Kt, tb.nat_off(mt, ks));
-          s[mt] = mfma32(a, qf[ks], s[mt]);
+          for (int mt = 0; mt < 2; ++mt) ka[i][mt] = lds_read_b128(Kt, tb.nat_off(mt, i));
+        } else {
+          const int u = i - KS, st = u / DT, t = u % DT;
+          vt[u] = cat(lds_read_tr(Vt, tb.tr_off(st, t, 0)), lds_read_tr(Vt, tb.tr_off(st, t, 1)));
         }
-      }
-      // keep four operand reads in flight ahead of the products
-#pragma unroll
-      for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-      for (int i_ = 0; i_ < 12; ++i_) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-#pragma unroll
-      for (int i_ = 0; i_ < 4; ++i_) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      // s[mt][4*i+jj] = q_qrow . k_kv with kv = j*BC + 32*mt + 8*i + 4*h + jj
+      };
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      bf16x8 pb[BC / 16];
       const int kvb = j * BC;
-      const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0);
-      if (need_mask) {
-        // a fence keeps this block a real branch: without it the compiler
-        // turns it into selects executed on every tile
+#pragma unroll
+      for (int i = 0; i < DIST; ++i) read_slot(i);
+#pragma unroll
+      for (int i = 0; i < NSL; ++i) {
         __builtin_amdgcn_sched_barrier(0);
+        if (i + DIST < NSL) read_slot(i + DIST);
+        if (i < KS) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) s[mt] = mfma32(ka[i][mt], qf[i], s[mt]);
+        } else {
+          const int u = i - KS, st = u / DT, t = u % DT;
+          oacc[t] = mfma32(vt[u], pb[st], oacc[t]);
+        }
+        if (i != KS - 1) continue;
+        __builtin_amdgcn_sched_barrier(0);
+        // s[mt][4*i+jj] = q_qrow . k_kv with kv = j*BC + 32*mt + 8*i + 4*h + jj
+        const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0);
+        if (need_mask) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+              const bool dead = (kv >= N) | (CAUSAL & (kv > qrow));
+              s[mt][r] = dead ? -INFINITY : s[mt][r];
+            }
+        }
+        float mx = m_run;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+        mx = half_max(mx);
+        // The reference max m_run is moved (and O, l rescaled) only when some
+        // row of the wave gains more than 2^8 over it; otherwise the tile's
+        // probabilities are taken against the old reference, which keeps them
+        // below 2^8 and changes nothing but the rounding (O and l carry the
+        // same factor, and LSE = scale*m_run + ln l for any reference).  Key 0
+        // is never masked, so the first tile always sets a finite reference.
+        if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 8.f) != 0) {
+          const float alpha = exp2_fast((m_run - mx) * c);
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+          m_run = mx;
+        }
+        const float nb = -m_run * c;
+        float rs = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-            const bool dead = (kv >= N) | (CAUSAL & (kv > qrow));
-            s[mt][r] = dead ? -INFINITY : s[mt][r];
+            const float p = exp2_fast(fmaf(s[mt][r], c, nb));
+            s[mt][r] = p;
+            rs += p;
           }
-      }
-      float mx = m_run;
+        l_run += rs;
+        // P^T as B operand, K-step st covers keys 16*st .. 16*st+15 of the
+        // tile: registers 0..3 <- keys 16st+4h+jj, 4..7 <- keys 16st+8+4h+jj
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-      mx = half_max(mx);
-      // The reference max m_run is moved (and O, l rescaled) only when some
-      // row of the wave gains more than 2^8 over it; otherwise the tile's
-      // probabilities are taken against the old reference, which keeps them
-      // below 2^8 and changes nothing but the rounding (O and l carry the
-      // same factor, and LSE = scale*m_run + ln l for any reference).  Key 0
-      // is never masked, so the first tile always sets a finite reference.
-      if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 8.f) != 0) {
-        const float alpha = exp2_fast((m_run - mx) * c);
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < DT; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-        m_run = mx;
-      }
-      const float nb = -m_run * c;
-      float rs = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(fmaf(s[mt][r], c, nb));
-          s[mt][r] = p;
-          rs += p;
-        }
-      l_run += rs;
-      // P^T as B operand, K-step st covers keys 16*st .. 16*st+15 of the tile:
-      // registers 0..3 <- keys 16st+4h+jj, 4..7 <- keys 16st+8+4h+jj
-#pragma unroll
-      for (int st = 0; st < BC / 16; ++st) {
-        const int mt = st >> 1, i0 = 2 * (st & 1);
-        const bf16x8 pb = pack8(s[mt][4 * i0 + 0], s[mt][4 * i0 + 1], s[mt][4 * i0 + 2], s[mt][4 * i0 + 3],
-                                s[mt][4 * i0 + 4], s[mt][4 * i0 + 5], s[mt][4 * i0 + 6], s[mt][4 * i0 + 7]);
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          const bf16x8 a = cat(lds_read_tr(Vt, tb.tr_off(st, t, 0)), lds_read_tr(Vt, tb.tr_off(st, t, 1)));
-          oacc[t] = mfma32(a, pb, oacc[t]);
+        for (int st = 0; st < BC / 16; ++st) {
+          const int mt = st >> 1, i0 = 2 * (st & 1);
+          pb[st] = pack8(s[mt][4 * i0 + 0], s[mt][4 * i0 + 1], s[mt][4 * i0 + 2], s[mt][4 * i0 + 3],
+                         s[mt][4 * i0 + 4], s[mt][4 * i0 + 5], s[mt][4 * i0 + 6], s[mt][4 * i0 + 7]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
   };
