@@ -105,7 +105,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       // issues the LDS reads of slot i + DIST before its products, with
       // scheduling fences between slots, so each product waits only for reads
       // issued DIST slots earlier (LDS returns in order).
-      constexpr int DIST = 3;
+#ifndef FA_DQ_DIST
+#define FA_DQ_DIST 3
+#endif
+      constexpr int DIST = FA_DQ_DIST;   // slots between an LDS read and its use
       constexpr int SPM = KS + 2 * DT;    // slots per 32-key half
       constexpr int NSL = 2 * SPM;
       bf16x8 ka[KS], va[KS], kt[2 * DT];

@@ -100,7 +100,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       // LDS reads of slot i + DIST before its products, with scheduling fences
       // between slots, so each product waits only for reads issued DIST slots
       // earlier (LDS returns in order).
-      constexpr int DIST = 3;
+#ifndef FA_FWD_DIST
+#define FA_FWD_DIST 3
+#endif
+      constexpr int DIST = FA_FWD_DIST;   // slots between an LDS read and its use
       constexpr int NPV = (BC / 16) * DT;
       constexpr int NSL = KS + NPV;
       bf16x8 ka[KS][2], vt[NPV];
