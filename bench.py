@@ -277,6 +277,24 @@ def main():
     else:
         ms_step = sum(step_ms) / len(step_ms)
 
+    # calibration: a vendor-library bf16 GEMM of 8192^3 on the same device
+    # (hipBLASLt through torch), the practical dense-MFMA rate of this part
+    # under its power limit, reported beside the nominal peak
+    gemm_tflops = None
+    if dtype == torch.bfloat16:
+        ga = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+        gb = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+        for _ in range(5):
+            gc = ga @ gb
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(20):
+            gc = ga @ gb
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gemm_tflops = 2 * 8192 ** 3 / (g0.elapsed_time(g1) / 20 * 1e-3) / 1e12
+        del ga, gb, gc
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2
         src = torch.ones(n, dtype=torch.bfloat16, device=dev)
@@ -348,6 +366,8 @@ def main():
             "flush_mib": args.flush_mib,
             "gpu": torch.cuda.get_device_name(0),
             "compute_units": props.multi_processor_count,
+            "vendor_gemm_bf16_tflops": round(gemm_tflops, 1) if gemm_tflops else None,
+            "dominant_kernel_frac_of_vendor_gemm": round(achieved / gemm_tflops, 4) if gemm_tflops else None,
             "peak_from_cus_at_2p4ghz": round(props.multi_processor_count * 4096 * 2.4e9 / 1e12, 1),
         },
     }
