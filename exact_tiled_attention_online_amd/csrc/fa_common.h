@@ -167,17 +167,17 @@ FA_DEV void dma4_buf(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, vo
 }
 
 // Fetch ROWS rows (ROWB bytes each) starting at row0 of a row-major bf16
-// matrix into a swizzled LDS tile, with the 4 waves of a workgroup.  Wave w,
+// matrix into a swizzled LDS tile, with the NW waves of a workgroup.  Wave w,
 // load j fills LDS bytes [(w*LPW + j) KB, +1 KB): tile row blk*RPL + lane/CH
 // at chunk position lane%CH, i.e. logical chunk (lane%CH) ^ swz(row).  Rows at
 // or past nrows read row nrows-1 instead (finite values the caller masks).
 // The per-lane byte offsets within a tile do not depend on row0, so they are
 // computed once; a whole tile is then fetched from a uniform base address plus
 // those offsets, and only a ragged last tile takes the clamped per-row path.
-template <int ROWB, int ROWS>
+template <int ROWB, int ROWS, int NW = 4>
 struct TileFetch {
-  static constexpr int CH = ROWB / 16, RPL = 1024 / ROWB, LPW = ROWS / RPL / 4;
-  static_assert(LPW * RPL * 4 == ROWS, "tile must split evenly over 4 waves");
+  static constexpr int CH = ROWB / 16, RPL = 1024 / ROWB, LPW = ROWS / RPL / NW;
+  static_assert(LPW * RPL * NW == ROWS, "tile must split evenly over the waves");
   unsigned goff[LPW];   // byte offset of this lane's chunk from the tile's first row
   int wave, lane;       // wave: uniform across the wave
   FA_DEV TileFetch(int wave_, int lane_) : wave(wave_), lane(lane_) {

@@ -24,11 +24,14 @@
 
 namespace fa {
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+#ifndef FA_FWD_NW
+#define FA_FWD_NW 8
+#endif
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c) {
-  constexpr int BR = 128, BC = 64;
+  constexpr int BR = 32 * NW, BC = 64;
   constexpr int ROWB = D * 2;        // bytes per row
   constexpr int KS = D / 16;         // K-steps of the S product
   constexpr int DT = D / 32;         // 32-row tiles of O^T
@@ -44,7 +47,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const TileBases<D * 2> tb(lane);
-  const TileFetch<D * 2, BC> fetch(wave, lane);
+  const TileFetch<D * 2, BC, NW> fetch(wave, lane);
   const int bid = blockIdx.x;
   const int head = bid % BH;
   // causal: the longest query blocks are dispatched first
@@ -225,9 +228,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse,
                                     int BH, int N, float scale, hipStream_t stream) {
-  const int nqb = (N + 127) / 128;
-  const dim3 grid((unsigned)(nqb * BH)), block(256);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), grid, block, 0, stream,
+  constexpr int NW = FA_FWD_NW, BR = 32 * NW;
+  const int nqb = (N + BR - 1) / BR;
+  const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), grid, block, 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
                      scale * kLog2e);
   return hipGetLastError();
