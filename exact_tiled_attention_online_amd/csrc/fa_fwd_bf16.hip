@@ -31,7 +31,12 @@ template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c) {
-  constexpr int BR = 32 * NW, BC = 64;
+#ifndef FA_FWD_BC64
+#define FA_FWD_BC64 128
+#endif
+  // key rows per tile: 128 where the registers allow it (d = 64), else 64
+  constexpr int BR = 32 * NW, BC = D == 64 ? FA_FWD_BC64 : 64;
+  constexpr int MT = BC / 32;        // 32-key halves of a tile
   constexpr int ROWB = D * 2;        // bytes per row
   constexpr int KS = D / 16;         // K-steps of the S product
   constexpr int DT = D / 32;         // 32-row tiles of O^T
@@ -109,28 +114,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
       constexpr int DIST = FA_FWD_DIST;   // slots between an LDS read and its use
       constexpr int NPV = (BC / 16) * DT;
       constexpr int NSL = KS + NPV;
-      bf16x8 ka[KS][2], vt[NPV];
+      bf16x8 ka[KS][MT], vt[NPV];
       auto read_slot = [&](int i) {
         if (i < KS) {
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) ka[i][mt] = lds_read_b128(Kt, tb.nat_off(mt, i));
+          for (int mt = 0; mt < MT; ++mt) ka[i][mt] = lds_read_b128(Kt, tb.nat_off(mt, i));
         } else {
           const int u = i - KS, st = u / DT, t = u % DT;
           vt[u] = cat(lds_read_tr(Vt, tb.tr_off(st, t, 0)), lds_read_tr(Vt, tb.tr_off(st, t, 1)));
         }
       };
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+      f32x16 s[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
       bf16x8 pb[BC / 16];
       const int kvb = j * BC;
 #pragma unroll
       for (int i = 0; i < DIST; ++i) read_slot(i);
-#pragma unroll
+#pragma clang loop unroll(full)
       for (int i = 0; i < NSL; ++i) {
         __builtin_amdgcn_sched_barrier(0);
         if (i + DIST < NSL) read_slot(i + DIST);
         if (i < KS) {
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) s[mt] = mfma32(ka[i][mt], qf[i], s[mt]);
+          for (int mt = 0; mt < MT; ++mt) s[mt] = mfma32(ka[i][mt], qf[i], s[mt]);
         } else {
           const int u = i - KS, st = u / DT, t = u % DT;
           oacc[t] = mfma32(vt[u], pb[st], oacc[t]);
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
         const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0);
         if (need_mask) {
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -151,7 +158,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
         }
         float mx = m_run;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
         mx = half_max(mx);
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
         const float nb = -m_run * c;
         float rs = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float p = exp2_fast(fmaf(s[mt][r], c, nb));
