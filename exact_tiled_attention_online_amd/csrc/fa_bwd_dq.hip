@@ -21,12 +21,15 @@
 
 namespace fa {
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
+#ifndef FA_DQ_NW
+#define FA_DQ_NW 8
+#endif
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
     bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c) {
-  constexpr int BR = 128, BC = 64;
+  constexpr int BR = 32 * NW, BC = 64;
   constexpr int ROWB = D * 2;        // bytes per row
   constexpr int KS = D / 16;         // K-steps of the S and dP products
   constexpr int DT = D / 32;         // 32-row tiles of dQ^T
@@ -42,7 +45,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const TileBases<D * 2> tb(lane);
-  const TileFetch<D * 2, BC> fetch(wave, lane);
+  const TileFetch<D * 2, BC, NW> fetch(wave, lane);
   const int bid = blockIdx.x;
   const int head = bid % BH;
   // causal: the longest query blocks are dispatched first
@@ -207,9 +210,10 @@ template <int D, bool CAUSAL>
 static hipError_t launch_bwd_dq_t(const void* q, const void* k, const void* v, const void* dO,
                                   const float* nlse, const float* ndrow, void* dq, int BH, int N, float scale,
                                   hipStream_t stream) {
-  const int nqb = (N + 127) / 128;
-  const dim3 grid((unsigned)(nqb * BH)), block(256);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
+  constexpr int NW = FA_DQ_NW, BR = 32 * NW;
+  const int nqb = (N + BR - 1) / BR;
+  const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
                      (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e);
   return hipGetLastError();
 }
