@@ -14,21 +14,27 @@
 //   dV_w += P^T dO_i               MFMA, A = P^T from the S accumulators,
 //                                  B = dO through transposing LDS reads
 //   dK_w += dS^T Q_i               MFMA, same shape with dS and Q
-//   dQ_i += dS K                   dS goes through LDS (it is needed with the
-//                                  query index across lanes); each wave takes a
+//   dQ_i += dS K                   only in the atomic-dQ variant: dS goes
+//                                  through LDS (it is needed with the query
+//                                  index across lanes); each wave takes a
 //                                  32-column slice of d with K^T held in
 //                                  registers; fp32 atomics into an accumulator.
+// The S and dP accumulators start from -LSE/scale and -D of their query rows,
+// so they end as S - LSE/scale and dP - D.
 // The accumulators hold fp32 and are converted once at write-back (page
 // "gsyq.cn news/1372000", 踩坑三).  scale is applied to dK here and to dQ by
 // the conversion kernel.
 //
 // Pipelining: Q/dO/LSE/D of the next query block are fetched straight into
-// the other LDS buffer (buffer loads into LDS) while the current block is used; the
-// dQ product of a block runs at the start of the next iteration so that its
-// atomics drain under the next block's products; one barrier per block.  The
-// loop body is instantiated per buffer so that every LDS buffer is a distinct
-// object (the compiler then knows the prefetch cannot alias the reads).
-// LDS addresses are a few per-lane bases plus compile-time offsets.
+// the other LDS buffer (buffer loads into LDS) while the current block is
+// used; one barrier per block.  Within a block the work is a fixed sequence of
+// 32 slots separated by scheduling fences (products, the LDS reads of the slot
+// three ahead, a share of the exponentials).  In the atomic-dQ variant the dQ
+// product of a block runs at the start of the next iteration so that its
+// atomics drain under the next block's products.  The loop body is
+// instantiated per buffer so that every LDS buffer is a distinct object (the
+// compiler then knows the prefetch cannot alias the reads).  LDS addresses are
+// a few per-lane bases plus compile-time offsets.
 #include "fa_common.h"
 #include "fa_launch.h"
 

@@ -2,8 +2,8 @@
 //
 // dQ_i = scale * sum_j dS_ij K_j (page "flash-attention-backpropagation"
 // (aiqz.cc), section QKV梯度), computed without atomics: one workgroup
-// (4 waves) owns BR = 128 query rows of one (batch, head), each wave 32 of
-// them, with the wave's Q and dO rows in registers and dQ accumulated in
+// (8 waves, two per SIMD) owns BR = 256 query rows of one (batch, head), each
+// wave 32 of them, with the wave's Q and dO rows in registers and dQ accumulated in
 // registers, and walks the key/value tiles of BC = 64 rows (double-buffered
 // through LDS).  Per tile and wave:
 //   S^T  = K_j Q_w^T           MFMA, A = K rows (LDS), B = Q_w (registers)
@@ -15,7 +15,9 @@
 //   dQ^T += K_j^T dS^T         MFMA, A = K^T through transposing LDS reads,
 //                              B = dS^T straight from the accumulators.
 // It repeats the S and dP products of the key/value-outer kernel instead of
-// exchanging dS through fp32 atomics.
+// exchanging dS through fp32 atomics.  Each 32-key half of a tile is a fixed
+// sequence of slots separated by scheduling fences, with the LDS operands of
+// each slot read a few slots ahead.
 #include "fa_common.h"
 #include "fa_launch.h"
 

@@ -1,13 +1,15 @@
 // fa_fwd_bf16.hip -- forward kernel, bf16 inputs/outputs, fp32 accumulation.
 //
-// One workgroup (4 waves) owns BR = 128 query rows of one (batch, head); each
-// wave owns 32 of them.  Key/value tiles of BC = 64 rows stream through two
-// LDS buffers (the next tile is fetched while the current one is used).  Per
-// tile and wave:
+// One workgroup (8 waves, one workgroup per CU, two waves per SIMD) owns
+// BR = 256 query rows of one (batch, head); each wave owns 32 of them.
+// Key/value tiles of BC rows (64 for d = 128, 128 for d = 64) stream through
+// two LDS buffers (the next tile is fetched while the current one is used).
+// Per tile and wave:
 //   S^T = K_j Q_w^T            v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
 //                              B = the wave's Q rows held in registers;
-//   online softmax             per lane one query row: running max m and
-//                              running sum l, rescale factor 2^(c(m_old-m_new))
+//   online softmax             per lane one query row: running reference max
+//                              m and running sum l, rescale factor
+//                              2^(c(m_old-m_new)) when m moves (see the tile)
 //                              (page "flash-attention-v2-sram-tiling"
 //                              (aiqz.cc), section 5; the l update uses the full
 //                              block sum as in the derivation on page
@@ -18,7 +20,9 @@
 // "flash-attention-backpropagation" (aiqz.cc), section Python 演示), and the
 // ledger LSE = scale*m + ln l is written instead of P.
 // The softmax runs in base 2 with the scale folded into one multiply-add:
-// p = 2^(c*s - c*m) with c = scale*log2(e).
+// p = 2^(c*s - c*m) with c = scale*log2(e).  Each tile is a fixed sequence of
+// slots (S products, the softmax, P V products) separated by scheduling
+// fences, with the LDS operands of each slot read a few slots ahead.
 #include "fa_common.h"
 #include "fa_launch.h"
 
