@@ -235,6 +235,7 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     P = lambda t: t.data_ptr()
+    lay = fa.FA_LAYOUT_BHND
 
     def check(st, what):
         if st != 0:
@@ -243,19 +244,19 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        check(fa.fa_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, N, d, w.causal, w.scale, sp, code), "fa_fwd")
+        check(fa.fa_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, N, d, w.causal, w.scale, sp, code, lay), "fa_fwd")
         if ev is not None:
             ev[1].record(stream)
-        check(fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, w.scale, P(ws), ws.numel(), sp, code),
-              "fa_bwd_preprocess")
+        check(fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, w.scale, P(ws), ws.numel(), sp, code,
+                                   lay), "fa_bwd_preprocess")
         if ev is not None:
             ev[2].record(stream)
         check(fa.fa_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, N, d, w.causal,
-                             w.scale, P(ws), ws.numel(), sp, code), "fa_bwd_dkdv")
+                             w.scale, P(ws), ws.numel(), sp, code, lay), "fa_bwd_dkdv")
         if ev is not None:
             ev[3].record(stream)
         check(fa.fa_bwd_dq(P(q), P(k), P(v), P(do), P(lse), P(dq), B, H, N, d, w.causal, w.scale,
-                           P(ws), ws.numel(), sp, code), "fa_bwd_dq")
+                           P(ws), ws.numel(), sp, code, lay), "fa_bwd_dq")
         if ev is not None:
             ev[4].record(stream)
 

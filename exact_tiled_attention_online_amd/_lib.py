@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
 FA_BF16, FA_FP32 = 0, 1
+FA_LAYOUT_BHND, FA_LAYOUT_BNHD = 0, 1
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_strerror")
@@ -38,17 +39,17 @@ def load():
                           "`python -m exact_tiled_attention_online_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i]
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i]
     lib.fa_fwd.restype = i
-    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i]
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i, i]
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
-    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, f, vp, sz, vp, i]
+    lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, f, vp, sz, vp, i, i]
     lib.fa_bwd_preprocess.restype = i
-    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i]
+    lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i, i]
     lib.fa_bwd_dkdv.restype = i
-    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i]
+    lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i, i]
     lib.fa_bwd_dq.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
@@ -58,35 +59,36 @@ def load():
 
 # ---- the C entry points, same names, raw integer pointers ------------------
 
-def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype) -> int:
-    return load().fa_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream, dtype)
+def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype, layout) -> int:
+    return load().fa_fwd(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), stream, dtype, layout)
 
 
 def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes,
-           stream, dtype) -> int:
+           stream, dtype, layout) -> int:
     return load().fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
-                         workspace, workspace_bytes, stream, dtype)
+                         workspace, workspace_bytes, stream, dtype, layout)
 
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
     return load().fa_bwd_workspace_bytes(B, H, N, d, dtype)
 
 
-def fa_bwd_preprocess(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype) -> int:
+def fa_bwd_preprocess(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype,
+                      layout) -> int:
     return load().fa_bwd_preprocess(o, dO, lse, B, H, N, d, float(scale), workspace, workspace_bytes,
-                                    stream, dtype)
+                                    stream, dtype, layout)
 
 
 def fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes,
-                stream, dtype) -> int:
+                stream, dtype, layout) -> int:
     return load().fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, int(causal), float(scale),
-                              workspace, workspace_bytes, stream, dtype)
+                              workspace, workspace_bytes, stream, dtype, layout)
 
 
 def fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, causal, scale, workspace, workspace_bytes,
-              stream, dtype) -> int:
+              stream, dtype, layout) -> int:
     return load().fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, int(causal), float(scale),
-                            workspace, workspace_bytes, stream, dtype)
+                            workspace, workspace_bytes, stream, dtype, layout)
 
 
 def fa_strerror(status: int) -> str:
@@ -107,9 +109,20 @@ def _dtype_code(t):
 def _check(ts, shape):
     for t in ts:
         if not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
-            raise ValueError("expected contiguous device tensors of shape [B,H,N,d]")
+            raise ValueError("expected contiguous device tensors of one shape")
         if t.dtype != ts[0].dtype:
             raise ValueError("q, k, v (and o, dO) must share one dtype")
+
+
+def _dims(q, layout):
+    """(B, H, N, d) of a tensor in the named layout."""
+    if layout == FA_LAYOUT_BHND:
+        B, H, N, d = q.shape
+    elif layout == FA_LAYOUT_BNHD:
+        B, N, H, d = q.shape
+    else:
+        raise ValueError(f"unknown layout {layout}")
+    return B, H, N, d
 
 
 def _stream(stream):
@@ -118,40 +131,45 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def forward(q, k, v, causal: bool, scale: float, out=None, lse=None, stream=None):
-    """O, LSE = attention forward on [B,H,N,d] device tensors (bf16 or fp32)."""
+def forward(q, k, v, causal: bool, scale: float, out=None, lse=None, stream=None,
+            layout: int = FA_LAYOUT_BHND):
+    """O, LSE = attention forward on device tensors (bf16 or fp32) of shape
+    [B,H,N,d] (layout FA_LAYOUT_BHND) or [B,N,H,d] (FA_LAYOUT_BNHD); LSE is
+    always [B,H,N] float32."""
     import torch
-    B, H, N, d = q.shape
+    B, H, N, d = _dims(q, layout)
     _check((q, k, v), q.shape)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
-                B, H, N, d, causal, scale, _stream(stream), _dtype_code(q))
+                B, H, N, d, causal, scale, _stream(stream), _dtype_code(q), layout)
     if st != FA_OK:
         raise FAError(st, "fa_fwd")
     return o, l
 
 
-def workspace(q):
+def workspace(q, layout: int = FA_LAYOUT_BHND):
     """A device byte buffer large enough for fa_bwd on q's shape and dtype."""
     import torch
-    B, H, N, d = q.shape
+    B, H, N, d = _dims(q, layout)
     n = fa_bwd_workspace_bytes(B, H, N, d, _dtype_code(q))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
 
 
-def backward(q, k, v, o, do, lse, causal: bool, scale: float, ws=None, grads=None, stream=None):
-    """dQ, dK, dV of attention on [B,H,N,d] device tensors, given O and LSE."""
+def backward(q, k, v, o, do, lse, causal: bool, scale: float, ws=None, grads=None, stream=None,
+             layout: int = FA_LAYOUT_BHND):
+    """dQ, dK, dV of attention on device tensors in the named layout, given O
+    and LSE from forward."""
     import torch
-    B, H, N, d = q.shape
+    B, H, N, d = _dims(q, layout)
     _check((q, k, v, o, do), q.shape)
     if ws is None:
-        ws = workspace(q)
+        ws = workspace(q, layout)
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(q),
                                                   torch.empty_like(q))
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
-                ws.data_ptr(), ws.numel(), _stream(stream), _dtype_code(q))
+                ws.data_ptr(), ws.numel(), _stream(stream), _dtype_code(q), layout)
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv

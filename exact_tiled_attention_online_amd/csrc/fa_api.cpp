@@ -20,8 +20,9 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Common shape / flag checks; returns FA_OK or an error status.
-int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype) {
+int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype, int layout) {
   if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID;
+  if (layout != FA_LAYOUT_BHND && layout != FA_LAYOUT_BNHD) return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID;
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
@@ -30,6 +31,8 @@ int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype) 
   if (elems >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
+
+fa::RowLayout row_layout(int H, int layout) { return fa::RowLayout{H, layout == FA_LAYOUT_BNHD ? 1 : 0}; }
 
 struct Workspace {
   float* ndrow;   // -D per query row
@@ -74,18 +77,18 @@ bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d, int 
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-           int causal, float scale, void* stream, int dtype) {
+           int causal, float scale, void* stream, int dtype, int layout) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
-  const int st = check_shape(B, H, N, d, causal, scale, dtype);
+  const int st = check_shape(B, H, N, d, causal, scale, dtype, layout);
   if (st != FA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == FA_BF16)
-    return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, s));
+    return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, row_layout(H, layout), s));
   return hip_status(fa::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                        static_cast<const float*>(v), static_cast<float*>(o), lse, B * H, N, d,
-                                       causal != 0, scale, s));
+                                       causal != 0, scale, row_layout(H, layout), s));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
@@ -94,23 +97,24 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
 }
 
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
-                      float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype) {
+                      float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype,
+                      int layout) {
   if (!o || !dO || !lse) return FA_ERR_INVALID;
-  const int st = check_shape(B, H, N, d, 0, scale, dtype);
+  const int st = check_shape(B, H, N, d, 0, scale, dtype, layout);
   if (st != FA_OK) return st;
   if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(lse, 4)) return FA_ERR_INVALID;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
   const Workspace w = carve(workspace, B, H, N, d, dtype);
   float* dq_acc = (dtype == FA_BF16 && dq_atomic_mode()) ? w.dq_acc : nullptr;
   return hip_status(fa::launch_bwd_pre(o, dO, lse, w.ndrow, w.nlse, dq_acc, B * H, N, d, scale,
-                                       dtype == FA_FP32, static_cast<hipStream_t>(stream)));
+                                       dtype == FA_FP32, row_layout(H, layout), static_cast<hipStream_t>(stream)));
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dk,
                 void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
-                size_t workspace_bytes, void* stream, int dtype) {
+                size_t workspace_bytes, void* stream, int dtype, int layout) {
   if (!q || !k || !v || !dO || !lse || !dk || !dv) return FA_ERR_INVALID;
-  const int st = check_shape(B, H, N, d, causal, scale, dtype);
+  const int st = check_shape(B, H, N, d, causal, scale, dtype, layout);
   if (st != FA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dk, 16) ||
       !aligned(dv, 16) || !aligned(lse, 4))
@@ -122,16 +126,16 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, con
     return hip_status(fa::launch_bwd_kv_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                             static_cast<const float*>(v), static_cast<const float*>(dO), lse,
                                             w.ndrow, static_cast<float*>(dk), static_cast<float*>(dv), B * H, N,
-                                            d, causal != 0, scale, s));
+                                            d, causal != 0, scale, row_layout(H, layout), s));
   return hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.nlse, w.ndrow, w.dq_acc, dk, dv, B * H, N, d,
-                                        causal != 0, scale, dq_atomic_mode(), s));
+                                        causal != 0, scale, dq_atomic_mode(), row_layout(H, layout), s));
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq, int B,
               int H, int N, int d, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream,
-              int dtype) {
+              int dtype, int layout) {
   if (!q || !k || !v || !dO || !lse || !dq) return FA_ERR_INVALID;
-  const int st = check_shape(B, H, N, d, causal, scale, dtype);
+  const int st = check_shape(B, H, N, d, causal, scale, dtype, layout);
   if (st != FA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dq, 16) ||
       !aligned(lse, 4))
@@ -142,28 +146,32 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const
   if (dtype == FA_FP32)
     return hip_status(fa::launch_bwd_q_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                            static_cast<const float*>(v), static_cast<const float*>(dO), lse,
-                                           w.ndrow, static_cast<float*>(dq), B * H, N, d, causal != 0, scale, s));
+                                           w.ndrow, static_cast<float*>(dq), B * H, N, d, causal != 0, scale,
+                                           row_layout(H, layout), s));
   if (dq_atomic_mode())
-    return hip_status(fa::launch_dq_convert(w.dq_acc, dq, (size_t)B * H * N * d, scale, s));
-  return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.nlse, w.ndrow, dq, B * H, N, d, causal != 0, scale, s));
+    return hip_status(fa::launch_dq_convert(w.dq_acc, dq, B * H, N, d, scale, row_layout(H, layout), s));
+  return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.nlse, w.ndrow, dq, B * H, N, d, causal != 0, scale,
+                                      row_layout(H, layout), s));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
            void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
-           size_t workspace_bytes, void* stream, int dtype) {
+           size_t workspace_bytes, void* stream, int dtype, int layout) {
   // all checks first, so that a rejected call launches nothing
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID;
-  const int st = check_shape(B, H, N, d, causal, scale, dtype);
+  const int st = check_shape(B, H, N, d, causal, scale, dtype, layout);
   if (st != FA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
-  int r = fa_bwd_preprocess(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype);
+  int r = fa_bwd_preprocess(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype, layout);
   if (r != FA_OK) return r;
-  r = fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype);
+  r = fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype,
+                  layout);
   if (r != FA_OK) return r;
-  return fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype);
+  return fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype,
+                   layout);
 }
 
 const char* fa_strerror(int status) {

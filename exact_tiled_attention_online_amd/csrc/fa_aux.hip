@@ -20,7 +20,8 @@ template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ ndrow, float* __restrict__ nlse,
-                                                      float* __restrict__ dq_acc, size_t rows, float inv_scale) {
+                                                      float* __restrict__ dq_acc, size_t rows, float inv_scale,
+                                                      int N, RowLayout lay) {
   constexpr int LPR = D / 8;            // lanes per row, 8 elements each
   constexpr int RPB = 256 / LPR;        // rows per block
   const int tid = threadIdx.x;
@@ -28,7 +29,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
   const int part = tid % LPR;
   float acc = 0.f;
   if (row < rows) {
-    const size_t base = row * D + part * 8;
+    // row = hb*N + n of the [B*H][N] statistics; the tensor row is found
+    // through the layout
+    const int hb = (int)(row / N), n = (int)(row - (size_t)hb * N);
+    const size_t base = lay.head_off(hb, N, D) + (size_t)n * lay.row_stride(D) + part * 8;
     if constexpr (sizeof(T) == 2) {
       const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(O + base);
       const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(dO + base);
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
       }
     }
     if (dq_acc) {
-      f32x4* z = reinterpret_cast<f32x4*>(dq_acc + base);
+      f32x4* z = reinterpret_cast<f32x4*>(dq_acc + row * D + part * 8);   // contiguous
       z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
       z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -59,7 +63,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
 }
 
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ndrow, float* nlse,
-                          float* dq_acc, int BH, int N, int d, float scale, bool fp32, hipStream_t stream) {
+                          float* dq_acc, int BH, int N, int d, float scale, bool fp32, RowLayout lay,
+                          hipStream_t stream) {
   const float inv_scale = 1.f / scale;
   const size_t rows = (size_t)BH * N;
   const int rpb = 256 / (d / 8);
@@ -67,25 +72,30 @@ hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float
   if (fp32) {
     if (d == 128)
       hipLaunchKernelGGL((bwd_pre_kernel<128, float>), grid, block, 0, stream, (const float*)o,
-                         (const float*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale);
+                         (const float*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale, N, lay);
     else
       hipLaunchKernelGGL((bwd_pre_kernel<64, float>), grid, block, 0, stream, (const float*)o,
-                         (const float*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale);
+                         (const float*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale, N, lay);
   } else {
     if (d == 128)
       hipLaunchKernelGGL((bwd_pre_kernel<128, bf16>), grid, block, 0, stream, (const bf16*)o,
-                         (const bf16*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale);
+                         (const bf16*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale, N, lay);
     else
       hipLaunchKernelGGL((bwd_pre_kernel<64, bf16>), grid, block, 0, stream, (const bf16*)o,
-                         (const bf16*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale);
+                         (const bf16*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale, N, lay);
   }
   return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
-                                                         size_t n8, float scale) {
+                                                         size_t n8, float scale, int N, int D, RowLayout lay) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
+  // i = (hb*N + n)*(D/8) + c8 in the contiguous accumulator
+  const int c8 = (int)(i % (D / 8));
+  const size_t row = i / (D / 8);
+  const int hb = (int)(row / N), n = (int)(row - (size_t)hb * N);
+  const size_t out = lay.head_off(hb, N, D) + (size_t)n * lay.row_stride(D) + 8 * c8;
   const f32x4* a = reinterpret_cast<const f32x4*>(acc) + 2 * i;
   const f32x4 x = a[0], y = a[1];
   bf16x8 r;
@@ -94,13 +104,14 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
     r[e] = (bf16)(x[e] * scale);
     r[4 + e] = (bf16)(y[e] * scale);
   }
-  reinterpret_cast<bf16x8*>(dq)[i] = r;
+  *reinterpret_cast<bf16x8*>(dq + out) = r;
 }
 
-hipError_t launch_dq_convert(const float* dq_acc, void* dq, size_t n, float scale, hipStream_t stream) {
-  const size_t n8 = n / 8;   // n = B*H*N*d, a multiple of 64
+hipError_t launch_dq_convert(const float* dq_acc, void* dq, int BH, int N, int d, float scale, RowLayout lay,
+                             hipStream_t stream) {
+  const size_t n8 = (size_t)BH * N * d / 8;
   const dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
-  hipLaunchKernelGGL(dq_convert_kernel, grid, block, 0, stream, dq_acc, (bf16*)dq, n8, scale);
+  hipLaunchKernelGGL(dq_convert_kernel, grid, block, 0, stream, dq_acc, (bf16*)dq, n8, scale, N, d, lay);
   return hipGetLastError();
 }
 

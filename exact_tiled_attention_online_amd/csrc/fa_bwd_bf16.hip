@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
     float* __restrict__ dQacc, bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb,
-    float scale, float c) {
+    float scale, float c, RowLayout lay) {
   constexpr int BC = 128, BR = 64;
   constexpr int ROWB = D * 2, CH = D / 8, KS = D / 16, DT = D / 32;
   constexpr int QTB = BR * ROWB;          // bytes of one Q or dO tile
@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, s16 = lane & 15;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the same value, known uniform
-  const TileFetch<D * 2, BR> qfetch(wave_u, lane);
+  const int RS = lay.row_stride(D);      // elements between a head's rows
+  const TileFetch<D * 2, BR> qfetch(wave_u, lane, RS * 2);
   // Work items.  Causal: item c of a head is the key-block pair
   // (c, nkb-1-c), whose query walks together always cover the same number of
   // blocks, so every workgroup does the same work; the first block is walked
@@ -93,14 +94,14 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   const int item = (W % 8 == 0) ? (bid % 8) * (W / 8) + bid / 8 : bid;
   const int head = item / P, c_item = item % P;
   const int nparts = (CAUSAL && 2 * c_item + 1 != nkb) ? 2 : 1;
-  const size_t hoff = (size_t)head * N * D;
+  const size_t hoff = lay.head_off(head, N, D);
   const bf16* Qh = Q + hoff;
   const bf16* Kh = K + hoff;
   const bf16* Vh = V + hoff;
   const bf16* Gh = dO + hoff;
   const float* Lh = NLSE + (size_t)head * N;   // -LSE / scale
   const float* Dh = NDR + (size_t)head * N;    // -D
-  float* dQh = dQacc + hoff;
+  float* dQh = dQacc + (size_t)head * N * D;   // contiguous [B*H][N][d] accumulator
 
   for (int part = 0; part < nparts; ++part) {
     const int kb = CAUSAL ? (part == 0 ? c_item : nkb - 1 - c_item) : c_item;
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
         const int row = ci / CH, ch = ci % CH;
         const int kv = kv0 + row;
         u32x4 x = u32x4{0, 0, 0, 0};
-        if (kv < N) x = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv * D + ch * 8);
+        if (kv < N) x = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv * RS + ch * 8);
         *reinterpret_cast<u32x4*>(&sK[tile_off<ROWB>(row, ch)]) = x;
       }
     }
@@ -129,8 +130,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (kvrow < N) {
-        kf[s] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kvrow * D + 16 * s + 8 * h);
-        vf[s] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kvrow * D + 16 * s + 8 * h);
+        kf[s] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kvrow * RS + 16 * s + 8 * h);
+        vf[s] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kvrow * RS + 16 * s + 8 * h);
       } else {
         kf[s] = bf16x8{};
         vf[s] = bf16x8{};
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
           const int ci = p * 64 + lane;
           const int row = ci / CH, ch = ci % CH;
           if (kvw + row < N)
-            *reinterpret_cast<u32x4*>(dst + (size_t)(kvw + row) * D + ch * 8) =
+            *reinterpret_cast<u32x4*>(dst + (size_t)(kvw + row) * RS + ch * 8) =
                 *reinterpret_cast<const u32x4*>(&stg[row * D + ch * 8]);
         }
       }
@@ -425,32 +426,34 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 template <int D, bool CAUSAL, bool DQA>
 static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v, const void* dO,
                                     const float* nlse, const float* ndrow, float* dq_acc, void* dk,
-                                    void* dv, int BH, int N, float scale, hipStream_t stream) {
+                                    void* dv, int BH, int N, float scale, RowLayout lay, hipStream_t stream) {
   const int nkb = (N + 127) / 128, nqb = (N + 63) / 64;
   const int items = CAUSAL ? (nkb + 1) / 2 : nkb;
   const dim3 grid((unsigned)(items * BH)), block(256);
   hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, DQA>), grid, block, 0, stream, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, dq_acc, (bf16*)dk,
-                     (bf16*)dv, BH, N, nqb, scale, scale * kLog2e);
+                     (bf16*)dv, BH, N, nqb, scale, scale * kLog2e, lay);
   return hipGetLastError();
 }
 
 template <bool DQA>
 static hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void* dO,
                                 const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
-                                int BH, int N, int d, bool causal, float scale, hipStream_t stream) {
+                                int BH, int N, int d, bool causal, float scale, RowLayout lay,
+                                hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_bwd_bf16_t<128, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, stream)
-                  : launch_bwd_bf16_t<128, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, stream);
-  return causal ? launch_bwd_bf16_t<64, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, stream)
-                : launch_bwd_bf16_t<64, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, stream);
+    return causal ? launch_bwd_bf16_t<128, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream)
+                  : launch_bwd_bf16_t<128, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream);
+  return causal ? launch_bwd_bf16_t<64, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream)
+                : launch_bwd_bf16_t<64, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dO,
                            const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
-                           int BH, int N, int d, bool causal, float scale, bool dq_atomic, hipStream_t stream) {
-  return dq_atomic ? launch_bwd_kv<true>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, d, causal, scale, stream)
-                   : launch_bwd_kv<false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, d, causal, scale, stream);
+                           int BH, int N, int d, bool causal, float scale, bool dq_atomic, RowLayout lay,
+                           hipStream_t stream) {
+  return dq_atomic ? launch_bwd_kv<true>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, d, causal, scale, lay, stream)
+                   : launch_bwd_kv<false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, d, causal, scale, lay, stream);
 }
 
 }  // namespace fa

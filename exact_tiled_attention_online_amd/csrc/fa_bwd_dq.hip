@@ -30,7 +30,7 @@ template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
-    bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c) {
+    bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, RowLayout lay) {
   constexpr int BR = 32 * NW, BC = 64;
   constexpr int ROWB = D * 2;        // bytes per row
   constexpr int KS = D / 16;         // K-steps of the S and dP products
@@ -47,12 +47,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const TileBases<D * 2> tb(lane);
-  const TileFetch<D * 2, BC, NW> fetch(wave, lane);
+  const int RS = lay.row_stride(D);      // elements between a head's rows
+  const TileFetch<D * 2, BC, NW> fetch(wave, lane, RS * 2);
   const int bid = blockIdx.x;
   const int head = bid % BH;
   // causal: the longest query blocks are dispatched first
   const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
-  const size_t hoff = (size_t)head * N * D;
+  const size_t hoff = lay.head_off(head, N, D);
   const bf16* Qh = Q + hoff;
   const bf16* Kh = K + hoff;
   const bf16* Vh = V + hoff;
@@ -66,8 +67,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     if (qrow < N) {
-      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + 16 * s + 8 * h);
-      gf[s] = *reinterpret_cast<const bf16x8*>(Gh + (size_t)qrow * D + 16 * s + 8 * h);
+      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * RS + 16 * s + 8 * h);
+      gf[s] = *reinterpret_cast<const bf16x8*>(Gh + (size_t)qrow * RS + 16 * s + 8 * h);
     } else {
       qf[s] = bf16x8{};
       gf[s] = bf16x8{};
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
 
   if (qrow >= N) return;
   // acc[t][4*i+jj] = dQ^T[d = 32t + 8i + 4h + jj][query qrow]
-  bf16* row = dQ + hoff + (size_t)qrow * D;
+  bf16* row = dQ + hoff + (size_t)qrow * RS;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -211,23 +212,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_dq_t(const void* q, const void* k, const void* v, const void* dO,
                                   const float* nlse, const float* ndrow, void* dq, int BH, int N, float scale,
-                                  hipStream_t stream) {
+                                  RowLayout lay, hipStream_t stream) {
   constexpr int NW = FA_DQ_NW, BR = 32 * NW;
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
-                     (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e);
+                     (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e,
+                     lay);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                          const float* ndrow, void* dq, int BH, int N, int d, bool causal, float scale,
-                         hipStream_t stream) {
+                         RowLayout lay, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_bwd_dq_t<128, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, stream)
-                  : launch_bwd_dq_t<128, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, stream);
-  return causal ? launch_bwd_dq_t<64, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, stream)
-                : launch_bwd_dq_t<64, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, stream);
+    return causal ? launch_bwd_dq_t<128, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream)
+                  : launch_bwd_dq_t<128, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream);
+  return causal ? launch_bwd_dq_t<64, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream)
+                : launch_bwd_dq_t<64, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream);
 }
 
 }  // namespace fa

@@ -148,6 +148,7 @@ struct TileBases {
 template <int B>
 using IC = std::integral_constant<int, B>;
 
+
 // Wave-wide direct fetch global -> LDS through a buffer resource: lane l's 16
 // (or 4) bytes, read from base + soffset (uniform) + voffset (per lane), land
 // at lds_base + 16*l (or 4*l); lds_base must be the same for the whole wave.
@@ -166,8 +167,9 @@ FA_DEV void dma4_buf(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)lds_base, 4, voff, soff, 0, 0);
 }
 
-// Fetch ROWS rows (ROWB bytes each) starting at row0 of a row-major bf16
-// matrix into a swizzled LDS tile, with the NW waves of a workgroup.  Wave w,
+// Fetch ROWS rows (ROWB bytes each, rsb bytes apart in global memory)
+// starting at row0 of a bf16 matrix into a swizzled LDS tile, with the NW
+// waves of a workgroup.  Wave w,
 // load j fills LDS bytes [(w*LPW + j) KB, +1 KB): tile row blk*RPL + lane/CH
 // at chunk position lane%CH, i.e. logical chunk (lane%CH) ^ swz(row).  Rows at
 // or past nrows read row nrows-1 instead (finite values the caller masks).
@@ -180,18 +182,20 @@ struct TileFetch {
   static_assert(LPW * RPL * NW == ROWS, "tile must split evenly over the waves");
   unsigned goff[LPW];   // byte offset of this lane's chunk from the tile's first row
   int wave, lane;       // wave: uniform across the wave
-  FA_DEV TileFetch(int wave_, int lane_) : wave(wave_), lane(lane_) {
+  unsigned rsb;         // bytes between consecutive rows in global memory
+  FA_DEV TileFetch(int wave_, int lane_, int row_stride_bytes)
+      : wave(wave_), lane(lane_), rsb((unsigned)row_stride_bytes) {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int row = (wave * LPW + j) * RPL + lane / CH;
       const int ch = (lane % CH) ^ swz<ROWB>(row);
-      goff[j] = (unsigned)(row * ROWB + ch * 16);
+      goff[j] = (unsigned)row * rsb + (unsigned)(ch * 16);
     }
   }
   FA_DEV void operator()(const bf16* src, int row0, int nrows, char* dst) const {
     if (row0 + ROWS <= nrows) {
       const __amdgpu_buffer_rsrc_t rs = raw_rsrc(src);
-      const unsigned soff = (unsigned)row0 * ROWB;
+      const unsigned soff = (unsigned)row0 * rsb;
 #pragma unroll
       for (int j = 0; j < LPW; ++j) dma16_buf(rs, goff[j], soff, dst + (wave * LPW + j) * 1024);
     } else {
@@ -201,7 +205,7 @@ struct TileFetch {
         const int row = blk * RPL + lane / CH;
         const int ch = (lane % CH) ^ swz<ROWB>(row);
         const int r = min(row0 + row, nrows - 1);
-        dma16_buf(raw_rsrc(src), (unsigned)(r * ROWB + ch * 16), 0, dst + blk * 1024);
+        dma16_buf(raw_rsrc(src), (unsigned)r * rsb + (unsigned)(ch * 16), 0, dst + blk * 1024);
       }
     }
   }

@@ -23,13 +23,13 @@ constexpr int F32_ROWS = 64;   // rows per workgroup (128 lanes)
 constexpr int F32_TILE = 32;   // streamed rows per LDS tile
 
 template <int D>
-FA_DEV void load_rows_f32(float* dst, const float* src, int row0, int nrows, int N, int tid) {
-  // dst: [F32_TILE][D] floats; src rows row0.. of one head
+FA_DEV void load_rows_f32(float* dst, const float* src, int row0, int nrows, int N, int tid, int rs) {
+  // dst: [F32_TILE][D] floats; src rows row0.. of one head, rs elements apart
   constexpr int V4 = D / 4;
   for (int e = tid; e < F32_TILE * V4; e += 128) {
     const int r = e / V4, c4 = e % V4;
     f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (r < nrows && row0 + r < N) x = reinterpret_cast<const f32x4*>(src + (size_t)(row0 + r) * D)[c4];
+    if (r < nrows && row0 + r < N) x = reinterpret_cast<const f32x4*>(src + (size_t)(row0 + r) * rs)[c4];
     reinterpret_cast<f32x4*>(dst + r * D)[c4] = x;
   }
 }
@@ -45,7 +45,8 @@ FA_DEV float half_dot(const float* a, const float* b) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
-                                                      float* __restrict__ LSE, int BH, int N, float scale) {
+                                                      float* __restrict__ LSE, int BH, int N, float scale,
+                                                      RowLayout lay) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sv[F32_TILE * D];
@@ -53,19 +54,20 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ 
   const int head = blockIdx.y;
   const int row0 = blockIdx.x * F32_ROWS;
   const int qrow = row0 + (tid >> 1);
-  const size_t hoff = (size_t)head * N * D;
+  const int RS = lay.row_stride(D);   // elements between a head's rows
+  const size_t hoff = lay.head_off(head, N, D);
   float qh[DH], oh[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
-    qh[c] = qrow < N ? Q[hoff + (size_t)qrow * D + half * DH + c] : 0.f;
+    qh[c] = qrow < N ? Q[hoff + (size_t)qrow * RS + half * DH + c] : 0.f;
     oh[c] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
   const int kv_end = CAUSAL ? min(N, row0 + F32_ROWS) : N;
   for (int t0 = 0; t0 < kv_end; t0 += F32_TILE) {
     __syncthreads();
-    load_rows_f32<D>(sk, K + hoff, t0, F32_TILE, N, tid);
-    load_rows_f32<D>(sv, V + hoff, t0, F32_TILE, N, tid);
+    load_rows_f32<D>(sk, K + hoff, t0, F32_TILE, N, tid, RS);
+    load_rows_f32<D>(sv, V + hoff, t0, F32_TILE, N, tid, RS);
     __syncthreads();
     float s[F32_TILE];
     float mx = m;
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ 
   if (qrow < N) {
     const float inv = 1.f / l;
 #pragma unroll
-    for (int c = 0; c < DH; ++c) O[hoff + (size_t)qrow * D + half * DH + c] = oh[c] * inv;
+    for (int c = 0; c < DH; ++c) O[hoff + (size_t)qrow * RS + half * DH + c] = oh[c] * inv;
     if (half == 0) LSE[(size_t)head * N + qrow] = m + logf(l);
   }
 }
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
                                                          const float* __restrict__ V, const float* __restrict__ dO,
                                                          const float* __restrict__ LSE, const float* __restrict__ NDR,
                                                          float* __restrict__ dK, float* __restrict__ dV, int N,
-                                                         float scale) {
+                                                         float scale, RowLayout lay) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float sq[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sg[F32_TILE * D];
@@ -118,20 +120,21 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
   const int head = blockIdx.y;
   const int row0 = blockIdx.x * F32_ROWS;
   const int kvrow = row0 + (tid >> 1);
-  const size_t hoff = (size_t)head * N * D;
+  const int RS = lay.row_stride(D);   // elements between a head's rows
+  const size_t hoff = lay.head_off(head, N, D);
   float kh[DH], vh[DH], dkh[DH], dvh[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
-    kh[c] = kvrow < N ? K[hoff + (size_t)kvrow * D + half * DH + c] : 0.f;
-    vh[c] = kvrow < N ? V[hoff + (size_t)kvrow * D + half * DH + c] : 0.f;
+    kh[c] = kvrow < N ? K[hoff + (size_t)kvrow * RS + half * DH + c] : 0.f;
+    vh[c] = kvrow < N ? V[hoff + (size_t)kvrow * RS + half * DH + c] : 0.f;
     dkh[c] = 0.f;
     dvh[c] = 0.f;
   }
   const int q_begin = CAUSAL ? (row0 / F32_TILE) * F32_TILE : 0;
   for (int t0 = q_begin; t0 < N; t0 += F32_TILE) {
     __syncthreads();
-    load_rows_f32<D>(sq, Q + hoff, t0, F32_TILE, N, tid);
-    load_rows_f32<D>(sg, dO + hoff, t0, F32_TILE, N, tid);
+    load_rows_f32<D>(sq, Q + hoff, t0, F32_TILE, N, tid, RS);
+    load_rows_f32<D>(sg, dO + hoff, t0, F32_TILE, N, tid, RS);
     if (tid < F32_TILE) {
       const int q = t0 + tid;
       sl[tid] = q < N ? LSE[(size_t)head * N + q] : 0.f;
@@ -155,8 +158,8 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
   if (kvrow < N) {
 #pragma unroll
     for (int c = 0; c < DH; ++c) {
-      dK[hoff + (size_t)kvrow * D + half * DH + c] = dkh[c] * scale;
-      dV[hoff + (size_t)kvrow * D + half * DH + c] = dvh[c];
+      dK[hoff + (size_t)kvrow * RS + half * DH + c] = dkh[c] * scale;
+      dV[hoff + (size_t)kvrow * RS + half * DH + c] = dvh[c];
     }
   }
 }
@@ -166,7 +169,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                         const float* __restrict__ V, const float* __restrict__ dO,
                                                         const float* __restrict__ LSE, const float* __restrict__ NDR,
-                                                        float* __restrict__ dQ, int N, float scale) {
+                                                        float* __restrict__ dQ, int N, float scale, RowLayout lay) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sv[F32_TILE * D];
@@ -174,12 +177,13 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
   const int head = blockIdx.y;
   const int row0 = blockIdx.x * F32_ROWS;
   const int qrow = row0 + (tid >> 1);
-  const size_t hoff = (size_t)head * N * D;
+  const int RS = lay.row_stride(D);   // elements between a head's rows
+  const size_t hoff = lay.head_off(head, N, D);
   float qh[DH], gh[DH], dqh[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
-    qh[c] = qrow < N ? Q[hoff + (size_t)qrow * D + half * DH + c] : 0.f;
-    gh[c] = qrow < N ? dO[hoff + (size_t)qrow * D + half * DH + c] : 0.f;
+    qh[c] = qrow < N ? Q[hoff + (size_t)qrow * RS + half * DH + c] : 0.f;
+    gh[c] = qrow < N ? dO[hoff + (size_t)qrow * RS + half * DH + c] : 0.f;
     dqh[c] = 0.f;
   }
   const float lse = qrow < N ? LSE[(size_t)head * N + qrow] : 0.f;
@@ -187,8 +191,8 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
   const int kv_end = CAUSAL ? min(N, row0 + F32_ROWS) : N;
   for (int t0 = 0; t0 < kv_end; t0 += F32_TILE) {
     __syncthreads();
-    load_rows_f32<D>(sk, K + hoff, t0, F32_TILE, N, tid);
-    load_rows_f32<D>(sv, V + hoff, t0, F32_TILE, N, tid);
+    load_rows_f32<D>(sk, K + hoff, t0, F32_TILE, N, tid, RS);
+    load_rows_f32<D>(sv, V + hoff, t0, F32_TILE, N, tid, RS);
     __syncthreads();
     for (int j = 0; j < F32_TILE; ++j) {
       const int kv = t0 + j;
@@ -203,63 +207,65 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
   }
   if (qrow < N) {
 #pragma unroll
-    for (int c = 0; c < DH; ++c) dQ[hoff + (size_t)qrow * D + half * DH + c] = dqh[c] * scale;
+    for (int c = 0; c < DH; ++c) dQ[hoff + (size_t)qrow * RS + half * DH + c] = dqh[c] * scale;
   }
 }
 
 template <int D, bool CAUSAL>
 static hipError_t fwd_f32_t(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
-                            int N, float scale, hipStream_t stream) {
+                            int N, float scale, RowLayout lay, hipStream_t stream) {
   const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, o, lse, BH, N, scale);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, o, lse, BH, N, scale, lay);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 static hipError_t bwd_kv_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
                                const float* ndrow, float* dk, float* dv, int BH, int N, float scale,
-                               hipStream_t stream) {
+                               RowLayout lay, hipStream_t stream) {
   const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
   hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dk, dv, N,
-                     scale);
+                     scale, lay);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 static hipError_t bwd_q_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
-                              const float* ndrow, float* dq, int BH, int N, float scale, hipStream_t stream) {
+                              const float* ndrow, float* dq, int BH, int N, float scale, RowLayout lay,
+                              hipStream_t stream) {
   const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
-  hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dq, N, scale);
+  hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dq, N, scale,
+                     lay);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N,
-                          int d, bool causal, float scale, hipStream_t stream) {
+                          int d, bool causal, float scale, RowLayout lay, hipStream_t stream) {
   if (d == 128)
-    return causal ? fwd_f32_t<128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                  : fwd_f32_t<128, false>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? fwd_f32_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                : fwd_f32_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);
+    return causal ? fwd_f32_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
+                  : fwd_f32_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
+  return causal ? fwd_f32_t<64, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
+                : fwd_f32_t<64, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
 }
 
 hipError_t launch_bwd_kv_f32(const float* q, const float* k, const float* v, const float* dO, const float* lse,
                              const float* ndrow, float* dk, float* dv, int BH, int N, int d, bool causal,
-                             float scale, hipStream_t stream) {
+                             float scale, RowLayout lay, hipStream_t stream) {
   if (d == 128)
-    return causal ? bwd_kv_f32_t<128, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, stream)
-                  : bwd_kv_f32_t<128, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, stream);
-  return causal ? bwd_kv_f32_t<64, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, stream)
-                : bwd_kv_f32_t<64, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, stream);
+    return causal ? bwd_kv_f32_t<128, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream)
+                  : bwd_kv_f32_t<128, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream);
+  return causal ? bwd_kv_f32_t<64, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream)
+                : bwd_kv_f32_t<64, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream);
 }
 
 hipError_t launch_bwd_q_f32(const float* q, const float* k, const float* v, const float* dO, const float* lse,
                             const float* ndrow, float* dq, int BH, int N, int d, bool causal, float scale,
-                            hipStream_t stream) {
+                            RowLayout lay, hipStream_t stream) {
   if (d == 128)
-    return causal ? bwd_q_f32_t<128, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, stream)
-                  : bwd_q_f32_t<128, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, stream);
-  return causal ? bwd_q_f32_t<64, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, stream)
-                : bwd_q_f32_t<64, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, stream);
+    return causal ? bwd_q_f32_t<128, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream)
+                  : bwd_q_f32_t<128, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream);
+  return causal ? bwd_q_f32_t<64, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream)
+                : bwd_q_f32_t<64, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream);
 }
 
 }  // namespace fa

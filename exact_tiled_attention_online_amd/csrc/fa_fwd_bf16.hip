@@ -34,7 +34,8 @@ namespace fa {
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c) {
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c,
+    RowLayout lay) {
 #ifndef FA_FWD_BC64
 #define FA_FWD_BC64 128
 #endif
@@ -56,12 +57,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const TileBases<D * 2> tb(lane);
-  const TileFetch<D * 2, BC, NW> fetch(wave, lane);
+  const int RS = lay.row_stride(D);      // elements between a head's rows
+  const TileFetch<D * 2, BC, NW> fetch(wave, lane, RS * 2);
   const int bid = blockIdx.x;
   const int head = bid % BH;
   // causal: the longest query blocks are dispatched first
   const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
-  const size_t hoff = (size_t)head * N * D;
+  const size_t hoff = lay.head_off(head, N, D);
   const bf16* Qh = Q + hoff;
   const bf16* Kh = K + hoff;
   const bf16* Vh = V + hoff;
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     if (qrow < N)
-      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * D + 16 * s + 8 * h);
+      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * RS + 16 * s + 8 * h);
     else
       qf[s] = bf16x8{};
   }
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   const float l_tot = half_sum(l_run);
   if (qrow < N) {
     const float inv = 1.f / l_tot;
-    bf16* Orow = O + hoff + (size_t)qrow * D;
+    bf16* Orow = O + hoff + (size_t)qrow * RS;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -238,23 +240,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                                    int BH, int N, float scale, hipStream_t stream) {
+                                    int BH, int N, float scale, RowLayout lay, hipStream_t stream) {
   constexpr int NW = FA_FWD_NW, BR = 32 * NW;
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), grid, block, 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
-                     scale * kLog2e);
+                     scale * kLog2e, lay);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                           int N, int d, bool causal, float scale, hipStream_t stream) {
+                           int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, stream);
-  return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);
+    return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
+                  : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
+  return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
+                : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
 }
 
 }  // namespace fa

@@ -7,38 +7,55 @@
 
 namespace fa {
 
+// Where the N rows of one (batch, head) sit in a q/k/v/o/dO/dq/dk/dv tensor:
+// [B,H,N,d] (each head's rows contiguous) or [B,N,H,d] (each token's H heads
+// contiguous, so a head's consecutive rows are H*d elements apart).  hb is
+// the flattened batch*head index.
+struct RowLayout {
+  int H;      // heads per batch
+  int bnhd;   // 0: [B,H,N,d]; 1: [B,N,H,d]
+  __host__ __device__ __forceinline__ int row_stride(int D) const { return bnhd ? H * D : D; }
+  __host__ __device__ __forceinline__ size_t head_off(int hb, int N, int D) const {
+    const int b = hb / H, h = hb - b * H;
+    return bnhd ? ((size_t)b * N * H + h) * D : (size_t)hb * N * D;
+  }
+};
+
+
 // bf16 forward: O, LSE.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                           int N, int d, bool causal, float scale, hipStream_t stream);
+                           int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream);
 
 // Backward preprocess: ndrow = -rowsum(dO o O) (fp32), nlse = -LSE / scale,
 // and, when dq_acc is not null, dq_acc = 0.  `fp32` selects the input type.
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ndrow, float* nlse,
-                          float* dq_acc, int BH, int N, int d, float scale, bool fp32, hipStream_t stream);
+                          float* dq_acc, int BH, int N, int d, float scale, bool fp32, RowLayout lay,
+                          hipStream_t stream);
 
 // bf16 key/value-block-outer backward: dK, dV written; with dq_atomic, dQ is
 // also accumulated (fp32, unscaled dS K) into dq_acc with atomics.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dO,
                            const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
-                           int BH, int N, int d, bool causal, float scale, bool dq_atomic,
+                           int BH, int N, int d, bool causal, float scale, bool dq_atomic, RowLayout lay,
                            hipStream_t stream);
 
 // bf16 query-block-outer dQ kernel: dQ = bf16(scale * dS K), no atomics.
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                          const float* ndrow, void* dq, int BH, int N, int d, bool causal, float scale,
-                         hipStream_t stream);
+                         RowLayout lay, hipStream_t stream);
 
-// dQ = bf16(scale * dq_acc).
-hipError_t launch_dq_convert(const float* dq_acc, void* dq, size_t n, float scale, hipStream_t stream);
+// dQ = bf16(scale * dq_acc); dq_acc is contiguous [B*H][N][d], dq in layout lay.
+hipError_t launch_dq_convert(const float* dq_acc, void* dq, int BH, int N, int d, float scale, RowLayout lay,
+                             hipStream_t stream);
 
 // fp32 path (plain VALU kernels, exact fp32 arithmetic).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int BH, int N, int d, bool causal, float scale, hipStream_t stream);
+                          int BH, int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream);
 hipError_t launch_bwd_kv_f32(const float* q, const float* k, const float* v, const float* dO,
                              const float* lse, const float* ndrow, float* dk, float* dv, int BH, int N,
-                             int d, bool causal, float scale, hipStream_t stream);
+                             int d, bool causal, float scale, RowLayout lay, hipStream_t stream);
 hipError_t launch_bwd_q_f32(const float* q, const float* k, const float* v, const float* dO,
                             const float* lse, const float* ndrow, float* dq, int BH, int N, int d,
-                            bool causal, float scale, hipStream_t stream);
+                            bool causal, float scale, RowLayout lay, hipStream_t stream);
 
 }  // namespace fa

@@ -15,9 +15,12 @@
  *             dK = scale * dS^T Q (page "flash-attention-backpropagation",
  *             sections 反向总览, Softmax梯度 and QKV梯度).
  *
- * Layout (every tensor): contiguous [B, H, N, d], row-major, d fastest, in
- * the element type named by `dtype` (FA_BF16: bfloat16, FA_FP32: float).
- * lse is float [B, H, N], natural log, in units of the scaled score
+ * Layout: q, k, v, o, dO, dq, dk, dv are contiguous, d fastest, in the element
+ * type named by `dtype` (FA_BF16: bfloat16, FA_FP32: float), all in the
+ * layout named by `layout`: FA_LAYOUT_BHND = [B, H, N, d] (each head's rows
+ * contiguous) or FA_LAYOUT_BNHD = [B, N, H, d] (each token's H heads
+ * contiguous, as a projection writes them, so no transpose is needed).
+ * lse is always float [B, H, N], natural log, in units of the scaled score
  * scale * q_i . k_j.  The causal mask keeps key j for query i iff j <= i
  * (queries and keys share the index range 0..N-1).
  *
@@ -55,8 +58,10 @@ typedef enum {
 
 typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
 
+typedef enum { FA_LAYOUT_BHND = 0, FA_LAYOUT_BNHD = 1 } fa_layout;
+
 /*
- * Forward pass.  Reads q, k, v; writes o ([B,H,N,d], dtype) and
+ * Forward pass.  Reads q, k, v; writes o (same layout and dtype) and
  * lse ([B,H,N], float).  One workgroup owns a block of query rows and streams
  * the key/value blocks through LDS, applying the online-softmax update of
  * page "flash-attention-v2-sram-tiling", section 5, with the normalisation by
@@ -65,7 +70,7 @@ typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, int causal, float scale,
-           void* stream, int dtype);
+           void* stream, int dtype, int layout);
 
 /*
  * Bytes of device workspace fa_bwd needs for this shape: the fp32 row term
@@ -79,7 +84,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
  * Backward pass.  Reads q, k, v, o, dO and the ledger lse written by fa_fwd
  * with the same q, k, v, causal and scale (the recompute of P^ is exact only
  * for the ledger of that forward: page "flash-attention-backpropagation",
- * section 数值稳定).  Writes dq, dk, dv ([B,H,N,d], dtype).  Uses `workspace`
+ * section 数值稳定).  Writes dq, dk, dv (same layout and dtype as q).  Uses `workspace`
  * (at least fa_bwd_workspace_bytes bytes) as scratch; it is fully overwritten.
  * Kernels, in stream order: D = rowsum(dO o O), the key/value-block-outer
  * kernel (dK, dV), the query-block-outer kernel (dQ).
@@ -87,7 +92,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dO, const float* lse, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, int causal, float scale,
-           void* workspace, size_t workspace_bytes, void* stream, int dtype);
+           void* workspace, size_t workspace_bytes, void* stream, int dtype, int layout);
 
 /*
  * The three stages fa_bwd runs, in this order on one stream, for callers that
@@ -110,13 +115,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * which measured faster.
  */
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
-                      float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype);
+                      float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype,
+                      int layout);
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
                 void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
-                void* workspace, size_t workspace_bytes, void* stream, int dtype);
+                void* workspace, size_t workspace_bytes, void* stream, int dtype, int layout);
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
               void* dq, int B, int H, int N, int d, int causal, float scale,
-              void* workspace, size_t workspace_bytes, void* stream, int dtype);
+              void* workspace, size_t workspace_bytes, void* stream, int dtype, int layout);
 
 /* Static, human-readable text for a status code. */
 const char* fa_strerror(int status);

@@ -28,29 +28,38 @@ def log(msg):
     sys.stdout.flush()
 
 
-def to_dev(x, dtype):
+def to_dev(x, dtype, layout=0):
+    """Upload a [B,H,N,d] array (or [B,H,N]) in the named layout."""
     import torch
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    a = np.asarray(x, dtype=np.float32)
+    if layout == fa.FA_LAYOUT_BNHD and a.ndim == 4:
+        a = a.transpose(0, 2, 1, 3)
+    t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
     return t.to(torch.bfloat16) if dtype == "bf16" else t
 
 
-def to_np(t):
-    return t.float().cpu().numpy().astype(np.float64)
+def to_np(t, layout=0):
+    """Download a device tensor as fp64 numpy, back in [B,H,N,d] order."""
+    a = t.float().cpu().numpy().astype(np.float64)
+    if layout == fa.FA_LAYOUT_BNHD and a.ndim == 4:
+        a = np.ascontiguousarray(a.transpose(0, 2, 1, 3))
+    return a
 
 
-def run_gpu(x, dtype, causal, scale, bwd=True, stream=None):
-    """fwd (+ bwd) on device; returns dict of fp64 numpy arrays."""
+def run_gpu(x, dtype, causal, scale, bwd=True, stream=None, layout=0):
+    """fwd (+ bwd) on device; returns dict of fp64 numpy arrays in [B,H,N,d]
+    order whatever the device layout."""
     import torch
-    q, k, v, do = (to_dev(x[n], dtype) for n in ("q", "k", "v", "do"))
-    o, lse = fa.forward(q, k, v, causal, scale, stream=stream)
+    q, k, v, do = (to_dev(x[n], dtype, layout) for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward(q, k, v, causal, scale, stream=stream, layout=layout)
     out = {"o_dev": o, "lse_dev": lse}
     if bwd:
-        dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal, scale, stream=stream)
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal, scale, stream=stream, layout=layout)
         out.update(dq_dev=dq, dk_dev=dk, dv_dev=dv)
     torch.cuda.synchronize()
-    res = {"o": to_np(o), "lse": to_np(lse)}
+    res = {"o": to_np(o, layout), "lse": to_np(lse)}
     if bwd:
-        res.update(dq=to_np(dq), dk=to_np(dk), dv=to_np(dv))
+        res.update(dq=to_np(dq, layout), dk=to_np(dk, layout), dv=to_np(dv, layout))
     res["_dev"] = out
     return res
 

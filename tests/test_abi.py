@@ -95,14 +95,15 @@ P = 0x10000  # a non-null, 256-byte aligned stand-in address; never dereferenced
 
 def fwd(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, causal=0, scale=0.125, stream=None,
-             dtype=fa.FA_BF16)
+             dtype=fa.FA_BF16, layout=fa.FA_LAYOUT_BHND)
     a.update(kw)
     return fa.fa_fwd(**a)
 
 
 def bwd(**kw):
     a = dict(q=P, k=P, v=P, o=P, dO=P, lse=P, dq=P, dk=P, dv=P, B=1, H=1, N=128, d=64, causal=0,
-             scale=0.125, workspace=P, workspace_bytes=1 << 30, stream=None, dtype=fa.FA_BF16)
+             scale=0.125, workspace=P, workspace_bytes=1 << 30, stream=None, dtype=fa.FA_BF16,
+             layout=fa.FA_LAYOUT_BHND)
     a.update(kw)
     return fa.fa_bwd(**a)
 
@@ -115,6 +116,7 @@ def bwd(**kw):
     (dict(scale=-0.1), -1), (dict(d=96), -2), (dict(d=256), -2), (dict(dtype=7), -2),
     (dict(q=P + 8), -1), (dict(lse=P + 2), -1),
     (dict(B=1024, H=1024, N=4096, d=128), -2),
+    (dict(layout=2), -1), (dict(layout=-1), -1),
 ])
 def test_fwd_rejects(kw, status):
     assert fwd(**kw) == status
@@ -125,7 +127,7 @@ def test_fwd_rejects(kw, status):
     (dict(dO=None), -1), (dict(dq=None), -1), (dict(dk=None), -1), (dict(dv=None), -1),
     (dict(N=-5), -1), (dict(d=32), -2), (dict(scale=float("-inf")), -1),
     (dict(workspace=None), -3), (dict(workspace_bytes=1000), -3), (dict(workspace=P + 16), -3),
-    (dict(dv=P + 4), -1),
+    (dict(dv=P + 4), -1), (dict(layout=7), -1),
 ])
 def test_bwd_rejects(kw, status):
     assert bwd(**kw) == status

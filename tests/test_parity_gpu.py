@@ -18,8 +18,8 @@ from gpu_util import compare, log, oracle_heads, run_gpu, to_dev, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _full_compare(x, dtype, causal, scale, where):
-    res = run_gpu(x, dtype, causal, scale)
+def _full_compare(x, dtype, causal, scale, where, layout=0):
+    res = run_gpu(x, dtype, causal, scale, layout=layout)
     B, H = x["q"].shape[:2]
     want = oracle_heads(x, causal, scale, heads=None)
     errs = {}
@@ -28,7 +28,7 @@ def _full_compare(x, dtype, causal, scale, where):
         e = compare(got, w, dtype, where=f"{where} head ({b},{h})")
         for n, v in e.items():
             errs[n] = max(errs.get(n, 0.0), v)
-    return errs
+    return errs, res
 
 
 EDGE = [(dtype, d, causal, n)
@@ -59,7 +59,7 @@ def test_workload_c1_fp32():
     w = gen.workload("c1")
     log(f"[workload] {w.name}")
     x = gen.make_inputs(w)
-    errs = _full_compare(x, "fp32", w.causal, w.scale, w.name)
+    errs, _ = _full_compare(x, "fp32", w.causal, w.scale, w.name)
     log(f"  max errors {errs}")
 
 
@@ -67,7 +67,7 @@ def test_workload_c2_bf16():
     w = gen.workload("c2")
     log(f"[workload] {w.name}")
     x = gen.make_inputs(w)
-    errs = _full_compare(x, "bf16", w.causal, w.scale, w.name)
+    errs, _ = _full_compare(x, "bf16", w.causal, w.scale, w.name)
     log(f"  max errors {errs}")
 
 
@@ -199,3 +199,54 @@ def test_atomic_dq_mode(monkeypatch, d, causal, n):
     w = gen.workload("c2")
     x = gen.make_inputs(w, shape=(1, 3, n, d), seed=4242 + n, dtype="bf16")
     _full_compare(x, "bf16", causal, 1.0 / math.sqrt(d), f"atomic d{d} c{int(causal)} N{n}")
+
+
+# [B, N, H, d] inputs (fa.FA_LAYOUT_BNHD): the kernels run the same arithmetic
+# in the same order and only address rows H*d elements apart, so the results
+# must be bit-identical to the [B, H, N, d] run on the transposed data, and
+# meet the oracle bar on their own.
+BNHD = [(dtype, d, causal, n)
+        for dtype in ("bf16", "fp32")
+        for d in (64, 128)
+        for causal in (False, True)
+        for n in (17, 300)]
+
+
+@pytest.mark.parametrize("dtype,d,causal,n", BNHD)
+def test_bnhd_layout(dtype, d, causal, n):
+    log(f"[bnhd] dtype={dtype} d={d} causal={causal} N={n}")
+    w = gen.workload("c2")
+    x = gen.make_inputs(w, shape=(2, 3, n, d), seed=5150 + n + d, dtype=dtype)
+    scale = 1.0 / math.sqrt(d)
+    _, got = _full_compare(x, dtype, causal, scale, f"bnhd {dtype} d{d} c{int(causal)} N{n}",
+                           layout=fa.FA_LAYOUT_BNHD)
+    ref_res = run_gpu(x, dtype, causal, scale)
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        assert np.array_equal(got[name], ref_res[name]), f"bnhd {name} differs from the BHND run"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bnhd_atomic_dq_mode(monkeypatch, causal):
+    monkeypatch.setenv("FA_DQ_MODE", "atomic")
+    log(f"[bnhd-atomic] causal={causal}")
+    w = gen.workload("c2")
+    x = gen.make_inputs(w, shape=(2, 3, 300, 128), seed=616, dtype="bf16")
+    _full_compare(x, "bf16", causal, 1.0 / math.sqrt(128), f"bnhd atomic c{int(causal)}",
+                  layout=fa.FA_LAYOUT_BNHD)
+
+
+def test_bnhd_full_size_matches_bhnd():
+    """At the causal (1, 32, 8192, 128) bf16 size the [B, N, H, d] run is
+    bit-identical to the [B, H, N, d] run, which the sampled-head tests tie to
+    the oracle."""
+    import torch
+    w = gen.workload("c4")
+    log(f"[bnhd-full] {w.name} {w.shape}")
+    x = gen.make_inputs(w)
+    a = run_gpu(x, w.dtype, w.causal, w.scale)
+    a.pop("_dev")
+    b = run_gpu(x, w.dtype, w.causal, w.scale, layout=fa.FA_LAYOUT_BNHD)
+    b.pop("_dev")
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        assert np.array_equal(a[name], b[name]), f"bnhd {name} differs from the BHND run"
+    torch.cuda.empty_cache()
