@@ -19,7 +19,9 @@
  * type named by `dtype` (FA_BF16: bfloat16, FA_FP32: float), all in the
  * layout named by `layout`: FA_LAYOUT_BHND = [B, H, N, d] (each head's rows
  * contiguous) or FA_LAYOUT_BNHD = [B, N, H, d] (each token's H heads
- * contiguous, as a projection writes them, so no transpose is needed).
+ * contiguous, as a projection writes them and as the PyTorch module of the
+ * blog.xiaohack.org "flops" page, item 知识点13, takes its input; no transpose
+ * is needed).  Any other layout value is FA_ERR_INVALID.
  * lse is always float [B, H, N], natural log, in units of the scaled score
  * scale * q_i . k_j.  The causal mask keeps key j for query i iff j <= i
  * (queries and keys share the index range 0..N-1).
