@@ -18,7 +18,7 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "round_bf16", "bf16_bits",
-           "make_inputs", "default_scale"]
+           "make_inputs", "default_scale", "DecodeWorkload", "DECODE", "make_decode_inputs"]
 
 
 @dataclass(frozen=True)
@@ -111,6 +111,55 @@ def make_inputs(w: Workload, shape=None, seed=None, sigma_qk=None, sigma_vdo=Non
     rng = np.random.default_rng(seed)
     out = {}
     for name, sig in (("q", sqk), ("k", sqk), ("v", svd), ("do", svd)):
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        if sig != 1.0:
+            x *= np.float32(sig)
+        if dtype == "bf16":
+            x = round_bf16(x)
+        out[name] = x
+    return out
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq query rows per head against a cache of Nk key/value rows."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+    sigma_qk: float
+    sigma_v: float
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.d)
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V, each read once by the split-key-range forward."""
+        return 2 * self.B * self.H * self.Nk * self.d * (2 if self.dtype == "bf16" else 4)
+
+
+# One decode step of a 32-head, d = 128 model for a batch of 8 sequences with
+# 16384 cached tokens each (the queries are the newest positions).
+DECODE = DecodeWorkload("decode_bf16_b8h32_q1_k16384_d128", 8, 32, 1, 16384, 128, "bf16", True,
+                        1.0, 1.0, 6)
+
+
+def make_decode_inputs(B, H, Nq, Nk, d, seed, dtype="bf16", sigma_qk=1.0, sigma_v=1.0):
+    """Seeded q [B,H,Nq,d], k and v [B,H,Nk,d] as float32 numpy arrays.
+
+    Same recipe as ``make_inputs``: one generator, draw order q, k, v, each
+    standard normal times its spread, rounded to bf16 for bf16 workloads.
+    """
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape, sig in (("q", (B, H, Nq, d), sigma_qk), ("k", (B, H, Nk, d), sigma_qk),
+                             ("v", (B, H, Nk, d), sigma_v)):
         x = rng.standard_normal(size=shape, dtype=np.float32)
         if sig != 1.0:
             x *= np.float32(sig)

@@ -48,6 +48,9 @@ __all__ = [
     "forward",
     "backward",
     "forward_backward",
+    "scores_rect",
+    "head_forward_rect",
+    "forward_rect",
 ]
 
 
@@ -189,3 +192,61 @@ def forward_backward(q, k, v, do, scale, causal, heads=None, panel_rows=2048):
         out[(bi, hi)] = head_panel(f64(q), f64(k), f64(v), f64(do), scale, causal,
                                    panel_rows=panel_rows)
     return out
+
+
+# ---- queries against a longer key sequence (decode) --------------------------
+#
+# The split-key-range forward serves Nq query rows against Nk >= Nq key rows
+# of the same head, the shape of decoding with a key/value cache (page
+# "flash-attention-v2-sram-tiling", the long-document inference scenario; the
+# decoding variant named on page "data.6616ai.com flash-attention").  The pages
+# do not define the causal mask for Nq != Nk; the reading taken here is that
+# the Nq queries are the last Nq positions of the sequence, so query i sits at
+# position Nk - Nq + i and keeps key j iff j <= i + Nk - Nq.  With Nq == Nk
+# this is the square mask above.
+
+
+def scores_rect(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
+    """S = scale * Q K^T for Nq query rows against Nk key rows of one head.
+
+    With ``causal``, S_ij = -inf for j > i + Nk - Nq (the queries are the
+    last Nq positions).  Requires Nq <= Nk when causal.
+    """
+    nq, nk = q.shape[0], k.shape[0]
+    s = scale * (q @ k.T)
+    if causal:
+        if nq > nk:
+            raise ValueError("causal attention needs Nq <= Nk")
+        rows = np.arange(nq)[:, None] + (nk - nq)
+        cols = np.arange(nk)[None, :]
+        s = np.where(cols > rows, -np.inf, s)
+    return s
+
+
+def head_forward_rect(q, k, v, scale, causal):
+    """O (Nq, d) and LSE (Nq,) of one head for Nq queries against Nk keys."""
+    p, _, lse = softmax_rows(scores_rect(q, k, scale, causal))
+    return p @ v, lse
+
+
+def forward_rect(q, k, v, scale, causal, heads=None):
+    """O [B,H,Nq,d] and LSE [B,H,Nq] for q [B,H,Nq,d] against k, v [B,H,Nk,d].
+
+    With ``heads`` (a list of (b, h)), returns a dict keyed by (b, h) of
+    dict(o, lse) for those heads only.
+    """
+    q, k, v = (np.asarray(t) for t in (q, k, v))
+    f64 = lambda t, bi, hi: np.asarray(t[bi, hi], dtype=np.float64)
+    if heads is not None:
+        out = {}
+        for bi, hi in heads:
+            o, lse = head_forward_rect(f64(q, bi, hi), f64(k, bi, hi), f64(v, bi, hi), scale, causal)
+            out[(bi, hi)] = dict(o=o, lse=lse)
+        return out
+    b, h, nq, dh = q.shape
+    o = np.empty((b, h, nq, dh))
+    lse = np.empty((b, h, nq))
+    for bi, hi in _heads(q):
+        o[bi, hi], lse[bi, hi] = head_forward_rect(f64(q, bi, hi), f64(k, bi, hi), f64(v, bi, hi),
+                                                   scale, causal)
+    return o, lse

@@ -45,3 +45,15 @@ def test_workload_table():
     fwd, bwd = c4.flops()
     assert fwd == 4 * 32 * 8192 ** 2 * 128 / 2 and bwd == 10 * 32 * 8192 ** 2 * 128 / 2
     assert c4.scale == 1 / np.sqrt(128)
+
+
+def test_decode_inputs_recipe():
+    from exact_tiled_attention_online_amd import inputs as gen
+    x = gen.make_decode_inputs(2, 3, 4, 50, 64, seed=9)
+    assert x["q"].shape == (2, 3, 4, 64) and x["k"].shape == (2, 3, 50, 64) and x["v"].shape == (2, 3, 50, 64)
+    y = gen.make_decode_inputs(2, 3, 4, 50, 64, seed=9)
+    for n in ("q", "k", "v"):
+        np.testing.assert_array_equal(x[n], y[n])
+        np.testing.assert_array_equal(gen.round_bf16(x[n]), x[n])
+    w = gen.DECODE
+    assert w.Nq <= w.Nk and w.kv_bytes() == 2 * w.B * w.H * w.Nk * w.d * 2
