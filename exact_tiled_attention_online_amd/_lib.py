@@ -18,7 +18,7 @@ FA_BF16, FA_FP32 = 0, 1
 FA_LAYOUT_BHND, FA_LAYOUT_BNHD = 0, 1
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
-           "fa_bwd_dq", "fa_strerror")
+           "fa_bwd_dq", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_strerror")
 
 _lib = None
 
@@ -51,6 +51,10 @@ def load():
     lib.fa_bwd_dkdv.restype = i
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i, i]
     lib.fa_bwd_dq.restype = i
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = sz
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp, i, i]
+    lib.fa_fwd_splitkv.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -89,6 +93,16 @@ def fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, causal, scale, workspace, worksp
               stream, dtype, layout) -> int:
     return load().fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, int(causal), float(scale),
                             workspace, workspace_bytes, stream, dtype, layout)
+
+
+def fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits) -> int:
+    return load().fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, workspace, workspace_bytes,
+                   stream, dtype, layout) -> int:
+    return load().fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale), num_splits,
+                                 workspace, workspace_bytes, stream, dtype, layout)
 
 
 def fa_strerror(status: int) -> str:
@@ -173,3 +187,28 @@ def backward(q, k, v, o, do, lse, causal: bool, scale: float, ws=None, grads=Non
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def forward_splitkv(q, k, v, causal: bool, scale: float, num_splits: int = 0, out=None, lse=None, ws=None,
+                    stream=None, layout: int = FA_LAYOUT_BHND):
+    """O, LSE for q [B,H,Nq,d] against k, v [B,H,Nk,d] (bf16 device tensors;
+    [B,Nq,H,d] / [B,Nk,H,d] with FA_LAYOUT_BNHD) through the split-key-range
+    forward.  With ``causal`` the queries are the last Nq positions."""
+    import torch
+    B, H, Nq, d = _dims(q, layout)
+    Nk = _dims(k, layout)[2]
+    _check((q,), q.shape)
+    _check((k, v), k.shape)
+    if k.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if ws is None:
+        n = fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Nq, Nk,
+                        d, causal, scale, num_splits, ws.data_ptr(), ws.numel(), _stream(stream),
+                        _dtype_code(q), layout)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_splitkv")
+    return o, l

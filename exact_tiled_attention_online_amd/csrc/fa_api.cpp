@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -70,6 +71,54 @@ bool dq_atomic_mode() {
 
 bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d, int dtype) {
   return ws && aligned(ws, kAlign) && bytes >= carve(nullptr, B, H, N, d, dtype).bytes;
+}
+
+// Key ranges of the split forward.  num_splits = 0 lets the library choose:
+// about kSplitTargetWGs workgroups in all, at least 4 tiles per range, at most
+// kMaxAutoSplits ranges.  Ranges are whole tiles and none is empty.
+constexpr int kMaxAutoSplits = 256;
+constexpr int kMaxSplits = 1024;
+constexpr long long kSplitTargetWGs = 1024;
+
+struct SplitPlan {
+  int nsplit, span;
+  float* opart;
+  float* lpart;
+  size_t bytes;
+};
+
+SplitPlan split_plan(void* base, int B, int H, int Nq, int Nk, int d, int num_splits) {
+  const int tiles = (Nk + fa::kSplitBC - 1) / fa::kSplitBC;
+  long long s = num_splits;
+  if (s <= 0) {
+    const long long wgs = (long long)B * H * ((Nq + 31) / 32);
+    s = std::min<long long>(kMaxAutoSplits, std::max<long long>(1, (kSplitTargetWGs + wgs - 1) / wgs));
+    s = std::min<long long>(s, std::max(1, tiles / 4));
+  }
+  s = std::min<long long>(s, tiles);
+  const int per = (int)((tiles + s - 1) / s);   // tiles per range
+  SplitPlan p{};
+  p.nsplit = (tiles + per - 1) / per;
+  p.span = per * fa::kSplitBC;
+  const size_t rows = (size_t)B * H * Nq;
+  char* c = static_cast<char*>(base);
+  p.opart = reinterpret_cast<float*>(c);
+  const size_t ob = round_up((size_t)p.nsplit * rows * d * sizeof(float));
+  p.lpart = reinterpret_cast<float*>(c + ob);
+  p.bytes = ob + round_up((size_t)p.nsplit * rows * sizeof(float));
+  return p;
+}
+
+int check_split(int B, int H, int Nq, int Nk, int d, int causal, float scale, int num_splits, int dtype,
+                int layout) {
+  int st = check_shape(B, H, Nq, d, causal, scale, dtype, layout);
+  if (st != FA_OK) return st;
+  st = check_shape(B, H, Nk, d, causal, scale, dtype, layout);
+  if (st != FA_OK) return st;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (causal && Nq > Nk) return FA_ERR_INVALID;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID;
+  return FA_OK;
 }
 
 }  // namespace
@@ -174,12 +223,37 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                    layout);
 }
 
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  if (check_split(B, H, Nq, Nk, d, 0, 1.f, num_splits, FA_BF16, FA_LAYOUT_BHND) != FA_OK) return 0;
+  return split_plan(nullptr, B, H, Nq, Nk, d, num_splits).bytes;
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                   int Nk, int d, int causal, float scale, int num_splits, void* workspace,
+                   size_t workspace_bytes, void* stream, int dtype, int layout) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
+  const int st = check_split(B, H, Nq, Nk, d, causal, scale, num_splits, dtype, layout);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  if (!workspace || !aligned(workspace, kAlign) ||
+      workspace_bytes < split_plan(nullptr, B, H, Nq, Nk, d, num_splits).bytes)
+    return FA_ERR_WORKSPACE;
+  const SplitPlan p = split_plan(workspace, B, H, Nq, Nk, d, num_splits);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const fa::RowLayout lay = row_layout(H, layout);
+  const int r = hip_status(fa::launch_fwd_split_bf16(q, k, v, p.opart, p.lpart, B * H, Nq, Nk, d, causal != 0,
+                                                     scale, p.nsplit, p.span, lay, s));
+  if (r != FA_OK) return r;
+  return hip_status(fa::launch_fwd_merge(p.opart, p.lpart, o, lse, B * H, Nq, d, p.nsplit, lay, s));
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad size, flag or scale)";
     case FA_ERR_UNSUPPORTED: return "unsupported head dim, dtype or size";
-    case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or too small";
+    case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP runtime reported a launch error";
     default: return "unknown status";
   }

@@ -11,6 +11,14 @@
 // (fp32) loads, reduced across those lanes with xor-shuffles.
 //
 // dq_convert: dQ = bf16(scale * acc), 8 elements per thread, 16-byte stores.
+//
+// fwd_merge: the key ranges of the split forward joined per query row.  With
+// each range's LSE_s and O_s (normalised by its own sum), m = max_s LSE_s,
+// LSE = m + ln sum_s exp(LSE_s - m) and O = sum_s exp(LSE_s - LSE) O_s: the
+// rule for joining partial softmax results (page
+// "flash-attention-v2-sram-tiling" (aiqz.cc), quiz question 10: take the
+// larger maximum and rescale each partial sum to it), with each range's sum
+// expressed at its own LSE.  d/8 lanes per row, 8 elements each.
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -112,6 +120,59 @@ hipError_t launch_dq_convert(const float* dq_acc, void* dq, int BH, int N, int d
   const size_t n8 = (size_t)BH * N * d / 8;
   const dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
   hipLaunchKernelGGL(dq_convert_kernel, grid, block, 0, stream, dq_acc, (bf16*)dq, n8, scale, N, d, lay);
+  return hipGetLastError();
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict__ opart,
+                                                        const float* __restrict__ lpart, bf16* __restrict__ O,
+                                                        float* __restrict__ LSE, int rows, int N, int nsplit,
+                                                        RowLayout lay) {
+  constexpr int LPR = D / 8;            // lanes per row, 8 elements each
+  constexpr int RPB = 256 / LPR;        // rows per block
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x * RPB + tid / LPR;
+  const int part = tid % LPR;
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lpart[(size_t)s * rows + row]);
+  float wsum = 0.f, acc[8] = {};
+  for (int s = 0; s < nsplit; ++s) {
+    const float ls = lpart[(size_t)s * rows + row];
+    // a range in which the row sees no key has LSE -inf and weight 0
+    const float w = ls == -INFINITY ? 0.f : exp2_fast((ls - m) * kLog2e);
+    wsum += w;
+    const float4* op = reinterpret_cast<const float4*>(opart + ((size_t)s * rows + row) * D + part * 8);
+    const float4 a = op[0], b = op[1];
+    acc[0] = fmaf(w, a.x, acc[0]);
+    acc[1] = fmaf(w, a.y, acc[1]);
+    acc[2] = fmaf(w, a.z, acc[2]);
+    acc[3] = fmaf(w, a.w, acc[3]);
+    acc[4] = fmaf(w, b.x, acc[4]);
+    acc[5] = fmaf(w, b.y, acc[5]);
+    acc[6] = fmaf(w, b.z, acc[6]);
+    acc[7] = fmaf(w, b.w, acc[7]);
+  }
+  const float inv = 1.f / wsum;
+  const int hb = row / N, n = row - hb * N;
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)(acc[e] * inv);
+  *reinterpret_cast<bf16x8*>(O + lay.head_off(hb, N, D) + (size_t)n * lay.row_stride(D) + part * 8) = r;
+  if (part == 0) LSE[row] = m + log2_fast(wsum) * kLn2;
+}
+
+hipError_t launch_fwd_merge(const float* opart, const float* lpart, void* o, float* lse, int BH, int Nq,
+                            int d, int nsplit, RowLayout lay, hipStream_t stream) {
+  const int rows = BH * Nq;
+  const int rpb = 256 / (d / 8);
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
+  if (d == 128)
+    hipLaunchKernelGGL((fwd_merge_kernel<128>), grid, block, 0, stream, opart, lpart, (bf16*)o, lse, rows, Nq,
+                       nsplit, lay);
+  else
+    hipLaunchKernelGGL((fwd_merge_kernel<64>), grid, block, 0, stream, opart, lpart, (bf16*)o, lse, rows, Nq,
+                       nsplit, lay);
   return hipGetLastError();
 }
 

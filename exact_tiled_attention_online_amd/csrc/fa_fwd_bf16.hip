@@ -23,6 +23,13 @@
 // p = 2^(c*s - c*m) with c = scale*log2(e).  Each tile is a fixed sequence of
 // slots (S products, the softmax, P V products) separated by scheduling
 // fences, with the LDS operands of each slot read a few slots ahead.
+//
+// Split-key-range mode (SPLIT): Nq query rows against Nk >= Nq key rows (the
+// decode shape), the key range of each head cut into contiguous ranges; each
+// workgroup runs the same online softmax over one range for one query block
+// and writes that range's O (normalised by its own l) and LSE.  The merge
+// kernel then combines the ranges with the rule for joining two partial
+// softmax results (page "flash-attention-v2-sram-tiling", quiz question 10).
 #include "fa_common.h"
 #include "fa_launch.h"
 
@@ -31,16 +38,27 @@ namespace fa {
 #ifndef FA_FWD_NW
 #define FA_FWD_NW 8
 #endif
-template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c,
-    RowLayout lay) {
 #ifndef FA_FWD_BC64
 #define FA_FWD_BC64 128
 #endif
-  // key rows per tile: 128 where the registers allow it (d = 64), else 64
-  constexpr int BR = 32 * NW, BC = D == 64 ? FA_FWD_BC64 : 64;
+// Arguments of the split-key-range mode (unused otherwise).
+struct SplitArgs {
+  int Nk;         // key/value rows per head
+  int off;        // causal offset: query row i sits at key position i + off (off = Nk - Nq)
+  int nsplit;     // key ranges per head
+  int span;       // keys per range, a multiple of the tile
+  float* opart;   // [nsplit][BH][N][D]: each range's O, normalised by its own l
+  float* lpart;   // [nsplit][BH][N]: each range's LSE, -inf where a row sees no key of it
+};
+
+template <int D, bool CAUSAL, int NW, int BC, bool SPLIT>
+__global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c,
+    RowLayout lay, SplitArgs sp) {
+  // BC: key rows per tile (128 where the registers allow it (d = 64), else 64;
+  // 32 in the split mode, whose one-wave workgroups need little LDS)
+  constexpr int BR = 32 * NW;
   constexpr int MT = BC / 32;        // 32-key halves of a tile
   constexpr int ROWB = D * 2;        // bytes per row
   constexpr int KS = D / 16;         // K-steps of the S product
@@ -61,12 +79,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
   const TileFetch<D * 2, BC, NW> fetch(wave, lane, RS * 2);
   const int bid = blockIdx.x;
   const int head = bid % BH;
-  // causal: the longest query blocks are dispatched first
-  const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
+  const int Nk = SPLIT ? sp.Nk : N;     // key rows
+  const int off = SPLIT ? sp.off : 0;   // causal offset of the query rows
+  int qb, split = 0;
+  if constexpr (SPLIT) {
+    split = (bid / BH) % sp.nsplit;
+    qb = bid / BH / sp.nsplit;
+  } else {
+    // causal: the longest query blocks are dispatched first
+    qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
+  }
   const size_t hoff = lay.head_off(head, N, D);
+  const size_t khoff = lay.head_off(head, Nk, D);
   const bf16* Qh = Q + hoff;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
+  const bf16* Kh = K + khoff;
+  const bf16* Vh = V + khoff;
 
   const int q0 = qb * BR + wave * 32;   // first query row of this wave
   const int qrow = q0 + l32;            // the query row this lane's statistics belong to
@@ -82,12 +109,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
       qf[s] = bf16x8{};
   }
 
-  const int kv_end = CAUSAL ? min(N, qb * BR + BR) : N;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  // keys of this workgroup: tiles jlo .. jlo + ntiles - 1 (all keys of the
+  // head unless split), cut at the causal limit of the block's last row
+  int kv_lo = 0, kv_end = Nk;
+  if constexpr (SPLIT) {
+    kv_lo = split * sp.span;
+    kv_end = min(Nk, kv_lo + sp.span);
+  }
+  if (CAUSAL) kv_end = min(kv_end, qb * BR + BR + off);
+  const int jlo = kv_lo / BC;
+  const int ntiles = max(0, (kv_end + BC - 1) / BC - jlo);
   int wave_tiles = 0;
   if (q0 < N) {
-    const int wkv_end = CAUSAL ? min(N, q0 + 32) : N;
-    wave_tiles = (wkv_end + BC - 1) / BC;
+    const int wkv_end = CAUSAL ? min(kv_end, q0 + 32 + off) : kv_end;
+    wave_tiles = max(0, (wkv_end + BC - 1) / BC - jlo);
   }
 
 
@@ -105,8 +140,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     const char* Kt = b ? sK1 : sK0;
     const char* Vt = b ? sV1 : sV0;
     if (j + 1 < ntiles) {
-      fetch(Kh, (j + 1) * BC, N, b ? sK0 : sK1);
-      fetch(Vh, (j + 1) * BC, N, b ? sV0 : sV1);
+      fetch(Kh, (jlo + j + 1) * BC, Nk, b ? sK0 : sK1);
+      fetch(Vh, (jlo + j + 1) * BC, Nk, b ? sV0 : sV1);
     }
     if (j < wave_tiles) {
       // Slots: KS slots of S products (two 32-key halves per K-step), then
@@ -134,7 +169,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
       bf16x8 pb[BC / 16];
-      const int kvb = j * BC;
+      const int kvb = (jlo + j) * BC;
 #pragma unroll
       for (int i = 0; i < DIST; ++i) read_slot(i);
 #pragma clang loop unroll(full)
@@ -150,15 +185,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
         }
         if (i != KS - 1) continue;
         __builtin_amdgcn_sched_barrier(0);
-        // s[mt][4*i+jj] = q_qrow . k_kv with kv = j*BC + 32*mt + 8*i + 4*h + jj
-        const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0);
+        // s[mt][4*i+jj] = q_qrow . k_kv with kv = kvb + 32*mt + 8*i + 4*h + jj
+        const bool need_mask = (kvb + BC > Nk) || (CAUSAL && kvb + BC - 1 > q0 + off);
         if (need_mask) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-              const bool dead = (kv >= N) | (CAUSAL & (kv > qrow));
+              const bool dead = (kv >= Nk) | (CAUSAL & (kv > qrow + off));
               s[mt][r] = dead ? -INFINITY : s[mt][r];
             }
         }
@@ -173,9 +208,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
         // probabilities are taken against the old reference, which keeps them
         // below 2^8 and changes nothing but the rounding (O and l carry the
         // same factor, and LSE = scale*m_run + ln l for any reference).  Key 0
-        // is never masked, so the first tile always sets a finite reference.
+        // is never masked, so the first tile always sets a finite reference;
+        // in the split mode a row may see no key of a tile or of its whole
+        // range, and its reference stays -inf (no rescale, p = 0) until it does.
         if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 8.f) != 0) {
-          const float alpha = exp2_fast((m_run - mx) * c);
+          const float alpha = (SPLIT && m_run == -INFINITY) ? 0.f : exp2_fast((m_run - mx) * c);
           l_run *= alpha;
 #pragma unroll
           for (int t = 0; t < DT; ++t)
@@ -183,7 +220,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
             for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
           m_run = mx;
         }
-        const float nb = -m_run * c;
+        const float nb = (SPLIT && m_run == -INFINITY) ? 0.f : -m_run * c;
         float rs = 0.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -208,8 +245,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
     __syncthreads();
   };
 
-  fetch(Kh, 0, N, sK0);
-  fetch(Vh, 0, N, sV0);
+  fetch(Kh, jlo * BC, Nk, sK0);
+  fetch(Vh, jlo * BC, Nk, sV0);
   __syncthreads();
   for (int j = 0;;) {
     body(IC<0>{}, j);
@@ -220,6 +257,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 
   if (q0 >= N) return;
   const float l_tot = half_sum(l_run);
+  if constexpr (SPLIT) {
+    if (qrow < N) {
+      // this range's O and LSE; a row that saw no key of the range has l = 0
+      const bool seen = l_tot > 0.f;
+      const float inv = seen ? 1.f / l_tot : 0.f;
+      const size_t prow = ((size_t)split * BH + head) * N + qrow;
+      float* orow = sp.opart + prow * D;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float4 v;
+          v.x = oacc[t][4 * i + 0] * inv;
+          v.y = oacc[t][4 * i + 1] * inv;
+          v.z = oacc[t][4 * i + 2] * inv;
+          v.w = oacc[t][4 * i + 3] * inv;
+          *reinterpret_cast<float4*>(orow + 32 * t + 8 * i + 4 * h) = v;
+        }
+      if (h == 0) sp.lpart[prow] = seen ? m_run * scale + log2_fast(l_tot) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (qrow < N) {
     const float inv = 1.f / l_tot;
     bf16* Orow = O + hoff + (size_t)qrow * RS;
@@ -241,12 +300,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse,
                                     int BH, int N, float scale, RowLayout lay, hipStream_t stream) {
-  constexpr int NW = FA_FWD_NW, BR = 32 * NW;
+  constexpr int NW = FA_FWD_NW, BR = 32 * NW, BC = D == 64 ? FA_FWD_BC64 : 64;
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW>), grid, block, 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, false>), grid, block, 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
-                     scale * kLog2e, lay);
+                     scale * kLog2e, lay, SplitArgs{});
   return hipGetLastError();
 }
 
@@ -257,6 +316,31 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                   : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
   return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
                 : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
+}
+
+// Split mode: one-wave workgroups of 32 query rows, 32-key tiles (16 KB of
+// LDS per K/V tile pair at d = 128, so several workgroups share a CU).
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v, int BH, int Nq,
+                                     float scale, RowLayout lay, const SplitArgs& sp, hipStream_t stream) {
+  constexpr int NW = 1, BR = 32 * NW;
+  const int nqb = (Nq + BR - 1) / BR;
+  const dim3 grid((unsigned)(nqb * sp.nsplit * BH)), block(64 * NW);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, kSplitBC, true>), grid, block, 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, nullptr, nullptr, BH, Nq, nqb, scale,
+                     scale * kLog2e, lay, sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, float* opart, float* lpart,
+                                 int BH, int Nq, int Nk, int d, bool causal, float scale, int nsplit,
+                                 int span, RowLayout lay, hipStream_t stream) {
+  const SplitArgs sp{Nk, Nk - Nq, nsplit, span, opart, lpart};
+  if (d == 128)
+    return causal ? launch_fwd_split_t<128, true>(q, k, v, BH, Nq, scale, lay, sp, stream)
+                  : launch_fwd_split_t<128, false>(q, k, v, BH, Nq, scale, lay, sp, stream);
+  return causal ? launch_fwd_split_t<64, true>(q, k, v, BH, Nq, scale, lay, sp, stream)
+                : launch_fwd_split_t<64, false>(q, k, v, BH, Nq, scale, lay, sp, stream);
 }
 
 }  // namespace fa

@@ -26,6 +26,19 @@ struct RowLayout {
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                            int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream);
 
+// Split-key-range bf16 forward (Nq queries against Nk >= Nq keys): the keys
+// of each head are cut into nsplit ranges of `span` keys (a multiple of
+// kSplitBC); writes each range's O (fp32, normalised by its own sum) to opart
+// [nsplit][BH][Nq][d] and its LSE to lpart [nsplit][BH][Nq].
+constexpr int kSplitBC = 32;
+hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, float* opart, float* lpart,
+                                 int BH, int Nq, int Nk, int d, bool causal, float scale, int nsplit,
+                                 int span, RowLayout lay, hipStream_t stream);
+
+// Combines the ranges of the split forward: O (bf16, layout lay) and LSE.
+hipError_t launch_fwd_merge(const float* opart, const float* lpart, void* o, float* lse, int BH, int Nq,
+                            int d, int nsplit, RowLayout lay, hipStream_t stream);
+
 // Backward preprocess: ndrow = -rowsum(dO o O) (fp32), nlse = -LSE / scale,
 // and, when dq_acc is not null, dq_acc = 0.  `fp32` selects the input type.
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ndrow, float* nlse,

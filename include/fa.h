@@ -54,7 +54,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID = -1,      /* null pointer, non-positive size, bad flag, bad scale */
   FA_ERR_UNSUPPORTED = -2,  /* head dim or dtype this build has no kernel for */
-  FA_ERR_WORKSPACE = -3,    /* backward workspace missing or too small */
+  FA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
   FA_ERR_HIP = -4           /* the HIP runtime reported a launch error */
 } fa_status;
 
@@ -125,6 +125,39 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, con
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
               void* dq, int B, int H, int N, int d, int causal, float scale,
               void* workspace, size_t workspace_bytes, void* stream, int dtype, int layout);
+
+/*
+ * Forward for Nq query rows against Nk key/value rows per head (the decode
+ * shape: a few new tokens against a long key/value cache), with the keys of
+ * each head cut into ranges that separate workgroups process at once.
+ *
+ * q, o: [B, H, Nq, d] (or [B, Nq, H, d]); k, v: [B, H, Nk, d] (or
+ * [B, Nk, H, d]), all bf16, in the layout named by `layout`; lse: float
+ * [B, H, Nq].  With causal = 1 the queries are the last Nq positions of the
+ * sequence: query i keeps key j iff j <= i + Nk - Nq (requires Nq <= Nk; with
+ * Nq == Nk this is fa_fwd's mask).  The results are those of the plain
+ * definition, as for fa_fwd.
+ *
+ * Each range runs the online softmax of page "flash-attention-v2-sram-tiling"
+ * (aiqz.cc), section 5, and leaves its O and its LSE in the workspace; a
+ * second kernel joins the ranges per row with the rule for merging partial
+ * softmax results (same page, quiz question 10: the larger maximum, each
+ * partial sum rescaled to it).
+ *
+ * num_splits: key ranges per head; 0 lets the library choose (about 1024
+ * workgroups in all, at least 128 keys per range, at most 256 ranges).
+ * Ranges are whole 32-key tiles and none is left empty, so fewer ranges than
+ * asked may be used.  The workspace must hold
+ * fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits) bytes (same
+ * num_splits), 256-byte aligned; its contents on entry do not matter.
+ * Supported: dtype FA_BF16 only (FA_ERR_UNSUPPORTED otherwise), d in
+ * {64, 128}, 0 <= num_splits <= 1024.  Errors, ownership and streams as for
+ * fa_fwd; a missing or small workspace is FA_ERR_WORKSPACE.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, int causal, float scale, int num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream, int dtype, int layout);
 
 /* Static, human-readable text for a status code. */
 const char* fa_strerror(int status);

@@ -144,3 +144,41 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(ImportError):
         _lib.load()
+
+
+def splitkv(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=4, Nk=1000, d=128, causal=1, scale=0.125,
+             num_splits=0, workspace=P, workspace_bytes=1 << 30, stream=None, dtype=fa.FA_BF16,
+             layout=fa.FA_LAYOUT_BHND)
+    a.update(kw)
+    return fa.fa_fwd_splitkv(**a)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(Nq=0), -1), (dict(Nk=0), -1), (dict(Nq=1001), -1), (dict(causal=2), -1),
+    (dict(num_splits=-1), -1), (dict(num_splits=1025), -1), (dict(layout=3), -1),
+    (dict(scale=float("nan")), -1), (dict(d=96), -2), (dict(dtype=fa.FA_FP32), -2), (dict(dtype=5), -2),
+    (dict(q=P + 8), -1), (dict(workspace=None), -3), (dict(workspace_bytes=100), -3),
+    (dict(workspace=P + 64), -3), (dict(B=64, H=64, Nk=1 << 20), -2),
+])
+def test_splitkv_rejects(kw, status):
+    assert splitkv(**kw) == status
+
+
+@needs_lib
+def test_splitkv_noncausal_allows_more_queries_than_keys_and_sizes_workspace():
+    # the query count may exceed the key count when not causal: only the
+    # workspace check stops this call (a null-free, too-small workspace)
+    assert splitkv(causal=0, Nq=2000, workspace_bytes=10) == -3
+    rows, tile = 1 * 2 * 4, 32
+    for ns in (1, 3, 7):
+        n = fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 1000, 128, ns)
+        tiles = (1000 + tile - 1) // tile
+        per = -(-tiles // ns)
+        used = -(-tiles // per)
+        r = lambda x: -(-x // 256) * 256
+        assert n == r(used * rows * 128 * 4) + r(used * rows * 4), ns
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 1000, 96, 0) == 0
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 1000, 128, 2000) == 0
