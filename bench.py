@@ -12,7 +12,9 @@ value = credited FLOPs of a step / step time, with the credited counts
 fwd = 4*B*H*N^2*d and bwd = 10*B*H*N^2*d, both halved for a causal mask.
 
 Prints one JSON line.  Default workload: B=1, H=32, N=8192, d=128, causal,
-bf16 (the headline shape).
+bf16 (the headline shape).  ``detail.decode`` adds the split-key-range forward
+(fa_fwd_splitkv) on a decode step of 8 x 32 heads, one query against 16384
+cached keys, with its HBM roofline (skip with --no-decode).
 """
 from __future__ import annotations
 
@@ -184,6 +186,75 @@ def oracle_check(w, heads, want, got):
             "max_err_over_tolerance": errs, "within_tolerance": ok}
 
 
+def decode_measurement(fa, gen, torch, dev, stream, with_oracle, reps=50, oracle_budget_s=4.0):
+    """The split-key-range forward (fa_fwd_splitkv) on the decode workload:
+    time per call from HIP events on the launch stream, its HBM roofline on the
+    algorithmic bytes (K, V and Q read once, O and LSE written once), and,
+    unless disabled, the oracle on whole heads as a check and a timed CPU
+    baseline in the same unit."""
+    import numpy as np
+    w = gen.DECODE
+    x = gen.make_decode_inputs(w.B, w.H, w.Nq, w.Nk, w.d, seed=w.seed, sigma_qk=w.sigma_qk, sigma_v=w.sigma_v)
+    q, k, v = (torch.from_numpy(x[n]).to(dev).to(torch.bfloat16) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    nbytes = fa.fa_fwd_splitkv_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, 0)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    sp = stream.cuda_stream
+
+    def call():
+        st = fa.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B,
+                               w.H, w.Nq, w.Nk, w.d, w.causal, w.scale, 0, ws.data_ptr(), ws.numel(), sp,
+                               fa.FA_BF16, fa.FA_LAYOUT_BHND)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd_splitkv")
+
+    for _ in range(10):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    algo = w.kv_bytes() + 2 * w.B * w.H * w.Nq * w.d * 2 + 4 * w.B * w.H * w.Nq
+    gbs = algo / (ms * 1e-3) / 1e9
+    res = {"workload": w.name,
+           "config": {"B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+                      "scale": w.scale, "num_splits": "auto",
+                      "inputs": f"N(0,{w.sigma_qk}^2) q,k; N(0,{w.sigma_v}^2) v; seed {w.seed}"},
+           "us_per_call": round(ms * 1e3, 2), "calls": reps,
+           "roofline": {"kernel": "fwd_bf16_kernel (split mode) + fwd_merge_kernel", "bound": "hbm",
+                        "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                        "algorithmic_bytes": int(algo)}}
+    if with_oracle:
+        from oracle import ref
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()
+        done, worst, t0 = 0, {"o": 0.0, "lse": 0.0}, time.perf_counter()
+        while done < len(heads):
+            b, h = heads[done]
+            r = ref.forward_rect(x["q"], x["k"], x["v"], w.scale, w.causal, heads=[(b, h)])[(b, h)]
+            worst["o"] = max(worst["o"], float(np.abs(got_o[b, h] - r["o"]).max())
+                             / (2e-2 * max(1e-2, float(np.abs(r["o"]).max()))))
+            worst["lse"] = max(worst["lse"], float(np.abs(got_l[b, h] - r["lse"]).max()) / 1e-3)
+            done += 1
+            if time.perf_counter() - t0 > oracle_budget_s:
+                break
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(algo * done / len(heads) / dt / 1e9, 3), "unit": "GB/s",
+                               "kind": "oracle",
+                               "sample": f"{done} of {len(heads)} heads, fp64 materialised forward, {dt:.1f} s"}
+        res["oracle_check"] = {"heads": done, "max_err_over_tolerance": {n: round(v, 4) for n, v in worst.items()},
+                               "within_tolerance": all(v <= 1.0 for v in worst.values())}
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +262,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4", help="c1..c5 (default c4, the headline shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the split-key-range forward on the decode workload (reported under detail)")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write a scratch buffer of this many MiB between timed steps (untimed), so "
                          "that the 256 MB last-level cache holds no inputs; the step time is then the "
@@ -372,6 +445,8 @@ def main():
             "peak_from_cus_at_2p4ghz": round(props.multi_processor_count * 4096 * 2.4e9 / 1e12, 1),
         },
     }
+    if not args.no_decode:
+        out["detail"]["decode"] = decode_measurement(fa, gen, torch, dev, stream, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         base, heads, ref = cpu_baseline(w, x)
         out["cpu_baseline"] = base
