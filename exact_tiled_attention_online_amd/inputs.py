@@ -18,7 +18,8 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "round_bf16", "bf16_bits",
-           "make_inputs", "default_scale", "DecodeWorkload", "DECODE", "make_decode_inputs"]
+           "make_inputs", "default_scale", "DecodeWorkload", "DECODE", "make_decode_inputs",
+           "e4m3_bits", "e4m3_to_f32", "make_fp8_inputs", "FP8_DESCALE"]
 
 
 @dataclass(frozen=True)
@@ -166,4 +167,64 @@ def make_decode_inputs(B, H, Nq, Nk, d, seed, dtype="bf16", sigma_qk=1.0, sigma_
         if dtype == "bf16":
             x = round_bf16(x)
         out[name] = x
+    return out
+
+
+# ---- FP8 (OCP e4m3fn) inputs ---------------------------------------------------
+#
+# e4m3fn: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities; the
+# codes S.1111.111 are NaN; largest finite value 448, smallest normal 2^-6,
+# subnormals k * 2^-9.
+
+def e4m3_to_f32(codes: np.ndarray) -> np.ndarray:
+    """float32 values of uint8 e4m3fn codes (NaN for S.1111.111)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int32)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return (sign * mag).astype(np.float32)
+
+
+_E4M3_POS = e4m3_to_f32(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)   # codes 0 .. 0x7E
+
+
+def e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """uint8 e4m3fn codes of float32 values, rounded to nearest, ties to the
+    even code; NaN and magnitudes above 448 give the NaN code."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x).astype(np.float64)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 1, len(_E4M3_POS) - 1)
+    lo = hi - 1
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(a <= _E4M3_POS[0], 0, code).astype(np.uint8)
+    code = np.where(np.isnan(a) | (a > 448.0), 0x7F, code).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << 7)
+
+
+# Per-tensor descale of the FP8 inputs: the stored code times 2^-6 is the
+# value, so standard-normal data (|x| < 7 at these sizes) stays below 448.
+FP8_DESCALE = 2.0 ** -6
+
+
+def make_fp8_inputs(shape, seed, sigma_qk=1.0, sigma_v=1.0, descale=FP8_DESCALE):
+    """Seeded FP8 q, k, v of one [B,H,N,d] shape: the e4m3fn codes (uint8),
+    the per-tensor descales, and the values they stand for (float32, exact:
+    code value times a power of two), which is what the oracle sees.
+
+    Recipe: one generator, draw order q, k, v, each standard normal times its
+    spread, divided by the descale, clipped to +-448 and rounded to e4m3fn."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, sig in (("q", sigma_qk), ("k", sigma_qk), ("v", sigma_v)):
+        x = rng.standard_normal(size=tuple(shape), dtype=np.float32)
+        if sig != 1.0:
+            x *= np.float32(sig)
+        codes = e4m3_bits(np.clip(x / np.float32(descale), -448.0, 448.0))
+        out[name + "8"] = codes
+        out[name] = (e4m3_to_f32(codes) * np.float32(descale)).astype(np.float32)
+        out["descale_" + name] = float(descale)
     return out
