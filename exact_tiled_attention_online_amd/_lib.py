@@ -18,7 +18,7 @@ FA_BF16, FA_FP32 = 0, 1
 FA_LAYOUT_BHND, FA_LAYOUT_BNHD = 0, 1
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
-           "fa_bwd_dq", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_strerror")
+           "fa_bwd_dq", "fa_fwd_fp8", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_strerror")
 
 _lib = None
 
@@ -51,6 +51,8 @@ def load():
     lib.fa_bwd_dkdv.restype = i
     lib.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i, i]
     lib.fa_bwd_dq.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, vp, i]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp, i, i]
@@ -93,6 +95,12 @@ def fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, causal, scale, workspace, worksp
               stream, dtype, layout) -> int:
     return load().fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, int(causal), float(scale),
                             workspace, workspace_bytes, stream, dtype, layout)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, causal, scale, descale_q, descale_k, descale_v, stream,
+               layout) -> int:
+    return load().fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), float(descale_q),
+                             float(descale_k), float(descale_v), stream, layout)
 
 
 def fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits) -> int:
@@ -211,4 +219,22 @@ def forward_splitkv(q, k, v, causal: bool, scale: float, num_splits: int = 0, ou
                         _dtype_code(q), layout)
     if st != FA_OK:
         raise FAError(st, "fa_fwd_splitkv")
+    return o, l
+
+
+def forward_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, causal: bool, scale: float,
+                out=None, lse=None, stream=None, layout: int = FA_LAYOUT_BHND):
+    """O (bf16), LSE for e4m3fn codes q8, k8, v8 (uint8 device tensors of one
+    shape, [B,H,N,d] or [B,N,H,d]) standing for descale * code."""
+    import torch
+    B, H, N, d = _dims(q8, layout)
+    _check((q8, k8, v8), q8.shape)
+    if q8.dtype != torch.uint8:
+        raise TypeError("FP8 inputs are passed as uint8 e4m3fn codes")
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    st = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, N, d, causal,
+                    scale, descale_q, descale_k, descale_v, _stream(stream), layout)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
     return o, l

@@ -223,6 +223,22 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                    layout);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               int causal, float scale, float descale_q, float descale_k, float descale_v, void* stream,
+               int layout) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, causal, scale, FA_BF16, layout);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  for (float x : {descale_q, descale_k, descale_v})
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID;
+  if (!std::isfinite(scale * descale_q * descale_k) || !(scale * descale_q * descale_k > 0.f)) return FA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  return hip_status(fa::launch_fwd_fp8(q, k, v, o, lse, B * H, N, causal != 0, scale, descale_q, descale_k,
+                                       descale_v, row_layout(H, layout), static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
   if (check_split(B, H, Nq, Nk, d, 0, 1.f, num_splits, FA_BF16, FA_LAYOUT_BHND) != FA_OK) return 0;
   return split_plan(nullptr, B, H, Nq, Nk, d, num_splits).bytes;

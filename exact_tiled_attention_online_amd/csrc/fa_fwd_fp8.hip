@@ -1,0 +1,304 @@
+// fa_fwd_fp8.hip -- forward kernel with FP8 (OCP e4m3fn) Q, K, V and per-tensor
+// descales; O in bf16, LSE in fp32.
+//
+// The method is the forward of fa_fwd_bf16.hip (online softmax, page
+// "flash-attention-v2-sram-tiling" (aiqz.cc), section 5; deferred
+// normalisation as in the NumPy demo of page
+// "flash-attention-backpropagation", section Python 演示), with both products
+// on gfx950's FP8 matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3
+// operands, unit block scales, fp32 accumulation), which does twice the work
+// per cycle of the bf16 one.  The FP8 forward of FlashAttention-3 is the
+// variant the pages name (page "data.6616ai.com flash-attention"); this is a
+// gfx950 design of it.
+//
+// Values: Q = descale_q * Q8 and so on, so S = (scale * descale_q * descale_k)
+// * (Q8 K8^T) and O = descale_v * softmax(S) V8.  The dot products of e4m3
+// codes are exact in fp32, so S and the softmax statistics (m, l, LSE) are as
+// accurate as in the bf16 kernel.  P is rounded to e4m3 for the P V product:
+// each probability is taken as p * 2^7 <= 2^8 (the reference maximum moves
+// whenever a row's maximum grows by more than a factor 2^1), which keeps it
+// below the e4m3 limit of 448 and above the subnormal range for every p that
+// matters; l sums the same scaled values in fp32, so the factor cancels in
+// O = sum(P V) / l and LSE subtracts 7 ln 2.
+//
+// Work split: one workgroup (8 waves, two per SIMD) owns 256 query rows of one
+// (batch, head), each wave 32; key/value tiles of 64 rows of 128 bytes stream
+// through two LDS buffers.  Per tile and wave:
+//   S^T (2 x 32 keys x 32 queries): A = K rows (natural 16-byte LDS reads),
+//       B = the wave's Q rows in registers; 2 K-steps of 64 d;
+//   O^T += V^T P^T, one K-step of all 64 keys: B = P^T packed to e4m3
+//       straight from the S^T accumulators (lane = query, 32 keys per lane),
+//       A = V^T gathered by the 8-bit transposing LDS read in the same key
+//       order as B.
+// Operand layout of the FP8 instruction: lane l holds row (or column) l % 32
+// and 32 consecutive K-values of group l / 32; any assignment of K-values to
+// bytes works as long as A and B use the same one, which is how P^T (in the
+// accumulator's key order) meets V^T.
+#include "fa_common.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+
+// e4m3 x e4m3 (format code 0 for A and B), unit E8M0 block scales (127 = 2^0)
+FA_DEV f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+FA_DEV i32x4v lds_read_i128(const char* base, int off) {
+  return *reinterpret_cast<const i32x4v*>(base + off);
+}
+
+// 8-bit transposing read: in each group of 16 lanes, lane 8u + c receives
+// byte c of the 8-byte segments addressed by lanes 2e + u, e = 0..7, as its
+// bytes e (measured on the device).
+FA_DEV i32x2v lds_read_tr8(const char* base, int off) {
+  typedef FA_LDS i32x2v lds_i32x2;
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base + off));
+}
+
+FA_DEV i32x8 cat8(i32x4v a, i32x4v b) { return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7); }
+
+FA_DEV i32x8 cat_tr(i32x2v a, i32x2v b, i32x2v c, i32x2v d) {
+  const i32x4v lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const i32x4v hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return cat8(lo, hi);
+}
+
+// four e4m3 codes of four floats in one dword (round to nearest even)
+FA_DEV int pack_fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(
+    const unsigned char* __restrict__ Q, const unsigned char* __restrict__ K,
+    const unsigned char* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N,
+    int nqb, float scale_qk, float c, float dv, RowLayout lay) {
+  static_assert(D == 128, "FP8 tiles are laid out for 128-byte rows");
+  constexpr int NW = 8, BR = 32 * NW, BC = 64;
+  constexpr int ROWB = D;            // bytes per e4m3 row
+  constexpr int KS = D / 64;         // K-steps of the S product
+  constexpr int DT = D / 32;         // 32-row tiles of O^T
+  constexpr int TILEB = BC * ROWB;   // bytes of one K or V tile
+
+  __shared__ __attribute__((aligned(1024))) char sK0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char sK1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char sV0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char sV1[TILEB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int RS = lay.row_stride(D);      // elements (= bytes) between a head's rows
+  const TileFetch<ROWB, BC, NW> fetch(wave, lane, RS);
+  const int bid = blockIdx.x;
+  const int head = bid % BH;
+  const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);   // longest blocks first
+  const size_t hoff = lay.head_off(head, N, D);
+  const unsigned char* Qh = Q + hoff;
+  // TileFetch moves bytes; it takes the tile base as a bf16 pointer
+  const bf16* Kh = reinterpret_cast<const bf16*>(K + hoff);
+  const bf16* Vh = reinterpret_cast<const bf16*>(V + hoff);
+
+  const int q0 = qb * BR + wave * 32;
+  const int qrow = q0 + l32;
+
+  // Q rows as B operands: lane (query l32, group h) holds d = 64s + 32h .. +31
+  i32x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (qrow < N) {
+      const i32x4v* p = reinterpret_cast<const i32x4v*>(Qh + (size_t)qrow * RS + 64 * s + 32 * h);
+      qf[s] = cat8(p[0], p[1]);
+    } else {
+      qf[s] = i32x8{};
+    }
+  }
+
+  // LDS offsets.  K operand (key row l32 of a 32-key half, bytes 64s + 32h ..
+  // +31 as two 16-byte chunks): kb[s][hf] + 4096 * half (swz depends on the
+  // row mod 16, so 32 rows down is a constant).
+  int kb[KS][2];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) kb[s][hf] = tile_off<ROWB>(l32, 4 * s + 2 * h + hf);
+  // V^T operand for the 32 d-rows 32t .. 32t+31: four transposing reads w;
+  // this lane supplies the segment of key row 16w + r0 (r0 as below), bytes
+  // 32t + 16(G%2) + 8u .. +7, so that the receiving lane (d, group g) gets,
+  // as its bytes 8w + e, V[key 16w + 8(e/4) + 4g + e%4][d]: the key order of
+  // the P^T operand.  Offset vb[t] + 2048 w.
+  int vb[DT];
+  {
+    const int G = (lane >> 4) & 3, e = (lane & 15) >> 1, u = lane & 1;
+    const int r0 = 8 * (e >> 2) + 4 * (G >> 1) + (e & 3);
+#pragma unroll
+    for (int t = 0; t < DT; ++t) vb[t] = r0 * ROWB + (((2 * t + (G & 1)) ^ swz<ROWB>(r0)) << 4) + 8 * u;
+  }
+
+  const int kv_end = CAUSAL ? min(N, qb * BR + BR) : N;
+  const int ntiles = (kv_end + BC - 1) / BC;
+  int wave_tiles = 0;
+  if (q0 < N) {
+    const int wkv_end = CAUSAL ? min(N, q0 + 32) : N;
+    wave_tiles = (wkv_end + BC - 1) / BC;
+  }
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  float m_run = -INFINITY;   // reference maximum of the raw code dot products
+  float l_run = 0.f;         // sum of 2^7 p, partial over this lane's half of the keys
+
+  auto body = [&](auto bc, int j) {
+    constexpr int b = decltype(bc)::value;
+    const char* Kt = b ? sK1 : sK0;
+    const char* Vt = b ? sV1 : sV0;
+    if (j + 1 < ntiles) {
+      fetch(Kh, (j + 1) * BC, N, b ? sK0 : sK1);
+      fetch(Vh, (j + 1) * BC, N, b ? sV0 : sV1);
+    }
+    if (j < wave_tiles) {
+      // Slots: KS slots of two S products (the two 32-key halves), the
+      // softmax, DT slots of one P V product; each slot first issues the LDS
+      // reads of the slot DIST ahead.
+      constexpr int DIST = 2;
+      constexpr int NSL = KS + DT;
+      i32x8 ka[KS][2], va[DT];
+      auto read_slot = [&](int i) {
+        if (i < KS) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            ka[i][mt] = cat8(lds_read_i128(Kt, kb[i][0] + 4096 * mt), lds_read_i128(Kt, kb[i][1] + 4096 * mt));
+        } else {
+          const int t = i - KS;
+          va[t] = cat_tr(lds_read_tr8(Vt, vb[t]), lds_read_tr8(Vt, vb[t] + 2048), lds_read_tr8(Vt, vb[t] + 4096),
+                         lds_read_tr8(Vt, vb[t] + 6144));
+        }
+      };
+      f32x16 s[2] = {f32x16{}, f32x16{}};
+      i32x8 pb;
+      const int kvb = j * BC;
+#pragma unroll
+      for (int i = 0; i < DIST; ++i) read_slot(i);
+#pragma clang loop unroll(full)
+      for (int i = 0; i < NSL; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + DIST < NSL) read_slot(i + DIST);
+        if (i < KS) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) s[mt] = mfma_fp8(ka[i][mt], qf[i], s[mt]);
+        } else {
+          oacc[i - KS] = mfma_fp8(va[i - KS], pb, oacc[i - KS]);
+        }
+        if (i != KS - 1) continue;
+        __builtin_amdgcn_sched_barrier(0);
+        // s[mt][4*r4+jj] = q8_qrow . k8_kv with kv = kvb + 32*mt + 8*r4 + 4*h + jj
+        const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0);
+        if (need_mask) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
+              const bool dead = (kv >= N) | (CAUSAL & (kv > qrow));
+              s[mt][r] = dead ? -INFINITY : s[mt][r];
+            }
+        }
+        float mx = m_run;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
+        mx = half_max(mx);
+        // as in the bf16 forward, the reference maximum moves (with O and l
+        // rescaled) only when a row gains more than a factor 2^1 over it, so
+        // that 2^7 p stays at most 2^8 < 448
+        if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 1.f) != 0) {
+          const float alpha = exp2_fast((m_run - mx) * c);
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+          m_run = mx;
+        }
+        const float nb = 7.f - m_run * c;
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = exp2_fast(fmaf(s[mt][r], c, nb));
+            s[mt][r] = p;
+            rs += p;
+          }
+        l_run += rs;
+        // P^T as the B operand: byte 16*mt + r of this lane (query qrow,
+        // group h) is the key kvb + 32*mt + 8*(r/4) + 4*h + r%4
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            pb[4 * mt + q] = pack_fp8x4(s[mt][4 * q], s[mt][4 * q + 1], s[mt][4 * q + 2], s[mt][4 * q + 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  };
+
+  fetch(Kh, 0, N, sK0);
+  fetch(Vh, 0, N, sV0);
+  __syncthreads();
+  for (int j = 0;;) {
+    body(IC<0>{}, j);
+    if (++j >= ntiles) break;
+    body(IC<1>{}, j);
+    if (++j >= ntiles) break;
+  }
+
+  if (q0 >= N) return;
+  const float l_tot = half_sum(l_run);
+  if (qrow < N) {
+    const float f = dv / l_tot;
+    bf16* Orow = O + hoff + (size_t)qrow * RS;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bf16x4 v;
+        v[0] = (bf16)(oacc[t][4 * i + 0] * f);
+        v[1] = (bf16)(oacc[t][4 * i + 1] * f);
+        v[2] = (bf16)(oacc[t][4 * i + 2] * f);
+        v[3] = (bf16)(oacc[t][4 * i + 3] * f);
+        *reinterpret_cast<bf16x4*>(Orow + 32 * t + 8 * i + 4 * h) = v;
+      }
+    if (h == 0) LSE[(size_t)head * N + qrow] = m_run * scale_qk + (log2_fast(l_tot) - 7.f) * kLn2;
+  }
+}
+
+template <bool CAUSAL>
+static hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                                   int N, float scale_qk, float dv, RowLayout lay, hipStream_t stream) {
+  constexpr int BR = 256;
+  const int nqb = (N + BR - 1) / BR;
+  const dim3 grid((unsigned)(nqb * BH)), block(512);
+  hipLaunchKernelGGL((fwd_fp8_kernel<128, CAUSAL>), grid, block, 0, stream, (const unsigned char*)q,
+                     (const unsigned char*)k, (const unsigned char*)v, (bf16*)o, lse, BH, N, nqb, scale_qk,
+                     scale_qk * kLog2e, dv, lay);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
+                          bool causal, float scale, float dq, float dk, float dv, RowLayout lay,
+                          hipStream_t stream) {
+  const float scale_qk = scale * dq * dk;
+  return causal ? launch_fwd_fp8_t<true>(q, k, v, o, lse, BH, N, scale_qk, dv, lay, stream)
+                : launch_fwd_fp8_t<false>(q, k, v, o, lse, BH, N, scale_qk, dv, lay, stream);
+}
+
+}  // namespace fa

@@ -26,6 +26,12 @@ struct RowLayout {
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                            int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream);
 
+// FP8 (e4m3fn) forward, d = 128: O (bf16) and LSE for Q = dq * Q8, K = dk * K8,
+// V = dv * V8.
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
+                          bool causal, float scale, float dq, float dk, float dv, RowLayout lay,
+                          hipStream_t stream);
+
 // Split-key-range bf16 forward (Nq queries against Nk >= Nq keys): the keys
 // of each head are cut into nsplit ranges of `span` keys (a multiple of
 // kSplitBC); writes each range's O (fp32, normalised by its own sum) to opart

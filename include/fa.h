@@ -127,6 +127,30 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const
               void* workspace, size_t workspace_bytes, void* stream, int dtype, int layout);
 
 /*
+ * Forward with FP8 inputs: q, k, v hold OCP e4m3fn codes (1 byte per
+ * element: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities; largest finite 448) in the layout named by `layout`, standing
+ * for Q = descale_q * q and so on (per-tensor descales, finite and > 0).
+ * Writes o in bf16 (same layout) and lse as fa_fwd does, for
+ * O = softmax(scale * Q K^T [+ causal mask]) V.
+ *
+ * The method is fa_fwd's (page "flash-attention-v2-sram-tiling", section 5)
+ * on the FP8 matrix instructions, the FP8 forward the pages attribute to
+ * FlashAttention-3 (page "data.6616ai.com flash-attention").  S and the
+ * softmax statistics are computed from the exact code products in fp32; the
+ * probabilities are rounded to e4m3 for the P V product (relative error at
+ * most 2^-4 each), so O carries an error of up to about 2^-4 * max|V|, while
+ * LSE is as accurate as fa_fwd's.
+ *
+ * Supported: d = 128 only (FA_ERR_UNSUPPORTED otherwise); B, H, N, causal,
+ * scale, layout, ownership, streams and errors as for fa_fwd.  Pointers must
+ * be 16-byte aligned (lse 4-byte).
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale,
+               float descale_q, float descale_k, float descale_v, void* stream, int layout);
+
+/*
  * Forward for Nq query rows against Nk key/value rows per head (the decode
  * shape: a few new tokens against a long key/value cache), with the keys of
  * each head cut into ranges that separate workgroups process at once.

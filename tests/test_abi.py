@@ -182,3 +182,22 @@ def test_splitkv_noncausal_allows_more_queries_than_keys_and_sizes_workspace():
         assert n == r(used * rows * 128 * 4) + r(used * rows * 4), ns
     assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 1000, 96, 0) == 0
     assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 1000, 128, 2000) == 0
+
+
+def fwd8(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=256, d=128, causal=1, scale=0.125, descale_q=0.5,
+             descale_k=0.5, descale_v=0.5, stream=None, layout=fa.FA_LAYOUT_BHND)
+    a.update(kw)
+    return fa.fa_fwd_fp8(**a)
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(v=None), -1), (dict(lse=None), -1), (dict(N=0), -1), (dict(causal=3), -1),
+    (dict(scale=0.0), -1), (dict(descale_q=0.0), -1), (dict(descale_k=-1.0), -1),
+    (dict(descale_v=float("inf")), -1), (dict(descale_q=float("nan")), -1), (dict(layout=2), -1),
+    (dict(d=64), -2), (dict(d=96), -2), (dict(k=P + 4), -1), (dict(o=P + 2), -1),
+    (dict(scale=1e30, descale_q=1e30, descale_k=1e30), -1),
+])
+def test_fp8_rejects(kw, status):
+    assert fwd8(**kw) == status

@@ -1,0 +1,101 @@
+"""GPU parity of the FP8 forward (fa_fwd_fp8, through the C ABI) against the
+fp64 oracle on the values the e4m3fn codes stand for (code times descale,
+exact in fp64).
+
+Bar, derived from the arithmetic: S and the softmax statistics come from
+exact code products accumulated in fp32, so LSE meets the bf16 bar (max-abs
+<= 1e-3).  O differs from the exact result only through rounding each
+probability (taken as 2^7 p, with every row holding one value 2^7) to e4m3
+for the P V product: relative error <= 2^-4 in the normal range, absolute
+<= 2^-10 below it, hence |O - O_ref| <= (2^-4 + N 2^-17) max|V| per head, plus
+the bf16 rounding of O (2^-9 max|O|).  Inputs with sharp scores (q, k spread
+3) are included so that a misplaced key cannot hide inside that bound: there
+O follows a few rows of V closely.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import exact_tiled_attention_online_amd as fa
+from exact_tiled_attention_online_amd import inputs as gen
+from gpu_util import LSE_ATOL, log, to_np
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fp8(x, causal, scale, layout=0):
+    import torch
+    def dev(a):
+        a = np.ascontiguousarray(a.transpose(0, 2, 1, 3) if layout == fa.FA_LAYOUT_BNHD else a)
+        return torch.from_numpy(a).cuda()
+    q8, k8, v8 = (dev(x[n]) for n in ("q8", "k8", "v8"))
+    o, lse = fa.forward_fp8(q8, k8, v8, x["descale_q"], x["descale_k"], x["descale_v"], causal, scale,
+                            layout=layout)
+    torch.cuda.synchronize()
+    return {"o": to_np(o, layout), "lse": to_np(lse)}
+
+
+def check(x, got, causal, scale, where):
+    o_ref, lse_ref = ref.forward(x["q"], x["k"], x["v"], scale, causal)
+    n = x["q"].shape[2]
+    worst = 0.0
+    for b in range(o_ref.shape[0]):
+        for h in range(o_ref.shape[1]):
+            vmax = float(np.abs(x["v"][b, h]).max())
+            tol_o = (2.0 ** -4 + n * 2.0 ** -17) * vmax + 2.0 ** -9 * float(np.abs(o_ref[b, h]).max())
+            err_o = float(np.abs(got["o"][b, h] - o_ref[b, h]).max())
+            err_l = float(np.abs(got["lse"][b, h] - lse_ref[b, h]).max())
+            assert np.isfinite(got["o"][b, h]).all() and np.isfinite(got["lse"][b, h]).all(), where
+            assert err_l <= LSE_ATOL, f"{where} head ({b},{h}): LSE err {err_l:.3e}"
+            assert err_o <= tol_o, f"{where} head ({b},{h}): O err {err_o:.3e} > {tol_o:.3e}"
+            worst = max(worst, err_o / tol_o)
+    return worst
+
+
+CASES = [(n, causal, sig) for n in (1, 17, 64, 129, 300, 1000) for causal in (False, True) for sig in (1.0, 3.0)]
+
+
+@pytest.mark.parametrize("n,causal,sig", CASES)
+def test_fp8_forward_matches_oracle(n, causal, sig):
+    log(f"[fp8] N={n} causal={causal} sigma_qk={sig}")
+    x = gen.make_fp8_inputs((2, 3, n, 128), seed=300 + n, sigma_qk=sig)
+    scale = 1.0 / math.sqrt(128)
+    got = run_fp8(x, causal, scale)
+    r = check(x, got, causal, scale, f"fp8 N{n} c{int(causal)} s{sig}")
+    log(f"  worst O error / bound {r:.3f}")
+
+
+def test_fp8_forward_other_descales_and_bnhd():
+    log("[fp8] descales, BNHD")
+    x = gen.make_fp8_inputs((1, 4, 500, 128), seed=71, sigma_qk=2.0, descale=2.0 ** -5)
+    x["descale_v"] = 0.37          # any positive descale: the values are code * descale
+    x["v"] = gen.e4m3_to_f32(x["v8"]) * np.float32(0.37)
+    for layout in (fa.FA_LAYOUT_BHND, fa.FA_LAYOUT_BNHD):
+        for causal in (False, True):
+            got = run_fp8(x, causal, 0.11, layout)
+            check(x, got, causal, 0.11, f"fp8 layout{layout} c{int(causal)}")
+
+
+def test_fp8_forward_full_size_sampled_heads():
+    """The causal 1 x 32 x 8192 x 128 shape in the benchmark's launch
+    configuration, checked on whole sampled heads."""
+    import torch
+    log("[fp8] full size")
+    shape = (1, 32, 8192, 128)
+    x = gen.make_fp8_inputs(shape, seed=4)
+    q8, k8, v8 = (torch.from_numpy(x[n]).cuda() for n in ("q8", "k8", "v8"))
+    scale = 1.0 / math.sqrt(128)
+    o, lse = fa.forward_fp8(q8, k8, v8, x["descale_q"], x["descale_k"], x["descale_v"], True, scale)
+    torch.cuda.synchronize()
+    got_o, got_l = to_np(o), to_np(lse)
+    assert np.isfinite(got_o).all() and np.isfinite(got_l).all()
+    for h in (0, 31):
+        want = ref.forward_rect(x["q"], x["k"], x["v"], scale, True, heads=[(0, h)])[(0, h)]
+        vmax = float(np.abs(x["v"][0, h]).max())
+        tol = (2.0 ** -4 + 8192 * 2.0 ** -17) * vmax + 2.0 ** -9 * float(np.abs(want["o"]).max())
+        assert float(np.abs(got_o[0, h] - want["o"]).max()) <= tol, h
+        assert float(np.abs(got_l[0, h] - want["lse"]).max()) <= LSE_ATOL, h
+    del q8, k8, v8, o, lse
+    torch.cuda.empty_cache()
