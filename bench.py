@@ -14,7 +14,9 @@ fwd = 4*B*H*N^2*d and bwd = 10*B*H*N^2*d, both halved for a causal mask.
 Prints one JSON line.  Default workload: B=1, H=32, N=8192, d=128, causal,
 bf16 (the headline shape).  ``detail.decode`` adds the split-key-range forward
 (fa_fwd_splitkv) on a decode step of 8 x 32 heads, one query against 16384
-cached keys, with its HBM roofline (skip with --no-decode).
+cached keys, with its HBM roofline (skip with --no-decode), and
+``detail.fp8_forward`` the FP8 forward (fa_fwd_fp8) on the headline shape
+against the FP8 peak (skip with --no-fp8).
 """
 from __future__ import annotations
 
@@ -29,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (twice the bf16 rate)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "attention fwd+bwd TFLOP/s and % bf16 MFMA peak, 1×MI355X, N=8192 d=128"
 COUNTERS = os.path.join(ROOT, "profiles", "counters_c4.json")
@@ -255,6 +258,65 @@ def decode_measurement(fa, gen, torch, dev, stream, with_oracle, reps=50, oracle
     return res
 
 
+def fp8_measurement(fa, gen, torch, dev, stream, w, with_oracle, reps=30, oracle_budget_s=4.0):
+    """The FP8 forward (fa_fwd_fp8) on the headline shape with e4m3fn inputs:
+    time per call from HIP events on the launch stream, credited forward
+    FLOPs (4*B*H*N^2*d, halved for causal) against the dense FP8 peak, and,
+    unless disabled, the oracle on whole heads (the values the codes stand
+    for) within the bound the tests use."""
+    import numpy as np
+    B, H, N, d = w.shape
+    x = gen.make_fp8_inputs((B, H, N, d), seed=w.seed, sigma_qk=w.sigma_qk, sigma_v=w.sigma_vdo)
+    q8, k8, v8 = (torch.from_numpy(x[n]).to(dev) for n in ("q8", "k8", "v8"))
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    sp = stream.cuda_stream
+
+    def call():
+        st = fa.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                           w.causal, w.scale, x["descale_q"], x["descale_k"], x["descale_v"], sp,
+                           fa.FA_LAYOUT_BHND)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd_fp8")
+
+    for _ in range(10):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    fl = w.flops()[0]
+    tf = fl / (ms * 1e-3) / 1e12
+    res = {"workload": w.name.replace("bf16", "fp8"), "dtype": "fp8 e4m3fn in, bf16 out",
+           "descales": [x["descale_q"], x["descale_k"], x["descale_v"]],
+           "us_per_call": round(ms * 1e3, 2), "calls": reps, "tflops": round(tf, 3),
+           "roofline": {"kernel": "fwd_fp8_kernel", "bound": "mfma", "achieved": round(tf, 3),
+                        "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                        "traffic": None}}
+    if with_oracle:
+        from oracle import ref
+        got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()
+        worst, done, t0 = {"o": 0.0, "lse": 0.0}, 0, time.perf_counter()
+        for h in range(H):
+            r = ref.forward_rect(x["q"], x["k"], x["v"], w.scale, w.causal, heads=[(0, h)])[(0, h)]
+            vmax = float(np.abs(x["v"][0, h]).max())
+            tol = (2.0 ** -4 + N * 2.0 ** -17) * vmax + 2.0 ** -9 * float(np.abs(r["o"]).max())
+            worst["o"] = max(worst["o"], float(np.abs(got_o[0, h] - r["o"]).max()) / tol)
+            worst["lse"] = max(worst["lse"], float(np.abs(got_l[0, h] - r["lse"]).max()) / 1e-3)
+            done += 1
+            if time.perf_counter() - t0 > oracle_budget_s:
+                break
+        res["oracle_check"] = {"heads": done, "max_err_over_tolerance": {n: round(v, 4) for n, v in worst.items()},
+                               "within_tolerance": all(v <= 1.0 for v in worst.values())}
+    del q8, k8, v8, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,6 +324,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4", help="c1..c5 (default c4, the headline shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 forward on the headline shape (reported under detail)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the split-key-range forward on the decode workload (reported under detail)")
     ap.add_argument("--flush-mib", type=int, default=0,
@@ -445,6 +509,8 @@ def main():
             "peak_from_cus_at_2p4ghz": round(props.multi_processor_count * 4096 * 2.4e9 / 1e12, 1),
         },
     }
+    if not args.no_fp8 and B == 1 and d == 128:
+        out["detail"]["fp8_forward"] = fp8_measurement(fa, gen, torch, dev, stream, w, not args.no_cpu_baseline)
     if not args.no_decode:
         out["detail"]["decode"] = decode_measurement(fa, gen, torch, dev, stream, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
