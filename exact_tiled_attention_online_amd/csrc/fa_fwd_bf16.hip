@@ -9,7 +9,8 @@
 //                              B = the wave's Q rows held in registers;
 //   online softmax             per lane one query row: running reference max
 //                              m and running sum l, rescale factor
-//                              2^(c(m_old-m_new)) when m moves (see the tile)
+//                              2^(c(m_old-m_new)) when m moves (see the tile;
+//                              the reference lags and moves only when needed)
 //                              (page "flash-attention-v2-sram-tiling"
 //                              (aiqz.cc), section 5; the l update uses the full
 //                              block sum as in the derivation on page
@@ -197,39 +198,64 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
               s[mt][r] = dead ? -INFINITY : s[mt][r];
             }
         }
-        float mx = m_run;
+        // The probabilities are taken against a lagging reference max m_run:
+        // it is moved (and O, l rescaled) only when a probability against the
+        // old one could exceed 2^8, which changes nothing but the rounding (O
+        // and l carry the same factor, and LSE = scale*m_run + ln l for any
+        // reference).  Key 0 is never masked, so the first tile always sets
+        // a finite reference; in the split mode a row may see no key of a tile
+        // or of its whole range, and its reference stays -inf (no rescale,
+        // p = 0) until it does.
+        f32x16 sc_[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mt][r]);
-        mx = half_max(mx);
-        // The reference max m_run is moved (and O, l rescaled) only when some
-        // row of the wave gains more than 2^8 over it; otherwise the tile's
-        // probabilities are taken against the old reference, which keeps them
-        // below 2^8 and changes nothing but the rounding (O and l carry the
-        // same factor, and LSE = scale*m_run + ln l for any reference).  Key 0
-        // is never masked, so the first tile always sets a finite reference;
-        // in the split mode a row may see no key of a tile or of its whole
-        // range, and its reference stays -inf (no rescale, p = 0) until it does.
-        if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 8.f) != 0) {
-          const float alpha = (SPLIT && m_run == -INFINITY) ? 0.f : exp2_fast((m_run - mx) * c);
-          l_run *= alpha;
-#pragma unroll
-          for (int t = 0; t < DT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
-          m_run = mx;
-        }
-        const float nb = (SPLIT && m_run == -INFINITY) ? 0.f : -m_run * c;
+        for (int mt = 0; mt < MT; ++mt) sc_[mt] = s[mt];
         float rs = 0.f;
+        auto exps = [&]() {
+          const float nb = (SPLIT && m_run == -INFINITY) ? 0.f : -m_run * c;
+          rs = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = exp2_fast(fmaf(s[mt][r], c, nb));
-            s[mt][r] = p;
-            rs += p;
+            for (int r = 0; r < 16; ++r) {
+              const float p = exp2_fast(fmaf(sc_[mt][r], c, nb));
+              s[mt][r] = p;
+              rs += p;
+            }
+        };
+        auto rescale_to_max = [&](float thresh) {
+          float mx = m_run;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc_[mt][r]);
+          mx = half_max(mx);
+          if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > thresh) != 0) {
+            const float alpha = (SPLIT && m_run == -INFINITY) ? 0.f : exp2_fast((m_run - mx) * c);
+            l_run *= alpha;
+#pragma unroll
+            for (int t = 0; t < DT; ++t)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
+            m_run = mx;
           }
+        };
+        if constexpr (SPLIT) {
+          rescale_to_max(8.f);
+          exps();
+        } else {
+          // The tile maximum is needed only when a probability could exceed
+          // 2^8: first try the old reference; a lane sum above 2^8 (or not
+          // finite: the first tile, against -inf) sends the wave through the
+          // exact maximum and a second pass, after which every p <= 1.  A sum
+          // at most 2^8 bounds every term, so the bound holds either way, and
+          // the common tile skips the maximum (16 three-way max instructions
+          // and a cross-lane step per lane).
+          exps();
+          if (__builtin_amdgcn_ballot_w64(!(rs <= 256.f)) != 0) {
+            rescale_to_max(0.f);
+            exps();
+          }
+        }
         l_run += rs;
         // P^T as B operand, K-step st covers keys 16*st .. 16*st+15 of the
         // tile: registers 0..3 <- keys 16st+4h+jj, 4..7 <- keys 16st+8+4h+jj
