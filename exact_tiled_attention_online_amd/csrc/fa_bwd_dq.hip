@@ -11,7 +11,8 @@
 //   P^   = 2^(c*(S - LSE/scale))  recompute from the ledger (section 数值稳定);
 //                              the lane holds one query row, so LSE and D
 //                              are per-lane scalars
-//   dS   = P^ o (dP - D)       (section Softmax梯度)
+//   dS   = P^ o (dP - D)       (section Softmax梯度); the dP accumulator
+//                              starts from -D
 //   dQ^T += K_j^T dS^T         MFMA, A = K^T through transposing LDS reads,
 //                              B = dS^T straight from the accumulators.
 // It repeats the S and dP products of the key/value-outer kernel instead of
@@ -142,7 +143,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
         if (k < KS) {
           if (k == 0) {
             s = f32x16{};
-            dp = f32x16{};
+            // dP starts from -D of this lane's query row, so that the products
+            // leave dP - D (every register of the lane belongs to that row)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[r] = ndrow;
           }
           s = mfma32(ka[k], qf[k], s);
           dp = mfma32(va[k], gf[k], dp);
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float p = exp2_fast(fmaf(s[r], c, nl2));
-              dp[r] = p * (dp[r] + ndrow);
+              dp[r] = p * dp[r];
             }
             // dS^T as B operand; K-step st = 2*mt + half covers keys 16*st ..
             // 16*st+15 of the tile: registers 0..3 <- keys 16st+4h+jj, 4..7 <-
