@@ -73,6 +73,14 @@ def _read_counter_csv(path):
     return per
 
 
+def _headline_instance(name, short):
+    """Whether a traced kernel name is `short`'s instantiation on the timed
+    path: the forward's last template argument selects its split mode, which
+    is a different launch."""
+    head = name.split("(")[0].strip()
+    return short in head and not (short == "fwd_bf16_kernel" and head.endswith("true>"))
+
+
 def summarize_counters(fetch_csv, write_csv, copy_mib, out_json):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE, with --copy-probe-mib) into HBM bytes per launch per kernel.
@@ -87,8 +95,12 @@ def summarize_counters(fetch_csv, write_csv, copy_mib, out_json):
         v = d.get(key, [])
         return sum(v) / len(v) if v else None
 
-    copy = [k for k in fetch if "copy" in k.lower() and "elementwise" in k.lower()]
-    # the probe copy is the largest copy kernel in the run
+    # the probe is torch's bf16 -> fp32 conversion kernel (the largest such
+    # launch in the run); other conversions have other read/write ratios
+    copy = [k for k in fetch if "bfloat16tofloat32" in k.replace("_", "").lower() or
+            "bfloat16tofloat32" in k.lower()]
+    if not copy:
+        raise SystemExit("no bf16 -> fp32 copy kernel in the counter run (was --copy-probe-mib given?)")
     ck = max(copy, key=lambda k: max(fetch[k]["FETCH_SIZE"]))
     f_fetch = known_read_kib / max(fetch[ck]["FETCH_SIZE"])
     f_write = known_write_kib / max(write[ck]["WRITE_SIZE"])
@@ -96,7 +108,7 @@ def summarize_counters(fetch_csv, write_csv, copy_mib, out_json):
                           "write_factor": round(f_write, 4)}}
     rows = []
     for short, srcs in KERNEL_SOURCES.items():
-        key = next((k for k in fetch if short in k), None)
+        key = next((k for k in fetch if _headline_instance(k, short)), None)
         if key is None or key not in write:
             continue
         fk, wkib = mean(fetch[key], "FETCH_SIZE"), mean(write[key], "WRITE_SIZE")
