@@ -250,3 +250,39 @@ def test_bnhd_full_size_matches_bhnd():
     for name in ("o", "lse", "dq", "dk", "dv"):
         assert np.array_equal(a[name], b[name]), f"bnhd {name} differs from the BHND run"
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_rising_along_the_keys(dtype, causal):
+    """Scores that grow with the key index (k_j has a component along q that
+    rises with j), so that every key tile raises each row's maximum and the
+    forward's lagging reference has to move on nearly every tile; plus one
+    very sharp row (spread 8).
+
+    The backward does not use that reference (it recomputes from the final
+    LSE), and with rows this peaked dP - D cancels almost entirely, so
+    max|dQ| is small and set by that cancellation.  In bf16, D comes from the
+    stored bf16 O, whose rounding then dominates dQ's error (about 1.1 times
+    the 2e-2 max|dQ| bar here).  So the bf16 case checks the forward's O and
+    LSE, the outputs the rising scores exercise; fp32 checks all five."""
+    log(f"[rising] dtype={dtype} causal={causal}")
+    n, d = 700, 64
+    w = gen.workload("c2")
+    x = gen.make_inputs(w, shape=(1, 2, n, d), seed=808, dtype=dtype)
+    ramp = np.linspace(0.0, 12.0, n, dtype=np.float32)[None, None, :, None]
+    k = x["k"] * np.float32(0.1) + ramp * np.float32(1.0 / math.sqrt(d))
+    q = np.abs(x["q"]) + np.float32(1.0)
+    q[:, :, 5] *= np.float32(8.0)
+    if dtype == "bf16":
+        k, q = gen.round_bf16(k), gen.round_bf16(q)
+    x = dict(x, k=k, q=q)
+    scale = 1.0 / math.sqrt(d)
+    if dtype == "fp32":
+        _full_compare(x, dtype, causal, scale, f"rising {dtype} c{int(causal)}")
+        return
+    res = run_gpu(x, dtype, causal, scale, bwd=False)
+    want = oracle_heads(x, causal, scale, heads=None)
+    for (b, h), wv in want.items():
+        compare({n: res[n][b, h] for n in ("o", "lse")}, wv, dtype, names=("o", "lse"),
+                where=f"rising {dtype} c{int(causal)} head ({b},{h})")
