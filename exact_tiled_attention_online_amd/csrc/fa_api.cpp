@@ -27,7 +27,7 @@ int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype, 
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID;
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
   const long long elems = (long long)B * H * N * d;
   if (elems >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
@@ -63,10 +63,11 @@ Workspace carve(void* base, int B, int H, int N, int d, int dtype) {
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 // dQ path of the bf16 backward: the query-block-outer kernel (default), or
-// fp32 atomics from the key/value-outer kernel when FA_DQ_MODE=atomic.
-bool dq_atomic_mode() {
+// fp32 atomics from the key/value-outer kernel when FA_DQ_MODE=atomic (d = 64
+// and 128 only; d = 96 always takes the default).
+bool dq_atomic_mode(int d) {
   const char* m = std::getenv("FA_DQ_MODE");
-  return m && std::strcmp(m, "atomic") == 0;
+  return d != 96 && m && std::strcmp(m, "atomic") == 0;
 }
 
 bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d, int dtype) {
@@ -141,7 +142,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
-  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128) || (dtype != FA_BF16 && dtype != FA_FP32)) return 0;
+  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 96 && d != 128) || (dtype != FA_BF16 && dtype != FA_FP32))
+    return 0;
   return carve(nullptr, B, H, N, d, dtype).bytes;
 }
 
@@ -154,7 +156,7 @@ int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, in
   if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(lse, 4)) return FA_ERR_INVALID;
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
   const Workspace w = carve(workspace, B, H, N, d, dtype);
-  float* dq_acc = (dtype == FA_BF16 && dq_atomic_mode()) ? w.dq_acc : nullptr;
+  float* dq_acc = (dtype == FA_BF16 && dq_atomic_mode(d)) ? w.dq_acc : nullptr;
   return hip_status(fa::launch_bwd_pre(o, dO, lse, w.ndrow, w.nlse, dq_acc, B * H, N, d, scale,
                                        dtype == FA_FP32, row_layout(H, layout), static_cast<hipStream_t>(stream)));
 }
@@ -177,7 +179,7 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, con
                                             w.ndrow, static_cast<float*>(dk), static_cast<float*>(dv), B * H, N,
                                             d, causal != 0, scale, row_layout(H, layout), s));
   return hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.nlse, w.ndrow, w.dq_acc, dk, dv, B * H, N, d,
-                                        causal != 0, scale, dq_atomic_mode(), row_layout(H, layout), s));
+                                        causal != 0, scale, dq_atomic_mode(d), row_layout(H, layout), s));
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq, int B,
@@ -197,7 +199,7 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const
                                            static_cast<const float*>(v), static_cast<const float*>(dO), lse,
                                            w.ndrow, static_cast<float*>(dq), B * H, N, d, causal != 0, scale,
                                            row_layout(H, layout), s));
-  if (dq_atomic_mode())
+  if (dq_atomic_mode(d))
     return hip_status(fa::launch_dq_convert(w.dq_acc, dq, B * H, N, d, scale, row_layout(H, layout), s));
   return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.nlse, w.ndrow, dq, B * H, N, d, causal != 0, scale,
                                       row_layout(H, layout), s));

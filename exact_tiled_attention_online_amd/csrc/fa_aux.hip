@@ -8,7 +8,8 @@
 // S - LSE/scale and dP - D.  Also the clear of the fp32 dQ accumulator (a fill
 // kernel, so the whole backward can be captured in a graph).
 // Each row of d elements is read by d/8 lanes with 16-byte (bf16) or 32-byte
-// (fp32) loads, reduced across those lanes with xor-shuffles.
+// (fp32) loads (in a group of 8 or 16 lanes), reduced across the group with
+// xor-shuffles.
 //
 // dq_convert: dQ = bf16(scale * acc), 8 elements per thread, 16-byte stores.
 //
@@ -24,19 +25,26 @@
 
 namespace fa {
 
+// lanes given to one row of D elements: D/8 rounded up to a power of two (the
+// cross-lane sums use xor-shuffles within that group)
+template <int D>
+constexpr int lanes_per_row() {
+  return D / 8 <= 8 ? 8 : 16;
+}
+
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO,
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ ndrow, float* __restrict__ nlse,
                                                       float* __restrict__ dq_acc, size_t rows, float inv_scale,
                                                       int N, RowLayout lay) {
-  constexpr int LPR = D / 8;            // lanes per row, 8 elements each
-  constexpr int RPB = 256 / LPR;        // rows per block
+  constexpr int LPR = lanes_per_row<D>();   // lanes per row (D/8 of them hold 8 elements each)
+  constexpr int RPB = 256 / LPR;            // rows per block
   const int tid = threadIdx.x;
   const size_t row = (size_t)blockIdx.x * RPB + tid / LPR;
   const int part = tid % LPR;
   float acc = 0.f;
-  if (row < rows) {
+  if (row < rows && part < D / 8) {
     // row = hb*N + n of the [B*H][N] statistics; the tensor row is found
     // through the layout
     const int hb = (int)(row / N), n = (int)(row - (size_t)hb * N);
@@ -75,22 +83,22 @@ hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float
                           hipStream_t stream) {
   const float inv_scale = 1.f / scale;
   const size_t rows = (size_t)BH * N;
-  const int rpb = 256 / (d / 8);
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
+  auto go = [&](auto dc, auto tc) {
+    constexpr int D = decltype(dc)::value;
+    using T = std::conditional_t<decltype(tc)::value == 1, float, bf16>;
+    constexpr int rpb = 256 / lanes_per_row<D>();
+    const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, T>), grid, block, 0, stream, (const T*)o, (const T*)dO, lse, ndrow,
+                       nlse, dq_acc, rows, inv_scale, N, lay);
+  };
   if (fp32) {
-    if (d == 128)
-      hipLaunchKernelGGL((bwd_pre_kernel<128, float>), grid, block, 0, stream, (const float*)o,
-                         (const float*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale, N, lay);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<64, float>), grid, block, 0, stream, (const float*)o,
-                         (const float*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale, N, lay);
+    if (d == 128) go(IC<128>{}, IC<1>{});
+    else if (d == 96) go(IC<96>{}, IC<1>{});
+    else go(IC<64>{}, IC<1>{});
   } else {
-    if (d == 128)
-      hipLaunchKernelGGL((bwd_pre_kernel<128, bf16>), grid, block, 0, stream, (const bf16*)o,
-                         (const bf16*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale, N, lay);
-    else
-      hipLaunchKernelGGL((bwd_pre_kernel<64, bf16>), grid, block, 0, stream, (const bf16*)o,
-                         (const bf16*)dO, lse, ndrow, nlse, dq_acc, rows, inv_scale, N, lay);
+    if (d == 128) go(IC<128>{}, IC<0>{});
+    else if (d == 96) go(IC<96>{}, IC<0>{});
+    else go(IC<64>{}, IC<0>{});
   }
   return hipGetLastError();
 }
@@ -128,12 +136,12 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict_
                                                         const float* __restrict__ lpart, bf16* __restrict__ O,
                                                         float* __restrict__ LSE, int rows, int N, int nsplit,
                                                         RowLayout lay) {
-  constexpr int LPR = D / 8;            // lanes per row, 8 elements each
-  constexpr int RPB = 256 / LPR;        // rows per block
+  constexpr int LPR = lanes_per_row<D>();   // lanes per row (D/8 of them hold 8 elements each)
+  constexpr int RPB = 256 / LPR;            // rows per block
   const int tid = threadIdx.x;
   const int row = blockIdx.x * RPB + tid / LPR;
   const int part = tid % LPR;
-  if (row >= rows) return;
+  if (row >= rows || part >= D / 8) return;
   float m = -INFINITY;
   for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lpart[(size_t)s * rows + row]);
   float wsum = 0.f, acc[8] = {};
@@ -165,14 +173,16 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict_
 hipError_t launch_fwd_merge(const float* opart, const float* lpart, void* o, float* lse, int BH, int Nq,
                             int d, int nsplit, RowLayout lay, hipStream_t stream) {
   const int rows = BH * Nq;
-  const int rpb = 256 / (d / 8);
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
-  if (d == 128)
-    hipLaunchKernelGGL((fwd_merge_kernel<128>), grid, block, 0, stream, opart, lpart, (bf16*)o, lse, rows, Nq,
+  auto go = [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    constexpr int rpb = 256 / lanes_per_row<D>();
+    const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
+    hipLaunchKernelGGL((fwd_merge_kernel<D>), grid, block, 0, stream, opart, lpart, (bf16*)o, lse, rows, Nq,
                        nsplit, lay);
-  else
-    hipLaunchKernelGGL((fwd_merge_kernel<64>), grid, block, 0, stream, opart, lpart, (bf16*)o, lse, rows, Nq,
-                       nsplit, lay);
+  };
+  if (d == 128) go(IC<128>{});
+  else if (d == 96) go(IC<96>{});
+  else go(IC<64>{});
   return hipGetLastError();
 }
 

@@ -56,7 +56,9 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     float* __restrict__ dQacc, bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb,
     float scale, float c, RowLayout lay) {
   constexpr int BC = 128, BR = 64;
-  constexpr int ROWB = D * 2, CH = D / 8, KS = D / 16, DT = D / 32;
+  // ROWB: LDS bytes per row (d * 2, or 256 for d = 96); CH: 16-byte chunks per row
+  constexpr int ROWB = lds_pitch<D>(), CH = D / 8, KS = D / 16, DT = D / 32;
+  static_assert(!DQA || D != 96, "the atomic dQ variant splits d into 32-column slices over 4 waves");
   constexpr int QTB = BR * ROWB;          // bytes of one Q or dO tile
   constexpr int NQT = (D == 128) ? 2 : 1; // query tiles of dQ per wave
 
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, s16 = lane & 15;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the same value, known uniform
   const int RS = lay.row_stride(D);      // elements between a head's rows
-  const TileFetch<D * 2, BR> qfetch(wave_u, lane, RS * 2);
+  const TileFetch<ROWB, BR, 4, CH> qfetch(wave_u, lane, RS * 2);
   // Work items.  Causal: item c of a head is the key-block pair
   // (c, nkb-1-c), whose query walks together always cover the same number of
   // blocks, so every workgroup does the same work; the first block is walked
@@ -308,13 +310,14 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
             dk[dt] = mfma32(da[st], tq[t][j], dk[dt]);
           }
         };
-        // P^ = 2^(c (S - LSE/scale)), dS = P^ o (dP - D) for the RPC registers
-        // of chunk ch of tile t (one chunk per slot of a phase); the bf16
-        // operands are packed once registers 0..7 and 8..15 are done
-        constexpr int RPC = 16 / KS;
+        // P^ = 2^(c (S - LSE/scale)), dS = P^ o (dP - D) for registers
+        // [16 ch / KS, 16 (ch+1) / KS) of tile t (chunk ch of KS, one per slot
+        // of a phase); the bf16 operands are packed once registers 0..7 and
+        // 8..15 are done
         auto elem_chunk = [&](int t, int ch) {
+          const int r0 = 16 * ch / KS, r1 = 16 * (ch + 1) / KS;
 #pragma unroll
-          for (int r = RPC * ch; r < RPC * ch + RPC; ++r) {
+          for (int r = r0; r < r1; ++r) {
             float p = exp2_fast(s[t][r] * c);
             if constexpr (MASK) {
               const int q = qb0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -324,8 +327,10 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
             s[t][r] = p;
             dp[t][r] = p * dp[t][r];
           }
-          if ((RPC * ch + RPC) % 8 == 0) {
-            const int hi = (RPC * ch + RPC) / 8 - 1, o = 8 * hi;
+#pragma unroll
+          for (int hi = 0; hi < 2; ++hi) {
+            if (!(r0 < 8 * hi + 8 && r1 >= 8 * hi + 8)) continue;
+            const int o = 8 * hi;
             pa[2 * t + hi] = pack8(s[t][o], s[t][o + 1], s[t][o + 2], s[t][o + 3],
                                    s[t][o + 4], s[t][o + 5], s[t][o + 6], s[t][o + 7]);
             da[2 * t + hi] = pack8(dp[t][o], dp[t][o + 1], dp[t][o + 2], dp[t][o + 3],
@@ -444,6 +449,11 @@ static hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, con
   if (d == 128)
     return causal ? launch_bwd_bf16_t<128, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream)
                   : launch_bwd_bf16_t<128, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream);
+  if constexpr (!DQA) {
+    if (d == 96)
+      return causal ? launch_bwd_bf16_t<96, true, false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream)
+                    : launch_bwd_bf16_t<96, false, false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream);
+  }
   return causal ? launch_bwd_bf16_t<64, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream)
                 : launch_bwd_bf16_t<64, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream);
 }

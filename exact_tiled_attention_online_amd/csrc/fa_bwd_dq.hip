@@ -33,7 +33,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
     bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, RowLayout lay) {
   constexpr int BR = 32 * NW, BC = 64;
-  constexpr int ROWB = D * 2;        // bytes per row
+  constexpr int ROWB = lds_pitch<D>();   // LDS bytes per row (d * 2, or 256 for d = 96)
   constexpr int KS = D / 16;         // K-steps of the S and dP products
   constexpr int DT = D / 32;         // 32-row tiles of dQ^T
   constexpr int TILEB = BC * ROWB;   // bytes of one K or V tile
@@ -47,9 +47,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
   // so, which keeps the wave-level conditions below scalar branches
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
-  const TileBases<D * 2> tb(lane);
+  const TileBases<ROWB> tb(lane);
   const int RS = lay.row_stride(D);      // elements between a head's rows
-  const TileFetch<D * 2, BC, NW> fetch(wave, lane, RS * 2);
+  const TileFetch<ROWB, BC, NW, D / 8> fetch(wave, lane, RS * 2);
   const int bid = blockIdx.x;
   const int head = bid % BH;
   // causal: the longest query blocks are dispatched first
@@ -232,6 +232,9 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   if (d == 128)
     return causal ? launch_bwd_dq_t<128, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream)
                   : launch_bwd_dq_t<128, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream);
+  if (d == 96)
+    return causal ? launch_bwd_dq_t<96, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream)
+                  : launch_bwd_dq_t<96, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream);
   return causal ? launch_bwd_dq_t<64, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream)
                 : launch_bwd_dq_t<64, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream);
 }

@@ -167,16 +167,26 @@ FA_DEV void dma4_buf(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)lds_base, 4, voff, soff, 0, 0);
 }
 
-// Fetch ROWS rows (ROWB bytes each, rsb bytes apart in global memory)
-// starting at row0 of a bf16 matrix into a swizzled LDS tile, with the NW
-// waves of a workgroup.  Wave w,
+// LDS row pitch (bytes) of a tile of D-wide bf16 rows.  The swizzles above
+// cover 128- and 256-byte rows; the 192-byte rows of d = 96 sit in 256-byte
+// slots, whose chunks 12..15 hold no data (and are never read).
+template <int D>
+constexpr int lds_pitch() {
+  return D * 2 <= 128 ? 128 : 256;
+}
+
+// Fetch ROWS rows (VC 16-byte chunks each in global memory, rsb bytes apart)
+// starting at row0 of a bf16 matrix into a swizzled LDS tile of ROWB-byte
+// rows (VC <= ROWB/16), with the NW waves of a workgroup.  Wave w,
 // load j fills LDS bytes [(w*LPW + j) KB, +1 KB): tile row blk*RPL + lane/CH
 // at chunk position lane%CH, i.e. logical chunk (lane%CH) ^ swz(row).  Rows at
-// or past nrows read row nrows-1 instead (finite values the caller masks).
+// or past nrows read row nrows-1 instead (finite values the caller masks);
+// lanes whose chunk is past the row's VC chunks read its last chunk again
+// (their LDS slots are padding).
 // The per-lane byte offsets within a tile do not depend on row0, so they are
 // computed once; a whole tile is then fetched from a uniform base address plus
 // those offsets, and only a ragged last tile takes the clamped per-row path.
-template <int ROWB, int ROWS, int NW = 4>
+template <int ROWB, int ROWS, int NW = 4, int VC = ROWB / 16>
 struct TileFetch {
   static constexpr int CH = ROWB / 16, RPL = 1024 / ROWB, LPW = ROWS / RPL / NW;
   static_assert(LPW * RPL * NW == ROWS, "tile must split evenly over the waves");
@@ -188,7 +198,7 @@ struct TileFetch {
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
       const int row = (wave * LPW + j) * RPL + lane / CH;
-      const int ch = (lane % CH) ^ swz<ROWB>(row);
+      const int ch = min((lane % CH) ^ swz<ROWB>(row), VC - 1);
       goff[j] = (unsigned)row * rsb + (unsigned)(ch * 16);
     }
   }
@@ -203,7 +213,7 @@ struct TileFetch {
       for (int j = 0; j < LPW; ++j) {
         const int blk = wave * LPW + j;
         const int row = blk * RPL + lane / CH;
-        const int ch = (lane % CH) ^ swz<ROWB>(row);
+        const int ch = min((lane % CH) ^ swz<ROWB>(row), VC - 1);
         const int r = min(row0 + row, nrows - 1);
         dma16_buf(raw_rsrc(src), (unsigned)r * rsb + (unsigned)(ch * 16), 0, dst + blk * 1024);
       }

@@ -244,6 +244,9 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
   if (d == 128)
     return causal ? fwd_f32_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
                   : fwd_f32_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
+  if (d == 96)
+    return causal ? fwd_f32_t<96, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
+                  : fwd_f32_t<96, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
   return causal ? fwd_f32_t<64, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
                 : fwd_f32_t<64, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
 }
@@ -254,6 +257,9 @@ hipError_t launch_bwd_kv_f32(const float* q, const float* k, const float* v, con
   if (d == 128)
     return causal ? bwd_kv_f32_t<128, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream)
                   : bwd_kv_f32_t<128, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream);
+  if (d == 96)
+    return causal ? bwd_kv_f32_t<96, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream)
+                  : bwd_kv_f32_t<96, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream);
   return causal ? bwd_kv_f32_t<64, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream)
                 : bwd_kv_f32_t<64, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream);
 }
@@ -264,6 +270,9 @@ hipError_t launch_bwd_q_f32(const float* q, const float* k, const float* v, cons
   if (d == 128)
     return causal ? bwd_q_f32_t<128, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream)
                   : bwd_q_f32_t<128, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream);
+  if (d == 96)
+    return causal ? bwd_q_f32_t<96, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream)
+                  : bwd_q_f32_t<96, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream);
   return causal ? bwd_q_f32_t<64, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream)
                 : bwd_q_f32_t<64, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream);
 }

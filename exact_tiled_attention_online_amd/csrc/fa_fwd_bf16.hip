@@ -2,7 +2,7 @@
 //
 // One workgroup (8 waves, one workgroup per CU, two waves per SIMD) owns
 // BR = 256 query rows of one (batch, head); each wave owns 32 of them.
-// Key/value tiles of BC rows (64 for d = 128, 128 for d = 64) stream through
+// Key/value tiles of BC rows (64 for d = 128 and 96, 128 for d = 64) stream through
 // two LDS buffers (the next tile is fetched while the current one is used).
 // Per tile and wave:
 //   S^T = K_j Q_w^T            v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
   // 32 in the split mode, whose one-wave workgroups need little LDS)
   constexpr int BR = 32 * NW;
   constexpr int MT = BC / 32;        // 32-key halves of a tile
-  constexpr int ROWB = D * 2;        // bytes per row
+  constexpr int ROWB = lds_pitch<D>();   // LDS bytes per row (d * 2, or 256 for d = 96)
   constexpr int KS = D / 16;         // K-steps of the S product
   constexpr int DT = D / 32;         // 32-row tiles of O^T
   constexpr int TILEB = BC * ROWB;   // bytes of one K or V tile
@@ -75,9 +75,9 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
   // so, which keeps the wave-level conditions below scalar branches
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
-  const TileBases<D * 2> tb(lane);
+  const TileBases<ROWB> tb(lane);
   const int RS = lay.row_stride(D);      // elements between a head's rows
-  const TileFetch<D * 2, BC, NW> fetch(wave, lane, RS * 2);
+  const TileFetch<ROWB, BC, NW, D / 8> fetch(wave, lane, RS * 2);
   const int bid = blockIdx.x;
   const int head = bid % BH;
   const int Nk = SPLIT ? sp.Nk : N;     // key rows
@@ -340,6 +340,9 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   if (d == 128)
     return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
                   : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
+  if (d == 96)
+    return causal ? launch_fwd_bf16_t<96, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
+                  : launch_fwd_bf16_t<96, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
   return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
                 : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
 }
@@ -365,6 +368,9 @@ hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, fl
   if (d == 128)
     return causal ? launch_fwd_split_t<128, true>(q, k, v, BH, Nq, scale, lay, sp, stream)
                   : launch_fwd_split_t<128, false>(q, k, v, BH, Nq, scale, lay, sp, stream);
+  if (d == 96)
+    return causal ? launch_fwd_split_t<96, true>(q, k, v, BH, Nq, scale, lay, sp, stream)
+                  : launch_fwd_split_t<96, false>(q, k, v, BH, Nq, scale, lay, sp, stream);
   return causal ? launch_fwd_split_t<64, true>(q, k, v, BH, Nq, scale, lay, sp, stream)
                 : launch_fwd_split_t<64, false>(q, k, v, BH, Nq, scale, lay, sp, stream);
 }

@@ -26,7 +26,7 @@
  * scale * q_i . k_j.  The causal mask keeps key j for query i iff j <= i
  * (queries and keys share the index range 0..N-1).
  *
- * Supported: d in {64, 128}; N >= 1 (any N, tails are masked); B, H >= 1 with
+ * Supported: d in {64, 96, 128}; N >= 1 (any N, tails are masked); B, H >= 1 with
  * B*H*N*d < 2^31; scale finite and > 0; causal in {0, 1}.
  *
  * Ownership: every pointer is a device pointer owned by the caller.  The
@@ -113,8 +113,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * Argument meaning, checks and errors are those of fa_bwd.  With the
  * environment variable FA_DQ_MODE=atomic (bf16 only) the dQ products run
  * inside fa_bwd_dkdv instead, as fp32 atomic adds into the workspace, and
- * fa_bwd_dq converts that accumulator; the default is the query-outer kernel,
- * which measured faster.
+ * fa_bwd_dq converts that accumulator (d = 64 and 128; d = 96 ignores the
+ * variable); the default is the query-outer kernel, which measured faster.
  */
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
                       float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype,
@@ -175,7 +175,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
  * fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits) bytes (same
  * num_splits), 256-byte aligned; its contents on entry do not matter.
  * Supported: dtype FA_BF16 only (FA_ERR_UNSUPPORTED otherwise), d in
- * {64, 128}, 0 <= num_splits <= 1024.  Errors, ownership and streams as for
+ * {64, 96, 128}, 0 <= num_splits <= 1024.  Errors, ownership and streams as for
  * fa_fwd; a missing or small workspace is FA_ERR_WORKSPACE.
  */
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);

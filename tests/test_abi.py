@@ -87,10 +87,15 @@ def test_workspace_size():
     assert f32 == 2 * 512
     assert fa.fa_bwd_workspace_bytes(1, 1, 100, 64, fa.FA_BF16) % 256 == 0
     assert fa.fa_bwd_workspace_bytes(0, 1, 128, 64, fa.FA_BF16) == 0
-    assert fa.fa_bwd_workspace_bytes(1, 1, 128, 96, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 128, 80, fa.FA_BF16) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 2, 100, 96, fa.FA_BF16) == round_up(200 * 4) * 2 + round_up(200 * 96 * 4)
 
 
 P = 0x10000  # a non-null, 256-byte aligned stand-in address; never dereferenced
+
+
+def round_up(x, a=256):
+    return -(-x // a) * a
 
 
 def fwd(**kw):
@@ -113,7 +118,7 @@ def bwd(**kw):
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
     (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1), (dict(causal=2), -1),
     (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1), (dict(scale=0.0), -1),
-    (dict(scale=-0.1), -1), (dict(d=96), -2), (dict(d=256), -2), (dict(dtype=7), -2),
+    (dict(scale=-0.1), -1), (dict(d=80), -2), (dict(d=256), -2), (dict(dtype=7), -2),
     (dict(q=P + 8), -1), (dict(lse=P + 2), -1),
     (dict(B=1024, H=1024, N=4096, d=128), -2),
     (dict(layout=2), -1), (dict(layout=-1), -1),
@@ -159,7 +164,7 @@ def splitkv(**kw):
     (dict(q=None), -1), (dict(k=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
     (dict(Nq=0), -1), (dict(Nk=0), -1), (dict(Nq=1001), -1), (dict(causal=2), -1),
     (dict(num_splits=-1), -1), (dict(num_splits=1025), -1), (dict(layout=3), -1),
-    (dict(scale=float("nan")), -1), (dict(d=96), -2), (dict(dtype=fa.FA_FP32), -2), (dict(dtype=5), -2),
+    (dict(scale=float("nan")), -1), (dict(d=80), -2), (dict(dtype=fa.FA_FP32), -2), (dict(dtype=5), -2),
     (dict(q=P + 8), -1), (dict(workspace=None), -3), (dict(workspace_bytes=100), -3),
     (dict(workspace=P + 64), -3), (dict(B=64, H=64, Nk=1 << 20), -2),
 ])
@@ -180,7 +185,7 @@ def test_splitkv_noncausal_allows_more_queries_than_keys_and_sizes_workspace():
         used = -(-tiles // per)
         r = lambda x: -(-x // 256) * 256
         assert n == r(used * rows * 128 * 4) + r(used * rows * 4), ns
-    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 1000, 96, 0) == 0
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 1000, 80, 0) == 0
     assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 1000, 128, 2000) == 0
 
 

@@ -33,7 +33,7 @@ def _full_compare(x, dtype, causal, scale, where, layout=0):
 
 EDGE = [(dtype, d, causal, n)
         for dtype in ("bf16", "fp32")
-        for d in (64, 128)
+        for d in (64, 96, 128)
         for causal in (False, True)
         for n in (1, 17, 64, 129, 300)]
 
@@ -207,7 +207,7 @@ def test_atomic_dq_mode(monkeypatch, d, causal, n):
 # meet the oracle bar on their own.
 BNHD = [(dtype, d, causal, n)
         for dtype in ("bf16", "fp32")
-        for d in (64, 128)
+        for d in (64, 96, 128)
         for causal in (False, True)
         for n in (17, 300)]
 
@@ -286,3 +286,32 @@ def test_scores_rising_along_the_keys(dtype, causal):
     for (b, h), wv in want.items():
         compare({n: res[n][b, h] for n in ("o", "lse")}, wv, dtype, names=("o", "lse"),
                 where=f"rising {dtype} c{int(causal)} head ({b},{h})")
+
+
+def test_head_dim_96_larger_size_sampled_heads():
+    """d = 96 (192-byte rows in 256-byte LDS slots) at a causal 2 x 12 x 4096
+    size in the launch configuration of the other sizes, on sampled heads."""
+    import torch
+    log("[d96] 2x12x4096x96 causal bf16")
+    w = gen.workload("c3")
+    x = gen.make_inputs(w, shape=(2, 12, 4096, 96), seed=96)
+    scale = 1.0 / math.sqrt(96)
+    res = run_gpu(x, "bf16", True, scale)
+    heads = [(0, 0), (1, 11)]
+    want = oracle_heads(x, True, scale, heads=heads)
+    for (b, h), wv in want.items():
+        compare({n: res[n][b, h] for n in wv}, wv, "bf16", where=f"d96 head ({b},{h})")
+    torch.cuda.empty_cache()
+
+
+def test_head_dim_96_atomic_mode_falls_back(monkeypatch):
+    """FA_DQ_MODE=atomic has no d = 96 variant; d = 96 keeps the query-outer
+    dQ kernel and the same results."""
+    log("[d96] atomic mode request")
+    w = gen.workload("c2")
+    x = gen.make_inputs(w, shape=(1, 2, 300, 96), seed=961)
+    a = run_gpu(x, "bf16", True, 0.1)
+    monkeypatch.setenv("FA_DQ_MODE", "atomic")
+    b = run_gpu(x, "bf16", True, 0.1)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert np.array_equal(a[n], b[n]), n

@@ -50,6 +50,8 @@ CASES = [
     (1, 2, 100, 100, 128, False, 4),
     (1, 1, 64, 8192, 128, True, 1024),
     (3, 2, 5, 31, 128, True, 0),
+    (2, 2, 3, 777, 96, True, 0),
+    (1, 3, 40, 500, 96, False, 2),
     (1, 1, 1, 1, 64, True, 0),
 ]
 
