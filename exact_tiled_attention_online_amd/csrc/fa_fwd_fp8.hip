@@ -21,9 +21,11 @@
 // matters; l sums the same scaled values in fp32, so the factor cancels in
 // O = sum(P V) / l and LSE subtracts 7 ln 2.
 //
-// Work split: one workgroup (8 waves, two per SIMD) owns 256 query rows of one
-// (batch, head), each wave 32; key/value tiles of 64 rows of 128 bytes stream
-// through two LDS buffers.  Per tile and wave:
+// Work split: one workgroup (4 waves) owns 128 query rows of one (batch, head),
+// each wave 32, and three workgroups share a CU (three waves per SIMD: the
+// softmax's vector work, which bounds this kernel, then overlaps the products
+// of other waves more often than with two); key/value tiles of 64 rows of 128
+// bytes stream through two LDS buffers.  Per tile and wave:
 //   S^T (2 x 32 keys x 32 queries): A = K rows (natural 16-byte LDS reads),
 //       B = the wave's Q rows in registers; 2 K-steps of 64 d;
 //   O^T += V^T P^T, one K-step of all 64 keys: B = P^T packed to e4m3
@@ -74,13 +76,18 @@ FA_DEV int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(
+#ifndef FA_FP8_NW
+#define FA_FP8_NW 4
+#endif
+// NW waves per workgroup; at about 160 VGPRs three waves fit per SIMD, so
+// three 4-wave workgroups share a CU
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
     const unsigned char* __restrict__ Q, const unsigned char* __restrict__ K,
     const unsigned char* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N,
     int nqb, float scale_qk, float c, float dv, RowLayout lay) {
   static_assert(D == 128, "FP8 tiles are laid out for 128-byte rows");
-  constexpr int NW = 8, BR = 32 * NW, BC = 64;
+  constexpr int BR = 32 * NW, BC = 64;
   constexpr int ROWB = D;            // bytes per e4m3 row
   constexpr int KS = D / 64;         // K-steps of the S product
   constexpr int DT = D / 32;         // 32-row tiles of O^T
@@ -284,10 +291,10 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(
 template <bool CAUSAL>
 static hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                                    int N, float scale_qk, float dv, RowLayout lay, hipStream_t stream) {
-  constexpr int BR = 256;
+  constexpr int NW = FA_FP8_NW, BR = 32 * NW;
   const int nqb = (N + BR - 1) / BR;
-  const dim3 grid((unsigned)(nqb * BH)), block(512);
-  hipLaunchKernelGGL((fwd_fp8_kernel<128, CAUSAL>), grid, block, 0, stream, (const unsigned char*)q,
+  const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
+  hipLaunchKernelGGL((fwd_fp8_kernel<128, CAUSAL, NW>), grid, block, 0, stream, (const unsigned char*)q,
                      (const unsigned char*)k, (const unsigned char*)v, (bf16*)o, lse, BH, N, nqb, scale_qk,
                      scale_qk * kLog2e, dv, lay);
   return hipGetLastError();
