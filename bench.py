@@ -14,7 +14,8 @@ fwd = 4*B*H*N^2*d and bwd = 10*B*H*N^2*d, both halved for a causal mask.
 Prints one JSON line.  Default workload: B=1, H=32, N=8192, d=128, causal,
 bf16 (the headline shape).  ``detail.decode`` adds the split-key-range forward
 (fa_fwd_splitkv) on a decode step of 8 x 32 heads, one query against 16384
-cached keys, with its HBM roofline (skip with --no-decode), and
+cached keys, with its HBM roofline, and ``detail.decode_fp8`` the same step
+against an FP8 cache (fa_fwd_splitkv_fp8) (skip both with --no-decode), and
 ``detail.fp8_forward`` the FP8 forward (fa_fwd_fp8) on the headline shape
 against the FP8 peak (skip with --no-fp8).
 """
@@ -266,6 +267,68 @@ def decode_measurement(fa, gen, torch, dev, stream, with_oracle, reps=50, oracle
         res["oracle_check"] = {"heads": done, "max_err_over_tolerance": {n: round(v, 4) for n, v in worst.items()},
                                "within_tolerance": all(v <= 1.0 for v in worst.values())}
     del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_fp8_measurement(fa, gen, torch, dev, stream, with_oracle, reps=50, oracle_budget_s=4.0):
+    """fa_fwd_splitkv_fp8 on the decode workload with e4m3fn q, k, v (an FP8
+    key/value cache): time per call, HBM roofline on the algorithmic bytes
+    (K, V, Q read once at one byte per element; O bf16 and LSE written once),
+    and the oracle on whole heads within the FP8 bound."""
+    import numpy as np
+    w = gen.DECODE
+    xq = gen.make_fp8_inputs((w.B, w.H, w.Nq, w.d), seed=w.seed, sigma_qk=w.sigma_qk)
+    xk = gen.make_fp8_inputs((w.B, w.H, w.Nk, w.d), seed=w.seed + 100, sigma_qk=w.sigma_qk, sigma_v=w.sigma_v)
+    q8, k8, v8 = (torch.from_numpy(a).to(dev) for a in (xq["q8"], xk["k8"], xk["v8"]))
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    nbytes = fa.fa_fwd_splitkv_fp8_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d, 0)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    sp = stream.cuda_stream
+    dq, dk, dv = xq["descale_q"], xk["descale_k"], xk["descale_v"]
+
+    def call():
+        st = fa.fa_fwd_splitkv_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   w.B, w.H, w.Nq, w.Nk, w.d, w.causal, w.scale, dq, dk, dv, 0, ws.data_ptr(),
+                                   ws.numel(), sp, fa.FA_LAYOUT_BHND)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd_splitkv_fp8")
+
+    for _ in range(10):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    algo = w.kv_bytes() // 2 + w.B * w.H * w.Nq * w.d * (1 + 2) + 4 * w.B * w.H * w.Nq
+    gbs = algo / (ms * 1e-3) / 1e9
+    res = {"workload": w.name.replace("bf16", "fp8"), "dtype": "fp8 e4m3fn q, k, v; bf16 out",
+           "us_per_call": round(ms * 1e3, 2), "calls": reps,
+           "roofline": {"kernel": "fwd_fp8_kernel (split mode) + fwd_merge_kernel", "bound": "hbm",
+                        "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "algorithmic_bytes": int(algo)}}
+    if with_oracle:
+        from oracle import ref
+        got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        worst, done, t0 = {"o": 0.0, "lse": 0.0}, 0, time.perf_counter()
+        for b, h in heads:
+            r = ref.forward_rect(xq["q"], xk["k"], xk["v"], w.scale, w.causal, heads=[(b, h)])[(b, h)]
+            vmax = float(np.abs(xk["v"][b, h]).max())
+            tol = (2.0 ** -4 + w.Nk * 2.0 ** -17) * vmax + 2.0 ** -9 * float(np.abs(r["o"]).max())
+            worst["o"] = max(worst["o"], float(np.abs(got_o[b, h] - r["o"]).max()) / tol)
+            worst["lse"] = max(worst["lse"], float(np.abs(got_l[b, h] - r["lse"]).max()) / 1e-3)
+            done += 1
+            if time.perf_counter() - t0 > oracle_budget_s:
+                break
+        res["oracle_check"] = {"heads": done, "max_err_over_tolerance": {n: round(v, 4) for n, v in worst.items()},
+                               "within_tolerance": all(v <= 1.0 for v in worst.values())}
+    del q8, k8, v8, o, lse, ws
     torch.cuda.empty_cache()
     return res
 
@@ -525,6 +588,7 @@ def main():
         out["detail"]["fp8_forward"] = fp8_measurement(fa, gen, torch, dev, stream, w, not args.no_cpu_baseline)
     if not args.no_decode:
         out["detail"]["decode"] = decode_measurement(fa, gen, torch, dev, stream, not args.no_cpu_baseline)
+        out["detail"]["decode_fp8"] = decode_fp8_measurement(fa, gen, torch, dev, stream, not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         base, heads, ref = cpu_baseline(w, x)
         out["cpu_baseline"] = base

@@ -9,5 +9,6 @@ FP8 forward, the split-key-range forward, fa_strerror) and the torch-tensor conv
 from ._lib import (  # noqa: F401
     FA_BF16, FA_FP32, FA_LAYOUT_BHND, FA_LAYOUT_BNHD, FAError, LIB_PATH, backward, fa_bwd,
     fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_bwd_workspace_bytes, fa_fwd, fa_fwd_fp8, fa_fwd_splitkv,
-    fa_fwd_splitkv_workspace_bytes, fa_strerror, forward, forward_fp8, forward_splitkv, load, workspace,
+    fa_fwd_splitkv_workspace_bytes, fa_fwd_splitkv_fp8, fa_fwd_splitkv_fp8_workspace_bytes, fa_strerror,
+    forward, forward_fp8, forward_splitkv, forward_splitkv_fp8, load, workspace,
 )

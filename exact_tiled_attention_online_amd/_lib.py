@@ -18,7 +18,8 @@ FA_BF16, FA_FP32 = 0, 1
 FA_LAYOUT_BHND, FA_LAYOUT_BNHD = 0, 1
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
-           "fa_bwd_dq", "fa_fwd_fp8", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv", "fa_strerror")
+           "fa_bwd_dq", "fa_fwd_fp8", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv",
+           "fa_fwd_splitkv_fp8_workspace_bytes", "fa_fwd_splitkv_fp8", "fa_strerror")
 
 _lib = None
 
@@ -57,6 +58,10 @@ def load():
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp, i, i]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_fp8_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_fwd_splitkv_fp8_workspace_bytes.restype = sz
+    lib.fa_fwd_splitkv_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, f, i, vp, sz, vp, i]
+    lib.fa_fwd_splitkv_fp8.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -111,6 +116,17 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, 
                    stream, dtype, layout) -> int:
     return load().fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale), num_splits,
                                  workspace, workspace_bytes, stream, dtype, layout)
+
+
+def fa_fwd_splitkv_fp8_workspace_bytes(B, H, Nq, Nk, d, num_splits) -> int:
+    return load().fa_fwd_splitkv_fp8_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+
+
+def fa_fwd_splitkv_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, descale_q, descale_k, descale_v,
+                       num_splits, workspace, workspace_bytes, stream, layout) -> int:
+    return load().fa_fwd_splitkv_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale),
+                                     float(descale_q), float(descale_k), float(descale_v), num_splits, workspace,
+                                     workspace_bytes, stream, layout)
 
 
 def fa_strerror(status: int) -> str:
@@ -237,4 +253,30 @@ def forward_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float
                     scale, descale_q, descale_k, descale_v, _stream(stream), layout)
     if st != FA_OK:
         raise FAError(st, "fa_fwd_fp8")
+    return o, l
+
+
+def forward_splitkv_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float, causal: bool,
+                        scale: float, num_splits: int = 0, out=None, lse=None, ws=None, stream=None,
+                        layout: int = FA_LAYOUT_BHND):
+    """O (bf16), LSE for e4m3fn codes q8 [B,H,Nq,d] against k8, v8 [B,H,Nk,d]
+    (uint8 device tensors; [B,Nq,H,d] / [B,Nk,H,d] with FA_LAYOUT_BNHD)
+    through the split-key-range FP8 forward."""
+    import torch
+    B, H, Nq, d = _dims(q8, layout)
+    Nk = _dims(k8, layout)[2]
+    _check((q8,), q8.shape)
+    _check((k8, v8), k8.shape)
+    if q8.dtype != torch.uint8 or k8.dtype != torch.uint8:
+        raise TypeError("FP8 inputs are passed as uint8 e4m3fn codes")
+    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device) if lse is None else lse
+    if ws is None:
+        n = fa_fwd_splitkv_fp8_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q8.device)
+    st = fa_fwd_splitkv_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Nq,
+                            Nk, d, causal, scale, descale_q, descale_k, descale_v, num_splits, ws.data_ptr(),
+                            ws.numel(), _stream(stream), layout)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_splitkv_fp8")
     return o, l

@@ -74,9 +74,10 @@ bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d, int 
   return ws && aligned(ws, kAlign) && bytes >= carve(nullptr, B, H, N, d, dtype).bytes;
 }
 
-// Key ranges of the split forward.  num_splits = 0 lets the library choose:
-// about kSplitTargetWGs workgroups in all, at least 4 tiles per range, at most
-// kMaxAutoSplits ranges.  Ranges are whole tiles and none is empty.
+// Key ranges of the split forwards (tiles of 32 keys for bf16, 64 for FP8).
+// num_splits = 0 lets the library choose: about kSplitTargetWGs workgroups in
+// all, at least 4 tiles per range, at most kMaxAutoSplits ranges.  Ranges are
+// whole tiles and none is empty.
 constexpr int kMaxAutoSplits = 256;
 constexpr int kMaxSplits = 1024;
 constexpr long long kSplitTargetWGs = 1024;
@@ -88,8 +89,8 @@ struct SplitPlan {
   size_t bytes;
 };
 
-SplitPlan split_plan(void* base, int B, int H, int Nq, int Nk, int d, int num_splits) {
-  const int tiles = (Nk + fa::kSplitBC - 1) / fa::kSplitBC;
+SplitPlan split_plan(void* base, int B, int H, int Nq, int Nk, int d, int num_splits, int tile = fa::kSplitBC) {
+  const int tiles = (Nk + tile - 1) / tile;
   long long s = num_splits;
   if (s <= 0) {
     const long long wgs = (long long)B * H * ((Nq + 31) / 32);
@@ -100,7 +101,7 @@ SplitPlan split_plan(void* base, int B, int H, int Nq, int Nk, int d, int num_sp
   const int per = (int)((tiles + s - 1) / s);   // tiles per range
   SplitPlan p{};
   p.nsplit = (tiles + per - 1) / per;
-  p.span = per * fa::kSplitBC;
+  p.span = per * tile;
   const size_t rows = (size_t)B * H * Nq;
   char* c = static_cast<char*>(base);
   p.opart = reinterpret_cast<float*>(c);
@@ -262,6 +263,35 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   const fa::RowLayout lay = row_layout(H, layout);
   const int r = hip_status(fa::launch_fwd_split_bf16(q, k, v, p.opart, p.lpart, B * H, Nq, Nk, d, causal != 0,
                                                      scale, p.nsplit, p.span, lay, s));
+  if (r != FA_OK) return r;
+  return hip_status(fa::launch_fwd_merge(p.opart, p.lpart, o, lse, B * H, Nq, d, p.nsplit, lay, s));
+}
+
+size_t fa_fwd_splitkv_fp8_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  if (check_split(B, H, Nq, Nk, d, 0, 1.f, num_splits, FA_BF16, FA_LAYOUT_BHND) != FA_OK || d != 128) return 0;
+  return split_plan(nullptr, B, H, Nq, Nk, d, num_splits, fa::kSplitBC8).bytes;
+}
+
+int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                       int Nk, int d, int causal, float scale, float descale_q, float descale_k, float descale_v,
+                       int num_splits, void* workspace, size_t workspace_bytes, void* stream, int layout) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
+  const int st = check_split(B, H, Nq, Nk, d, causal, scale, num_splits, FA_BF16, layout);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  for (float x : {descale_q, descale_k, descale_v})
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID;
+  if (!std::isfinite(scale * descale_q * descale_k) || !(scale * descale_q * descale_k > 0.f)) return FA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  if (!workspace || !aligned(workspace, kAlign) ||
+      workspace_bytes < split_plan(nullptr, B, H, Nq, Nk, d, num_splits, fa::kSplitBC8).bytes)
+    return FA_ERR_WORKSPACE;
+  const SplitPlan p = split_plan(workspace, B, H, Nq, Nk, d, num_splits, fa::kSplitBC8);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const fa::RowLayout lay = row_layout(H, layout);
+  const int r = hip_status(fa::launch_fwd_split_fp8(q, k, v, p.opart, p.lpart, B * H, Nq, Nk, causal != 0, scale,
+                                                    descale_q, descale_k, descale_v, p.nsplit, p.span, lay, s));
   if (r != FA_OK) return r;
   return hip_status(fa::launch_fwd_merge(p.opart, p.lpart, o, lse, B * H, Nq, d, p.nsplit, lay, s));
 }

@@ -42,16 +42,6 @@ namespace fa {
 #ifndef FA_FWD_BC64
 #define FA_FWD_BC64 128
 #endif
-// Arguments of the split-key-range mode (unused otherwise).
-struct SplitArgs {
-  int Nk;         // key/value rows per head
-  int off;        // causal offset: query row i sits at key position i + off (off = Nk - Nq)
-  int nsplit;     // key ranges per head
-  int span;       // keys per range, a multiple of the tile
-  float* opart;   // [nsplit][BH][N][D]: each range's O, normalised by its own l
-  float* lpart;   // [nsplit][BH][N]: each range's LSE, -inf where a row sees no key of it
-};
-
 template <int D, bool CAUSAL, int NW, int BC, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,

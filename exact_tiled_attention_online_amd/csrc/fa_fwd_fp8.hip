@@ -80,12 +80,14 @@ FA_DEV int pack_fp8x4(float a, float b, float c, float d) {
 #define FA_FP8_NW 4
 #endif
 // NW waves per workgroup; at about 160 VGPRs three waves fit per SIMD, so
-// three 4-wave workgroups share a CU
-template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
+// three 4-wave workgroups share a CU.  SPLIT: the split-key-range mode of the
+// bf16 forward (Nq queries against Nk keys, one range of whole tiles per
+// workgroup, partial O and LSE to the workspace for the merge kernel).
+template <int D, bool CAUSAL, int NW, bool SPLIT>
+__global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
     const unsigned char* __restrict__ Q, const unsigned char* __restrict__ K,
     const unsigned char* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N,
-    int nqb, float scale_qk, float c, float dv, RowLayout lay) {
+    int nqb, float scale_qk, float c, float dv, RowLayout lay, SplitArgs sp) {
   static_assert(D == 128, "FP8 tiles are laid out for 128-byte rows");
   constexpr int BR = 32 * NW, BC = 64;
   constexpr int ROWB = D;            // bytes per e4m3 row
@@ -104,12 +106,21 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
   const TileFetch<ROWB, BC, NW> fetch(wave, lane, RS);
   const int bid = blockIdx.x;
   const int head = bid % BH;
-  const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);   // longest blocks first
+  const int Nk = SPLIT ? sp.Nk : N;     // key rows
+  const int off = SPLIT ? sp.off : 0;   // causal offset of the query rows
+  int qb, split = 0;
+  if constexpr (SPLIT) {
+    split = (bid / BH) % sp.nsplit;
+    qb = bid / BH / sp.nsplit;
+  } else {
+    qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);   // longest blocks first
+  }
   const size_t hoff = lay.head_off(head, N, D);
+  const size_t khoff = lay.head_off(head, Nk, D);
   const unsigned char* Qh = Q + hoff;
   // TileFetch moves bytes; it takes the tile base as a bf16 pointer
-  const bf16* Kh = reinterpret_cast<const bf16*>(K + hoff);
-  const bf16* Vh = reinterpret_cast<const bf16*>(V + hoff);
+  const bf16* Kh = reinterpret_cast<const bf16*>(K + khoff);
+  const bf16* Vh = reinterpret_cast<const bf16*>(V + khoff);
 
   const int q0 = qb * BR + wave * 32;
   const int qrow = q0 + l32;
@@ -147,12 +158,19 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
     for (int t = 0; t < DT; ++t) vb[t] = r0 * ROWB + (((2 * t + (G & 1)) ^ swz<ROWB>(r0)) << 4) + 8 * u;
   }
 
-  const int kv_end = CAUSAL ? min(N, qb * BR + BR) : N;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  // keys of this workgroup: tiles jlo .. jlo + ntiles - 1
+  int kv_lo = 0, kv_end = Nk;
+  if constexpr (SPLIT) {
+    kv_lo = split * sp.span;
+    kv_end = min(Nk, kv_lo + sp.span);
+  }
+  if (CAUSAL) kv_end = min(kv_end, qb * BR + BR + off);
+  const int jlo = kv_lo / BC;
+  const int ntiles = max(0, (kv_end + BC - 1) / BC - jlo);
   int wave_tiles = 0;
   if (q0 < N) {
-    const int wkv_end = CAUSAL ? min(N, q0 + 32) : N;
-    wave_tiles = (wkv_end + BC - 1) / BC;
+    const int wkv_end = CAUSAL ? min(kv_end, q0 + 32 + off) : kv_end;
+    wave_tiles = max(0, (wkv_end + BC - 1) / BC - jlo);
   }
 
   f32x16 oacc[DT];
@@ -166,8 +184,8 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
     const char* Kt = b ? sK1 : sK0;
     const char* Vt = b ? sV1 : sV0;
     if (j + 1 < ntiles) {
-      fetch(Kh, (j + 1) * BC, N, b ? sK0 : sK1);
-      fetch(Vh, (j + 1) * BC, N, b ? sV0 : sV1);
+      fetch(Kh, (jlo + j + 1) * BC, Nk, b ? sK0 : sK1);
+      fetch(Vh, (jlo + j + 1) * BC, Nk, b ? sV0 : sV1);
     }
     if (j < wave_tiles) {
       // Slots: KS slots of two S products (the two 32-key halves), the
@@ -189,7 +207,7 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
       };
       f32x16 s[2] = {f32x16{}, f32x16{}};
       i32x8 pb;
-      const int kvb = j * BC;
+      const int kvb = (jlo + j) * BC;
 #pragma unroll
       for (int i = 0; i < DIST; ++i) read_slot(i);
 #pragma clang loop unroll(full)
@@ -205,14 +223,14 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
         if (i != KS - 1) continue;
         __builtin_amdgcn_sched_barrier(0);
         // s[mt][4*r4+jj] = q8_qrow . k8_kv with kv = kvb + 32*mt + 8*r4 + 4*h + jj
-        const bool need_mask = (kvb + BC > N) || (CAUSAL && kvb + BC - 1 > q0);
+        const bool need_mask = (kvb + BC > Nk) || (CAUSAL && kvb + BC - 1 > q0 + off);
         if (need_mask) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
-              const bool dead = (kv >= N) | (CAUSAL & (kv > qrow));
+              const bool dead = (kv >= Nk) | (CAUSAL & (kv > qrow + off));
               s[mt][r] = dead ? -INFINITY : s[mt][r];
             }
         }
@@ -224,9 +242,10 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
         mx = half_max(mx);
         // as in the bf16 forward, the reference maximum moves (with O and l
         // rescaled) only when a row gains more than a factor 2^1 over it, so
-        // that 2^7 p stays at most 2^8 < 448
+        // that 2^7 p stays at most 2^8 < 448 (split mode: a row that has seen
+        // no key yet keeps -inf, no rescale and p = 0, as in the bf16 forward)
         if (__builtin_amdgcn_ballot_w64((mx - m_run) * c > 1.f) != 0) {
-          const float alpha = exp2_fast((m_run - mx) * c);
+          const float alpha = (SPLIT && m_run == -INFINITY) ? 0.f : exp2_fast((m_run - mx) * c);
           l_run *= alpha;
 #pragma unroll
           for (int t = 0; t < DT; ++t)
@@ -234,7 +253,7 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
             for (int r = 0; r < 16; ++r) oacc[t][r] *= alpha;
           m_run = mx;
         }
-        const float nb = 7.f - m_run * c;
+        const float nb = (SPLIT && m_run == -INFINITY) ? 7.f : 7.f - m_run * c;
         float rs = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -258,8 +277,8 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
     __syncthreads();
   };
 
-  fetch(Kh, 0, N, sK0);
-  fetch(Vh, 0, N, sV0);
+  fetch(Kh, jlo * BC, Nk, sK0);
+  fetch(Vh, jlo * BC, Nk, sV0);
   __syncthreads();
   for (int j = 0;;) {
     body(IC<0>{}, j);
@@ -270,6 +289,28 @@ __global__ __launch_bounds__(64 * NW, 12 / NW) void fwd_fp8_kernel(
 
   if (q0 >= N) return;
   const float l_tot = half_sum(l_run);
+  if constexpr (SPLIT) {
+    if (qrow < N) {
+      // this range's O and LSE; a row that saw no key of the range has l = 0
+      const bool seen = l_tot > 0.f;
+      const float f = seen ? dv / l_tot : 0.f;
+      const size_t prow = ((size_t)split * BH + head) * N + qrow;
+      float* orow = sp.opart + prow * D;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float4 x;
+          x.x = oacc[t][4 * i + 0] * f;
+          x.y = oacc[t][4 * i + 1] * f;
+          x.z = oacc[t][4 * i + 2] * f;
+          x.w = oacc[t][4 * i + 3] * f;
+          *reinterpret_cast<float4*>(orow + 32 * t + 8 * i + 4 * h) = x;
+        }
+      if (h == 0) sp.lpart[prow] = seen ? m_run * scale_qk + (log2_fast(l_tot) - 7.f) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (qrow < N) {
     const float f = dv / l_tot;
     bf16* Orow = O + hoff + (size_t)qrow * RS;
@@ -294,9 +335,9 @@ static hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, 
   constexpr int NW = FA_FP8_NW, BR = 32 * NW;
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
-  hipLaunchKernelGGL((fwd_fp8_kernel<128, CAUSAL, NW>), grid, block, 0, stream, (const unsigned char*)q,
+  hipLaunchKernelGGL((fwd_fp8_kernel<128, CAUSAL, NW, false>), grid, block, 0, stream, (const unsigned char*)q,
                      (const unsigned char*)k, (const unsigned char*)v, (bf16*)o, lse, BH, N, nqb, scale_qk,
-                     scale_qk * kLog2e, dv, lay);
+                     scale_qk * kLog2e, dv, lay, SplitArgs{});
   return hipGetLastError();
 }
 
@@ -306,6 +347,29 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
   const float scale_qk = scale * dq * dk;
   return causal ? launch_fwd_fp8_t<true>(q, k, v, o, lse, BH, N, scale_qk, dv, lay, stream)
                 : launch_fwd_fp8_t<false>(q, k, v, o, lse, BH, N, scale_qk, dv, lay, stream);
+}
+
+// Split mode: one-wave workgroups of 32 query rows against one key range of
+// whole 64-key tiles (32 KB of LDS), partial results to the workspace.
+template <bool CAUSAL>
+static hipError_t launch_fwd_split_fp8_t(const void* q, const void* k, const void* v, int BH, int Nq,
+                                         float scale_qk, float dv, RowLayout lay, const SplitArgs& sp,
+                                         hipStream_t stream) {
+  const int nqb = (Nq + 31) / 32;
+  const dim3 grid((unsigned)(nqb * sp.nsplit * BH)), block(64);
+  hipLaunchKernelGGL((fwd_fp8_kernel<128, CAUSAL, 1, true>), grid, block, 0, stream, (const unsigned char*)q,
+                     (const unsigned char*)k, (const unsigned char*)v, nullptr, nullptr, BH, Nq, nqb, scale_qk,
+                     scale_qk * kLog2e, dv, lay, sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_split_fp8(const void* q, const void* k, const void* v, float* opart, float* lpart,
+                                int BH, int Nq, int Nk, bool causal, float scale, float dq, float dk, float dv,
+                                int nsplit, int span, RowLayout lay, hipStream_t stream) {
+  const SplitArgs sp{Nk, Nk - Nq, nsplit, span, opart, lpart};
+  const float scale_qk = scale * dq * dk;
+  return causal ? launch_fwd_split_fp8_t<true>(q, k, v, BH, Nq, scale_qk, dv, lay, sp, stream)
+                : launch_fwd_split_fp8_t<false>(q, k, v, BH, Nq, scale_qk, dv, lay, sp, stream);
 }
 
 }  // namespace fa

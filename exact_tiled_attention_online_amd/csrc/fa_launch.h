@@ -22,6 +22,16 @@ struct RowLayout {
 };
 
 
+// Arguments of the forward kernels' split-key-range mode (unused otherwise).
+struct SplitArgs {
+  int Nk;         // key/value rows per head
+  int off;        // causal offset: query row i sits at key position i + off (off = Nk - Nq)
+  int nsplit;     // key ranges per head
+  int span;       // keys per range, a multiple of the kernel's tile
+  float* opart;   // [nsplit][BH][N][D]: each range's O, normalised by its own l
+  float* lpart;   // [nsplit][BH][N]: each range's LSE, -inf where a row sees no key of it
+};
+
 // bf16 forward: O, LSE.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                            int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream);
@@ -40,6 +50,13 @@ constexpr int kSplitBC = 32;
 hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, float* opart, float* lpart,
                                  int BH, int Nq, int Nk, int d, bool causal, float scale, int nsplit,
                                  int span, RowLayout lay, hipStream_t stream);
+
+// The same for FP8 (e4m3fn) q, k, v with per-tensor descales, d = 128; ranges
+// are whole kSplitBC8-key tiles.
+constexpr int kSplitBC8 = 64;
+hipError_t launch_fwd_split_fp8(const void* q, const void* k, const void* v, float* opart, float* lpart,
+                                int BH, int Nq, int Nk, bool causal, float scale, float dq, float dk, float dv,
+                                int nsplit, int span, RowLayout lay, hipStream_t stream);
 
 // Combines the ranges of the split forward: O (bf16, layout lay) and LSE.
 hipError_t launch_fwd_merge(const float* opart, const float* lpart, void* o, float* lse, int BH, int Nq,

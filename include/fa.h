@@ -183,6 +183,21 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int Nq, int Nk, int d, int causal, float scale, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream, int dtype, int layout);
 
+/*
+ * The split-key-range forward with FP8 inputs: fa_fwd_splitkv's shapes,
+ * masks, ranges, workspace rules and results, with q, k, v given as e4m3fn
+ * codes and per-tensor descales as in fa_fwd_fp8 (decoding against an FP8
+ * key/value cache reads half the bytes of bf16).  Ranges are whole 64-key
+ * tiles; the workspace must hold fa_fwd_splitkv_fp8_workspace_bytes(...)
+ * bytes for the same num_splits.  Accuracy as fa_fwd_fp8.  Supported: d = 128
+ * only; other arguments and errors as for fa_fwd_splitkv and fa_fwd_fp8.
+ */
+size_t fa_fwd_splitkv_fp8_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Nq, int Nk, int d, int causal, float scale,
+                       float descale_q, float descale_k, float descale_v, int num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream, int layout);
+
 /* Static, human-readable text for a status code. */
 const char* fa_strerror(int status);
 

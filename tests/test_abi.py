@@ -206,3 +206,28 @@ def fwd8(**kw):
 ])
 def test_fp8_rejects(kw, status):
     assert fwd8(**kw) == status
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(Nq=0), -1), (dict(Nq=1001), -1), (dict(num_splits=-2), -1),
+    (dict(descale_v=0.0), -1), (dict(d=64), -2), (dict(layout=4), -1), (dict(workspace=None), -3),
+    (dict(workspace_bytes=64), -3),
+])
+def test_splitkv_fp8_rejects(kw, status):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=4, Nk=1000, d=128, causal=1, scale=0.125, descale_q=1.0,
+             descale_k=1.0, descale_v=1.0, num_splits=0, workspace=P, workspace_bytes=1 << 30, stream=None,
+             layout=fa.FA_LAYOUT_BHND)
+    a.update(kw)
+    assert fa.fa_fwd_splitkv_fp8(**a) == status
+
+
+@needs_lib
+def test_splitkv_fp8_workspace_uses_64_key_tiles():
+    tiles = -(-1000 // 64)
+    for ns in (1, 4, 9):
+        per = -(-tiles // ns)
+        used = -(-tiles // per)
+        r = lambda x: -(-x // 256) * 256
+        assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, 128, ns) == r(used * 8 * 128 * 4) + r(used * 8 * 4)
+    assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, 96, 0) == 0

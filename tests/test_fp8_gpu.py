@@ -99,3 +99,38 @@ def test_fp8_forward_full_size_sampled_heads():
         assert float(np.abs(got_l[0, h] - want["lse"]).max()) <= LSE_ATOL, h
     del q8, k8, v8, o, lse
     torch.cuda.empty_cache()
+
+
+SPLIT_CASES = [
+    # B, H, Nq, Nk, causal, num_splits
+    (2, 3, 1, 1000, True, 0),
+    (1, 4, 7, 513, False, 3),
+    (2, 2, 32, 4096, True, 0),
+    (1, 2, 33, 2000, True, 5),
+    (1, 2, 100, 100, True, 0),
+    (3, 2, 5, 31, False, 0),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,causal,ns", SPLIT_CASES)
+def test_fp8_split_forward_matches_oracle(B, H, Nq, Nk, causal, ns):
+    """The split-key-range FP8 forward (decode against an FP8 cache) meets the
+    same bound: each range's O is a convex combination with the bound above
+    (N = its keys), and the merge mixes them with weights summing to one."""
+    import torch
+    log(f"[fp8-split] B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} splits={ns}")
+    xq = gen.make_fp8_inputs((B, H, Nq, 128), seed=500 + Nq + Nk, sigma_qk=2.0)
+    xk = gen.make_fp8_inputs((B, H, Nk, 128), seed=600 + Nq + Nk, sigma_qk=2.0)
+    q8, k8, v8 = (torch.from_numpy(a).cuda() for a in (xq["q8"], xk["k8"], xk["v8"]))
+    scale = 1.0 / math.sqrt(128)
+    o, lse = fa.forward_splitkv_fp8(q8, k8, v8, xq["descale_q"], xk["descale_k"], xk["descale_v"], causal, scale,
+                                    num_splits=ns)
+    torch.cuda.synchronize()
+    got_o, got_l = to_np(o), to_np(lse)
+    ro, rl = ref.forward_rect(xq["q"], xk["k"], xk["v"], scale, causal)
+    for b in range(B):
+        for h in range(H):
+            vmax = float(np.abs(xk["v"][b, h]).max())
+            tol = (2.0 ** -4 + Nk * 2.0 ** -17) * vmax + 2.0 ** -9 * float(np.abs(ro[b, h]).max())
+            assert float(np.abs(got_o[b, h] - ro[b, h]).max()) <= tol, (b, h)
+            assert float(np.abs(got_l[b, h] - rl[b, h]).max()) <= LSE_ATOL, (b, h)
