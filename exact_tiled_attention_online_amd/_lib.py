@@ -19,7 +19,8 @@ FA_LAYOUT_BHND, FA_LAYOUT_BNHD = 0, 1
 
 EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_fwd_fp8", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv",
-           "fa_fwd_splitkv_fp8_workspace_bytes", "fa_fwd_splitkv_fp8", "fa_strerror")
+           "fa_fwd_splitkv_fp8_workspace_bytes", "fa_fwd_splitkv_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
+           "fa_strerror")
 
 _lib = None
 
@@ -62,6 +63,12 @@ def load():
     lib.fa_fwd_splitkv_fp8_workspace_bytes.restype = sz
     lib.fa_fwd_splitkv_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, f, i, vp, sz, vp, i]
     lib.fa_fwd_splitkv_fp8.restype = i
+    u64, u32 = ctypes.c_ulonglong, ctypes.c_uint
+    lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, u64, u32, vp, i]
+    lib.fa_fwd_dropout.restype = i
+    lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, u64, u32, vp, sz,
+                                   vp, i]
+    lib.fa_bwd_dropout.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -127,6 +134,17 @@ def fa_fwd_splitkv_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, descale_
     return load().fa_fwd_splitkv_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale),
                                      float(descale_q), float(descale_k), float(descale_v), num_splits, workspace,
                                      workspace_bytes, stream, layout)
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, causal, scale, drop_t, seed, offset, stream, layout) -> int:
+    return load().fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), int(drop_t), int(seed),
+                                 int(offset), stream, layout)
+
+
+def fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, drop_t, seed, offset, workspace,
+                   workspace_bytes, stream, layout) -> int:
+    return load().fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
+                                 int(drop_t), int(seed), int(offset), workspace, workspace_bytes, stream, layout)
 
 
 def fa_strerror(status: int) -> str:
@@ -280,3 +298,47 @@ def forward_splitkv_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_
     if st != FA_OK:
         raise FAError(st, "fa_fwd_splitkv_fp8")
     return o, l
+
+
+def drop_threshold(p: float) -> int:
+    """The integer threshold t of the dropout entry points for a drop
+    probability p: t = round(256 p), so that t / 256 is the probability
+    actually used (0 <= p < 255.5 / 256)."""
+    t = int(round(256.0 * float(p)))
+    if not 0 <= t <= 255:
+        raise ValueError(f"drop probability {p} outside [0, 255/256]")
+    return t
+
+
+def forward_dropout(q, k, v, causal: bool, scale: float, p_drop: float, seed: int, offset: int = 0, out=None,
+                    lse=None, stream=None, layout: int = FA_LAYOUT_BHND):
+    """O, LSE of attention with dropout (drop probability round(256 p)/256,
+    mask from (seed, offset)) on bf16 device tensors in the named layout."""
+    import torch
+    B, H, N, d = _dims(q, layout)
+    _check((q, k, v), q.shape)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, N, d, causal,
+                        scale, drop_threshold(p_drop), seed, offset, _stream(stream), layout)
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_dropout")
+    return o, l
+
+
+def backward_dropout(q, k, v, o, do, lse, causal: bool, scale: float, p_drop: float, seed: int, offset: int = 0,
+                     ws=None, grads=None, stream=None, layout: int = FA_LAYOUT_BHND):
+    """dQ, dK, dV for the O, LSE of forward_dropout with the same arguments."""
+    import torch
+    B, H, N, d = _dims(q, layout)
+    _check((q, k, v, o, do), q.shape)
+    if ws is None:
+        ws = workspace(q, layout)
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(q),
+                                                  torch.empty_like(q))
+    st = fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
+                        drop_threshold(p_drop), seed, offset, ws.data_ptr(), ws.numel(), _stream(stream), layout)
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_dropout")
+    return dq, dk, dv

@@ -226,6 +226,53 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                    layout);
 }
 
+namespace {
+fa::DropArgs drop_args(int drop_t, unsigned long long seed, unsigned offset) {
+  return fa::DropArgs{(unsigned)(seed & 0xFFFFFFFFull), (unsigned)(seed >> 32), offset, (unsigned)drop_t,
+                      256.f / (float)(256 - drop_t)};
+}
+}  // namespace
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   int causal, float scale, int drop_t, unsigned long long seed, unsigned offset, void* stream,
+                   int layout) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, causal, scale, FA_BF16, layout);
+  if (st != FA_OK) return st;
+  if (drop_t < 0 || drop_t > 255) return FA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  const fa::DropArgs dr = drop_args(drop_t, seed, offset);
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, row_layout(H, layout),
+                                        static_cast<hipStream_t>(stream), &dr));
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, int drop_t,
+                   unsigned long long seed, unsigned offset, void* workspace, size_t workspace_bytes,
+                   void* stream, int layout) {
+  // all checks first, so that a rejected call launches nothing
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, causal, scale, FA_BF16, layout);
+  if (st != FA_OK) return st;
+  if (drop_t < 0 || drop_t > 255) return FA_ERR_INVALID;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, FA_BF16)) return FA_ERR_WORKSPACE;
+  const Workspace w = carve(workspace, B, H, N, d, FA_BF16);
+  const fa::RowLayout lay = row_layout(H, layout);
+  const fa::DropArgs dr = drop_args(drop_t, seed, offset);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int r = hip_status(fa::launch_bwd_pre(o, dO, lse, w.ndrow, w.nlse, nullptr, B * H, N, d, scale, false, lay, s));
+  if (r != FA_OK) return r;
+  r = hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.nlse, w.ndrow, nullptr, dk, dv, B * H, N, d, causal != 0,
+                                     scale, false, lay, s, &dr));
+  if (r != FA_OK) return r;
+  return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.nlse, w.ndrow, dq, B * H, N, d, causal != 0, scale, lay, s,
+                                      &dr));
+}
+
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                int causal, float scale, float descale_q, float descale_k, float descale_v, void* stream,
                int layout) {

@@ -36,6 +36,7 @@
 // compiler then knows the prefetch cannot alias the reads).  LDS addresses are
 // a few per-lane bases plus compile-time offsets.
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -49,12 +50,17 @@ FA_DEV int ds_off(int row, int col) {
   return row * 128 + (slot << 3) + ((col & 3) << 1);
 }
 
-template <int D, bool CAUSAL, bool DQA>
-__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
-    float* __restrict__ dQacc, bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb,
-    float scale, float c, RowLayout lay) {
+// The kernel body, shared by the plain kernels and the dropout kernel (DROP:
+// with keep mask Z and keep scale s, dV = s (P^ o Z)^T dO and
+// dS = P^ o (s (dP~ - D) + (s - 1) D) where kept, P^ o (-D) where dropped,
+// dP~ - D being what the dP accumulator holds).
+template <int D, bool CAUSAL, bool DQA, bool DROP>
+FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                          const bf16* __restrict__ dO, const float* __restrict__ NLSE,
+                          const float* __restrict__ NDR, float* __restrict__ dQacc, bf16* __restrict__ dK,
+                          bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, RowLayout lay,
+                          DropArgs dr) {
+  static_assert(!(DQA && DROP), "the dropout backward takes dQ from the query-outer kernel");
   constexpr int BC = 128, BR = 64;
   // ROWB: LDS bytes per row (d * 2, or 256 for d = 96); CH: 16-byte chunks per row
   constexpr int ROWB = lds_pitch<D>(), CH = D / 8, KS = D / 16, DT = D / 32;
@@ -269,6 +275,18 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
         constexpr int DIST = FA_KV_DIST;   // slots between an LDS read and its use
         constexpr int NG = 4 * KS;                 // groups per step (KS = 2*DT)
         f32x16 s[2], dp[2];
+        // dropout: per query tile, the generator of this lane quad's 4x4 block
+        // in query group lane % 4 (its rounds run in the KS slots before the
+        // tile's elementwise phase), then the block's bytes turned so that
+        // word i holds this lane's key for query group i
+        Philox4 ph[2];
+        u32x4 dw[2];
+        if constexpr (DROP) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            ph[t] = Philox4{(uint32_t)kvrow >> 2, (uint32_t)(qb0 + 32 * t + 8 * (lane & 3) + 4 * h) >> 2,
+                            (uint32_t)head, dr.offset};
+        }
         bf16x8 qa[2][KS], ga[2][KS];               // S/dP operands (Q, dO rows)
         bf16x8 tq[2][2 * DT], tg[2][2 * DT];       // dV/dK operands (transposed)
         auto read_group = [&](int g) {
@@ -324,8 +342,16 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
               const bool dead = (q >= N) | (kvrow >= N) | (CAUSAL & (kvrow > q));
               p = dead ? 0.f : p;
             }
-            s[t][r] = p;
-            dp[t][r] = p * dp[t][r];
+            if constexpr (DROP) {
+              // -D of the register's query row, as the dP accumulator started
+              const float nd = Dt[32 * t + 8 * (r >> 2) + 4 * h + (r & 3)];
+              const bool keep = kept(dw[t][r >> 2], r & 3, dr.thresh);
+              s[t][r] = keep ? p : 0.f;
+              dp[t][r] = p * (keep ? fmaf(dr.keep_scale, dp[t][r], (1.f - dr.keep_scale) * nd) : nd);
+            } else {
+              s[t][r] = p;
+              dp[t][r] = p * dp[t][r];
+            }
           }
 #pragma unroll
           for (int hi = 0; hi < 2; ++hi) {
@@ -341,11 +367,22 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 #pragma unroll
         for (int g = 0; g < DIST; ++g) read_group(g);
         init_acc(1);
-#pragma unroll
+        // full unrolling is required (every register array index below is a
+        // compile-time constant); the dropout variant's body is past the size
+        // up to which a plain unroll pragma is honoured
+#pragma clang loop unroll(full)
         for (int g = 0; g < NG; ++g) {
           __builtin_amdgcn_sched_barrier(0);
           if (g + DIST < NG) read_group(g + DIST);
           products(g);
+          if constexpr (DROP) {
+            // tile t's rounds run in the KS slots before its elementwise phase
+            if (g < 2 * KS) {
+              const int t = g / KS, u = g % KS;
+              ph[t].rounds(10 * u / KS, 10 * (u + 1) / KS, dr.k0, dr.k1);
+              if (u == KS - 1) dw[t] = quad_transpose(byte_transpose(ph[t].words()), lane & 3);
+            }
+          }
           if (g >= KS && g < 2 * KS) elem_chunk(0, g - KS);
           if (g >= 2 * KS && g < 3 * KS) elem_chunk(1, g - 2 * KS);
         }
@@ -409,7 +446,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = 8 * (r >> 2) + 4 * h + (r & 3);
-            const float x = pass == 0 ? dk[dt][r] * scale : dv[dt][r];
+            const float x = pass == 0 ? dk[dt][r] * scale : (DROP ? dv[dt][r] * dr.keep_scale : dv[dt][r]);
             stg[row * D + 32 * dt + l32] = (bf16)x;
           }
         bf16* dst = (pass == 0 ? dK : dV) + hoff;
@@ -429,12 +466,40 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 }
 
 template <int D, bool CAUSAL, bool DQA>
+__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
+    float* __restrict__ dQacc, bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb,
+    float scale, float c, RowLayout lay) {
+  bwd_bf16_body<D, CAUSAL, DQA, false>(Q, K, V, dO, NLSE, NDR, dQacc, dK, dV, BH, N, nqb, scale, c, lay,
+                                       DropArgs{});
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_bf16_dropout_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, RowLayout lay,
+    DropArgs dr) {
+  bwd_bf16_body<D, CAUSAL, false, true>(Q, K, V, dO, NLSE, NDR, nullptr, dK, dV, BH, N, nqb, scale, c, lay, dr);
+}
+
+template <int D, bool CAUSAL, bool DQA>
 static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v, const void* dO,
                                     const float* nlse, const float* ndrow, float* dq_acc, void* dk,
-                                    void* dv, int BH, int N, float scale, RowLayout lay, hipStream_t stream) {
+                                    void* dv, int BH, int N, float scale, RowLayout lay, hipStream_t stream,
+                                    const DropArgs* drop) {
   const int nkb = (N + 127) / 128, nqb = (N + 63) / 64;
   const int items = CAUSAL ? (nkb + 1) / 2 : nkb;
   const dim3 grid((unsigned)(items * BH)), block(256);
+  if constexpr (!DQA) {
+    if (drop) {
+      hipLaunchKernelGGL((bwd_bf16_dropout_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH,
+                         N, nqb, scale, scale * kLog2e, lay, *drop);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, DQA>), grid, block, 0, stream, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, dq_acc, (bf16*)dk,
                      (bf16*)dv, BH, N, nqb, scale, scale * kLog2e, lay);
@@ -445,25 +510,27 @@ template <bool DQA>
 static hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void* dO,
                                 const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
                                 int BH, int N, int d, bool causal, float scale, RowLayout lay,
-                                hipStream_t stream) {
+                                hipStream_t stream, const DropArgs* drop) {
   if (d == 128)
-    return causal ? launch_bwd_bf16_t<128, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream)
-                  : launch_bwd_bf16_t<128, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream);
+    return causal ? launch_bwd_bf16_t<128, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop)
+                  : launch_bwd_bf16_t<128, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop);
   if constexpr (!DQA) {
     if (d == 96)
-      return causal ? launch_bwd_bf16_t<96, true, false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream)
-                    : launch_bwd_bf16_t<96, false, false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream);
+      return causal ? launch_bwd_bf16_t<96, true, false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop)
+                    : launch_bwd_bf16_t<96, false, false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop);
   }
-  return causal ? launch_bwd_bf16_t<64, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream)
-                : launch_bwd_bf16_t<64, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream);
+  return causal ? launch_bwd_bf16_t<64, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop)
+                : launch_bwd_bf16_t<64, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dO,
                            const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
                            int BH, int N, int d, bool causal, float scale, bool dq_atomic, RowLayout lay,
-                           hipStream_t stream) {
-  return dq_atomic ? launch_bwd_kv<true>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, d, causal, scale, lay, stream)
-                   : launch_bwd_kv<false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, d, causal, scale, lay, stream);
+                           hipStream_t stream, const DropArgs* drop) {
+  // the dropout backward has no atomic-dQ form (the caller never asks for it)
+  if (dq_atomic && drop) return hipErrorInvalidValue;
+  return dq_atomic ? launch_bwd_kv<true>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, d, causal, scale, lay, stream, nullptr)
+                   : launch_bwd_kv<false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, d, causal, scale, lay, stream, drop);
 }
 
 }  // namespace fa

@@ -20,6 +20,7 @@
 // sequence of slots separated by scheduling fences, with the LDS operands of
 // each slot read a few slots ahead.
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -27,11 +28,15 @@ namespace fa {
 #ifndef FA_DQ_NW
 #define FA_DQ_NW 8
 #endif
-template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
-    bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, RowLayout lay) {
+// The kernel body, shared by the plain kernel and the dropout kernel (DROP:
+// with keep mask Z and keep scale s, dP = s Z o (dO V^T), so that
+// dS = P^ o (s (dP~ - D) + (s - 1) D) where kept and P^ o (-D) where dropped,
+// dP~ - D being what the dP accumulator holds).
+template <int D, bool CAUSAL, int NW, bool DROP>
+FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                        const bf16* __restrict__ dO, const float* __restrict__ NLSE,
+                        const float* __restrict__ NDR, bf16* __restrict__ dQ, int BH, int N, int nqb,
+                        float scale, float c, RowLayout lay, DropArgs dr) {
   constexpr int BR = 32 * NW, BC = 64;
   constexpr int ROWB = lds_pitch<D>();   // LDS bytes per row (d * 2, or 256 for d = 96)
   constexpr int KS = D / 16;         // K-steps of the S and dP products
@@ -78,6 +83,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
   // -LSE * log2(e) and -D of this lane's query row
   const float nl2 = qrow < N ? NLSE[(size_t)head * N + qrow] * c : 0.f;
   const float ndrow = qrow < N ? NDR[(size_t)head * N + qrow] : 0.f;
+  // dropout: a kept dS is P^ (s acc + (1 - s) ndrow), with acc = dP~ + ndrow
+  const float kd = DROP ? (1.f - dr.keep_scale) * ndrow : 0.f;
 
   const int kv_end = CAUSAL ? min(N, qb * BR + BR) : N;
   const int ntiles = (kv_end + BC - 1) / BC;
@@ -133,6 +140,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
       };
       f32x16 s, dp;
       bf16x8 db[2];
+      // dropout: the generator of this lane quad's 4x4 block in key group
+      // lane % 4 of the current 32-key half; its rounds run in the half's
+      // S/dP slots
+      Philox4 ph;
 #pragma unroll
       for (int i = 0; i < DIST; ++i) read_slot(i);
 #pragma unroll
@@ -142,6 +153,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
         if (i + DIST < NSL) read_slot(i + DIST);
         if (k < KS) {
           if (k == 0) {
+            if constexpr (DROP)
+              ph = Philox4{(uint32_t)(kvb + 32 * mt + 8 * (lane & 3) + 4 * h) >> 2, (uint32_t)qrow >> 2,
+                           (uint32_t)head, dr.offset};
             s = f32x16{};
             // dP starts from -D of this lane's query row, so that the products
             // leave dP - D (every register of the lane belongs to that row)
@@ -150,6 +164,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
           }
           s = mfma32(ka[k], qf[k], s);
           dp = mfma32(va[k], gf[k], dp);
+          if constexpr (DROP) ph.rounds(10 * k / KS, 10 * (k + 1) / KS, dr.k0, dr.k1);
           if (k == KS - 1) {
             __builtin_amdgcn_sched_barrier(0);
             // register r: key kvb + 32*mt + 8*(r/4) + 4*h + r%4, query qrow.
@@ -162,10 +177,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
                 s[r] = dead ? -INFINITY : s[r];
               }
             }
+            if constexpr (DROP) {
+              const u32x4 w = quad_transpose(ph.words(), lane & 3);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float p = exp2_fast(fmaf(s[r], c, nl2));
-              dp[r] = p * dp[r];
+              for (int r = 0; r < 16; ++r) {
+                const float p = exp2_fast(fmaf(s[r], c, nl2));
+                dp[r] = p * (kept(w[r >> 2], r & 3, dr.thresh) ? fmaf(dr.keep_scale, dp[r], kd) : ndrow);
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const float p = exp2_fast(fmaf(s[r], c, nl2));
+                dp[r] = p * dp[r];
+              }
             }
             // dS^T as B operand; K-step st = 2*mt + half covers keys 16*st ..
             // 16*st+15 of the tile: registers 0..3 <- keys 16st+4h+jj, 4..7 <-
@@ -213,30 +237,51 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
     }
 }
 
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
+    bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, RowLayout lay) {
+  bwd_dq_body<D, CAUSAL, NW, false>(Q, K, V, dO, NLSE, NDR, dQ, BH, N, nqb, scale, c, lay, DropArgs{});
+}
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_dropout_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
+    bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, RowLayout lay, DropArgs dr) {
+  bwd_dq_body<D, CAUSAL, NW, true>(Q, K, V, dO, NLSE, NDR, dQ, BH, N, nqb, scale, c, lay, dr);
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_dq_t(const void* q, const void* k, const void* v, const void* dO,
                                   const float* nlse, const float* ndrow, void* dq, int BH, int N, float scale,
-                                  RowLayout lay, hipStream_t stream) {
+                                  RowLayout lay, hipStream_t stream, const DropArgs* drop) {
   constexpr int NW = FA_DQ_NW, BR = 32 * NW;
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
-                     (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e,
-                     lay);
+  if (drop)
+    hipLaunchKernelGGL((bwd_dq_dropout_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale,
+                       scale * kLog2e, lay, *drop);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e,
+                       lay);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                          const float* ndrow, void* dq, int BH, int N, int d, bool causal, float scale,
-                         RowLayout lay, hipStream_t stream) {
+                         RowLayout lay, hipStream_t stream, const DropArgs* drop) {
   if (d == 128)
-    return causal ? launch_bwd_dq_t<128, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream)
-                  : launch_bwd_dq_t<128, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream);
+    return causal ? launch_bwd_dq_t<128, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop)
+                  : launch_bwd_dq_t<128, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop);
   if (d == 96)
-    return causal ? launch_bwd_dq_t<96, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream)
-                  : launch_bwd_dq_t<96, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream);
-  return causal ? launch_bwd_dq_t<64, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream)
-                : launch_bwd_dq_t<64, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream);
+    return causal ? launch_bwd_dq_t<96, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop)
+                  : launch_bwd_dq_t<96, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop);
+  return causal ? launch_bwd_dq_t<64, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop)
+                : launch_bwd_dq_t<64, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop);
 }
 
 }  // namespace fa

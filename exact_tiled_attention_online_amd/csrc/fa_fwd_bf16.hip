@@ -32,6 +32,7 @@
 // kernel then combines the ranges with the rule for joining two partial
 // softmax results (page "flash-attention-v2-sram-tiling", quiz question 10).
 #include "fa_common.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -42,11 +43,14 @@ namespace fa {
 #ifndef FA_FWD_BC64
 #define FA_FWD_BC64 128
 #endif
-template <int D, bool CAUSAL, int NW, int BC, bool SPLIT>
-__global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c,
-    RowLayout lay, SplitArgs sp) {
+// The kernel body, shared by the plain kernel and the dropout kernel (DROP:
+// the probabilities that multiply V are those of the dropout forward; the
+// row sums, hence l and LSE, are those of all probabilities).
+template <int D, bool CAUSAL, int NW, int BC, bool SPLIT, bool DROP>
+FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                          bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale,
+                          float c, RowLayout lay, SplitArgs sp, DropArgs dr) {
+  static_assert(!(SPLIT && DROP), "dropout runs on the square training shape only");
   // BC: key rows per tile (128 where the registers allow it (d = 64), else 64;
   // 32 in the split mode, whose one-wave workgroups need little LDS)
   constexpr int BR = 32 * NW;
@@ -161,6 +165,16 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
       for (int mt = 0; mt < MT; ++mt) s[mt] = f32x16{};
       bf16x8 pb[BC / 16];
       const int kvb = (jlo + j) * BC;
+      // dropout: the generator for the 4x4 block of this lane's quad of query
+      // rows and key group (lane % 4) of each 32-key half; its rounds run in
+      // the S-product slots, which carry no other vector work
+      Philox4 ph[DROP ? MT : 1];
+      if constexpr (DROP) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          ph[mt] = Philox4{(uint32_t)(kvb + 32 * mt + 8 * (lane & 3) + 4 * h) >> 2, (uint32_t)qrow >> 2,
+                           (uint32_t)head, dr.offset};
+      }
 #pragma unroll
       for (int i = 0; i < DIST; ++i) read_slot(i);
 #pragma clang loop unroll(full)
@@ -170,6 +184,10 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
         if (i < KS) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) s[mt] = mfma32(ka[i][mt], qf[i], s[mt]);
+          if constexpr (DROP) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) ph[mt].rounds(10 * i / KS, 10 * (i + 1) / KS, dr.k0, dr.k1);
+          }
         } else {
           const int u = i - KS, st = u / DT, t = u % DT;
           oacc[t] = mfma32(vt[u], pb[st], oacc[t]);
@@ -247,6 +265,15 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
           }
         }
         l_run += rs;
+        if constexpr (DROP) {
+          // dropped probabilities leave the P V product (l keeps them)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const u32x4 w = quad_transpose(ph[mt].words(), lane & 3);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[mt][r] = kept(w[r >> 2], r & 3, dr.thresh) ? s[mt][r] : 0.f;
+          }
+        }
         // P^T as B operand, K-step st covers keys 16*st .. 16*st+15 of the
         // tile: registers 0..3 <- keys 16st+4h+jj, 4..7 <- keys 16st+8+4h+jj
 #pragma unroll
@@ -296,7 +323,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
     return;
   }
   if (qrow < N) {
-    const float inv = 1.f / l_tot;
+    const float inv = (DROP ? dr.keep_scale : 1.f) / l_tot;
     bf16* Orow = O + hoff + (size_t)qrow * RS;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
@@ -313,28 +340,51 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
   }
 }
 
+template <int D, bool CAUSAL, int NW, int BC, bool SPLIT>
+__global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c,
+    RowLayout lay, SplitArgs sp) {
+  fwd_bf16_body<D, CAUSAL, NW, BC, SPLIT, false>(Q, K, V, O, LSE, BH, N, nqb, scale, c, lay, sp, DropArgs{});
+}
+
+template <int D, bool CAUSAL, int NW, int BC>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_dropout_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c,
+    RowLayout lay, DropArgs dr) {
+  fwd_bf16_body<D, CAUSAL, NW, BC, false, true>(Q, K, V, O, LSE, BH, N, nqb, scale, c, lay, SplitArgs{}, dr);
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                                    int BH, int N, float scale, RowLayout lay, hipStream_t stream) {
+                                    int BH, int N, float scale, RowLayout lay, hipStream_t stream,
+                                    const DropArgs* drop) {
   constexpr int NW = FA_FWD_NW, BR = 32 * NW, BC = D == 64 ? FA_FWD_BC64 : 64;
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, false>), grid, block, 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
-                     scale * kLog2e, lay, SplitArgs{});
+  if (drop)
+    hipLaunchKernelGGL((fwd_bf16_dropout_kernel<D, CAUSAL, NW, BC>), grid, block, 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
+                       scale * kLog2e, lay, *drop);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, false>), grid, block, 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
+                       scale * kLog2e, lay, SplitArgs{});
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                           int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream) {
+                           int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream,
+                           const DropArgs* drop) {
   if (d == 128)
-    return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
-                  : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
+    return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream, drop)
+                  : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream, drop);
   if (d == 96)
-    return causal ? launch_fwd_bf16_t<96, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
-                  : launch_fwd_bf16_t<96, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
-  return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
-                : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
+    return causal ? launch_fwd_bf16_t<96, true>(q, k, v, o, lse, BH, N, scale, lay, stream, drop)
+                  : launch_fwd_bf16_t<96, false>(q, k, v, o, lse, BH, N, scale, lay, stream, drop);
+  return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, lay, stream, drop)
+                : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, lay, stream, drop);
 }
 
 // Split mode: one-wave workgroups of 32 query rows, 32-key tiles (16 KB of

@@ -32,9 +32,22 @@ struct SplitArgs {
   float* lpart;   // [nsplit][BH][N]: each range's LSE, -inf where a row sees no key of it
 };
 
-// bf16 forward: O, LSE.
+// Attention dropout (inverted, on the normalised probabilities): score
+// (query i, key j) of head bh is kept iff byte j%4 of word i%4 of
+// Philox4x32-10(counter (j/4, i/4, bh, offset), key (k0, k1)) is >= thresh;
+// kept probabilities are multiplied by keep_scale = 256 / (256 - thresh).
+struct DropArgs {
+  unsigned k0, k1;    // Philox key: the seed's low and high 32 bits
+  unsigned offset;    // counter word 3
+  unsigned thresh;    // t in 0..255: drop probability t / 256
+  float keep_scale;   // 256 / (256 - t)
+};
+
+// bf16 forward: O, LSE; with `drop`, O uses the dropped probabilities (LSE
+// does not change).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                           int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream);
+                           int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream,
+                           const DropArgs* drop = nullptr);
 
 // FP8 (e4m3fn) forward, d = 128: O (bf16) and LSE for Q = dq * Q8, K = dk * K8,
 // V = dv * V8.
@@ -69,16 +82,18 @@ hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float
                           hipStream_t stream);
 
 // bf16 key/value-block-outer backward: dK, dV written; with dq_atomic, dQ is
-// also accumulated (fp32, unscaled dS K) into dq_acc with atomics.
+// also accumulated (fp32, unscaled dS K) into dq_acc with atomics.  With
+// `drop` (only without dq_atomic), the gradients of the dropout forward.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dO,
                            const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
                            int BH, int N, int d, bool causal, float scale, bool dq_atomic, RowLayout lay,
-                           hipStream_t stream);
+                           hipStream_t stream, const DropArgs* drop = nullptr);
 
-// bf16 query-block-outer dQ kernel: dQ = bf16(scale * dS K), no atomics.
+// bf16 query-block-outer dQ kernel: dQ = bf16(scale * dS K), no atomics;
+// with `drop`, the dQ of the dropout forward.
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                          const float* ndrow, void* dq, int BH, int N, int d, bool causal, float scale,
-                         RowLayout lay, hipStream_t stream);
+                         RowLayout lay, hipStream_t stream, const DropArgs* drop = nullptr);
 
 // dQ = bf16(scale * dq_acc); dq_acc is contiguous [B*H][N][d], dq in layout lay.
 hipError_t launch_dq_convert(const float* dq_acc, void* dq, int BH, int N, int d, float scale, RowLayout lay,

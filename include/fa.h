@@ -127,6 +127,48 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const
               void* workspace, size_t workspace_bytes, void* stream, int dtype, int layout);
 
 /*
+ * Forward and backward with dropout on the attention probabilities (page
+ * "blog.xiaohack.org/tag/flops", section 7, lists dropout inside the fused
+ * softmax step; the pages define it no further).  Inverted dropout of the
+ * normalised probabilities:
+ *   P = softmax(scale * Q K^T [+ causal mask]), LSE as for fa_fwd (unchanged),
+ *   O = (256 / (256 - drop_t)) * (P o Z) V,
+ * with Z_ij = 1 (kept) or 0 (dropped).  A score is dropped with probability
+ * drop_t / 256; drop_t is an integer in 0 .. 255 (0 keeps everything and
+ * gives fa_fwd's O).
+ *
+ * Z is not stored: every kernel regenerates it from the counter-based
+ * generator Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011).  For head
+ * bh = b * H + h, query i and key j: the 4x4 block (i / 4, j / 4) is one call
+ * with counter (j / 4, i / 4, bh, offset) and key (seed mod 2^32,
+ * seed / 2^32); Z_ij = 1 iff byte j % 4 (bits 8(j%4) .. 8(j%4)+7) of output
+ * word i % 4 is >= drop_t.  The same (seed, offset) reproduces the same mask;
+ * callers change offset (or seed) between independent uses.
+ *
+ * fa_bwd_dropout takes the O and LSE fa_fwd_dropout wrote with the same
+ * q, k, v, causal, scale, drop_t, seed and offset, and writes dq, dk, dv of
+ * the loss sum(dO o O) for that mask:
+ *   D_i = sum_c dO_ic O_ic,  dP = (256 / (256 - drop_t)) * Z o (dO V^T),
+ *   dS = P o (dP - D 1^T),  dV = (256 / (256 - drop_t)) (P o Z)^T dO,
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * bf16 only (no dtype argument); d in {64, 96, 128}.  B, H, N, causal,
+ * scale, layout, pointers, alignment, ownership, streams and errors are those
+ * of fa_fwd and fa_bwd; the workspace is fa_bwd's
+ * (fa_bwd_workspace_bytes(B, H, N, d, FA_BF16)).  drop_t outside 0 .. 255 is
+ * FA_ERR_INVALID.  dQ always comes from the query-outer kernel (FA_DQ_MODE is
+ * ignored).
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale,
+                   int drop_t, unsigned long long seed, unsigned offset, void* stream, int layout);
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, int causal, float scale,
+                   int drop_t, unsigned long long seed, unsigned offset,
+                   void* workspace, size_t workspace_bytes, void* stream, int layout);
+
+/*
  * Forward with FP8 inputs: q, k, v hold OCP e4m3fn codes (1 byte per
  * element: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
  * infinities; largest finite 448) in the layout named by `layout`, standing

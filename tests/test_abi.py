@@ -44,13 +44,14 @@ def header_signatures():
 def _ctype_of(c_type):
     if "*" in c_type:
         return ctypes.c_void_p
-    return {"int": ctypes.c_int, "float": ctypes.c_float, "size_t": ctypes.c_size_t}[c_type]
+    return {"int": ctypes.c_int, "float": ctypes.c_float, "size_t": ctypes.c_size_t,
+            "unsigned": ctypes.c_uint, "unsigned long long": ctypes.c_ulonglong}[c_type]
 
 
 @needs_lib
 def test_binding_argtypes_match_header():
     """Every ctypes prototype in the binding has the header's parameter count
-    and kinds (pointer, int, float, size_t), so a change of the C signature
+    and kinds (pointer, int, unsigned, unsigned long long, float, size_t), so a change of the C signature
     cannot be marshalled wrongly."""
     lib = _lib.load()
     sigs = header_signatures()
@@ -231,3 +232,40 @@ def test_splitkv_fp8_workspace_uses_64_key_tiles():
         r = lambda x: -(-x // 256) * 256
         assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, 128, ns) == r(used * 8 * 128 * 4) + r(used * 8 * 4)
     assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, 96, 0) == 0
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(N=0), -1), (dict(causal=2), -1), (dict(scale=-1.0), -1),
+    (dict(drop_t=-1), -1), (dict(drop_t=256), -1), (dict(layout=3), -1), (dict(d=80), -2), (dict(v=P + 8), -1),
+])
+def test_fwd_dropout_rejects(kw, status):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=64, d=128, causal=1, scale=0.125, drop_t=26, seed=7,
+             offset=0, stream=None, layout=fa.FA_LAYOUT_BHND)
+    a.update(kw)
+    assert fa.fa_fwd_dropout(**a) == status
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(dO=None), -1), (dict(dk=None), -1), (dict(H=0), -1), (dict(drop_t=300), -1), (dict(d=32), -2),
+    (dict(workspace=None), -3), (dict(workspace_bytes=1024), -3), (dict(workspace=P + 16), -3),
+    (dict(lse=P + 2), -1),
+])
+def test_bwd_dropout_rejects(kw, status):
+    a = dict(q=P, k=P, v=P, o=P, dO=P, lse=P, dq=P, dk=P, dv=P, B=1, H=2, N=64, d=128, causal=1, scale=0.125,
+             drop_t=26, seed=(1 << 63) + 5, offset=3, workspace=P,
+             workspace_bytes=fa.fa_bwd_workspace_bytes(1, 2, 64, 128, fa.FA_BF16), stream=None,
+             layout=fa.FA_LAYOUT_BHND)
+    a.update(kw)
+    assert fa.fa_bwd_dropout(**a) == status
+
+
+def test_drop_threshold_rounds_to_256ths():
+    assert fa.drop_threshold(0.0) == 0
+    assert fa.drop_threshold(0.1) == 26
+    assert fa.drop_threshold(0.25) == 64
+    assert fa.drop_threshold(255 / 256) == 255
+    for bad in (-0.01, 0.999, 1.0):
+        with pytest.raises(ValueError):
+            fa.drop_threshold(bad)
