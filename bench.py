@@ -392,6 +392,82 @@ def fp8_measurement(fa, gen, torch, dev, stream, w, with_oracle, reps=30, oracle
     return res
 
 
+DROP_T = 26   # drop probability 26/256 (about 0.1) for the dropout measurement
+
+
+def dropout_measurement(fa, torch, stream, w, q, k, v, do, ws, plain_fwd_ms, plain_bwd_ms, with_oracle, x=None,
+                        reps=20):
+    """Attention with dropout (fa_fwd_dropout, fa_bwd_dropout) on the
+    headline tensors: per-call times from HIP events on the launch stream,
+    credited FLOPs as for the plain step (dropout adds no products), the
+    forward kernel against the dense bf16 peak, the cost over the plain path,
+    and, unless disabled, the first 1024 query rows of head (0, 0) against the
+    dropout oracle (O, LSE)."""
+    import numpy as np
+    B, H, N, d = w.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    sp = stream.cuda_stream
+    seed, offset = 0x5EED0123456789AB, 3
+    P = lambda t: t.data_ptr()
+
+    def fwd():
+        st = fa.fa_fwd_dropout(P(q), P(k), P(v), P(o), P(lse), B, H, N, d, w.causal, w.scale, DROP_T, seed, offset,
+                               sp, fa.FA_LAYOUT_BHND)
+        if st != 0:
+            raise fa.FAError(st, "fa_fwd_dropout")
+
+    def bwd():
+        st = fa.fa_bwd_dropout(P(q), P(k), P(v), P(o), P(do), P(lse), P(dq), P(dk), P(dv), B, H, N, d, w.causal,
+                               w.scale, DROP_T, seed, offset, P(ws), ws.numel(), sp, fa.FA_LAYOUT_BHND)
+        if st != 0:
+            raise fa.FAError(st, "fa_bwd_dropout")
+
+    for _ in range(5):
+        fwd()
+        bwd()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+    fwd_fl, bwd_fl = w.flops()
+    fwd_tf = fwd_fl / (fwd_ms * 1e-3) / 1e12
+    res = {"workload": w.name + "_dropout", "drop_t": DROP_T, "drop_probability": DROP_T / 256,
+           "generator": "Philox4x32-10, one call per 4x4 block", "fwd_ms": round(fwd_ms, 4),
+           "bwd_ms": round(bwd_ms, 4), "step_ms": round(fwd_ms + bwd_ms, 4), "reps": reps,
+           "tflops": round((fwd_fl + bwd_fl) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 3),
+           "fwd_over_plain": round(fwd_ms / plain_fwd_ms, 3), "bwd_over_plain": round(bwd_ms / plain_bwd_ms, 3),
+           "roofline": {"kernel": "fwd_bf16_dropout_kernel", "bound": "mfma", "achieved": round(fwd_tf, 3),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None}}
+    if with_oracle and x is not None:
+        from oracle import dropout as drop
+        from oracle import ref
+        rows = min(N, 1024)
+        q0, k0, v0 = (np.asarray(x[n][0, 0], dtype=np.float64) for n in ("q", "k", "v"))
+        keep = drop.keep_mask(0, seed, offset, DROP_T, N, N, row0=0, rows=rows)
+        s = ref.scores(q0[:rows], k0, w.scale, w.causal, row0=0)
+        p, _, want_l = ref.softmax_rows(s)
+        want_o = drop.keep_scale(DROP_T) * np.where(keep, p, 0.0) @ v0
+        got_o = o[0, 0, :rows].float().cpu().numpy()
+        got_l = lse[0, 0, :rows].cpu().numpy()
+        e_o = float(np.abs(got_o - want_o).max()) / (2e-2 * max(1e-2, float(np.abs(want_o).max())))
+        e_l = float(np.abs(got_l - want_l).max()) / 1e-3
+        res["oracle_check"] = {"rows": f"head (0,0), query rows 0..{rows - 1}",
+                               "max_err_over_tolerance": {"o": round(e_o, 4), "lse": round(e_l, 4)},
+                               "within_tolerance": e_o <= 1.0 and e_l <= 1.0}
+    del o, lse, dq, dk, dv
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +477,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 forward on the headline shape (reported under detail)")
+    ap.add_argument("--no-dropout", action="store_true",
+                    help="skip the dropout forward and backward on the headline shape (reported under detail)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the split-key-range forward on the decode workload (reported under detail)")
     ap.add_argument("--flush-mib", type=int, default=0,
@@ -584,6 +662,9 @@ def main():
             "peak_from_cus_at_2p4ghz": round(props.multi_processor_count * 4096 * 2.4e9 / 1e12, 1),
         },
     }
+    if not args.no_dropout and dtype == torch.bfloat16:
+        out["detail"]["dropout"] = dropout_measurement(fa, torch, stream, w, q, k, v, do, ws, fwd_ms, bwd_ms,
+                                                       not args.no_cpu_baseline, x)
     if not args.no_fp8 and B == 1 and d == 128:
         out["detail"]["fp8_forward"] = fp8_measurement(fa, gen, torch, dev, stream, w, not args.no_cpu_baseline)
     if not args.no_decode:

@@ -31,6 +31,18 @@
 
 namespace fa {
 
+// 32 x 32 -> 64-bit product with one v_mad_u64_u32.  Written as a plain
+// 64-bit multiply, the compiler splits about half of the products into a
+// v_mul_hi_u32 / v_mul_lo_u32 pair, two quarter-rate instructions instead of
+// one (the forward with dropout measured 689 -> 659 us at the causal
+// 1 x 32 x 8192 x 128 shape).  The carry-out the instruction also writes is
+// discarded.
+FA_DEV uint64_t mul_wide(uint32_t a, uint32_t m) {
+  uint64_t p, carry;
+  asm("v_mad_u64_u32 %0, %1, %2, %3, 0" : "=v"(p), "=s"(carry) : "v"(a), "s"(m));
+  return p;
+}
+
 // Philox4x32 state: four counter words.
 struct Philox4 {
   uint32_t x0, x1, x2, x3;
@@ -41,8 +53,8 @@ struct Philox4 {
     for (int r = r0; r < r1; ++r) {
       const uint32_t rk0 = k0 + (uint32_t)r * 0x9E3779B9u;
       const uint32_t rk1 = k1 + (uint32_t)r * 0xBB67AE85u;
-      const uint64_t p0 = (uint64_t)x0 * 0xD2511F53u;
-      const uint64_t p1 = (uint64_t)x2 * 0xCD9E8D57u;
+      const uint64_t p0 = mul_wide(x0, 0xD2511F53u);
+      const uint64_t p1 = mul_wide(x2, 0xCD9E8D57u);
       const uint32_t n0 = (uint32_t)(p1 >> 32) ^ x1 ^ rk0;
       const uint32_t n2 = (uint32_t)(p0 >> 32) ^ x3 ^ rk1;
       x1 = (uint32_t)p1;
