@@ -94,3 +94,40 @@ def test_captured_splitkv_replays_bitwise():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(o, want_o) and torch.equal(lse, want_l), rep
+
+
+def test_captured_dropout_step_replays_bitwise():
+    """The dropout forward + backward regenerate their mask from (seed,
+    offset) in every kernel and keep no state between calls, so a captured
+    step replays to the same bits; a step captured with another offset gives
+    another mask."""
+    import torch
+    B, H, N, d = 1, 4, 777, 128
+    scale = 1.0 / math.sqrt(d)
+    log(f"[graph] dropout fwd+bwd B={B} H={H} N={N} d={d}")
+    t = _step_tensors(B, H, N, d, seed=21)
+
+    def enqueue(offset):
+        fa.forward_dropout(t["q"], t["k"], t["v"], True, scale, 0.125, 77, offset, out=t["o"], lse=t["lse"])
+        fa.backward_dropout(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], True, scale, 0.125, 77, offset,
+                            ws=t["ws"], grads=(t["dq"], t["dk"], t["dv"]))
+
+    enqueue(5)
+    torch.cuda.synchronize()
+    want = _snapshot(t)
+    enqueue(6)
+    torch.cuda.synchronize()
+    other = _snapshot(t)
+    assert not torch.equal(other["o"], want["o"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        enqueue(5)
+    for rep in range(3):
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            t[n].fill_(float("nan"))
+        t["ws"].fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, ref in want.items():
+            assert torch.equal(t[n], ref), (rep, n)
