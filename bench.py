@@ -82,6 +82,39 @@ def _headline_instance(name, short):
     return short in head and not (short == "fwd_bf16_kernel" and head.endswith("true>"))
 
 
+def summarize_busy(csv_path, last):
+    """Clock and matrix-pipe use per kernel from one rocprofv3 run with
+    --kernel-trace --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES: per
+    dispatch, GRBM_GUI_ACTIVE (summed over the 8 XCDs) / 8 over the duration
+    is the shader clock, and SQ_VALU_MFMA_BUSY_CYCLES over that many cycles
+    of every SIMD (4 per CU) is the fraction of cycles the matrix pipes are
+    busy.  Averages over the last `last` dispatches of each kernel."""
+    import collections
+    import csv
+    rows = collections.defaultdict(dict)
+    for r in csv.DictReader(open(csv_path)):
+        d = rows[int(r["Dispatch_Id"])]
+        d["name"] = r["Kernel_Name"]
+        d["dur"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    per = collections.defaultdict(list)
+    for _, d in sorted(rows.items()):
+        if "GRBM_GUI_ACTIVE" not in d or "SQ_VALU_MFMA_BUSY_CYCLES" not in d or d["dur"] <= 0:
+            continue
+        cycles = d["GRBM_GUI_ACTIVE"] / 8
+        ghz = cycles / d["dur"]
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * 256 * 4) if cycles else 0.0
+        per[_short_name(d["name"])].append((d["dur"] / 1000.0, ghz, busy))
+    print("| kernel | dispatches | avg us | clock GHz | MFMA busy (of cycles) | busy x GHz |")
+    print("|---|---|---|---|---|---|")
+    for name, v in sorted(per.items(), key=lambda kv: -sum(x[0] for x in kv[1][-last:])):
+        v = v[-last:]
+        us, ghz, busy = (sum(x[i] for x in v) / len(v) for i in range(3))
+        if us < 100 or busy == 0.0:   # short or MFMA-free launches: the clock estimate is not meaningful
+            continue
+        print(f"| `{name}` | {len(v)} | {us:.1f} | {ghz:.2f} | {busy:.3f} | {busy * ghz:.2f} |")
+
+
 def summarize_counters(fetch_csv, write_csv, copy_mib, out_json):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE, with --copy-probe-mib) into HBM bytes per launch per kernel.
@@ -125,6 +158,15 @@ def summarize_counters(fetch_csv, write_csv, copy_mib, out_json):
     print("\n".join(rows))
 
 
+def _short_name(name):
+    """A traced kernel name without its argument list (torch kernels by their
+    function name)."""
+    short = name.split("(")[0].replace("void ", "")
+    if "at::native" in short:
+        short = "torch " + short.split("::")[2].split("<")[0]
+    return short[:70]
+
+
 def summarize_trace(trace_csv, last):
     """Markdown table of kernel durations (us) from a rocprofv3 kernel trace:
     all launches, and the last `last` launches of each kernel, which are the
@@ -139,10 +181,7 @@ def summarize_trace(trace_csv, last):
     for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
         ds = [d for _, d in sorted(v)]
         tail = ds[-last:]
-        short = name.split("(")[0].replace("void ", "")
-        if "at::native" in short:
-            short = "torch " + short.split("::")[2].split("<")[0]
-        print(f"| `{short[:70]}` | {len(ds)} | {sum(ds) / len(ds):.1f} | {sum(tail) / len(tail):.1f} | "
+        print(f"| `{_short_name(name)}` | {len(ds)} | {sum(ds) / len(ds):.1f} | {sum(tail) / len(tail):.1f} | "
               f"{min(ds):.1f} | {max(ds):.1f} |")
 
 
@@ -490,10 +529,16 @@ def main():
                          "(the calibration kernel for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB"),
                     help="write profiles/counters_c4.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-busy", nargs=2, metavar=("PMC_CSV", "LAST"),
+                    help="print per-kernel clock and MFMA-busy fraction from a rocprofv3 --kernel-trace --pmc "
+                         "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES run and exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "LAST"),
                     help="print per-kernel durations from a rocprofv3 --kernel-trace CSV: over all "
                          "launches and over the last LAST launches (the timed steps) and exit")
     args = ap.parse_args()
+    if args.summarize_busy:
+        summarize_busy(args.summarize_busy[0], int(args.summarize_busy[1]))
+        return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], int(args.summarize_trace[1]))
         return 0
