@@ -269,3 +269,15 @@ def test_drop_threshold_rounds_to_256ths():
     for bad in (-0.01, 0.999, 1.0):
         with pytest.raises(ValueError):
             fa.drop_threshold(bad)
+
+
+@needs_lib
+def test_tensors_of_2_pow_31_elements_are_unsupported():
+    """The kernels index a tensor's elements within 31 bits per call; the
+    largest accepted shape is tested on the GPU (63 x 32 x 8192 x 128)."""
+    big = dict(q=P, k=P, v=P, o=P, lse=P, B=64, H=32, N=8192, d=128, causal=1, scale=0.125, stream=None,
+               dtype=fa.FA_BF16, layout=fa.FA_LAYOUT_BHND)
+    assert fa.fa_fwd(**big) == -2
+    assert fa.fa_fwd(**dict(big, B=1, H=1, N=1 << 24)) == -2   # one head of 2^24 rows x 128
+    assert fa.fa_fwd_dropout(q=P, k=P, v=P, o=P, lse=P, B=64, H=32, N=8192, d=128, causal=1, scale=0.125, drop_t=0,
+                             seed=0, offset=0, stream=None, layout=fa.FA_LAYOUT_BHND) == -2

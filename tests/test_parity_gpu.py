@@ -315,3 +315,33 @@ def test_head_dim_96_atomic_mode_falls_back(monkeypatch):
     b = run_gpu(x, "bf16", True, 0.1)
     for n in ("o", "lse", "dq", "dk", "dv"):
         assert np.array_equal(a[n], b[n]), n
+
+
+def test_maximum_size_sampled_heads():
+    """The largest shape the library takes with the headline geometry: B=63,
+    H=32, N=8192, d=128 causal, 2.11e9 elements per tensor (the ABI limit is
+    2^31), so every per-head base and row offset runs through the 64-bit
+    address arithmetic.  Inputs come from a seeded device generator; three
+    whole heads (the first, one in the middle, the last) go to the oracle with
+    the exact bf16 values the kernels saw."""
+    import torch
+    B, H, N, d = 63, 32, 8192, 128
+    assert B * H * N * d < 2 ** 31 and 64 * H * N * d >= 2 ** 31
+    log(f"[max size] B={B} H={H} N={N} d={d} causal, {B * H * N * d:.3e} elements per tensor")
+    scale = 1.0 / math.sqrt(d)
+    g = torch.Generator(device="cuda").manual_seed(63)
+    q, k, v, do = (torch.randn((B, H, N, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(4))
+    o, lse = fa.forward(q, k, v, True, scale)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, True, scale)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (31, 17), (B - 1, H - 1)):
+        x = {n: t[b, h].float().cpu().numpy().astype(np.float64)[None, None] for n, t in
+             (("q", q), ("k", k), ("v", v), ("do", do))}
+        want = oracle_heads(x, True, scale, heads=[(0, 0)])[(0, 0)]
+        got = {"o": to_np(o[b, h]), "lse": to_np(lse[b, h]), "dq": to_np(dq[b, h]), "dk": to_np(dk[b, h]),
+               "dv": to_np(dv[b, h])}
+        errs = compare(got, want, "bf16", where=f"max size head ({b},{h})")
+        log(f"  head ({b},{h}) max errors {errs}")
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
