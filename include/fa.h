@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID = -1,      /* null pointer, non-positive size, bad flag, bad scale */
-  FA_ERR_UNSUPPORTED = -2,  /* head dim or dtype this build has no kernel for */
+  FA_ERR_UNSUPPORTED = -2,  /* head dim or dtype the library has no kernel for */
   FA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
   FA_ERR_HIP = -4           /* the HIP runtime reported a launch error */
 } fa_status;

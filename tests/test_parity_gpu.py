@@ -105,7 +105,7 @@ def test_full_size_sampled_heads(big_runs, key):
 
 @pytest.mark.parametrize("key", ["c3", "c4", "c5"])
 def test_full_size_invariants(big_runs, key):
-    """Sum_j dK_j = 0, Sum_j dV_j = Sum_i dO_i, O inside the box spanned by V,
+    """Sum_j dK_j = 0, Sum_j dV_j = Sum_i dO_i, O within the per-column range of V,
     on every head (consequences of sum_j dS_ij = 0 and of stochastic rows)."""
     w, x, res = big_runs(key)
     log(f"[invariants] {w.name}")
