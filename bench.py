@@ -39,7 +39,7 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters_c4.json")
 # sources each timed kernel is built from (a counter record is valid only for these)
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["fa_fwd_bf16.hip", "fa_common.h", "fa_dropout.h"],
-    "bwd_bf16_kernel": ["fa_bwd_bf16.hip", "fa_common.h", "fa_dropout.h"],
+    "bwd_bf16_kernel": ["fa_bwd_bf16.hip", "fa_bwd_kv_body.h", "fa_common.h", "fa_dropout.h"],
     "bwd_dq_kernel": ["fa_bwd_dq.hip", "fa_common.h", "fa_dropout.h"],
     "bwd_pre_kernel": ["fa_aux.hip", "fa_common.h"],
 }

@@ -27,7 +27,8 @@ int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype, 
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID;
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
-  if (d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
+  // d = 256: bf16 only (the fp32 kernels hold a row of q and o per lane pair)
+  if (d != 64 && d != 96 && d != 128 && !(d == 256 && dtype == FA_BF16)) return FA_ERR_UNSUPPORTED;
   const long long elems = (long long)B * H * N * d;
   if (elems >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
@@ -64,10 +65,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 // dQ path of the bf16 backward: the query-block-outer kernel (default), or
 // fp32 atomics from the key/value-outer kernel when FA_DQ_MODE=atomic (d = 64
-// and 128 only; d = 96 always takes the default).
+// and 128 only; d = 96 and 256 always take the default).
 bool dq_atomic_mode(int d) {
   const char* m = std::getenv("FA_DQ_MODE");
-  return d != 96 && m && std::strcmp(m, "atomic") == 0;
+  return (d == 64 || d == 128) && m && std::strcmp(m, "atomic") == 0;
 }
 
 bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d, int dtype) {
@@ -117,7 +118,7 @@ int check_split(int B, int H, int Nq, int Nk, int d, int causal, float scale, in
   if (st != FA_OK) return st;
   st = check_shape(B, H, Nk, d, causal, scale, dtype, layout);
   if (st != FA_OK) return st;
-  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 || d == 256) return FA_ERR_UNSUPPORTED;
   if (causal && Nq > Nk) return FA_ERR_INVALID;
   if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID;
   return FA_OK;
@@ -143,7 +144,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
-  if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 96 && d != 128) || (dtype != FA_BF16 && dtype != FA_FP32))
+  if (B < 1 || H < 1 || N < 1 || (dtype != FA_BF16 && dtype != FA_FP32) ||
+      (d != 64 && d != 96 && d != 128 && !(d == 256 && dtype == FA_BF16)))
     return 0;
   return carve(nullptr, B, H, N, d, dtype).bytes;
 }
@@ -240,6 +242,7 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
   const int st = check_shape(B, H, N, d, causal, scale, FA_BF16, layout);
   if (st != FA_OK) return st;
   if (drop_t < 0 || drop_t > 255) return FA_ERR_INVALID;
+  if (d == 256) return FA_ERR_UNSUPPORTED;   // no dropout kernels at d = 256
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
   const fa::DropArgs dr = drop_args(drop_t, seed, offset);
@@ -256,6 +259,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   const int st = check_shape(B, H, N, d, causal, scale, FA_BF16, layout);
   if (st != FA_OK) return st;
   if (drop_t < 0 || drop_t > 255) return FA_ERR_INVALID;
+  if (d == 256) return FA_ERR_UNSUPPORTED;   // no dropout kernels at d = 256
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;

@@ -8,8 +8,8 @@
 // S - LSE/scale and dP - D.  Also the clear of the fp32 dQ accumulator (a fill
 // kernel, so the whole backward can be captured in a graph).
 // Each row of d elements is read by d/8 lanes with 16-byte (bf16) or 32-byte
-// (fp32) loads (in a group of 8 or 16 lanes), reduced across the group with
-// xor-shuffles.
+// (fp32) loads (in a group of 8, 16 or 32 lanes), reduced across the group
+// with xor-shuffles.
 //
 // dq_convert: dQ = bf16(scale * acc), 8 elements per thread, 16-byte stores.
 //
@@ -29,7 +29,7 @@ namespace fa {
 // cross-lane sums use xor-shuffles within that group)
 template <int D>
 constexpr int lanes_per_row() {
-  return D / 8 <= 8 ? 8 : 16;
+  return D / 8 <= 8 ? 8 : (D / 8 <= 16 ? 16 : 32);
 }
 
 template <int D, typename T>
@@ -98,6 +98,7 @@ hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float
   } else {
     if (d == 128) go(IC<128>{}, IC<0>{});
     else if (d == 96) go(IC<96>{}, IC<0>{});
+    else if (d == 256) go(IC<256>{}, IC<0>{});
     else go(IC<64>{}, IC<0>{});
   }
   return hipGetLastError();

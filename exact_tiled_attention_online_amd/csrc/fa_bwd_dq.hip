@@ -2,8 +2,8 @@
 //
 // dQ_i = scale * sum_j dS_ij K_j (page "flash-attention-backpropagation"
 // (aiqz.cc), section QKV梯度), computed without atomics: one workgroup
-// (8 waves, two per SIMD) owns BR = 256 query rows of one (batch, head), each
-// wave 32 of them, with the wave's Q and dO rows in registers and dQ accumulated in
+// (8 waves, two per SIMD; d = 256: 4 waves, one per SIMD) owns BR = 256 (128)
+// query rows of one (batch, head), each wave 32 of them, with the wave's Q and dO rows in registers and dQ accumulated in
 // registers, and walks the key/value tiles of BC = 64 rows (double-buffered
 // through LDS).  Per tile and wave:
 //   S^T  = K_j Q_w^T           MFMA, A = K rows (LDS), B = Q_w (registers)
@@ -146,7 +146,10 @@ FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, 
       Philox4 ph;
 #pragma unroll
       for (int i = 0; i < DIST; ++i) read_slot(i);
-#pragma unroll
+      // full unrolling is required (every register array index below is a
+      // compile-time constant); at d = 256 the body is past the size up to
+      // which a plain unroll pragma is honoured
+#pragma clang loop unroll(full)
       for (int i = 0; i < NSL; ++i) {
         const int mt = i / SPM, k = i % SPM;
         __builtin_amdgcn_sched_barrier(0);
@@ -237,8 +240,15 @@ FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, 
     }
 }
 
+// waves per SIMD the kernel is built for: at d = 256 the wave's Q and dO rows
+// and its dQ accumulator alone take 256 registers
+template <int D, int NW>
+constexpr int dq_min_blocks() {
+  return D > 128 ? 4 / NW : 8 / NW;
+}
+
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
+__global__ __launch_bounds__(64 * NW, (dq_min_blocks<D, NW>())) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
     bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, RowLayout lay) {
@@ -246,7 +256,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_kernel(
 }
 
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void bwd_dq_dropout_kernel(
+__global__ __launch_bounds__(64 * NW, (dq_min_blocks<D, NW>())) void bwd_dq_dropout_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
     bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, RowLayout lay, DropArgs dr) {
@@ -257,17 +267,20 @@ template <int D, bool CAUSAL>
 static hipError_t launch_bwd_dq_t(const void* q, const void* k, const void* v, const void* dO,
                                   const float* nlse, const float* ndrow, void* dq, int BH, int N, float scale,
                                   RowLayout lay, hipStream_t stream, const DropArgs* drop) {
-  constexpr int NW = FA_DQ_NW, BR = 32 * NW;
+  constexpr int NW = D == 256 ? 4 : FA_DQ_NW, BR = 32 * NW;   // d = 256: one wave per SIMD
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
-  if (drop)
-    hipLaunchKernelGGL((bwd_dq_dropout_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale,
-                       scale * kLog2e, lay, *drop);
-  else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e,
-                       lay);
+  if constexpr (D != 256) {   // no dropout form at d = 256
+    if (drop) {
+      hipLaunchKernelGGL((bwd_dq_dropout_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb,
+                         scale, scale * kLog2e, lay, *drop);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
+                     (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e,
+                     lay);
   return hipGetLastError();
 }
 
@@ -277,6 +290,9 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   if (d == 128)
     return causal ? launch_bwd_dq_t<128, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop)
                   : launch_bwd_dq_t<128, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop);
+  if (d == 256)
+    return causal ? launch_bwd_dq_t<256, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop)
+                  : launch_bwd_dq_t<256, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop);
   if (d == 96)
     return causal ? launch_bwd_dq_t<96, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop)
                   : launch_bwd_dq_t<96, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop);

@@ -1,0 +1,20 @@
+// fa_bwd_kv256.hip -- the key/value-block-outer backward (dK, dV) at d = 256.
+// The kernel body is fa_bwd_kv_body.h's; this file exists so that the build
+// can compile it without VGPR-form MFMA results (-amdgpu-mfma-vgpr-form): at
+// d = 256 a wave holds K and V rows, half of dK and dV, and the S and dP tiles
+// (about 490 registers), and with that option the compiler's AGPR-rewrite
+// pass fails on it, while without it the kernel fits without spills.
+#include "fa_bwd_kv_body.h"
+
+namespace fa {
+
+hipError_t launch_bwd_kv256(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
+                            const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
+                            RowLayout lay, hipStream_t stream) {
+  return causal ? launch_bwd_bf16_t<256, true, false>(q, k, v, dO, nlse, ndrow, nullptr, dk, dv, BH, N, scale, lay,
+                                                      stream, nullptr)
+                : launch_bwd_bf16_t<256, false, false>(q, k, v, dO, nlse, ndrow, nullptr, dk, dv, BH, N, scale, lay,
+                                                       stream, nullptr);
+}
+
+}  // namespace fa

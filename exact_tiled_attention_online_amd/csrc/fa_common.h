@@ -63,17 +63,19 @@ FA_DEV float half_sum(float x) {
 // The LDS of gfx950 serves 256 bytes per clock as 64 four-byte banks: a
 // 16-byte read (ds_read_b128) is served 16 lanes at a time, an 8-byte
 // transposing read 32 lanes at a time (measured with the bank-conflict
-// counter).  A tile of rows of ROWB bytes (ROWB = 256 or 128) is stored as
+// counter).  A tile of rows of ROWB bytes (ROWB = 128, 256 or 512) is stored as
 // 16-byte chunks, chunk c of row r at chunk position c ^ swz(r):
 //   ROWB = 256: swz(r) = 4*(r%4) + (r/4)%4
 //   ROWB = 128: swz(r) = 4*((r/2)%2) + (r/4)%4
 // so that both the operand reads (16 consecutive rows at one chunk) and the
 // transposing reads (4 consecutive rows, first a multiple of 4, times 4
 // consecutive chunks, first a multiple of 4) touch 16 distinct 16-byte bank
-// groups.  swz(r) depends on r % 16 only.
+// groups.  swz(r) depends on r % 16 only.  512-byte rows (d = 256) take the
+// 256-byte swizzle: it leaves bit 4 of the chunk index alone, so chunks
+// 16..31 sit 256 bytes after chunks 0..15 in the same bank groups.
 template <int ROWB>
 FA_DEV int swz(int r) {
-  if constexpr (ROWB == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  if constexpr (ROWB >= 256) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
@@ -124,25 +126,30 @@ template <int ROWB>
 struct TileBases {
   static constexpr int KS = ROWB / 32;   // 16-wide K-steps per row
   static constexpr int DT = ROWB / 64;   // 32-column groups per row
+  // Chunks 16 and up sit 256 bytes after chunks 0..15 (the swizzle only
+  // touches the low 4 bits of the chunk index), so 512-byte rows need no more
+  // bases than 256-byte ones: KSB, DTB bases plus compile-time offsets.
+  static constexpr int KSB = KS < 8 ? KS : 8;
+  static constexpr int DTB = DT < 4 ? DT : 4;
   // natural operand (lane = row 32*t + l32, registers = 8 elements of chunk
-  // 2*ks + h):  off(t, ks) = nat[ks] + 32*t*ROWB
-  int nat[KS];
+  // 2*ks + h):  off(t, ks) = nat[ks % KSB] + 256*(ks / KSB) + 32*t*ROWB
+  int nat[KSB];
   // transposed operand (lane = column 32*t + 16*(g%2) + s, registers = rows
   // k0..k0+3 and k0+8..k0+11 with k0 = 16*st + 4*h):
-  // off(st, t, hi) = tr[t][hi] + 16*st*ROWB
-  int tr[DT][2];
+  // off(st, t, hi) = tr[t % DTB][hi] + 256*(t / DTB) + 16*st*ROWB
+  int tr[DTB][2];
   FA_DEV TileBases(int lane) {
     const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, s16 = lane & 15;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) nat[ks] = tile_off<ROWB>(l32, 2 * ks + h);
+    for (int ks = 0; ks < KSB; ++ks) nat[ks] = tile_off<ROWB>(l32, 2 * ks + h);
 #pragma unroll
-    for (int t = 0; t < DT; ++t)
+    for (int t = 0; t < DTB; ++t)
 #pragma unroll
       for (int hi = 0; hi < 2; ++hi)
         tr[t][hi] = tile_off_elem<ROWB>(4 * h + (s16 >> 2) + 8 * hi, 32 * t + 16 * (g & 1) + 4 * (s16 & 3));
   }
-  FA_DEV int nat_off(int t, int ks) const { return nat[ks] + 32 * t * ROWB; }
-  FA_DEV int tr_off(int st, int t, int hi) const { return tr[t][hi] + 16 * st * ROWB; }
+  FA_DEV int nat_off(int t, int ks) const { return nat[ks % KSB] + 256 * (ks / KSB) + 32 * t * ROWB; }
+  FA_DEV int tr_off(int st, int t, int hi) const { return tr[t % DTB][hi] + 256 * (t / DTB) + 16 * st * ROWB; }
 };
 
 template <int B>
@@ -168,11 +175,11 @@ FA_DEV void dma4_buf(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, vo
 }
 
 // LDS row pitch (bytes) of a tile of D-wide bf16 rows.  The swizzles above
-// cover 128- and 256-byte rows; the 192-byte rows of d = 96 sit in 256-byte
-// slots, whose chunks 12..15 hold no data (and are never read).
+// cover 128-, 256- and 512-byte rows; the 192-byte rows of d = 96 sit in
+// 256-byte slots, whose chunks 12..15 hold no data (and are never read).
 template <int D>
 constexpr int lds_pitch() {
-  return D * 2 <= 128 ? 128 : 256;
+  return D * 2 <= 128 ? 128 : (D * 2 <= 256 ? 256 : 512);
 }
 
 // Fetch ROWS rows (VC 16-byte chunks each in global memory, rsb bytes apart)

@@ -1,8 +1,10 @@
 // fa_fwd_bf16.hip -- forward kernel, bf16 inputs/outputs, fp32 accumulation.
 //
 // One workgroup (8 waves, one workgroup per CU, two waves per SIMD) owns
-// BR = 256 query rows of one (batch, head); each wave owns 32 of them.
-// Key/value tiles of BC rows (64 for d = 128 and 96, 128 for d = 64) stream through
+// BR = 256 query rows of one (batch, head); each wave owns 32 of them (d = 256:
+// 4 waves, 128 rows, one wave per SIMD).
+// Key/value tiles of BC rows (64 for d = 128 and 96, 128 for d = 64, 32 for
+// d = 256) stream through
 // two LDS buffers (the next tile is fetched while the current one is used).
 // Per tile and wave:
 //   S^T = K_j Q_w^T            v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
@@ -340,8 +342,15 @@ FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
   }
 }
 
+// waves per SIMD the kernel is built for: d = 256 needs more than half the
+// register file per wave (Q rows and the O accumulator alone take 192)
+template <int D, int NW, bool SPLIT>
+constexpr int fwd_min_blocks() {
+  return SPLIT ? 2 : (D > 128 ? 4 / NW : 8 / NW);
+}
+
 template <int D, bool CAUSAL, int NW, int BC, bool SPLIT>
-__global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * NW, (fwd_min_blocks<D, NW, SPLIT>())) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c,
     RowLayout lay, SplitArgs sp) {
@@ -349,7 +358,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 8 / NW) void fwd_bf16_kernel(
 }
 
 template <int D, bool CAUSAL, int NW, int BC>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_dropout_kernel(
+__global__ __launch_bounds__(64 * NW, (fwd_min_blocks<D, NW, false>())) void fwd_bf16_dropout_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c,
     RowLayout lay, DropArgs dr) {
@@ -360,17 +369,22 @@ template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse,
                                     int BH, int N, float scale, RowLayout lay, hipStream_t stream,
                                     const DropArgs* drop) {
-  constexpr int NW = FA_FWD_NW, BR = 32 * NW, BC = D == 64 ? FA_FWD_BC64 : 64;
+  // d = 256: 4-wave workgroups (one wave per SIMD) and 32-key tiles
+  constexpr int NW = D == 256 ? 4 : FA_FWD_NW, BR = 32 * NW;
+  constexpr int BC = D == 64 ? FA_FWD_BC64 : (D == 256 ? 32 : 64);
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
-  if (drop)
-    hipLaunchKernelGGL((fwd_bf16_dropout_kernel<D, CAUSAL, NW, BC>), grid, block, 0, stream,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
-                       scale * kLog2e, lay, *drop);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, false>), grid, block, 0, stream,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
-                       scale * kLog2e, lay, SplitArgs{});
+  if constexpr (D != 256) {   // no dropout form at d = 256
+    if (drop) {
+      hipLaunchKernelGGL((fwd_bf16_dropout_kernel<D, CAUSAL, NW, BC>), grid, block, 0, stream,
+                         (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
+                         scale * kLog2e, lay, *drop);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, false>), grid, block, 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
+                     scale * kLog2e, lay, SplitArgs{});
   return hipGetLastError();
 }
 
@@ -380,6 +394,9 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   if (d == 128)
     return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream, drop)
                   : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream, drop);
+  if (d == 256)
+    return causal ? launch_fwd_bf16_t<256, true>(q, k, v, o, lse, BH, N, scale, lay, stream, drop)
+                  : launch_fwd_bf16_t<256, false>(q, k, v, o, lse, BH, N, scale, lay, stream, drop);
   if (d == 96)
     return causal ? launch_fwd_bf16_t<96, true>(q, k, v, o, lse, BH, N, scale, lay, stream, drop)
                   : launch_fwd_bf16_t<96, false>(q, k, v, o, lse, BH, N, scale, lay, stream, drop);

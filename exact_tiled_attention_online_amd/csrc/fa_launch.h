@@ -89,6 +89,12 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            int BH, int N, int d, bool causal, float scale, bool dq_atomic, RowLayout lay,
                            hipStream_t stream, const DropArgs* drop = nullptr);
 
+// The same at d = 256 (no atomic-dQ or dropout form), from its own
+// translation unit.
+hipError_t launch_bwd_kv256(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
+                            const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
+                            RowLayout lay, hipStream_t stream);
+
 // bf16 query-block-outer dQ kernel: dQ = bf16(scale * dS K), no atomics;
 // with `drop`, the dQ of the dropout forward.
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* nlse,

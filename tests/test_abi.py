@@ -119,7 +119,8 @@ def bwd(**kw):
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
     (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1), (dict(causal=2), -1),
     (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1), (dict(scale=0.0), -1),
-    (dict(scale=-0.1), -1), (dict(d=80), -2), (dict(d=256), -2), (dict(dtype=7), -2),
+    (dict(scale=-0.1), -1), (dict(d=80), -2), (dict(d=512), -2), (dict(d=256, dtype=fa.FA_FP32), -2),
+    (dict(dtype=7), -2),
     (dict(q=P + 8), -1), (dict(lse=P + 2), -1),
     (dict(B=1024, H=1024, N=4096, d=128), -2),
     (dict(layout=2), -1), (dict(layout=-1), -1),
@@ -281,3 +282,22 @@ def test_tensors_of_2_pow_31_elements_are_unsupported():
     assert fa.fa_fwd(**dict(big, B=1, H=1, N=1 << 24)) == -2   # one head of 2^24 rows x 128
     assert fa.fa_fwd_dropout(q=P, k=P, v=P, o=P, lse=P, B=64, H=32, N=8192, d=128, causal=1, scale=0.125, drop_t=0,
                              seed=0, offset=0, stream=None, layout=fa.FA_LAYOUT_BHND) == -2
+
+
+@needs_lib
+def test_head_dim_256_is_bf16_fwd_bwd_only():
+    """d = 256 exists for the bf16 forward and backward; the fp32 path, the
+    split-key-range and FP8 forwards and dropout have no d = 256 kernels."""
+    base = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=64, d=256, causal=1, scale=0.0625, stream=None,
+                layout=fa.FA_LAYOUT_BHND)
+    assert fa.fa_fwd(**base, dtype=fa.FA_FP32) == -2
+    assert fa.fa_fwd(**dict(base, q=None), dtype=fa.FA_BF16) == -1   # d = 256 bf16 passes the shape check
+    assert fa.fa_bwd_workspace_bytes(1, 2, 64, 256, fa.FA_BF16) > 0
+    assert fa.fa_bwd_workspace_bytes(1, 2, 64, 256, fa.FA_FP32) == 0
+    assert fa.fa_fwd_dropout(**base, drop_t=26, seed=1, offset=0) == -2
+    assert fa.fa_fwd_fp8(**base, descale_q=1.0, descale_k=1.0, descale_v=1.0) == -2
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 64, 256, 0) == 0
+    sk = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=4, Nk=64, d=256, causal=1, scale=0.0625, num_splits=0,
+              workspace=P, workspace_bytes=1 << 20, stream=None, dtype=fa.FA_BF16, layout=fa.FA_LAYOUT_BHND)
+    assert fa.fa_fwd_splitkv(**sk) == -2
+

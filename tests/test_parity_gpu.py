@@ -36,6 +36,8 @@ EDGE = [(dtype, d, causal, n)
         for d in (64, 96, 128)
         for causal in (False, True)
         for n in (1, 17, 64, 129, 300)]
+# head dim 256: bf16 only
+EDGE += [("bf16", 256, causal, n) for causal in (False, True) for n in (1, 17, 64, 129, 300)]
 
 
 @pytest.mark.parametrize("dtype,d,causal,n", EDGE)
@@ -345,3 +347,28 @@ def test_maximum_size_sampled_heads():
         log(f"  head ({b},{h}) max errors {errs}")
     del q, k, v, do, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_256_bnhd_layout(causal):
+    log(f"[d256 bnhd] causal={causal}")
+    w = gen.workload("c2")
+    x = gen.make_inputs(w, shape=(2, 3, 333, 256), seed=256)
+    _full_compare(x, "bf16", causal, 1.0 / 16.0, f"d256 bnhd c{int(causal)}", layout=fa.FA_LAYOUT_BNHD)
+
+
+def test_head_dim_256_larger_size_sampled_heads():
+    """d = 256 with several query blocks and key tiles per head and many
+    workgroups: causal 1 x 16 x 4096 x 256, two whole heads."""
+    import torch
+    w = gen.workload("c3")
+    log("[d256 large] 1x16x4096x256 causal")
+    x = gen.make_inputs(w, shape=(1, 16, 4096, 256), seed=2561)
+    res = run_gpu(x, "bf16", True, 1.0 / 16.0)
+    want = oracle_heads(x, True, 1.0 / 16.0, heads=[(0, 0), (0, 15)])
+    for (b, h), wv in want.items():
+        errs = compare({n: res[n][b, h] for n in wv}, wv, "bf16", where=f"d256 large head ({b},{h})")
+        log(f"  head ({b},{h}) max errors {errs}")
+    del res
+    torch.cuda.empty_cache()
+
