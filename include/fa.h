@@ -26,8 +26,10 @@
  * scale * q_i . k_j.  The causal mask keeps key j for query i iff j <= i
  * (queries and keys share the index range 0..N-1).
  *
- * Supported: d in {64, 96, 128}; N >= 1 (any N, tails are masked); B, H >= 1 with
- * B*H*N*d < 2^31; scale finite and > 0; causal in {0, 1}.
+ * Supported: d in {64, 96, 128}, and d = 256 for bf16 (fa_fwd, fa_bwd and its
+ * stages; other d, and fp32 at d = 256, are FA_ERR_UNSUPPORTED); N >= 1 (any
+ * N, tails are masked); B, H >= 1 with B*H*N*d < 2^31; scale finite and > 0;
+ * causal in {0, 1}.
  *
  * Ownership: every pointer is a device pointer owned by the caller.  The
  * library allocates and frees nothing and never synchronises; each call only
