@@ -76,10 +76,13 @@ def _read_counter_csv(path):
 
 def _headline_instance(name, short):
     """Whether a traced kernel name is `short`'s instantiation on the timed
-    path: the forward's last template argument selects its split mode, which
-    is a different launch."""
+    path (d = 128): the forward's last template argument selects its split
+    mode, which is a different launch, and other head dims are other
+    instantiations (mangled names carry the head dim as ILi128E)."""
     head = name.split("(")[0].strip()
-    return short in head and not (short == "fwd_bf16_kernel" and head.endswith("true>"))
+    if short not in head or not (f"{short}<128," in head or "ILi128E" in head):
+        return False
+    return not (short == "fwd_bf16_kernel" and head.endswith("true>"))
 
 
 def summarize_busy(csv_path, last):
@@ -431,6 +434,82 @@ def fp8_measurement(fa, gen, torch, dev, stream, w, with_oracle, reps=30, oracle
     return res
 
 
+def head_dim_256_measurement(fa, torch, stream, with_oracle, reps=10):
+    """Head dim 256 at the headline's credited FLOPs: causal 1 x 16 x 8192 x
+    256, bf16 (inputs from a seeded device generator).  Per-stage times from
+    HIP events on the launch stream, credited TFLOP/s, the dominant kernel
+    against the dense bf16 peak (its algorithmic FLOPs: 4 products of
+    2*B*H*N^2*d/2 for dK/dV, 3 for dQ, 2 for the forward) and, unless
+    disabled, 256 query rows of head (0, 0) (O, LSE) against the oracle."""
+    import numpy as np
+    B, H, N, d = 1, 16, 8192, 256
+    scale = 1.0 / 16.0
+    g = torch.Generator(device=stream.device).manual_seed(256)
+    q, k, v, do = (torch.randn((B, H, N, d), generator=g, device=stream.device).to(torch.bfloat16) for _ in range(4))
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ws = fa.workspace(q)
+    sp = stream.cuda_stream
+    P = lambda t: t.data_ptr()
+    lay = fa.FA_LAYOUT_BHND
+
+    def step(ev=None):
+        calls = [
+            lambda: fa.fa_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, N, d, True, scale, sp, fa.FA_BF16, lay),
+            lambda: fa.fa_bwd_preprocess(P(o), P(do), P(lse), B, H, N, d, scale, P(ws), ws.numel(), sp, fa.FA_BF16,
+                                         lay),
+            lambda: fa.fa_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, N, d, True, scale, P(ws),
+                                   ws.numel(), sp, fa.FA_BF16, lay),
+            lambda: fa.fa_bwd_dq(P(q), P(k), P(v), P(do), P(lse), P(dq), B, H, N, d, True, scale, P(ws), ws.numel(),
+                                 sp, fa.FA_BF16, lay),
+        ]
+        for i, c in enumerate(calls):
+            if ev is not None:
+                ev[i].record(stream)
+            st = c()
+            if st != 0:
+                raise fa.FAError(st, "head dim 256 step")
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(3):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    avg = lambda a, b: sum(e[a].elapsed_time(e[b]) for e in evs) / reps
+    fwd_ms, pre_ms, kv_ms, dq_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    unit = 2 * B * H * N * N * d / 2    # one causal N x N x d product
+    fwd_fl, bwd_fl = 2 * unit, 5 * unit
+    kernels = {"fwd_bf16_kernel": (fwd_ms, 2 * unit), "bwd_bf16_kernel": (kv_ms, 4 * unit),
+               "bwd_dq_kernel": (dq_ms, 3 * unit)}
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    tf = kernels[dom][1] / (kernels[dom][0] * 1e-3) / 1e12
+    res = {"workload": "bf16_b1h16_n8192_d256_causal", "fwd_ms": round(fwd_ms, 4),
+           "bwd_ms": round(pre_ms + kv_ms + dq_ms, 4), "bwd_dkdv_ms": round(kv_ms, 4), "bwd_dq_ms": round(dq_ms, 4),
+           "tflops": round((fwd_fl + bwd_fl) / ((fwd_ms + pre_ms + kv_ms + dq_ms) * 1e-3) / 1e12, 3),
+           "kernel_tflops": {n: round(f / (t * 1e-3) / 1e12, 3) for n, (t, f) in kernels.items()},
+           "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+    if with_oracle:
+        from oracle import ref
+        rows = 256
+        q0, k0, v0 = (t[0, 0].float().cpu().numpy().astype(np.float64) for t in (q, k, v))
+        p, _, want_l = ref.softmax_rows(ref.scores(q0[:rows], k0, scale, True))
+        want_o = p @ v0
+        e_o = float(np.abs(o[0, 0, :rows].float().cpu().numpy() - want_o).max()) / (
+            2e-2 * max(1e-2, float(np.abs(want_o).max())))
+        e_l = float(np.abs(lse[0, 0, :rows].cpu().numpy() - want_l).max()) / 1e-3
+        res["oracle_check"] = {"rows": f"head (0,0), query rows 0..{rows - 1}",
+                               "max_err_over_tolerance": {"o": round(e_o, 4), "lse": round(e_l, 4)},
+                               "within_tolerance": e_o <= 1.0 and e_l <= 1.0}
+    del q, k, v, do, o, dq, dk, dv, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 DROP_T = 26   # drop probability 26/256 (about 0.1) for the dropout measurement
 
 
@@ -516,6 +595,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 forward on the headline shape (reported under detail)")
+    ap.add_argument("--no-d256", action="store_true",
+                    help="skip the head dim 256 step (1 x 16 x 8192 x 256, reported under detail)")
     ap.add_argument("--no-dropout", action="store_true",
                     help="skip the dropout forward and backward on the headline shape (reported under detail)")
     ap.add_argument("--no-decode", action="store_true",
@@ -710,6 +791,8 @@ def main():
     if not args.no_dropout and dtype == torch.bfloat16:
         out["detail"]["dropout"] = dropout_measurement(fa, torch, stream, w, q, k, v, do, ws, fwd_ms, bwd_ms,
                                                        not args.no_cpu_baseline, x)
+    if not args.no_d256 and dtype == torch.bfloat16:
+        out["detail"]["head_dim_256"] = head_dim_256_measurement(fa, torch, stream, not args.no_cpu_baseline)
     if not args.no_fp8 and B == 1 and d == 128:
         out["detail"]["fp8_forward"] = fp8_measurement(fa, gen, torch, dev, stream, w, not args.no_cpu_baseline)
     if not args.no_decode:
