@@ -242,7 +242,6 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
   const int st = check_shape(B, H, N, d, causal, scale, FA_BF16, layout);
   if (st != FA_OK) return st;
   if (drop_t < 0 || drop_t > 255) return FA_ERR_INVALID;
-  if (d == 256) return FA_ERR_UNSUPPORTED;   // no dropout kernels at d = 256
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
   const fa::DropArgs dr = drop_args(drop_t, seed, offset);
@@ -259,7 +258,6 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   const int st = check_shape(B, H, N, d, causal, scale, FA_BF16, layout);
   if (st != FA_OK) return st;
   if (drop_t < 0 || drop_t > 255) return FA_ERR_INVALID;
-  if (d == 256) return FA_ERR_UNSUPPORTED;   // no dropout kernels at d = 256
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;

@@ -17,7 +17,7 @@ static hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, con
     if (d == 96)
       return causal ? launch_bwd_bf16_t<96, true, false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop)
                     : launch_bwd_bf16_t<96, false, false>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop);
-    if (d == 256) return launch_bwd_kv256(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, causal, scale, lay, stream);
+    if (d == 256) return launch_bwd_kv256(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, causal, scale, lay, stream, drop);
   }
   return causal ? launch_bwd_bf16_t<64, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop)
                 : launch_bwd_bf16_t<64, false, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop);

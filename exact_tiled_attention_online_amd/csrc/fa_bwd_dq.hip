@@ -270,13 +270,11 @@ static hipError_t launch_bwd_dq_t(const void* q, const void* k, const void* v, c
   constexpr int NW = D == 256 ? 4 : FA_DQ_NW, BR = 32 * NW;   // d = 256: one wave per SIMD
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
-  if constexpr (D != 256) {   // no dropout form at d = 256
-    if (drop) {
-      hipLaunchKernelGGL((bwd_dq_dropout_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb,
-                         scale, scale * kLog2e, lay, *drop);
-      return hipGetLastError();
-    }
+  if (drop) {
+    hipLaunchKernelGGL((bwd_dq_dropout_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb,
+                       scale, scale * kLog2e, lay, *drop);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
                      (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e,

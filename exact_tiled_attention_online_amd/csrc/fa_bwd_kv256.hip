@@ -1,4 +1,5 @@
-// fa_bwd_kv256.hip -- the key/value-block-outer backward (dK, dV) at d = 256.
+// fa_bwd_kv256.hip -- the key/value-block-outer backward (dK, dV) at d = 256,
+// plain and with dropout.
 // The kernel body is fa_bwd_kv_body.h's; this file exists so that the build
 // can compile it without VGPR-form MFMA results (-amdgpu-mfma-vgpr-form): at
 // d = 256 a wave holds K and V rows, half of dK and dV, and the S and dP tiles
@@ -10,11 +11,11 @@ namespace fa {
 
 hipError_t launch_bwd_kv256(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                             const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
-                            RowLayout lay, hipStream_t stream) {
+                            RowLayout lay, hipStream_t stream, const DropArgs* drop) {
   return causal ? launch_bwd_bf16_t<256, true, false>(q, k, v, dO, nlse, ndrow, nullptr, dk, dv, BH, N, scale, lay,
-                                                      stream, nullptr)
+                                                      stream, drop)
                 : launch_bwd_bf16_t<256, false, false>(q, k, v, dO, nlse, ndrow, nullptr, dk, dv, BH, N, scale, lay,
-                                                       stream, nullptr);
+                                                       stream, drop);
 }
 
 }  // namespace fa

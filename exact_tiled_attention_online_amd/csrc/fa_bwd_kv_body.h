@@ -512,7 +512,7 @@ static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v,
   const int nkb = (N + BC - 1) / BC, nqb = (N + 63) / 64;
   const int items = CAUSAL ? (nkb + 1) / 2 : nkb;
   const dim3 grid((unsigned)(items * BH)), block(256);
-  if constexpr (!DQA && D != 256) {   // no dropout form at d = 256
+  if constexpr (!DQA) {
     if (drop) {
       hipLaunchKernelGGL((bwd_bf16_dropout_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q,
                          (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH,

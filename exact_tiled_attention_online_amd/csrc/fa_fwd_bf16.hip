@@ -374,13 +374,11 @@ static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v,
   constexpr int BC = D == 64 ? FA_FWD_BC64 : (D == 256 ? 32 : 64);
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
-  if constexpr (D != 256) {   // no dropout form at d = 256
-    if (drop) {
-      hipLaunchKernelGGL((fwd_bf16_dropout_kernel<D, CAUSAL, NW, BC>), grid, block, 0, stream,
-                         (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
-                         scale * kLog2e, lay, *drop);
-      return hipGetLastError();
-    }
+  if (drop) {
+    hipLaunchKernelGGL((fwd_bf16_dropout_kernel<D, CAUSAL, NW, BC>), grid, block, 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,
+                       scale * kLog2e, lay, *drop);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, NW, BC, false>), grid, block, 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, BH, N, nqb, scale,

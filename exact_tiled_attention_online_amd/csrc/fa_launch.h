@@ -93,7 +93,7 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
 // translation unit.
 hipError_t launch_bwd_kv256(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                             const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
-                            RowLayout lay, hipStream_t stream);
+                            RowLayout lay, hipStream_t stream, const DropArgs* drop = nullptr);
 
 // bf16 query-block-outer dQ kernel: dQ = bf16(scale * dS K), no atomics;
 // with `drop`, the dQ of the dropout forward.

@@ -27,7 +27,8 @@
  * (queries and keys share the index range 0..N-1).
  *
  * Supported: d in {64, 96, 128}, and d = 256 for bf16 (fa_fwd, fa_bwd and its
- * stages; other d, and fp32 at d = 256, are FA_ERR_UNSUPPORTED); N >= 1 (any
+ * stages, and the dropout forward and backward; other d, fp32 at d = 256 and
+ * the FP8 and split-key-range forwards at d = 256 are FA_ERR_UNSUPPORTED); N >= 1 (any
  * N, tails are masked); B, H >= 1 with B*H*N*d < 2^31; scale finite and > 0;
  * causal in {0, 1}.
  *
@@ -154,7 +155,7 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const
  *   dS = P o (dP - D 1^T),  dV = (256 / (256 - drop_t)) (P o Z)^T dO,
  *   dQ = scale dS K,  dK = scale dS^T Q.
  *
- * bf16 only (no dtype argument); d in {64, 96, 128}.  B, H, N, causal,
+ * bf16 only (no dtype argument); d in {64, 96, 128, 256}.  B, H, N, causal,
  * scale, layout, pointers, alignment, ownership, streams and errors are those
  * of fa_fwd and fa_bwd; the workspace is fa_bwd's
  * (fa_bwd_workspace_bytes(B, H, N, d, FA_BF16)).  drop_t outside 0 .. 255 is

@@ -286,15 +286,16 @@ def test_tensors_of_2_pow_31_elements_are_unsupported():
 
 @needs_lib
 def test_head_dim_256_is_bf16_fwd_bwd_only():
-    """d = 256 exists for the bf16 forward and backward; the fp32 path, the
-    split-key-range and FP8 forwards and dropout have no d = 256 kernels."""
+    """d = 256 exists for the bf16 forward and backward (with and without
+    dropout); the fp32 path and the split-key-range and FP8 forwards have no
+    d = 256 kernels."""
     base = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=64, d=256, causal=1, scale=0.0625, stream=None,
                 layout=fa.FA_LAYOUT_BHND)
     assert fa.fa_fwd(**base, dtype=fa.FA_FP32) == -2
     assert fa.fa_fwd(**dict(base, q=None), dtype=fa.FA_BF16) == -1   # d = 256 bf16 passes the shape check
     assert fa.fa_bwd_workspace_bytes(1, 2, 64, 256, fa.FA_BF16) > 0
     assert fa.fa_bwd_workspace_bytes(1, 2, 64, 256, fa.FA_FP32) == 0
-    assert fa.fa_fwd_dropout(**base, drop_t=26, seed=1, offset=0) == -2
+    assert fa.fa_fwd_dropout(**dict(base, o=None), drop_t=26, seed=1, offset=0) == -1   # shape accepted
     assert fa.fa_fwd_fp8(**base, descale_q=1.0, descale_k=1.0, descale_v=1.0) == -2
     assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 64, 256, 0) == 0
     sk = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=4, Nk=64, d=256, causal=1, scale=0.0625, num_splits=0,

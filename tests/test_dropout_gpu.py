@@ -62,7 +62,7 @@ def _identity_inputs(B, H, N, d, seed, which, do_eye=False):
     return x
 
 
-MASK_CASES = [(d, n, causal) for d in (64, 96, 128) for n in (d, 37) for causal in (False, True)]
+MASK_CASES = [(d, n, causal) for d in (64, 96, 128, 256) for n in (d, 37) for causal in (False, True)]
 
 
 @pytest.mark.parametrize("d,n,causal", MASK_CASES)
@@ -179,6 +179,7 @@ def _compare_all(x, causal, scale, t, seed, off, layout=0, where=""):
 
 VALUE_CASES = [(d, n, causal, t) for d in (64, 96, 128) for n in (1, 64, 129, 300)
                for causal in (False, True) for t in (26, 128)]
+VALUE_CASES += [(256, n, causal, 77) for n in (1, 129, 300) for causal in (False, True)]
 
 
 @pytest.mark.parametrize("d,n,causal,t", VALUE_CASES)
