@@ -218,6 +218,32 @@ def cpu_baseline(w, x, budget_s=12.0):
     return base, heads[:done], results
 
 
+def cpu_single_core(gen, budget_s=8.0):
+    """The oracle on one core (BLAS held to one thread) on whole heads of
+    the c1, c2 and c3 workloads: seconds per head and credited TFLOP/s, with
+    at most budget_s / 3 seconds per workload (at least one head each)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import ref
+    out = {}
+    with threadpool_limits(limits=1):
+        for key in ("c1", "c2", "c3"):
+            w = gen.workload(key)
+            B, H, N, d = w.shape
+            x = gen.make_inputs(w, shape=(1, 1, N, d), seed=w.seed)
+            fwd1, bwd1 = w.flops()
+            per_head = (fwd1 + bwd1) / (B * H)
+            done, t0 = 0, time.perf_counter()
+            while True:
+                ref.forward_backward(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal)
+                done += 1
+                if time.perf_counter() - t0 > budget_s / 3:
+                    break
+            dt = time.perf_counter() - t0
+            out[w.name] = {"s_per_head": round(dt / done, 4), "heads": done,
+                           "tflops": round(per_head * done / dt / 1e12, 6), "cores": 1}
+    return out
+
+
 # the parity bar of the test suite: fp32 max-abs 1e-4; bf16 max-abs 2e-2 * max|ref|
 # (max|ref| taken as at least 1e-2); LSE max-abs 1e-3
 def oracle_check(w, heads, want, got):
@@ -801,6 +827,7 @@ def main():
     if not args.no_cpu_baseline:
         base, heads, ref = cpu_baseline(w, x)
         out["cpu_baseline"] = base
+        out["detail"]["cpu_single_core"] = cpu_single_core(gen)
         out["detail"]["oracle_check"] = oracle_check(w, heads, ref, {"o": o, "lse": lse, "dq": dq,
                                                                     "dk": dk, "dv": dv})
     print(json.dumps(out), flush=True)
