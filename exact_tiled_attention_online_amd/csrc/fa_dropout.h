@@ -55,8 +55,9 @@ struct Philox4 {
       const uint32_t rk1 = k1 + (uint32_t)r * 0xBB67AE85u;
       const uint64_t p0 = mul_wide(x0, 0xD2511F53u);
       const uint64_t p1 = mul_wide(x2, 0xCD9E8D57u);
-      const uint32_t n0 = (uint32_t)(p1 >> 32) ^ x1 ^ rk0;
-      const uint32_t n2 = (uint32_t)(p0 >> 32) ^ x3 ^ rk1;
+      // three-input xors as one v_bitop3_b32 each (truth table 0x96)
+      const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), x1, rk0, 0x96);
+      const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), x3, rk1, 0x96);
       x1 = (uint32_t)p1;
       x3 = (uint32_t)p0;
       x0 = n0;
