@@ -372,3 +372,21 @@ def test_head_dim_256_larger_size_sampled_heads():
     del res
     torch.cuda.empty_cache()
 
+
+
+@pytest.mark.parametrize("d,n", [(128, 8155), (256, 4099)])
+def test_large_ragged_sampled_heads(d, n):
+    """A ragged last tile behind many full ones (N not a multiple of any tile
+    or block size), causal, on two whole heads."""
+    import torch
+    log(f"[large ragged] d={d} N={n}")
+    w = gen.workload("c4")
+    x = gen.make_inputs(w, shape=(1, 3, n, d), seed=n)
+    scale = 1.0 / math.sqrt(d)
+    res = run_gpu(x, "bf16", True, scale)
+    want = oracle_heads(x, True, scale, heads=[(0, 0), (0, 2)])
+    for (b, h), wv in want.items():
+        errs = compare({k: res[k][b, h] for k in wv}, wv, "bf16", where=f"large ragged d{d} head ({b},{h})")
+        log(f"  head ({b},{h}) max errors {errs}")
+    del res
+    torch.cuda.empty_cache()
