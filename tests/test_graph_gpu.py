@@ -131,3 +131,43 @@ def test_captured_dropout_step_replays_bitwise():
         torch.cuda.synchronize()
         for n, ref in want.items():
             assert torch.equal(t[n], ref), (rep, n)
+
+
+def test_captured_fp8_forward_and_d256_step_replay_bitwise():
+    """The FP8 forward and the d = 256 forward + backward enqueue kernels
+    only, so captured calls replay to the eager bits."""
+    import torch
+    log("[graph] FP8 forward and d = 256 step")
+    x8 = gen.make_fp8_inputs((1, 4, 700, 128), seed=88)
+    q8, k8, v8 = (torch.from_numpy(x8[n]).cuda() for n in ("q8", "k8", "v8"))
+    o8 = torch.empty((1, 4, 700, 128), dtype=torch.bfloat16, device="cuda")
+    l8 = torch.empty((1, 4, 700), dtype=torch.float32, device="cuda")
+
+    def fp8():
+        fa.forward_fp8(q8, k8, v8, x8["descale_q"], x8["descale_k"], x8["descale_v"], True, 128 ** -0.5,
+                       out=o8, lse=l8)
+
+    t = _step_tensors(1, 2, 600, 256, seed=89)
+
+    def d256():
+        _enqueue_step(t, 1, 2, 600, 256, True, 1.0 / 16.0, torch.cuda.current_stream())
+
+    fp8()
+    d256()
+    torch.cuda.synchronize()
+    want = (o8.clone(), l8.clone(), _snapshot(t))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp8()
+        d256()
+    for rep in range(3):
+        o8.fill_(float("nan"))
+        l8.fill_(float("nan"))
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            t[n].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o8, want[0]) and torch.equal(l8, want[1]), rep
+        for n, ref in want[2].items():
+            assert torch.equal(t[n], ref), (rep, n)
