@@ -4,7 +4,9 @@
 // can compile it without VGPR-form MFMA results (-amdgpu-mfma-vgpr-form): at
 // d = 256 a wave holds K and V rows, half of dK and dV, and the S and dP tiles
 // (about 490 registers), and with that option the compiler's AGPR-rewrite
-// pass fails on it, while without it the kernel fits without spills.
+// pass fails on it, while without it the kernel fits without spills.  Two
+// waves share each 32-key slice (one per half of d), so a workgroup of 4
+// waves owns 64 keys here rather than the 128 of d <= 128.
 #include "fa_bwd_kv_body.h"
 
 namespace fa {
