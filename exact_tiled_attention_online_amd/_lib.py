@@ -137,14 +137,15 @@ def fa_fwd_splitkv_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, descale_
 
 
 def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, causal, scale, drop_t, seed, offset, stream, layout) -> int:
-    return load().fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), int(drop_t), int(seed),
-                                 int(offset), stream, layout)
+    return load().fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), int(drop_t),
+                                 _check_uint(seed, 64, "seed"), _check_uint(offset, 32, "offset"), stream, layout)
 
 
 def fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, drop_t, seed, offset, workspace,
                    workspace_bytes, stream, layout) -> int:
     return load().fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
-                                 int(drop_t), int(seed), int(offset), workspace, workspace_bytes, stream, layout)
+                                 int(drop_t), _check_uint(seed, 64, "seed"), _check_uint(offset, 32, "offset"),
+                                 workspace, workspace_bytes, stream, layout)
 
 
 def fa_strerror(status: int) -> str:
@@ -168,6 +169,34 @@ def _check(ts, shape):
             raise ValueError("expected contiguous device tensors of one shape")
         if t.dtype != ts[0].dtype:
             raise ValueError("q, k, v (and o, dO) must share one dtype")
+        if t.device != ts[0].device:
+            raise ValueError("all tensors must be on one device")
+
+
+def _check_buf(t, shape, dtype, device, name):
+    """A caller-supplied output or statistics buffer: the kernels write (or
+    read) exactly `shape` elements of `dtype` through its pointer."""
+    if (t.device != device or t.dtype != dtype or not t.is_contiguous()
+            or tuple(t.shape) != tuple(shape)):
+        raise ValueError(f"{name}: expected a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
+def _check_ws(ws, device):
+    """The workspace is passed as (pointer, byte count): a contiguous uint8
+    device tensor, so that numel() is its size in bytes."""
+    import torch
+    if ws.device != device or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("workspace: expected a contiguous uint8 tensor on the inputs' device")
+    return ws
+
+
+def _check_uint(x, bits, name):
+    x = int(x)
+    if not 0 <= x < (1 << bits):
+        raise ValueError(f"{name} = {x} is outside [0, 2^{bits})")
+    return x
 
 
 def _dims(q, layout):
@@ -195,8 +224,9 @@ def forward(q, k, v, causal: bool, scale: float, out=None, lse=None, stream=None
     import torch
     B, H, N, d = _dims(q, layout)
     _check((q, k, v), q.shape)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = torch.empty_like(q) if out is None else _check_buf(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+         else _check_buf(lse, (B, H, N), torch.float32, q.device, "lse"))
     st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
                 B, H, N, d, causal, scale, _stream(stream), _dtype_code(q), layout)
     if st != FA_OK:
@@ -219,10 +249,12 @@ def backward(q, k, v, o, do, lse, causal: bool, scale: float, ws=None, grads=Non
     import torch
     B, H, N, d = _dims(q, layout)
     _check((q, k, v, o, do), q.shape)
-    if ws is None:
-        ws = workspace(q, layout)
-    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(q),
-                                                  torch.empty_like(q))
+    _check_buf(lse, (B, H, N), torch.float32, q.device, "lse")
+    ws = workspace(q, layout) if ws is None else _check_ws(ws, q.device)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = (_check_buf(g, q.shape, q.dtype, q.device, n) for g, n in zip(grads, ("dq", "dk", "dv")))
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
                 ws.data_ptr(), ws.numel(), _stream(stream), _dtype_code(q), layout)
@@ -241,13 +273,16 @@ def forward_splitkv(q, k, v, causal: bool, scale: float, num_splits: int = 0, ou
     Nk = _dims(k, layout)[2]
     _check((q,), q.shape)
     _check((k, v), k.shape)
-    if k.dtype != q.dtype:
-        raise ValueError("q, k, v must share one dtype")
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("q, k, v must share one dtype and device")
+    o = torch.empty_like(q) if out is None else _check_buf(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None
+         else _check_buf(lse, (B, H, Nq), torch.float32, q.device, "lse"))
     if ws is None:
         n = fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits)
         ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+    else:
+        _check_ws(ws, q.device)
     st = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Nq, Nk,
                         d, causal, scale, num_splits, ws.data_ptr(), ws.numel(), _stream(stream),
                         _dtype_code(q), layout)
@@ -265,8 +300,10 @@ def forward_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_v: float
     _check((q8, k8, v8), q8.shape)
     if q8.dtype != torch.uint8:
         raise TypeError("FP8 inputs are passed as uint8 e4m3fn codes")
-    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None else out
-    l = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    o = (torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None
+         else _check_buf(out, q8.shape, torch.bfloat16, q8.device, "out"))
+    l = (torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None
+         else _check_buf(lse, (B, H, N), torch.float32, q8.device, "lse"))
     st = fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, N, d, causal,
                     scale, descale_q, descale_k, descale_v, _stream(stream), layout)
     if st != FA_OK:
@@ -287,11 +324,17 @@ def forward_splitkv_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_
     _check((k8, v8), k8.shape)
     if q8.dtype != torch.uint8 or k8.dtype != torch.uint8:
         raise TypeError("FP8 inputs are passed as uint8 e4m3fn codes")
-    o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None else out
-    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device) if lse is None else lse
+    if k8.device != q8.device:
+        raise ValueError("q8, k8, v8 must share one device")
+    o = (torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None
+         else _check_buf(out, q8.shape, torch.bfloat16, q8.device, "out"))
+    l = (torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device) if lse is None
+         else _check_buf(lse, (B, H, Nq), torch.float32, q8.device, "lse"))
     if ws is None:
         n = fa_fwd_splitkv_fp8_workspace_bytes(B, H, Nq, Nk, d, num_splits)
         ws = torch.empty(max(n, 256), dtype=torch.uint8, device=q8.device)
+    else:
+        _check_ws(ws, q8.device)
     st = fa_fwd_splitkv_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Nq,
                             Nk, d, causal, scale, descale_q, descale_k, descale_v, num_splits, ws.data_ptr(),
                             ws.numel(), _stream(stream), layout)
@@ -317,8 +360,9 @@ def forward_dropout(q, k, v, causal: bool, scale: float, p_drop: float, seed: in
     import torch
     B, H, N, d = _dims(q, layout)
     _check((q, k, v), q.shape)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = torch.empty_like(q) if out is None else _check_buf(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+         else _check_buf(lse, (B, H, N), torch.float32, q.device, "lse"))
     st = fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, N, d, causal,
                         scale, drop_threshold(p_drop), seed, offset, _stream(stream), layout)
     if st != FA_OK:
@@ -332,10 +376,12 @@ def backward_dropout(q, k, v, o, do, lse, causal: bool, scale: float, p_drop: fl
     import torch
     B, H, N, d = _dims(q, layout)
     _check((q, k, v, o, do), q.shape)
-    if ws is None:
-        ws = workspace(q, layout)
-    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(q),
-                                                  torch.empty_like(q))
+    _check_buf(lse, (B, H, N), torch.float32, q.device, "lse")
+    ws = workspace(q, layout) if ws is None else _check_ws(ws, q.device)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    else:
+        dq, dk, dv = (_check_buf(g, q.shape, q.dtype, q.device, n) for g, n in zip(grads, ("dq", "dk", "dv")))
     st = fa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale,
                         drop_threshold(p_drop), seed, offset, ws.data_ptr(), ws.numel(), _stream(stream), layout)

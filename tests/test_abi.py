@@ -302,3 +302,40 @@ def test_head_dim_256_is_bf16_fwd_bwd_only():
               workspace=P, workspace_bytes=1 << 20, stream=None, dtype=fa.FA_BF16, layout=fa.FA_LAYOUT_BHND)
     assert fa.fa_fwd_splitkv(**sk) == -2
 
+
+
+@needs_lib
+@pytest.mark.parametrize("kw", [dict(seed=-1), dict(seed=1 << 64), dict(offset=-1), dict(offset=1 << 32)])
+def test_dropout_seed_and_offset_out_of_range_raise(kw):
+    """ctypes would wrap these silently into another mask; the binding raises
+    before the C call."""
+    fwd = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=64, d=128, causal=1, scale=0.125, drop_t=26, seed=7,
+               offset=0, stream=None, layout=fa.FA_LAYOUT_BHND)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_dropout(**dict(fwd, **kw))
+    bwd = dict(fwd, dO=P, dq=P, dk=P, dv=P, workspace=P, workspace_bytes=1 << 20)
+    with pytest.raises(ValueError):
+        fa.fa_bwd_dropout(**dict(bwd, **kw))
+
+
+def test_buffer_checks_of_the_binding():
+    """Caller-supplied outputs, statistics and workspaces are checked for
+    shape, dtype, contiguity and device before their pointers are used (host
+    tensors stand in for device ones here)."""
+    import torch
+    from exact_tiled_attention_online_amd import _lib
+    dev = torch.device("cpu")
+    good = torch.empty((1, 2, 64), dtype=torch.float32)
+    assert _lib._check_buf(good, (1, 2, 64), torch.float32, dev, "lse") is good
+    for bad in (torch.empty((1, 2, 63), dtype=torch.float32), torch.empty((1, 2, 64), dtype=torch.bfloat16),
+                torch.empty((1, 64, 2), dtype=torch.float32).transpose(1, 2), torch.empty((2, 64)),
+                torch.empty((1, 2, 64), dtype=torch.float32, device="meta")):
+        with pytest.raises(ValueError):
+            _lib._check_buf(bad, (1, 2, 64), torch.float32, dev, "lse")
+    ws = torch.empty(4096, dtype=torch.uint8)
+    assert _lib._check_ws(ws, dev) is ws
+    for bad in (torch.empty(1024, dtype=torch.float32), ws[::2], torch.empty(4096, dtype=torch.uint8, device="meta")):
+        with pytest.raises(ValueError):
+            _lib._check_ws(bad, dev)
+    assert _lib._check_uint((1 << 64) - 1, 64, "seed") == (1 << 64) - 1
+    assert _lib._check_uint(0, 32, "offset") == 0

@@ -390,3 +390,35 @@ def test_large_ragged_sampled_heads(d, n):
         log(f"  head ({b},{h}) max errors {errs}")
     del res
     torch.cuda.empty_cache()
+
+
+def test_conveniences_reject_mismatched_buffers():
+    """Outputs, LSE, gradients and workspaces handed to the torch
+    conveniences are checked before any launch: each mismatched buffer raises
+    ValueError, and the outputs given alongside stay untouched."""
+    import torch
+    B, H, N, d = 1, 2, 64, 128
+    log(f"[buffers] B={B} H={H} N={N} d={d}")
+    q, k, v, do = (torch.randn((B, H, N, d), device="cuda").to(torch.bfloat16) for _ in range(4))
+    o, lse = fa.forward(q, k, v, True, 0.125)
+    short_o = torch.full((B, H, N - 1, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    f32_o = torch.full((B, H, N, d), 7.0, dtype=torch.float32, device="cuda")
+    short_l = torch.full((B, H, N - 1), 7.0, dtype=torch.float32, device="cuda")
+    strided_l = torch.full((B, N, H), 7.0, dtype=torch.float32, device="cuda").transpose(1, 2)
+    for kw in (dict(out=short_o), dict(out=f32_o), dict(lse=short_l), dict(lse=strided_l)):
+        with pytest.raises(ValueError):
+            fa.forward(q, k, v, True, 0.125, **kw)
+        with pytest.raises(ValueError):
+            fa.forward_dropout(q, k, v, True, 0.125, 0.1, 3, **kw)
+    good = (torch.empty_like(q), torch.empty_like(q), torch.empty_like(q))
+    for kw in (dict(grads=(good[0], good[1], short_o)), dict(ws=torch.empty(1 << 20, device="cuda")),
+               dict(ws=torch.empty(1 << 20, dtype=torch.uint8, device="cuda")[::2])):
+        with pytest.raises(ValueError):
+            fa.backward(q, k, v, o, do, lse, True, 0.125, **kw)
+        with pytest.raises(ValueError):
+            fa.backward_dropout(q, k, v, o, do, lse, True, 0.125, 0.1, 3, **kw)
+    with pytest.raises(ValueError):
+        fa.backward(q, k, v, o, do, short_l, True, 0.125)
+    torch.cuda.synchronize()
+    for t in (short_o, f32_o, short_l, strided_l):
+        assert bool((t == 7.0).all())
