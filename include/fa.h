@@ -55,7 +55,7 @@ extern "C" {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_INVALID = -1,      /* null pointer, non-positive size, bad flag, bad scale */
+  FA_ERR_INVALID = -1,      /* null or misaligned pointer, non-positive size, bad flag, bad scale */
   FA_ERR_UNSUPPORTED = -2,  /* head dim or dtype the library has no kernel for */
   FA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
   FA_ERR_HIP = -4           /* the HIP runtime reported a launch error */
@@ -80,8 +80,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * Bytes of device workspace fa_bwd needs for this shape: the fp32 row term
  * D [B,H,N], the ledger in base 2 [B,H,N] and, for bf16, room for an fp32
- * dQ accumulator [B,H,N,d] (used only with FA_DQ_MODE=atomic).  The caller allocates it (any 256-byte-aligned
- * device buffer); its contents on entry do not matter.
+ * dQ accumulator [B,H,N,d] (used only with FA_DQ_MODE=atomic at d = 64 or
+ * 128).  The caller allocates it (any 256-byte-aligned device buffer); its
+ * contents on entry do not matter.  Returns 0 for a non-positive size or a
+ * head dim or dtype that fa_bwd has no kernel for.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
 
@@ -116,8 +118,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  * Argument meaning, checks and errors are those of fa_bwd.  With the
  * environment variable FA_DQ_MODE=atomic (bf16 only) the dQ products run
  * inside fa_bwd_dkdv instead, as fp32 atomic adds into the workspace, and
- * fa_bwd_dq converts that accumulator (d = 64 and 128; d = 96 ignores the
- * variable); the default is the query-outer kernel, which measured faster.
+ * fa_bwd_dq converts that accumulator (d = 64 and 128; d = 96 and 256 ignore
+ * the variable); the default is the query-outer kernel, which measured faster.
  */
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
                       float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype,
@@ -218,8 +220,9 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
  * Ranges are whole 32-key tiles and none is left empty, so fewer ranges than
  * asked may be used.  The workspace must hold
  * fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits) bytes (same
- * num_splits), 256-byte aligned; its contents on entry do not matter.
- * Supported: dtype FA_BF16 only (FA_ERR_UNSUPPORTED otherwise), d in
+ * num_splits), 256-byte aligned; its contents on entry do not matter (the
+ * size function returns 0 for shapes, d or num_splits that fa_fwd_splitkv
+ * rejects).  Supported: dtype FA_BF16 only (FA_ERR_UNSUPPORTED otherwise), d in
  * {64, 96, 128}, 0 <= num_splits <= 1024.  Errors, ownership and streams as for
  * fa_fwd; a missing or small workspace is FA_ERR_WORKSPACE.
  */
