@@ -97,7 +97,6 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
   // swizzle leaves chunk bit 4 alone); a compile-time 0 when DH = 1
   static_assert(DH == 1 || DTW == TileBases<ROWB>::DTB, "one part of d per set of tile bases");
   const int doff = DH > 1 ? 256 * __builtin_amdgcn_readfirstlane(dpart) : 0;
-  const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, s16 = lane & 15;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the same value, known uniform
   const int RS = lay.row_stride(D);      // elements between a head's rows
   const TileFetch<ROWB, BR, 4, CH> qfetch(wave_u, lane, RS * 2);
@@ -125,7 +124,13 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const float* Dh = NDR + (size_t)head * N;    // -D
   float* dQh = dQacc + (size_t)head * N * D;   // contiguous [B*H][N][d] accumulator
 
-  for (int part = 0; part < nparts; ++part) {
+  auto run_part = [&](int part) {
+    // Lane indices, re-derived per part from an opaque copy of the lane id:
+    // otherwise the compiler computes lane-dependent addresses once for both
+    // parts and keeps them live across the first.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int l32 = ln & 31, h = ln >> 5, g = ln >> 4, s16 = ln & 15;
     const int kb = CAUSAL ? (part == 0 ? c_item : nkb - 1 - c_item) : c_item;
     const bool ascend = part == 1;
     const int kv0 = kb * BC;
@@ -138,7 +143,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
       constexpr int KPT = BC * CH / 256;
 #pragma unroll
       for (int p = 0; p < KPT; ++p) {
-        const int ci = p * 256 + tid;
+        const int ci = p * 256 + 64 * wave_u + ln;
         const int row = ci / CH, ch = ci % CH;
         const int kv = kv0 + row;
         u32x4 x = u32x4{0, 0, 0, 0};
@@ -168,11 +173,11 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
     if constexpr (DQA) {
 #pragma unroll
       for (int s = 0; s < BC / 16; ++s)
-        ktf[s] = tr_operand<ROWB>(sK, 16 * s + 8 * h, 16 * s + 8 * h + 4, 32 * dsl + 16 * (g & 1), lane);
+        ktf[s] = tr_operand<ROWB>(sK, 16 * s + 8 * h, 16 * s + 8 * h + 4, 32 * dsl + 16 * (g & 1), ln);
     }
 
     // ---- per-lane LDS address bases ------------------------------------------
-    const TileBases<ROWB> tb(lane);
+    const TileBases<ROWB> tb(ln);
     // transposed A operand of dQ (registers = key rows) from the dS tile:
     // offset(s, u, hi) = baseE[u][hi] + 2048*s.
     int baseE[NQT][2];
@@ -198,11 +203,11 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
       qfetch(Qh, qb0, N, dQt);
       qfetch(Gh, qb0, N, dGt);
       if (qb0 + BR <= N) {
-        if (wave_u == 0) dma4_buf(raw_rsrc(Lh), 4 * lane, 4 * qb0, dL);
-        if (wave_u == 1) dma4_buf(raw_rsrc(Dh), 4 * lane, 4 * qb0, dD);
+        if (wave_u == 0) dma4_buf(raw_rsrc(Lh), 4 * ln, 4 * qb0, dL);
+        if (wave_u == 1) dma4_buf(raw_rsrc(Dh), 4 * ln, 4 * qb0, dD);
       } else {
-        if (wave_u == 0) dma4_buf(raw_rsrc(Lh), 4 * min(qb0 + lane, N - 1), 0, dL);
-        if (wave_u == 1) dma4_buf(raw_rsrc(Dh), 4 * min(qb0 + lane, N - 1), 0, dD);
+        if (wave_u == 0) dma4_buf(raw_rsrc(Lh), 4 * min(qb0 + ln, N - 1), 0, dL);
+        if (wave_u == 1) dma4_buf(raw_rsrc(Dh), 4 * min(qb0 + ln, N - 1), 0, dD);
       }
     };
 
@@ -301,7 +306,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
         if constexpr (DROP) {
 #pragma unroll
           for (int t = 0; t < 2; ++t)
-            ph[t] = Philox4{(uint32_t)kvrow >> 2, (uint32_t)(qb0 + 32 * t + 8 * (lane & 3) + 4 * h) >> 2,
+            ph[t] = Philox4{(uint32_t)kvrow >> 2, (uint32_t)(qb0 + 32 * t + 8 * (ln & 3) + 4 * h) >> 2,
                             (uint32_t)head, dr.offset};
         }
         bf16x8 qa[2][KS], ga[2][KS];               // S/dP operands (Q, dO rows)
@@ -397,7 +402,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
             if (g < 2 * KS) {
               const int t = g / KS, u = g % KS;
               ph[t].rounds(10 * u / KS, 10 * (u + 1) / KS, dr.k0, dr.k1);
-              if (u == KS - 1) dw[t] = quad_transpose(byte_transpose(ph[t].words()), lane & 3);
+              if (u == KS - 1) dw[t] = quad_transpose(byte_transpose(ph[t].words()), ln & 3);
             }
           }
           if (g >= KS && g < KS + EC) elem_chunk(0, g - KS);
@@ -472,7 +477,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
         constexpr int OPW = 32 * CW / 64;   // 16-byte stores per lane
 #pragma unroll
         for (int p = 0; p < OPW; ++p) {
-          const int ci = p * 64 + lane;
+          const int ci = p * 64 + ln;
           const int row = ci / CW, ch = ci % CW;
           if (kvw + row < N)
             *reinterpret_cast<u32x4*>(dst + (size_t)(kvw + row) * RS + c0 + ch * 8) =
@@ -481,7 +486,10 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
       }
       __syncthreads();   // the next part refills the query buffers
     }
-  }
+  };
+  // two inlined copies rather than a loop, for the same reason
+  run_part(0);
+  if (nparts > 1) run_part(1);
 }
 
 template <int D, bool CAUSAL, bool DQA>
