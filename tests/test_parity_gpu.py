@@ -419,6 +419,23 @@ def test_conveniences_reject_mismatched_buffers():
             fa.backward_dropout(q, k, v, o, do, lse, True, 0.125, 0.1, 3, **kw)
     with pytest.raises(ValueError):
         fa.backward(q, k, v, o, do, short_l, True, 0.125)
+    # FP8 forward: bf16 output of the inputs' shape
+    q8, k8, v8 = (torch.zeros((B, H, N, d), dtype=torch.uint8, device="cuda") for _ in range(3))
+    for kw in (dict(out=f32_o), dict(out=short_o), dict(lse=short_l)):
+        with pytest.raises(ValueError):
+            fa.forward_fp8(q8, k8, v8, 1.0, 1.0, 1.0, True, 0.125, **kw)
+    # split-key-range forward: 4 queries against the 64 keys; uint8 workspace
+    qd, q8d = q[:, :, :4].contiguous(), q8[:, :, :4].contiguous()
+    o4 = torch.full((B, H, 4, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    l4 = torch.full((B, H, 4), 7.0, dtype=torch.float32, device="cuda")
+    bad_split = (dict(out=short_o, lse=l4), dict(out=o4, lse=short_l),
+                 dict(out=o4, lse=l4, ws=torch.empty(1 << 20, device="cuda")),
+                 dict(out=o4, lse=l4, ws=torch.empty(1 << 20, dtype=torch.uint8, device="cuda")[1::2]))
+    for kw in bad_split:
+        with pytest.raises(ValueError):
+            fa.forward_splitkv(qd, k, v, True, 0.125, **kw)
+        with pytest.raises(ValueError):
+            fa.forward_splitkv_fp8(q8d, k8, v8, 1.0, 1.0, 1.0, True, 0.125, **kw)
     torch.cuda.synchronize()
-    for t in (short_o, f32_o, short_l, strided_l):
+    for t in (short_o, f32_o, short_l, strided_l, o4, l4):
         assert bool((t == 7.0).all())
