@@ -349,6 +349,34 @@ def test_maximum_size_sampled_heads():
     torch.cuda.empty_cache()
 
 
+def test_maximum_size_d256_sampled_heads():
+    """The largest d = 256 shape of the same kind: B=63, H=16, N=8192 causal,
+    2.11e9 elements per tensor (one batch more reaches the 2^31 limit), through
+    the d = 256 forward, preprocess, dK/dV and dQ kernels; three whole heads
+    against the oracle as above."""
+    import torch
+    B, H, N, d = 63, 16, 8192, 256
+    assert B * H * N * d < 2 ** 31 and (B + 1) * H * N * d >= 2 ** 31
+    log(f"[max size d256] B={B} H={H} N={N} d={d} causal, {B * H * N * d:.3e} elements per tensor")
+    scale = 1.0 / math.sqrt(d)
+    g = torch.Generator(device="cuda").manual_seed(256)
+    q, k, v, do = (torch.randn((B, H, N, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(4))
+    o, lse = fa.forward(q, k, v, True, scale)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, True, scale)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (31, 9), (B - 1, H - 1)):
+        x = {n: t[b, h].float().cpu().numpy().astype(np.float64)[None, None] for n, t in
+             (("q", q), ("k", k), ("v", v), ("do", do))}
+        want = oracle_heads(x, True, scale, heads=[(0, 0)])[(0, 0)]
+        got = {"o": to_np(o[b, h]), "lse": to_np(lse[b, h]), "dq": to_np(dq[b, h]), "dk": to_np(dk[b, h]),
+               "dv": to_np(dv[b, h])}
+        errs = compare(got, want, "bf16", where=f"max size d256 head ({b},{h})")
+        log(f"  head ({b},{h}) max errors {errs}")
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_head_dim_256_bnhd_layout(causal):
     log(f"[d256 bnhd] causal={causal}")
