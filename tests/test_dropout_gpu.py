@@ -248,3 +248,32 @@ def test_sampled_heads_large_causal():
         errs = compare({n: got[n][b, h] for n in want}, want, "bf16", where=f"large head ({b},{h})")
         assert errs["dq"] <= 2e-2 * np.abs(want["dq"]).max()
         log(f"  head ({b},{h}) max errors {errs}")
+
+
+def test_maximum_size_sampled_heads():
+    """Dropout at the largest shape of the headline geometry: B=63, H=32,
+    N=8192, d=128 causal, 2.11e9 elements per tensor, p = 26/256.  The mask
+    counter carries the flattened head index (up to 2015) and the tensors'
+    64-bit offsets run through every dropout kernel; three whole heads (the
+    first, a middle and the last) against the dropout oracle with the exact
+    bf16 values the kernels saw."""
+    import torch
+    B, H, N, d = 63, 32, 8192, 128
+    scale, seed, off, t = 1.0 / math.sqrt(d), 0xABCDEF0123456789, 11, 26
+    log(f"[drop max size] B={B} H={H} N={N} d={d} causal t={t}")
+    g = torch.Generator(device="cuda").manual_seed(6326)
+    q, k, v, do = (torch.randn((B, H, N, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                   for _ in range(4))
+    o, lse = fa.forward_dropout(q, k, v, True, scale, t / 256, seed=seed, offset=off)
+    dq, dk, dv = fa.backward_dropout(q, k, v, o, do, lse, True, scale, t / 256, seed=seed, offset=off)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (40, 13), (B - 1, H - 1)):
+        hx = {n: tt[b, h].float().cpu().numpy().astype(np.float64) for n, tt in
+              (("q", q), ("k", k), ("v", v), ("do", do))}
+        want = dr.head_panel_dropout(hx["q"], hx["k"], hx["v"], hx["do"], scale, True, b * H + h, seed, off, t)
+        got = {"o": to_np(o[b, h]), "lse": to_np(lse[b, h]), "dq": to_np(dq[b, h]), "dk": to_np(dk[b, h]),
+               "dv": to_np(dv[b, h])}
+        errs = compare(got, want, "bf16", where=f"drop max size head ({b},{h})")
+        log(f"  head ({b},{h}) max errors {errs}")
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
