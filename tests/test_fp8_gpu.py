@@ -134,3 +134,33 @@ def test_fp8_split_forward_matches_oracle(B, H, Nq, Nk, causal, ns):
             tol = (2.0 ** -4 + Nk * 2.0 ** -17) * vmax + 2.0 ** -9 * float(np.abs(ro[b, h]).max())
             assert float(np.abs(got_o[b, h] - ro[b, h]).max()) <= tol, (b, h)
             assert float(np.abs(got_l[b, h] - rl[b, h]).max()) <= LSE_ATOL, (b, h)
+
+
+def test_fp8_forward_maximum_size_sampled_heads():
+    """The FP8 forward at the largest shape of the headline geometry: B=63,
+    H=32, N=8192, d=128 causal, 2.11e9 one-byte codes per tensor (generated
+    on the device: normal values over the descale, clipped to the largest
+    finite e4m3fn value); three whole heads against the oracle on the values
+    the codes stand for, with the bound above."""
+    import torch
+    B, H, N, d = 63, 32, 8192, 128
+    ds, scale = 2.0 ** -5, 1.0 / math.sqrt(128)
+    log(f"[fp8 max size] B={B} H={H} N={N} d={d} causal")
+    g = torch.Generator(device="cuda").manual_seed(8863)
+
+    def codes():
+        x = torch.randn((B, H, N, d), generator=g, device="cuda", dtype=torch.float32)
+        x.mul_(1.0 / ds).clamp_(-448.0, 448.0)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+    q8, k8, v8 = codes(), codes(), codes()
+    o, lse = fa.forward_fp8(q8, k8, v8, ds, ds, ds, True, scale)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (25, 7), (B - 1, H - 1)):
+        x = {n: (gen.e4m3_to_f32(t[b, h].cpu().numpy()).astype(np.float64) * ds)[None, None]
+             for n, t in (("q", q8), ("k", k8), ("v", v8))}
+        got = {"o": to_np(o[b, h])[None, None], "lse": to_np(lse[b, h])[None, None]}
+        r = check(x, got, True, scale, f"fp8 max size head ({b},{h})")
+        log(f"  head ({b},{h}) worst O error / bound {r:.3f}")
+    del q8, k8, v8, o, lse
+    torch.cuda.empty_cache()

@@ -109,3 +109,50 @@ def test_decode_workload_full_size_sampled_heads():
         compare({"o": got["o"][b, h], "lse": got["lse"][b, h]}, r, "bf16", names=("o", "lse"),
                 where=f"decode head ({b},{h})")
     torch.cuda.empty_cache()
+
+
+def test_maximum_size_decode_sampled_heads():
+    """The split forward at the largest key/value cache the ABI takes for
+    8 x 32 heads: one query against Nk = 65535 keys, d = 128 (2.15e9 - 32768
+    elements per K and V tensor), bf16 and FP8 (codes of the same values'
+    kind); three whole heads against the oracle."""
+    import torch
+    B, H, Nq, Nk, d = 8, 32, 1, 65535, 128
+    assert B * H * Nk * d < 2 ** 31 and B * H * (Nk + 1) * d >= 2 ** 31
+    scale, ds = 1.0 / math.sqrt(d), 2.0 ** -5
+    log(f"[decode max size] B={B} H={H} Nq={Nq} Nk={Nk} d={d}")
+    g = torch.Generator(device="cuda").manual_seed(65535)
+    q = torch.randn((B, H, Nq, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    k, v = (torch.randn((B, H, Nk, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+            for _ in range(2))
+    o, lse = fa.forward_splitkv(q, k, v, True, scale)
+    torch.cuda.synchronize()
+    heads = ((0, 0), (3, 20), (B - 1, H - 1))
+    for b, h in heads:
+        want = ref.forward_rect(*(t[b, h].float().cpu().numpy()[None, None] for t in (q, k, v)), scale, True,
+                                heads=[(0, 0)])[(0, 0)]
+        errs = compare({"o": to_np(o[b, h]), "lse": to_np(lse[b, h])}, want, "bf16", names=("o", "lse"),
+                       where=f"decode max size head ({b},{h})")
+        log(f"  bf16 head ({b},{h}) max errors {errs}")
+    del k, v
+    torch.cuda.empty_cache()
+
+    def codes(shape):
+        x = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+        x.mul_(1.0 / ds).clamp_(-448.0, 448.0)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+    q8, k8, v8 = codes((B, H, Nq, d)), codes((B, H, Nk, d)), codes((B, H, Nk, d))
+    o8, lse8 = fa.forward_splitkv_fp8(q8, k8, v8, ds, ds, ds, True, scale)
+    torch.cuda.synchronize()
+    for b, h in heads:
+        qh, kh, vh = (gen.e4m3_to_f32(t[b, h].cpu().numpy()).astype(np.float64) * ds for t in (q8, k8, v8))
+        o_ref, lse_ref = ref.head_forward_rect(qh, kh, vh, scale, True)
+        # the FP8 bound: P rounded to e4m3 for the P V product
+        tol_o = (2.0 ** -4 + Nk * 2.0 ** -17) * float(np.abs(vh).max()) + 2.0 ** -9 * float(np.abs(o_ref).max())
+        err_o = float(np.abs(to_np(o8[b, h]) - o_ref).max())
+        err_l = float(np.abs(to_np(lse8[b, h]) - lse_ref).max())
+        assert err_l <= 1e-3 and err_o <= tol_o, (b, h, err_o, tol_o, err_l)
+        log(f"  fp8 head ({b},{h}) O err {err_o:.3e} (bound {tol_o:.3e}), LSE err {err_l:.2e}")
+    del q8, k8, v8, o8, lse8
+    torch.cuda.empty_cache()
