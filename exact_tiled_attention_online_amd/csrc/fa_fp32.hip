@@ -20,6 +20,11 @@
 namespace fa {
 
 constexpr int F32_ROWS = 64;   // rows per workgroup (128 lanes)
+
+// One-dimensional grid: workgroup x is row block x % nrb of head x / nrb, so
+// that any number of heads the interface accepts fits (a grid's second
+// dimension holds at most 65535 workgroups).
+inline unsigned f32_grid(int BH, int N) { return (unsigned)BH * (unsigned)((N + F32_ROWS - 1) / F32_ROWS); }
 constexpr int F32_TILE = 32;   // streamed rows per LDS tile
 
 template <int D>
@@ -51,8 +56,9 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ 
   __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sv[F32_TILE * D];
   const int tid = threadIdx.x, half = tid & 1;
-  const int head = blockIdx.y;
-  const int row0 = blockIdx.x * F32_ROWS;
+  const int nrb = (N + F32_ROWS - 1) / F32_ROWS;
+  const int head = blockIdx.x / nrb;
+  const int row0 = (blockIdx.x - head * nrb) * F32_ROWS;
   const int qrow = row0 + (tid >> 1);
   const int RS = lay.row_stride(D);   // elements between a head's rows
   const size_t hoff = lay.head_off(head, N, D);
@@ -117,8 +123,9 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
   __shared__ __attribute__((aligned(16))) float sg[F32_TILE * D];
   __shared__ float sl[F32_TILE], sd[F32_TILE];
   const int tid = threadIdx.x, half = tid & 1;
-  const int head = blockIdx.y;
-  const int row0 = blockIdx.x * F32_ROWS;
+  const int nrb = (N + F32_ROWS - 1) / F32_ROWS;
+  const int head = blockIdx.x / nrb;
+  const int row0 = (blockIdx.x - head * nrb) * F32_ROWS;
   const int kvrow = row0 + (tid >> 1);
   const int RS = lay.row_stride(D);   // elements between a head's rows
   const size_t hoff = lay.head_off(head, N, D);
@@ -174,8 +181,9 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
   __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sv[F32_TILE * D];
   const int tid = threadIdx.x, half = tid & 1;
-  const int head = blockIdx.y;
-  const int row0 = blockIdx.x * F32_ROWS;
+  const int nrb = (N + F32_ROWS - 1) / F32_ROWS;
+  const int head = blockIdx.x / nrb;
+  const int row0 = (blockIdx.x - head * nrb) * F32_ROWS;
   const int qrow = row0 + (tid >> 1);
   const int RS = lay.row_stride(D);   // elements between a head's rows
   const size_t hoff = lay.head_off(head, N, D);
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
 template <int D, bool CAUSAL>
 static hipError_t fwd_f32_t(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
                             int N, float scale, RowLayout lay, hipStream_t stream) {
-  const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
+  const dim3 grid(f32_grid(BH, N)), block(128);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, o, lse, BH, N, scale, lay);
   return hipGetLastError();
 }
@@ -223,7 +231,7 @@ template <int D, bool CAUSAL>
 static hipError_t bwd_kv_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
                                const float* ndrow, float* dk, float* dv, int BH, int N, float scale,
                                RowLayout lay, hipStream_t stream) {
-  const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
+  const dim3 grid(f32_grid(BH, N)), block(128);
   hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dk, dv, N,
                      scale, lay);
   return hipGetLastError();
@@ -233,7 +241,7 @@ template <int D, bool CAUSAL>
 static hipError_t bwd_q_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
                               const float* ndrow, float* dq, int BH, int N, float scale, RowLayout lay,
                               hipStream_t stream) {
-  const dim3 grid((unsigned)((N + F32_ROWS - 1) / F32_ROWS), (unsigned)BH), block(128);
+  const dim3 grid(f32_grid(BH, N)), block(128);
   hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dq, N, scale,
                      lay);
   return hipGetLastError();

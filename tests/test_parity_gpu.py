@@ -349,6 +349,24 @@ def test_maximum_size_sampled_heads():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_more_heads_than_a_grid_dimension_holds(dtype):
+    """70000 heads (B=2, H=35000) of N=3, d=64: more workgroups along the
+    head index than a grid's second dimension can hold (65535), so every
+    kernel must take the head from a one-dimensional grid; the first, a
+    middle and the last head against the oracle, causal and not."""
+    B, H, N, d = 2, 35000, 3, 64
+    log(f"[many heads] {dtype} B={B} H={H} N={N} d={d}")
+    x = gen.make_inputs(gen.workload("c1" if dtype == "fp32" else "c2"), shape=(B, H, N, d), seed=70000)
+    for causal in (False, True):
+        res = run_gpu(x, dtype, causal, 0.125)
+        heads = [(0, 0), (1, 17499), (B - 1, H - 1)]
+        want = oracle_heads(x, causal, 0.125, heads)
+        for b, h in heads:
+            compare({n: res[n][b, h] for n in ("o", "lse", "dq", "dk", "dv")}, want[(b, h)], dtype,
+                    where=f"many heads {dtype} c{int(causal)} head ({b},{h})")
+
+
 def test_maximum_size_d256_sampled_heads():
     """The largest d = 256 shape of the same kind: B=63, H=16, N=8192 causal,
     2.11e9 elements per tensor (one batch more reaches the 2^31 limit), through
