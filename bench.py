@@ -45,6 +45,22 @@ KERNEL_SOURCES = {
 }
 
 
+# Other instantiations whose HBM bytes the counter summary also records, for
+# the detail rooflines: key -> (template head and head dim, sources).
+DETAIL_COUNTERS = {
+    "fwd_bf16_dropout_kernel": (("fwd_bf16_dropout_kernel", 128), ["fa_fwd_bf16.hip", "fa_common.h", "fa_dropout.h"]),
+    "bwd_bf16_kernel_d256": (("bwd_bf16_kernel", 256),
+                             ["fa_bwd_kv256.hip", "fa_bwd_kv_body.h", "fa_common.h", "fa_dropout.h"]),
+}
+
+
+def _detail_instance(name, key):
+    """Whether a traced kernel name is the DETAIL_COUNTERS entry `key`."""
+    (short, d), _ = DETAIL_COUNTERS[key]
+    head = name.split("(")[0].strip()
+    return f"::{short}<{d}," in head or f"{len(short)}{short}ILi{d}E" in head
+
+
 def source_digest(names):
     h = hashlib.sha256()
     for n in names:
@@ -60,7 +76,8 @@ def traffic_from_counters(kernel):
         return None
     with open(COUNTERS) as f:
         c = json.load(f).get(kernel)
-    if not c or c.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
+    srcs = KERNEL_SOURCES.get(kernel) or DETAIL_COUNTERS.get(kernel, (None, None))[1]
+    if not c or not srcs or c.get("source_digest") != source_digest(srcs):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -144,8 +161,10 @@ def summarize_counters(fetch_csv, write_csv, copy_mib, out_json):
     out = {"copy_probe": {"kernel": ck, "mib": copy_mib, "fetch_factor": round(f_fetch, 4),
                           "write_factor": round(f_write, 4)}}
     rows = []
-    for short, srcs in KERNEL_SOURCES.items():
-        key = next((k for k in fetch if _headline_instance(k, short)), None)
+    wanted = [(short, srcs, lambda k, s=short: _headline_instance(k, s)) for short, srcs in KERNEL_SOURCES.items()]
+    wanted += [(name, srcs, lambda k, n=name: _detail_instance(k, n)) for name, (_, srcs) in DETAIL_COUNTERS.items()]
+    for short, srcs, match in wanted:
+        key = next((k for k in fetch if match(k)), None)
         if key is None or key not in write:
             continue
         fk, wkib = mean(fetch[key], "FETCH_SIZE"), mean(write[key], "WRITE_SIZE")
@@ -518,7 +537,9 @@ def head_dim_256_measurement(fa, torch, stream, with_oracle, reps=10):
            "tflops": round((fwd_fl + bwd_fl) / ((fwd_ms + pre_ms + kv_ms + dq_ms) * 1e-3) / 1e12, 3),
            "kernel_tflops": {n: round(f / (t * 1e-3) / 1e12, 3) for n, (t, f) in kernels.items()},
            "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_BF16_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": traffic_from_counters("bwd_bf16_kernel_d256") if dom == "bwd_bf16_kernel"
+                        else None}}
     if with_oracle:
         from oracle import ref
         rows = 256
@@ -591,7 +612,7 @@ def dropout_measurement(fa, torch, stream, w, q, k, v, do, ws, plain_fwd_ms, pla
            "fwd_over_plain": round(fwd_ms / plain_fwd_ms, 3), "bwd_over_plain": round(bwd_ms / plain_bwd_ms, 3),
            "roofline": {"kernel": "fwd_bf16_dropout_kernel", "bound": "mfma", "achieved": round(fwd_tf, 3),
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                        "traffic": None}}
+                        "traffic": traffic_from_counters("fwd_bf16_dropout_kernel")}}
     if with_oracle and x is not None:
         from oracle import dropout as drop
         from oracle import ref

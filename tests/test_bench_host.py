@@ -36,6 +36,21 @@ def test_headline_instance(name, short, want):
     assert bench._headline_instance(name, short) == want
 
 
+FWD_DROP = "void fa::fwd_bf16_dropout_kernel<128, true, 8, 64>(__bf16 const*)"
+KV_256 = "void fa::bwd_bf16_kernel<256, true, false>(__bf16 const*)"
+
+
+@pytest.mark.parametrize("name,key,want", [
+    (FWD_DROP, "fwd_bf16_dropout_kernel", True), (FWD, "fwd_bf16_dropout_kernel", False),
+    (KV_256, "bwd_bf16_kernel_d256", True), (KV, "bwd_bf16_kernel_d256", False),
+    ("void fa::bwd_bf16_dropout_kernel<256, true>(__bf16 const*)", "bwd_bf16_kernel_d256", False),
+    ("_ZN2fa15bwd_bf16_kernelILi256ELb1ELb0EEEvPKDF16b", "bwd_bf16_kernel_d256", True),
+    ("_ZN2fa23bwd_bf16_dropout_kernelILi256ELb1EEEvPKDF16b", "bwd_bf16_kernel_d256", False),
+])
+def test_detail_instance(name, key, want):
+    assert bench._detail_instance(name, key) == want
+
+
 def _write_pmc(path, rows):
     """rows: (dispatch, kernel, counter, value[, start, end])"""
     with open(path, "w", newline="") as f:
@@ -54,9 +69,11 @@ def test_counter_summary_calibrates_on_the_copy_probe(tmp_path):
     same factors (mean over its launches)."""
     mib = 16
     fetch = [(1, COPY, "FETCH_SIZE", mib * 1024 / 2), (2, FWD, "FETCH_SIZE", 1000.0), (3, FWD, "FETCH_SIZE", 3000.0),
-             (4, FWD_256, "FETCH_SIZE", 9e9), (5, KV, "FETCH_SIZE", 500.0)]
+             (4, FWD_256, "FETCH_SIZE", 9e9), (5, KV, "FETCH_SIZE", 500.0), (6, KV_256, "FETCH_SIZE", 700.0),
+             (7, FWD_DROP, "FETCH_SIZE", 80.0)]
     write = [(1, COPY, "WRITE_SIZE", 2 * mib * 1024), (2, FWD, "WRITE_SIZE", 100.0), (3, FWD, "WRITE_SIZE", 300.0),
-             (4, FWD_256, "WRITE_SIZE", 9e9), (5, KV, "WRITE_SIZE", 50.0)]
+             (4, FWD_256, "WRITE_SIZE", 9e9), (5, KV, "WRITE_SIZE", 50.0), (6, KV_256, "WRITE_SIZE", 70.0),
+             (7, FWD_DROP, "WRITE_SIZE", 8.0)]
     fp, wp, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "c.json"
     _write_pmc(fp, fetch)
     _write_pmc(wp, write)
@@ -69,6 +86,10 @@ def test_counter_summary_calibrates_on_the_copy_probe(tmp_path):
     assert c["bwd_bf16_kernel"]["hbm_bytes_per_launch"] == int((500.0 * 2 + 50.0) * 1024)
     assert c["fwd_bf16_kernel"]["source_digest"] == bench.source_digest(bench.KERNEL_SOURCES["fwd_bf16_kernel"])
     assert "bwd_dq_kernel" not in c
+    assert c["bwd_bf16_kernel_d256"]["hbm_bytes_per_launch"] == int((700.0 * 2 + 70.0) * 1024)
+    assert c["fwd_bf16_dropout_kernel"]["hbm_bytes_per_launch"] == int((80.0 * 2 + 8.0) * 1024)
+    assert c["bwd_bf16_kernel_d256"]["source_digest"] == bench.source_digest(
+        bench.DETAIL_COUNTERS["bwd_bf16_kernel_d256"][1])
 
 
 def test_traffic_is_dropped_once_the_sources_change(tmp_path, monkeypatch):
