@@ -46,11 +46,13 @@ KERNEL_SOURCES = {
 
 
 # Other instantiations whose HBM bytes the counter summary also records, for
-# the detail rooflines: key -> (template head and head dim, sources).
+# the detail rooflines: key -> (template name and head dim, sources).  The
+# FP8 forward's split mode (last template argument true) is another launch.
 DETAIL_COUNTERS = {
     "fwd_bf16_dropout_kernel": (("fwd_bf16_dropout_kernel", 128), ["fa_fwd_bf16.hip", "fa_common.h", "fa_dropout.h"]),
     "bwd_bf16_kernel_d256": (("bwd_bf16_kernel", 256),
                              ["fa_bwd_kv256.hip", "fa_bwd_kv_body.h", "fa_common.h", "fa_dropout.h"]),
+    "fwd_fp8_kernel": (("fwd_fp8_kernel", 128), ["fa_fwd_fp8.hip", "fa_common.h"]),
 }
 
 
@@ -58,6 +60,8 @@ def _detail_instance(name, key):
     """Whether a traced kernel name is the DETAIL_COUNTERS entry `key`."""
     (short, d), _ = DETAIL_COUNTERS[key]
     head = name.split("(")[0].strip()
+    if short == "fwd_fp8_kernel" and head.endswith("true>"):
+        return False
     return f"::{short}<{d}," in head or f"{len(short)}{short}ILi{d}E" in head
 
 
@@ -458,7 +462,7 @@ def fp8_measurement(fa, gen, torch, dev, stream, w, with_oracle, reps=30, oracle
            "us_per_call": round(ms * 1e3, 2), "calls": reps, "tflops": round(tf, 3),
            "roofline": {"kernel": "fwd_fp8_kernel", "bound": "mfma", "achieved": round(tf, 3),
                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                        "traffic": None}}
+                        "traffic": traffic_from_counters("fwd_fp8_kernel")}}
     if with_oracle:
         from oracle import ref
         got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()

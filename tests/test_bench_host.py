@@ -46,6 +46,8 @@ KV_256 = "void fa::bwd_bf16_kernel<256, true, false>(__bf16 const*)"
     ("void fa::bwd_bf16_dropout_kernel<256, true>(__bf16 const*)", "bwd_bf16_kernel_d256", False),
     ("_ZN2fa15bwd_bf16_kernelILi256ELb1ELb0EEEvPKDF16b", "bwd_bf16_kernel_d256", True),
     ("_ZN2fa23bwd_bf16_dropout_kernelILi256ELb1EEEvPKDF16b", "bwd_bf16_kernel_d256", False),
+    ("void fa::fwd_fp8_kernel<128, true, 4, false>(unsigned char const*)", "fwd_fp8_kernel", True),
+    ("void fa::fwd_fp8_kernel<128, true, 1, true>(unsigned char const*)", "fwd_fp8_kernel", False),
 ])
 def test_detail_instance(name, key, want):
     assert bench._detail_instance(name, key) == want
