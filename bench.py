@@ -46,23 +46,36 @@ KERNEL_SOURCES = {
 
 
 # Other instantiations whose HBM bytes the counter summary also records, for
-# the detail rooflines: key -> (template name and head dim, sources).  The
-# FP8 forward's split mode (last template argument true) is another launch.
+# the detail rooflines: key -> ((template name, head dim, split), sources).
+# split: True / False for the forwards' split mode (last template argument
+# true) or not, None where the kernel has no such argument.  A decode call is
+# a split forward plus the merge kernel.
+_FWD, _FP8 = ["fa_fwd_bf16.hip", "fa_common.h", "fa_dropout.h"], ["fa_fwd_fp8.hip", "fa_common.h"]
 DETAIL_COUNTERS = {
-    "fwd_bf16_dropout_kernel": (("fwd_bf16_dropout_kernel", 128), ["fa_fwd_bf16.hip", "fa_common.h", "fa_dropout.h"]),
-    "bwd_bf16_kernel_d256": (("bwd_bf16_kernel", 256),
+    "fwd_bf16_dropout_kernel": (("fwd_bf16_dropout_kernel", 128, None), _FWD),
+    "bwd_bf16_kernel_d256": (("bwd_bf16_kernel", 256, None),
                              ["fa_bwd_kv256.hip", "fa_bwd_kv_body.h", "fa_common.h", "fa_dropout.h"]),
-    "fwd_fp8_kernel": (("fwd_fp8_kernel", 128), ["fa_fwd_fp8.hip", "fa_common.h"]),
+    "fwd_fp8_kernel": (("fwd_fp8_kernel", 128, False), _FP8),
+    "fwd_bf16_kernel_split": (("fwd_bf16_kernel", 128, True), _FWD),
+    "fwd_fp8_kernel_split": (("fwd_fp8_kernel", 128, True), _FP8),
+    "fwd_merge_kernel": (("fwd_merge_kernel", 128, None), ["fa_aux.hip", "fa_common.h"]),
 }
 
 
 def _detail_instance(name, key):
     """Whether a traced kernel name is the DETAIL_COUNTERS entry `key`."""
-    (short, d), _ = DETAIL_COUNTERS[key]
+    (short, d, split), _ = DETAIL_COUNTERS[key]
     head = name.split("(")[0].strip()
-    if short == "fwd_fp8_kernel" and head.endswith("true>"):
+    if split is not None and head.endswith("true>") != split:
         return False
-    return f"::{short}<{d}," in head or f"{len(short)}{short}ILi{d}E" in head
+    return (f"::{short}<{d}," in head or f"::{short}<{d}>" in head or
+            (split is None and f"{len(short)}{short}ILi{d}E" in head))
+
+
+def decode_traffic(split_key):
+    """HBM bytes of one decode call: the split forward plus the merge."""
+    a, b = traffic_from_counters(split_key), traffic_from_counters("fwd_merge_kernel")
+    return None if a is None or b is None else a + b
 
 
 def source_digest(names):
@@ -335,7 +348,7 @@ def decode_measurement(fa, gen, torch, dev, stream, with_oracle, reps=50, oracle
            "us_per_call": round(ms * 1e3, 2), "calls": reps,
            "roofline": {"kernel": "fwd_bf16_kernel (split mode) + fwd_merge_kernel", "bound": "hbm",
                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": decode_traffic("fwd_bf16_kernel_split"),
                         "algorithmic_bytes": int(algo)}}
     if with_oracle:
         from oracle import ref
@@ -402,7 +415,8 @@ def decode_fp8_measurement(fa, gen, torch, dev, stream, with_oracle, reps=50, or
            "us_per_call": round(ms * 1e3, 2), "calls": reps,
            "roofline": {"kernel": "fwd_fp8_kernel (split mode) + fwd_merge_kernel", "bound": "hbm",
                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "algorithmic_bytes": int(algo)}}
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": decode_traffic("fwd_fp8_kernel_split"),
+                        "algorithmic_bytes": int(algo)}}
     if with_oracle:
         from oracle import ref
         got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()

@@ -48,9 +48,25 @@ KV_256 = "void fa::bwd_bf16_kernel<256, true, false>(__bf16 const*)"
     ("_ZN2fa23bwd_bf16_dropout_kernelILi256ELb1EEEvPKDF16b", "bwd_bf16_kernel_d256", False),
     ("void fa::fwd_fp8_kernel<128, true, 4, false>(unsigned char const*)", "fwd_fp8_kernel", True),
     ("void fa::fwd_fp8_kernel<128, true, 1, true>(unsigned char const*)", "fwd_fp8_kernel", False),
+    ("void fa::fwd_fp8_kernel<128, true, 1, true>(unsigned char const*)", "fwd_fp8_kernel_split", True),
+    (FWD_SPLIT, "fwd_bf16_kernel_split", True), (FWD, "fwd_bf16_kernel_split", False),
+    ("void fa::fwd_merge_kernel<128>(float const*)", "fwd_merge_kernel", True),
+    ("void fa::fwd_merge_kernel<64>(float const*)", "fwd_merge_kernel", False),
 ])
+
 def test_detail_instance(name, key, want):
     assert bench._detail_instance(name, key) == want
+
+
+def test_decode_traffic_is_split_plus_merge(tmp_path, monkeypatch):
+    path = tmp_path / "c.json"
+    dig = lambda k: bench.source_digest(bench.DETAIL_COUNTERS[k][1])
+    json.dump({"fwd_bf16_kernel_split": {"hbm_bytes_per_launch": 1000, "source_digest": dig("fwd_bf16_kernel_split")},
+               "fwd_merge_kernel": {"hbm_bytes_per_launch": 20, "source_digest": dig("fwd_merge_kernel")}},
+              open(path, "w"))
+    monkeypatch.setattr(bench, "COUNTERS", str(path))
+    assert bench.decode_traffic("fwd_bf16_kernel_split") == 1020
+    assert bench.decode_traffic("fwd_fp8_kernel_split") is None
 
 
 def _write_pmc(path, rows):
