@@ -23,8 +23,6 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_bwd_bf16.hip", "fa_bwd_kv256.hip", "fa_bwd_dq.hip", "fa_aux.hip",
            "fa_fp32.hip", "fa_api.cpp"]
-# sources built without VGPR-form MFMA results (see fa_bwd_kv256.hip)
-NO_VGPR_FORM = {"fa_bwd_kv256.hip"}
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.
 # -amdgpu-mfma-vgpr-form: MFMA results in VGPRs where they fit, so that fewer
@@ -39,11 +37,7 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-munsafe
 def _compile(src: str):
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
-    flags = DEVICE_FLAGS
-    if src in NO_VGPR_FORM:
-        i = flags.index("-amdgpu-mfma-vgpr-form")
-        flags = flags[:i - 1] + flags[i + 1:]   # drop "-mllvm -amdgpu-mfma-vgpr-form"
-    cmd = [HIPCC] + flags + ["-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
+    cmd = [HIPCC] + DEVICE_FLAGS + ["-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
