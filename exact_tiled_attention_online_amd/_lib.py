@@ -16,8 +16,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
 FA_BF16, FA_FP32 = 0, 1
 FA_LAYOUT_BHND, FA_LAYOUT_BNHD = 0, 1
+FA_DQ_HANDOFF, FA_DQ_RECOMPUTE, FA_DQ_ATOMIC = 0, 1, 2
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_preprocess", "fa_bwd_dkdv",
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_workspace_size", "fa_bwd_preprocess", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_fwd_fp8", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv",
            "fa_fwd_splitkv_fp8_workspace_bytes", "fa_fwd_splitkv_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
            "fa_strerror")
@@ -47,6 +48,8 @@ def load():
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, f, vp, sz, vp, i, i]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i, i]
@@ -89,6 +92,10 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, workspace
 
 def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
     return load().fa_bwd_workspace_bytes(B, H, N, d, dtype)
+
+
+def fa_bwd_workspace_size(B, H, N, d, causal, dtype, dq_method) -> int:
+    return load().fa_bwd_workspace_size(B, H, N, d, int(causal), dtype, dq_method)
 
 
 def fa_bwd_preprocess(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype,
@@ -234,23 +241,29 @@ def forward(q, k, v, causal: bool, scale: float, out=None, lse=None, stream=None
     return o, l
 
 
-def workspace(q, layout: int = FA_LAYOUT_BHND):
-    """A device byte buffer large enough for fa_bwd on q's shape and dtype."""
+def workspace(q, layout: int = FA_LAYOUT_BHND, causal: bool = False, method: int = FA_DQ_HANDOFF):
+    """A device byte buffer for fa_bwd on q's shape and dtype, sized for the dQ
+    method `method` (the library takes the hand-off whenever the buffer holds
+    it).  The hand-off buffer of a non-causal backward also serves a causal one.
+    Never smaller than fa_bwd_workspace_bytes (which, with FA_DQ_MODE=atomic,
+    holds the atomic method's accumulator)."""
     import torch
     B, H, N, d = _dims(q, layout)
-    n = fa_bwd_workspace_bytes(B, H, N, d, _dtype_code(q))
+    code = _dtype_code(q)
+    n = max(fa_bwd_workspace_size(B, H, N, d, causal, code, method), fa_bwd_workspace_bytes(B, H, N, d, code))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
 
 
 def backward(q, k, v, o, do, lse, causal: bool, scale: float, ws=None, grads=None, stream=None,
-             layout: int = FA_LAYOUT_BHND):
+             layout: int = FA_LAYOUT_BHND, method: int = FA_DQ_HANDOFF):
     """dQ, dK, dV of attention on device tensors in the named layout, given O
-    and LSE from forward."""
+    and LSE from forward.  Without `ws`, a workspace for `method` is allocated
+    (FA_DQ_RECOMPUTE: the smallest one)."""
     import torch
     B, H, N, d = _dims(q, layout)
     _check((q, k, v, o, do), q.shape)
     _check_buf(lse, (B, H, N), torch.float32, q.device, "lse")
-    ws = workspace(q, layout) if ws is None else _check_ws(ws, q.device)
+    ws = workspace(q, layout, causal, method) if ws is None else _check_ws(ws, q.device)
     if grads is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     else:
@@ -371,13 +384,13 @@ def forward_dropout(q, k, v, causal: bool, scale: float, p_drop: float, seed: in
 
 
 def backward_dropout(q, k, v, o, do, lse, causal: bool, scale: float, p_drop: float, seed: int, offset: int = 0,
-                     ws=None, grads=None, stream=None, layout: int = FA_LAYOUT_BHND):
+                     ws=None, grads=None, stream=None, layout: int = FA_LAYOUT_BHND, method: int = FA_DQ_HANDOFF):
     """dQ, dK, dV for the O, LSE of forward_dropout with the same arguments."""
     import torch
     B, H, N, d = _dims(q, layout)
     _check((q, k, v, o, do), q.shape)
     _check_buf(lse, (B, H, N), torch.float32, q.device, "lse")
-    ws = workspace(q, layout) if ws is None else _check_ws(ws, q.device)
+    ws = workspace(q, layout, causal, method) if ws is None else _check_ws(ws, q.device)
     if grads is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     else:

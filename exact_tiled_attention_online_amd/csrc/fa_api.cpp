@@ -15,6 +15,7 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr size_t kDsSink = 4096;   // the dS buffer's sink (fa::DsOut)
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -36,14 +37,50 @@ int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype, 
 
 fa::RowLayout row_layout(int H, int layout) { return fa::RowLayout{H, layout == FA_LAYOUT_BNHD ? 1 : 0}; }
 
+// Bytes of the dS hand-off buffer per (batch, head): query block i (64 rows)
+// holds 2i + 2 (causal) or ceil(N/32) (otherwise) slices of 4 KB.  The buffer
+// is followed by a 4 KB sink (fa::DsOut).
+size_t ds_head_bytes(int N, bool causal) {
+  const int nqb = (N + 63) / 64, nks = (N + 31) / 32;
+  return fa::ds_block_off(causal, nqb, nks);
+}
+
+// The bytes past the two per-row statistics that a dQ method needs: the fp32
+// accumulator of the atomic method, the dS buffer of the hand-off, nothing for
+// the recompute.  0 with ok = false where the method does not exist for the
+// arguments or the size does not fit in a size_t.
+size_t region_bytes(int method, int B, int H, int N, int d, bool causal, int dtype, bool* ok) {
+  *ok = true;
+  const size_t BH = (size_t)B * H;
+  if (method == FA_DQ_RECOMPUTE) return 0;
+  if (dtype != FA_BF16) {
+    *ok = false;
+    return 0;
+  }
+  if (method == FA_DQ_ATOMIC) {
+    if (d != 64 && d != 128) *ok = false;
+    return *ok ? round_up(BH * N * d * sizeof(float)) : 0;
+  }
+  if (method == FA_DQ_HANDOFF) {
+    const size_t hb = ds_head_bytes(N, causal);
+    if (hb > ((size_t)1 << 62) / BH) {
+      *ok = false;
+      return 0;
+    }
+    return round_up(BH * hb) + kDsSink;
+  }
+  *ok = false;
+  return 0;
+}
+
 struct Workspace {
   float* ndrow;   // -D per query row
   float* nlse;    // -LSE / scale per query row
-  float* dq_acc;  // bf16 only
-  size_t bytes;
+  char* region;   // dQ accumulator (atomic) or dS buffer (hand-off)
+  size_t bytes;   // total for the method (0: the method does not exist here)
 };
 
-Workspace carve(void* base, int B, int H, int N, int d, int dtype) {
+Workspace carve(void* base, int B, int H, int N, int d, bool causal, int dtype, int method) {
   const size_t rows = (size_t)B * H * N;
   Workspace w{};
   char* p = static_cast<char*>(base);
@@ -52,27 +89,38 @@ Workspace carve(void* base, int B, int H, int N, int d, int dtype) {
   off += round_up(rows * sizeof(float));
   w.nlse = reinterpret_cast<float*>(p + off);
   off += round_up(rows * sizeof(float));
-  w.dq_acc = nullptr;
-  if (dtype == FA_BF16) {
-    w.dq_acc = reinterpret_cast<float*>(p + off);
-    off += round_up(rows * d * sizeof(float));
-  }
-  w.bytes = off;
+  w.region = p + off;
+  bool ok = false;
+  const size_t extra = region_bytes(method, B, H, N, d, causal, dtype, &ok);
+  w.bytes = ok ? off + extra : 0;
   return w;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
-// dQ path of the bf16 backward: the query-block-outer kernel (default), or
-// fp32 atomics from the key/value-outer kernel when FA_DQ_MODE=atomic (d = 64
-// and 128 only; d = 96 and 256 always take the default).
-bool dq_atomic_mode(int d) {
+// The dQ method a backward call takes.  FA_DQ_MODE=atomic (bf16, d = 64 or
+// 128, not with dropout) or FA_DQ_MODE=recompute force one, for A/B
+// measurement; otherwise the hand-off when the workspace holds its buffer, and
+// the recompute kernel when it does not.  The choice depends only on the
+// arguments and the environment, so the three stage calls of one backward
+// agree.
+int dq_method(int B, int H, int N, int d, bool causal, int dtype, size_t workspace_bytes, bool dropout) {
+  if (dtype != FA_BF16) return FA_DQ_RECOMPUTE;
   const char* m = std::getenv("FA_DQ_MODE");
-  return (d == 64 || d == 128) && m && std::strcmp(m, "atomic") == 0;
+  if (m && std::strcmp(m, "atomic") == 0 && !dropout && (d == 64 || d == 128)) return FA_DQ_ATOMIC;
+  if (m && std::strcmp(m, "recompute") == 0) return FA_DQ_RECOMPUTE;
+  const Workspace h = carve(nullptr, B, H, N, d, causal, dtype, FA_DQ_HANDOFF);
+  return (h.bytes != 0 && workspace_bytes >= h.bytes) ? FA_DQ_HANDOFF : FA_DQ_RECOMPUTE;
 }
 
-bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d, int dtype) {
-  return ws && aligned(ws, kAlign) && bytes >= carve(nullptr, B, H, N, d, dtype).bytes;
+bool workspace_ok(const void* ws, size_t bytes, int B, int H, int N, int d, bool causal, int dtype, int method) {
+  const size_t need = carve(nullptr, B, H, N, d, causal, dtype, method).bytes;
+  return ws && aligned(ws, kAlign) && need != 0 && bytes >= need;
+}
+
+fa::DsOut ds_out(const Workspace& w, int B, int H, int N, bool causal) {
+  const size_t hb = ds_head_bytes(N, causal);
+  return fa::DsOut{w.region, hb, (N + 31) / 32, w.region + round_up((size_t)B * H * hb)};
 }
 
 // Key ranges of the split forwards (tiles of 32 keys for bf16, 64 for FP8).
@@ -143,11 +191,16 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                                        causal != 0, scale, row_layout(H, layout), s));
 }
 
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype, int dq_method) {
+  if (check_shape(B, H, N, d, causal, 1.f, dtype, FA_LAYOUT_BHND) != FA_OK) return 0;
+  return carve(nullptr, B, H, N, d, causal != 0, dtype, dq_method).bytes;
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
-  if (B < 1 || H < 1 || N < 1 || (dtype != FA_BF16 && dtype != FA_FP32) ||
-      (d != 64 && d != 96 && d != 128 && !(d == 256 && dtype == FA_BF16)))
-    return 0;
-  return carve(nullptr, B, H, N, d, dtype).bytes;
+  if (check_shape(B, H, N, d, 0, 1.f, dtype, FA_LAYOUT_BHND) != FA_OK) return 0;
+  // the recompute method's statistics, or with FA_DQ_MODE=atomic the
+  // accumulator too; the hand-off buffer depends on causal (fa_bwd_workspace_size)
+  return carve(nullptr, B, H, N, d, false, dtype, dq_method(B, H, N, d, false, dtype, 0, false)).bytes;
 }
 
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
@@ -157,9 +210,13 @@ int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, in
   const int st = check_shape(B, H, N, d, 0, scale, dtype, layout);
   if (st != FA_OK) return st;
   if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(lse, 4)) return FA_ERR_INVALID;
-  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
-  const Workspace w = carve(workspace, B, H, N, d, dtype);
-  float* dq_acc = (dtype == FA_BF16 && dq_atomic_mode(d)) ? w.dq_acc : nullptr;
+  // the statistics sit at the same place for every method; only the atomic
+  // method needs more here (its accumulator is cleared)
+  const bool atomic = dq_method(B, H, N, d, false, dtype, 0, false) == FA_DQ_ATOMIC;
+  const int method = atomic ? FA_DQ_ATOMIC : FA_DQ_RECOMPUTE;
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, false, dtype, method)) return FA_ERR_WORKSPACE;
+  const Workspace w = carve(workspace, B, H, N, d, false, dtype, method);
+  float* dq_acc = atomic ? reinterpret_cast<float*>(w.region) : nullptr;
   return hip_status(fa::launch_bwd_pre(o, dO, lse, w.ndrow, w.nlse, dq_acc, B * H, N, d, scale,
                                        dtype == FA_FP32, row_layout(H, layout), static_cast<hipStream_t>(stream)));
 }
@@ -173,16 +230,19 @@ int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, con
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dk, 16) ||
       !aligned(dv, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
-  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
-  const Workspace w = carve(workspace, B, H, N, d, dtype);
+  const int method = dq_method(B, H, N, d, causal != 0, dtype, workspace_bytes, false);
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, dtype, method)) return FA_ERR_WORKSPACE;
+  const Workspace w = carve(workspace, B, H, N, d, causal != 0, dtype, method);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == FA_FP32)
     return hip_status(fa::launch_bwd_kv_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                             static_cast<const float*>(v), static_cast<const float*>(dO), lse,
                                             w.ndrow, static_cast<float*>(dk), static_cast<float*>(dv), B * H, N,
                                             d, causal != 0, scale, row_layout(H, layout), s));
-  return hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.nlse, w.ndrow, w.dq_acc, dk, dv, B * H, N, d,
-                                        causal != 0, scale, dq_atomic_mode(d), row_layout(H, layout), s));
+  const fa::DsOut ds = method == FA_DQ_HANDOFF ? ds_out(w, B, H, N, causal != 0) : fa::DsOut{};
+  return hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.nlse, w.ndrow, reinterpret_cast<float*>(w.region), dk, dv,
+                                        B * H, N, d, causal != 0, scale, method == FA_DQ_ATOMIC,
+                                        row_layout(H, layout), s, nullptr, ds));
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq, int B,
@@ -194,18 +254,22 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dq, 16) ||
       !aligned(lse, 4))
     return FA_ERR_INVALID;
-  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
-  const Workspace w = carve(workspace, B, H, N, d, dtype);
+  const int method = dq_method(B, H, N, d, causal != 0, dtype, workspace_bytes, false);
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, dtype, method)) return FA_ERR_WORKSPACE;
+  const Workspace w = carve(workspace, B, H, N, d, causal != 0, dtype, method);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const fa::RowLayout lay = row_layout(H, layout);
   if (dtype == FA_FP32)
     return hip_status(fa::launch_bwd_q_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                            static_cast<const float*>(v), static_cast<const float*>(dO), lse,
-                                           w.ndrow, static_cast<float*>(dq), B * H, N, d, causal != 0, scale,
-                                           row_layout(H, layout), s));
-  if (dq_atomic_mode(d))
-    return hip_status(fa::launch_dq_convert(w.dq_acc, dq, B * H, N, d, scale, row_layout(H, layout), s));
-  return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.nlse, w.ndrow, dq, B * H, N, d, causal != 0, scale,
-                                      row_layout(H, layout), s));
+                                           w.ndrow, static_cast<float*>(dq), B * H, N, d, causal != 0, scale, lay,
+                                           s));
+  if (method == FA_DQ_ATOMIC)
+    return hip_status(fa::launch_dq_convert(reinterpret_cast<float*>(w.region), dq, B * H, N, d, scale, lay, s));
+  if (method == FA_DQ_HANDOFF)
+    return hip_status(fa::launch_bwd_dq_ds(ds_out(w, B, H, N, causal != 0), k, dq, B * H, N, d, causal != 0, scale, lay,
+                                           s));
+  return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.nlse, w.ndrow, dq, B * H, N, d, causal != 0, scale, lay, s));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
@@ -218,7 +282,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
-  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, dtype,
+                    dq_method(B, H, N, d, causal != 0, dtype, workspace_bytes, false)))
+    return FA_ERR_WORKSPACE;
   int r = fa_bwd_preprocess(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype, layout);
   if (r != FA_OK) return r;
   r = fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype,
@@ -261,16 +327,21 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
-  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, FA_BF16)) return FA_ERR_WORKSPACE;
-  const Workspace w = carve(workspace, B, H, N, d, FA_BF16);
+  const int method = dq_method(B, H, N, d, causal != 0, FA_BF16, workspace_bytes, true);
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, FA_BF16, method)) return FA_ERR_WORKSPACE;
+  const Workspace w = carve(workspace, B, H, N, d, causal != 0, FA_BF16, method);
   const fa::RowLayout lay = row_layout(H, layout);
   const fa::DropArgs dr = drop_args(drop_t, seed, offset);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const fa::DsOut ds = method == FA_DQ_HANDOFF ? ds_out(w, B, H, N, causal != 0) : fa::DsOut{};
   int r = hip_status(fa::launch_bwd_pre(o, dO, lse, w.ndrow, w.nlse, nullptr, B * H, N, d, scale, false, lay, s));
   if (r != FA_OK) return r;
   r = hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.nlse, w.ndrow, nullptr, dk, dv, B * H, N, d, causal != 0,
-                                     scale, false, lay, s, &dr));
+                                     scale, false, lay, s, &dr, ds));
   if (r != FA_OK) return r;
+  // the dS in the buffer already carries the mask: dQ = dS K as without dropout
+  if (method == FA_DQ_HANDOFF)
+    return hip_status(fa::launch_bwd_dq_ds(ds, k, dq, B * H, N, d, causal != 0, scale, lay, s));
   return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.nlse, w.ndrow, dq, B * H, N, d, causal != 0, scale, lay, s,
                                       &dr));
 }

@@ -1,6 +1,6 @@
 // fa_bwd_kv_body.h -- the key/value-block-outer backward kernel (dK, dV), bf16
 // inputs/outputs, fp32 accumulation; instantiated by fa_bwd_bf16.hip (d <= 128)
-// and fa_bwd_kv256.hip (d = 256, built without VGPR-form MFMA results).
+// and fa_bwd_kv256.hip (d = 256).
 //
 // Key/value-block outer, query-block inner (page
 // "flash-attention-backpropagation" (aiqz.cc), section QKV梯度): one
@@ -21,6 +21,20 @@
 //                                  index across lanes); each wave takes a
 //                                  32-column slice of d with K^T held in
 //                                  registers; fp32 atomics into an accumulator.
+// In the hand-off variant (DSO) the bf16 dS operand of every computed block is
+// also stored to a buffer (layout: DsOut in fa_launch.h), from which a separate
+// kernel forms dQ = dS K without recomputing S and dP.  Each query tile's
+// stores are issued in the slot right after its dS is packed (holding dS in
+// registers into the next step instead made the compiler's register use jump
+// past the file), and the barrier closing the step does not wait for them:
+// vector memory operations retire in issue order, so once at most the step's
+// four stores are outstanding the prefetch issued before them has landed in
+// LDS; the barrier waits for that and for the wave's LDS reads only (a
+// workgroup barrier with a full fence would wait for the stores too).  Every
+// wave issues exactly four stores per step (one whose keys all lie past the
+// block's queries writes zeros to a sink), so that this wait is the same on
+// every path and the compiler's own count of outstanding operations stays
+// exact.
 // The S and dP accumulators start from -LSE/scale and -D of their query rows,
 // so they end as S - LSE/scale and dP - D.
 // The accumulators hold fp32 and are converted once at write-back (page
@@ -57,13 +71,14 @@ FA_DEV int ds_off(int row, int col) {
 // with keep mask Z and keep scale s, dV = s (P^ o Z)^T dO and
 // dS = P^ o (s (dP~ - D) + (s - 1) D) where kept, P^ o (-D) where dropped,
 // dP~ - D being what the dP accumulator holds).
-template <int D, bool CAUSAL, bool DQA, bool DROP>
+template <int D, bool CAUSAL, bool DQA, bool DROP, bool DSO>
 FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                           const bf16* __restrict__ dO, const float* __restrict__ NLSE,
                           const float* __restrict__ NDR, float* __restrict__ dQacc, bf16* __restrict__ dK,
                           bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, RowLayout lay,
-                          DropArgs dr) {
-  static_assert(!(DQA && DROP), "the dropout backward takes dQ from the query-outer kernel");
+                          DropArgs dr, DsOut dso) {
+  static_assert(!(DQA && DROP), "the dropout backward takes dQ from another kernel");
+  static_assert(!(DQA && DSO), "dQ comes from atomics or from the hand-off, not both");
   // DH waves share a 32-key slice, each accumulating dK, dV for D/DH columns
   // (d = 256: two, so that a wave's registers hold K, V and half of dK, dV);
   // a workgroup of 4 waves then owns BC = 128/DH keys
@@ -137,6 +152,12 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
     const int kvw = kv0 + 32 * slice;        // first key row of this wave
     const int kvrow = kvw + l32;             // key row of this lane in the S accumulators
     const int krow = 32 * slice + l32;       // the same row within the block
+
+    // dS hand-off: the wave's slice column within its head.  At d = 256 both
+    // waves of a slice compute the same dS (the same instructions on the same
+    // operands) and both store it: the second write repeats the first's bytes.
+    char* dsw = nullptr;
+    if constexpr (DSO) dsw = dso.buf + (size_t)head * dso.head_bytes + (size_t)(kv0 / 32 + wave_u / DH) * 4096u;
 
     // ---- K block into LDS (for K^T), then the register operands -------------
     if constexpr (DQA) {
@@ -268,8 +289,14 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
       if (k > 0) dq_product(i - dir, b ? sS0 : sS1);
       __builtin_amdgcn_sched_barrier(0);
       const int qb0 = i * BR;
-      // this wave's keys are all later than all queries of the block: P^ = 0
-      const bool skip = (kvw >= N) || (CAUSAL && qb0 + BR - 1 < kvw);
+      // this wave's keys are all later than all queries of the block: P^ = 0.
+      // The hand-off variant runs such a step anyway (masked, it yields
+      // dS = 0; the waves of a workgroup move in step, so it costs no time)
+      // and stores to the sink, so that every path issues the same four
+      // stores, which its barrier below counts on.
+      const bool dead = (kvw >= N) || (CAUSAL && qb0 + BR - 1 < kvw);
+      const bool skip = DSO ? false : dead;
+      bf16x8 dsv[BR / 16];   // the hand-off: this step's dS operands
       // one pass over the block; MASK: apply the causal / tail mask (a
       // compile-time variant, so the common unmasked path carries no mask code)
       auto compute = [&](auto mc) {
@@ -409,6 +436,10 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
           if (g >= 2 * KS && g < 2 * KS + EC) elem_chunk(1, g - 2 * KS);
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DSO) {
+#pragma unroll
+          for (int st = 0; st < BR / 16; ++st) dsv[st] = da[st];
+        }
         // dS (bf16) to LDS, [key][query], for the dQ product of the atomic variant
         if constexpr (DQA) {
 #pragma unroll
@@ -433,7 +464,22 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
           *reinterpret_cast<u32x2*>(&St[ds_off(krow, 16 * st + 8 + 4 * h)]) = u32x2{0, 0};
         }
       }
-      __syncthreads();
+      if constexpr (DSO) {
+        char* p = (dead ? dso.sink : dsw + ds_block_off(CAUSAL, i, dso.nks)) + 16 * ln;
+#pragma unroll
+        for (int st = 0; st < BR / 16; ++st) *reinterpret_cast<bf16x8*>(p + 1024 * st) = dsv[st];
+        // s_waitcnt vmcnt(4) lgkmcnt(0): all but the four stores (expcnt
+        // never waited for).  No fence: a release fence covers the loads into
+        // LDS and so waits for every memory operation; the empty asm
+        // statements with a memory clobber keep the compiler from moving
+        // memory accesses across the barrier.
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0x0074);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      } else {
+        __syncthreads();
+      }
     };
 
     if (nsteps > 0) {
@@ -498,33 +544,56 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
     float* __restrict__ dQacc, bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb,
     float scale, float c, RowLayout lay) {
-  bwd_bf16_body<D, CAUSAL, DQA, false>(Q, K, V, dO, NLSE, NDR, dQacc, dK, dV, BH, N, nqb, scale, c, lay,
-                                       DropArgs{});
+  bwd_bf16_body<D, CAUSAL, DQA, false, false>(Q, K, V, dO, NLSE, NDR, dQacc, dK, dV, BH, N, nqb, scale, c, lay,
+                                              DropArgs{}, DsOut{});
 }
 
+// the same, also storing dS to the hand-off buffer
 template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_bf16_ds_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, RowLayout lay,
+    DsOut dso) {
+  bwd_bf16_body<D, CAUSAL, false, false, true>(Q, K, V, dO, NLSE, NDR, nullptr, dK, dV, BH, N, nqb, scale, c,
+                                               lay, DropArgs{}, dso);
+}
+
+template <int D, bool CAUSAL, bool DSO>
 __global__ __launch_bounds__(256, 1) void bwd_bf16_dropout_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, RowLayout lay,
-    DropArgs dr) {
-  bwd_bf16_body<D, CAUSAL, false, true>(Q, K, V, dO, NLSE, NDR, nullptr, dK, dV, BH, N, nqb, scale, c, lay, dr);
+    DropArgs dr, DsOut dso) {
+  bwd_bf16_body<D, CAUSAL, false, true, DSO>(Q, K, V, dO, NLSE, NDR, nullptr, dK, dV, BH, N, nqb, scale, c, lay,
+                                             dr, dso);
 }
 
 template <int D, bool CAUSAL, bool DQA>
 static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v, const void* dO,
                                     const float* nlse, const float* ndrow, float* dq_acc, void* dk,
                                     void* dv, int BH, int N, float scale, RowLayout lay, hipStream_t stream,
-                                    const DropArgs* drop) {
+                                    const DropArgs* drop, DsOut ds) {
   constexpr int BC = D == 256 ? 64 : 128;   // keys per workgroup
   const int nkb = (N + BC - 1) / BC, nqb = (N + 63) / 64;
   const int items = CAUSAL ? (nkb + 1) / 2 : nkb;
   const dim3 grid((unsigned)(items * BH)), block(256);
   if constexpr (!DQA) {
     if (drop) {
-      hipLaunchKernelGGL((bwd_bf16_dropout_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH,
-                         N, nqb, scale, scale * kLog2e, lay, *drop);
+      if (ds.buf)
+        hipLaunchKernelGGL((bwd_bf16_dropout_kernel<D, CAUSAL, true>), grid, block, 0, stream, (const bf16*)q,
+                           (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH,
+                           N, nqb, scale, scale * kLog2e, lay, *drop, ds);
+      else
+        hipLaunchKernelGGL((bwd_bf16_dropout_kernel<D, CAUSAL, false>), grid, block, 0, stream, (const bf16*)q,
+                           (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH,
+                           N, nqb, scale, scale * kLog2e, lay, *drop, DsOut{});
+      return hipGetLastError();
+    }
+    if (ds.buf) {
+      hipLaunchKernelGGL((bwd_bf16_ds_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
+                         (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH, N, nqb, scale,
+                         scale * kLog2e, lay, ds);
       return hipGetLastError();
     }
   }

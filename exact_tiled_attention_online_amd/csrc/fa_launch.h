@@ -43,6 +43,25 @@ struct DropArgs {
   float keep_scale;   // 256 / (256 - t)
 };
 
+// dS hand-off buffer, written by the key/value-outer backward kernel and
+// streamed by the dS K kernel.  Unit: a 1 KB micro-tile, dS of 32 keys x 16
+// queries as the 64 lanes of a wave hold it after the elementwise step: lane
+// key + 32h holds 16 bytes, queries 16st + 4h + 0..3 then 16st + 8 + 4h + 0..3
+// (st: the 16-query group within a 64-query block).  Per (batch, head), query
+// block i (64 rows) holds its 32-key slices ks in order, 4 KB each (micro-tiles
+// st = 0..3): causal slices 0..2i+1 (those reaching the diagonal; the last
+// block may leave its last slot unused), otherwise slices 0..nks-1.  Entries of
+// masked (query, key) pairs inside a stored slice hold 0.
+struct DsOut {
+  char* buf;          // the buffer (null: no hand-off)
+  size_t head_bytes;  // bytes per (batch, head): ds_block_off(causal, nqb, nks)
+  int nks;            // 32-key slices per head, ceil(N / 32)
+  char* sink;         // 4 KB that absorb the stores of waves with no dS to store
+};
+__host__ __device__ __forceinline__ size_t ds_block_off(bool causal, int i, int nks) {
+  return causal ? (size_t)i * (size_t)(i + 1) * 4096u : (size_t)i * (size_t)nks * 4096u;
+}
+
 // bf16 forward: O, LSE; with `drop`, O uses the dropped probabilities (LSE
 // does not change).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
@@ -82,18 +101,24 @@ hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float
                           hipStream_t stream);
 
 // bf16 key/value-block-outer backward: dK, dV written; with dq_atomic, dQ is
-// also accumulated (fp32, unscaled dS K) into dq_acc with atomics.  With
-// `drop` (only without dq_atomic), the gradients of the dropout forward.
+// also accumulated (fp32, unscaled dS K) into dq_acc with atomics; with a
+// non-null ds.buf (not with dq_atomic), every computed dS block is stored to
+// the hand-off buffer.  With `drop` (only without dq_atomic), the gradients of
+// the dropout forward.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dO,
                            const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
                            int BH, int N, int d, bool causal, float scale, bool dq_atomic, RowLayout lay,
-                           hipStream_t stream, const DropArgs* drop = nullptr);
+                           hipStream_t stream, const DropArgs* drop = nullptr, DsOut ds = DsOut{});
 
-// The same at d = 256 (no atomic-dQ or dropout form), from its own
-// translation unit.
+// The same at d = 256 (no atomic-dQ form), from its own translation unit.
 hipError_t launch_bwd_kv256(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                             const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
-                            RowLayout lay, hipStream_t stream, const DropArgs* drop = nullptr);
+                            RowLayout lay, hipStream_t stream, const DropArgs* drop, DsOut ds);
+
+// dQ = bf16(scale * dS K) from the hand-off buffer (query-block outer, no
+// recompute, no atomics).
+hipError_t launch_bwd_dq_ds(DsOut ds, const void* k, void* dq, int BH, int N, int d, bool causal, float scale,
+                            RowLayout lay, hipStream_t stream);
 
 // bf16 query-block-outer dQ kernel: dQ = bf16(scale * dS K), no atomics;
 // with `drop`, the dQ of the dropout forward.

@@ -66,6 +66,35 @@ typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
 typedef enum { FA_LAYOUT_BHND = 0, FA_LAYOUT_BNHD = 1 } fa_layout;
 
 /*
+ * How the bf16 backward forms dQ = scale * dS K (page
+ * "flash-attention-backpropagation", section QKV梯度):
+ *   FA_DQ_HANDOFF   the key/value-outer kernel stores the bf16 dS of each pair
+ *                   of blocks, the operand its single recompute of P^ produced
+ *                   (page "gsyq.cn news/1372000", 踩坑二: one recompute per
+ *                   pair of blocks feeds all three gradients), into the
+ *                   workspace; a query-outer kernel streams it and forms
+ *                   dS K.  Fastest; needs a workspace of 2 bytes per
+ *                   (query, key) pair the mask keeps (rounded up to 64 x 32
+ *                   tiles): about B*H*N^2 bytes causal, 2*B*H*N^2 otherwise.
+ *   FA_DQ_RECOMPUTE a query-outer kernel recomputes S, P^, dP and dS per pair
+ *                   of blocks and forms dS K in registers; needs only the
+ *                   per-row statistics.
+ *   FA_DQ_ATOMIC    the key/value-outer kernel adds dS K into an fp32
+ *                   accumulator in the workspace with atomics, and a last
+ *                   kernel converts it (d = 64 and 128, no dropout; measured
+ *                   slowest, kept for comparison).
+ * fa_bwd, its stages and fa_bwd_dropout take the hand-off whenever
+ * workspace_bytes >= fa_bwd_workspace_size(..., FA_DQ_HANDOFF) for their
+ * B, H, N, d and causal, and the recompute otherwise.  The environment
+ * variable FA_DQ_MODE=recompute forces the recompute, and FA_DQ_MODE=atomic
+ * the atomic method (where it exists; the workspace must then hold its
+ * accumulator).  The methods differ only in rounding (they round S, P^ and dS
+ * at different points and sum in different orders); the hand-off and the
+ * recompute are each bitwise reproducible, the atomic method is not.
+ */
+typedef enum { FA_DQ_HANDOFF = 0, FA_DQ_RECOMPUTE = 1, FA_DQ_ATOMIC = 2 } fa_dq_method;
+
+/*
  * Forward pass.  Reads q, k, v; writes o (same layout and dtype) and
  * lse ([B,H,N], float).  One workgroup owns a block of query rows and streams
  * the key/value blocks through LDS, applying the online-softmax update of
@@ -78,12 +107,22 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            void* stream, int dtype, int layout);
 
 /*
- * Bytes of device workspace fa_bwd needs for this shape: the fp32 row term
- * D [B,H,N], the ledger in base 2 [B,H,N] and, for bf16, room for an fp32
- * dQ accumulator [B,H,N,d] (used only with FA_DQ_MODE=atomic at d = 64 or
- * 128).  The caller allocates it (any 256-byte-aligned device buffer); its
- * contents on entry do not matter.  Returns 0 for a non-positive size or a
- * head dim or dtype that fa_bwd has no kernel for.
+ * Bytes of device workspace fa_bwd needs for this shape with the given dQ
+ * method (fa_dq_method): the fp32 row term D [B,H,N] and the ledger divided by
+ * scale [B,H,N], plus the dS buffer (FA_DQ_HANDOFF; its size depends on
+ * causal) or the fp32 dQ accumulator [B,H,N,d] (FA_DQ_ATOMIC).  The caller
+ * allocates it (any 256-byte-aligned device buffer); its contents on entry do
+ * not matter.  Returns 0 for arguments fa_bwd rejects, for a method that does
+ * not exist there (FA_DQ_HANDOFF and FA_DQ_ATOMIC are bf16 only, FA_DQ_ATOMIC
+ * d = 64 and 128 only) and for a size beyond 2^62 bytes.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype, int dq_method);
+
+/*
+ * The smallest workspace of fa_bwd: fa_bwd_workspace_size(B, H, N, d, causal,
+ * dtype, FA_DQ_RECOMPUTE) (which does not depend on causal), or with
+ * FA_DQ_MODE=atomic set the atomic method's.  A backward given this much takes
+ * the recompute method.  Returns 0 for arguments fa_bwd rejects.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
 
@@ -92,9 +131,10 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
  * with the same q, k, v, causal and scale (the recompute of P^ is exact only
  * for the ledger of that forward: page "flash-attention-backpropagation",
  * section 数值稳定).  Writes dq, dk, dv (same layout and dtype as q).  Uses `workspace`
- * (at least fa_bwd_workspace_bytes bytes) as scratch; it is fully overwritten.
- * Kernels, in stream order: D = rowsum(dO o O), the key/value-block-outer
- * kernel (dK, dV), the query-block-outer kernel (dQ).
+ * (at least fa_bwd_workspace_bytes bytes; the dQ method follows from its size,
+ * see fa_dq_method) as scratch; it is overwritten.  Kernels, in stream order:
+ * D = rowsum(dO o O), the key/value-block-outer kernel (dK, dV, and the dS
+ * buffer of the hand-off), the query-block-outer kernel (dQ).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const void* dO, const float* lse, void* dq, void* dk, void* dv,
@@ -112,14 +152,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *   start their S and dP accumulators from these values).  scale must be the
  *   one later passed to fa_bwd_dkdv and fa_bwd_dq.
  * fa_bwd_dkdv: the key/value-block-outer kernel (section QKV梯度): recomputes
- *   P^ and dS per pair of blocks and writes dk and dv.
- * fa_bwd_dq: the query-block-outer kernel: recomputes S, P^, dP, dS per pair
- *   of blocks and writes dq (no atomics).
- * Argument meaning, checks and errors are those of fa_bwd.  With the
- * environment variable FA_DQ_MODE=atomic (bf16 only) the dQ products run
- * inside fa_bwd_dkdv instead, as fp32 atomic adds into the workspace, and
- * fa_bwd_dq converts that accumulator (d = 64 and 128; d = 96 and 256 ignore
- * the variable); the default is the query-outer kernel, which measured faster.
+ *   P^ and dS per pair of blocks and writes dk and dv (with the hand-off also
+ *   the dS buffer; with the atomic method also the dQ accumulator).
+ * fa_bwd_dq: dq from the dS buffer (hand-off), by the recomputing
+ *   query-block-outer kernel, or by converting the accumulator (atomic).
+ * Argument meaning, checks and errors are those of fa_bwd; the three calls
+ * must get the same workspace and workspace_bytes, so that they take the same
+ * dQ method.
  */
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
                       float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype,
@@ -159,10 +198,10 @@ int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const
  *
  * bf16 only (no dtype argument); d in {64, 96, 128, 256}.  B, H, N, causal,
  * scale, layout, pointers, alignment, ownership, streams and errors are those
- * of fa_fwd and fa_bwd; the workspace is fa_bwd's
- * (fa_bwd_workspace_bytes(B, H, N, d, FA_BF16)).  drop_t outside 0 .. 255 is
- * FA_ERR_INVALID.  dQ always comes from the query-outer kernel (FA_DQ_MODE is
- * ignored).
+ * of fa_fwd and fa_bwd; the workspace is fa_bwd's, and its size chooses the
+ * hand-off (the stored dS carries the mask) or the recompute (which
+ * regenerates it) as there.  drop_t outside 0 .. 255 is FA_ERR_INVALID.
+ * FA_DQ_MODE=atomic is ignored (there is no atomic dropout kernel).
  */
 int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int N, int d, int causal, float scale,

@@ -46,15 +46,16 @@ def to_np(t, layout=0):
     return a
 
 
-def run_gpu(x, dtype, causal, scale, bwd=True, stream=None, layout=0):
-    """fwd (+ bwd) on device; returns dict of fp64 numpy arrays in [B,H,N,d]
-    order whatever the device layout."""
+def run_gpu(x, dtype, causal, scale, bwd=True, stream=None, layout=0, method=fa.FA_DQ_HANDOFF):
+    """fwd (+ bwd, with a workspace sized for the dQ method `method`) on
+    device; returns dict of fp64 numpy arrays in [B,H,N,d] order whatever the
+    device layout."""
     import torch
     q, k, v, do = (to_dev(x[n], dtype, layout) for n in ("q", "k", "v", "do"))
     o, lse = fa.forward(q, k, v, causal, scale, stream=stream, layout=layout)
     out = {"o_dev": o, "lse_dev": lse}
     if bwd:
-        dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal, scale, stream=stream, layout=layout)
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal, scale, stream=stream, layout=layout, method=method)
         out.update(dq_dev=dq, dk_dev=dk, dv_dev=dv)
     torch.cuda.synchronize()
     res = {"o": to_np(o, layout), "lse": to_np(lse)}

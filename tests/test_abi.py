@@ -80,16 +80,51 @@ def test_strerror():
 
 
 @needs_lib
-def test_workspace_size():
+def test_workspace_size(monkeypatch):
+    monkeypatch.delenv("FA_DQ_MODE", raising=False)
     rows = 1 * 32 * 8192
+    # the smallest workspace: the two per-row statistics (recompute method)
     bf = fa.fa_bwd_workspace_bytes(1, 32, 8192, 128, fa.FA_BF16)
-    assert bf == 2 * rows * 4 + rows * 128 * 4
+    assert bf == 2 * rows * 4
     f32 = fa.fa_bwd_workspace_bytes(1, 1, 128, 64, fa.FA_FP32)
     assert f32 == 2 * 512
     assert fa.fa_bwd_workspace_bytes(1, 1, 100, 64, fa.FA_BF16) % 256 == 0
     assert fa.fa_bwd_workspace_bytes(0, 1, 128, 64, fa.FA_BF16) == 0
     assert fa.fa_bwd_workspace_bytes(1, 1, 128, 80, fa.FA_BF16) == 0
-    assert fa.fa_bwd_workspace_bytes(1, 2, 100, 96, fa.FA_BF16) == round_up(200 * 4) * 2 + round_up(200 * 96 * 4)
+    assert fa.fa_bwd_workspace_bytes(1, 2, 100, 96, fa.FA_BF16) == round_up(200 * 4) * 2
+    # with FA_DQ_MODE=atomic it holds the fp32 accumulator too
+    monkeypatch.setenv("FA_DQ_MODE", "atomic")
+    assert fa.fa_bwd_workspace_bytes(1, 32, 8192, 128, fa.FA_BF16) == 2 * rows * 4 + rows * 128 * 4
+    assert fa.fa_bwd_workspace_bytes(1, 2, 100, 96, fa.FA_BF16) == round_up(200 * 4) * 2   # no atomic d = 96
+
+
+def handoff_head_bytes(N, causal):
+    """The dS buffer's bytes per head: query block i (64 rows) keeps 4 KB per
+    32-key slice, 2i + 2 slices causal, ceil(N / 32) otherwise."""
+    nqb, nks = -(-N // 64), -(-N // 32)
+    return 4096 * sum((2 * i + 2) if causal else nks for i in range(nqb))
+
+
+@needs_lib
+@pytest.mark.parametrize("B,H,N,d", [(1, 32, 8192, 128), (2, 3, 100, 64), (1, 1, 1, 96), (1, 2, 4099, 256),
+                                     (4, 16, 1024, 64)])
+def test_workspace_size_per_method(B, H, N, d):
+    rows = B * H * N
+    stats = 2 * round_up(rows * 4)
+    for causal in (0, 1):
+        ws = lambda m, dt=fa.FA_BF16: fa.fa_bwd_workspace_size(B, H, N, d, causal, dt, m)
+        assert ws(fa.FA_DQ_RECOMPUTE) == stats
+        assert ws(fa.FA_DQ_HANDOFF) == stats + round_up(B * H * handoff_head_bytes(N, causal)) + 4096
+        assert ws(fa.FA_DQ_ATOMIC) == (stats + round_up(rows * d * 4) if d in (64, 128) else 0)
+        # fp32 has only the recompute kernels (and no d = 256)
+        assert ws(fa.FA_DQ_HANDOFF, fa.FA_FP32) == 0
+        assert ws(fa.FA_DQ_RECOMPUTE, fa.FA_FP32) == (stats if d != 256 else 0)
+        assert ws(7) == 0
+    # the causal buffer keeps about half of the (query, key) pairs
+    assert (fa.fa_bwd_workspace_size(1, 1, 8192, 128, 1, fa.FA_BF16, fa.FA_DQ_HANDOFF)
+            < 0.51 * fa.fa_bwd_workspace_size(1, 1, 8192, 128, 0, fa.FA_BF16, fa.FA_DQ_HANDOFF))
+    assert fa.fa_bwd_workspace_size(0, 1, 128, 64, 0, fa.FA_BF16, fa.FA_DQ_HANDOFF) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, 128, 64, 2, fa.FA_BF16, fa.FA_DQ_HANDOFF) == 0
 
 
 P = 0x10000  # a non-null, 256-byte aligned stand-in address; never dereferenced
@@ -250,7 +285,7 @@ def test_fwd_dropout_rejects(kw, status):
 @needs_lib
 @pytest.mark.parametrize("kw,status", [
     (dict(dO=None), -1), (dict(dk=None), -1), (dict(H=0), -1), (dict(drop_t=300), -1), (dict(d=32), -2),
-    (dict(workspace=None), -3), (dict(workspace_bytes=1024), -3), (dict(workspace=P + 16), -3),
+    (dict(workspace=None), -3), (dict(workspace_bytes=1023), -3), (dict(workspace=P + 16), -3),
     (dict(lse=P + 2), -1),
 ])
 def test_bwd_dropout_rejects(kw, status):

@@ -26,7 +26,7 @@ from oracle import ref
 pytestmark = pytest.mark.gpu
 
 
-def run_dropout(x, causal, scale, t, seed, offset, layout=0, bwd=True):
+def run_dropout(x, causal, scale, t, seed, offset, layout=0, bwd=True, method=fa.FA_DQ_HANDOFF):
     import torch
     q, k, v, do = (to_dev(x[n], "bf16", layout) for n in ("q", "k", "v", "do"))
     p = t / 256.0
@@ -34,7 +34,8 @@ def run_dropout(x, causal, scale, t, seed, offset, layout=0, bwd=True):
     o, lse = fa.forward_dropout(q, k, v, causal, scale, p, seed, offset, layout=layout)
     res = {"o": o, "lse": lse}
     if bwd:
-        dq, dk, dv = fa.backward_dropout(q, k, v, o, do, lse, causal, scale, p, seed, offset, layout=layout)
+        dq, dk, dv = fa.backward_dropout(q, k, v, o, do, lse, causal, scale, p, seed, offset, layout=layout,
+                                         method=method)
         res.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return {n: to_np(tns, layout if n != "lse" else 0) for n, tns in res.items()}
@@ -123,14 +124,17 @@ def test_dkdv_kernel_mask_bit_exact(d, n, causal):
 
 
 @pytest.mark.parametrize("d,n,causal", MASK_CASES)
-def test_dq_kernel_mask_bit_exact(d, n, causal):
-    """K = V = I, dO = 1: dQ[:, :N] = scale dS; bits as in the dK/dV test."""
-    log(f"[drop-mask dq] d={d} N={n} causal={causal}")
+@pytest.mark.parametrize("method", [fa.FA_DQ_RECOMPUTE, fa.FA_DQ_HANDOFF])
+def test_dq_kernel_mask_bit_exact(d, n, causal, method):
+    """K = V = I, dO = 1: dQ[:, :N] = scale dS; bits as in the dK/dV test.
+    The recompute kernel regenerates the mask; with the hand-off dQ comes
+    from the dS the key/value-outer kernel stored."""
+    log(f"[drop-mask dq] d={d} N={n} causal={causal} method={method}")
     B, H, t, seed, off = 1, 2, 128, 987654321, 42
     x = _identity_inputs(B, H, n, d, 29 + d + n, which=("q",))
     scale = 1.0 / math.sqrt(d)
     sk = dr.keep_scale(t)
-    got = run_dropout(x, causal, scale, t, seed, off)
+    got = run_dropout(x, causal, scale, t, seed, off, method=method)
     for h in range(H):
         p, D, z = _ds_and_bits(x, 0, h, H, n, scale, causal, t, seed, off)
         live = p > 1e-3
@@ -166,8 +170,8 @@ def compare_dropout(got, want, x, b, h, scale, causal, where):
     return errs
 
 
-def _compare_all(x, causal, scale, t, seed, off, layout=0, where=""):
-    got = run_dropout(x, causal, scale, t, seed, off, layout=layout)
+def _compare_all(x, causal, scale, t, seed, off, layout=0, where="", method=fa.FA_DQ_HANDOFF):
+    got = run_dropout(x, causal, scale, t, seed, off, layout=layout, method=method)
     want = dr.forward_backward_dropout(x["q"], x["k"], x["v"], x["do"], scale, causal, seed, off, t)
     errs = {}
     for (b, h), w in want.items():
@@ -183,11 +187,13 @@ VALUE_CASES += [(256, n, causal, 77) for n in (1, 129, 300) for causal in (False
 
 
 @pytest.mark.parametrize("d,n,causal,t", VALUE_CASES)
-def test_values_small_and_ragged(d, n, causal, t):
-    log(f"[drop-values] d={d} N={n} causal={causal} t={t}")
+@pytest.mark.parametrize("method", [fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE])
+def test_values_small_and_ragged(d, n, causal, t, method):
+    log(f"[drop-values] d={d} N={n} causal={causal} t={t} method={method}")
     w = gen.workload("c2")
     x = gen.make_inputs(w, shape=(2, 2, n, d), seed=3000 + n + d + t)
-    _compare_all(x, causal, 1.0 / math.sqrt(d), t, seed=1000 + n, off=t, where=f"d{d} N{n} c{int(causal)} t{t}")
+    _compare_all(x, causal, 1.0 / math.sqrt(d), t, seed=1000 + n, off=t, where=f"d{d} N{n} c{int(causal)} t{t}",
+                 method=method)
 
 
 @pytest.mark.parametrize("causal", [False, True])

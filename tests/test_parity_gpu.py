@@ -18,8 +18,8 @@ from gpu_util import compare, log, oracle_heads, run_gpu, to_dev, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _full_compare(x, dtype, causal, scale, where, layout=0):
-    res = run_gpu(x, dtype, causal, scale, layout=layout)
+def _full_compare(x, dtype, causal, scale, where, layout=0, method=fa.FA_DQ_HANDOFF):
+    res = run_gpu(x, dtype, causal, scale, layout=layout, method=method)
     B, H = x["q"].shape[:2]
     want = oracle_heads(x, causal, scale, heads=None)
     errs = {}
@@ -31,21 +31,26 @@ def _full_compare(x, dtype, causal, scale, where, layout=0):
     return errs, res
 
 
-EDGE = [(dtype, d, causal, n)
+# bf16 runs both dQ methods (the dS hand-off and the recompute kernel); fp32
+# has only the recompute kernels
+EDGE = [(dtype, d, causal, n, m)
         for dtype in ("bf16", "fp32")
         for d in (64, 96, 128)
         for causal in (False, True)
-        for n in (1, 17, 64, 129, 300)]
+        for n in (1, 17, 64, 129, 300)
+        for m in ((fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE) if dtype == "bf16" else (fa.FA_DQ_RECOMPUTE,))]
 # head dim 256: bf16 only
-EDGE += [("bf16", 256, causal, n) for causal in (False, True) for n in (1, 17, 64, 129, 300)]
+EDGE += [("bf16", 256, causal, n, m) for causal in (False, True) for n in (1, 17, 64, 129, 300)
+         for m in (fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE)]
+METHOD_NAME = {fa.FA_DQ_HANDOFF: "handoff", fa.FA_DQ_RECOMPUTE: "recompute", fa.FA_DQ_ATOMIC: "atomic"}
 
 
-@pytest.mark.parametrize("dtype,d,causal,n", EDGE)
-def test_small_and_ragged(dtype, d, causal, n):
-    log(f"[edge] dtype={dtype} d={d} causal={causal} N={n}")
+@pytest.mark.parametrize("dtype,d,causal,n,method", EDGE)
+def test_small_and_ragged(dtype, d, causal, n, method):
+    log(f"[edge] dtype={dtype} d={d} causal={causal} N={n} dq={METHOD_NAME[method]}")
     w = gen.workload("c2")
     x = gen.make_inputs(w, shape=(1, 2, n, d), seed=1000 + n + d, dtype=dtype)
-    _full_compare(x, dtype, causal, 1.0 / math.sqrt(d), f"edge {dtype} d{d} c{int(causal)} N{n}")
+    _full_compare(x, dtype, causal, 1.0 / math.sqrt(d), f"edge {dtype} d{d} c{int(causal)} N{n}", method=method)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -129,6 +134,34 @@ def test_full_size_invariants(big_runs, key):
     slack = 1e-2 * np.abs(v).max()
     assert (res["o"] <= hi + slack).all() and (res["o"] >= lo - slack).all()
     assert np.isfinite(res["lse"]).all()
+
+
+@pytest.mark.parametrize("key,d", [("c4", 128), ("c3", 128), ("c2", 64), ("c3", 96), ("c3", 256)])
+def test_dq_methods_at_size(key, d):
+    """The dS hand-off against the recompute kernel, in the benchmark's launch
+    configuration: dK and dV come from the same arithmetic in both (the
+    hand-off kernel only adds the dS stores), so they must be bit-identical;
+    dQ differs in rounding only, and both meet the oracle bar on sampled
+    heads (the first and the last)."""
+    import torch
+    w = gen.workload(key)
+    B, H, N = w.shape[:3]
+    if d != w.shape[3]:   # the workload's geometry at another head dim
+        B, H = 1, 8
+    log(f"[dq methods] {w.name} B={B} H={H} N={N} d={d}")
+    x = gen.make_inputs(w, shape=(B, H, N, d), seed=4000 + d)
+    a = run_gpu(x, "bf16", w.causal, 1.0 / math.sqrt(d), method=fa.FA_DQ_HANDOFF)
+    b = run_gpu(x, "bf16", w.causal, 1.0 / math.sqrt(d), method=fa.FA_DQ_RECOMPUTE)
+    for n in ("o", "lse", "dk", "dv"):
+        assert np.array_equal(a[n], b[n]), f"{n} differs between the dQ methods"
+    heads = [(0, 0), (B - 1, H - 1)]
+    want = oracle_heads(x, w.causal, 1.0 / math.sqrt(d), heads=heads)
+    for bh, wv in want.items():
+        for name, r in (("handoff", a), ("recompute", b)):
+            errs = compare({"dq": r["dq"][bh]}, wv, "bf16", names=("dq",), where=f"{name} {w.name} d{d} head {bh}")
+            log(f"  {name} head {bh} dq max error {errs['dq']:.3e}")
+    del a, b
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -325,7 +358,8 @@ def test_maximum_size_sampled_heads():
     2^31), so every per-head base and row offset runs through the 64-bit
     address arithmetic.  Inputs come from a seeded device generator; three
     whole heads (the first, one in the middle, the last) go to the oracle with
-    the exact bf16 values the kernels saw."""
+    the exact bf16 values the kernels saw.  Both dQ methods: the hand-off
+    buffer is 136 GB here, so its byte offsets run far past 2^32."""
     import torch
     B, H, N, d = 63, 32, 8192, 128
     assert B * H * N * d < 2 ** 31 and 64 * H * N * d >= 2 ** 31
@@ -335,17 +369,24 @@ def test_maximum_size_sampled_heads():
     q, k, v, do = (torch.randn((B, H, N, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
                    for _ in range(4))
     o, lse = fa.forward(q, k, v, True, scale)
-    dq, dk, dv = fa.backward(q, k, v, o, do, lse, True, scale)
-    torch.cuda.synchronize()
-    for b, h in ((0, 0), (31, 17), (B - 1, H - 1)):
+    heads = ((0, 0), (31, 17), (B - 1, H - 1))
+    want = {}
+    for b, h in heads:
         x = {n: t[b, h].float().cpu().numpy().astype(np.float64)[None, None] for n, t in
              (("q", q), ("k", k), ("v", v), ("do", do))}
-        want = oracle_heads(x, True, scale, heads=[(0, 0)])[(0, 0)]
-        got = {"o": to_np(o[b, h]), "lse": to_np(lse[b, h]), "dq": to_np(dq[b, h]), "dk": to_np(dk[b, h]),
-               "dv": to_np(dv[b, h])}
-        errs = compare(got, want, "bf16", where=f"max size head ({b},{h})")
-        log(f"  head ({b},{h}) max errors {errs}")
-    del q, k, v, do, o, lse, dq, dk, dv
+        want[(b, h)] = oracle_heads(x, True, scale, heads=[(0, 0)])[(0, 0)]
+    for method in (fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE):
+        log(f"  backward, dQ by {METHOD_NAME[method]}")
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, True, scale, method=method)
+        torch.cuda.synchronize()
+        for b, h in heads:
+            got = {"o": to_np(o[b, h]), "lse": to_np(lse[b, h]), "dq": to_np(dq[b, h]), "dk": to_np(dk[b, h]),
+                   "dv": to_np(dv[b, h])}
+            errs = compare(got, want[(b, h)], "bf16", where=f"max size {METHOD_NAME[method]} head ({b},{h})")
+            log(f"  head ({b},{h}) max errors {errs}")
+        del dq, dk, dv
+        torch.cuda.empty_cache()
+    del q, k, v, do, o, lse
     torch.cuda.empty_cache()
 
 
@@ -371,7 +412,7 @@ def test_maximum_size_d256_sampled_heads():
     """The largest d = 256 shape of the same kind: B=63, H=16, N=8192 causal,
     2.11e9 elements per tensor (one batch more reaches the 2^31 limit), through
     the d = 256 forward, preprocess, dK/dV and dQ kernels; three whole heads
-    against the oracle as above."""
+    against the oracle as above, for both dQ methods."""
     import torch
     B, H, N, d = 63, 16, 8192, 256
     assert B * H * N * d < 2 ** 31 and (B + 1) * H * N * d >= 2 ** 31
@@ -381,17 +422,24 @@ def test_maximum_size_d256_sampled_heads():
     q, k, v, do = (torch.randn((B, H, N, d), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
                    for _ in range(4))
     o, lse = fa.forward(q, k, v, True, scale)
-    dq, dk, dv = fa.backward(q, k, v, o, do, lse, True, scale)
-    torch.cuda.synchronize()
-    for b, h in ((0, 0), (31, 9), (B - 1, H - 1)):
+    heads = ((0, 0), (31, 9), (B - 1, H - 1))
+    want = {}
+    for b, h in heads:
         x = {n: t[b, h].float().cpu().numpy().astype(np.float64)[None, None] for n, t in
              (("q", q), ("k", k), ("v", v), ("do", do))}
-        want = oracle_heads(x, True, scale, heads=[(0, 0)])[(0, 0)]
-        got = {"o": to_np(o[b, h]), "lse": to_np(lse[b, h]), "dq": to_np(dq[b, h]), "dk": to_np(dk[b, h]),
-               "dv": to_np(dv[b, h])}
-        errs = compare(got, want, "bf16", where=f"max size d256 head ({b},{h})")
-        log(f"  head ({b},{h}) max errors {errs}")
-    del q, k, v, do, o, lse, dq, dk, dv
+        want[(b, h)] = oracle_heads(x, True, scale, heads=[(0, 0)])[(0, 0)]
+    for method in (fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE):
+        log(f"  backward, dQ by {METHOD_NAME[method]}")
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, True, scale, method=method)
+        torch.cuda.synchronize()
+        for b, h in heads:
+            got = {"o": to_np(o[b, h]), "lse": to_np(lse[b, h]), "dq": to_np(dq[b, h]), "dk": to_np(dk[b, h]),
+                   "dv": to_np(dv[b, h])}
+            errs = compare(got, want[(b, h)], "bf16", where=f"max size d256 {METHOD_NAME[method]} head ({b},{h})")
+            log(f"  head ({b},{h}) max errors {errs}")
+        del dq, dk, dv
+        torch.cuda.empty_cache()
+    del q, k, v, do, o, lse
     torch.cuda.empty_cache()
 
 
