@@ -11,7 +11,8 @@
 // One workgroup (4 waves) owns 128 query rows of one (batch, head): query
 // blocks 2I and 2I+1 of 64 rows, each wave a 32-row half of one block, with
 // dQ^T (d x 32) in registers.  It walks the keys in stages of 64 (two 32-key
-// slices of the buffer), double-buffered through LDS:
+// slices of the buffer) through LDS, K one stage ahead, dS (the HBM stream)
+// two stages ahead:
 //   K stage       64 rows, swizzled tile, fetched by all four waves
 //   dS stage      per wave, the two 1 KB micro-tiles (16 queries each) of its
 //                 32 queries for each of the two slices
@@ -20,8 +21,9 @@
 //                        LDS reads (lane = d column, resp. query; registers =
 //                        keys, in the same order on both sides).
 // A micro-tile holds lane (key + 32h)'s 16 bytes (queries 16st + 4h + 0..3,
-// then 16st + 8 + 4h + 0..3).  It lands in LDS through buffer loads straight
-// into LDS, lane l fetching 16-byte chunk l ^ 4*bit5(l) ^ 8*u (u: the
+// then 16st + 8 + 4h + 0..3).  It lands in LDS through non-temporal buffer
+// loads straight into LDS (each byte is read once; measured 9% faster than
+// cached loads), lane l fetching 16-byte chunk l ^ 4*bit5(l) ^ 8*u (u: the
 // micro-tile's position within the 32 queries), so that the 32 lanes of a
 // transposing read (4 keys x 16 queries, two micro-tiles) hit 32 distinct
 // 8-byte bank slots.
@@ -40,13 +42,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const char* __restric
   constexpr int KC = 64;                 // keys per stage
   constexpr int KTB = KC * ROWB;         // bytes of a K stage
   constexpr int WSB = 4096;              // dS bytes of a stage per wave (2 slices x 2 micro-tiles)
+  // K stages double-buffered (fetched one stage ahead), dS stages in three
+  // buffers (fetched two stages ahead: dS is the stream from HBM)
   __shared__ __attribute__((aligned(1024))) char sK0[KTB];
   __shared__ __attribute__((aligned(1024))) char sK1[KTB];
   __shared__ __attribute__((aligned(1024))) char sS0[4 * WSB];
   __shared__ __attribute__((aligned(1024))) char sS1[4 * WSB];
+  __shared__ __attribute__((aligned(1024))) char sS2[4 * WSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, h = lane >> 5, g = lane >> 4, s16 = lane & 15;
+  const int h = lane >> 5, g = lane >> 4, s16 = lane & 15;
+  const int l32 = lane & 31;
   const int nI = (nqb + 1) / 2;   // 128-row work items per head
   const int bid = blockIdx.x;
   const int head = bid % BH;
@@ -65,9 +71,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const char* __restric
   const TileFetch<ROWB, KC, 4, D / 8> kfetch(wave, lane, RS * 2);
   const TileBases<ROWB> tb(lane);
 
-  // the wave's block in the buffer; slice ks of it sits ks * 4 KB further
+  // the wave's block in the buffer (block 0 of the head for a wave without
+  // one: its fetches below stay in bounds and are never read); slice ks of it
+  // sits ks * 4 KB further
   const __amdgpu_buffer_rsrc_t rs =
       raw_rsrc(dsbuf + (size_t)head * ds_head_bytes + ds_block_off(CAUSAL, has_blk ? b : 0, nks));
+  const int last_sl = max(nsl_w, 1) - 1;   // fetches of slices past the block's re-read its last one
   unsigned voff[2];   // micro-tile 2qt + u: the chunk this lane fetches
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -90,53 +99,90 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const char* __restric
       }
   }
 
-  auto fetch = [&](int s, char* Kt, char* St) {
-    kfetch(Kh, KC * s, N, Kt);
+  // Every fetch call issues the same loads on every path (stages past the
+  // end re-read the last one, slices past the wave's block re-read its last
+  // slice), so that the wait closing each stage can count them: the four dS
+  // loads of the newest fetch are the only ones it leaves outstanding.
+  auto fetch_k = [&](int s, char* Kt) { kfetch(Kh, KC * min(s, nstage - 1), N, Kt); };
+  auto fetch_ds = [&](int s, char* St) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int ks = 2 * s + j;
-      if (ks < nsl_w) {
+      const int ks = min(2 * s + j, last_sl);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) dma16_buf(rs, voff[u], (unsigned)ks * 4096u, St + wave * WSB + (2 * j + u) * 1024);
-      }
+      for (int u = 0; u < 2; ++u)   // non-temporal (aux bit 1): dS is read once
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(St + wave * WSB + (2 * j + u) * 1024), 16, voff[u],
+                                                 (unsigned)ks * 4096u, 0, 2);
     }
+  };
+  // s_waitcnt vmcnt(4) lgkmcnt(0), then the barrier; no fence (a release
+  // fence covers the loads into LDS and so waits for all of them), empty asm
+  // statements with a memory clobber keep memory accesses on their side
+  auto stage_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0074);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   f32x16 acc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) acc[t] = f32x16{};
 
-  auto body = [&](auto bc, int s) {
-    constexpr int bb = decltype(bc)::value;
-    const char* Kt = bb ? sK1 : sK0;
-    const char* St = (bb ? sS1 : sS0) + wave * WSB;
-    if (s + 1 < nstage) fetch(s + 1, bb ? sK0 : sK1, bb ? sS0 : sS1);
+  // stage s: products from K buffer s % 2 and dS buffer s % 3, while K of
+  // stage s+1 and dS of stage s+2 are fetched into the buffers stage s-1 used.
+  // All of the stage's operands are read from LDS before those fetches are
+  // issued (80 registers), so that no read waits for a load issued after it
+  // (the compiler cannot tell the fetch targets apart from the buffers read).
+  auto body = [&](auto kc, auto sc, int s) {
+    constexpr int kb = decltype(kc)::value, sb = decltype(sc)::value;
+    const char* Kt = kb ? sK1 : sK0;
+    const char* St = (sb == 0 ? sS0 : (sb == 1 ? sS1 : sS2)) + wave * WSB;
+    bf16x8 bop[4], aop[4][DT];
 #pragma unroll
     for (int kst = 0; kst < 4; ++kst) {
       const int j = kst >> 1;
       if (2 * s + j < nsl_w) {
         const char* Sj = St + 2048 * j;
-        const bf16x8 bop = cat(lds_read_tr(Sj, boff[kst & 1][0]), lds_read_tr(Sj, boff[kst & 1][1]));
+        bop[kst] = cat(lds_read_tr(Sj, boff[kst & 1][0]), lds_read_tr(Sj, boff[kst & 1][1]));
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          const bf16x8 aop = cat(lds_read_tr(Kt, tb.tr_off(kst, t, 0)), lds_read_tr(Kt, tb.tr_off(kst, t, 1)));
-          acc[t] = mfma32(aop, bop, acc[t]);
-        }
+        for (int t = 0; t < DT; ++t)
+          aop[kst][t] = cat(lds_read_tr(Kt, tb.tr_off(kst, t, 0)), lds_read_tr(Kt, tb.tr_off(kst, t, 1)));
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_k(s + 1, kb ? sK0 : sK1);
+    fetch_ds(s + 2, sb == 0 ? sS2 : (sb == 1 ? sS0 : sS1));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kst = 0; kst < 4; ++kst) {
+      if (2 * s + (kst >> 1) < nsl_w) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t) acc[t] = mfma32(aop[kst][t], bop[kst], acc[t]);
+      }
+    }
+    stage_barrier();
   };
 
-  if (nstage > 0) {
-    fetch(0, sK0, sS0);
-    __syncthreads();
-    for (int s = 0;;) {
-      body(IC<0>{}, s);
-      if (++s >= nstage) break;
-      body(IC<1>{}, s);
-      if (++s >= nstage) break;
-    }
+  fetch_k(0, sK0);
+  fetch_ds(0, sS0);
+  fetch_ds(1, sS1);
+  stage_barrier();
+  for (int s = 0;;) {
+    body(IC<0>{}, IC<0>{}, s);
+    if (++s >= nstage) break;
+    body(IC<1>{}, IC<1>{}, s);
+    if (++s >= nstage) break;
+    body(IC<0>{}, IC<2>{}, s);
+    if (++s >= nstage) break;
+    body(IC<1>{}, IC<0>{}, s);
+    if (++s >= nstage) break;
+    body(IC<0>{}, IC<1>{}, s);
+    if (++s >= nstage) break;
+    body(IC<1>{}, IC<2>{}, s);
+    if (++s >= nstage) break;
   }
+  // the fetches past the end must land before the workgroup's LDS goes
+  __builtin_amdgcn_s_waitcnt(0x0070);
 
   const int qrow = 64 * b + 32 * qt + l32;
   if (!has_blk || qrow >= N) return;

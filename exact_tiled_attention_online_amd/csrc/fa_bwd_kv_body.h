@@ -21,20 +21,23 @@
 //                                  index across lanes); each wave takes a
 //                                  32-column slice of d with K^T held in
 //                                  registers; fp32 atomics into an accumulator.
-// In the hand-off variant (DSO) the bf16 dS operand of every computed block is
-// also stored to a buffer (layout: DsOut in fa_launch.h), from which a separate
-// kernel forms dQ = dS K without recomputing S and dP.  Each query tile's
-// stores are issued in the slot right after its dS is packed (holding dS in
-// registers into the next step instead made the compiler's register use jump
-// past the file), and the barrier closing the step does not wait for them:
-// vector memory operations retire in issue order, so once at most the step's
-// four stores are outstanding the prefetch issued before them has landed in
-// LDS; the barrier waits for that and for the wave's LDS reads only (a
-// workgroup barrier with a full fence would wait for the stores too).  Every
-// wave issues exactly four stores per step (one whose keys all lie past the
-// block's queries writes zeros to a sink), so that this wait is the same on
-// every path and the compiler's own count of outstanding operations stays
-// exact.
+// In the hand-off variant (DSO) the bf16 dS operands of every block are also
+// stored to a buffer (layout: DsOut in fa_launch.h), from which a separate
+// kernel forms dQ = dS K without recomputing S and dP:
+//  - the four 16-byte stores of a step follow the step's products, after the
+//    masked and unmasked paths join (stores inside the two paths leave the
+//    compiler counting 0, 4 or 8 of them; holding dS into the next step made
+//    its register use jump past the file);
+//  - the barrier closing the step does not wait for them: vector memory
+//    operations retire in issue order, so once at most those four are
+//    outstanding the prefetch issued before them has landed in LDS, and the
+//    barrier waits for that and for the wave's LDS reads only (a workgroup
+//    barrier with a full fence would wait for the stores too);
+//  - a wave whose keys all lie past the block's queries runs the masked step
+//    anyway (dS = 0; the waves of a workgroup move in step, so it costs no
+//    time) and stores to a sink, so that every path issues the same stores;
+//  - the stores are non-temporal: nothing here reads them back (measured: the
+//    dQ kernel then reads the buffer 7% faster, this kernel is unchanged).
 // The S and dP accumulators start from -LSE/scale and -D of their query rows,
 // so they end as S - LSE/scale and dP - D.
 // The accumulators hold fp32 and are converted once at write-back (page
@@ -467,7 +470,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
       if constexpr (DSO) {
         char* p = (dead ? dso.sink : dsw + ds_block_off(CAUSAL, i, dso.nks)) + 16 * ln;
 #pragma unroll
-        for (int st = 0; st < BR / 16; ++st) *reinterpret_cast<bf16x8*>(p + 1024 * st) = dsv[st];
+        for (int st = 0; st < BR / 16; ++st) __builtin_nontemporal_store(dsv[st], reinterpret_cast<bf16x8*>(p + 1024 * st));
         // s_waitcnt vmcnt(4) lgkmcnt(0): all but the four stores (expcnt
         // never waited for).  No fence: a release fence covers the loads into
         // LDS and so waits for every memory operation; the empty asm
