@@ -10,6 +10,10 @@ every kernel give each kernel's average duration over the same timed steps.
 
 value = credited FLOPs of a step / step time, with the credited counts
 fwd = 4*B*H*N^2*d and bwd = 10*B*H*N^2*d, both halved for a causal mask.
+``target`` holds the backward's own credited rate over the dense bf16 peak
+beside the 0.40 bar the backward is built against.  The backward's dQ method
+is the library's choice for the workspace given (the dS hand-off; with
+FA_DQ_MODE=recompute the recomputing dQ kernel), reported as detail.dq_mode.
 
 Prints one JSON line.  Default workload: B=1, H=32, N=8192, d=128, causal,
 bf16 (the headline shape).  ``detail.decode`` adds the split-key-range forward
@@ -42,7 +46,34 @@ KERNEL_SOURCES = {
     "bwd_bf16_kernel": ["fa_bwd_bf16.hip", "fa_bwd_kv_body.h", "fa_common.h", "fa_dropout.h"],
     "bwd_dq_kernel": ["fa_bwd_dq.hip", "fa_common.h", "fa_dropout.h"],
     "bwd_pre_kernel": ["fa_aux.hip", "fa_common.h"],
+    "bwd_bf16_ds_kernel": ["fa_bwd_bf16.hip", "fa_bwd_kv_body.h", "fa_common.h", "fa_dropout.h", "fa_launch.h"],
+    "bwd_dq_ds_kernel": ["fa_bwd_dq_ds.hip", "fa_common.h", "fa_launch.h"],
 }
+DQ_METHODS = {0: "handoff", 1: "recompute", 2: "atomic"}
+
+
+def ds_buffer_bytes(B, H, N, causal):
+    """Bytes of the dS hand-off buffer (the dQ kernel reads each once): per
+    head, 64-row query block i keeps 2i + 2 (causal) or ceil(N/32) 32-key
+    slices of 4 KB (the diagonal's masked entries included)."""
+    nqb, nks = -(-N // 64), -(-N // 32)
+    per_head = 4096 * (nqb * (nqb + 1) if causal else nqb * nks)
+    return B * H * per_head
+
+
+def backward_kernels(method, unit, T, ds_bytes, kv_ms, dq_ms, suffix=""):
+    """Per backward kernel of a dQ method: (name, ms, bound, algorithmic work
+    per launch).  MFMA-bound kernels count the products they compute (unit =
+    one N x N x d product); the hand-off's dQ kernel is bound by reading dS,
+    and counts dS, K read and dQ written once (T elements each of K and dQ)."""
+    if method == "handoff":
+        return [("bwd_bf16_ds_kernel" + suffix, kv_ms, "mfma", 4 * unit),      # S, dP, dV, dK (+ dS stores)
+                ("bwd_dq_ds_kernel" + suffix, dq_ms, "hbm", ds_bytes + 2 * T * 2)]
+    if method == "atomic":
+        return [("bwd_bf16_kernel" + suffix, kv_ms, "mfma", 5 * unit),         # ... + dQ atomics
+                ("dq_convert_kernel" + suffix, dq_ms, "hbm", T * 4 + T * 2)]
+    return [("bwd_bf16_kernel" + suffix, kv_ms, "mfma", 4 * unit),             # S, dP, dV, dK
+            ("bwd_dq_kernel" + suffix, dq_ms, "mfma", 3 * unit)]               # S, dP, dQ
 
 
 # Other instantiations whose HBM bytes the counter summary also records, for
@@ -53,8 +84,9 @@ KERNEL_SOURCES = {
 _FWD, _FP8 = ["fa_fwd_bf16.hip", "fa_common.h", "fa_dropout.h"], ["fa_fwd_fp8.hip", "fa_common.h"]
 DETAIL_COUNTERS = {
     "fwd_bf16_dropout_kernel": (("fwd_bf16_dropout_kernel", 128, None), _FWD),
-    "bwd_bf16_kernel_d256": (("bwd_bf16_kernel", 256, None),
-                             ["fa_bwd_kv256.hip", "fa_bwd_kv_body.h", "fa_common.h", "fa_dropout.h"]),
+    "bwd_bf16_ds_kernel_d256": (("bwd_bf16_ds_kernel", 256, None),
+                                ["fa_bwd_kv256.hip", "fa_bwd_kv_body.h", "fa_common.h", "fa_dropout.h", "fa_launch.h"]),
+    "bwd_dq_ds_kernel_d256": (("bwd_dq_ds_kernel", 256, None), ["fa_bwd_dq_ds.hip", "fa_common.h", "fa_launch.h"]),
     "fwd_fp8_kernel": (("fwd_fp8_kernel", 128, False), _FP8),
     "fwd_bf16_kernel_split": (("fwd_bf16_kernel", 128, True), _FWD),
     "fwd_fp8_kernel_split": (("fwd_fp8_kernel", 128, True), _FP8),
@@ -502,8 +534,10 @@ def head_dim_256_measurement(fa, torch, stream, with_oracle, reps=10):
     256, bf16 (inputs from a seeded device generator).  Per-stage times from
     HIP events on the launch stream, credited TFLOP/s, the dominant kernel
     against the dense bf16 peak (its algorithmic FLOPs: 4 products of
-    2*B*H*N^2*d/2 for dK/dV, 3 for dQ, 2 for the forward) and, unless
-    disabled, 256 query rows of head (0, 0) (O, LSE) against the oracle."""
+    2*B*H*N^2*d/2 for dK/dV, 3 for the recomputing dQ kernel, 2 for the
+    forward; the hand-off's dQ kernel is HBM-bound and reported in GB/s) and,
+    unless disabled, 256 query rows of head (0, 0) (O, LSE) against the
+    oracle."""
     import numpy as np
     B, H, N, d = 1, 16, 8192, 256
     scale = 1.0 / 16.0
@@ -546,17 +580,26 @@ def head_dim_256_measurement(fa, torch, stream, with_oracle, reps=10):
     fwd_ms, pre_ms, kv_ms, dq_ms = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
     unit = 2 * B * H * N * N * d / 2    # one causal N x N x d product
     fwd_fl, bwd_fl = 2 * unit, 5 * unit
-    kernels = {"fwd_bf16_kernel": (fwd_ms, 2 * unit), "bwd_bf16_kernel": (kv_ms, 4 * unit),
-               "bwd_dq_kernel": (dq_ms, 3 * unit)}
+    method = DQ_METHODS[fa.fa_bwd_dq_method(B, H, N, d, True, fa.FA_BF16, ws.numel(), 0)]
+    bk = backward_kernels(method, unit, B * H * N * d, ds_buffer_bytes(B, H, N, True), kv_ms, dq_ms)
+    kernels = {"fwd_bf16_kernel": (fwd_ms, 2 * unit)}
+    kernels.update({n: (t, fl) for n, t, bound, fl in bk if bound == "mfma"})
+    hbm = {n: (t, b) for n, t, bound, b in bk if bound == "hbm"}
     dom = max(kernels, key=lambda n: kernels[n][0])
     tf = kernels[dom][1] / (kernels[dom][0] * 1e-3) / 1e12
-    res = {"workload": "bf16_b1h16_n8192_d256_causal", "fwd_ms": round(fwd_ms, 4),
-           "bwd_ms": round(pre_ms + kv_ms + dq_ms, 4), "bwd_dkdv_ms": round(kv_ms, 4), "bwd_dq_ms": round(dq_ms, 4),
-           "tflops": round((fwd_fl + bwd_fl) / ((fwd_ms + pre_ms + kv_ms + dq_ms) * 1e-3) / 1e12, 3),
+    bwd_ms = pre_ms + kv_ms + dq_ms
+    res = {"workload": "bf16_b1h16_n8192_d256_causal", "dq_mode": method, "fwd_ms": round(fwd_ms, 4),
+           "bwd_ms": round(bwd_ms, 4), "bwd_dkdv_ms": round(kv_ms, 4), "bwd_dq_ms": round(dq_ms, 4),
+           "bwd_frac_peak": round(bwd_fl / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "tflops": round((fwd_fl + bwd_fl) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 3),
            "kernel_tflops": {n: round(f / (t * 1e-3) / 1e12, 3) for n, (t, f) in kernels.items()},
+           "hbm_kernels": {n: {"achieved_gbs": round(b / (t * 1e-3) / 1e9, 1),
+                               "frac": round(b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                               "traffic": traffic_from_counters(n + "_d256") if n + "_d256" in DETAIL_COUNTERS
+                               else None} for n, (t, b) in hbm.items()},
            "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(tf, 3), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                        "traffic": traffic_from_counters("bwd_bf16_kernel_d256") if dom == "bwd_bf16_kernel"
+                        "traffic": traffic_from_counters(dom + "_d256") if dom + "_d256" in DETAIL_COUNTERS
                         else None}}
     if with_oracle:
         from oracle import ref
@@ -793,23 +836,24 @@ def main():
     unit = bwd_fl / 5.0             # one N x N x d product: 2*B*H*N^2*d FLOPs (halved if causal)
     value = (fwd_fl + bwd_fl) / (ms_step * 1e-3) / 1e12
     bwd_ms = pre_ms + kv_ms + dq_ms
-    atomic = os.environ.get("FA_DQ_MODE") == "atomic"
-    # algorithmic FLOPs per launch of each kernel: the products it computes
-    kernels = {
-        "fwd_bf16_kernel": (fwd_ms, 2 * unit),                       # S, P V
-        "bwd_bf16_kernel": (kv_ms, (5 if atomic else 4) * unit),     # S, dP, dV, dK (+ dQ)
-    }
-    if not atomic:
-        kernels["bwd_dq_kernel"] = (dq_ms, 3 * unit)                 # S, dP, dQ
-    dom = max(kernels, key=lambda k: kernels[k][0])
-    dom_ms, dom_fl = kernels[dom]
-    achieved = dom_fl / (dom_ms * 1e-3) / 1e12
+    method = DQ_METHODS[fa.fa_bwd_dq_method(B, H, N, d, w.causal, code, ws.numel(), 0)]
     elem = 2 if w.dtype == "bf16" else 4
     T = B * H * N * d
+    # algorithmic work per launch of each kernel: the products it computes
+    # (MFMA-bound) or the bytes it must move (HBM-bound)
+    bk = backward_kernels(method, unit, T, ds_buffer_bytes(B, H, N, w.causal), kv_ms, dq_ms)
+    mfma_k = {"fwd_bf16_kernel": (fwd_ms, 2 * unit)}                  # S, P V
+    mfma_k.update({n: (t, fl) for n, t, bound, fl in bk if bound == "mfma"})
+    hbm_k = {n: (t, b) for n, t, bound, b in bk if bound == "hbm"}
+    dom = max(mfma_k, key=lambda k: mfma_k[k][0])
+    dom_ms, dom_fl = mfma_k[dom]
+    achieved = dom_fl / (dom_ms * 1e-3) / 1e12
     pre_bytes = 2 * T * elem + 12 * B * H * N
-    traffic = traffic_from_counters(dom) if (args.workload == "c4" and not atomic) else None
-    pre_traffic = traffic_from_counters("bwd_pre_kernel") if args.workload == "c4" else None
+    headline = args.workload == "c4" and w.dtype == "bf16"
+    traffic = traffic_from_counters(dom) if headline else None
+    pre_traffic = traffic_from_counters("bwd_pre_kernel") if headline else None
     props = torch.cuda.get_device_properties(0)
+    bwd_frac = bwd_fl / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
 
     out = {
         "metric": METRIC,
@@ -829,15 +873,23 @@ def main():
         "roofline": {"kernel": dom, "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "target": {"what": "backward credited TFLOP/s (10*B*H*N^2*d, halved causal, over bwd_ms) / dense bf16 peak",
+                   "value": round(bwd_frac, 4), "bar": 0.40, "met": bool(bwd_frac >= 0.40),
+                   "bwd_ms": round(bwd_ms, 4), "bwd_ms_at_bar": round(bwd_fl / (0.40 * PEAK_BF16_TFLOPS * 1e12) * 1e3, 4)},
         "detail": {
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "bwd_preprocess_ms": round(pre_ms, 4), "bwd_dkdv_ms": round(kv_ms, 4),
-            "bwd_dq_ms": round(dq_ms, 4), "dq_mode": "atomic" if atomic else "query-outer",
+            "bwd_dq_ms": round(dq_ms, 4), "dq_mode": method,
             "fwd_tflops": round(fwd_fl / (fwd_ms * 1e-3) / 1e12, 3),
             "bwd_tflops": round(bwd_fl / (bwd_ms * 1e-3) / 1e12, 3),
             "fwd_frac_peak": round(fwd_fl / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "bwd_frac_peak": round(bwd_fl / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "kernel_tflops": {k: round(f / (t * 1e-3) / 1e12, 3) for k, (t, f) in kernels.items()},
+            "kernel_tflops": {k: round(f / (t * 1e-3) / 1e12, 3) for k, (t, f) in mfma_k.items()},
+            "hbm_kernels": {k: {"bound": "hbm", "achieved": round(b / (t * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                "algorithmic_bytes": int(b),
+                                "traffic": traffic_from_counters(k) if headline else None}
+                            for k, (t, b) in hbm_k.items()},
             "preprocess_roofline": {"kernel": "bwd_pre_kernel", "bound": "hbm",
                                     "achieved": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
                                     "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -18,7 +18,8 @@ FA_BF16, FA_FP32 = 0, 1
 FA_LAYOUT_BHND, FA_LAYOUT_BNHD = 0, 1
 FA_DQ_HANDOFF, FA_DQ_RECOMPUTE, FA_DQ_ATOMIC = 0, 1, 2
 
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_workspace_size", "fa_bwd_preprocess", "fa_bwd_dkdv",
+EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_workspace_size", "fa_bwd_dq_method",
+           "fa_bwd_preprocess", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_fwd_fp8", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv",
            "fa_fwd_splitkv_fp8_workspace_bytes", "fa_fwd_splitkv_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
            "fa_strerror")
@@ -50,6 +51,8 @@ def load():
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd_dq_method.argtypes = [i, i, i, i, i, i, sz, i]
+    lib.fa_bwd_dq_method.restype = i
     lib.fa_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, f, vp, sz, vp, i, i]
     lib.fa_bwd_preprocess.restype = i
     lib.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, sz, vp, i, i]
@@ -96,6 +99,10 @@ def fa_bwd_workspace_bytes(B, H, N, d, dtype) -> int:
 
 def fa_bwd_workspace_size(B, H, N, d, causal, dtype, dq_method) -> int:
     return load().fa_bwd_workspace_size(B, H, N, d, int(causal), dtype, dq_method)
+
+
+def fa_bwd_dq_method(B, H, N, d, causal, dtype, workspace_bytes, dropout) -> int:
+    return load().fa_bwd_dq_method(B, H, N, d, int(causal), dtype, workspace_bytes, int(dropout))
 
 
 def fa_bwd_preprocess(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype,

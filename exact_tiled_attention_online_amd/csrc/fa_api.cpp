@@ -196,6 +196,14 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype, 
   return carve(nullptr, B, H, N, d, causal != 0, dtype, dq_method).bytes;
 }
 
+int fa_bwd_dq_method(int B, int H, int N, int d, int causal, int dtype, size_t workspace_bytes, int dropout) {
+  const int st = check_shape(B, H, N, d, causal, 1.f, dtype, FA_LAYOUT_BHND);
+  if (st != FA_OK) return st;
+  if (dropout != 0 && dropout != 1) return FA_ERR_INVALID;
+  if (dropout && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  return dq_method(B, H, N, d, causal != 0, dtype, workspace_bytes, dropout != 0);
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
   if (check_shape(B, H, N, d, 0, 1.f, dtype, FA_LAYOUT_BHND) != FA_OK) return 0;
   // the recompute method's statistics, or with FA_DQ_MODE=atomic the

@@ -119,6 +119,16 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype, int dq_method);
 
 /*
+ * The dQ method (fa_dq_method) that fa_bwd and its stages (dropout = 0) or
+ * fa_bwd_dropout (dropout = 1) take for these arguments, a workspace of
+ * workspace_bytes bytes and the current FA_DQ_MODE; a negative fa_status for
+ * arguments they reject (B, H, N < 1, an unsupported d or dtype, causal not
+ * 0 or 1, dropout not 0 or 1).  Whether the workspace is large enough for the
+ * method is the calls' own check (FA_ERR_WORKSPACE).
+ */
+int fa_bwd_dq_method(int B, int H, int N, int d, int causal, int dtype, size_t workspace_bytes, int dropout);
+
+/*
  * The smallest workspace of fa_bwd: fa_bwd_workspace_size(B, H, N, d, causal,
  * dtype, FA_DQ_RECOMPUTE) (which does not depend on causal), or with
  * FA_DQ_MODE=atomic set the atomic method's.  A backward given this much takes

@@ -127,6 +127,35 @@ def test_workspace_size_per_method(B, H, N, d):
     assert fa.fa_bwd_workspace_size(1, 1, 128, 64, 2, fa.FA_BF16, fa.FA_DQ_HANDOFF) == 0
 
 
+@needs_lib
+def test_dq_method_follows_the_workspace(monkeypatch):
+    """fa_bwd takes the dS hand-off exactly when the workspace holds its
+    buffer, the recompute otherwise; FA_DQ_MODE forces one (atomic only where
+    that method exists, never with dropout)."""
+    monkeypatch.delenv("FA_DQ_MODE", raising=False)
+    for (B, H, N, d) in ((1, 32, 8192, 128), (2, 3, 100, 64), (1, 2, 4099, 256), (1, 1, 17, 96)):
+        for causal in (0, 1):
+            need = fa.fa_bwd_workspace_size(B, H, N, d, causal, fa.FA_BF16, fa.FA_DQ_HANDOFF)
+            m = lambda ws, drop=0: fa.fa_bwd_dq_method(B, H, N, d, causal, fa.FA_BF16, ws, drop)
+            assert m(need) == fa.FA_DQ_HANDOFF and m(need + 1) == fa.FA_DQ_HANDOFF
+            assert m(need - 1) == fa.FA_DQ_RECOMPUTE and m(0) == fa.FA_DQ_RECOMPUTE
+            assert m(need, 1) == fa.FA_DQ_HANDOFF and m(need - 1, 1) == fa.FA_DQ_RECOMPUTE
+            assert fa.fa_bwd_dq_method(B, H, N, d, causal, fa.FA_FP32, need, 0) == (
+                fa.FA_DQ_RECOMPUTE if d != 256 else -2)
+    monkeypatch.setenv("FA_DQ_MODE", "recompute")
+    assert fa.fa_bwd_dq_method(1, 1, 128, 64, 1, fa.FA_BF16, 1 << 40, 0) == fa.FA_DQ_RECOMPUTE
+    monkeypatch.setenv("FA_DQ_MODE", "atomic")
+    assert fa.fa_bwd_dq_method(1, 1, 128, 64, 1, fa.FA_BF16, 0, 0) == fa.FA_DQ_ATOMIC
+    assert fa.fa_bwd_dq_method(1, 1, 128, 64, 1, fa.FA_BF16, 1 << 40, 1) == fa.FA_DQ_HANDOFF
+    assert fa.fa_bwd_dq_method(1, 1, 128, 96, 1, fa.FA_BF16, 1 << 40, 0) == fa.FA_DQ_HANDOFF
+    # rejected arguments
+    assert fa.fa_bwd_dq_method(0, 1, 128, 64, 1, fa.FA_BF16, 0, 0) == -1
+    assert fa.fa_bwd_dq_method(1, 1, 128, 80, 1, fa.FA_BF16, 0, 0) == -2
+    assert fa.fa_bwd_dq_method(1, 1, 128, 64, 2, fa.FA_BF16, 0, 0) == -1
+    assert fa.fa_bwd_dq_method(1, 1, 128, 64, 1, fa.FA_BF16, 0, 2) == -1
+    assert fa.fa_bwd_dq_method(1, 1, 128, 64, 1, fa.FA_FP32, 0, 1) == -2
+
+
 P = 0x10000  # a non-null, 256-byte aligned stand-in address; never dereferenced
 
 

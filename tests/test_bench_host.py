@@ -21,6 +21,8 @@ FWD_256 = "void fa::fwd_bf16_kernel<256, true, 4, 32, false>(__bf16 const*)"
 KV = "void fa::bwd_bf16_kernel<128, true, false>(__bf16 const*)"
 KV_DROP = "void fa::bwd_bf16_dropout_kernel<128, true>(__bf16 const*)"
 DQ = "void fa::bwd_dq_kernel<128, true, 8>(__bf16 const*)"
+KV_DS = "void fa::bwd_bf16_ds_kernel<128, true>(__bf16 const*)"
+DQ_DS = "void fa::bwd_dq_ds_kernel<128, true>(char const*)"
 PRE = "_ZN2fa14bwd_pre_kernelILi128EDF16bEEvPKT0_S3_PKfPfS6_S6_mfiNS_9RowLayoutE"
 PRE_256 = "_ZN2fa14bwd_pre_kernelILi256EDF16bEEvPKT0_S3_PKfPfS6_S6_mfiNS_9RowLayoutE"
 COPY = ("void at::native::vectorized_elementwise_kernel<4, at::native::bfloat16tofloat32_copy_kernel_cuda"
@@ -31,21 +33,26 @@ COPY = ("void at::native::vectorized_elementwise_kernel<4, at::native::bfloat16t
     (FWD, "fwd_bf16_kernel", True), (FWD_SPLIT, "fwd_bf16_kernel", False), (FWD_256, "fwd_bf16_kernel", False),
     (KV, "bwd_bf16_kernel", True), (KV_DROP, "bwd_bf16_kernel", False), (DQ, "bwd_dq_kernel", True),
     (PRE, "bwd_pre_kernel", True), (PRE_256, "bwd_pre_kernel", False), (KV, "bwd_dq_kernel", False),
+    (KV_DS, "bwd_bf16_ds_kernel", True), (KV_DS, "bwd_bf16_kernel", False), (DQ_DS, "bwd_dq_ds_kernel", True),
+    (DQ_DS, "bwd_dq_kernel", False), (DQ, "bwd_dq_ds_kernel", False),
 ])
 def test_headline_instance(name, short, want):
     assert bench._headline_instance(name, short) == want
 
 
 FWD_DROP = "void fa::fwd_bf16_dropout_kernel<128, true, 8, 64>(__bf16 const*)"
-KV_256 = "void fa::bwd_bf16_kernel<256, true, false>(__bf16 const*)"
+KV_256 = "void fa::bwd_bf16_ds_kernel<256, true>(__bf16 const*)"
 
 
 @pytest.mark.parametrize("name,key,want", [
     (FWD_DROP, "fwd_bf16_dropout_kernel", True), (FWD, "fwd_bf16_dropout_kernel", False),
-    (KV_256, "bwd_bf16_kernel_d256", True), (KV, "bwd_bf16_kernel_d256", False),
-    ("void fa::bwd_bf16_dropout_kernel<256, true>(__bf16 const*)", "bwd_bf16_kernel_d256", False),
-    ("_ZN2fa15bwd_bf16_kernelILi256ELb1ELb0EEEvPKDF16b", "bwd_bf16_kernel_d256", True),
-    ("_ZN2fa23bwd_bf16_dropout_kernelILi256ELb1EEEvPKDF16b", "bwd_bf16_kernel_d256", False),
+    (KV_256, "bwd_bf16_ds_kernel_d256", True), (KV_DS, "bwd_bf16_ds_kernel_d256", False),
+    ("void fa::bwd_bf16_kernel<256, true, false>(__bf16 const*)", "bwd_bf16_ds_kernel_d256", False),
+    ("void fa::bwd_bf16_dropout_kernel<256, true, true>(__bf16 const*)", "bwd_bf16_ds_kernel_d256", False),
+    ("_ZN2fa18bwd_bf16_ds_kernelILi256ELb1EEEvPKDF16b", "bwd_bf16_ds_kernel_d256", True),
+    ("_ZN2fa23bwd_bf16_dropout_kernelILi256ELb1ELb1EEEvPKDF16b", "bwd_bf16_ds_kernel_d256", False),
+    ("void fa::bwd_dq_ds_kernel<256, true>(char const*)", "bwd_dq_ds_kernel_d256", True),
+    (DQ_DS, "bwd_dq_ds_kernel_d256", False),
     ("void fa::fwd_fp8_kernel<128, true, 4, false>(unsigned char const*)", "fwd_fp8_kernel", True),
     ("void fa::fwd_fp8_kernel<128, true, 1, true>(unsigned char const*)", "fwd_fp8_kernel", False),
     ("void fa::fwd_fp8_kernel<128, true, 1, true>(unsigned char const*)", "fwd_fp8_kernel_split", True),
@@ -104,10 +111,10 @@ def test_counter_summary_calibrates_on_the_copy_probe(tmp_path):
     assert c["bwd_bf16_kernel"]["hbm_bytes_per_launch"] == int((500.0 * 2 + 50.0) * 1024)
     assert c["fwd_bf16_kernel"]["source_digest"] == bench.source_digest(bench.KERNEL_SOURCES["fwd_bf16_kernel"])
     assert "bwd_dq_kernel" not in c
-    assert c["bwd_bf16_kernel_d256"]["hbm_bytes_per_launch"] == int((700.0 * 2 + 70.0) * 1024)
+    assert c["bwd_bf16_ds_kernel_d256"]["hbm_bytes_per_launch"] == int((700.0 * 2 + 70.0) * 1024)
     assert c["fwd_bf16_dropout_kernel"]["hbm_bytes_per_launch"] == int((80.0 * 2 + 8.0) * 1024)
-    assert c["bwd_bf16_kernel_d256"]["source_digest"] == bench.source_digest(
-        bench.DETAIL_COUNTERS["bwd_bf16_kernel_d256"][1])
+    assert c["bwd_bf16_ds_kernel_d256"]["source_digest"] == bench.source_digest(
+        bench.DETAIL_COUNTERS["bwd_bf16_ds_kernel_d256"][1])
 
 
 def test_traffic_is_dropped_once_the_sources_change(tmp_path, monkeypatch):
@@ -157,3 +164,21 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_ds_buffer_bytes_and_backward_kernels():
+    """The dS buffer the hand-off's dQ kernel reads (4 KB per 64-query x
+    32-key slice; causal: 2i + 2 slices for query block i) and the work each
+    backward kernel is credited with per method."""
+    assert bench.ds_buffer_bytes(1, 32, 8192, True) == 32 * 4096 * 128 * 129
+    assert bench.ds_buffer_bytes(4, 16, 1024, False) == 64 * 4096 * 16 * 32
+    assert bench.ds_buffer_bytes(1, 1, 100, True) == 4096 * 2 * 3
+    # within 1% of 2 bytes per kept (query, key) pair at the headline shape
+    pairs = 32 * 8192 * 8193 // 2
+    assert abs(bench.ds_buffer_bytes(1, 32, 8192, True) / (2 * pairs) - 1) < 0.01
+    k = bench.backward_kernels("handoff", 10.0, 1000, 5000, 1.0, 0.5)
+    assert k == [("bwd_bf16_ds_kernel", 1.0, "mfma", 40.0), ("bwd_dq_ds_kernel", 0.5, "hbm", 5000 + 4000)]
+    k = bench.backward_kernels("recompute", 10.0, 1000, 5000, 1.0, 0.5)
+    assert k == [("bwd_bf16_kernel", 1.0, "mfma", 40.0), ("bwd_dq_kernel", 0.5, "mfma", 30.0)]
+    k = bench.backward_kernels("atomic", 10.0, 1000, 5000, 1.0, 0.5)
+    assert k[0] == ("bwd_bf16_kernel", 1.0, "mfma", 50.0) and k[1][2] == "hbm"
