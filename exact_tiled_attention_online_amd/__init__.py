@@ -15,5 +15,6 @@ from ._lib import (  # noqa: F401
     backward_dropout, drop_threshold, fa_bwd_dropout, fa_fwd_dropout, forward_dropout,
     fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_bwd_workspace_bytes, fa_fwd, fa_fwd_fp8, fa_fwd_splitkv,
     fa_fwd_splitkv_workspace_bytes, fa_fwd_splitkv_fp8, fa_fwd_splitkv_fp8_workspace_bytes, fa_strerror,
+    fa_fwd_splitkv_noalloc, FA_SPLITKV_NOALLOC_MAX_BYTES, FA_ERR_SCRATCH,
     forward, forward_fp8, forward_splitkv, forward_splitkv_fp8, load, workspace,
 )

@@ -13,7 +13,8 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
-FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+FA_SPLITKV_NOALLOC_MAX_BYTES = 32 * 1024 * 1024
 FA_BF16, FA_FP32 = 0, 1
 FA_LAYOUT_BHND, FA_LAYOUT_BNHD = 0, 1
 FA_DQ_HANDOFF, FA_DQ_RECOMPUTE, FA_DQ_ATOMIC = 0, 1, 2
@@ -22,6 +23,7 @@ EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_workspace_size"
            "fa_bwd_preprocess", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_fwd_fp8", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv",
            "fa_fwd_splitkv_fp8_workspace_bytes", "fa_fwd_splitkv_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
+           "fa_fwd_splitkv_noalloc",
            "fa_strerror")
 
 _lib = None
@@ -65,6 +67,8 @@ def load():
     lib.fa_fwd_splitkv_workspace_bytes.restype = sz
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp, i, i]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, i]
+    lib.fa_fwd_splitkv_noalloc.restype = i
     lib.fa_fwd_splitkv_fp8_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_fwd_splitkv_fp8_workspace_bytes.restype = sz
     lib.fa_fwd_splitkv_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, f, i, vp, sz, vp, i]
@@ -137,6 +141,12 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, 
                    stream, dtype, layout) -> int:
     return load().fa_fwd_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale), num_splits,
                                  workspace, workspace_bytes, stream, dtype, layout)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, stream, dtype,
+                           layout) -> int:
+    return load().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, int(causal), float(scale), num_splits,
+                                         stream, dtype, layout)
 
 
 def fa_fwd_splitkv_fp8_workspace_bytes(B, H, Nq, Nk, d, num_splits) -> int:

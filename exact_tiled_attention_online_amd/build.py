@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libfa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_bwd_bf16.hip", "fa_bwd_kv256.hip", "fa_bwd_dq.hip",
-           "fa_bwd_dq_ds.hip", "fa_aux.hip", "fa_fp32.hip", "fa_api.cpp"]
+           "fa_bwd_dq_ds.hip", "fa_aux.hip", "fa_fp32.hip", "fa_noalloc.hip", "fa_api.cpp"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.
 # -amdgpu-mfma-vgpr-form: MFMA results in VGPRs where they fit, so that fewer

@@ -431,6 +431,8 @@ const char* fa_strerror(int status) {
     case FA_ERR_UNSUPPORTED: return "unsupported head dim, dtype or size";
     case FA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP runtime reported a launch error";
+    case FA_ERR_SCRATCH: return "the call needs more than the no-allocation entry point's static scratch "
+                                "(FA_SPLITKV_NOALLOC_MAX_BYTES); use fewer key ranges or the workspace form";
     default: return "unknown status";
   }
 }

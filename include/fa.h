@@ -58,7 +58,8 @@ typedef enum {
   FA_ERR_INVALID = -1,      /* null or misaligned pointer, non-positive size, bad flag, bad scale */
   FA_ERR_UNSUPPORTED = -2,  /* head dim or dtype the library has no kernel for */
   FA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
-  FA_ERR_HIP = -4           /* the HIP runtime reported a launch error */
+  FA_ERR_HIP = -4,          /* the HIP runtime reported a launch error */
+  FA_ERR_SCRATCH = -5       /* fa_fwd_splitkv_noalloc: the call needs more than its static scratch */
 } fa_status;
 
 typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
@@ -279,6 +280,27 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int n
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int Nq, int Nk, int d, int causal, float scale, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream, int dtype, int layout);
+
+/*
+ * fa_fwd_splitkv without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  The per-range
+ * partial results live in a static device array of the library,
+ * FA_SPLITKV_NOALLOC_MAX_BYTES bytes on each GPU it runs on, held until the
+ * process ends; its address on a device is looked up (hipGetSymbolAddress)
+ * on the first call there.  Arguments, checks and results are fa_fwd_splitkv's
+ * (the same kernels run; outputs are bit-identical to fa_fwd_splitkv with the
+ * same num_splits).  A call whose fa_fwd_splitkv_workspace_bytes exceeds
+ * FA_SPLITKV_NOALLOC_MAX_BYTES returns FA_ERR_SCRATCH and launches nothing
+ * (fewer ranges, num_splits, need less).  All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (different streams, or host
+ * threads) race on it and must be serialised by the caller.  The array needs
+ * no clearing: each call writes every partial result it reads.
+ */
+#define FA_SPLITKV_NOALLOC_MAX_BYTES (32u * 1024u * 1024u)
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, int causal, float scale, int num_splits,
+                           void* stream, int dtype, int layout);
 
 /*
  * The split-key-range forward with FP8 inputs: fa_fwd_splitkv's shapes,

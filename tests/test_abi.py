@@ -74,7 +74,7 @@ def test_library_exports_every_declared_symbol():
 
 @needs_lib
 def test_strerror():
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert isinstance(fa.fa_strerror(st), str) and fa.fa_strerror(st)
     assert fa.fa_strerror(12345) == "unknown status"
 
@@ -403,3 +403,34 @@ def test_buffer_checks_of_the_binding():
             _lib._check_ws(bad, dev)
     assert _lib._check_uint((1 << 64) - 1, 64, "seed") == (1 << 64) - 1
     assert _lib._check_uint(0, 32, "offset") == 0
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1), (dict(B=0), -1), (dict(Nq=0), -1),
+    (dict(causal=2), -1), (dict(scale=0.0), -1), (dict(d=80), -2), (dict(d=256), -2), (dict(dtype=fa.FA_FP32), -2),
+    (dict(causal=1, Nq=2000, Nk=1000), -1), (dict(num_splits=-1), -1), (dict(num_splits=5000), -1),
+    (dict(layout=5), -1), (dict(q=P + 8), -1),
+    # more partial results than the static scratch holds: 64 ranges x 4096 rows x (128 + 1) floats
+    (dict(B=1, H=64, Nq=64, Nk=8192, num_splits=64), -5),
+])
+def test_splitkv_noalloc_rejects(kw, status):
+    """The no-allocation split forward checks every argument of
+    fa_fwd_splitkv, and the scratch bound, before any HIP call (no GPU here:
+    a call that got past the checks would fail with FA_ERR_HIP instead)."""
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=4, Nk=1000, d=128, causal=1, scale=0.125, num_splits=0,
+             stream=None, dtype=fa.FA_BF16, layout=fa.FA_LAYOUT_BHND)
+    a.update(kw)
+    assert fa.fa_fwd_splitkv_noalloc(**a) == status
+
+
+@needs_lib
+def test_splitkv_noalloc_bound_is_the_workspace_size():
+    """The largest call it takes is the one whose fa_fwd_splitkv workspace fits
+    FA_SPLITKV_NOALLOC_MAX_BYTES."""
+    assert _lib.FA_SPLITKV_NOALLOC_MAX_BYTES == 32 * 1024 * 1024
+    n = fa.fa_fwd_splitkv_workspace_bytes(1, 64, 64, 8192, 128, 64)
+    assert n > _lib.FA_SPLITKV_NOALLOC_MAX_BYTES
+    assert fa.fa_fwd_splitkv_workspace_bytes(8, 32, 1, 16384, 128, 0) < _lib.FA_SPLITKV_NOALLOC_MAX_BYTES
+    header = open(HEADER).read()
+    assert "#define FA_SPLITKV_NOALLOC_MAX_BYTES (32u * 1024u * 1024u)" in header
