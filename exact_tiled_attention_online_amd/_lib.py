@@ -240,6 +240,16 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _check_kv_heads(q, k, layout, what="k, v"):
+    """The key/value cache of a split forward must have q's batch, heads and
+    head dim (the kernels address K and V rows with q's (B, H, d)); only the
+    row count may differ."""
+    B, H, _, d = _dims(q, layout)
+    Bk, Hk, _, dk = _dims(k, layout)
+    if (Bk, Hk, dk) != (B, H, d):
+        raise ValueError(f"{what}: expected batch, heads and head dim {(B, H, d)} as q, got {(Bk, Hk, dk)}")
+
+
 def forward(q, k, v, causal: bool, scale: float, out=None, lse=None, stream=None,
             layout: int = FA_LAYOUT_BHND):
     """O, LSE = attention forward on device tensors (bf16 or fp32) of shape
@@ -305,6 +315,7 @@ def forward_splitkv(q, k, v, causal: bool, scale: float, num_splits: int = 0, ou
     _check((k, v), k.shape)
     if k.dtype != q.dtype or k.device != q.device:
         raise ValueError("q, k, v must share one dtype and device")
+    _check_kv_heads(q, k, layout)
     o = torch.empty_like(q) if out is None else _check_buf(out, q.shape, q.dtype, q.device, "out")
     l = (torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None
          else _check_buf(lse, (B, H, Nq), torch.float32, q.device, "lse"))
@@ -356,6 +367,7 @@ def forward_splitkv_fp8(q8, k8, v8, descale_q: float, descale_k: float, descale_
         raise TypeError("FP8 inputs are passed as uint8 e4m3fn codes")
     if k8.device != q8.device:
         raise ValueError("q8, k8, v8 must share one device")
+    _check_kv_heads(q8, k8, layout, "k8, v8")
     o = (torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device) if out is None
          else _check_buf(out, q8.shape, torch.bfloat16, q8.device, "out"))
     l = (torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device) if lse is None

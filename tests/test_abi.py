@@ -434,3 +434,21 @@ def test_splitkv_noalloc_bound_is_the_workspace_size():
     assert fa.fa_fwd_splitkv_workspace_bytes(8, 32, 1, 16384, 128, 0) < _lib.FA_SPLITKV_NOALLOC_MAX_BYTES
     header = open(HEADER).read()
     assert "#define FA_SPLITKV_NOALLOC_MAX_BYTES (32u * 1024u * 1024u)" in header
+
+
+def test_split_conveniences_check_the_cache_geometry():
+    """forward_splitkv / forward_splitkv_fp8 take a key/value cache only with
+    q's batch, heads and head dim (checked on shapes, before any launch)."""
+    class Shape:
+        def __init__(self, shape):
+            self.shape = shape
+
+    q = Shape((2, 4, 3, 128))
+    _lib._check_kv_heads(q, Shape((2, 4, 1000, 128)), fa.FA_LAYOUT_BHND)
+    for bad in ((2, 1, 1000, 128), (2, 4, 1000, 64), (1, 4, 1000, 128)):
+        with pytest.raises(ValueError):
+            _lib._check_kv_heads(q, Shape(bad), fa.FA_LAYOUT_BHND)
+    # [B, N, H, d]: heads are the third dimension
+    _lib._check_kv_heads(Shape((2, 3, 4, 128)), Shape((2, 1000, 4, 128)), fa.FA_LAYOUT_BNHD)
+    with pytest.raises(ValueError):
+        _lib._check_kv_heads(Shape((2, 3, 4, 128)), Shape((2, 1000, 1, 128)), fa.FA_LAYOUT_BNHD)

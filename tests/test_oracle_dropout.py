@@ -34,6 +34,33 @@ def test_philox_rounds_match_numpy_philox4x64(case):
         assert list(dr.philox_scalar(words, key, width=64)) == raw[4 * blk:4 * blk + 4]
 
 
+def _kat():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "philox4x32_10_kat.json")
+    return [([int(w, 16) for w in v["ctr"]], [int(w, 16) for w in v["key"]], [int(w, 16) for w in v["out"]])
+            for v in json.load(open(path))["vectors"]]
+
+
+def test_philox4x32_known_answers():
+    """The 32-bit generator (the one the mask uses) reproduces the published
+    Philox4x32-10 known-answer vectors, scalar and vectorised: this pins its
+    constants, which the width-64 comparison with numpy does not reach."""
+    for ctr, key, want in _kat():
+        assert list(dr.philox_scalar(ctr, key, width=32)) == want
+        got = dr.philox4x32_10(*(np.array([c]) for c in ctr), *key)
+        assert [int(x[0]) for x in got] == want
+
+
+@pytest.mark.parametrize("name", ["M0", "M1", "W0", "W1"])
+def test_philox4x32_known_answers_catch_a_mistyped_constant(monkeypatch, name):
+    """One flipped bit in any of the four 32-bit constants fails the vectors."""
+    bad = dict(dr.PHILOX[32])
+    bad[name] ^= 1 << 7
+    monkeypatch.setitem(dr.PHILOX, 32, bad)
+    assert any(list(dr.philox_scalar(ctr, key, width=32)) != want for ctr, key, want in _kat())
+
+
 def test_philox_width64_catches_swapped_outputs():
     """A round that swaps its two multiplier lanes no longer matches numpy."""
     key, ctr = [3, 5], [7, 11, 13, 17]

@@ -530,6 +530,14 @@ def test_conveniences_reject_mismatched_buffers():
             fa.forward_splitkv(qd, k, v, True, 0.125, **kw)
         with pytest.raises(ValueError):
             fa.forward_splitkv_fp8(q8d, k8, v8, 1.0, 1.0, 1.0, True, 0.125, **kw)
+    # a key/value cache with fewer heads (grouped-query shape) or another head
+    # dim than q: the kernels would read K and V with q's head offsets
+    for kc in (k[:, :1].contiguous(), k[..., :64].contiguous()):
+        with pytest.raises(ValueError):
+            fa.forward_splitkv(qd, kc, kc, True, 0.125, out=o4, lse=l4)
+        k8c = torch.zeros(kc.shape, dtype=torch.uint8, device="cuda")
+        with pytest.raises(ValueError):
+            fa.forward_splitkv_fp8(q8d, k8c, k8c, 1.0, 1.0, 1.0, True, 0.125, out=o4, lse=l4)
     torch.cuda.synchronize()
     for t in (short_o, f32_o, short_l, strided_l, o4, l4):
         assert bool((t == 7.0).all())
