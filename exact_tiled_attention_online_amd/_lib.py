@@ -8,6 +8,7 @@ fallback implementation.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -40,10 +41,34 @@ def load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+    _lib = _open(LIB_PATH)
+    return _lib
+
+
+_variants = {}
+
+
+@contextlib.contextmanager
+def using_library(path):
+    """Route every entry point of this module to another build of the library
+    (the checking variants libfa_debug_sync.so and libfa_tile_alt.so) for the
+    duration of the block: tests run the same calls against both builds."""
+    global _lib
+    prev = load()
+    if path not in _variants:
+        _variants[path] = _open(path)
+    _lib = _variants[path]
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
+def _open(path):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python -m exact_tiled_attention_online_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i]
     lib.fa_fwd.restype = i
@@ -81,7 +106,6 @@ def load():
     lib.fa_bwd_dropout.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

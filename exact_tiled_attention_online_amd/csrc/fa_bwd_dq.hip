@@ -109,6 +109,7 @@ FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, 
     if (j + 1 < ntiles) {
       fetch(Kh, (j + 1) * BC, N, b ? sK0 : sK1);
       fetch(Vh, (j + 1) * BC, N, b ? sV0 : sV1);
+      FA_DEBUG_BARRIER();
     }
     if (j < wave_tiles) {
       const int kvb = j * BC;

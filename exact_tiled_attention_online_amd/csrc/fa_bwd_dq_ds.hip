@@ -152,6 +152,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const char* __restric
     __builtin_amdgcn_sched_barrier(0);
     fetch_k(s + 1, kb ? sK0 : sK1);
     fetch_ds(s + 2, sb == 0 ? sS2 : (sb == 1 ? sS0 : sS1));
+    FA_DEBUG_BARRIER();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kst = 0; kst < 4; ++kst) {

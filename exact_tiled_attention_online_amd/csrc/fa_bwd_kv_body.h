@@ -289,6 +289,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
       char* St = b ? sS1 : sS0;
       const int dir = ascend ? 1 : -1;
       if (k + 1 < nsteps) fetch(i + dir, b ? sQ0 : sQ1, b ? sG0 : sG1, b ? sL0 : sL1, b ? sD0 : sD1);
+      FA_DEBUG_BARRIER();
       if (k > 0) dq_product(i - dir, b ? sS0 : sS1);
       __builtin_amdgcn_sched_barrier(0);
       const int qb0 = i * BR;

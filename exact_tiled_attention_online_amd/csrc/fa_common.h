@@ -155,6 +155,20 @@ struct TileBases {
 template <int B>
 using IC = std::integral_constant<int, B>;
 
+// FA_DEBUG_SYNC (a checking build, libfa_debug_sync.so): a full workgroup
+// barrier (every memory operation of every wave complete) right after each
+// prefetch of a next tile is issued, so that the prefetch has landed before
+// the current tile's reads begin and no wave runs ahead into a buffer another
+// wave still reads.  Its results must be bit-identical to the normal build's;
+// a difference points at a missing wait or barrier around an LDS buffer swap.
+#ifdef FA_DEBUG_SYNC
+#define FA_DEBUG_BARRIER() __syncthreads()
+#else
+#define FA_DEBUG_BARRIER() \
+  do {                      \
+  } while (0)
+#endif
+
 
 // Wave-wide direct fetch global -> LDS through a buffer resource: lane l's 16
 // (or 4) bytes, read from base + soffset (uniform) + voffset (per lane), land

@@ -139,6 +139,7 @@ FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
     if (j + 1 < ntiles) {
       fetch(Kh, (jlo + j + 1) * BC, Nk, b ? sK0 : sK1);
       fetch(Vh, (jlo + j + 1) * BC, Nk, b ? sV0 : sV1);
+      FA_DEBUG_BARRIER();
     }
     if (j < wave_tiles) {
       // Slots: KS slots of S products (two 32-key halves per K-step), then

@@ -186,6 +186,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
     if (j + 1 < ntiles) {
       fetch(Kh, (jlo + j + 1) * BC, Nk, b ? sK0 : sK1);
       fetch(Vh, (jlo + j + 1) * BC, Nk, b ? sV0 : sV1);
+      FA_DEBUG_BARRIER();
     }
     if (j < wave_tiles) {
       // Slots: KS slots of two S products (the two 32-key halves), the

@@ -1,0 +1,92 @@
+"""The two checking builds of the library against the same calls.
+
+libfa_debug_sync.so (FA_DEBUG_SYNC) puts a full workgroup barrier after every
+prefetch of a next tile, so that no read can run ahead of a load into LDS
+and no wave can refill a buffer another wave still reads.  The kernels
+pipeline their LDS buffers with a single barrier per tile (and, in the dS
+hand-off kernels, barriers that deliberately leave stores outstanding); a
+missing wait there would show as a difference from this build.  Every output
+must be bit-identical.
+
+libfa_tile_alt.so is another tile configuration: 4-wave forward and
+recomputing-dQ workgroups (128 query rows instead of 256) and other operand
+read distances in the dK/dV, dQ and forward pipelines.  Its outputs must meet
+the oracle bar.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import exact_tiled_attention_online_amd as fa
+from exact_tiled_attention_online_amd import _lib
+from exact_tiled_attention_online_amd import build as fab
+from exact_tiled_attention_online_amd import inputs as gen
+from gpu_util import compare, log, oracle_heads, run_gpu, to_dev, to_np
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+
+DEBUG = fab.variant_path("debug_sync")
+ALT = fab.variant_path("tile_alt")
+
+# (B, H, N, d, causal)
+SHAPES = [(1, 4, 1000, 128, True), (2, 3, 700, 64, False), (1, 3, 333, 96, True), (1, 2, 600, 256, True),
+          (1, 2, 129, 128, False)]
+
+
+def _step(x, d, causal, method):
+    """Plain fwd + bwd (given dQ method), FP8 fwd, split fwd and dropout
+    fwd + bwd on the same inputs; every output as a device tensor."""
+    import torch
+    scale = 1.0 / math.sqrt(d)
+    out = {}
+    r = run_gpu(x, "bf16", causal, scale, method=method)["_dev"]
+    out.update({f"plain_{k}": v for k, v in r.items()})
+    q, k, v, do = (to_dev(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    o, lse = fa.forward_dropout(q, k, v, causal, scale, 0.125, seed=77, offset=3)
+    g = fa.backward_dropout(q, k, v, o, do, lse, causal, scale, 0.125, seed=77, offset=3, method=method)
+    out.update(drop_o=o, drop_lse=lse, drop_dq=g[0], drop_dk=g[1], drop_dv=g[2])
+    if d != 256:
+        qs = q[:, :, :7].contiguous()
+        out["split_o"], out["split_lse"] = fa.forward_splitkv(qs, k, v, causal, scale, num_splits=3)
+    if d == 128:
+        x8 = gen.make_fp8_inputs(tuple(x["q"].shape), seed=11)
+        q8, k8, v8 = (torch.from_numpy(x8[n]).cuda() for n in ("q8", "k8", "v8"))
+        out["fp8_o"], out["fp8_lse"] = fa.forward_fp8(q8, k8, v8, x8["descale_q"], x8["descale_k"],
+                                                      x8["descale_v"], causal, scale)
+    torch.cuda.synchronize()
+    return {k: v.clone() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SHAPES)
+@pytest.mark.parametrize("method", [fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE])
+def test_debug_sync_build_gives_the_same_bits(B, H, N, d, causal, method):
+    import torch
+    log(f"[debug-sync] B={B} H={H} N={N} d={d} causal={causal} method={method}")
+    x = gen.make_inputs(gen.workload("c3"), shape=(B, H, N, d), seed=N + d)
+    a = _step(x, d, causal, method)
+    with _lib.using_library(DEBUG):
+        b = _step(x, d, causal, method)
+    for name in a:
+        assert torch.equal(a[name], b[name]), f"{name} differs from the build with a barrier after every prefetch"
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", SHAPES + [(1, 8, 4099, 128, True)])
+@pytest.mark.parametrize("method", [fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE])
+def test_other_tile_configuration_meets_the_bar(B, H, N, d, causal, method):
+    log(f"[tile-alt] B={B} H={H} N={N} d={d} causal={causal} method={method}")
+    x = gen.make_inputs(gen.workload("c3"), shape=(B, H, N, d), seed=N + d + 1)
+    scale = 1.0 / math.sqrt(d)
+    heads = [(0, 0), (B - 1, H - 1)]
+    want = oracle_heads(x, causal, scale, heads=heads)
+    with _lib.using_library(ALT):
+        res = run_gpu(x, "bf16", causal, scale, method=method)
+    for bh, wv in want.items():
+        compare({n: res[n][bh] for n in wv}, wv, "bf16", where=f"tile-alt d{d} N{N} head {bh}")
+
+
+def test_variant_libraries_are_built_from_the_same_sources():
+    for path in (DEBUG, ALT):
+        assert os.path.exists(path), path
