@@ -30,8 +30,10 @@ int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype, 
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
   // d = 256: bf16 only (the fp32 kernels hold a row of q and o per lane pair)
   if (d != 64 && d != 96 && d != 128 && !(d == 256 && dtype == FA_BF16)) return FA_ERR_UNSUPPORTED;
-  const long long elems = (long long)B * H * N * d;
-  if (elems >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
+  // B * H * N * d < 2^31, checked factor by factor so that no product of
+  // three 31-bit sizes is formed (it would overflow a 64-bit integer)
+  const long long rows = (long long)B * H;
+  if (rows >= (1LL << 31) || rows * N >= (1LL << 31) || rows * N * d >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
