@@ -11,6 +11,18 @@ for the P V product: relative error <= 2^-4 in the normal range, absolute
 the bf16 rounding of O (2^-9 max|O|).  Inputs with sharp scores (q, k spread
 3) are included so that a misplaced key cannot hide inside that bound: there
 O follows a few rows of V closely.
+
+That worst-case bound grows with max|V| while O of a long causal row
+shrinks, so on its own it cannot see a misplaced key tile at N = 8192.  A
+second, per-element bound uses that the roundings are independent: the error
+of O_ic is sum_j P_ij e_ij V_jc with |e_ij| <= 2^-4, RMS <= 2^-4/sqrt(3), in
+e4m3's normal range (2^7 p >= 2^-6), and absolute rounding <= 2^-17 on p
+below it (RMS 2^-17/sqrt(12); the row sum l >= 1), so
+  |O_ic - O_ref_ic| <= 7 sqrt(sum_j V_jc^2 (P_ij^2 2^-8 / 3 + 2^-34 / 12))
+                       + 2^-9 |O_ref_ic|.
+At seven standard deviations the chance that a correct kernel exceeds it is
+below 1e-11 per element; a planted mistake in the oracle (one key tile
+displaced by one tile) fails it at the full size.
 """
 import math
 
@@ -19,6 +31,7 @@ import pytest
 
 import exact_tiled_attention_online_amd as fa
 from exact_tiled_attention_online_amd import inputs as gen
+from fp8_bound import displaced_tile, stat_ratio
 from gpu_util import LSE_ATOL, log, to_np
 from oracle import ref
 
@@ -64,7 +77,10 @@ def test_fp8_forward_matches_oracle(n, causal, sig):
     scale = 1.0 / math.sqrt(128)
     got = run_fp8(x, causal, scale)
     r = check(x, got, causal, scale, f"fp8 N{n} c{int(causal)} s{sig}")
-    log(f"  worst O error / bound {r:.3f}")
+    rs = max(stat_ratio(x["q"][b, h], x["k"][b, h], x["v"][b, h], got["o"][b, h], scale, causal)
+             for b in range(2) for h in range(3))
+    log(f"  worst O error / bound {r:.3f}, / per-element bound {rs:.3f}")
+    assert rs <= 1.0, rs
 
 
 def test_fp8_forward_other_descales_and_bnhd():
@@ -91,12 +107,21 @@ def test_fp8_forward_full_size_sampled_heads():
     torch.cuda.synchronize()
     got_o, got_l = to_np(o), to_np(lse)
     assert np.isfinite(got_o).all() and np.isfinite(got_l).all()
-    for h in (0, 31):
+    for h in (0, 15, 31):
         want = ref.forward_rect(x["q"], x["k"], x["v"], scale, True, heads=[(0, h)])[(0, h)]
         vmax = float(np.abs(x["v"][0, h]).max())
         tol = (2.0 ** -4 + 8192 * 2.0 ** -17) * vmax + 2.0 ** -9 * float(np.abs(want["o"]).max())
         assert float(np.abs(got_o[0, h] - want["o"]).max()) <= tol, h
         assert float(np.abs(got_l[0, h] - want["lse"]).max()) <= LSE_ATOL, h
+        r = stat_ratio(x["q"][0, h], x["k"][0, h], x["v"][0, h], got_o[0, h], scale, True)
+        log(f"  head {h}: O error / per-element bound {r:.3f}")
+        assert r <= 1.0, (h, r)
+    # the per-element bound sees a displaced key tile that the worst-case
+    # bound lets pass: checked against an oracle with that planted mistake
+    k2, v2 = displaced_tile(x["k"][0, 0], x["v"][0, 0], at=40)
+    r_bad = stat_ratio(x["q"][0, 0], k2, v2, got_o[0, 0], scale, True)
+    log(f"  planted displaced tile: ratio {r_bad:.2f}")
+    assert r_bad > 1.0, r_bad
     del q8, k8, v8, o, lse
     torch.cuda.empty_cache()
 
@@ -161,6 +186,8 @@ def test_fp8_forward_maximum_size_sampled_heads():
              for n, t in (("q", q8), ("k", k8), ("v", v8))}
         got = {"o": to_np(o[b, h])[None, None], "lse": to_np(lse[b, h])[None, None]}
         r = check(x, got, True, scale, f"fp8 max size head ({b},{h})")
-        log(f"  head ({b},{h}) worst O error / bound {r:.3f}")
+        rs = stat_ratio(x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], got["o"][0, 0], scale, True)
+        log(f"  head ({b},{h}) worst O error / bound {r:.3f}, / per-element bound {rs:.3f}")
+        assert rs <= 1.0, rs
     del q8, k8, v8, o, lse
     torch.cuda.empty_cache()

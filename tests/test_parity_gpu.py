@@ -78,7 +78,8 @@ def test_workload_c2_bf16():
     log(f"  max errors {errs}")
 
 
-SAMPLED = {"c3": [(0, 0), (1, 15)], "c4": [(0, 0), (0, 31)], "c5": [(0, 5)]}
+# the first, a middle and the last head of each workload
+SAMPLED = {"c3": [(0, 0), (1, 7), (1, 15)], "c4": [(0, 0), (0, 15), (0, 31)], "c5": [(0, 0), (0, 4), (0, 7)]}
 
 
 @pytest.fixture(scope="module")
@@ -287,21 +288,11 @@ def test_bnhd_full_size_matches_bhnd():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("causal", [False, True])
-def test_scores_rising_along_the_keys(dtype, causal):
+def _rising_inputs(dtype):
     """Scores that grow with the key index (k_j has a component along q that
     rises with j), so that every key tile raises each row's maximum and the
     forward's lagging reference has to move on nearly every tile; plus one
-    very sharp row (spread 8).
-
-    The backward does not use that reference (it recomputes from the final
-    LSE), and with rows this peaked dP - D cancels almost entirely, so
-    max|dQ| is small and set by that cancellation.  In bf16, D comes from the
-    stored bf16 O, whose rounding then dominates dQ's error (about 1.1 times
-    the 2e-2 max|dQ| bar here).  So the bf16 case checks the forward's O and
-    LSE, the outputs the rising scores exercise; fp32 checks all five."""
-    log(f"[rising] dtype={dtype} causal={causal}")
+    very sharp row (spread 8)."""
     n, d = 700, 64
     w = gen.workload("c2")
     x = gen.make_inputs(w, shape=(1, 2, n, d), seed=808, dtype=dtype)
@@ -311,16 +302,45 @@ def test_scores_rising_along_the_keys(dtype, causal):
     q[:, :, 5] *= np.float32(8.0)
     if dtype == "bf16":
         k, q = gen.round_bf16(k), gen.round_bf16(q)
-    x = dict(x, k=k, q=q)
-    scale = 1.0 / math.sqrt(d)
-    if dtype == "fp32":
-        _full_compare(x, dtype, causal, scale, f"rising {dtype} c{int(causal)}")
-        return
-    res = run_gpu(x, dtype, causal, scale, bwd=False)
+    return dict(x, k=k, q=q), 1.0 / math.sqrt(d)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_rising_along_the_keys(dtype, causal):
+    """O, LSE, dK and dV on rows whose scores rise along the keys (fp32: dQ
+    too).  The backward does not use the forward's lagging reference (it
+    recomputes from the final LSE).  bf16 dQ is the separate, expected
+    failure below."""
+    log(f"[rising] dtype={dtype} causal={causal}")
+    x, scale = _rising_inputs(dtype)
+    names = ("o", "lse", "dq", "dk", "dv") if dtype == "fp32" else ("o", "lse", "dk", "dv")
+    res = run_gpu(x, dtype, causal, scale)
     want = oracle_heads(x, causal, scale, heads=None)
     for (b, h), wv in want.items():
-        compare({n: res[n][b, h] for n in ("o", "lse")}, wv, dtype, names=("o", "lse"),
+        compare({n: res[n][b, h] for n in names}, wv, dtype, names=names,
                 where=f"rising {dtype} c{int(causal)} head ({b},{h})")
+
+
+RISING_DQ_XFAIL = ("bf16 dQ misses the 2e-2 max|dQ| bar on these non-causal rows: D = rowsum(dO o O) is formed "
+                   "from the stored bf16 O, and with rows this peaked dP - D cancels to about 1% of its terms, so "
+                   "max|dQ| is that remainder and O's 2^-9 rounding in D dominates the error")
+
+
+@pytest.mark.parametrize("causal", [pytest.param(False, marks=pytest.mark.xfail(strict=True, reason=RISING_DQ_XFAIL)),
+                                    True])
+def test_scores_rising_along_the_keys_bf16_dq(causal):
+    """bf16 dQ on the rising rows (the default dQ method, the dS hand-off).
+    Causal rows pass the bar; the non-causal ones are a known, explicit
+    failure (reason above)."""
+    log(f"[rising dq] bf16 causal={causal}")
+    x, scale = _rising_inputs("bf16")
+    res = run_gpu(x, "bf16", causal, scale)
+    want = oracle_heads(x, causal, scale, heads=None)
+    for (b, h), wv in want.items():
+        err = float(np.abs(res["dq"][b, h] - wv["dq"]).max())
+        log(f"  head ({b},{h}) dq error / bar {err / (2e-2 * max(1e-2, float(np.abs(wv['dq']).max()))):.3f}")
+        compare({"dq": res["dq"][b, h]}, wv, "bf16", names=("dq",), where=f"rising bf16 dq c{int(causal)} ({b},{h})")
 
 
 def test_head_dim_96_larger_size_sampled_heads():
