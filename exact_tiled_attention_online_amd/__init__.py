@@ -16,5 +16,6 @@ from ._lib import (  # noqa: F401
     fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_bwd_workspace_bytes, fa_fwd, fa_fwd_fp8, fa_fwd_splitkv,
     fa_fwd_splitkv_workspace_bytes, fa_fwd_splitkv_fp8, fa_fwd_splitkv_fp8_workspace_bytes, fa_strerror,
     fa_fwd_splitkv_noalloc, FA_SPLITKV_NOALLOC_MAX_BYTES, FA_ERR_SCRATCH,
+    fa_fwd_strided, fa_bwd_strided, forward_strided, backward_strided,
     forward, forward_fp8, forward_splitkv, forward_splitkv_fp8, load, workspace,
 )

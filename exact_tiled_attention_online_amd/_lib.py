@@ -24,7 +24,7 @@ EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_workspace_size"
            "fa_bwd_preprocess", "fa_bwd_dkdv",
            "fa_bwd_dq", "fa_fwd_fp8", "fa_fwd_splitkv_workspace_bytes", "fa_fwd_splitkv",
            "fa_fwd_splitkv_fp8_workspace_bytes", "fa_fwd_splitkv_fp8", "fa_fwd_dropout", "fa_bwd_dropout",
-           "fa_fwd_splitkv_noalloc",
+           "fa_fwd_splitkv_noalloc", "fa_fwd_strided", "fa_bwd_strided",
            "fa_strerror")
 
 _lib = None
@@ -104,6 +104,11 @@ def _open(path):
     lib.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, u64, u32, vp, sz,
                                    vp, i]
     lib.fa_bwd_dropout.restype = i
+    pll = ctypes.POINTER(ctypes.c_longlong)
+    lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, pll, vp, i]
+    lib.fa_fwd_strided.restype = i
+    lib.fa_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, pll, vp, sz, vp, i]
+    lib.fa_bwd_strided.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
     return lib
@@ -194,6 +199,32 @@ def fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, d
     return load().fa_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
                                  int(drop_t), _check_uint(seed, 64, "seed"), _check_uint(offset, 32, "offset"),
                                  workspace, workspace_bytes, stream, layout)
+
+
+def _strides_arg(strides):
+    """A host array of element strides for the strided calls (None: NULL)."""
+    if strides is None:
+        return None
+    vals = [int(x) for x in strides]
+    return (ctypes.c_longlong * len(vals))(*vals)
+
+
+def fa_fwd_strided(q, k, v, o, lse, B, H, N, d, causal, scale, strides, stream, dtype) -> int:
+    """strides: 12 integers, (batch, head, row) element strides of q, k, v, o."""
+    if strides is not None and len(strides) != 12:
+        raise ValueError("fa_fwd_strided takes 12 strides (3 each for q, k, v, o)")
+    return load().fa_fwd_strided(q, k, v, o, lse, B, H, N, d, int(causal), float(scale), _strides_arg(strides),
+                                 stream, dtype)
+
+
+def fa_bwd_strided(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, strides, workspace,
+                   workspace_bytes, stream, dtype) -> int:
+    """strides: 24 integers, (batch, head, row) element strides of q, k, v,
+    o, dO, dq, dk, dv."""
+    if strides is not None and len(strides) != 24:
+        raise ValueError("fa_bwd_strided takes 24 strides (3 each for q, k, v, o, dO, dq, dk, dv)")
+    return load().fa_bwd_strided(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, int(causal), float(scale),
+                                 _strides_arg(strides), workspace, workspace_bytes, stream, dtype)
 
 
 def fa_strerror(status: int) -> str:
@@ -324,6 +355,66 @@ def backward(q, k, v, o, do, lse, causal: bool, scale: float, ws=None, grads=Non
                 ws.data_ptr(), ws.numel(), _stream(stream), _dtype_code(q), layout)
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def _view(t, shape, dtype, device, name):
+    """(stride_b, stride_h, stride_n) in elements of a [B,H,N,d] device view
+    whose rows are contiguous (any other strides: slices of a packed buffer,
+    permuted dimensions, padding between rows).  A dimension of one entry
+    reports stride 0 (its stride never enters an address)."""
+    if not t.is_cuda or t.device != device or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected a {dtype} view of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    if shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError(f"{name}: the head dim must be contiguous (stride 1), got strides {t.stride()}")
+    return tuple(0 if shape[i] == 1 else t.stride(i) for i in range(3))
+
+
+def forward_strided(q, k, v, causal: bool, scale: float, out=None, lse=None, stream=None):
+    """O, LSE of attention on [B,H,N,d] views with any strides whose rows are
+    contiguous, e.g. q, k, v = qkv.view(B, N, 3, H, d).permute(2, 0, 3, 1, 4)
+    for a packed projection, with no copy.  O is a new contiguous [B,H,N,d]
+    tensor unless `out` (any such view) is given; LSE is [B,H,N] float32."""
+    import torch
+    B, H, N, d = q.shape
+    shape, dt, dev = (B, H, N, d), q.dtype, q.device
+    st = []
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        st += _view(t, shape, dt, dev, n)
+    o = torch.empty(shape, dtype=dt, device=dev) if out is None else out
+    st += _view(o, shape, dt, dev, "out")
+    l = (torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None
+         else _check_buf(lse, (B, H, N), torch.float32, dev, "lse"))
+    r = fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, N, d, causal,
+                       scale, st, _stream(stream), _dtype_code(q))
+    if r != FA_OK:
+        raise FAError(r, "fa_fwd_strided")
+    return o, l
+
+
+def backward_strided(q, k, v, o, do, lse, causal: bool, scale: float, ws=None, grads=None, stream=None,
+                     method: int = FA_DQ_HANDOFF):
+    """dQ, dK, dV on [B,H,N,d] views with any strides whose rows are
+    contiguous (as forward_strided).  `grads` may be three such views (for
+    example slices of one packed gradient buffer); otherwise new contiguous
+    [B,H,N,d] tensors are returned."""
+    import torch
+    B, H, N, d = q.shape
+    shape, dt, dev = (B, H, N, d), q.dtype, q.device
+    if grads is None:
+        grads = tuple(torch.empty(shape, dtype=dt, device=dev) for _ in range(3))
+    dq, dk, dv = grads
+    st = []
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        st += _view(t, shape, dt, dev, n)
+    _check_buf(lse, (B, H, N), torch.float32, dev, "lse")
+    ws = workspace(q, FA_LAYOUT_BHND, causal, method) if ws is None else _check_ws(ws, dev)
+    r = fa_bwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, causal, scale, st,
+                       ws.data_ptr(), ws.numel(), _stream(stream), _dtype_code(q))
+    if r != FA_OK:
+        raise FAError(r, "fa_bwd_strided")
     return dq, dk, dv
 
 

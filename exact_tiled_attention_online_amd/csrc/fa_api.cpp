@@ -5,6 +5,8 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <iterator>
+#include <utility>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -37,7 +39,46 @@ int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype, 
   return FA_OK;
 }
 
-fa::RowLayout row_layout(int H, int layout) { return fa::RowLayout{H, layout == FA_LAYOUT_BNHD ? 1 : 0}; }
+// Dense layouts: every tensor [B,H,N,d] or [B,N,H,d]; q, o, dO and dq have
+// Nq rows per head, k, v, dk and dv Nk.  Sizes have passed check_shape.
+fa::RowLayout dense_rows(int H, int N, int d, int layout) {
+  if (layout == FA_LAYOUT_BNHD) return fa::RowLayout{(long long)N * H * d, d, H * d};
+  return fa::RowLayout{(long long)H * N * d, (long long)N * d, d};
+}
+fa::Layouts dense_layouts(int H, int Nq, int Nk, int d, int layout) {
+  const fa::RowLayout a = dense_rows(H, Nq, d, layout), b = dense_rows(H, Nk, d, layout);
+  return fa::Layouts{a, b, b, a, a, a, b, b, H};
+}
+
+// One tensor's layout from a caller's element strides st = {batch, head, row}
+// (rows of d contiguous elements of esize bytes).  Rejects a negative stride,
+// one that breaks the 16-byte alignment of rows, a head whose rows reach
+// 2^31 bytes (the kernels address a head's rows with 32-bit byte offsets), a
+// view reaching past 2^62 bytes, and, for an output, a view in which two rows
+// overlap (checked by the sufficient rule: with the dimensions of more than
+// one entry taken by increasing stride, each stride is at least the extent of
+// everything inside it).
+bool strided_rows(const long long* st, int B, int H, int N, int d, int esize, bool output, fa::RowLayout* out) {
+  const long long sb = st[0], sh = st[1], sn = st[2];
+  const long long unit = 16 / esize;
+  for (long long x : {sb, sh, sn})
+    if (x < 0 || x % unit != 0 || x > (1LL << 40)) return false;
+  if ((__int128)N * sn * esize >= ((__int128)1 << 31)) return false;
+  const __int128 extent = (__int128)(B - 1) * sb + (__int128)(H - 1) * sh + (__int128)(N - 1) * sn + d;
+  if (extent * esize > ((__int128)1 << 62)) return false;
+  if (output) {
+    std::pair<long long, long long> dims[3] = {{sb, B}, {sh, H}, {sn, N}};   // (stride, entries)
+    std::sort(std::begin(dims), std::end(dims));
+    __int128 inner = d;
+    for (const auto& dm : dims) {
+      if (dm.second == 1) continue;
+      if ((__int128)dm.first < inner) return false;
+      inner += (__int128)(dm.second - 1) * dm.first;
+    }
+  }
+  *out = fa::RowLayout{sb, sh, (int)sn};
+  return true;
+}
 
 // Bytes of the dS hand-off buffer per (batch, head): query block i (64 rows)
 // holds 2i + 2 (causal) or ceil(N/32) (otherwise) slices of 4 KB.  The buffer
@@ -174,23 +215,147 @@ int check_split(int B, int H, int Nq, int Nk, int d, int causal, float scale, in
   return FA_OK;
 }
 
+// The forward and backward calls on given layouts, after every check their
+// public forms share (shape, flags, pointers, alignment); the public forms
+// differ only in where the layouts come from.
+int fwd_core(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+             int causal, float scale, void* stream, int dtype, const fa::Layouts& L) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, causal, scale, dtype, FA_LAYOUT_BHND);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == FA_BF16) return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, L, s));
+  return hip_status(fa::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                       static_cast<const float*>(v), static_cast<float*>(o), lse, B * H, N, d,
+                                       causal != 0, scale, L, s));
+}
+
+int pre_core(const void* o, const void* dO, const float* lse, int B, int H, int N, int d, float scale,
+             void* workspace, size_t workspace_bytes, void* stream, int dtype, const fa::Layouts& L) {
+  if (!o || !dO || !lse) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, 0, scale, dtype, FA_LAYOUT_BHND);
+  if (st != FA_OK) return st;
+  if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(lse, 4)) return FA_ERR_INVALID;
+  // the statistics sit at the same place for every method; only the atomic
+  // method needs more here (its accumulator is cleared)
+  const bool atomic = dq_method(B, H, N, d, false, dtype, 0, false) == FA_DQ_ATOMIC;
+  const int method = atomic ? FA_DQ_ATOMIC : FA_DQ_RECOMPUTE;
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, false, dtype, method)) return FA_ERR_WORKSPACE;
+  const Workspace w = carve(workspace, B, H, N, d, false, dtype, method);
+  float* dq_acc = atomic ? reinterpret_cast<float*>(w.region) : nullptr;
+  return hip_status(fa::launch_bwd_pre(o, dO, lse, w.ndrow, w.nlse, dq_acc, B * H, N, d, scale, dtype == FA_FP32,
+                                       L, static_cast<hipStream_t>(stream)));
+}
+
+int dkdv_core(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dk, void* dv,
+              int B, int H, int N, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+              void* stream, int dtype, const fa::Layouts& L) {
+  if (!q || !k || !v || !dO || !lse || !dk || !dv) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, causal, scale, dtype, FA_LAYOUT_BHND);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dk, 16) ||
+      !aligned(dv, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  const int method = dq_method(B, H, N, d, causal != 0, dtype, workspace_bytes, false);
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, dtype, method)) return FA_ERR_WORKSPACE;
+  const Workspace w = carve(workspace, B, H, N, d, causal != 0, dtype, method);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == FA_FP32)
+    return hip_status(fa::launch_bwd_kv_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                            static_cast<const float*>(v), static_cast<const float*>(dO), lse,
+                                            w.ndrow, static_cast<float*>(dk), static_cast<float*>(dv), B * H, N,
+                                            d, causal != 0, scale, L, s));
+  const fa::DsOut ds = method == FA_DQ_HANDOFF ? ds_out(w, B, H, N, causal != 0) : fa::DsOut{};
+  return hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.nlse, w.ndrow, reinterpret_cast<float*>(w.region), dk, dv,
+                                        B * H, N, d, causal != 0, scale, method == FA_DQ_ATOMIC, L, s, nullptr, ds));
+}
+
+int dq_core(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq, int B, int H,
+            int N, int d, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype,
+            const fa::Layouts& L) {
+  if (!q || !k || !v || !dO || !lse || !dq) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, causal, scale, dtype, FA_LAYOUT_BHND);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dq, 16) ||
+      !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  const int method = dq_method(B, H, N, d, causal != 0, dtype, workspace_bytes, false);
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, dtype, method)) return FA_ERR_WORKSPACE;
+  const Workspace w = carve(workspace, B, H, N, d, causal != 0, dtype, method);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == FA_FP32)
+    return hip_status(fa::launch_bwd_q_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                           static_cast<const float*>(v), static_cast<const float*>(dO), lse,
+                                           w.ndrow, static_cast<float*>(dq), B * H, N, d, causal != 0, scale, L,
+                                           s));
+  if (method == FA_DQ_ATOMIC)
+    return hip_status(fa::launch_dq_convert(reinterpret_cast<float*>(w.region), dq, B * H, N, d, scale, L, s));
+  if (method == FA_DQ_HANDOFF)
+    return hip_status(fa::launch_bwd_dq_ds(ds_out(w, B, H, N, causal != 0), k, dq, B * H, N, d, causal != 0, scale,
+                                           L, s));
+  return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.nlse, w.ndrow, dq, B * H, N, d, causal != 0, scale, L, s));
+}
+
+int bwd_core(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+             void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
+             size_t workspace_bytes, void* stream, int dtype, const fa::Layouts& L) {
+  // all checks first, so that a rejected call launches nothing
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID;
+  const int st = check_shape(B, H, N, d, causal, scale, dtype, FA_LAYOUT_BHND);
+  if (st != FA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID;
+  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, dtype,
+                    dq_method(B, H, N, d, causal != 0, dtype, workspace_bytes, false)))
+    return FA_ERR_WORKSPACE;
+  int r = pre_core(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype, L);
+  if (r != FA_OK) return r;
+  r = dkdv_core(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype, L);
+  if (r != FA_OK) return r;
+  return dq_core(q, k, v, dO, lse, dq, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype, L);
+}
+
+// Layouts of the strided calls: strides holds 3 values per tensor, for the
+// tensors of `slots` (members of fa::Layouts) in that order; `outputs` marks
+// the slots the call writes.  Unused slots keep the first tensor's layout.
+bool strided_layouts(const long long* strides, std::initializer_list<fa::RowLayout fa::Layouts::*> slots,
+                     unsigned outputs, int B, int H, int N, int d, int dtype, fa::Layouts* L) {
+  if (!strides) return false;
+  const int esize = dtype == FA_FP32 ? 4 : 2;
+  int i = 0;
+  for (auto slot : slots) {
+    fa::RowLayout r{};
+    if (!strided_rows(strides + 3 * i, B, H, N, d, esize, (outputs >> i) & 1u, &r)) return false;
+    if (i == 0) *L = fa::Layouts{r, r, r, r, r, r, r, r, H};
+    L->*slot = r;
+    ++i;
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
            int causal, float scale, void* stream, int dtype, int layout) {
-  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
   const int st = check_shape(B, H, N, d, causal, scale, dtype, layout);
   if (st != FA_OK) return st;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+  return fwd_core(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype, dense_layouts(H, N, N, d, layout));
+}
+
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   int causal, float scale, const long long* strides, void* stream, int dtype) {
+  const int st = check_shape(B, H, N, d, causal, scale, dtype, FA_LAYOUT_BHND);
+  if (st != FA_OK) return st;
+  fa::Layouts L{};
+  if (!strided_layouts(strides, {&fa::Layouts::q, &fa::Layouts::k, &fa::Layouts::v, &fa::Layouts::o}, 0x8u, B, H,
+                       N, d, dtype, &L))
     return FA_ERR_INVALID;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == FA_BF16)
-    return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, row_layout(H, layout), s));
-  return hip_status(fa::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                                       static_cast<const float*>(v), static_cast<float*>(o), lse, B * H, N, d,
-                                       causal != 0, scale, row_layout(H, layout), s));
+  return fwd_core(q, k, v, o, lse, B, H, N, d, causal, scale, stream, dtype, L);
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int causal, int dtype, int dq_method) {
@@ -216,92 +381,51 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
 int fa_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int N, int d,
                       float scale, void* workspace, size_t workspace_bytes, void* stream, int dtype,
                       int layout) {
-  if (!o || !dO || !lse) return FA_ERR_INVALID;
   const int st = check_shape(B, H, N, d, 0, scale, dtype, layout);
   if (st != FA_OK) return st;
-  if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(lse, 4)) return FA_ERR_INVALID;
-  // the statistics sit at the same place for every method; only the atomic
-  // method needs more here (its accumulator is cleared)
-  const bool atomic = dq_method(B, H, N, d, false, dtype, 0, false) == FA_DQ_ATOMIC;
-  const int method = atomic ? FA_DQ_ATOMIC : FA_DQ_RECOMPUTE;
-  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, false, dtype, method)) return FA_ERR_WORKSPACE;
-  const Workspace w = carve(workspace, B, H, N, d, false, dtype, method);
-  float* dq_acc = atomic ? reinterpret_cast<float*>(w.region) : nullptr;
-  return hip_status(fa::launch_bwd_pre(o, dO, lse, w.ndrow, w.nlse, dq_acc, B * H, N, d, scale,
-                                       dtype == FA_FP32, row_layout(H, layout), static_cast<hipStream_t>(stream)));
+  return pre_core(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype,
+                  dense_layouts(H, N, N, d, layout));
 }
 
 int fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dk,
                 void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
                 size_t workspace_bytes, void* stream, int dtype, int layout) {
-  if (!q || !k || !v || !dO || !lse || !dk || !dv) return FA_ERR_INVALID;
   const int st = check_shape(B, H, N, d, causal, scale, dtype, layout);
   if (st != FA_OK) return st;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dk, 16) ||
-      !aligned(dv, 16) || !aligned(lse, 4))
-    return FA_ERR_INVALID;
-  const int method = dq_method(B, H, N, d, causal != 0, dtype, workspace_bytes, false);
-  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, dtype, method)) return FA_ERR_WORKSPACE;
-  const Workspace w = carve(workspace, B, H, N, d, causal != 0, dtype, method);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == FA_FP32)
-    return hip_status(fa::launch_bwd_kv_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                                            static_cast<const float*>(v), static_cast<const float*>(dO), lse,
-                                            w.ndrow, static_cast<float*>(dk), static_cast<float*>(dv), B * H, N,
-                                            d, causal != 0, scale, row_layout(H, layout), s));
-  const fa::DsOut ds = method == FA_DQ_HANDOFF ? ds_out(w, B, H, N, causal != 0) : fa::DsOut{};
-  return hip_status(fa::launch_bwd_bf16(q, k, v, dO, w.nlse, w.ndrow, reinterpret_cast<float*>(w.region), dk, dv,
-                                        B * H, N, d, causal != 0, scale, method == FA_DQ_ATOMIC,
-                                        row_layout(H, layout), s, nullptr, ds));
+  return dkdv_core(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype,
+                   dense_layouts(H, N, N, d, layout));
 }
 
 int fa_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, void* dq, int B,
               int H, int N, int d, int causal, float scale, void* workspace, size_t workspace_bytes, void* stream,
               int dtype, int layout) {
-  if (!q || !k || !v || !dO || !lse || !dq) return FA_ERR_INVALID;
   const int st = check_shape(B, H, N, d, causal, scale, dtype, layout);
   if (st != FA_OK) return st;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(dq, 16) ||
-      !aligned(lse, 4))
-    return FA_ERR_INVALID;
-  const int method = dq_method(B, H, N, d, causal != 0, dtype, workspace_bytes, false);
-  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, dtype, method)) return FA_ERR_WORKSPACE;
-  const Workspace w = carve(workspace, B, H, N, d, causal != 0, dtype, method);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const fa::RowLayout lay = row_layout(H, layout);
-  if (dtype == FA_FP32)
-    return hip_status(fa::launch_bwd_q_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                                           static_cast<const float*>(v), static_cast<const float*>(dO), lse,
-                                           w.ndrow, static_cast<float*>(dq), B * H, N, d, causal != 0, scale, lay,
-                                           s));
-  if (method == FA_DQ_ATOMIC)
-    return hip_status(fa::launch_dq_convert(reinterpret_cast<float*>(w.region), dq, B * H, N, d, scale, lay, s));
-  if (method == FA_DQ_HANDOFF)
-    return hip_status(fa::launch_bwd_dq_ds(ds_out(w, B, H, N, causal != 0), k, dq, B * H, N, d, causal != 0, scale, lay,
-                                           s));
-  return hip_status(fa::launch_bwd_dq(q, k, v, dO, w.nlse, w.ndrow, dq, B * H, N, d, causal != 0, scale, lay, s));
+  return dq_core(q, k, v, dO, lse, dq, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype,
+                 dense_layouts(H, N, N, d, layout));
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
            void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
            size_t workspace_bytes, void* stream, int dtype, int layout) {
-  // all checks first, so that a rejected call launches nothing
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_INVALID;
   const int st = check_shape(B, H, N, d, causal, scale, dtype, layout);
   if (st != FA_OK) return st;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dO, 16) ||
-      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+  return bwd_core(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream,
+                  dtype, dense_layouts(H, N, N, d, layout));
+}
+
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+                   const long long* strides, void* workspace, size_t workspace_bytes, void* stream, int dtype) {
+  const int st = check_shape(B, H, N, d, causal, scale, dtype, FA_LAYOUT_BHND);
+  if (st != FA_OK) return st;
+  using L8 = fa::Layouts;
+  fa::Layouts L{};
+  if (!strided_layouts(strides, {&L8::q, &L8::k, &L8::v, &L8::o, &L8::g, &L8::dq, &L8::dk, &L8::dv}, 0xE0u, B, H, N,
+                       d, dtype, &L))
     return FA_ERR_INVALID;
-  if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, dtype,
-                    dq_method(B, H, N, d, causal != 0, dtype, workspace_bytes, false)))
-    return FA_ERR_WORKSPACE;
-  int r = fa_bwd_preprocess(o, dO, lse, B, H, N, d, scale, workspace, workspace_bytes, stream, dtype, layout);
-  if (r != FA_OK) return r;
-  r = fa_bwd_dkdv(q, k, v, dO, lse, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype,
-                  layout);
-  if (r != FA_OK) return r;
-  return fa_bwd_dq(q, k, v, dO, lse, dq, B, H, N, d, causal, scale, workspace, workspace_bytes, stream, dtype,
-                   layout);
+  return bwd_core(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, causal, scale, workspace, workspace_bytes, stream,
+                  dtype, L);
 }
 
 namespace {
@@ -321,7 +445,8 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
   const fa::DropArgs dr = drop_args(drop_t, seed, offset);
-  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale, row_layout(H, layout),
+  return hip_status(fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, causal != 0, scale,
+                                        dense_layouts(H, N, N, d, layout),
                                         static_cast<hipStream_t>(stream), &dr));
 }
 
@@ -340,7 +465,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
   const int method = dq_method(B, H, N, d, causal != 0, FA_BF16, workspace_bytes, true);
   if (!workspace_ok(workspace, workspace_bytes, B, H, N, d, causal != 0, FA_BF16, method)) return FA_ERR_WORKSPACE;
   const Workspace w = carve(workspace, B, H, N, d, causal != 0, FA_BF16, method);
-  const fa::RowLayout lay = row_layout(H, layout);
+  const fa::Layouts lay = dense_layouts(H, N, N, d, layout);
   const fa::DropArgs dr = drop_args(drop_t, seed, offset);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const fa::DsOut ds = method == FA_DQ_HANDOFF ? ds_out(w, B, H, N, causal != 0) : fa::DsOut{};
@@ -369,7 +494,8 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
   return hip_status(fa::launch_fwd_fp8(q, k, v, o, lse, B * H, N, causal != 0, scale, descale_q, descale_k,
-                                       descale_v, row_layout(H, layout), static_cast<hipStream_t>(stream)));
+                                       descale_v, dense_layouts(H, N, N, d, layout),
+                                       static_cast<hipStream_t>(stream)));
 }
 
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
@@ -390,7 +516,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
     return FA_ERR_WORKSPACE;
   const SplitPlan p = split_plan(workspace, B, H, Nq, Nk, d, num_splits);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const fa::RowLayout lay = row_layout(H, layout);
+  const fa::Layouts lay = dense_layouts(H, Nq, Nk, d, layout);
   const int r = hip_status(fa::launch_fwd_split_bf16(q, k, v, p.opart, p.lpart, B * H, Nq, Nk, d, causal != 0,
                                                      scale, p.nsplit, p.span, lay, s));
   if (r != FA_OK) return r;
@@ -419,7 +545,7 @@ int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o, flo
     return FA_ERR_WORKSPACE;
   const SplitPlan p = split_plan(workspace, B, H, Nq, Nk, d, num_splits, fa::kSplitBC8);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const fa::RowLayout lay = row_layout(H, layout);
+  const fa::Layouts lay = dense_layouts(H, Nq, Nk, d, layout);
   const int r = hip_status(fa::launch_fwd_split_fp8(q, k, v, p.opart, p.lpart, B * H, Nq, Nk, causal != 0, scale,
                                                     descale_q, descale_k, descale_v, p.nsplit, p.span, lay, s));
   if (r != FA_OK) return r;

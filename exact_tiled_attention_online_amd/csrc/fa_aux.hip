@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
                                                       const float* __restrict__ lse,
                                                       float* __restrict__ ndrow, float* __restrict__ nlse,
                                                       float* __restrict__ dq_acc, size_t rows, float inv_scale,
-                                                      int N, RowLayout lay) {
+                                                      int N, Layouts lay) {
   constexpr int LPR = lanes_per_row<D>();   // lanes per row (D/8 of them hold 8 elements each)
   constexpr int RPB = 256 / LPR;            // rows per block
   const int tid = threadIdx.x;
@@ -48,15 +48,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
     // row = hb*N + n of the [B*H][N] statistics; the tensor row is found
     // through the layout
     const int hb = (int)(row / N), n = (int)(row - (size_t)hb * N);
-    const size_t base = lay.head_off(hb, N, D) + (size_t)n * lay.row_stride(D) + part * 8;
+    const size_t obase = lay.off(lay.o, hb) + (size_t)n * lay.o.sn + part * 8;
+    const size_t gbase = lay.off(lay.g, hb) + (size_t)n * lay.g.sn + part * 8;
     if constexpr (sizeof(T) == 2) {
-      const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(O + base);
-      const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(dO + base);
+      const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(O + obase);
+      const bf16x8 g8 = *reinterpret_cast<const bf16x8*>(dO + gbase);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf((float)o8[e], (float)g8[e], acc);
     } else {
-      const f32x4* o4 = reinterpret_cast<const f32x4*>(O + base);
-      const f32x4* g4 = reinterpret_cast<const f32x4*>(dO + base);
+      const f32x4* o4 = reinterpret_cast<const f32x4*>(O + obase);
+      const f32x4* g4 = reinterpret_cast<const f32x4*>(dO + gbase);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const f32x4 a = o4[h], b = g4[h];
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
 }
 
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ndrow, float* nlse,
-                          float* dq_acc, int BH, int N, int d, float scale, bool fp32, RowLayout lay,
+                          float* dq_acc, int BH, int N, int d, float scale, bool fp32, Layouts lay,
                           hipStream_t stream) {
   const float inv_scale = 1.f / scale;
   const size_t rows = (size_t)BH * N;
@@ -105,14 +106,14 @@ hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float
 }
 
 __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
-                                                         size_t n8, float scale, int N, int D, RowLayout lay) {
+                                                         size_t n8, float scale, int N, int D, Layouts lay) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
   // i = (hb*N + n)*(D/8) + c8 in the contiguous accumulator
   const int c8 = (int)(i % (D / 8));
   const size_t row = i / (D / 8);
   const int hb = (int)(row / N), n = (int)(row - (size_t)hb * N);
-  const size_t out = lay.head_off(hb, N, D) + (size_t)n * lay.row_stride(D) + 8 * c8;
+  const size_t out = lay.off(lay.dq, hb) + (size_t)n * lay.dq.sn + 8 * c8;
   const f32x4* a = reinterpret_cast<const f32x4*>(acc) + 2 * i;
   const f32x4 x = a[0], y = a[1];
   bf16x8 r;
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
   *reinterpret_cast<bf16x8*>(dq + out) = r;
 }
 
-hipError_t launch_dq_convert(const float* dq_acc, void* dq, int BH, int N, int d, float scale, RowLayout lay,
+hipError_t launch_dq_convert(const float* dq_acc, void* dq, int BH, int N, int d, float scale, Layouts lay,
                              hipStream_t stream) {
   const size_t n8 = (size_t)BH * N * d / 8;
   const dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
@@ -136,7 +137,7 @@ template <int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict__ opart,
                                                         const float* __restrict__ lpart, bf16* __restrict__ O,
                                                         float* __restrict__ LSE, int rows, int N, int nsplit,
-                                                        RowLayout lay) {
+                                                        Layouts lay) {
   constexpr int LPR = lanes_per_row<D>();   // lanes per row (D/8 of them hold 8 elements each)
   constexpr int RPB = 256 / LPR;            // rows per block
   const int tid = threadIdx.x;
@@ -167,12 +168,12 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict_
   bf16x8 r;
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = (bf16)(acc[e] * inv);
-  *reinterpret_cast<bf16x8*>(O + lay.head_off(hb, N, D) + (size_t)n * lay.row_stride(D) + part * 8) = r;
+  *reinterpret_cast<bf16x8*>(O + lay.off(lay.o, hb) + (size_t)n * lay.o.sn + part * 8) = r;
   if (part == 0) LSE[row] = m + log2_fast(wsum) * kLn2;
 }
 
 hipError_t launch_fwd_merge(const float* opart, const float* lpart, void* o, float* lse, int BH, int Nq,
-                            int d, int nsplit, RowLayout lay, hipStream_t stream) {
+                            int d, int nsplit, Layouts lay, hipStream_t stream) {
   const int rows = BH * Nq;
   auto go = [&](auto dc) {
     constexpr int D = decltype(dc)::value;

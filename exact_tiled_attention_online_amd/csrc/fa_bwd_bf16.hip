@@ -8,7 +8,7 @@ namespace fa {
 template <bool DQA>
 static hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, const void* dO,
                                 const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
-                                int BH, int N, int d, bool causal, float scale, RowLayout lay,
+                                int BH, int N, int d, bool causal, float scale, Layouts lay,
                                 hipStream_t stream, const DropArgs* drop, DsOut ds) {
   if (d == 128)
     return causal ? launch_bwd_bf16_t<128, true, DQA>(q, k, v, dO, nlse, ndrow, dq_acc, dk, dv, BH, N, scale, lay, stream, drop, ds)
@@ -25,7 +25,7 @@ static hipError_t launch_bwd_kv(const void* q, const void* k, const void* v, con
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dO,
                            const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
-                           int BH, int N, int d, bool causal, float scale, bool dq_atomic, RowLayout lay,
+                           int BH, int N, int d, bool causal, float scale, bool dq_atomic, Layouts lay,
                            hipStream_t stream, const DropArgs* drop, DsOut ds) {
   // neither the dropout backward nor the hand-off has an atomic-dQ form (the
   // caller never asks for them)

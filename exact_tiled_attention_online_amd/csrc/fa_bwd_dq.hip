@@ -36,7 +36,7 @@ template <int D, bool CAUSAL, int NW, bool DROP>
 FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                         const bf16* __restrict__ dO, const float* __restrict__ NLSE,
                         const float* __restrict__ NDR, bf16* __restrict__ dQ, int BH, int N, int nqb,
-                        float scale, float c, RowLayout lay, DropArgs dr) {
+                        float scale, float c, Layouts lay, DropArgs dr) {
   constexpr int BR = 32 * NW, BC = 64;
   constexpr int ROWB = lds_pitch<D>();   // LDS bytes per row (d * 2, or 256 for d = 96)
   constexpr int KS = D / 16;         // K-steps of the S and dP products
@@ -53,17 +53,16 @@ FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const TileBases<ROWB> tb(lane);
-  const int RS = lay.row_stride(D);      // elements between a head's rows
-  const TileFetch<ROWB, BC, NW, D / 8> fetch(wave, lane, RS * 2);
+  const TileFetch<ROWB, BC, NW, D / 8> fetch(wave, lane, lay.k.sn * 2);   // K rows; V rows at vrs
+  const unsigned vrs = (unsigned)lay.v.sn * 2u;
   const int bid = blockIdx.x;
   const int head = bid % BH;
   // causal: the longest query blocks are dispatched first
   const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
-  const size_t hoff = lay.head_off(head, N, D);
-  const bf16* Qh = Q + hoff;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
-  const bf16* Gh = dO + hoff;
+  const bf16* Qh = Q + lay.off(lay.q, head);
+  const bf16* Kh = K + lay.off(lay.k, head);
+  const bf16* Vh = V + lay.off(lay.v, head);
+  const bf16* Gh = dO + lay.off(lay.g, head);
 
   const int q0 = qb * BR + wave * 32;   // first query row of this wave
   const int qrow = q0 + l32;            // the query row this lane's statistics belong to
@@ -73,8 +72,8 @@ FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, 
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     if (qrow < N) {
-      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * RS + 16 * s + 8 * h);
-      gf[s] = *reinterpret_cast<const bf16x8*>(Gh + (size_t)qrow * RS + 16 * s + 8 * h);
+      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * lay.q.sn + 16 * s + 8 * h);
+      gf[s] = *reinterpret_cast<const bf16x8*>(Gh + (size_t)qrow * lay.g.sn + 16 * s + 8 * h);
     } else {
       qf[s] = bf16x8{};
       gf[s] = bf16x8{};
@@ -108,7 +107,7 @@ FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, 
     const char* Vt = b ? sV1 : sV0;
     if (j + 1 < ntiles) {
       fetch(Kh, (j + 1) * BC, N, b ? sK0 : sK1);
-      fetch(Vh, (j + 1) * BC, N, b ? sV0 : sV1);
+      fetch(Vh, (j + 1) * BC, N, b ? sV0 : sV1, vrs);
       FA_DEBUG_BARRIER();
     }
     if (j < wave_tiles) {
@@ -216,7 +215,7 @@ FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, 
   };
 
   fetch(Kh, 0, N, sK0);
-  fetch(Vh, 0, N, sV0);
+  fetch(Vh, 0, N, sV0, vrs);
   __syncthreads();
   for (int j = 0;;) {
     body(IC<0>{}, j);
@@ -227,7 +226,7 @@ FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, 
 
   if (qrow >= N) return;
   // acc[t][4*i+jj] = dQ^T[d = 32t + 8i + 4h + jj][query qrow]
-  bf16* row = dQ + hoff + (size_t)qrow * RS;
+  bf16* row = dQ + lay.off(lay.dq, head) + (size_t)qrow * lay.dq.sn;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -252,7 +251,7 @@ template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, (dq_min_blocks<D, NW>())) void bwd_dq_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
-    bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, RowLayout lay) {
+    bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, Layouts lay) {
   bwd_dq_body<D, CAUSAL, NW, false>(Q, K, V, dO, NLSE, NDR, dQ, BH, N, nqb, scale, c, lay, DropArgs{});
 }
 
@@ -260,14 +259,14 @@ template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, (dq_min_blocks<D, NW>())) void bwd_dq_dropout_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
-    bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, RowLayout lay, DropArgs dr) {
+    bf16* __restrict__ dQ, int BH, int N, int nqb, float scale, float c, Layouts lay, DropArgs dr) {
   bwd_dq_body<D, CAUSAL, NW, true>(Q, K, V, dO, NLSE, NDR, dQ, BH, N, nqb, scale, c, lay, dr);
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_dq_t(const void* q, const void* k, const void* v, const void* dO,
                                   const float* nlse, const float* ndrow, void* dq, int BH, int N, float scale,
-                                  RowLayout lay, hipStream_t stream, const DropArgs* drop) {
+                                  Layouts lay, hipStream_t stream, const DropArgs* drop) {
   constexpr int NW = D == 256 ? 4 : FA_DQ_NW, BR = 32 * NW;   // d = 256: one wave per SIMD
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
@@ -285,7 +284,7 @@ static hipError_t launch_bwd_dq_t(const void* q, const void* k, const void* v, c
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                          const float* ndrow, void* dq, int BH, int N, int d, bool causal, float scale,
-                         RowLayout lay, hipStream_t stream, const DropArgs* drop) {
+                         Layouts lay, hipStream_t stream, const DropArgs* drop) {
   if (d == 128)
     return causal ? launch_bwd_dq_t<128, true>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop)
                   : launch_bwd_dq_t<128, false>(q, k, v, dO, nlse, ndrow, dq, BH, N, scale, lay, stream, drop);

@@ -36,7 +36,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const char* __restrict__ dsbuf, size_t ds_head_bytes,
                                                             int nks, const bf16* __restrict__ K,
                                                             bf16* __restrict__ dQ, int BH, int N, int nqb,
-                                                            float scale, RowLayout lay) {
+                                                            float scale, Layouts lay) {
   constexpr int ROWB = lds_pitch<D>();   // LDS bytes per K row (d * 2, or 256 for d = 96)
   constexpr int DT = D / 32;             // 32-row tiles of dQ^T
   constexpr int KC = 64;                 // keys per stage
@@ -65,10 +65,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const char* __restric
   auto slices = [&](int blk) { return CAUSAL ? min(2 * blk + 2, nks) : nks; };
   const int nsl_w = has_blk ? slices(b) : 0;
   const int nstage = (slices(min(2 * I + 1, nqb - 1)) + 1) / 2;
-  const size_t hoff = lay.head_off(head, N, D);
-  const bf16* Kh = K + hoff;
-  const int RS = lay.row_stride(D);
-  const TileFetch<ROWB, KC, 4, D / 8> kfetch(wave, lane, RS * 2);
+  const bf16* Kh = K + lay.off(lay.k, head);
+  const TileFetch<ROWB, KC, 4, D / 8> kfetch(wave, lane, lay.k.sn * 2);
   const TileBases<ROWB> tb(lane);
 
   // the wave's block in the buffer (block 0 of the head for a wave without
@@ -188,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const char* __restric
   const int qrow = 64 * b + 32 * qt + l32;
   if (!has_blk || qrow >= N) return;
   // acc[t][4*i+jj] = dQ^T[d = 32t + 8i + 4h + jj][query qrow]
-  bf16* row = dQ + hoff + (size_t)qrow * RS;
+  bf16* row = dQ + lay.off(lay.dq, head) + (size_t)qrow * lay.dq.sn;
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -203,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_kernel(const char* __restric
 }
 
 template <int D, bool CAUSAL>
-static hipError_t launch_dq_ds_t(DsOut ds, const void* k, void* dq, int BH, int N, float scale, RowLayout lay,
+static hipError_t launch_dq_ds_t(DsOut ds, const void* k, void* dq, int BH, int N, float scale, Layouts lay,
                                  hipStream_t stream) {
   const int nqb = (N + 63) / 64, nI = (nqb + 1) / 2;
   const dim3 grid((unsigned)(nI * BH)), block(256);
@@ -213,7 +211,7 @@ static hipError_t launch_dq_ds_t(DsOut ds, const void* k, void* dq, int BH, int 
 }
 
 hipError_t launch_bwd_dq_ds(DsOut ds, const void* k, void* dq, int BH, int N, int d, bool causal, float scale,
-                            RowLayout lay, hipStream_t stream) {
+                            Layouts lay, hipStream_t stream) {
   auto go = [&](auto dc) {
     constexpr int D = decltype(dc)::value;
     return causal ? launch_dq_ds_t<D, true>(ds, k, dq, BH, N, scale, lay, stream)

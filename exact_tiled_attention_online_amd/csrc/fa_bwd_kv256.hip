@@ -12,7 +12,7 @@ namespace fa {
 
 hipError_t launch_bwd_kv256(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                             const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
-                            RowLayout lay, hipStream_t stream, const DropArgs* drop, DsOut ds) {
+                            Layouts lay, hipStream_t stream, const DropArgs* drop, DsOut ds) {
   return causal ? launch_bwd_bf16_t<256, true, false>(q, k, v, dO, nlse, ndrow, nullptr, dk, dv, BH, N, scale, lay,
                                                       stream, drop, ds)
                 : launch_bwd_bf16_t<256, false, false>(q, k, v, dO, nlse, ndrow, nullptr, dk, dv, BH, N, scale, lay,

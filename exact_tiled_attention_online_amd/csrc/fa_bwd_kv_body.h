@@ -78,7 +78,7 @@ template <int D, bool CAUSAL, bool DQA, bool DROP, bool DSO>
 FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                           const bf16* __restrict__ dO, const float* __restrict__ NLSE,
                           const float* __restrict__ NDR, float* __restrict__ dQacc, bf16* __restrict__ dK,
-                          bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, RowLayout lay,
+                          bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, Layouts lay,
                           DropArgs dr, DsOut dso) {
   static_assert(!(DQA && DROP), "the dropout backward takes dQ from another kernel");
   static_assert(!(DQA && DSO), "dQ comes from atomics or from the hand-off, not both");
@@ -116,8 +116,8 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
   static_assert(DH == 1 || DTW == TileBases<ROWB>::DTB, "one part of d per set of tile bases");
   const int doff = DH > 1 ? 256 * __builtin_amdgcn_readfirstlane(dpart) : 0;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the same value, known uniform
-  const int RS = lay.row_stride(D);      // elements between a head's rows
-  const TileFetch<ROWB, BR, 4, CH> qfetch(wave_u, lane, RS * 2);
+  const TileFetch<ROWB, BR, 4, CH> qfetch(wave_u, lane, lay.q.sn * 2);   // Q rows; dO rows at grs
+  const unsigned grs = (unsigned)lay.g.sn * 2u;
   // Work items.  Causal: item c of a head is the key-block pair
   // (c, nkb-1-c), whose query walks together always cover the same number of
   // blocks, so every workgroup does the same work; the first block is walked
@@ -133,11 +133,10 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int item = (W % 8 == 0) ? (bid % 8) * (W / 8) + bid / 8 : bid;
   const int head = item / P, c_item = item % P;
   const int nparts = (CAUSAL && 2 * c_item + 1 != nkb) ? 2 : 1;
-  const size_t hoff = lay.head_off(head, N, D);
-  const bf16* Qh = Q + hoff;
-  const bf16* Kh = K + hoff;
-  const bf16* Vh = V + hoff;
-  const bf16* Gh = dO + hoff;
+  const bf16* Qh = Q + lay.off(lay.q, head);
+  const bf16* Kh = K + lay.off(lay.k, head);
+  const bf16* Vh = V + lay.off(lay.v, head);
+  const bf16* Gh = dO + lay.off(lay.g, head);
   const float* Lh = NLSE + (size_t)head * N;   // -LSE / scale
   const float* Dh = NDR + (size_t)head * N;    // -D
   float* dQh = dQacc + (size_t)head * N * D;   // contiguous [B*H][N][d] accumulator
@@ -171,7 +170,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
         const int row = ci / CH, ch = ci % CH;
         const int kv = kv0 + row;
         u32x4 x = u32x4{0, 0, 0, 0};
-        if (kv < N) x = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv * RS + ch * 8);
+        if (kv < N) x = *reinterpret_cast<const u32x4*>(Kh + (size_t)kv * lay.k.sn + ch * 8);
         *reinterpret_cast<u32x4*>(&sK[tile_off<ROWB>(row, ch)]) = x;
       }
     }
@@ -181,8 +180,8 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if (kvrow < N) {
-        kf[s] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kvrow * RS + 16 * s + 8 * h);
-        vf[s] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kvrow * RS + 16 * s + 8 * h);
+        kf[s] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kvrow * lay.k.sn + 16 * s + 8 * h);
+        vf[s] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kvrow * lay.v.sn + 16 * s + 8 * h);
       } else {
         kf[s] = bf16x8{};
         vf[s] = bf16x8{};
@@ -225,7 +224,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
     auto fetch = [&](int i, char* dQt, char* dGt, float* dL, float* dD) {
       const int qb0 = i * BR;
       qfetch(Qh, qb0, N, dQt);
-      qfetch(Gh, qb0, N, dGt);
+      qfetch(Gh, qb0, N, dGt, grs);
       if (qb0 + BR <= N) {
         if (wave_u == 0) dma4_buf(raw_rsrc(Lh), 4 * ln, 4 * qb0, dL);
         if (wave_u == 1) dma4_buf(raw_rsrc(Dh), 4 * ln, 4 * qb0, dD);
@@ -523,14 +522,15 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
             const float x = pass == 0 ? dk[dt][r] * scale : (DROP ? dv[dt][r] * dr.keep_scale : dv[dt][r]);
             stg[row * D + c0 + 32 * dt + l32] = (bf16)x;
           }
-        bf16* dst = (pass == 0 ? dK : dV) + hoff;
+        bf16* dst = pass == 0 ? dK + lay.off(lay.dk, head) : dV + lay.off(lay.dv, head);
+        const int ors = pass == 0 ? lay.dk.sn : lay.dv.sn;
         constexpr int OPW = 32 * CW / 64;   // 16-byte stores per lane
 #pragma unroll
         for (int p = 0; p < OPW; ++p) {
           const int ci = p * 64 + ln;
           const int row = ci / CW, ch = ci % CW;
           if (kvw + row < N)
-            *reinterpret_cast<u32x4*>(dst + (size_t)(kvw + row) * RS + c0 + ch * 8) =
+            *reinterpret_cast<u32x4*>(dst + (size_t)(kvw + row) * ors + c0 + ch * 8) =
                 *reinterpret_cast<const u32x4*>(&stg[row * D + c0 + ch * 8]);
         }
       }
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
     float* __restrict__ dQacc, bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb,
-    float scale, float c, RowLayout lay) {
+    float scale, float c, Layouts lay) {
   bwd_bf16_body<D, CAUSAL, DQA, false, false>(Q, K, V, dO, NLSE, NDR, dQacc, dK, dV, BH, N, nqb, scale, c, lay,
                                               DropArgs{}, DsOut{});
 }
@@ -557,7 +557,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_bf16_ds_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, RowLayout lay,
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, Layouts lay,
     DsOut dso) {
   bwd_bf16_body<D, CAUSAL, false, false, true>(Q, K, V, dO, NLSE, NDR, nullptr, dK, dV, BH, N, nqb, scale, c,
                                                lay, DropArgs{}, dso);
@@ -567,32 +567,50 @@ template <int D, bool CAUSAL, bool DSO>
 __global__ __launch_bounds__(256, 1) void bwd_bf16_dropout_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ NLSE, const float* __restrict__ NDR,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, RowLayout lay,
+    bf16* __restrict__ dK, bf16* __restrict__ dV, int BH, int N, int nqb, float scale, float c, Layouts lay,
     DropArgs dr, DsOut dso) {
   bwd_bf16_body<D, CAUSAL, false, true, DSO>(Q, K, V, dO, NLSE, NDR, nullptr, dK, dV, BH, N, nqb, scale, c, lay,
                                              dr, dso);
 }
 
+// Grid of the key/value-outer kernels: one workgroup per work item (a pair of
+// key blocks when causal, one otherwise) of each head.
+template <int D, bool CAUSAL>
+static dim3 bwd_kv_grid(int BH, int N) {
+  constexpr int BC = D == 256 ? 64 : 128;   // keys per workgroup
+  const int nkb = (N + BC - 1) / BC;
+  return dim3((unsigned)((CAUSAL ? (nkb + 1) / 2 : nkb) * BH));
+}
+
+template <int D, bool CAUSAL, bool DSO>
+static hipError_t launch_bwd_dropout_t(const void* q, const void* k, const void* v, const void* dO,
+                                       const float* nlse, const float* ndrow, void* dk, void* dv, int BH, int N,
+                                       float scale, Layouts lay, hipStream_t stream, const DropArgs& drop,
+                                       DsOut ds) {
+  const dim3 grid = bwd_kv_grid<D, CAUSAL>(BH, N), block(256);
+  hipLaunchKernelGGL((bwd_bf16_dropout_kernel<D, CAUSAL, DSO>), grid, block, 0, stream, (const bf16*)q,
+                     (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH, N, (N + 63) / 64, scale, scale * kLog2e, lay, drop,
+                     DSO ? ds : DsOut{});
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, bool DQA>
 static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v, const void* dO,
                                     const float* nlse, const float* ndrow, float* dq_acc, void* dk,
-                                    void* dv, int BH, int N, float scale, RowLayout lay, hipStream_t stream,
+                                    void* dv, int BH, int N, float scale, Layouts lay, hipStream_t stream,
                                     const DropArgs* drop, DsOut ds) {
-  constexpr int BC = D == 256 ? 64 : 128;   // keys per workgroup
-  const int nkb = (N + BC - 1) / BC, nqb = (N + 63) / 64;
-  const int items = CAUSAL ? (nkb + 1) / 2 : nkb;
-  const dim3 grid((unsigned)(items * BH)), block(256);
+  const int nqb = (N + 63) / 64;
+  const dim3 grid = bwd_kv_grid<D, CAUSAL>(BH, N), block(256);
   if constexpr (!DQA) {
     if (drop) {
       if (ds.buf)
-        hipLaunchKernelGGL((bwd_bf16_dropout_kernel<D, CAUSAL, true>), grid, block, 0, stream, (const bf16*)q,
-                           (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH,
-                           N, nqb, scale, scale * kLog2e, lay, *drop, ds);
+        return launch_bwd_dropout_t<D, CAUSAL, true>(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, scale, lay, stream,
+                                                     *drop, ds);
+      if constexpr (D == 256)
+        return launch_bwd_kv256_drop(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, CAUSAL, scale, lay, stream, *drop);
       else
-        hipLaunchKernelGGL((bwd_bf16_dropout_kernel<D, CAUSAL, false>), grid, block, 0, stream, (const bf16*)q,
-                           (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH,
-                           N, nqb, scale, scale * kLog2e, lay, *drop, DsOut{});
-      return hipGetLastError();
+        return launch_bwd_dropout_t<D, CAUSAL, false>(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, scale, lay,
+                                                      stream, *drop, ds);
     }
     if (ds.buf) {
       hipLaunchKernelGGL((bwd_bf16_ds_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,

@@ -230,14 +230,37 @@ struct TileFetch {
 #pragma unroll
       for (int j = 0; j < LPW; ++j) dma16_buf(rs, goff[j], soff, dst + (wave * LPW + j) * 1024);
     } else {
+      ragged(src, row0, nrows, dst, rsb);
+    }
+  }
+  // The same for a matrix whose rows are rsb2 bytes apart.  Its per-lane
+  // offsets are this fetcher's moved by row * (rsb2 - rsb): one lane term and
+  // one uniform term per load instead of a second set of offsets (registers
+  // the callers do not have).  The wrapping 32-bit sums are exact, since every
+  // true offset is below 2^31.
+  FA_DEV void operator()(const bf16* src, int row0, int nrows, char* dst, unsigned rsb2) const {
+    if (row0 + ROWS <= nrows) {
+      const __amdgpu_buffer_rsrc_t rs = raw_rsrc(src);
+      const unsigned delta = rsb2 - rsb;
+      const unsigned lane_shift = (unsigned)(lane / CH) * delta;
+      const unsigned soff = (unsigned)row0 * rsb2;
 #pragma unroll
-      for (int j = 0; j < LPW; ++j) {
-        const int blk = wave * LPW + j;
-        const int row = blk * RPL + lane / CH;
-        const int ch = min((lane % CH) ^ swz<ROWB>(row), VC - 1);
-        const int r = min(row0 + row, nrows - 1);
-        dma16_buf(raw_rsrc(src), (unsigned)r * rsb + (unsigned)(ch * 16), 0, dst + blk * 1024);
-      }
+      for (int j = 0; j < LPW; ++j)
+        dma16_buf(rs, goff[j] + lane_shift + (unsigned)((wave * LPW + j) * RPL) * delta, soff,
+                  dst + (wave * LPW + j) * 1024);
+    } else {
+      ragged(src, row0, nrows, dst, rsb2);
+    }
+  }
+  // a tile reaching past nrows: per-row clamped offsets
+  FA_DEV void ragged(const bf16* src, int row0, int nrows, char* dst, unsigned stride) const {
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int blk = wave * LPW + j;
+      const int row = blk * RPL + lane / CH;
+      const int ch = min((lane % CH) ^ swz<ROWB>(row), VC - 1);
+      const int r = min(row0 + row, nrows - 1);
+      dma16_buf(raw_rsrc(src), (unsigned)r * stride + (unsigned)(ch * 16), 0, dst + blk * 1024);
     }
   }
 };

@@ -51,7 +51,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
                                                       float* __restrict__ LSE, int BH, int N, float scale,
-                                                      RowLayout lay) {
+                                                      Layouts lay) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sv[F32_TILE * D];
@@ -60,20 +60,18 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ 
   const int head = blockIdx.x / nrb;
   const int row0 = (blockIdx.x - head * nrb) * F32_ROWS;
   const int qrow = row0 + (tid >> 1);
-  const int RS = lay.row_stride(D);   // elements between a head's rows
-  const size_t hoff = lay.head_off(head, N, D);
   float qh[DH], oh[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
-    qh[c] = qrow < N ? Q[hoff + (size_t)qrow * RS + half * DH + c] : 0.f;
+    qh[c] = qrow < N ? Q[lay.off(lay.q, head) + (size_t)qrow * lay.q.sn + half * DH + c] : 0.f;
     oh[c] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
   const int kv_end = CAUSAL ? min(N, row0 + F32_ROWS) : N;
   for (int t0 = 0; t0 < kv_end; t0 += F32_TILE) {
     __syncthreads();
-    load_rows_f32<D>(sk, K + hoff, t0, F32_TILE, N, tid, RS);
-    load_rows_f32<D>(sv, V + hoff, t0, F32_TILE, N, tid, RS);
+    load_rows_f32<D>(sk, K + lay.off(lay.k, head), t0, F32_TILE, N, tid, lay.k.sn);
+    load_rows_f32<D>(sv, V + lay.off(lay.v, head), t0, F32_TILE, N, tid, lay.v.sn);
     __syncthreads();
     float s[F32_TILE];
     float mx = m;
@@ -105,8 +103,9 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ 
   }
   if (qrow < N) {
     const float inv = 1.f / l;
+    float* orow = O + lay.off(lay.o, head) + (size_t)qrow * lay.o.sn + half * DH;
 #pragma unroll
-    for (int c = 0; c < DH; ++c) O[hoff + (size_t)qrow * RS + half * DH + c] = oh[c] * inv;
+    for (int c = 0; c < DH; ++c) orow[c] = oh[c] * inv;
     if (half == 0) LSE[(size_t)head * N + qrow] = m + logf(l);
   }
 }
@@ -117,7 +116,7 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
                                                          const float* __restrict__ V, const float* __restrict__ dO,
                                                          const float* __restrict__ LSE, const float* __restrict__ NDR,
                                                          float* __restrict__ dK, float* __restrict__ dV, int N,
-                                                         float scale, RowLayout lay) {
+                                                         float scale, Layouts lay) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float sq[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sg[F32_TILE * D];
@@ -127,21 +126,19 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
   const int head = blockIdx.x / nrb;
   const int row0 = (blockIdx.x - head * nrb) * F32_ROWS;
   const int kvrow = row0 + (tid >> 1);
-  const int RS = lay.row_stride(D);   // elements between a head's rows
-  const size_t hoff = lay.head_off(head, N, D);
   float kh[DH], vh[DH], dkh[DH], dvh[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
-    kh[c] = kvrow < N ? K[hoff + (size_t)kvrow * RS + half * DH + c] : 0.f;
-    vh[c] = kvrow < N ? V[hoff + (size_t)kvrow * RS + half * DH + c] : 0.f;
+    kh[c] = kvrow < N ? K[lay.off(lay.k, head) + (size_t)kvrow * lay.k.sn + half * DH + c] : 0.f;
+    vh[c] = kvrow < N ? V[lay.off(lay.v, head) + (size_t)kvrow * lay.v.sn + half * DH + c] : 0.f;
     dkh[c] = 0.f;
     dvh[c] = 0.f;
   }
   const int q_begin = CAUSAL ? (row0 / F32_TILE) * F32_TILE : 0;
   for (int t0 = q_begin; t0 < N; t0 += F32_TILE) {
     __syncthreads();
-    load_rows_f32<D>(sq, Q + hoff, t0, F32_TILE, N, tid, RS);
-    load_rows_f32<D>(sg, dO + hoff, t0, F32_TILE, N, tid, RS);
+    load_rows_f32<D>(sq, Q + lay.off(lay.q, head), t0, F32_TILE, N, tid, lay.q.sn);
+    load_rows_f32<D>(sg, dO + lay.off(lay.g, head), t0, F32_TILE, N, tid, lay.g.sn);
     if (tid < F32_TILE) {
       const int q = t0 + tid;
       sl[tid] = q < N ? LSE[(size_t)head * N + q] : 0.f;
@@ -165,8 +162,8 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
   if (kvrow < N) {
 #pragma unroll
     for (int c = 0; c < DH; ++c) {
-      dK[hoff + (size_t)kvrow * RS + half * DH + c] = dkh[c] * scale;
-      dV[hoff + (size_t)kvrow * RS + half * DH + c] = dvh[c];
+      dK[lay.off(lay.dk, head) + (size_t)kvrow * lay.dk.sn + half * DH + c] = dkh[c] * scale;
+      dV[lay.off(lay.dv, head) + (size_t)kvrow * lay.dv.sn + half * DH + c] = dvh[c];
     }
   }
 }
@@ -176,7 +173,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                         const float* __restrict__ V, const float* __restrict__ dO,
                                                         const float* __restrict__ LSE, const float* __restrict__ NDR,
-                                                        float* __restrict__ dQ, int N, float scale, RowLayout lay) {
+                                                        float* __restrict__ dQ, int N, float scale, Layouts lay) {
   constexpr int DH = D / 2;
   __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sv[F32_TILE * D];
@@ -185,13 +182,11 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
   const int head = blockIdx.x / nrb;
   const int row0 = (blockIdx.x - head * nrb) * F32_ROWS;
   const int qrow = row0 + (tid >> 1);
-  const int RS = lay.row_stride(D);   // elements between a head's rows
-  const size_t hoff = lay.head_off(head, N, D);
   float qh[DH], gh[DH], dqh[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
-    qh[c] = qrow < N ? Q[hoff + (size_t)qrow * RS + half * DH + c] : 0.f;
-    gh[c] = qrow < N ? dO[hoff + (size_t)qrow * RS + half * DH + c] : 0.f;
+    qh[c] = qrow < N ? Q[lay.off(lay.q, head) + (size_t)qrow * lay.q.sn + half * DH + c] : 0.f;
+    gh[c] = qrow < N ? dO[lay.off(lay.g, head) + (size_t)qrow * lay.g.sn + half * DH + c] : 0.f;
     dqh[c] = 0.f;
   }
   const float lse = qrow < N ? LSE[(size_t)head * N + qrow] : 0.f;
@@ -199,8 +194,8 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
   const int kv_end = CAUSAL ? min(N, row0 + F32_ROWS) : N;
   for (int t0 = 0; t0 < kv_end; t0 += F32_TILE) {
     __syncthreads();
-    load_rows_f32<D>(sk, K + hoff, t0, F32_TILE, N, tid, RS);
-    load_rows_f32<D>(sv, V + hoff, t0, F32_TILE, N, tid, RS);
+    load_rows_f32<D>(sk, K + lay.off(lay.k, head), t0, F32_TILE, N, tid, lay.k.sn);
+    load_rows_f32<D>(sv, V + lay.off(lay.v, head), t0, F32_TILE, N, tid, lay.v.sn);
     __syncthreads();
     for (int j = 0; j < F32_TILE; ++j) {
       const int kv = t0 + j;
@@ -214,14 +209,15 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
     }
   }
   if (qrow < N) {
+    float* dqrow = dQ + lay.off(lay.dq, head) + (size_t)qrow * lay.dq.sn + half * DH;
 #pragma unroll
-    for (int c = 0; c < DH; ++c) dQ[hoff + (size_t)qrow * RS + half * DH + c] = dqh[c] * scale;
+    for (int c = 0; c < DH; ++c) dqrow[c] = dqh[c] * scale;
   }
 }
 
 template <int D, bool CAUSAL>
 static hipError_t fwd_f32_t(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
-                            int N, float scale, RowLayout lay, hipStream_t stream) {
+                            int N, float scale, Layouts lay, hipStream_t stream) {
   const dim3 grid(f32_grid(BH, N)), block(128);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, o, lse, BH, N, scale, lay);
   return hipGetLastError();
@@ -230,7 +226,7 @@ static hipError_t fwd_f32_t(const float* q, const float* k, const float* v, floa
 template <int D, bool CAUSAL>
 static hipError_t bwd_kv_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
                                const float* ndrow, float* dk, float* dv, int BH, int N, float scale,
-                               RowLayout lay, hipStream_t stream) {
+                               Layouts lay, hipStream_t stream) {
   const dim3 grid(f32_grid(BH, N)), block(128);
   hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dk, dv, N,
                      scale, lay);
@@ -239,7 +235,7 @@ static hipError_t bwd_kv_f32_t(const float* q, const float* k, const float* v, c
 
 template <int D, bool CAUSAL>
 static hipError_t bwd_q_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
-                              const float* ndrow, float* dq, int BH, int N, float scale, RowLayout lay,
+                              const float* ndrow, float* dq, int BH, int N, float scale, Layouts lay,
                               hipStream_t stream) {
   const dim3 grid(f32_grid(BH, N)), block(128);
   hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dq, N, scale,
@@ -248,7 +244,7 @@ static hipError_t bwd_q_f32_t(const float* q, const float* k, const float* v, co
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N,
-                          int d, bool causal, float scale, RowLayout lay, hipStream_t stream) {
+                          int d, bool causal, float scale, Layouts lay, hipStream_t stream) {
   if (d == 128)
     return causal ? fwd_f32_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
                   : fwd_f32_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
@@ -261,7 +257,7 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 
 hipError_t launch_bwd_kv_f32(const float* q, const float* k, const float* v, const float* dO, const float* lse,
                              const float* ndrow, float* dk, float* dv, int BH, int N, int d, bool causal,
-                             float scale, RowLayout lay, hipStream_t stream) {
+                             float scale, Layouts lay, hipStream_t stream) {
   if (d == 128)
     return causal ? bwd_kv_f32_t<128, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream)
                   : bwd_kv_f32_t<128, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream);
@@ -274,7 +270,7 @@ hipError_t launch_bwd_kv_f32(const float* q, const float* k, const float* v, con
 
 hipError_t launch_bwd_q_f32(const float* q, const float* k, const float* v, const float* dO, const float* lse,
                             const float* ndrow, float* dq, int BH, int N, int d, bool causal, float scale,
-                            RowLayout lay, hipStream_t stream) {
+                            Layouts lay, hipStream_t stream) {
   if (d == 128)
     return causal ? bwd_q_f32_t<128, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream)
                   : bwd_q_f32_t<128, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream);

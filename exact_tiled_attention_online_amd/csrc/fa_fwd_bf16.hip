@@ -51,7 +51,7 @@ namespace fa {
 template <int D, bool CAUSAL, int NW, int BC, bool SPLIT, bool DROP>
 FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                           bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale,
-                          float c, RowLayout lay, SplitArgs sp, DropArgs dr) {
+                          float c, Layouts lay, SplitArgs sp, DropArgs dr) {
   static_assert(!(SPLIT && DROP), "dropout runs on the square training shape only");
   // BC: key rows per tile (128 where the registers allow it (d = 64), else 64;
   // 32 in the split mode, whose one-wave workgroups need little LDS)
@@ -72,8 +72,8 @@ FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   const TileBases<ROWB> tb(lane);
-  const int RS = lay.row_stride(D);      // elements between a head's rows
-  const TileFetch<ROWB, BC, NW, D / 8> fetch(wave, lane, RS * 2);
+  const TileFetch<ROWB, BC, NW, D / 8> fetch(wave, lane, lay.k.sn * 2);   // K rows; V rows at vrs
+  const unsigned vrs = (unsigned)lay.v.sn * 2u;
   const int bid = blockIdx.x;
   const int head = bid % BH;
   const int Nk = SPLIT ? sp.Nk : N;     // key rows
@@ -86,11 +86,9 @@ FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
     // causal: the longest query blocks are dispatched first
     qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
   }
-  const size_t hoff = lay.head_off(head, N, D);
-  const size_t khoff = lay.head_off(head, Nk, D);
-  const bf16* Qh = Q + hoff;
-  const bf16* Kh = K + khoff;
-  const bf16* Vh = V + khoff;
+  const bf16* Qh = Q + lay.off(lay.q, head);
+  const bf16* Kh = K + lay.off(lay.k, head);
+  const bf16* Vh = V + lay.off(lay.v, head);
 
   const int q0 = qb * BR + wave * 32;   // first query row of this wave
   const int qrow = q0 + l32;            // the query row this lane's statistics belong to
@@ -101,7 +99,7 @@ FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     if (qrow < N)
-      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * RS + 16 * s + 8 * h);
+      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * lay.q.sn + 16 * s + 8 * h);
     else
       qf[s] = bf16x8{};
   }
@@ -138,7 +136,7 @@ FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
     const char* Vt = b ? sV1 : sV0;
     if (j + 1 < ntiles) {
       fetch(Kh, (jlo + j + 1) * BC, Nk, b ? sK0 : sK1);
-      fetch(Vh, (jlo + j + 1) * BC, Nk, b ? sV0 : sV1);
+      fetch(Vh, (jlo + j + 1) * BC, Nk, b ? sV0 : sV1, vrs);
       FA_DEBUG_BARRIER();
     }
     if (j < wave_tiles) {
@@ -292,7 +290,7 @@ FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
   };
 
   fetch(Kh, jlo * BC, Nk, sK0);
-  fetch(Vh, jlo * BC, Nk, sV0);
+  fetch(Vh, jlo * BC, Nk, sV0, vrs);
   __syncthreads();
   for (int j = 0;;) {
     body(IC<0>{}, j);
@@ -327,7 +325,7 @@ FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
   }
   if (qrow < N) {
     const float inv = (DROP ? dr.keep_scale : 1.f) / l_tot;
-    bf16* Orow = O + hoff + (size_t)qrow * RS;
+    bf16* Orow = O + lay.off(lay.o, head) + (size_t)qrow * lay.o.sn;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -354,7 +352,7 @@ template <int D, bool CAUSAL, int NW, int BC, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, (fwd_min_blocks<D, NW, SPLIT>())) void fwd_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c,
-    RowLayout lay, SplitArgs sp) {
+    Layouts lay, SplitArgs sp) {
   fwd_bf16_body<D, CAUSAL, NW, BC, SPLIT, false>(Q, K, V, O, LSE, BH, N, nqb, scale, c, lay, sp, DropArgs{});
 }
 
@@ -362,13 +360,13 @@ template <int D, bool CAUSAL, int NW, int BC>
 __global__ __launch_bounds__(64 * NW, (fwd_min_blocks<D, NW, false>())) void fwd_bf16_dropout_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqb, float scale, float c,
-    RowLayout lay, DropArgs dr) {
+    Layouts lay, DropArgs dr) {
   fwd_bf16_body<D, CAUSAL, NW, BC, false, true>(Q, K, V, O, LSE, BH, N, nqb, scale, c, lay, SplitArgs{}, dr);
 }
 
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                                    int BH, int N, float scale, RowLayout lay, hipStream_t stream,
+                                    int BH, int N, float scale, Layouts lay, hipStream_t stream,
                                     const DropArgs* drop) {
   // d = 256: 4-wave workgroups (one wave per SIMD) and 32-key tiles
   constexpr int NW = D == 256 ? 4 : FA_FWD_NW, BR = 32 * NW;
@@ -388,7 +386,7 @@ static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v,
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                           int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream,
+                           int N, int d, bool causal, float scale, Layouts lay, hipStream_t stream,
                            const DropArgs* drop) {
   if (d == 128)
     return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream, drop)
@@ -407,7 +405,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
 // LDS per K/V tile pair at d = 128, so several workgroups share a CU).
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v, int BH, int Nq,
-                                     float scale, RowLayout lay, const SplitArgs& sp, hipStream_t stream) {
+                                     float scale, Layouts lay, const SplitArgs& sp, hipStream_t stream) {
   constexpr int NW = 1, BR = 32 * NW;
   const int nqb = (Nq + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * sp.nsplit * BH)), block(64 * NW);
@@ -419,7 +417,7 @@ static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v
 
 hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, float* opart, float* lpart,
                                  int BH, int Nq, int Nk, int d, bool causal, float scale, int nsplit,
-                                 int span, RowLayout lay, hipStream_t stream) {
+                                 int span, Layouts lay, hipStream_t stream) {
   const SplitArgs sp{Nk, Nk - Nq, nsplit, span, opart, lpart};
   if (d == 128)
     return causal ? launch_fwd_split_t<128, true>(q, k, v, BH, Nq, scale, lay, sp, stream)

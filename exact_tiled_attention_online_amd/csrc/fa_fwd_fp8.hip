@@ -87,7 +87,7 @@ template <int D, bool CAUSAL, int NW, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
     const unsigned char* __restrict__ Q, const unsigned char* __restrict__ K,
     const unsigned char* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N,
-    int nqb, float scale_qk, float c, float dv, RowLayout lay, SplitArgs sp) {
+    int nqb, float scale_qk, float c, float dv, Layouts lay, SplitArgs sp) {
   static_assert(D == 128, "FP8 tiles are laid out for 128-byte rows");
   constexpr int BR = 32 * NW, BC = 64;
   constexpr int ROWB = D;            // bytes per e4m3 row
@@ -102,8 +102,9 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
-  const int RS = lay.row_stride(D);      // elements (= bytes) between a head's rows
-  const TileFetch<ROWB, BC, NW> fetch(wave, lane, RS);
+  // strides in elements (= bytes for the e4m3 inputs)
+  const TileFetch<ROWB, BC, NW> fetch(wave, lane, lay.k.sn);   // K rows; V rows at vrs
+  const unsigned vrs = (unsigned)lay.v.sn;
   const int bid = blockIdx.x;
   const int head = bid % BH;
   const int Nk = SPLIT ? sp.Nk : N;     // key rows
@@ -115,12 +116,10 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
   } else {
     qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);   // longest blocks first
   }
-  const size_t hoff = lay.head_off(head, N, D);
-  const size_t khoff = lay.head_off(head, Nk, D);
-  const unsigned char* Qh = Q + hoff;
+  const unsigned char* Qh = Q + lay.off(lay.q, head);
   // TileFetch moves bytes; it takes the tile base as a bf16 pointer
-  const bf16* Kh = reinterpret_cast<const bf16*>(K + khoff);
-  const bf16* Vh = reinterpret_cast<const bf16*>(V + khoff);
+  const bf16* Kh = reinterpret_cast<const bf16*>(K + lay.off(lay.k, head));
+  const bf16* Vh = reinterpret_cast<const bf16*>(V + lay.off(lay.v, head));
 
   const int q0 = qb * BR + wave * 32;
   const int qrow = q0 + l32;
@@ -130,7 +129,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     if (qrow < N) {
-      const i32x4v* p = reinterpret_cast<const i32x4v*>(Qh + (size_t)qrow * RS + 64 * s + 32 * h);
+      const i32x4v* p = reinterpret_cast<const i32x4v*>(Qh + (size_t)qrow * lay.q.sn + 64 * s + 32 * h);
       qf[s] = cat8(p[0], p[1]);
     } else {
       qf[s] = i32x8{};
@@ -185,7 +184,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
     const char* Vt = b ? sV1 : sV0;
     if (j + 1 < ntiles) {
       fetch(Kh, (jlo + j + 1) * BC, Nk, b ? sK0 : sK1);
-      fetch(Vh, (jlo + j + 1) * BC, Nk, b ? sV0 : sV1);
+      fetch(Vh, (jlo + j + 1) * BC, Nk, b ? sV0 : sV1, vrs);
       FA_DEBUG_BARRIER();
     }
     if (j < wave_tiles) {
@@ -279,7 +278,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
   };
 
   fetch(Kh, jlo * BC, Nk, sK0);
-  fetch(Vh, jlo * BC, Nk, sV0);
+  fetch(Vh, jlo * BC, Nk, sV0, vrs);
   __syncthreads();
   for (int j = 0;;) {
     body(IC<0>{}, j);
@@ -314,7 +313,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
   }
   if (qrow < N) {
     const float f = dv / l_tot;
-    bf16* Orow = O + hoff + (size_t)qrow * RS;
+    bf16* Orow = O + lay.off(lay.o, head) + (size_t)qrow * lay.o.sn;
 #pragma unroll
     for (int t = 0; t < DT; ++t)
 #pragma unroll
@@ -332,7 +331,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
 
 template <bool CAUSAL>
 static hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                                   int N, float scale_qk, float dv, RowLayout lay, hipStream_t stream) {
+                                   int N, float scale_qk, float dv, Layouts lay, hipStream_t stream) {
   constexpr int NW = FA_FP8_NW, BR = 32 * NW;
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
@@ -343,7 +342,7 @@ static hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, 
 }
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                          bool causal, float scale, float dq, float dk, float dv, RowLayout lay,
+                          bool causal, float scale, float dq, float dk, float dv, Layouts lay,
                           hipStream_t stream) {
   const float scale_qk = scale * dq * dk;
   return causal ? launch_fwd_fp8_t<true>(q, k, v, o, lse, BH, N, scale_qk, dv, lay, stream)
@@ -354,7 +353,7 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
 // whole 64-key tiles (32 KB of LDS), partial results to the workspace.
 template <bool CAUSAL>
 static hipError_t launch_fwd_split_fp8_t(const void* q, const void* k, const void* v, int BH, int Nq,
-                                         float scale_qk, float dv, RowLayout lay, const SplitArgs& sp,
+                                         float scale_qk, float dv, Layouts lay, const SplitArgs& sp,
                                          hipStream_t stream) {
   const int nqb = (Nq + 31) / 32;
   const dim3 grid((unsigned)(nqb * sp.nsplit * BH)), block(64);
@@ -366,7 +365,7 @@ static hipError_t launch_fwd_split_fp8_t(const void* q, const void* k, const voi
 
 hipError_t launch_fwd_split_fp8(const void* q, const void* k, const void* v, float* opart, float* lpart,
                                 int BH, int Nq, int Nk, bool causal, float scale, float dq, float dk, float dv,
-                                int nsplit, int span, RowLayout lay, hipStream_t stream) {
+                                int nsplit, int span, Layouts lay, hipStream_t stream) {
   const SplitArgs sp{Nk, Nk - Nq, nsplit, span, opart, lpart};
   const float scale_qk = scale * dq * dk;
   return causal ? launch_fwd_split_fp8_t<true>(q, k, v, BH, Nq, scale_qk, dv, lay, sp, stream)

@@ -7,20 +7,27 @@
 
 namespace fa {
 
-// Where the N rows of one (batch, head) sit in a q/k/v/o/dO/dq/dk/dv tensor:
-// [B,H,N,d] (each head's rows contiguous) or [B,N,H,d] (each token's H heads
-// contiguous, so a head's consecutive rows are H*d elements apart).  hb is
-// the flattened batch*head index.
+// Where the rows of one tensor sit: element c of row n of head h in batch b
+// is b*sb + h*sh + n*sn + c elements past the tensor's base (the d elements
+// of a row are contiguous).  hb is the flattened index b*H + h.  The dense
+// [B,H,N,d] and [B,N,H,d] orders are two choices of the strides; a view into
+// a packed projection buffer (q, k, v as slices of one [B,N,3,H,d] tensor) is
+// another.
 struct RowLayout {
-  int H;      // heads per batch
-  int bnhd;   // 0: [B,H,N,d]; 1: [B,N,H,d]
-  __host__ __device__ __forceinline__ int row_stride(int D) const { return bnhd ? H * D : D; }
-  __host__ __device__ __forceinline__ size_t head_off(int hb, int N, int D) const {
-    const int b = hb / H, h = hb - b * H;
-    return bnhd ? ((size_t)b * N * H + h) * D : (size_t)hb * N * D;
-  }
+  long long sb, sh;   // batch and head strides (elements)
+  int sn;             // row stride (elements)
 };
 
+// The layouts of every tensor of one call (g: dO); each kernel reads those of
+// the tensors it touches.  H is common to all, so a kernel splits hb once.
+struct Layouts {
+  RowLayout q, k, v, o, g, dq, dk, dv;
+  int H;   // heads per batch
+  __host__ __device__ __forceinline__ size_t off(const RowLayout& t, int hb) const {
+    const int b = hb / H, h = hb - b * H;
+    return (size_t)((long long)b * t.sb + (long long)h * t.sh);
+  }
+};
 
 // Arguments of the forward kernels' split-key-range mode (unused otherwise).
 struct SplitArgs {
@@ -65,13 +72,13 @@ __host__ __device__ __forceinline__ size_t ds_block_off(bool causal, int i, int 
 // bf16 forward: O, LSE; with `drop`, O uses the dropped probabilities (LSE
 // does not change).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                           int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream,
+                           int N, int d, bool causal, float scale, Layouts lay, hipStream_t stream,
                            const DropArgs* drop = nullptr);
 
 // FP8 (e4m3fn) forward, d = 128: O (bf16) and LSE for Q = dq * Q8, K = dk * K8,
 // V = dv * V8.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                          bool causal, float scale, float dq, float dk, float dv, RowLayout lay,
+                          bool causal, float scale, float dq, float dk, float dv, Layouts lay,
                           hipStream_t stream);
 
 // Split-key-range bf16 forward (Nq queries against Nk >= Nq keys): the keys
@@ -81,23 +88,23 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
 constexpr int kSplitBC = 32;
 hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, float* opart, float* lpart,
                                  int BH, int Nq, int Nk, int d, bool causal, float scale, int nsplit,
-                                 int span, RowLayout lay, hipStream_t stream);
+                                 int span, Layouts lay, hipStream_t stream);
 
 // The same for FP8 (e4m3fn) q, k, v with per-tensor descales, d = 128; ranges
 // are whole kSplitBC8-key tiles.
 constexpr int kSplitBC8 = 64;
 hipError_t launch_fwd_split_fp8(const void* q, const void* k, const void* v, float* opart, float* lpart,
                                 int BH, int Nq, int Nk, bool causal, float scale, float dq, float dk, float dv,
-                                int nsplit, int span, RowLayout lay, hipStream_t stream);
+                                int nsplit, int span, Layouts lay, hipStream_t stream);
 
-// Combines the ranges of the split forward: O (bf16, layout lay) and LSE.
+// Combines the ranges of the split forward: O (bf16, layout lay.o) and LSE.
 hipError_t launch_fwd_merge(const float* opart, const float* lpart, void* o, float* lse, int BH, int Nq,
-                            int d, int nsplit, RowLayout lay, hipStream_t stream);
+                            int d, int nsplit, Layouts lay, hipStream_t stream);
 
 // Backward preprocess: ndrow = -rowsum(dO o O) (fp32), nlse = -LSE / scale,
 // and, when dq_acc is not null, dq_acc = 0.  `fp32` selects the input type.
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ndrow, float* nlse,
-                          float* dq_acc, int BH, int N, int d, float scale, bool fp32, RowLayout lay,
+                          float* dq_acc, int BH, int N, int d, float scale, bool fp32, Layouts lay,
                           hipStream_t stream);
 
 // bf16 key/value-block-outer backward: dK, dV written; with dq_atomic, dQ is
@@ -107,37 +114,45 @@ hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float
 // the dropout forward.
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dO,
                            const float* nlse, const float* ndrow, float* dq_acc, void* dk, void* dv,
-                           int BH, int N, int d, bool causal, float scale, bool dq_atomic, RowLayout lay,
+                           int BH, int N, int d, bool causal, float scale, bool dq_atomic, Layouts lay,
                            hipStream_t stream, const DropArgs* drop = nullptr, DsOut ds = DsOut{});
 
-// The same at d = 256 (no atomic-dQ form), from its own translation unit.
+// The same at d = 256 (no atomic-dQ form; plain, hand-off and dropout), from
+// its own translation unit.
 hipError_t launch_bwd_kv256(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                             const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
-                            RowLayout lay, hipStream_t stream, const DropArgs* drop, DsOut ds);
+                            Layouts lay, hipStream_t stream, const DropArgs* drop, DsOut ds);
+
+// d = 256 with dropout, without the hand-off: from a unit of its own, built
+// without VGPR-form MFMA results (with them the compiler's AGPR-copy rewrite
+// crashes on these kernels, which sit at the register limit).
+hipError_t launch_bwd_kv256_drop(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
+                                 const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
+                                 Layouts lay, hipStream_t stream, const DropArgs& drop);
 
 // dQ = bf16(scale * dS K) from the hand-off buffer (query-block outer, no
 // recompute, no atomics).
 hipError_t launch_bwd_dq_ds(DsOut ds, const void* k, void* dq, int BH, int N, int d, bool causal, float scale,
-                            RowLayout lay, hipStream_t stream);
+                            Layouts lay, hipStream_t stream);
 
 // bf16 query-block-outer dQ kernel: dQ = bf16(scale * dS K), no atomics;
 // with `drop`, the dQ of the dropout forward.
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                          const float* ndrow, void* dq, int BH, int N, int d, bool causal, float scale,
-                         RowLayout lay, hipStream_t stream, const DropArgs* drop = nullptr);
+                         Layouts lay, hipStream_t stream, const DropArgs* drop = nullptr);
 
-// dQ = bf16(scale * dq_acc); dq_acc is contiguous [B*H][N][d], dq in layout lay.
-hipError_t launch_dq_convert(const float* dq_acc, void* dq, int BH, int N, int d, float scale, RowLayout lay,
+// dQ = bf16(scale * dq_acc); dq_acc is contiguous [B*H][N][d], dq in layout lay.dq.
+hipError_t launch_dq_convert(const float* dq_acc, void* dq, int BH, int N, int d, float scale, Layouts lay,
                              hipStream_t stream);
 
 // fp32 path (plain VALU kernels, exact fp32 arithmetic).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int BH, int N, int d, bool causal, float scale, RowLayout lay, hipStream_t stream);
+                          int BH, int N, int d, bool causal, float scale, Layouts lay, hipStream_t stream);
 hipError_t launch_bwd_kv_f32(const float* q, const float* k, const float* v, const float* dO,
                              const float* lse, const float* ndrow, float* dk, float* dv, int BH, int N,
-                             int d, bool causal, float scale, RowLayout lay, hipStream_t stream);
+                             int d, bool causal, float scale, Layouts lay, hipStream_t stream);
 hipError_t launch_bwd_q_f32(const float* q, const float* k, const float* v, const float* dO,
                             const float* lse, const float* ndrow, float* dq, int BH, int N, int d,
-                            bool causal, float scale, RowLayout lay, hipStream_t stream);
+                            bool causal, float scale, Layouts lay, hipStream_t stream);
 
 }  // namespace fa

@@ -21,7 +21,9 @@
  * contiguous) or FA_LAYOUT_BNHD = [B, N, H, d] (each token's H heads
  * contiguous, as a projection writes them and as the PyTorch module of the
  * blog.xiaohack.org "flops" page, item 知识点13, takes its input; no transpose
- * is needed).  Any other layout value is FA_ERR_INVALID.
+ * is needed).  Any other layout value is FA_ERR_INVALID.  fa_fwd_strided and
+ * fa_bwd_strided take any strides per tensor instead (views into a packed
+ * projection buffer, for one).
  * lse is always float [B, H, N], natural log, in units of the scaled score
  * scale * q_i . k_j.  The causal mask keeps key j for query i iff j <= i
  * (queries and keys share the index range 0..N-1).
@@ -106,6 +108,41 @@ typedef enum { FA_DQ_HANDOFF = 0, FA_DQ_RECOMPUTE = 1, FA_DQ_ATOMIC = 2 } fa_dq_
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, int causal, float scale,
            void* stream, int dtype, int layout);
+
+/*
+ * fa_fwd and fa_bwd on strided views: each tensor is a [B, H, N, d] view
+ * given by its base pointer and three element strides, so that element c of
+ * row n of head h in batch b sits at base + b*stride_b + h*stride_h +
+ * n*stride_n + c (the d elements of a row contiguous).  Q, K, V and dO as
+ * slices of one packed projection [B, N, 3, H, d] (and dQ, dK, dV as slices
+ * of its gradient) are such views, passed without a copy; the (B, N, H, d)
+ * input of the PyTorch module of the blog.xiaohack.org "flops" page, item
+ * 知识点13, is one without the packing.
+ *
+ * strides: host memory, 3 values (stride_b, stride_h, stride_n) per tensor:
+ * fa_fwd_strided 12 for q, k, v, o; fa_bwd_strided 24 for q, k, v, o, dO,
+ * dq, dk, dv (o being the forward's output, read here).  lse and the
+ * workspace are those of fa_fwd and fa_bwd (lse contiguous [B, H, N]).  Each
+ * stride must be >= 0, at most 2^40, and a multiple of 16 bytes (8 bf16 or 4
+ * fp32 elements), with N * stride_n under 2^31 bytes (a head's rows are
+ * addressed with 32-bit byte offsets) and every view within 2^62 bytes;
+ * within an output view no two rows may overlap (a zero or short stride of a
+ * dimension with more than one entry is rejected); otherwise FA_ERR_INVALID.
+ * Inputs may repeat rows (a zero stride broadcasts).  Outputs must not
+ * overlap one another or any input, as for the dense calls.  Everything else
+ * (dtypes, d, sizes, scale, causal, workspace, dQ method, streams, errors) is
+ * that of fa_fwd and fa_bwd, and the results are bitwise those of the dense
+ * calls on the same values: the kernels are the same and only the addresses
+ * differ.
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale,
+                   const long long* strides, void* stream, int dtype);
+int fa_bwd_strided(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, int causal, float scale,
+                   const long long* strides, void* workspace, size_t workspace_bytes,
+                   void* stream, int dtype);
 
 /*
  * Bytes of device workspace fa_bwd needs for this shape with the given dQ

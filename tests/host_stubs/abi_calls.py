@@ -40,6 +40,9 @@ lib.fa_fwd_splitkv.argtypes = [vp] * 5 + [i32] * 6 + [f32, i32, vp, sz, vp, i32,
 lib.fa_fwd_splitkv_fp8_workspace_bytes.restype = sz
 lib.fa_fwd_splitkv_fp8_workspace_bytes.argtypes = [i32] * 6
 lib.fa_fwd_splitkv_fp8.argtypes = [vp] * 5 + [i32] * 6 + [f32] * 4 + [i32, vp, sz, vp, i32]
+pll = C.POINTER(C.c_longlong)
+lib.fa_fwd_strided.argtypes = [vp] * 5 + [i32] * 5 + [f32, pll, vp, i32]
+lib.fa_bwd_strided.argtypes = [vp] * 9 + [i32] * 5 + [f32, pll, vp, sz, vp, i32]
 lib.fa_strerror.restype = C.c_char_p
 lib.fa_strerror.argtypes = [i32]
 
@@ -131,6 +134,72 @@ for d in (64, 96, 128):
                     expect(st, OK, f"splitkv fp8 c={causal} {B}x{H}x{Nq}x{Nk} ns={ns}")
                     n_split += 1
 print(f"split forwards: {n_split} calls", flush=True)
+
+# strided views: accepted layouts run (here: reach the stand-in launchers),
+# and every accepted output view is free of overlap, checked by enumerating
+# its element offsets on small shapes
+def strided(vals):
+    return (C.c_longlong * len(vals))(*vals)
+
+
+def overlaps(B, H, N, d, st):
+    seen = set()
+    for b in range(B):
+        for h in range(H):
+            for n in range(N):
+                base = b * st[0] + h * st[1] + n * st[2]
+                for c in range(d):
+                    if base + c in seen:
+                        return True
+                    seen.add(base + c)
+    return False
+
+
+n_str = n_accepted = 0
+for dtype, unit in ((BF16, 8), (FP32, 4)):
+    for B, H, N, d in [(2, 3, 33, 64), (1, 2, 5, 96), (3, 1, 2, 128), (1, 1, 1, 64)]:
+        if dtype == FP32 and d == 256:
+            continue
+        packed = [N * 3 * H * d, d, 3 * H * d]        # a slice of [B, N, 3, H, d]
+        bhnd = [H * N * d, N * d, d]
+        bnhd = [N * H * d, d, H * d]
+        padded = [H * N * (d + 2 * unit), N * (d + 2 * unit), d + 2 * unit]
+        for combo in ([packed] * 3 + [bhnd], [bnhd] * 4, [padded, packed, bhnd, bnhd],
+                      [[0, bhnd[1], bhnd[2]]] * 3 + [bhnd]):   # inputs broadcast over the batch
+            vals = [x for t in combo for x in t]
+            st = lib.fa_fwd_strided(q, k, v, o, lse, B, H, N, d, 1, 0.125, strided(vals), None, dtype)
+            expect(st, OK, f"fwd_strided dt={dtype} {B}x{H}x{N}x{d} {combo}")
+            need = lib.fa_bwd_workspace_size(B, H, N, d, 1, dtype, RECOMPUTE)
+            bvals = vals[:12] + combo[3] + combo[0] + combo[1] + combo[2]
+            st = with_ws(need, lambda ws: lib.fa_bwd_strided(q, k, v, o, dO, lse, dq, dk, dv, B, H, N, d, 1, 0.125,
+                                                             strided(bvals), ws, need, None, dtype))
+            want = OK if combo[0][0] != 0 or B == 1 else INVALID   # dq on the broadcast layout overlaps
+            expect(st, want, f"bwd_strided dt={dtype} {B}x{H}x{N}x{d} {combo}")
+            n_str += 2
+        # random output strides: whatever is accepted must not overlap
+        import random
+        rng = random.Random(1234 + B * 100 + N + d + dtype)
+        for _ in range(150):
+            so = [rng.choice([0, unit, d, d + unit, H * d, N * d, rng.randrange(0, 4 * N * H * d + 1, unit)])
+                  for _ in range(3)]
+            vals = bhnd * 3 + so
+            st = lib.fa_fwd_strided(q, k, v, o, lse, B, H, N, d, 0, 0.125, strided(vals), None, dtype)
+            if st == OK and overlaps(B, H, N, d, so):
+                fails.append(f"accepted an overlapping output view {so} for {B}x{H}x{N}x{d}")
+            n_accepted += st == OK
+            if st not in (OK, INVALID):
+                fails.append(f"fwd_strided status {st} for {so}")
+            n_str += 1
+# stride values at and past the limits: rejected, with no overflow in the checks
+for big in (1 << 40, (1 << 40) + 8, 1 << 62, (1 << 63) - 8, -(1 << 63)):
+    vals = [big, 64 * 33, 64] + [3 * 33 * 64, 33 * 64, 64] * 3
+    lib.fa_fwd_strided(q, k, v, o, lse, 2, 3, 33, 64, 0, 0.125, strided(vals), None, BF16)
+    vals = [3 * 33 * 64, 33 * 64, 64] * 3 + [3 * 33 * 64, big, 64]
+    lib.fa_fwd_strided(q, k, v, o, lse, 2, 3, 33, 64, 0, 0.125, strided(vals), None, BF16)
+    n_str += 2
+if n_accepted < 100:
+    fails.append(f"only {n_accepted} random output views were accepted: the overlap check proves little")
+print(f"strided: {n_str} calls, {n_accepted} random output views accepted", flush=True)
 
 # rejections: arguments the checks must stop before any size arithmetic
 expect(lib.fa_fwd(None, k, v, o, lse, 1, 1, 1, 64, 0, 0.125, None, BF16, 0), INVALID, "null q")

@@ -26,16 +26,16 @@ bool bad(bool cond) { return cond; }
 
 namespace fa {
 
-hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, float*, int, int, int, bool, float, RowLayout,
+hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, float*, int, int, int, bool, float, Layouts,
                            hipStream_t, const DropArgs*) {
   return hipSuccess;
 }
 hipError_t launch_fwd_fp8(const void*, const void*, const void*, void*, float*, int, int, bool, float, float, float,
-                          float, RowLayout, hipStream_t) {
+                          float, Layouts, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_fwd_split_bf16(const void*, const void*, const void*, float* opart, float* lpart, int BH, int Nq,
-                                 int Nk, int d, bool, float, int nsplit, int span, RowLayout, hipStream_t) {
+                                 int Nk, int d, bool, float, int nsplit, int span, Layouts, hipStream_t) {
   if (bad(span % kSplitBC != 0 || (long long)nsplit * span < Nk || (long long)(nsplit - 1) * span >= Nk))
     return hipErrorInvalidValue;
   touch(opart, (size_t)nsplit * BH * Nq * d * sizeof(float));
@@ -43,7 +43,7 @@ hipError_t launch_fwd_split_bf16(const void*, const void*, const void*, float* o
   return hipSuccess;
 }
 hipError_t launch_fwd_split_fp8(const void*, const void*, const void*, float* opart, float* lpart, int BH, int Nq,
-                                int Nk, bool, float, float, float, float, int nsplit, int span, RowLayout,
+                                int Nk, bool, float, float, float, float, int nsplit, int span, Layouts,
                                 hipStream_t) {
   if (bad(span % kSplitBC8 != 0 || (long long)nsplit * span < Nk || (long long)(nsplit - 1) * span >= Nk))
     return hipErrorInvalidValue;
@@ -52,13 +52,13 @@ hipError_t launch_fwd_split_fp8(const void*, const void*, const void*, float* op
   return hipSuccess;
 }
 hipError_t launch_fwd_merge(const float* opart, const float* lpart, void*, float*, int BH, int Nq, int d, int nsplit,
-                            RowLayout, hipStream_t) {
+                            Layouts, hipStream_t) {
   read(opart, (size_t)nsplit * BH * Nq * d * sizeof(float));
   read(lpart, (size_t)nsplit * BH * Nq * sizeof(float));
   return hipSuccess;
 }
 hipError_t launch_bwd_pre(const void*, const void*, const float*, float* ndrow, float* nlse, float* dq_acc, int BH,
-                          int N, int d, float, bool, RowLayout, hipStream_t) {
+                          int N, int d, float, bool, Layouts, hipStream_t) {
   touch(ndrow, (size_t)BH * N * sizeof(float));
   touch(nlse, (size_t)BH * N * sizeof(float));
   if (dq_acc) touch(dq_acc, (size_t)BH * N * d * sizeof(float));
@@ -66,7 +66,7 @@ hipError_t launch_bwd_pre(const void*, const void*, const float*, float* ndrow, 
 }
 hipError_t launch_bwd_bf16(const void*, const void*, const void*, const void*, const float* nlse, const float* ndrow,
                            float* dq_acc, void*, void*, int BH, int N, int d, bool causal, float, bool dq_atomic,
-                           RowLayout, hipStream_t, const DropArgs* drop, DsOut ds) {
+                           Layouts, hipStream_t, const DropArgs* drop, DsOut ds) {
   if (dq_atomic && (drop || ds.buf)) return hipErrorInvalidValue;
   read(nlse, (size_t)BH * N * sizeof(float));
   read(ndrow, (size_t)BH * N * sizeof(float));
@@ -80,10 +80,10 @@ hipError_t launch_bwd_bf16(const void*, const void*, const void*, const void*, c
   return hipSuccess;
 }
 hipError_t launch_bwd_kv256(const void*, const void*, const void*, const void*, const float*, const float*, void*,
-                            void*, int, int, bool, float, RowLayout, hipStream_t, const DropArgs*, DsOut) {
+                            void*, int, int, bool, float, Layouts, hipStream_t, const DropArgs*, DsOut) {
   return hipSuccess;   // reached only through launch_bwd_bf16 in the real library
 }
-hipError_t launch_bwd_dq_ds(DsOut ds, const void*, void*, int BH, int N, int, bool causal, float, RowLayout,
+hipError_t launch_bwd_dq_ds(DsOut ds, const void*, void*, int BH, int N, int, bool causal, float, Layouts,
                             hipStream_t) {
   const int nqb = (N + 63) / 64, nks = (N + 31) / 32;
   if (bad(ds.nks != nks || ds.head_bytes != ds_block_off(causal, nqb, nks))) return hipErrorInvalidValue;
@@ -91,26 +91,26 @@ hipError_t launch_bwd_dq_ds(DsOut ds, const void*, void*, int BH, int N, int, bo
   return hipSuccess;
 }
 hipError_t launch_bwd_dq(const void*, const void*, const void*, const void*, const float* nlse, const float* ndrow,
-                         void*, int BH, int N, int, bool, float, RowLayout, hipStream_t, const DropArgs*) {
+                         void*, int BH, int N, int, bool, float, Layouts, hipStream_t, const DropArgs*) {
   read(nlse, (size_t)BH * N * sizeof(float));
   read(ndrow, (size_t)BH * N * sizeof(float));
   return hipSuccess;
 }
-hipError_t launch_dq_convert(const float* dq_acc, void*, int BH, int N, int d, float, RowLayout, hipStream_t) {
+hipError_t launch_dq_convert(const float* dq_acc, void*, int BH, int N, int d, float, Layouts, hipStream_t) {
   read(dq_acc, (size_t)BH * N * d * sizeof(float));
   return hipSuccess;
 }
 hipError_t launch_fwd_f32(const float*, const float*, const float*, float*, float*, int, int, int, bool, float,
-                          RowLayout, hipStream_t) {
+                          Layouts, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_bwd_kv_f32(const float*, const float*, const float*, const float*, const float*, const float* ndrow,
-                             float*, float*, int BH, int N, int, bool, float, RowLayout, hipStream_t) {
+                             float*, float*, int BH, int N, int, bool, float, Layouts, hipStream_t) {
   read(ndrow, (size_t)BH * N * sizeof(float));
   return hipSuccess;
 }
 hipError_t launch_bwd_q_f32(const float*, const float*, const float*, const float*, const float*, const float* ndrow,
-                            float*, int BH, int N, int, bool, float, RowLayout, hipStream_t) {
+                            float*, int BH, int N, int, bool, float, Layouts, hipStream_t) {
   read(ndrow, (size_t)BH * N * sizeof(float));
   return hipSuccess;
 }

@@ -42,6 +42,8 @@ def header_signatures():
 
 
 def _ctype_of(c_type):
+    if c_type == "const long long*":
+        return ctypes.POINTER(ctypes.c_longlong)
     if "*" in c_type:
         return ctypes.c_void_p
     return {"int": ctypes.c_int, "float": ctypes.c_float, "size_t": ctypes.c_size_t,
@@ -202,6 +204,78 @@ def test_fwd_rejects(kw, status):
 ])
 def test_bwd_rejects(kw, status):
     assert bwd(**kw) == status
+
+
+def dense_strides(B, H, N, d, layout=fa.FA_LAYOUT_BHND):
+    if layout == fa.FA_LAYOUT_BNHD:
+        return [N * H * d, d, H * d]
+    return [H * N * d, N * d, d]
+
+
+def fwd_strided(strides=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, N=128, d=64, causal=0, scale=0.125, stream=None,
+             dtype=fa.FA_BF16)
+    a.update(kw)
+    if strides is None:
+        strides = dense_strides(a["B"], a["H"], a["N"], a["d"]) * 4
+    return fa.fa_fwd_strided(strides=strides, **a)
+
+
+def bwd_strided(strides=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, dO=P, lse=P, dq=P, dk=P, dv=P, B=2, H=3, N=128, d=64, causal=0,
+             scale=0.125, workspace=P, workspace_bytes=1 << 30, stream=None, dtype=fa.FA_BF16)
+    a.update(kw)
+    if strides is None:
+        strides = dense_strides(a["B"], a["H"], a["N"], a["d"]) * 8
+    return fa.fa_bwd_strided(strides=strides, **a)
+
+
+def _set(strides, tensor, values):
+    s = list(strides)
+    s[3 * tensor:3 * tensor + 3] = values
+    return s
+
+
+D = dense_strides(2, 3, 128, 64)
+
+
+@needs_lib
+@pytest.mark.parametrize("strides,kw,status", [
+    (None, dict(q=None), -1), (None, dict(d=80), -2), (None, dict(N=0), -1), (None, dict(q=P + 8), -1),
+    (None, dict(dtype=fa.FA_FP32, d=256), -2),
+    (_set(D * 4, 0, [D[0], D[1], -64]), {}, -1),           # negative row stride
+    (_set(D * 4, 1, [D[0], D[1], 68]), {}, -1),            # k rows 136 bytes apart: not 16-byte aligned
+    (_set(D * 4, 2, [D[0], 4, D[2]]), {}, -1),             # v head stride of 8 bytes
+    (_set(D * 4, 0, [1 << 41, D[1], D[2]]), {}, -1),       # beyond 2^40
+    (_set(D * 4, 0, [D[0], D[1], 1 << 23]), {}, -1),       # 128 rows of 2^24 bytes: 2^31
+    (_set(D * 4, 3, [0, D[1], D[2]]), {}, -1),             # o: two batches on the same rows
+    (_set(D * 4, 3, [D[0], D[1], 32]), {}, -1),            # o rows of 64 elements 32 apart
+    (_set(D * 4, 3, [D[0], 64, 64]), {}, -1),              # o: heads and rows interleave onto each other
+])
+def test_fwd_strided_rejects(strides, kw, status):
+    assert fwd_strided(strides, **kw) == status
+
+
+def test_fwd_strided_rejects_a_null_stride_array():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libfa.so not built")
+    lib = _lib.load()
+    assert lib.fa_fwd_strided(P, P, P, P, P, 1, 1, 128, 64, 0, 0.125, None, None, fa.FA_BF16) == -1
+    with pytest.raises(ValueError):
+        fa.fa_fwd_strided(P, P, P, P, P, 1, 1, 128, 64, 0, 0.125, [0] * 11, None, fa.FA_BF16)
+
+
+@needs_lib
+@pytest.mark.parametrize("strides,kw,status", [
+    (None, dict(dv=None), -1), (None, dict(workspace=None), -3), (None, dict(workspace_bytes=100), -3),
+    (_set(D * 8, 4, [D[0], D[1], 12]), {}, -1),            # dO rows 24 bytes apart
+    (_set(D * 8, 5, [D[0], 0, D[2]]), {}, -1),             # dq: every head on the same rows
+    (_set(D * 8, 7, [D[0], D[1], 0]), {}, -1),             # dv: every row on one row
+    (_set(D * 8, 6, [D[0], D[1], 4]), dict(dtype=fa.FA_FP32), -1),   # fp32 dk rows of 64 overlapping
+    (_set(D * 8, 6, [D[0], D[1], 6]), dict(dtype=fa.FA_FP32), -1),   # fp32 stride of 24 bytes
+])
+def test_bwd_strided_rejects(strides, kw, status):
+    assert bwd_strided(strides, **kw) == status
 
 
 @needs_lib
