@@ -24,12 +24,14 @@
 // In the hand-off variant (DSO) the bf16 dS operands of every block are also
 // stored to a buffer (layout: DsOut in fa_launch.h), from which a separate
 // kernel forms dQ = dS K without recomputing S and dP:
-//  - the four 16-byte stores of a step follow the step's products, after the
+//  - the 16-byte stores of a step (four per wave, two at d = 256, where the
+//    two waves of a key slice hold the same dS and each stores half of it)
+//    follow the step's products, after the
 //    masked and unmasked paths join (stores inside the two paths leave the
 //    compiler counting 0, 4 or 8 of them; holding dS into the next step made
 //    its register use jump past the file);
 //  - the barrier closing the step does not wait for them: vector memory
-//    operations retire in issue order, so once at most those four are
+//    operations retire in issue order, so once at most those stores are
 //    outstanding the prefetch issued before them has landed in LDS, and the
 //    barrier waits for that and for the wave's LDS reads only (a workgroup
 //    barrier with a full fence would wait for the stores too);
@@ -157,7 +159,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
 
     // dS hand-off: the wave's slice column within its head.  At d = 256 both
     // waves of a slice compute the same dS (the same instructions on the same
-    // operands) and both store it: the second write repeats the first's bytes.
+    // operands); each stores half of its micro-tiles.
     char* dsw = nullptr;
     if constexpr (DSO) dsw = dso.buf + (size_t)head * dso.head_bytes + (size_t)(kv0 / 32 + wave_u / DH) * 4096u;
 
@@ -295,11 +297,16 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
       // this wave's keys are all later than all queries of the block: P^ = 0.
       // The hand-off variant runs such a step anyway (masked, it yields
       // dS = 0; the waves of a workgroup move in step, so it costs no time)
-      // and stores to the sink, so that every path issues the same four
-      // stores, which its barrier below counts on.
+      // and stores to the sink, so that every path issues the same stores,
+      // which its barrier below counts on.
       const bool dead = (kvw >= N) || (CAUSAL && qb0 + BR - 1 < kvw);
       const bool skip = DSO ? false : dead;
-      bf16x8 dsv[BR / 16];   // the hand-off: this step's dS operands
+      // the hand-off: the dS micro-tiles this wave stores, SPW of the BR / 16
+      // (at d = 256 the two waves of a slice hold the same dS; the wave with
+      // dpart = 1 stores the second half)
+      constexpr int SPW = BR / 16 / DH;
+      const int st0 = DH > 1 ? SPW * __builtin_amdgcn_readfirstlane(dpart) : 0;
+      bf16x8 dsv[SPW];
       // one pass over the block; MASK: apply the causal / tail mask (a
       // compile-time variant, so the common unmasked path carries no mask code)
       auto compute = [&](auto mc) {
@@ -441,7 +448,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (DSO) {
 #pragma unroll
-          for (int st = 0; st < BR / 16; ++st) dsv[st] = da[st];
+          for (int st = 0; st < SPW; ++st) dsv[st] = DH > 1 ? (st0 ? da[SPW + st] : da[st]) : da[st];
         }
         // dS (bf16) to LDS, [key][query], for the dQ product of the atomic variant
         if constexpr (DQA) {
@@ -468,16 +475,17 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
         }
       }
       if constexpr (DSO) {
-        char* p = (dead ? dso.sink : dsw + ds_block_off(CAUSAL, i, dso.nks)) + 16 * ln;
+        char* p = (dead ? dso.sink : dsw + ds_block_off(CAUSAL, i, dso.nks)) + 16 * ln + 1024 * st0;
 #pragma unroll
-        for (int st = 0; st < BR / 16; ++st) __builtin_nontemporal_store(dsv[st], reinterpret_cast<bf16x8*>(p + 1024 * st));
-        // s_waitcnt vmcnt(4) lgkmcnt(0): all but the four stores (expcnt
-        // never waited for).  No fence: a release fence covers the loads into
-        // LDS and so waits for every memory operation; the empty asm
-        // statements with a memory clobber keep the compiler from moving
-        // memory accesses across the barrier.
+        for (int st = 0; st < SPW; ++st) __builtin_nontemporal_store(dsv[st], reinterpret_cast<bf16x8*>(p + 1024 * st));
+        // s_waitcnt vmcnt(SPW) lgkmcnt(0): all but the stores (expcnt never
+        // waited for).  No fence: a release fence covers the loads into LDS
+        // and so waits for every memory operation; the empty asm statements
+        // with a memory clobber keep the compiler from moving memory accesses
+        // across the barrier.
+        static_assert(SPW >= 1 && SPW <= 15, "vmcnt field");
         asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0x0074);
+        __builtin_amdgcn_s_waitcnt(0x0070 | SPW);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       } else {
@@ -603,14 +611,22 @@ static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v,
   const dim3 grid = bwd_kv_grid<D, CAUSAL>(BH, N), block(256);
   if constexpr (!DQA) {
     if (drop) {
-      if (ds.buf)
+      if constexpr (D == 256 && !CAUSAL) {
+        return launch_bwd_kv256_drop(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, CAUSAL, scale, lay, stream, *drop, ds);
+      } else if constexpr (D == 256) {
+        // causal d = 256: only the hand-off kernel is built in this unit
+        if (!ds.buf)
+          return launch_bwd_kv256_drop(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, CAUSAL, scale, lay, stream, *drop,
+                                       ds);
         return launch_bwd_dropout_t<D, CAUSAL, true>(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, scale, lay, stream,
                                                      *drop, ds);
-      if constexpr (D == 256)
-        return launch_bwd_kv256_drop(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, CAUSAL, scale, lay, stream, *drop);
-      else
+      } else {
+        if (ds.buf)
+          return launch_bwd_dropout_t<D, CAUSAL, true>(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, scale, lay, stream,
+                                                       *drop, ds);
         return launch_bwd_dropout_t<D, CAUSAL, false>(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, scale, lay,
                                                       stream, *drop, ds);
+      }
     }
     if (ds.buf) {
       hipLaunchKernelGGL((bwd_bf16_ds_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,

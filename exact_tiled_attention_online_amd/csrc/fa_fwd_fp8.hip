@@ -70,9 +70,13 @@ FA_DEV i32x8 cat_tr(i32x2v a, i32x2v b, i32x2v c, i32x2v d) {
   return cat8(lo, hi);
 }
 
-// four e4m3 codes of four floats in one dword (round to nearest even)
+// four e4m3 codes of four floats in one dword (round to nearest even).  The
+// first conversion writes the low half and keeps the high half of its third
+// operand, which the second conversion then overwrites; passing a's own bits
+// there (a dies here) lets the result take a's register, where a constant 0
+// cost one register initialisation per dword.
 FA_DEV int pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -254,16 +258,19 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
           m_run = mx;
         }
         const float nb = (SPLIT && m_run == -INFINITY) ? 7.f : 7.f - m_run * c;
-        float rs = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = exp2_fast(fmaf(s[mt][r], c, nb));
-            s[mt][r] = p;
-            rs += p;
-          }
-        l_run += rs;
+          for (int r = 0; r < 16; ++r) s[mt][r] = exp2_fast(fmaf(s[mt][r], c, nb));
+        // the tile's sum as a tree (31 adds, no chain through a zero start)
+        float part[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part[r] = s[0][r] + s[1][r];
+#pragma unroll
+        for (int w = 8; w > 0; w >>= 1)
+#pragma unroll
+          for (int r = 0; r < w; ++r) part[r] += part[r + w];
+        l_run += part[0];
         // P^T as the B operand: byte 16*mt + r of this lane (query qrow,
         // group h) is the key kvb + 32*mt + 8*(r/4) + 4*h + r%4
 #pragma unroll

@@ -123,12 +123,13 @@ hipError_t launch_bwd_kv256(const void* q, const void* k, const void* v, const v
                             const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
                             Layouts lay, hipStream_t stream, const DropArgs* drop, DsOut ds);
 
-// d = 256 with dropout, without the hand-off: from a unit of its own, built
-// without VGPR-form MFMA results (with them the compiler's AGPR-copy rewrite
-// crashes on these kernels, which sit at the register limit).
+// d = 256 with dropout, except the causal kernel with the dS stores: from a
+// unit of its own, built without VGPR-form MFMA results (with them the
+// compiler's AGPR-copy rewrite crashes on these kernels, which sit at the
+// register limit).  ds.buf selects the hand-off kernel as in launch_bwd_bf16.
 hipError_t launch_bwd_kv256_drop(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                                  const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
-                                 Layouts lay, hipStream_t stream, const DropArgs& drop);
+                                 Layouts lay, hipStream_t stream, const DropArgs& drop, DsOut ds);
 
 // dQ = bf16(scale * dS K) from the hand-off buffer (query-block outer, no
 // recompute, no atomics).
