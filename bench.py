@@ -184,6 +184,63 @@ def summarize_busy(csv_path, last):
         print(f"| `{name}` | {len(v)} | {us:.1f} | {ghz:.2f} | {busy:.3f} | {busy * ghz:.2f} |")
 
 
+STALL_COUNTERS_A = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                    "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAIT_ANY")
+STALL_COUNTERS_B = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_ACTIVE_INST_MISC",
+                    "SQ_WAVES", "GRBM_GUI_ACTIVE")
+
+
+def summarize_stalls(csv_a, csv_b, last):
+    """Issue and stall breakdown per kernel from two rocprofv3 --pmc runs of
+    this script (STALL_COUNTERS_A, then STALL_COUNTERS_B; one pass may hold at
+    most 8 SQ counters).  Per kernel, averages over its last `last`
+    dispatches:
+      - instructions per wave (SQ_INSTS_* / SQ_WAVES; SQ_INSTS_VALU counts the
+        MFMA instructions too, so the VALU column subtracts them);
+      - the VALU issue time those instructions need, at 4 cycles per
+        instruction of a 64-lane wave, as a fraction of all SIMD cycles
+        (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs): a lower bound on the vector
+        pipe's share of the kernel;
+      - the matrix pipe's busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over the same);
+      - SQ_ACTIVE_INST_ANY, SQ_WAIT_INST_ANY and SQ_WAIT_ANY as fractions of
+        SQ_WAVE_CYCLES (the wave issuing; waiting for an instruction to issue,
+        its operands or a functional unit; waiting on s_waitcnt or a barrier)."""
+    import collections
+    import csv
+    rows = collections.defaultdict(dict)
+    for tag, path in (("a", csv_a), ("b", csv_b)):
+        for r in csv.DictReader(open(path)):
+            d = rows[(tag, int(r["Dispatch_Id"]))]
+            d["name"] = _short_name(r["Kernel_Name"])
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for (tag, _), d in sorted(rows.items()):
+        for key, val in d.items():
+            if key != "name":
+                per[d["name"]][key].append(val)
+    out = []
+    for name, c in per.items():
+        if not all(k in c for k in STALL_COUNTERS_A + STALL_COUNTERS_B):
+            continue
+        m = {k: sum(v[-last:]) / len(v[-last:]) for k, v in c.items()}
+        if m["SQ_INSTS_MFMA"] <= 0 or m["SQ_WAVES"] <= 0 or m["SQ_WAVE_CYCLES"] <= 0:
+            continue
+        simd_cycles = m["GRBM_GUI_ACTIVE"] / 8 * 1024
+        waves = m["SQ_WAVES"]
+        valu = m["SQ_INSTS_VALU"] - m["SQ_INSTS_MFMA"]
+        wc = m["SQ_WAVE_CYCLES"]
+        out.append((simd_cycles, f"| `{name}` | {waves:.0f} | {valu / waves:.0f} | {m['SQ_INSTS_MFMA'] / waves:.0f} | "
+                                 f"{m['SQ_INSTS_LDS'] / waves:.0f} | {4 * valu / simd_cycles:.2f} | "
+                                 f"{m['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.2f} | "
+                                 f"{m['SQ_ACTIVE_INST_ANY'] / wc:.2f} | {m['SQ_WAIT_INST_ANY'] / wc:.2f} | "
+                                 f"{m['SQ_WAIT_ANY'] / wc:.2f} |"))
+    print("| kernel | waves | VALU / wave | MFMA / wave | LDS / wave | VALU issue (of SIMD cycles) | "
+          "MFMA busy (of SIMD cycles) | issuing | waiting to issue | waiting (waitcnt, barrier) |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for _, line in sorted(out, key=lambda t: -t[0]):
+        print(line)
+
+
 def summarize_counters(fetch_csv, write_csv, copy_mib, out_json):
     """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
     WRITE_SIZE, with --copy-probe-mib) into HBM bytes per launch per kernel.
@@ -721,6 +778,9 @@ def main():
     ap.add_argument("--summarize-busy", nargs=2, metavar=("PMC_CSV", "LAST"),
                     help="print per-kernel clock and MFMA-busy fraction from a rocprofv3 --kernel-trace --pmc "
                          "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES run and exit")
+    ap.add_argument("--summarize-stalls", nargs=3, metavar=("PMC_A_CSV", "PMC_B_CSV", "LAST"),
+                    help="print per-kernel instruction counts, pipe use and stall fractions from two "
+                         "rocprofv3 --pmc runs (the counters of STALL_COUNTERS_A, then STALL_COUNTERS_B) and exit")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "LAST"),
                     help="print per-kernel durations from a rocprofv3 --kernel-trace CSV: over all "
                          "launches and over the last LAST launches (the timed steps) and exit")
@@ -730,6 +790,9 @@ def main():
         return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace[0], int(args.summarize_trace[1]))
+        return 0
+    if args.summarize_stalls:
+        summarize_stalls(args.summarize_stalls[0], args.summarize_stalls[1], int(args.summarize_stalls[2]))
         return 0
     if args.summarize_counters:
         fcsv, wcsv, mib = args.summarize_counters

@@ -146,6 +146,31 @@ def test_busy_summary_clock_and_fraction(tmp_path, capsys):
     assert cells[1] == "3" and cells[2] == "500.0" and cells[3] == "2.00" and cells[4] == "0.500"
 
 
+def test_stall_summary_counts_and_fractions(tmp_path, capsys):
+    """Two passes over the same two dispatches: per wave 100000 VALU
+    instructions besides 20000 MFMA ones; 8 XCDs x 1e6 active cycles are
+    1e6 cycles of each of the 1024 SIMDs, of which 4 x 1e5 x 1024 (0.4) are
+    VALU issue and 0.5e6 x 1024 matrix-pipe busy; the wave-cycle fractions
+    are taken as given."""
+    a, b = [], []
+    for dsp in range(2):
+        for name, val in (("SQ_WAVE_CYCLES", 1000.0), ("SQ_BUSY_CYCLES", 1.0), ("SQ_WAIT_INST_ANY", 300.0),
+                          ("SQ_ACTIVE_INST_ANY", 450.0), ("SQ_ACTIVE_INST_VALU", 1.0), ("SQ_ACTIVE_INST_LDS", 1.0),
+                          ("SQ_VALU_MFMA_BUSY_CYCLES", 0.5e6 * 1024), ("SQ_WAIT_ANY", 250.0)):
+            a.append((dsp, KV, name, val, 0, 1))
+        for name, val in (("SQ_INSTS_VALU", 120000.0 * 1024), ("SQ_INSTS_MFMA", 20000.0 * 1024),
+                          ("SQ_INSTS_LDS", 30000.0 * 1024), ("SQ_INSTS_SALU", 1.0), ("SQ_ACTIVE_INST_MISC", 1.0),
+                          ("SQ_WAVES", 1024.0), ("GRBM_GUI_ACTIVE", 8e6)):
+            b.append((dsp, KV, name, val, 0, 1))
+    pa, pb = tmp_path / "a.csv", tmp_path / "b.csv"
+    _write_pmc(pa, a)
+    _write_pmc(pb, b)
+    bench.summarize_stalls(str(pa), str(pb), 2)
+    line = next(l for l in capsys.readouterr().out.splitlines() if "bwd_bf16_kernel" in l)
+    cells = [c.strip() for c in line.strip("|").split("|")]
+    assert cells[1:] == ["1024", "100000", "20000", "30000", "0.40", "0.50", "0.45", "0.30", "0.25"], cells
+
+
 def test_trace_summary_last_launches(tmp_path, capsys):
     p = tmp_path / "t.csv"
     with open(p, "w", newline="") as f:
