@@ -209,7 +209,7 @@ int check_split(int B, int H, int Nq, int Nk, int d, int causal, float scale, in
   if (st != FA_OK) return st;
   st = check_shape(B, H, Nk, d, causal, scale, dtype, layout);
   if (st != FA_OK) return st;
-  if (dtype != FA_BF16 || d == 256) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   if (causal && Nq > Nk) return FA_ERR_INVALID;
   if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_INVALID;
   return FA_OK;

@@ -183,6 +183,7 @@ hipError_t launch_fwd_merge(const float* opart, const float* lpart, void* o, flo
                        nsplit, lay);
   };
   if (d == 128) go(IC<128>{});
+  else if (d == 256) go(IC<256>{});
   else if (d == 96) go(IC<96>{});
   else go(IC<64>{});
   return hipGetLastError();

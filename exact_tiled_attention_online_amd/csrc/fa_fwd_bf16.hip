@@ -345,7 +345,7 @@ FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
 // register file per wave (Q rows and the O accumulator alone take 192)
 template <int D, int NW, bool SPLIT>
 constexpr int fwd_min_blocks() {
-  return SPLIT ? 2 : (D > 128 ? 4 / NW : 8 / NW);
+  return SPLIT ? (D > 128 ? 1 : 2) : (D > 128 ? 4 / NW : 8 / NW);
 }
 
 template <int D, bool CAUSAL, int NW, int BC, bool SPLIT>
@@ -419,6 +419,9 @@ hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, fl
                                  int BH, int Nq, int Nk, int d, bool causal, float scale, int nsplit,
                                  int span, Layouts lay, hipStream_t stream) {
   const SplitArgs sp{Nk, Nk - Nq, nsplit, span, opart, lpart};
+  if (d == 256)
+    return causal ? launch_fwd_split_t<256, true>(q, k, v, BH, Nq, scale, lay, sp, stream)
+                  : launch_fwd_split_t<256, false>(q, k, v, BH, Nq, scale, lay, sp, stream);
   if (d == 128)
     return causal ? launch_fwd_split_t<128, true>(q, k, v, BH, Nq, scale, lay, sp, stream)
                   : launch_fwd_split_t<128, false>(q, k, v, BH, Nq, scale, lay, sp, stream);

@@ -29,8 +29,9 @@
  * (queries and keys share the index range 0..N-1).
  *
  * Supported: d in {64, 96, 128}, and d = 256 for bf16 (fa_fwd, fa_bwd and its
- * stages, and the dropout forward and backward; other d, fp32 at d = 256 and
- * the FP8 and split-key-range forwards at d = 256 are FA_ERR_UNSUPPORTED); N >= 1 (any
+ * stages, the strided calls, the dropout forward and backward and the bf16
+ * split-key-range forward; other d, fp32 at d = 256 and the FP8 forwards at
+ * d = 256 are FA_ERR_UNSUPPORTED); N >= 1 (any
  * N, tails are masked); B, H >= 1 with B*H*N*d < 2^31; scale finite and > 0;
  * causal in {0, 1}.
  *
@@ -310,7 +311,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
  * num_splits), 256-byte aligned; its contents on entry do not matter (the
  * size function returns 0 for shapes, d or num_splits that fa_fwd_splitkv
  * rejects).  Supported: dtype FA_BF16 only (FA_ERR_UNSUPPORTED otherwise), d in
- * {64, 96, 128}, 0 <= num_splits <= 1024.  Errors, ownership and streams as for
+ * {64, 96, 128, 256}, 0 <= num_splits <= 1024.  Errors, ownership and streams as for
  * fa_fwd; a missing or small workspace is FA_ERR_WORKSPACE.
  */
 size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);

@@ -423,10 +423,10 @@ def test_tensors_of_2_pow_31_elements_are_unsupported():
 
 
 @needs_lib
-def test_head_dim_256_is_bf16_fwd_bwd_only():
+def test_head_dim_256_is_bf16_only_and_not_fp8():
     """d = 256 exists for the bf16 forward and backward (with and without
-    dropout); the fp32 path and the split-key-range and FP8 forwards have no
-    d = 256 kernels."""
+    dropout) and the bf16 split-key-range forward; the fp32 path and the FP8
+    forwards have no d = 256 kernels."""
     base = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=64, d=256, causal=1, scale=0.0625, stream=None,
                 layout=fa.FA_LAYOUT_BHND)
     assert fa.fa_fwd(**base, dtype=fa.FA_FP32) == -2
@@ -435,10 +435,14 @@ def test_head_dim_256_is_bf16_fwd_bwd_only():
     assert fa.fa_bwd_workspace_bytes(1, 2, 64, 256, fa.FA_FP32) == 0
     assert fa.fa_fwd_dropout(**dict(base, o=None), drop_t=26, seed=1, offset=0) == -1   # shape accepted
     assert fa.fa_fwd_fp8(**base, descale_q=1.0, descale_k=1.0, descale_v=1.0) == -2
-    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 64, 256, 0) == 0
-    sk = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=4, Nk=64, d=256, causal=1, scale=0.0625, num_splits=0,
+    # split: 64 keys are 2 tiles, fewer than the 4 a range takes at least, so one range: O and LSE
+    # partials of 4 rows x 2 heads
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 64, 256, 0) == round_up(1 * 2 * 4 * 256 * 4) + 256
+    assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 64, 256, 0) == 0
+    sk = dict(q=None, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=4, Nk=64, d=256, causal=1, scale=0.0625, num_splits=0,
               workspace=P, workspace_bytes=1 << 20, stream=None, dtype=fa.FA_BF16, layout=fa.FA_LAYOUT_BHND)
-    assert fa.fa_fwd_splitkv(**sk) == -2
+    assert fa.fa_fwd_splitkv(**sk) == -1   # the shape passes; the null q is rejected
+    assert fa.fa_fwd_splitkv(**dict(sk, q=P, dtype=fa.FA_FP32)) == -2
 
 
 
@@ -482,7 +486,7 @@ def test_buffer_checks_of_the_binding():
 @needs_lib
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1), (dict(B=0), -1), (dict(Nq=0), -1),
-    (dict(causal=2), -1), (dict(scale=0.0), -1), (dict(d=80), -2), (dict(d=256), -2), (dict(dtype=fa.FA_FP32), -2),
+    (dict(causal=2), -1), (dict(scale=0.0), -1), (dict(d=80), -2), (dict(d=512), -2), (dict(dtype=fa.FA_FP32), -2),
     (dict(causal=1, Nq=2000, Nk=1000), -1), (dict(num_splits=-1), -1), (dict(num_splits=5000), -1),
     (dict(layout=5), -1), (dict(q=P + 8), -1),
     # more partial results than the static scratch holds: 64 ranges x 4096 rows x (128 + 1) floats

@@ -53,6 +53,10 @@ CASES = [
     (2, 2, 3, 777, 96, True, 0),
     (1, 3, 40, 500, 96, False, 2),
     (1, 1, 1, 1, 64, True, 0),
+    (2, 3, 1, 1000, 256, True, 0),
+    (1, 2, 33, 777, 256, False, 3),
+    (1, 2, 100, 100, 256, True, 0),
+    (1, 1, 7, 4099, 256, True, 1024),
 ]
 
 
