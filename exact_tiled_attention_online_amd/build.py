@@ -40,7 +40,7 @@ def variant_path(name=None):
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_bwd_bf16.hip", "fa_bwd_kv256.hip", "fa_bwd_kv256_drop.hip",
-           "fa_bwd_dq.hip",
+           "fa_bwd_kv2.hip", "fa_bwd_dq.hip",
            "fa_bwd_dq_ds.hip", "fa_aux.hip", "fa_fp32.hip", "fa_noalloc.hip", "fa_api.cpp"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in device code.

@@ -1,6 +1,7 @@
 // fa_bwd_kv_body.h -- the key/value-block-outer backward kernel (dK, dV), bf16
-// inputs/outputs, fp32 accumulation; instantiated by fa_bwd_bf16.hip (d <= 128)
-// and fa_bwd_kv256.hip (d = 256).
+// inputs/outputs, fp32 accumulation; instantiated by fa_bwd_bf16.hip (d <= 128),
+// fa_bwd_kv256.hip (d = 256) and fa_bwd_kv256_drop.hip (three d = 256 dropout
+// kernels, built without VGPR-form MFMA results).
 //
 // Key/value-block outer, query-block inner (page
 // "flash-attention-backpropagation" (aiqz.cc), section QKV梯度): one

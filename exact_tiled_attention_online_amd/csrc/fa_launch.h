@@ -131,6 +131,12 @@ hipError_t launch_bwd_kv256_drop(const void* q, const void* k, const void* v, co
                                  const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
                                  Layouts lay, hipStream_t stream, const DropArgs& drop, DsOut ds);
 
+// d = 128, without dropout or the atomic dQ: the key/value-outer kernel with
+// two waves per SIMD (fa_bwd_kv2.hip); with ds.buf, also storing dS.
+hipError_t launch_bwd_kv2(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
+                          const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
+                          Layouts lay, hipStream_t stream, DsOut ds);
+
 // dQ = bf16(scale * dS K) from the hand-off buffer (query-block outer, no
 // recompute, no atomics).
 hipError_t launch_bwd_dq_ds(DsOut ds, const void* k, void* dq, int BH, int N, int d, bool causal, float scale,

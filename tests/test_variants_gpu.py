@@ -12,6 +12,9 @@ libfa_tile_alt.so is another tile configuration: 4-wave forward and
 recomputing-dQ workgroups (128 query rows instead of 256) and other operand
 read distances in the dK/dV, dQ and forward pipelines.  Its outputs must meet
 the oracle bar.
+
+The two-waves-per-SIMD dK/dV kernel (FA_KV_KERNEL=2, d = 128) is held to
+the oracle bar and to the same bit identity with the checking build.
 """
 import math
 import os
@@ -90,3 +93,37 @@ def test_other_tile_configuration_meets_the_bar(B, H, N, d, causal, method):
 def test_variant_libraries_are_built_from_the_same_sources():
     for path in (DEBUG, ALT):
         assert os.path.exists(path), path
+
+
+# the two-waves-per-SIMD dK/dV kernel (d = 128, selected per call with
+# FA_KV_KERNEL=2): ragged tails, both masks, both dQ methods
+KV2_CASES = [(1, 2, n, causal) for n in (1, 17, 64, 129, 300) for causal in (False, True)]
+KV2_CASES += [(2, 3, 1000, True), (1, 4, 4099, False)]
+
+
+@pytest.mark.parametrize("B,H,N,causal", KV2_CASES)
+@pytest.mark.parametrize("method", [fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE])
+def test_two_wave_dkdv_kernel_meets_the_bar(monkeypatch, B, H, N, causal, method):
+    log(f"[kv2] B={B} H={H} N={N} causal={causal} method={method}")
+    monkeypatch.setenv("FA_KV_KERNEL", "2")
+    x = gen.make_inputs(gen.workload("c3"), shape=(B, H, N, 128), seed=N + 5)
+    scale = 1.0 / math.sqrt(128)
+    res = run_gpu(x, "bf16", causal, scale, method=method)
+    want = oracle_heads(x, causal, scale, heads=None)
+    for (b, h), w in want.items():
+        got = {n: res[n][b, h] for n in ("o", "lse", "dq", "dk", "dv")}
+        compare(got, w, "bf16", where=f"kv2 N{N} c{int(causal)} head ({b},{h})")
+
+
+@pytest.mark.parametrize("B,H,N,causal", [(1, 4, 1000, True), (1, 2, 129, False)])
+@pytest.mark.parametrize("method", [fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE])
+def test_two_wave_dkdv_kernel_debug_sync_same_bits(monkeypatch, B, H, N, causal, method):
+    import torch
+    log(f"[kv2 debug-sync] B={B} H={H} N={N} causal={causal} method={method}")
+    monkeypatch.setenv("FA_KV_KERNEL", "2")
+    x = gen.make_inputs(gen.workload("c3"), shape=(B, H, N, 128), seed=N + 6)
+    a = _step(x, 128, causal, method)
+    with _lib.using_library(DEBUG):
+        b = _step(x, 128, causal, method)
+    for name in a:
+        assert torch.equal(a[name], b[name]), f"{name} differs from the build with a barrier after every prefetch"
