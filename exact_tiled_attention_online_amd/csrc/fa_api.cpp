@@ -487,13 +487,13 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
   const int st = check_shape(B, H, N, d, causal, scale, FA_BF16, layout);
   if (st != FA_OK) return st;
-  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (d == 256) return FA_ERR_UNSUPPORTED;   // FP8 tiles hold rows of at most 128 bytes
   for (float x : {descale_q, descale_k, descale_v})
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID;
   if (!std::isfinite(scale * descale_q * descale_k) || !(scale * descale_q * descale_k > 0.f)) return FA_ERR_INVALID;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
-  return hip_status(fa::launch_fwd_fp8(q, k, v, o, lse, B * H, N, causal != 0, scale, descale_q, descale_k,
+  return hip_status(fa::launch_fwd_fp8(q, k, v, o, lse, B * H, N, d, causal != 0, scale, descale_q, descale_k,
                                        descale_v, dense_layouts(H, N, N, d, layout),
                                        static_cast<hipStream_t>(stream)));
 }
@@ -524,7 +524,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 }
 
 size_t fa_fwd_splitkv_fp8_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
-  if (check_split(B, H, Nq, Nk, d, 0, 1.f, num_splits, FA_BF16, FA_LAYOUT_BHND) != FA_OK || d != 128) return 0;
+  if (check_split(B, H, Nq, Nk, d, 0, 1.f, num_splits, FA_BF16, FA_LAYOUT_BHND) != FA_OK || d == 256) return 0;
   return split_plan(nullptr, B, H, Nq, Nk, d, num_splits, fa::kSplitBC8).bytes;
 }
 
@@ -534,7 +534,7 @@ int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o, flo
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
   const int st = check_split(B, H, Nq, Nk, d, causal, scale, num_splits, FA_BF16, layout);
   if (st != FA_OK) return st;
-  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (d == 256) return FA_ERR_UNSUPPORTED;   // FP8 tiles hold rows of at most 128 bytes
   for (float x : {descale_q, descale_k, descale_v})
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID;
   if (!std::isfinite(scale * descale_q * descale_k) || !(scale * descale_q * descale_k > 0.f)) return FA_ERR_INVALID;
@@ -546,7 +546,7 @@ int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o, flo
   const SplitPlan p = split_plan(workspace, B, H, Nq, Nk, d, num_splits, fa::kSplitBC8);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const fa::Layouts lay = dense_layouts(H, Nq, Nk, d, layout);
-  const int r = hip_status(fa::launch_fwd_split_fp8(q, k, v, p.opart, p.lpart, B * H, Nq, Nk, causal != 0, scale,
+  const int r = hip_status(fa::launch_fwd_split_fp8(q, k, v, p.opart, p.lpart, B * H, Nq, Nk, d, causal != 0, scale,
                                                     descale_q, descale_k, descale_v, p.nsplit, p.span, lay, s));
   if (r != FA_OK) return r;
   return hip_status(fa::launch_fwd_merge(p.opart, p.lpart, o, lse, B * H, Nq, d, p.nsplit, lay, s));

@@ -92,10 +92,13 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
     const unsigned char* __restrict__ Q, const unsigned char* __restrict__ K,
     const unsigned char* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N,
     int nqb, float scale_qk, float c, float dv, Layouts lay, SplitArgs sp) {
-  static_assert(D == 128, "FP8 tiles are laid out for 128-byte rows");
+  static_assert(D == 64 || D == 96 || D == 128, "FP8 tiles hold rows of at most 128 bytes");
   constexpr int BR = 32 * NW, BC = 64;
-  constexpr int ROWB = D;            // bytes per e4m3 row
-  constexpr int KS = D / 64;         // K-steps of the S product
+  // LDS rows are 128 bytes for every head dim (the 128-byte swizzle); d = 64
+  // and 96 fill 4 and 6 of their 8 chunks, and the fetch points the other
+  // lanes at a row's last chunk (in bounds, finite, multiplied by zeros below)
+  constexpr int ROWB = 128;
+  constexpr int KS = (D + 63) / 64;  // K-steps of 64 d of the S product
   constexpr int DT = D / 32;         // 32-row tiles of O^T
   constexpr int TILEB = BC * ROWB;   // bytes of one K or V tile
 
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h = lane >> 5;
   // strides in elements (= bytes for the e4m3 inputs)
-  const TileFetch<ROWB, BC, NW> fetch(wave, lane, lay.k.sn);   // K rows; V rows at vrs
+  const TileFetch<ROWB, BC, NW, D / 16> fetch(wave, lane, lay.k.sn);   // K rows; V rows at vrs
   const unsigned vrs = (unsigned)lay.v.sn;
   const int bid = blockIdx.x;
   const int head = bid % BH;
@@ -128,11 +131,13 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
   const int q0 = qb * BR + wave * 32;
   const int qrow = q0 + l32;
 
-  // Q rows as B operands: lane (query l32, group h) holds d = 64s + 32h .. +31
+  // Q rows as B operands: lane (query l32, group h) holds d = 64s + 32h .. +31;
+  // zeros past d (d = 96: the second K-step's upper half), so that the
+  // padding chunks of the K tiles add nothing to S
   i32x8 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    if (qrow < N) {
+    if (qrow < N && 64 * s + 32 * h < D) {
       const i32x4v* p = reinterpret_cast<const i32x4v*>(Qh + (size_t)qrow * lay.q.sn + 64 * s + 32 * h);
       qf[s] = cat8(p[0], p[1]);
     } else {
@@ -336,47 +341,59 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
   }
 }
 
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 static hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                                    int N, float scale_qk, float dv, Layouts lay, hipStream_t stream) {
   constexpr int NW = FA_FP8_NW, BR = 32 * NW;
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
-  hipLaunchKernelGGL((fwd_fp8_kernel<128, CAUSAL, NW, false>), grid, block, 0, stream, (const unsigned char*)q,
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW, false>), grid, block, 0, stream, (const unsigned char*)q,
                      (const unsigned char*)k, (const unsigned char*)v, (bf16*)o, lse, BH, N, nqb, scale_qk,
                      scale_qk * kLog2e, dv, lay, SplitArgs{});
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, float dq, float dk, float dv, Layouts lay,
                           hipStream_t stream) {
   const float scale_qk = scale * dq * dk;
-  return causal ? launch_fwd_fp8_t<true>(q, k, v, o, lse, BH, N, scale_qk, dv, lay, stream)
-                : launch_fwd_fp8_t<false>(q, k, v, o, lse, BH, N, scale_qk, dv, lay, stream);
+  auto go = [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    return causal ? launch_fwd_fp8_t<D, true>(q, k, v, o, lse, BH, N, scale_qk, dv, lay, stream)
+                  : launch_fwd_fp8_t<D, false>(q, k, v, o, lse, BH, N, scale_qk, dv, lay, stream);
+  };
+  if (d == 64) return go(IC<64>{});
+  if (d == 96) return go(IC<96>{});
+  return go(IC<128>{});
 }
 
 // Split mode: one-wave workgroups of 32 query rows against one key range of
 // whole 64-key tiles (32 KB of LDS), partial results to the workspace.
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 static hipError_t launch_fwd_split_fp8_t(const void* q, const void* k, const void* v, int BH, int Nq,
                                          float scale_qk, float dv, Layouts lay, const SplitArgs& sp,
                                          hipStream_t stream) {
   const int nqb = (Nq + 31) / 32;
   const dim3 grid((unsigned)(nqb * sp.nsplit * BH)), block(64);
-  hipLaunchKernelGGL((fwd_fp8_kernel<128, CAUSAL, 1, true>), grid, block, 0, stream, (const unsigned char*)q,
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 1, true>), grid, block, 0, stream, (const unsigned char*)q,
                      (const unsigned char*)k, (const unsigned char*)v, nullptr, nullptr, BH, Nq, nqb, scale_qk,
                      scale_qk * kLog2e, dv, lay, sp);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_split_fp8(const void* q, const void* k, const void* v, float* opart, float* lpart,
-                                int BH, int Nq, int Nk, bool causal, float scale, float dq, float dk, float dv,
-                                int nsplit, int span, Layouts lay, hipStream_t stream) {
+                                int BH, int Nq, int Nk, int d, bool causal, float scale, float dq, float dk,
+                                float dv, int nsplit, int span, Layouts lay, hipStream_t stream) {
   const SplitArgs sp{Nk, Nk - Nq, nsplit, span, opart, lpart};
   const float scale_qk = scale * dq * dk;
-  return causal ? launch_fwd_split_fp8_t<true>(q, k, v, BH, Nq, scale_qk, dv, lay, sp, stream)
-                : launch_fwd_split_fp8_t<false>(q, k, v, BH, Nq, scale_qk, dv, lay, sp, stream);
+  auto go = [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    return causal ? launch_fwd_split_fp8_t<D, true>(q, k, v, BH, Nq, scale_qk, dv, lay, sp, stream)
+                  : launch_fwd_split_fp8_t<D, false>(q, k, v, BH, Nq, scale_qk, dv, lay, sp, stream);
+  };
+  if (d == 64) return go(IC<64>{});
+  if (d == 96) return go(IC<96>{});
+  return go(IC<128>{});
 }
 
 }  // namespace fa

@@ -277,9 +277,9 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
  * most 2^-4 each), so O carries an error of up to about 2^-4 * max|V|, while
  * LSE is as accurate as fa_fwd's.
  *
- * Supported: d = 128 only (FA_ERR_UNSUPPORTED otherwise); B, H, N, causal,
- * scale, layout, ownership, streams and errors as for fa_fwd.  Pointers must
- * be 16-byte aligned (lse 4-byte).
+ * Supported: d in {64, 96, 128} (FA_ERR_UNSUPPORTED otherwise); B, H, N,
+ * causal, scale, layout, ownership, streams and errors as for fa_fwd.
+ * Pointers must be 16-byte aligned (lse 4-byte).
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, int causal, float scale,
@@ -346,8 +346,9 @@ int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
  * codes and per-tensor descales as in fa_fwd_fp8 (decoding against an FP8
  * key/value cache reads half the bytes of bf16).  Ranges are whole 64-key
  * tiles; the workspace must hold fa_fwd_splitkv_fp8_workspace_bytes(...)
- * bytes for the same num_splits.  Accuracy as fa_fwd_fp8.  Supported: d = 128
- * only; other arguments and errors as for fa_fwd_splitkv and fa_fwd_fp8.
+ * bytes for the same num_splits.  Accuracy as fa_fwd_fp8.  Supported: d in
+ * {64, 96, 128}; other arguments and errors as for fa_fwd_splitkv and
+ * fa_fwd_fp8 (fa_fwd_splitkv_fp8_workspace_bytes returns 0 for any other d).
  */
 size_t fa_fwd_splitkv_fp8_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
 int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o, float* lse,

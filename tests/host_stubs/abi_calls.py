@@ -126,12 +126,12 @@ for d in (64, 96, 128):
                                                                      0.125, ns, ws, need - 1, None, BF16, 1))
                 expect(st, WORKSPACE, f"splitkv short d={d} ns={ns}")
                 n_split += 2
-                if d == 128:
+                if True:   # the FP8 split forward exists at d = 64, 96 and 128
                     need8 = lib.fa_fwd_splitkv_fp8_workspace_bytes(B, H, Nq, Nk, d, ns)
                     st = with_ws(need8, lambda ws: lib.fa_fwd_splitkv_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal,
                                                                           0.125, 1.0, 1.0, 1.0, ns, ws, need8,
                                                                           None, 0))
-                    expect(st, OK, f"splitkv fp8 c={causal} {B}x{H}x{Nq}x{Nk} ns={ns}")
+                    expect(st, OK, f"splitkv fp8 d={d} c={causal} {B}x{H}x{Nq}x{Nk} ns={ns}")
                     n_split += 1
 print(f"split forwards: {n_split} calls", flush=True)
 

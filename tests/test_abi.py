@@ -341,7 +341,7 @@ def fwd8(**kw):
     (dict(q=None), -1), (dict(v=None), -1), (dict(lse=None), -1), (dict(N=0), -1), (dict(causal=3), -1),
     (dict(scale=0.0), -1), (dict(descale_q=0.0), -1), (dict(descale_k=-1.0), -1),
     (dict(descale_v=float("inf")), -1), (dict(descale_q=float("nan")), -1), (dict(layout=2), -1),
-    (dict(d=64), -2), (dict(d=96), -2), (dict(k=P + 4), -1), (dict(o=P + 2), -1),
+    (dict(d=256), -2), (dict(d=80), -2), (dict(k=P + 4), -1), (dict(o=P + 2), -1),
     (dict(scale=1e30, descale_q=1e30, descale_k=1e30), -1),
 ])
 def test_fp8_rejects(kw, status):
@@ -351,7 +351,7 @@ def test_fp8_rejects(kw, status):
 @needs_lib
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(Nq=0), -1), (dict(Nq=1001), -1), (dict(num_splits=-2), -1),
-    (dict(descale_v=0.0), -1), (dict(d=64), -2), (dict(layout=4), -1), (dict(workspace=None), -3),
+    (dict(descale_v=0.0), -1), (dict(d=256), -2), (dict(d=80), -2), (dict(layout=4), -1), (dict(workspace=None), -3),
     (dict(workspace_bytes=64), -3),
 ])
 def test_splitkv_fp8_rejects(kw, status):
@@ -369,8 +369,10 @@ def test_splitkv_fp8_workspace_uses_64_key_tiles():
         per = -(-tiles // ns)
         used = -(-tiles // per)
         r = lambda x: -(-x // 256) * 256
-        assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, 128, ns) == r(used * 8 * 128 * 4) + r(used * 8 * 4)
-    assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, 96, 0) == 0
+        for d in (64, 96, 128):
+            assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, d, ns) == r(used * 8 * d * 4) + r(used * 8 * 4)
+    assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, 256, 0) == 0
+    assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, 80, 0) == 0
 
 
 @needs_lib

@@ -191,3 +191,66 @@ def test_fp8_forward_maximum_size_sampled_heads():
         assert rs <= 1.0, rs
     del q8, k8, v8, o, lse
     torch.cuda.empty_cache()
+
+
+# head dims 64 and 96: LDS rows of 128 bytes with 4 or 6 chunks of data; at d =
+# 96 the second 64-wide K-step of S multiplies the padding chunks by the
+# zeros Q holds past d
+HD_CASES = [(d, n, causal, sig) for d in (64, 96) for n in (1, 17, 129, 300) for causal in (False, True)
+            for sig in (1.0, 3.0)]
+
+
+@pytest.mark.parametrize("d,n,causal,sig", HD_CASES)
+def test_fp8_forward_other_head_dims(d, n, causal, sig):
+    log(f"[fp8 d{d}] N={n} causal={causal} sigma_qk={sig}")
+    x = gen.make_fp8_inputs((2, 3, n, d), seed=700 + n + d, sigma_qk=sig)
+    scale = 1.0 / math.sqrt(d)
+    got = run_fp8(x, causal, scale)
+    r = check(x, got, causal, scale, f"fp8 d{d} N{n} c{int(causal)} s{sig}")
+    rs = max(stat_ratio(x["q"][b, h], x["k"][b, h], x["v"][b, h], got["o"][b, h], scale, causal)
+             for b in range(2) for h in range(3))
+    log(f"  worst O error / bound {r:.3f}, / per-element bound {rs:.3f}")
+    assert rs <= 1.0, rs
+
+
+@pytest.mark.parametrize("d", [64, 96])
+def test_fp8_forward_other_head_dims_larger_size(d):
+    """Whole heads of a causal 1 x 4 x 4096 shape (64 key tiles) in both
+    layouts, with the planted displaced tile that the per-element bound must
+    reject."""
+    log(f"[fp8 d{d}] 1x4x4096 causal")
+    x = gen.make_fp8_inputs((1, 4, 4096, d), seed=800 + d)
+    scale = 1.0 / math.sqrt(d)
+    for layout in (fa.FA_LAYOUT_BHND, fa.FA_LAYOUT_BNHD):
+        got = run_fp8(x, True, scale, layout)
+        check(x, got, True, scale, f"fp8 d{d} 4096 layout{layout}")
+        for h in range(4):
+            r = stat_ratio(x["q"][0, h], x["k"][0, h], x["v"][0, h], got["o"][0, h], scale, True)
+            assert r <= 1.0, (layout, h, r)
+    k2, v2 = displaced_tile(x["k"][0, 1], x["v"][0, 1], at=30)
+    r_bad = stat_ratio(x["q"][0, 1], k2, v2, got["o"][0, 1], scale, True)
+    log(f"  planted displaced tile: ratio {r_bad:.2f}")
+    assert r_bad > 1.0, r_bad
+
+
+@pytest.mark.parametrize("d", [64, 96])
+@pytest.mark.parametrize("B,H,Nq,Nk,causal,ns", [(2, 3, 1, 1000, True, 0), (1, 2, 33, 2000, True, 5),
+                                                 (1, 4, 7, 513, False, 3)])
+def test_fp8_split_forward_other_head_dims(d, B, H, Nq, Nk, causal, ns):
+    import torch
+    log(f"[fp8-split d{d}] B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} splits={ns}")
+    xq = gen.make_fp8_inputs((B, H, Nq, d), seed=900 + Nq + Nk + d, sigma_qk=2.0)
+    xk = gen.make_fp8_inputs((B, H, Nk, d), seed=950 + Nq + Nk + d, sigma_qk=2.0)
+    q8, k8, v8 = (torch.from_numpy(a).cuda() for a in (xq["q8"], xk["k8"], xk["v8"]))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.forward_splitkv_fp8(q8, k8, v8, xq["descale_q"], xk["descale_k"], xk["descale_v"], causal, scale,
+                                    num_splits=ns)
+    torch.cuda.synchronize()
+    got_o, got_l = to_np(o), to_np(lse)
+    ro, rl = ref.forward_rect(xq["q"], xk["k"], xk["v"], scale, causal)
+    for b in range(B):
+        for h in range(H):
+            vmax = float(np.abs(xk["v"][b, h]).max())
+            tol = (2.0 ** -4 + Nk * 2.0 ** -17) * vmax + 2.0 ** -9 * float(np.abs(ro[b, h]).max())
+            assert float(np.abs(got_o[b, h] - ro[b, h]).max()) <= tol, (b, h)
+            assert float(np.abs(got_l[b, h] - rl[b, h]).max()) <= LSE_ATOL, (b, h)
