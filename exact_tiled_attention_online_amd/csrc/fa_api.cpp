@@ -28,7 +28,7 @@ int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype, 
   if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID;
   if (layout != FA_LAYOUT_BHND && layout != FA_LAYOUT_BNHD) return FA_ERR_INVALID;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID;   // any finite scale (negative and 0 included)
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
   // d = 256: bf16 only (the fp32 kernels hold a row of q and o per lane pair)
   if (d != 64 && d != 96 && d != 128 && !(d == 256 && dtype == FA_BF16)) return FA_ERR_UNSUPPORTED;
@@ -490,7 +490,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   if (d == 256) return FA_ERR_UNSUPPORTED;   // FP8 tiles hold rows of at most 128 bytes
   for (float x : {descale_q, descale_k, descale_v})
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID;
-  if (!std::isfinite(scale * descale_q * descale_k) || !(scale * descale_q * descale_k > 0.f)) return FA_ERR_INVALID;
+  if (!std::isfinite(scale * descale_q * descale_k)) return FA_ERR_INVALID;   // the scores' factor
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
   return hip_status(fa::launch_fwd_fp8(q, k, v, o, lse, B * H, N, d, causal != 0, scale, descale_q, descale_k,
@@ -537,7 +537,7 @@ int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o, flo
   if (d == 256) return FA_ERR_UNSUPPORTED;   // FP8 tiles hold rows of at most 128 bytes
   for (float x : {descale_q, descale_k, descale_v})
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID;
-  if (!std::isfinite(scale * descale_q * descale_k) || !(scale * descale_q * descale_k > 0.f)) return FA_ERR_INVALID;
+  if (!std::isfinite(scale * descale_q * descale_k)) return FA_ERR_INVALID;   // the scores' factor
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID;
   if (!workspace || !aligned(workspace, kAlign) ||

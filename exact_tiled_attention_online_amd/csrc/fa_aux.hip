@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O, c
 hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float* ndrow, float* nlse,
                           float* dq_acc, int BH, int N, int d, float scale, bool fp32, Layouts lay,
                           hipStream_t stream) {
-  const float inv_scale = 1.f / scale;
+  const float inv_scale = 1.f / ledger_scale(scale);   // the ledger the bf16 kernels start from
   const size_t rows = (size_t)BH * N;
   auto go = [&](auto dc, auto tc) {
     constexpr int D = decltype(dc)::value;

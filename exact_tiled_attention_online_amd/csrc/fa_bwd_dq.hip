@@ -171,13 +171,15 @@ FA_DEV void bwd_dq_body(const bf16* __restrict__ Q, const bf16* __restrict__ K, 
           if (k == KS - 1) {
             __builtin_amdgcn_sched_barrier(0);
             // register r: key kvb + 32*mt + 8*(r/4) + 4*h + r%4, query qrow.
-            // Masked scores become -inf (P^ = 0), behind one uniform branch.
+            // Masked scores become an infinity of c's opposite sign (c s = -inf,
+            // P^ = 0; c < 0 for a negative scale), behind one uniform branch.
             if (need_mask) {
+              const float dead_s = c > 0.f ? -INFINITY : INFINITY;
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int kv = kvb + 32 * mt + 8 * (r >> 2) + 4 * h + (r & 3);
                 const bool dead = (kv >= N) | (qrow >= N) | (CAUSAL & (kv > qrow));
-                s[r] = dead ? -INFINITY : s[r];
+                s[r] = dead ? dead_s : s[r];
               }
             }
             if constexpr (DROP) {
@@ -270,15 +272,15 @@ static hipError_t launch_bwd_dq_t(const void* q, const void* k, const void* v, c
   constexpr int NW = D == 256 ? 4 : FA_DQ_NW, BR = 32 * NW;   // d = 256: one wave per SIMD
   const int nqb = (N + BR - 1) / BR;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * NW);
+  const float c = ledger_scale(scale) * kLog2e;   // dQ keeps the caller's scale
   if (drop) {
     hipLaunchKernelGGL((bwd_dq_dropout_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb,
-                       scale, scale * kLog2e, lay, *drop);
+                       scale, c, lay, *drop);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, NW>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
-                     (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, scale * kLog2e,
-                     lay);
+                     (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dq, BH, N, nqb, scale, c, lay);
   return hipGetLastError();
 }
 

@@ -366,7 +366,7 @@ hipError_t launch_bwd_kv2(const void* q, const void* k, const void* v, const voi
   const int nkb = (N + BC - 1) / BC, nqb = (N + 63) / 64;
   const int items = causal ? (nkb + 1) / 2 : nkb;
   const dim3 grid((unsigned)(items * BH)), block(512);
-  const float c = scale * kLog2e;
+  const float c = ledger_scale(scale) * kLog2e;   // dK keeps the caller's scale
   auto go = [&](auto kern, DsOut d) {
     hipLaunchKernelGGL(kern, grid, block, 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
                        (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH, N, nqb, scale, c, lay, d);

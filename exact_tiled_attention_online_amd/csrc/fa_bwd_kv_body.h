@@ -598,7 +598,8 @@ static hipError_t launch_bwd_dropout_t(const void* q, const void* k, const void*
                                        DsOut ds) {
   const dim3 grid = bwd_kv_grid<D, CAUSAL>(BH, N), block(256);
   hipLaunchKernelGGL((bwd_bf16_dropout_kernel<D, CAUSAL, DSO>), grid, block, 0, stream, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH, N, (N + 63) / 64, scale, scale * kLog2e, lay, drop,
+                     (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH, N,
+                     (N + 63) / 64, scale, ledger_scale(scale) * kLog2e, lay, drop,
                      DSO ? ds : DsOut{});
   return hipGetLastError();
 }
@@ -610,6 +611,7 @@ static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v,
                                     const DropArgs* drop, DsOut ds) {
   const int nqb = (N + 63) / 64;
   const dim3 grid = bwd_kv_grid<D, CAUSAL>(BH, N), block(256);
+  const float c = ledger_scale(scale) * kLog2e;   // dK keeps the caller's scale
   if constexpr (!DQA) {
     if (drop) {
       if constexpr (D == 256 && !CAUSAL) {
@@ -632,13 +634,13 @@ static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v,
     if (ds.buf) {
       hipLaunchKernelGGL((bwd_bf16_ds_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)dO, nlse, ndrow, (bf16*)dk, (bf16*)dv, BH, N, nqb, scale,
-                         scale * kLog2e, lay, ds);
+                         c, lay, ds);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL, DQA>), grid, block, 0, stream, (const bf16*)q,
                      (const bf16*)k, (const bf16*)v, (const bf16*)dO, nlse, ndrow, dq_acc, (bf16*)dk,
-                     (bf16*)dv, BH, N, nqb, scale, scale * kLog2e, lay);
+                     (bf16*)dv, BH, N, nqb, scale, c, lay);
   return hipGetLastError();
 }
 

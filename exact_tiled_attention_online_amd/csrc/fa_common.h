@@ -265,6 +265,13 @@ struct TileFetch {
   }
 };
 
+// x with the sign of every element flipped when neg (uniform), else x: the
+// sign of a negative scale folded into a bf16 operand (exact).
+FA_DEV bf16x8 neg_bf16x8(bf16x8 x, int neg) {
+  const uint32_t m = neg ? 0x80008000u : 0u;
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, x) ^ u32x4{m, m, m, m});
+}
+
 FA_DEV bf16x8 pack8(float a0, float a1, float a2, float a3, float b0, float b1, float b2, float b3) {
   bf16x8 r;
   r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;

@@ -99,7 +99,8 @@ FA_DEV void fwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     if (qrow < N)
-      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * lay.q.sn + 16 * s + 8 * h);
+      qf[s] = neg_bf16x8(*reinterpret_cast<const bf16x8*>(Qh + (size_t)qrow * lay.q.sn + 16 * s + 8 * h),
+                         lay.qk_neg);
     else
       qf[s] = bf16x8{};
   }
@@ -388,6 +389,8 @@ static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v,
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                            int N, int d, bool causal, float scale, Layouts lay, hipStream_t stream,
                            const DropArgs* drop) {
+  lay.qk_neg = scale < 0.f;
+  scale = softmax_scale(scale);
   if (d == 128)
     return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream, drop)
                   : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream, drop);
@@ -418,6 +421,8 @@ static hipError_t launch_fwd_split_t(const void* q, const void* k, const void* v
 hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, float* opart, float* lpart,
                                  int BH, int Nq, int Nk, int d, bool causal, float scale, int nsplit,
                                  int span, Layouts lay, hipStream_t stream) {
+  lay.qk_neg = scale < 0.f;
+  scale = softmax_scale(scale);
   const SplitArgs sp{Nk, Nk - Nq, nsplit, span, opart, lpart};
   if (d == 256)
     return causal ? launch_fwd_split_t<256, true>(q, k, v, BH, Nq, scale, lay, sp, stream)

@@ -139,7 +139,9 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
   for (int s = 0; s < KS; ++s) {
     if (qrow < N && 64 * s + 32 * h < D) {
       const i32x4v* p = reinterpret_cast<const i32x4v*>(Qh + (size_t)qrow * lay.q.sn + 64 * s + 32 * h);
-      qf[s] = cat8(p[0], p[1]);
+      // a negative scale: the sign bit of every e4m3 code flipped (exact)
+      const int m = lay.qk_neg ? (int)0x80808080u : 0;
+      qf[s] = cat8(p[0], p[1]) ^ i32x8{m, m, m, m, m, m, m, m};
     } else {
       qf[s] = i32x8{};
     }
@@ -356,7 +358,8 @@ static hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, float dq, float dk, float dv, Layouts lay,
                           hipStream_t stream) {
-  const float scale_qk = scale * dq * dk;
+  lay.qk_neg = scale < 0.f;
+  const float scale_qk = softmax_scale(fabsf(scale) * dq * dk);
   auto go = [&](auto dc) {
     constexpr int D = decltype(dc)::value;
     return causal ? launch_fwd_fp8_t<D, true>(q, k, v, o, lse, BH, N, scale_qk, dv, lay, stream)
@@ -385,7 +388,8 @@ hipError_t launch_fwd_split_fp8(const void* q, const void* k, const void* v, flo
                                 int BH, int Nq, int Nk, int d, bool causal, float scale, float dq, float dk,
                                 float dv, int nsplit, int span, Layouts lay, hipStream_t stream) {
   const SplitArgs sp{Nk, Nk - Nq, nsplit, span, opart, lpart};
-  const float scale_qk = scale * dq * dk;
+  lay.qk_neg = scale < 0.f;
+  const float scale_qk = softmax_scale(fabsf(scale) * dq * dk);
   auto go = [&](auto dc) {
     constexpr int D = decltype(dc)::value;
     return causal ? launch_fwd_split_fp8_t<D, true>(q, k, v, BH, Nq, scale_qk, dv, lay, sp, stream)

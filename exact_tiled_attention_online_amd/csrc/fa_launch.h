@@ -3,6 +3,7 @@
 // validated by the C-ABI layer (fa_api.cpp) before any of these is called.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stddef.h>
 
 namespace fa {
@@ -23,11 +24,30 @@ struct RowLayout {
 struct Layouts {
   RowLayout q, k, v, o, g, dq, dk, dv;
   int H;   // heads per batch
+  // 1 for a negative scale in the bf16 and FP8 forwards: they flip the sign
+  // of their Q operand and run the softmax with softmax_scale(scale) > 0.  Set
+  // by the forward launchers from the scale they are given.
+  int qk_neg = 0;
   __host__ __device__ __forceinline__ size_t off(const RowLayout& t, int hb) const {
     const int b = hb / H, h = hb - b * H;
     return (size_t)((long long)b * t.sb + (long long)h * t.sh);
   }
 };
+
+// The scale the softmax of the bf16 and FP8 forwards runs with: |scale|, at
+// least 2^-100.  They take the row maximum of raw dot products q.k, which needs
+// a positive scale; the sign of a negative one goes into Q (Layouts::qk_neg).
+// Below 2^-100 in magnitude (0 included) every score of a row is the same to
+// fp32 rounding (|scale * q.k| < 2^-100 times the largest dot product), as it
+// is with 2^-100.
+inline float softmax_scale(float scale) { return fmaxf(fabsf(scale), 0x1p-100f); }
+
+// The scale of the backward's ledger -LSE/scale and of its recompute
+// P^ = 2^(scale log2(e) (q.k - LSE/scale)), which holds for either sign: the
+// caller's scale, or 2^-100 below 2^-100 in magnitude, where every recomputed
+// probability of a row is e^-LSE to fp32 rounding and the ledger must stay
+// finite.  dQ and dK keep the caller's scale.
+inline float ledger_scale(float scale) { return fabsf(scale) >= 0x1p-100f ? scale : 0x1p-100f; }
 
 // Arguments of the forward kernels' split-key-range mode (unused otherwise).
 struct SplitArgs {

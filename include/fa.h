@@ -32,8 +32,9 @@
  * stages, the strided calls, the dropout forward and backward and the bf16
  * split-key-range forward; other d, fp32 at d = 256 and the FP8 forwards at
  * d = 256 are FA_ERR_UNSUPPORTED); N >= 1 (any
- * N, tails are masked); B, H >= 1 with B*H*N*d < 2^31; scale finite and > 0;
- * causal in {0, 1}.
+ * N, tails are masked); B, H >= 1 with B*H*N*d < 2^31; scale any finite value
+ * (negative and 0 included: S = scale * Q K^T as written; below 2^-100 in
+ * magnitude every score of a row is equal to fp32 rounding); causal in {0, 1}.
  *
  * Ownership: every pointer is a device pointer owned by the caller.  The
  * library allocates and frees nothing and never synchronises; each call only
@@ -271,11 +272,12 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
  *
  * The method is fa_fwd's (page "flash-attention-v2-sram-tiling", section 5)
  * on the FP8 matrix instructions, the FP8 forward the pages attribute to
- * FlashAttention-3 (page "data.6616ai.com flash-attention").  S and the
- * softmax statistics are computed from the exact code products in fp32; the
+ * FlashAttention-3 (page "data.6616ai.com flash-attention").  S comes from
+ * the FP8 matrix instruction, whose dot products of codes are within
+ * 2^-14 * sum_c |q_c k_c| of the exact sum (measured), so LSE is within
+ * 1e-3 + 2^-14 * |scale| * max_j sum_c |q_ic k_jc| of the exact value; the
  * probabilities are rounded to e4m3 for the P V product (relative error at
- * most 2^-4 each), so O carries an error of up to about 2^-4 * max|V|, while
- * LSE is as accurate as fa_fwd's.
+ * most 2^-4 each), so O carries an error of up to about 2^-4 * max|V|.
  *
  * Supported: d in {64, 96, 128} (FA_ERR_UNSUPPORTED otherwise); B, H, N,
  * causal, scale, layout, ownership, streams and errors as for fa_fwd.

@@ -41,3 +41,29 @@ def displaced_tile(k, v, tile=64, at=1):
     return k2, v2
 
 
+
+
+# The FP8 matrix instruction does not add the 32 or 64 code products of a
+# dot product exactly in fp32: measured on single dot products (N = 1, so that
+# LSE = scale * q.k; tests/test_fp8_gpu.py::test_fp8_score_error), its result
+# differs from the exact sum by up to 1.96e-5 (about 2^-15.6) times
+# sum_c |q_c k_c|, for d = 64 and 128 and spreads 0.25 to 4.  The LSE bar of
+# the FP8 forward therefore adds 2^-14 (three times that) times the largest
+# |scale| sum_c |q_ic k_jc| of the row to the bf16 bar of 1e-3.
+SCORE_REL = 2.0 ** -14
+
+
+def lse_bar(q, k, scale, causal, lse_atol=1e-3, panel=512):
+    """Per-row LSE tolerance of the FP8 forward for one head (q [Nq, d], k
+    [Nk, d] in fp64; causal with the query rows at the end of the keys)."""
+    n, nk = q.shape[0], k.shape[0]
+    out = np.empty(n)
+    aq, ak = np.abs(q), np.abs(k)
+    for r0 in range(0, n, panel):
+        r1 = min(n, r0 + panel)
+        m = aq[r0:r1] @ ak.T
+        if causal:
+            rows = np.arange(r0, r1)[:, None] + (nk - n)
+            m = np.where(np.arange(nk)[None, :] > rows, 0.0, m)
+        out[r0:r1] = lse_atol + SCORE_REL * abs(scale) * m.max(axis=1)
+    return out

@@ -184,8 +184,7 @@ def bwd(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
     (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1), (dict(causal=2), -1),
-    (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1), (dict(scale=0.0), -1),
-    (dict(scale=-0.1), -1), (dict(d=80), -2), (dict(d=512), -2), (dict(d=256, dtype=fa.FA_FP32), -2),
+    (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1), (dict(d=80), -2), (dict(d=512), -2), (dict(d=256, dtype=fa.FA_FP32), -2),
     (dict(dtype=7), -2),
     (dict(q=P + 8), -1), (dict(lse=P + 2), -1),
     (dict(B=1024, H=1024, N=4096, d=128), -2),
@@ -339,7 +338,7 @@ def fwd8(**kw):
 @needs_lib
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(v=None), -1), (dict(lse=None), -1), (dict(N=0), -1), (dict(causal=3), -1),
-    (dict(scale=0.0), -1), (dict(descale_q=0.0), -1), (dict(descale_k=-1.0), -1),
+    (dict(scale=float("-inf")), -1), (dict(descale_q=0.0), -1), (dict(descale_k=-1.0), -1),
     (dict(descale_v=float("inf")), -1), (dict(descale_q=float("nan")), -1), (dict(layout=2), -1),
     (dict(d=256), -2), (dict(d=80), -2), (dict(k=P + 4), -1), (dict(o=P + 2), -1),
     (dict(scale=1e30, descale_q=1e30, descale_k=1e30), -1),
@@ -377,7 +376,7 @@ def test_splitkv_fp8_workspace_uses_64_key_tiles():
 
 @needs_lib
 @pytest.mark.parametrize("kw,status", [
-    (dict(q=None), -1), (dict(o=None), -1), (dict(N=0), -1), (dict(causal=2), -1), (dict(scale=-1.0), -1),
+    (dict(q=None), -1), (dict(o=None), -1), (dict(N=0), -1), (dict(causal=2), -1), (dict(scale=float("nan")), -1),
     (dict(drop_t=-1), -1), (dict(drop_t=256), -1), (dict(layout=3), -1), (dict(d=80), -2), (dict(v=P + 8), -1),
 ])
 def test_fwd_dropout_rejects(kw, status):
@@ -488,7 +487,7 @@ def test_buffer_checks_of_the_binding():
 @needs_lib
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1), (dict(B=0), -1), (dict(Nq=0), -1),
-    (dict(causal=2), -1), (dict(scale=0.0), -1), (dict(d=80), -2), (dict(d=512), -2), (dict(dtype=fa.FA_FP32), -2),
+    (dict(causal=2), -1), (dict(scale=float("nan")), -1), (dict(d=80), -2), (dict(d=512), -2), (dict(dtype=fa.FA_FP32), -2),
     (dict(causal=1, Nq=2000, Nk=1000), -1), (dict(num_splits=-1), -1), (dict(num_splits=5000), -1),
     (dict(layout=5), -1), (dict(q=P + 8), -1),
     # more partial results than the static scratch holds: 64 ranges x 4096 rows x (128 + 1) floats
@@ -532,3 +531,14 @@ def test_split_conveniences_check_the_cache_geometry():
     _lib._check_kv_heads(Shape((2, 3, 4, 128)), Shape((2, 1000, 4, 128)), fa.FA_LAYOUT_BNHD)
     with pytest.raises(ValueError):
         _lib._check_kv_heads(Shape((2, 3, 4, 128)), Shape((2, 1000, 1, 128)), fa.FA_LAYOUT_BNHD)
+
+
+@needs_lib
+@pytest.mark.parametrize("scale", [-0.125, -1e-30, 0.0, -0.0, 1e-40, 3.0e38])
+def test_any_finite_scale_passes_the_checks(scale):
+    """Any finite scale is accepted (the checks then reach the null pointer
+    that follows them): negative, zero, subnormal and huge values."""
+    assert fwd(scale=scale, o=None) == -1
+    assert bwd(scale=scale, dq=None) == -1
+    assert fwd(scale=scale, d=80) == -2            # the shape check ran past the scale
+    assert bwd(scale=scale, d=80) == -2

@@ -158,8 +158,8 @@ def compare_dropout(got, want, x, b, h, scale, causal, where):
     q, k, v, do = (x[n][b, h] for n in ("q", "k", "v", "do"))
     _, _, _, p = ref.head_forward(q, k, v, scale, causal)
     dD = 2.0 ** -8 * np.abs(do * want["o"]).sum(axis=1)
-    extra = {"dq": scale * dD.max() * np.abs(k).max(),
-             "dk": scale * (p * dD[:, None]).sum(axis=0).max() * np.abs(q).max()}
+    extra = {"dq": abs(scale) * dD.max() * np.abs(k).max(),
+             "dk": abs(scale) * (p * dD[:, None]).sum(axis=0).max() * np.abs(q).max()}
     for n in ("dq", "dk"):
         g, r = np.asarray(got[n]), np.asarray(want[n])
         assert np.isfinite(g).all(), f"{where} {n}: non-finite values"
