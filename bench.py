@@ -21,7 +21,8 @@ bf16 (the headline shape).  ``detail.decode`` adds the split-key-range forward
 cached keys, with its HBM roofline, and ``detail.decode_fp8`` the same step
 against an FP8 cache (fa_fwd_splitkv_fp8) (skip both with --no-decode), and
 ``detail.fp8_forward`` the FP8 forward (fa_fwd_fp8) on the headline shape
-against the FP8 peak (skip with --no-fp8).
+against the FP8 peak (skip with --no-fp8); ``detail.head_dim_256.fp8_forward``
+the FP8 forward on the head dim 256 shape.
 """
 from __future__ import annotations
 
@@ -527,12 +528,14 @@ def decode_fp8_measurement(fa, gen, torch, dev, stream, with_oracle, reps=50, or
     return res
 
 
-def fp8_measurement(fa, gen, torch, dev, stream, w, with_oracle, reps=30, oracle_budget_s=4.0):
-    """The FP8 forward (fa_fwd_fp8) on the headline shape with e4m3fn inputs:
+def fp8_measurement(fa, gen, torch, dev, stream, w, with_oracle, reps=30, oracle_budget_s=4.0,
+                    counters="fwd_fp8_kernel"):
+    """The FP8 forward (fa_fwd_fp8) on workload w's shape with e4m3fn inputs:
     time per call from HIP events on the launch stream, credited forward
     FLOPs (4*B*H*N^2*d, halved for causal) against the dense FP8 peak, and,
     unless disabled, the oracle on whole heads (the values the codes stand
-    for) within the bound the tests use."""
+    for) within the bound the tests use.  `counters` names the stored
+    rocprofv3 counter entry for this shape (None: none taken)."""
     import numpy as np
     B, H, N, d = w.shape
     x = gen.make_fp8_inputs((B, H, N, d), seed=w.seed, sigma_qk=w.sigma_qk, sigma_v=w.sigma_vdo)
@@ -565,7 +568,7 @@ def fp8_measurement(fa, gen, torch, dev, stream, w, with_oracle, reps=30, oracle
            "us_per_call": round(ms * 1e3, 2), "calls": reps, "tflops": round(tf, 3),
            "roofline": {"kernel": "fwd_fp8_kernel", "bound": "mfma", "achieved": round(tf, 3),
                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
-                        "traffic": traffic_from_counters("fwd_fp8_kernel")}}
+                        "traffic": traffic_from_counters(counters) if counters else None}}
     if with_oracle:
         from oracle import ref
         got_o, got_l = o.float().cpu().numpy(), lse.cpu().numpy()
@@ -759,7 +762,7 @@ def main():
     ap.add_argument("--workload", default="c4", help="c1..c5 (default c4, the headline shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the FP8 forward on the headline shape (reported under detail)")
+                    help="skip the FP8 forwards on the headline and head dim 256 shapes (reported under detail)")
     ap.add_argument("--no-d256", action="store_true",
                     help="skip the head dim 256 step (1 x 16 x 8192 x 256, reported under detail)")
     ap.add_argument("--no-dropout", action="store_true",
@@ -973,6 +976,10 @@ def main():
                                                        not args.no_cpu_baseline, x)
     if not args.no_d256 and dtype == torch.bfloat16:
         out["detail"]["head_dim_256"] = head_dim_256_measurement(fa, torch, stream, not args.no_cpu_baseline)
+        if not args.no_fp8:
+            w256 = gen.Workload("bf16_b1h16_n8192_d256_causal", 1, 16, 8192, 256, "bf16", True, 1.0, 1.0, 256)
+            out["detail"]["head_dim_256"]["fp8_forward"] = fp8_measurement(
+                fa, gen, torch, dev, stream, w256, not args.no_cpu_baseline, counters=None)
     if not args.no_fp8 and B == 1 and d == 128:
         out["detail"]["fp8_forward"] = fp8_measurement(fa, gen, torch, dev, stream, w, not args.no_cpu_baseline)
     if not args.no_decode:

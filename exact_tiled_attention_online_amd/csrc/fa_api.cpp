@@ -487,7 +487,6 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
   const int st = check_shape(B, H, N, d, causal, scale, FA_BF16, layout);
   if (st != FA_OK) return st;
-  if (d == 256) return FA_ERR_UNSUPPORTED;   // FP8 tiles hold rows of at most 128 bytes
   for (float x : {descale_q, descale_k, descale_v})
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID;
   if (!std::isfinite(scale * descale_q * descale_k)) return FA_ERR_INVALID;   // the scores' factor
@@ -524,7 +523,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 }
 
 size_t fa_fwd_splitkv_fp8_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
-  if (check_split(B, H, Nq, Nk, d, 0, 1.f, num_splits, FA_BF16, FA_LAYOUT_BHND) != FA_OK || d == 256) return 0;
+  if (check_split(B, H, Nq, Nk, d, 0, 1.f, num_splits, FA_BF16, FA_LAYOUT_BHND) != FA_OK) return 0;
   return split_plan(nullptr, B, H, Nq, Nk, d, num_splits, fa::kSplitBC8).bytes;
 }
 
@@ -534,7 +533,6 @@ int fa_fwd_splitkv_fp8(const void* q, const void* k, const void* v, void* o, flo
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID;
   const int st = check_split(B, H, Nq, Nk, d, causal, scale, num_splits, FA_BF16, layout);
   if (st != FA_OK) return st;
-  if (d == 256) return FA_ERR_UNSUPPORTED;   // FP8 tiles hold rows of at most 128 bytes
   for (float x : {descale_q, descale_k, descale_v})
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_INVALID;
   if (!std::isfinite(scale * descale_q * descale_k)) return FA_ERR_INVALID;   // the scores' factor

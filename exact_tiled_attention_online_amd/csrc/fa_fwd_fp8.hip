@@ -88,16 +88,18 @@ FA_DEV int pack_fp8x4(float a, float b, float c, float d) {
 // bf16 forward (Nq queries against Nk keys, one range of whole tiles per
 // workgroup, partial O and LSE to the workspace for the merge kernel).
 template <int D, bool CAUSAL, int NW, bool SPLIT>
-__global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
+__global__ __launch_bounds__(64 * NW, D == 256 ? 1 : (SPLIT ? 2 : 12 / NW)) void fwd_fp8_kernel(
     const unsigned char* __restrict__ Q, const unsigned char* __restrict__ K,
     const unsigned char* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE, int BH, int N,
     int nqb, float scale_qk, float c, float dv, Layouts lay, SplitArgs sp) {
-  static_assert(D == 64 || D == 96 || D == 128, "FP8 tiles hold rows of at most 128 bytes");
+  static_assert(D == 64 || D == 96 || D == 128 || D == 256, "FP8 head dims");
   constexpr int BR = 32 * NW, BC = 64;
-  // LDS rows are 128 bytes for every head dim (the 128-byte swizzle); d = 64
-  // and 96 fill 4 and 6 of their 8 chunks, and the fetch points the other
-  // lanes at a row's last chunk (in bounds, finite, multiplied by zeros below)
-  constexpr int ROWB = 128;
+  // LDS rows are 128 bytes up to d = 128 (the 128-byte swizzle) and 256 bytes
+  // at d = 256 (the 256-byte swizzle); d = 64 and 96 fill 4 and 6 of their 8
+  // chunks, and the fetch points the other lanes at a row's last chunk (in
+  // bounds, finite, multiplied by zeros below).  Every offset of 16 or 32
+  // rows is a multiple of ROWB (the swizzles depend on the row mod 16 only).
+  constexpr int ROWB = D <= 128 ? 128 : 256;
   constexpr int KS = (D + 63) / 64;  // K-steps of 64 d of the S product
   constexpr int DT = D / 32;         // 32-row tiles of O^T
   constexpr int TILEB = BC * ROWB;   // bytes of one K or V tile
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
   }
 
   // LDS offsets.  K operand (key row l32 of a 32-key half, bytes 64s + 32h ..
-  // +31 as two 16-byte chunks): kb[s][hf] + 4096 * half (swz depends on the
+  // +31 as two 16-byte chunks): kb[s][hf] + 32 * ROWB * half (swz depends on the
   // row mod 16, so 32 rows down is a constant).
   int kb[KS][2];
 #pragma unroll
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
   // this lane supplies the segment of key row 16w + r0 (r0 as below), bytes
   // 32t + 16(G%2) + 8u .. +7, so that the receiving lane (d, group g) gets,
   // as its bytes 8w + e, V[key 16w + 8(e/4) + 4g + e%4][d]: the key order of
-  // the P^T operand.  Offset vb[t] + 2048 w.
+  // the P^T operand.  Offset vb[t] + 16 * ROWB * w.
   int vb[DT];
   {
     const int G = (lane >> 4) & 3, e = (lane & 15) >> 1, u = lane & 1;
@@ -209,11 +211,12 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 12 / NW) void fwd_fp8_kernel(
         if (i < KS) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
-            ka[i][mt] = cat8(lds_read_i128(Kt, kb[i][0] + 4096 * mt), lds_read_i128(Kt, kb[i][1] + 4096 * mt));
+            ka[i][mt] = cat8(lds_read_i128(Kt, kb[i][0] + 32 * ROWB * mt),
+                             lds_read_i128(Kt, kb[i][1] + 32 * ROWB * mt));
         } else {
           const int t = i - KS;
-          va[t] = cat_tr(lds_read_tr8(Vt, vb[t]), lds_read_tr8(Vt, vb[t] + 2048), lds_read_tr8(Vt, vb[t] + 4096),
-                         lds_read_tr8(Vt, vb[t] + 6144));
+          va[t] = cat_tr(lds_read_tr8(Vt, vb[t]), lds_read_tr8(Vt, vb[t] + 16 * ROWB),
+                         lds_read_tr8(Vt, vb[t] + 32 * ROWB), lds_read_tr8(Vt, vb[t] + 48 * ROWB));
         }
       };
       f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -367,6 +370,7 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
   };
   if (d == 64) return go(IC<64>{});
   if (d == 96) return go(IC<96>{});
+  if (d == 256) return go(IC<256>{});
   return go(IC<128>{});
 }
 
@@ -397,6 +401,7 @@ hipError_t launch_fwd_split_fp8(const void* q, const void* k, const void* v, flo
   };
   if (d == 64) return go(IC<64>{});
   if (d == 96) return go(IC<96>{});
+  if (d == 256) return go(IC<256>{});
   return go(IC<128>{});
 }
 

@@ -95,7 +95,7 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int N, int d, bool causal, float scale, Layouts lay, hipStream_t stream,
                            const DropArgs* drop = nullptr);
 
-// FP8 (e4m3fn) forward, d = 64, 96 or 128: O (bf16) and LSE for Q = dq * Q8,
+// FP8 (e4m3fn) forward, d = 64, 96, 128 or 256: O (bf16) and LSE for Q = dq * Q8,
 // K = dk * K8, V = dv * V8.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                           bool causal, float scale, float dq, float dk, float dv, Layouts lay,
@@ -110,8 +110,8 @@ hipError_t launch_fwd_split_bf16(const void* q, const void* k, const void* v, fl
                                  int BH, int Nq, int Nk, int d, bool causal, float scale, int nsplit,
                                  int span, Layouts lay, hipStream_t stream);
 
-// The same for FP8 (e4m3fn) q, k, v with per-tensor descales, d = 64, 96 or
-// 128; ranges are whole kSplitBC8-key tiles.
+// The same for FP8 (e4m3fn) q, k, v with per-tensor descales, d = 64, 96, 128
+// or 256; ranges are whole kSplitBC8-key tiles.
 constexpr int kSplitBC8 = 64;
 hipError_t launch_fwd_split_fp8(const void* q, const void* k, const void* v, float* opart, float* lpart,
                                 int BH, int Nq, int Nk, int d, bool causal, float scale, float dq, float dk, float dv,

@@ -28,10 +28,10 @@
  * scale * q_i . k_j.  The causal mask keeps key j for query i iff j <= i
  * (queries and keys share the index range 0..N-1).
  *
- * Supported: d in {64, 96, 128}, and d = 256 for bf16 (fa_fwd, fa_bwd and its
- * stages, the strided calls, the dropout forward and backward and the bf16
- * split-key-range forward; other d, fp32 at d = 256 and the FP8 forwards at
- * d = 256 are FA_ERR_UNSUPPORTED); N >= 1 (any
+ * Supported: d in {64, 96, 128, 256}, except fp32 at d = 256 (d = 256 runs
+ * for bf16 in fa_fwd, fa_bwd and its stages, the strided calls, the dropout
+ * forward and backward and the split-key-range forward, and in the FP8
+ * forwards; other d and fp32 at d = 256 are FA_ERR_UNSUPPORTED); N >= 1 (any
  * N, tails are masked); B, H >= 1 with B*H*N*d < 2^31; scale any finite value
  * (negative and 0 included: S = scale * Q K^T as written; below 2^-100 in
  * magnitude every score of a row is equal to fp32 rounding); causal in {0, 1}.
@@ -279,8 +279,8 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
  * probabilities are rounded to e4m3 for the P V product (relative error at
  * most 2^-4 each), so O carries an error of up to about 2^-4 * max|V|.
  *
- * Supported: d in {64, 96, 128} (FA_ERR_UNSUPPORTED otherwise); B, H, N,
- * causal, scale, layout, ownership, streams and errors as for fa_fwd.
+ * Supported: d in {64, 96, 128, 256}; B, H, N, causal, scale, layout,
+ * ownership, streams and errors as for fa_fwd.
  * Pointers must be 16-byte aligned (lse 4-byte).
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -349,7 +349,7 @@ int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
  * key/value cache reads half the bytes of bf16).  Ranges are whole 64-key
  * tiles; the workspace must hold fa_fwd_splitkv_fp8_workspace_bytes(...)
  * bytes for the same num_splits.  Accuracy as fa_fwd_fp8.  Supported: d in
- * {64, 96, 128}; other arguments and errors as for fa_fwd_splitkv and
+ * {64, 96, 128, 256}; other arguments and errors as for fa_fwd_splitkv and
  * fa_fwd_fp8 (fa_fwd_splitkv_fp8_workspace_bytes returns 0 for any other d).
  */
 size_t fa_fwd_splitkv_fp8_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);

@@ -111,7 +111,7 @@ for d in (64, 96, 128, 256):
 print(f"backward: {n_calls} calls", flush=True)
 
 n_split = 0
-for d in (64, 96, 128):
+for d in (64, 96, 128, 256):
     for causal in (0, 1):
         for B, H, Nq, Nk in [(1, 1, 1, 1), (2, 3, 1, 1000), (1, 2, 7, 4097), (2, 1, 64, 64), (1, 1, 5, 300)]:
             for ns in (0, 1, 2, 3, 7, 1024):
@@ -126,14 +126,18 @@ for d in (64, 96, 128):
                                                                      0.125, ns, ws, need - 1, None, BF16, 1))
                 expect(st, WORKSPACE, f"splitkv short d={d} ns={ns}")
                 n_split += 2
-                if True:   # the FP8 split forward exists at d = 64, 96 and 128
-                    need8 = lib.fa_fwd_splitkv_fp8_workspace_bytes(B, H, Nq, Nk, d, ns)
-                    st = with_ws(need8, lambda ws: lib.fa_fwd_splitkv_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal,
-                                                                          0.125, 1.0, 1.0, 1.0, ns, ws, need8,
-                                                                          None, 0))
-                    expect(st, OK, f"splitkv fp8 d={d} c={causal} {B}x{H}x{Nq}x{Nk} ns={ns}")
-                    n_split += 1
-print(f"split forwards: {n_split} calls", flush=True)
+                need8 = lib.fa_fwd_splitkv_fp8_workspace_bytes(B, H, Nq, Nk, d, ns)
+                st = with_ws(need8, lambda ws: lib.fa_fwd_splitkv_fp8(q, k, v, o, lse, B, H, Nq, Nk, d, causal,
+                                                                      0.125, 1.0, 1.0, 1.0, ns, ws, need8,
+                                                                      None, 0))
+                expect(st, OK, f"splitkv fp8 d={d} c={causal} {B}x{H}x{Nq}x{Nk} ns={ns}")
+                n_split += 1
+        for B, H, N in SHAPES:
+            for lay in (0, 1):
+                st = lib.fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, causal, 0.125, 1.0, 1.0, 1.0, None, lay)
+                expect(st, OK, f"fa_fwd_fp8 d={d} c={causal} {B}x{H}x{N} lay={lay}")
+                n_split += 1
+print(f"split and FP8 forwards: {n_split} calls", flush=True)
 
 # strided views: accepted layouts run (here: reach the stand-in launchers),
 # and every accepted output view is free of overlap, checked by enumerating

@@ -32,7 +32,7 @@ hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, float*,
 }
 hipError_t launch_fwd_fp8(const void*, const void*, const void*, void*, float*, int, int, int d, bool, float, float,
                           float, float, Layouts, hipStream_t) {
-  return bad(d != 64 && d != 96 && d != 128) ? hipErrorInvalidValue : hipSuccess;
+  return bad(d != 64 && d != 96 && d != 128 && d != 256) ? hipErrorInvalidValue : hipSuccess;
 }
 hipError_t launch_fwd_split_bf16(const void*, const void*, const void*, float* opart, float* lpart, int BH, int Nq,
                                  int Nk, int d, bool, float, int nsplit, int span, Layouts, hipStream_t) {
@@ -46,7 +46,7 @@ hipError_t launch_fwd_split_fp8(const void*, const void*, const void*, float* op
                                 int Nk, int d, bool, float, float, float, float, int nsplit, int span, Layouts,
                                 hipStream_t) {
   if (bad(span % kSplitBC8 != 0 || (long long)nsplit * span < Nk || (long long)(nsplit - 1) * span >= Nk ||
-          (d != 64 && d != 96 && d != 128)))
+          (d != 64 && d != 96 && d != 128 && d != 256)))
     return hipErrorInvalidValue;
   touch(opart, (size_t)nsplit * BH * Nq * d * sizeof(float));
   touch(lpart, (size_t)nsplit * BH * Nq * sizeof(float));

@@ -340,7 +340,7 @@ def fwd8(**kw):
     (dict(q=None), -1), (dict(v=None), -1), (dict(lse=None), -1), (dict(N=0), -1), (dict(causal=3), -1),
     (dict(scale=float("-inf")), -1), (dict(descale_q=0.0), -1), (dict(descale_k=-1.0), -1),
     (dict(descale_v=float("inf")), -1), (dict(descale_q=float("nan")), -1), (dict(layout=2), -1),
-    (dict(d=256), -2), (dict(d=80), -2), (dict(k=P + 4), -1), (dict(o=P + 2), -1),
+    (dict(d=80), -2), (dict(d=512), -2), (dict(k=P + 4), -1), (dict(o=P + 2), -1),
     (dict(scale=1e30, descale_q=1e30, descale_k=1e30), -1),
 ])
 def test_fp8_rejects(kw, status):
@@ -350,7 +350,7 @@ def test_fp8_rejects(kw, status):
 @needs_lib
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(Nq=0), -1), (dict(Nq=1001), -1), (dict(num_splits=-2), -1),
-    (dict(descale_v=0.0), -1), (dict(d=256), -2), (dict(d=80), -2), (dict(layout=4), -1), (dict(workspace=None), -3),
+    (dict(descale_v=0.0), -1), (dict(d=512), -2), (dict(d=80), -2), (dict(layout=4), -1), (dict(workspace=None), -3),
     (dict(workspace_bytes=64), -3),
 ])
 def test_splitkv_fp8_rejects(kw, status):
@@ -368,9 +368,8 @@ def test_splitkv_fp8_workspace_uses_64_key_tiles():
         per = -(-tiles // ns)
         used = -(-tiles // per)
         r = lambda x: -(-x // 256) * 256
-        for d in (64, 96, 128):
+        for d in (64, 96, 128, 256):
             assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, d, ns) == r(used * 8 * d * 4) + r(used * 8 * 4)
-    assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, 256, 0) == 0
     assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 1000, 80, 0) == 0
 
 
@@ -424,10 +423,10 @@ def test_tensors_of_2_pow_31_elements_are_unsupported():
 
 
 @needs_lib
-def test_head_dim_256_is_bf16_only_and_not_fp8():
+def test_head_dim_256_is_bf16_and_fp8_not_fp32():
     """d = 256 exists for the bf16 forward and backward (with and without
-    dropout) and the bf16 split-key-range forward; the fp32 path and the FP8
-    forwards have no d = 256 kernels."""
+    dropout), the bf16 split-key-range forward and the two FP8 forwards; the
+    fp32 path has no d = 256 kernels."""
     base = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=64, d=256, causal=1, scale=0.0625, stream=None,
                 layout=fa.FA_LAYOUT_BHND)
     assert fa.fa_fwd(**base, dtype=fa.FA_FP32) == -2
@@ -435,11 +434,12 @@ def test_head_dim_256_is_bf16_only_and_not_fp8():
     assert fa.fa_bwd_workspace_bytes(1, 2, 64, 256, fa.FA_BF16) > 0
     assert fa.fa_bwd_workspace_bytes(1, 2, 64, 256, fa.FA_FP32) == 0
     assert fa.fa_fwd_dropout(**dict(base, o=None), drop_t=26, seed=1, offset=0) == -1   # shape accepted
-    assert fa.fa_fwd_fp8(**base, descale_q=1.0, descale_k=1.0, descale_v=1.0) == -2
+    assert fa.fa_fwd_fp8(**dict(base, q=None), descale_q=1.0, descale_k=1.0, descale_v=1.0) == -1   # shape accepted
     # split: 64 keys are 2 tiles, fewer than the 4 a range takes at least, so one range: O and LSE
     # partials of 4 rows x 2 heads
     assert fa.fa_fwd_splitkv_workspace_bytes(1, 2, 4, 64, 256, 0) == round_up(1 * 2 * 4 * 256 * 4) + 256
-    assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 64, 256, 0) == 0
+    # FP8: 64 keys are one 64-key tile, so one range as well
+    assert fa.fa_fwd_splitkv_fp8_workspace_bytes(1, 2, 4, 64, 256, 0) == round_up(1 * 2 * 4 * 256 * 4) + 256
     sk = dict(q=None, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=4, Nk=64, d=256, causal=1, scale=0.0625, num_splits=0,
               workspace=P, workspace_bytes=1 << 20, stream=None, dtype=fa.FA_BF16, layout=fa.FA_LAYOUT_BHND)
     assert fa.fa_fwd_splitkv(**sk) == -1   # the shape passes; the null q is rejected

@@ -200,8 +200,8 @@ def test_fp8_forward_maximum_size_sampled_heads():
 
 # head dims 64 and 96: LDS rows of 128 bytes with 4 or 6 chunks of data; at d =
 # 96 the second 64-wide K-step of S multiplies the padding chunks by the
-# zeros Q holds past d
-HD_CASES = [(d, n, causal, sig) for d in (64, 96) for n in (1, 17, 129, 300) for causal in (False, True)
+# zeros Q holds past d.  d = 256: LDS rows of 256 bytes, four 64-wide K-steps
+HD_CASES = [(d, n, causal, sig) for d in (64, 96, 256) for n in (1, 17, 129, 300) for causal in (False, True)
             for sig in (1.0, 3.0)]
 
 
@@ -218,7 +218,7 @@ def test_fp8_forward_other_head_dims(d, n, causal, sig):
     assert rs <= 1.0, rs
 
 
-@pytest.mark.parametrize("d", [64, 96])
+@pytest.mark.parametrize("d", [64, 96, 256])
 def test_fp8_forward_other_head_dims_larger_size(d):
     """Whole heads of a causal 1 x 4 x 4096 shape (64 key tiles) in both
     layouts, with the planted displaced tile that the per-element bound must
@@ -238,7 +238,7 @@ def test_fp8_forward_other_head_dims_larger_size(d):
     assert r_bad > 1.0, r_bad
 
 
-@pytest.mark.parametrize("d", [64, 96])
+@pytest.mark.parametrize("d", [64, 96, 256])
 @pytest.mark.parametrize("B,H,Nq,Nk,causal,ns", [(2, 3, 1, 1000, True, 0), (1, 2, 33, 2000, True, 5),
                                                  (1, 4, 7, 513, False, 3)])
 def test_fp8_split_forward_other_head_dims(d, B, H, Nq, Nk, causal, ns):
@@ -269,7 +269,7 @@ def test_fp8_score_error():
     head dim and input spread; every one within 2^-14 sum_c |q_c k_c|."""
     import torch
     worst = 0.0
-    for d in (64, 96, 128):
+    for d in (64, 96, 128, 256):
         for sig in (0.25, 1.0, 4.0):
             x = gen.make_fp8_inputs((1, 4096, 1, d), seed=11 + d, sigma_qk=sig)
             q8, k8, v8 = (torch.from_numpy(x[n]).cuda() for n in ("q8", "k8", "v8"))

@@ -75,7 +75,7 @@ def test_negative_scale_larger_size_sampled_heads(causal):
         compare({n: res[n][b, h] for n in ("o", "lse", "dq", "dk", "dv")}, w, "bf16", where=f"head ({b},{h})")
 
 
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_forward_at_other_scales(d, causal):
     import torch
