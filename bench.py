@@ -78,15 +78,17 @@ def backward_kernels(method, unit, T, ds_bytes, kv_ms, dq_ms, suffix=""):
 
 
 # Other instantiations whose HBM bytes the counter summary also records, for
-# the detail rooflines: key -> ((template name, head dim, split), sources).
+# the detail rooflines: key -> ((template name, head dim, split), sources);
+# for a kernel templated on flags alone, its template arguments in place of
+# the head dim.
 # split: True / False for the forwards' split mode (last template argument
 # true) or not, None where the kernel has no such argument.  A decode call is
 # a split forward plus the merge kernel.
 _FWD, _FP8 = ["fa_fwd_bf16.hip", "fa_common.h", "fa_dropout.h"], ["fa_fwd_fp8.hip", "fa_common.h"]
 DETAIL_COUNTERS = {
     "fwd_bf16_dropout_kernel": (("fwd_bf16_dropout_kernel", 128, None), _FWD),
-    "bwd_bf16_ds_kernel_d256": (("bwd_bf16_ds_kernel", 256, None),
-                                ["fa_bwd_kv256.hip", "fa_bwd_kv_body.h", "fa_common.h", "fa_dropout.h", "fa_launch.h"]),
+    "bwd256_kernel_d256": (("bwd256_kernel", "true, false, true", None),
+                           ["fa_bwd_kv256.hip", "fa_bwd_kv256_body.h", "fa_common.h", "fa_dropout.h", "fa_launch.h"]),
     "bwd_dq_ds_kernel_d256": (("bwd_dq_ds_kernel", 256, None), ["fa_bwd_dq_ds.hip", "fa_common.h", "fa_launch.h"]),
     "fwd_fp8_kernel": (("fwd_fp8_kernel", 128, False), _FP8),
     "fwd_bf16_kernel_split": (("fwd_bf16_kernel", 128, True), _FWD),
@@ -642,6 +644,8 @@ def head_dim_256_measurement(fa, torch, stream, with_oracle, reps=10):
     fwd_fl, bwd_fl = 2 * unit, 5 * unit
     method = DQ_METHODS[fa.fa_bwd_dq_method(B, H, N, d, True, fa.FA_BF16, ws.numel(), 0)]
     bk = backward_kernels(method, unit, B * H * N * d, ds_buffer_bytes(B, H, N, True), kv_ms, dq_ms)
+    # d = 256 has its own dK/dV kernel (bwd256_kernel<causal, dropout, dS stores>)
+    bk = [("bwd256_kernel" if n.startswith("bwd_bf16") else n, t, bound, w) for n, t, bound, w in bk]
     kernels = {"fwd_bf16_kernel": (fwd_ms, 2 * unit)}
     kernels.update({n: (t, fl) for n, t, bound, fl in bk if bound == "mfma"})
     hbm = {n: (t, b) for n, t, bound, b in bk if bound == "hbm"}

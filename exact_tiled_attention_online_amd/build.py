@@ -53,28 +53,12 @@ DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-munsafe
                 "-Rpass-analysis=kernel-resource-usage", "-Wno-unused-command-line-argument"]
 
 
-# Device flags one source is built without (in every variant): the d = 256
-# dropout kernels of the recompute method sit at the register limit, where
-# -amdgpu-mfma-vgpr-form makes the compiler's AGPR-copy rewrite crash.  The
-# flag only chooses the register class of MFMA results, not the arithmetic.
-SOURCE_DROP_FLAGS = {"fa_bwd_kv256_drop.hip": ("-mllvm", "-amdgpu-mfma-vgpr-form")}
-
-
-def _device_flags(src):
-    drop = SOURCE_DROP_FLAGS.get(src)
-    flags = list(DEVICE_FLAGS)
-    if not drop:
-        return flags
-    i = next(i for i in range(len(flags)) if tuple(flags[i:i + len(drop)]) == drop)
-    return flags[:i] + flags[i + len(drop):]
-
-
 def _compile(job):
     src, variant = job
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, (variant + "." if variant else "") + src + ".o")
     extra = VARIANTS[variant] if variant else []
-    cmd = [HIPCC] + _device_flags(src) + extra + ["-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
+    cmd = [HIPCC] + DEVICE_FLAGS + extra + ["-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, "-O2", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,7 +1,6 @@
 // fa_bwd_kv_body.h -- the key/value-block-outer backward kernel (dK, dV), bf16
-// inputs/outputs, fp32 accumulation; instantiated by fa_bwd_bf16.hip (d <= 128),
-// fa_bwd_kv256.hip (d = 256) and fa_bwd_kv256_drop.hip (three d = 256 dropout
-// kernels, built without VGPR-form MFMA results).
+// inputs/outputs, fp32 accumulation, d = 64, 96 and 128; instantiated by
+// fa_bwd_bf16.hip (d = 256 has a kernel of its own, fa_bwd_kv256_body.h).
 //
 // Key/value-block outer, query-block inner (page
 // "flash-attention-backpropagation" (aiqz.cc), section QKV梯度): one
@@ -25,9 +24,7 @@
 // In the hand-off variant (DSO) the bf16 dS operands of every block are also
 // stored to a buffer (layout: DsOut in fa_launch.h), from which a separate
 // kernel forms dQ = dS K without recomputing S and dP:
-//  - the 16-byte stores of a step (four per wave, two at d = 256, where the
-//    two waves of a key slice hold the same dS and each stores half of it)
-//    follow the step's products, after the
+//  - the four 16-byte stores of a step follow the step's products, after the
 //    masked and unmasked paths join (stores inside the two paths leave the
 //    compiler counting 0, 4 or 8 of them; holding dS into the next step made
 //    its register use jump past the file);
@@ -85,14 +82,12 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
                           DropArgs dr, DsOut dso) {
   static_assert(!(DQA && DROP), "the dropout backward takes dQ from another kernel");
   static_assert(!(DQA && DSO), "dQ comes from atomics or from the hand-off, not both");
-  // DH waves share a 32-key slice, each accumulating dK, dV for D/DH columns
-  // (d = 256: two, so that a wave's registers hold K, V and half of dK, dV);
-  // a workgroup of 4 waves then owns BC = 128/DH keys
-  constexpr int DH = D == 256 ? 2 : 1;
-  constexpr int BC = 128 / DH, BR = 64;
+  static_assert(D == 64 || D == 96 || D == 128, "head dims of this kernel");
+  // each wave owns a 32-key slice; a workgroup of 4 waves owns BC keys
+  constexpr int BC = 128, BR = 64;
   // ROWB: LDS bytes per row (d * 2, or 256 for d = 96); CH: 16-byte chunks per row
   constexpr int ROWB = lds_pitch<D>(), CH = D / 8, KS = D / 16, DT = D / 32;
-  constexpr int DTW = DT / DH;   // 32-column tiles of dK, dV per wave
+  constexpr int DTW = DT;   // 32-column tiles of dK, dV per wave
   static_assert(!DQA || (D == 64 || D == 128), "the atomic dQ variant splits d into 32-column slices over 4 waves");
   constexpr int QTB = BR * ROWB;          // bytes of one Q or dO tile
   constexpr int NQT = (D == 128) ? 2 : 1; // query tiles of dQ per wave
@@ -112,12 +107,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
   __shared__ __attribute__((aligned(1024))) char sK[SKB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slice = wave / DH, dpart = wave % DH;   // 32-key slice, part of d
-  // byte offset of this wave's part of d in a transposed operand read: the
-  // second 128 columns of a 512-byte row sit 256 bytes after the first (the
-  // swizzle leaves chunk bit 4 alone); a compile-time 0 when DH = 1
-  static_assert(DH == 1 || DTW == TileBases<ROWB>::DTB, "one part of d per set of tile bases");
-  const int doff = DH > 1 ? 256 * __builtin_amdgcn_readfirstlane(dpart) : 0;
+  const int slice = wave;   // 32-key slice
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the same value, known uniform
   const TileFetch<ROWB, BR, 4, CH> qfetch(wave_u, lane, lay.q.sn * 2);   // Q rows; dO rows at grs
   const unsigned grs = (unsigned)lay.g.sn * 2u;
@@ -158,11 +148,9 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
     const int kvrow = kvw + l32;             // key row of this lane in the S accumulators
     const int krow = 32 * slice + l32;       // the same row within the block
 
-    // dS hand-off: the wave's slice column within its head.  At d = 256 both
-    // waves of a slice compute the same dS (the same instructions on the same
-    // operands); each stores half of its micro-tiles.
+    // dS hand-off: the wave's slice column within its head
     char* dsw = nullptr;
-    if constexpr (DSO) dsw = dso.buf + (size_t)head * dso.head_bytes + (size_t)(kv0 / 32 + wave_u / DH) * 4096u;
+    if constexpr (DSO) dsw = dso.buf + (size_t)head * dso.head_bytes + (size_t)(kv0 / 32 + wave_u) * 4096u;
 
     // ---- K block into LDS (for K^T), then the register operands -------------
     if constexpr (DQA) {
@@ -302,11 +290,8 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
       // which its barrier below counts on.
       const bool dead = (kvw >= N) || (CAUSAL && qb0 + BR - 1 < kvw);
       const bool skip = DSO ? false : dead;
-      // the hand-off: the dS micro-tiles this wave stores, SPW of the BR / 16
-      // (at d = 256 the two waves of a slice hold the same dS; the wave with
-      // dpart = 1 stores the second half)
-      constexpr int SPW = BR / 16 / DH;
-      const int st0 = DH > 1 ? SPW * __builtin_amdgcn_readfirstlane(dpart) : 0;
+      // the hand-off: the BR / 16 dS micro-tiles this wave stores
+      constexpr int SPW = BR / 16;
       bf16x8 dsv[SPW];
       // one pass over the block; MASK: apply the causal / tail mask (a
       // compile-time variant, so the common unmasked path carries no mask code)
@@ -330,10 +315,9 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
 #define FA_KV_DIST 3
 #endif
         constexpr int DIST = FA_KV_DIST;   // slots between an LDS read and its use
-        constexpr int NG = 2 * KS + 4 * DTW;       // groups per step (4 * KS when DH = 1)
-        // chunks of the elementwise phase of a tile: at most 8, so that at
-        // d = 256 tile 1's operands are packed before its dV, dK products
-        constexpr int EC = KS < 8 ? KS : 8;
+        constexpr int NG = 2 * KS + 4 * DTW;       // groups per step (4 * KS)
+        // chunks of the elementwise phase of a tile: one per K-step slot
+        constexpr int EC = KS;
         f32x16 s[2], dp[2];
         // dropout: per query tile, the generator of this lane quad's 4x4 block
         // in query group lane % 4 (its rounds run in the KS slots before the
@@ -358,7 +342,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
           } else {
             const int t = (g - 2 * KS) / (2 * DTW), j = (g - 2 * KS) % (2 * DTW);
             const int st = 2 * t + j / DTW, dt = j % DTW;
-            const int o0 = tb.tr_off(st, dt, 0) + doff, o1 = tb.tr_off(st, dt, 1) + doff;
+            const int o0 = tb.tr_off(st, dt, 0), o1 = tb.tr_off(st, dt, 1);
             tg[t][j] = cat(lds_read_tr(Gt, o0), lds_read_tr(Gt, o1));
             tq[t][j] = cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1));
           }
@@ -449,7 +433,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (DSO) {
 #pragma unroll
-          for (int st = 0; st < SPW; ++st) dsv[st] = DH > 1 ? (st0 ? da[SPW + st] : da[st]) : da[st];
+          for (int st = 0; st < SPW; ++st) dsv[st] = da[st];
         }
         // dS (bf16) to LDS, [key][query], for the dQ product of the atomic variant
         if constexpr (DQA) {
@@ -476,7 +460,7 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
         }
       }
       if constexpr (DSO) {
-        char* p = (dead ? dso.sink : dsw + ds_block_off(CAUSAL, i, dso.nks)) + 16 * ln + 1024 * st0;
+        char* p = (dead ? dso.sink : dsw + ds_block_off(CAUSAL, i, dso.nks)) + 16 * ln;
 #pragma unroll
         for (int st = 0; st < SPW; ++st) __builtin_nontemporal_store(dsv[st], reinterpret_cast<bf16x8*>(p + 1024 * st));
         // s_waitcnt vmcnt(SPW) lgkmcnt(0): all but the stores (expcnt never
@@ -512,15 +496,15 @@ FA_DEV void bwd_bf16_body(const bf16* __restrict__ Q, const bf16* __restrict__ K
     }
 
     // ---- write-back: dK = scale * acc, dV = acc ------------------------------
-    // Each wave stages its own 32 rows (its D/DH columns) through a private
+    // Each wave stages its own 32 rows through a private
     // LDS region of 32 rows (the query buffers, idle after the walk) to turn
     // the accumulator layout into 16-byte row stores.  Accumulator r of tile
-    // dt: key 32*slice + 8*(r/4) + 4h + r%4, d (D/DH)*dpart + 32*dt + l32.
+    // dt: key 32*slice + 8*(r/4) + 4h + r%4, d 32*dt + l32.
     {
       char* region = (wave < 2 ? sQ0 : sG0) + (wave & 1) * (32 * ROWB);
       bf16* stg = reinterpret_cast<bf16*>(region);   // [32][D] plain row-major
-      constexpr int CW = CH / DH;                     // 16-byte chunks of a row this wave writes
-      const int c0 = dpart * (D / DH);                // first column of this wave
+      constexpr int CW = CH;                          // 16-byte chunks of a row
+      constexpr int c0 = 0;                           // first column
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -586,7 +570,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_dropout_kernel(
 // key blocks when causal, one otherwise) of each head.
 template <int D, bool CAUSAL>
 static dim3 bwd_kv_grid(int BH, int N) {
-  constexpr int BC = D == 256 ? 64 : 128;   // keys per workgroup
+  constexpr int BC = 128;   // keys per workgroup
   const int nkb = (N + BC - 1) / BC;
   return dim3((unsigned)((CAUSAL ? (nkb + 1) / 2 : nkb) * BH));
 }
@@ -614,22 +598,11 @@ static hipError_t launch_bwd_bf16_t(const void* q, const void* k, const void* v,
   const float c = ledger_scale(scale) * kLog2e;   // dK keeps the caller's scale
   if constexpr (!DQA) {
     if (drop) {
-      if constexpr (D == 256 && !CAUSAL) {
-        return launch_bwd_kv256_drop(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, CAUSAL, scale, lay, stream, *drop, ds);
-      } else if constexpr (D == 256) {
-        // causal d = 256: only the hand-off kernel is built in this unit
-        if (!ds.buf)
-          return launch_bwd_kv256_drop(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, CAUSAL, scale, lay, stream, *drop,
-                                       ds);
+      if (ds.buf)
         return launch_bwd_dropout_t<D, CAUSAL, true>(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, scale, lay, stream,
                                                      *drop, ds);
-      } else {
-        if (ds.buf)
-          return launch_bwd_dropout_t<D, CAUSAL, true>(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, scale, lay, stream,
-                                                       *drop, ds);
-        return launch_bwd_dropout_t<D, CAUSAL, false>(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, scale, lay,
-                                                      stream, *drop, ds);
-      }
+      return launch_bwd_dropout_t<D, CAUSAL, false>(q, k, v, dO, nlse, ndrow, dk, dv, BH, N, scale, lay,
+                                                    stream, *drop, ds);
     }
     if (ds.buf) {
       hipLaunchKernelGGL((bwd_bf16_ds_kernel<D, CAUSAL>), grid, block, 0, stream, (const bf16*)q, (const bf16*)k,

@@ -41,16 +41,15 @@ def test_headline_instance(name, short, want):
 
 
 FWD_DROP = "void fa::fwd_bf16_dropout_kernel<128, true, 8, 64>(__bf16 const*)"
-KV_256 = "void fa::bwd_bf16_ds_kernel<256, true>(__bf16 const*)"
+KV_256 = "void fa::bwd256_kernel<true, false, true>(__bf16 const*)"
 
 
 @pytest.mark.parametrize("name,key,want", [
     (FWD_DROP, "fwd_bf16_dropout_kernel", True), (FWD, "fwd_bf16_dropout_kernel", False),
-    (KV_256, "bwd_bf16_ds_kernel_d256", True), (KV_DS, "bwd_bf16_ds_kernel_d256", False),
-    ("void fa::bwd_bf16_kernel<256, true, false>(__bf16 const*)", "bwd_bf16_ds_kernel_d256", False),
-    ("void fa::bwd_bf16_dropout_kernel<256, true, true>(__bf16 const*)", "bwd_bf16_ds_kernel_d256", False),
-    ("_ZN2fa18bwd_bf16_ds_kernelILi256ELb1EEEvPKDF16b", "bwd_bf16_ds_kernel_d256", True),
-    ("_ZN2fa23bwd_bf16_dropout_kernelILi256ELb1ELb1EEEvPKDF16b", "bwd_bf16_ds_kernel_d256", False),
+    (KV_256, "bwd256_kernel_d256", True), (KV_DS, "bwd256_kernel_d256", False),
+    ("void fa::bwd256_kernel<true, false, false>(__bf16 const*)", "bwd256_kernel_d256", False),
+    ("void fa::bwd256_kernel<true, true, true>(__bf16 const*)", "bwd256_kernel_d256", False),
+    ("void fa::bwd256_kernel<false, false, true>(__bf16 const*)", "bwd256_kernel_d256", False),
     ("void fa::bwd_dq_ds_kernel<256, true>(char const*)", "bwd_dq_ds_kernel_d256", True),
     (DQ_DS, "bwd_dq_ds_kernel_d256", False),
     ("void fa::fwd_fp8_kernel<128, true, 4, false>(unsigned char const*)", "fwd_fp8_kernel", True),
@@ -111,10 +110,10 @@ def test_counter_summary_calibrates_on_the_copy_probe(tmp_path):
     assert c["bwd_bf16_kernel"]["hbm_bytes_per_launch"] == int((500.0 * 2 + 50.0) * 1024)
     assert c["fwd_bf16_kernel"]["source_digest"] == bench.source_digest(bench.KERNEL_SOURCES["fwd_bf16_kernel"])
     assert "bwd_dq_kernel" not in c
-    assert c["bwd_bf16_ds_kernel_d256"]["hbm_bytes_per_launch"] == int((700.0 * 2 + 70.0) * 1024)
+    assert c["bwd256_kernel_d256"]["hbm_bytes_per_launch"] == int((700.0 * 2 + 70.0) * 1024)
     assert c["fwd_bf16_dropout_kernel"]["hbm_bytes_per_launch"] == int((80.0 * 2 + 8.0) * 1024)
-    assert c["bwd_bf16_ds_kernel_d256"]["source_digest"] == bench.source_digest(
-        bench.DETAIL_COUNTERS["bwd_bf16_ds_kernel_d256"][1])
+    assert c["bwd256_kernel_d256"]["source_digest"] == bench.source_digest(
+        bench.DETAIL_COUNTERS["bwd256_kernel_d256"][1])
 
 
 def test_traffic_is_dropped_once_the_sources_change(tmp_path, monkeypatch):
