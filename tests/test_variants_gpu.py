@@ -5,7 +5,7 @@ prefetch of a next tile, so that no read can run ahead of a load into LDS
 and no wave can refill a buffer another wave still reads.  The kernels
 pipeline their LDS buffers with a single barrier per tile (and, in the dS
 hand-off kernels, barriers that deliberately leave stores outstanding); a
-missing wait there would show as a difference from this build.  Every output
+missing wait there would show as a difference from the checking library.  Every output
 must be bit-identical.
 
 libfa_tile_alt.so is another tile configuration: 4-wave forward and
