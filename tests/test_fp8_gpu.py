@@ -166,15 +166,17 @@ def test_fp8_split_forward_matches_oracle(B, H, Nq, Nk, causal, ns):
             assert (np.abs(got_l[b, h] - rl[b, h]) <= bar_l).all(), (b, h)
 
 
-def test_fp8_forward_maximum_size_sampled_heads():
+@pytest.mark.parametrize("H,d", [(32, 128), (16, 256)])
+def test_fp8_forward_maximum_size_sampled_heads(H, d):
     """The FP8 forward at the largest shape of the headline geometry: B=63,
-    H=32, N=8192, d=128 causal, 2.11e9 one-byte codes per tensor (generated
-    on the device: normal values over the descale, clipped to the largest
-    finite e4m3fn value); three whole heads against the oracle on the values
-    the codes stand for, with the bound above."""
+    H=32, N=8192, d=128 causal (and its d = 256 counterpart, H=16), 2.11e9
+    one-byte codes per tensor (generated on the device: normal values over
+    the descale, clipped to the largest finite e4m3fn value); three whole
+    heads against the oracle on the values the codes stand for, with the
+    bound above."""
     import torch
-    B, H, N, d = 63, 32, 8192, 128
-    ds, scale = 2.0 ** -5, 1.0 / math.sqrt(128)
+    B, N = 63, 8192
+    ds, scale = 2.0 ** -5, 1.0 / math.sqrt(d)
     log(f"[fp8 max size] B={B} H={H} N={N} d={d} causal")
     g = torch.Generator(device="cuda").manual_seed(8863)
 
