@@ -30,8 +30,7 @@ int check_shape(int B, int H, int N, int d, int causal, float scale, int dtype, 
   if (causal != 0 && causal != 1) return FA_ERR_INVALID;
   if (!std::isfinite(scale)) return FA_ERR_INVALID;   // any finite scale (negative and 0 included)
   if (dtype != FA_BF16 && dtype != FA_FP32) return FA_ERR_UNSUPPORTED;
-  // d = 256: bf16 only (the fp32 kernels hold a row of q and o per lane pair)
-  if (d != 64 && d != 96 && d != 128 && !(d == 256 && dtype == FA_BF16)) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   // B * H * N * d < 2^31, checked factor by factor so that no product of
   // three 31-bit sizes is formed (it would overflow a 64-bit integer)
   const long long rows = (long long)B * H;

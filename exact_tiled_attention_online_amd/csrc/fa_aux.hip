@@ -95,6 +95,7 @@ hipError_t launch_bwd_pre(const void* o, const void* dO, const float* lse, float
   if (fp32) {
     if (d == 128) go(IC<128>{}, IC<1>{});
     else if (d == 96) go(IC<96>{}, IC<1>{});
+    else if (d == 256) go(IC<256>{}, IC<1>{});
     else go(IC<64>{}, IC<1>{});
   } else {
     if (d == 128) go(IC<128>{}, IC<0>{});

@@ -1,10 +1,13 @@
 // fa_fp32.hip -- fp32 path: the same tiled method in exact fp32 VALU
 // arithmetic (no MFMA rounding of operands), for fp32 callers.
 //
-// Work split: a pair of lanes owns one row (query row in the forward and in
-// the dQ kernel, key row in the dK/dV kernel), each lane half of d; a dot
-// product is the two halves' partial sums combined with one xor-shuffle.
-// The streamed operand rows sit in LDS and every lane reads the same element
+// Work split: LP lanes own one row (query row in the forward and in the dQ
+// kernel, key row in the dK/dV kernel), each lane d/LP of its elements; a dot
+// product is the LP partial sums combined with xor-shuffles.  LP = 2 for
+// d <= 128; at d = 256, 4 in the forward and 8 in the backward kernels, so
+// that a lane's slices of its rows (q and o; k, v, dk and dv; q, dO and dq)
+// stay in registers.  A workgroup of 128 lanes owns 128/LP rows.  The
+// streamed operand rows sit in LDS and every lane reads the same element
 // (broadcast).
 //
 // forward   : online softmax over 32-key tiles (page
@@ -19,12 +22,17 @@
 
 namespace fa {
 
-constexpr int F32_ROWS = 64;   // rows per workgroup (128 lanes)
+// lanes per row: the forward (F) and the backward kernels (B)
+template <int D> constexpr int f32_lp_fwd() { return D == 256 ? 4 : 2; }
+template <int D> constexpr int f32_lp_bwd() { return D == 256 ? 8 : 2; }
 
 // One-dimensional grid: workgroup x is row block x % nrb of head x / nrb, so
 // that any number of heads the interface accepts fits (a grid's second
-// dimension holds at most 65535 workgroups).
-inline unsigned f32_grid(int BH, int N) { return (unsigned)BH * (unsigned)((N + F32_ROWS - 1) / F32_ROWS); }
+// dimension holds at most 65535 workgroups); a workgroup owns 128/LP rows.
+inline unsigned f32_grid(int BH, int N, int LP) {
+  const int rows = 128 / LP;
+  return (unsigned)BH * (unsigned)((N + rows - 1) / rows);
+}
 constexpr int F32_TILE = 32;   // streamed rows per LDS tile
 
 template <int D>
@@ -39,12 +47,16 @@ FA_DEV void load_rows_f32(float* dst, const float* src, int row0, int nrows, int
   }
 }
 
-template <int D>
-FA_DEV float half_dot(const float* a, const float* b) {
+// the dot product of a row split over LP lanes: this lane's D/LP elements,
+// then the partial sums of the LP lanes
+template <int D, int LP>
+FA_DEV float part_dot(const float* a, const float* b) {
   float s = 0.f;
 #pragma unroll
-  for (int c = 0; c < D / 2; ++c) s = fmaf(a[c], b[c], s);
-  return s + __shfl_xor(s, 1);
+  for (int c = 0; c < D / LP; ++c) s = fmaf(a[c], b[c], s);
+#pragma unroll
+  for (int x = 1; x < LP; x <<= 1) s += __shfl_xor(s, x);
+  return s;
 }
 
 template <int D, bool CAUSAL>
@@ -52,14 +64,14 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ 
                                                       const float* __restrict__ V, float* __restrict__ O,
                                                       float* __restrict__ LSE, int BH, int N, float scale,
                                                       Layouts lay) {
-  constexpr int DH = D / 2;
+  constexpr int LP = f32_lp_fwd<D>(), DH = D / LP, ROWS = 128 / LP;
   __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sv[F32_TILE * D];
-  const int tid = threadIdx.x, half = tid & 1;
-  const int nrb = (N + F32_ROWS - 1) / F32_ROWS;
+  const int tid = threadIdx.x, half = tid & (LP - 1);   // this lane's part of the row
+  const int nrb = (N + ROWS - 1) / ROWS;
   const int head = blockIdx.x / nrb;
-  const int row0 = (blockIdx.x - head * nrb) * F32_ROWS;
-  const int qrow = row0 + (tid >> 1);
+  const int row0 = (blockIdx.x - head * nrb) * ROWS;
+  const int qrow = row0 + tid / LP;
   float qh[DH], oh[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
@@ -67,7 +79,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ 
     oh[c] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int kv_end = CAUSAL ? min(N, row0 + F32_ROWS) : N;
+  const int kv_end = CAUSAL ? min(N, row0 + ROWS) : N;
   for (int t0 = 0; t0 < kv_end; t0 += F32_TILE) {
     __syncthreads();
     load_rows_f32<D>(sk, K + lay.off(lay.k, head), t0, F32_TILE, N, tid, lay.k.sn);
@@ -78,7 +90,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const float* __restrict__ 
 #pragma unroll
     for (int j = 0; j < F32_TILE; ++j) {
       const int kv = t0 + j;
-      float x = half_dot<D>(qh, sk + j * D + half * DH) * scale;
+      float x = part_dot<D, LP>(qh, sk + j * D + half * DH) * scale;
       if (kv >= N || (CAUSAL && kv > qrow)) x = -INFINITY;
       s[j] = x;
       mx = fmaxf(mx, x);
@@ -117,15 +129,15 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
                                                          const float* __restrict__ LSE, const float* __restrict__ NDR,
                                                          float* __restrict__ dK, float* __restrict__ dV, int N,
                                                          float scale, Layouts lay) {
-  constexpr int DH = D / 2;
+  constexpr int LP = f32_lp_bwd<D>(), DH = D / LP, ROWS = 128 / LP;
   __shared__ __attribute__((aligned(16))) float sq[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sg[F32_TILE * D];
   __shared__ float sl[F32_TILE], sd[F32_TILE];
-  const int tid = threadIdx.x, half = tid & 1;
-  const int nrb = (N + F32_ROWS - 1) / F32_ROWS;
+  const int tid = threadIdx.x, half = tid & (LP - 1);   // this lane's part of the row
+  const int nrb = (N + ROWS - 1) / ROWS;
   const int head = blockIdx.x / nrb;
-  const int row0 = (blockIdx.x - head * nrb) * F32_ROWS;
-  const int kvrow = row0 + (tid >> 1);
+  const int row0 = (blockIdx.x - head * nrb) * ROWS;
+  const int kvrow = row0 + tid / LP;
   float kh[DH], vh[DH], dkh[DH], dvh[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
@@ -147,10 +159,10 @@ __global__ __launch_bounds__(128) void bwd_kv_f32_kernel(const float* __restrict
     __syncthreads();
     for (int j = 0; j < F32_TILE; ++j) {
       const int q = t0 + j;
-      const float sc = half_dot<D>(sq + j * D + half * DH, kh) * scale;
+      const float sc = part_dot<D, LP>(sq + j * D + half * DH, kh) * scale;
       float p = expf(sc - sl[j]);
       if (q >= N || kvrow >= N || (CAUSAL && kvrow > q)) p = 0.f;
-      const float dp = half_dot<D>(sg + j * D + half * DH, vh);
+      const float dp = part_dot<D, LP>(sg + j * D + half * DH, vh);
       const float ds = p * (dp + sd[j]);   // sd holds -D
 #pragma unroll
       for (int c = 0; c < DH; ++c) {
@@ -174,14 +186,14 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
                                                         const float* __restrict__ V, const float* __restrict__ dO,
                                                         const float* __restrict__ LSE, const float* __restrict__ NDR,
                                                         float* __restrict__ dQ, int N, float scale, Layouts lay) {
-  constexpr int DH = D / 2;
+  constexpr int LP = f32_lp_bwd<D>(), DH = D / LP, ROWS = 128 / LP;
   __shared__ __attribute__((aligned(16))) float sk[F32_TILE * D];
   __shared__ __attribute__((aligned(16))) float sv[F32_TILE * D];
-  const int tid = threadIdx.x, half = tid & 1;
-  const int nrb = (N + F32_ROWS - 1) / F32_ROWS;
+  const int tid = threadIdx.x, half = tid & (LP - 1);   // this lane's part of the row
+  const int nrb = (N + ROWS - 1) / ROWS;
   const int head = blockIdx.x / nrb;
-  const int row0 = (blockIdx.x - head * nrb) * F32_ROWS;
-  const int qrow = row0 + (tid >> 1);
+  const int row0 = (blockIdx.x - head * nrb) * ROWS;
+  const int qrow = row0 + tid / LP;
   float qh[DH], gh[DH], dqh[DH];
 #pragma unroll
   for (int c = 0; c < DH; ++c) {
@@ -191,7 +203,7 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
   }
   const float lse = qrow < N ? LSE[(size_t)head * N + qrow] : 0.f;
   const float ndrow = qrow < N ? NDR[(size_t)head * N + qrow] : 0.f;   // -D
-  const int kv_end = CAUSAL ? min(N, row0 + F32_ROWS) : N;
+  const int kv_end = CAUSAL ? min(N, row0 + ROWS) : N;
   for (int t0 = 0; t0 < kv_end; t0 += F32_TILE) {
     __syncthreads();
     load_rows_f32<D>(sk, K + lay.off(lay.k, head), t0, F32_TILE, N, tid, lay.k.sn);
@@ -199,10 +211,10 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
     __syncthreads();
     for (int j = 0; j < F32_TILE; ++j) {
       const int kv = t0 + j;
-      const float sc = half_dot<D>(qh, sk + j * D + half * DH) * scale;
+      const float sc = part_dot<D, LP>(qh, sk + j * D + half * DH) * scale;
       float p = expf(sc - lse);
       if (qrow >= N || kv >= N || (CAUSAL && kv > qrow)) p = 0.f;
-      const float dp = half_dot<D>(gh, sv + j * D + half * DH);
+      const float dp = part_dot<D, LP>(gh, sv + j * D + half * DH);
       const float ds = p * (dp + ndrow);
 #pragma unroll
       for (int c = 0; c < DH; ++c) dqh[c] = fmaf(ds, sk[j * D + half * DH + c], dqh[c]);
@@ -218,7 +230,7 @@ __global__ __launch_bounds__(128) void bwd_q_f32_kernel(const float* __restrict_
 template <int D, bool CAUSAL>
 static hipError_t fwd_f32_t(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
                             int N, float scale, Layouts lay, hipStream_t stream) {
-  const dim3 grid(f32_grid(BH, N)), block(128);
+  const dim3 grid(f32_grid(BH, N, f32_lp_fwd<D>())), block(128);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, o, lse, BH, N, scale, lay);
   return hipGetLastError();
 }
@@ -227,7 +239,7 @@ template <int D, bool CAUSAL>
 static hipError_t bwd_kv_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
                                const float* ndrow, float* dk, float* dv, int BH, int N, float scale,
                                Layouts lay, hipStream_t stream) {
-  const dim3 grid(f32_grid(BH, N)), block(128);
+  const dim3 grid(f32_grid(BH, N, f32_lp_bwd<D>())), block(128);
   hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dk, dv, N,
                      scale, lay);
   return hipGetLastError();
@@ -237,7 +249,7 @@ template <int D, bool CAUSAL>
 static hipError_t bwd_q_f32_t(const float* q, const float* k, const float* v, const float* dO, const float* lse,
                               const float* ndrow, float* dq, int BH, int N, float scale, Layouts lay,
                               hipStream_t stream) {
-  const dim3 grid(f32_grid(BH, N)), block(128);
+  const dim3 grid(f32_grid(BH, N, f32_lp_bwd<D>())), block(128);
   hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), grid, block, 0, stream, q, k, v, dO, lse, ndrow, dq, N, scale,
                      lay);
   return hipGetLastError();
@@ -248,6 +260,9 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
   if (d == 128)
     return causal ? fwd_f32_t<128, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
                   : fwd_f32_t<128, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
+  if (d == 256)
+    return causal ? fwd_f32_t<256, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
+                  : fwd_f32_t<256, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
   if (d == 96)
     return causal ? fwd_f32_t<96, true>(q, k, v, o, lse, BH, N, scale, lay, stream)
                   : fwd_f32_t<96, false>(q, k, v, o, lse, BH, N, scale, lay, stream);
@@ -261,6 +276,9 @@ hipError_t launch_bwd_kv_f32(const float* q, const float* k, const float* v, con
   if (d == 128)
     return causal ? bwd_kv_f32_t<128, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream)
                   : bwd_kv_f32_t<128, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream);
+  if (d == 256)
+    return causal ? bwd_kv_f32_t<256, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream)
+                  : bwd_kv_f32_t<256, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream);
   if (d == 96)
     return causal ? bwd_kv_f32_t<96, true>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream)
                   : bwd_kv_f32_t<96, false>(q, k, v, dO, lse, ndrow, dk, dv, BH, N, scale, lay, stream);
@@ -274,6 +292,9 @@ hipError_t launch_bwd_q_f32(const float* q, const float* k, const float* v, cons
   if (d == 128)
     return causal ? bwd_q_f32_t<128, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream)
                   : bwd_q_f32_t<128, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream);
+  if (d == 256)
+    return causal ? bwd_q_f32_t<256, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream)
+                  : bwd_q_f32_t<256, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream);
   if (d == 96)
     return causal ? bwd_q_f32_t<96, true>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream)
                   : bwd_q_f32_t<96, false>(q, k, v, dO, lse, ndrow, dq, BH, N, scale, lay, stream);

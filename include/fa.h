@@ -28,10 +28,9 @@
  * scale * q_i . k_j.  The causal mask keeps key j for query i iff j <= i
  * (queries and keys share the index range 0..N-1).
  *
- * Supported: d in {64, 96, 128, 256}, except fp32 at d = 256 (d = 256 runs
- * for bf16 in fa_fwd, fa_bwd and its stages, the strided calls, the dropout
- * forward and backward and the split-key-range forward, and in the FP8
- * forwards; other d and fp32 at d = 256 are FA_ERR_UNSUPPORTED); N >= 1 (any
+ * Supported: d in {64, 96, 128, 256} in every call, with the dtypes each
+ * call lists (fa_fwd, fa_bwd and its stages and the strided calls: FA_BF16
+ * and FA_FP32); other d are FA_ERR_UNSUPPORTED; N >= 1 (any
  * N, tails are masked); B, H >= 1 with B*H*N*d < 2^31; scale any finite value
  * (negative and 0 included: S = scale * Q K^T as written; below 2^-100 in
  * magnitude every score of a row is equal to fp32 rounding); causal in {0, 1}.

@@ -118,9 +118,9 @@ def test_workspace_size_per_method(B, H, N, d):
         assert ws(fa.FA_DQ_RECOMPUTE) == stats
         assert ws(fa.FA_DQ_HANDOFF) == stats + round_up(B * H * handoff_head_bytes(N, causal)) + 4096
         assert ws(fa.FA_DQ_ATOMIC) == (stats + round_up(rows * d * 4) if d in (64, 128) else 0)
-        # fp32 has only the recompute kernels (and no d = 256)
+        # fp32 has only the recompute kernels
         assert ws(fa.FA_DQ_HANDOFF, fa.FA_FP32) == 0
-        assert ws(fa.FA_DQ_RECOMPUTE, fa.FA_FP32) == (stats if d != 256 else 0)
+        assert ws(fa.FA_DQ_RECOMPUTE, fa.FA_FP32) == stats
         assert ws(7) == 0
     # the causal buffer keeps about half of the (query, key) pairs
     assert (fa.fa_bwd_workspace_size(1, 1, 8192, 128, 1, fa.FA_BF16, fa.FA_DQ_HANDOFF)
@@ -142,8 +142,7 @@ def test_dq_method_follows_the_workspace(monkeypatch):
             assert m(need) == fa.FA_DQ_HANDOFF and m(need + 1) == fa.FA_DQ_HANDOFF
             assert m(need - 1) == fa.FA_DQ_RECOMPUTE and m(0) == fa.FA_DQ_RECOMPUTE
             assert m(need, 1) == fa.FA_DQ_HANDOFF and m(need - 1, 1) == fa.FA_DQ_RECOMPUTE
-            assert fa.fa_bwd_dq_method(B, H, N, d, causal, fa.FA_FP32, need, 0) == (
-                fa.FA_DQ_RECOMPUTE if d != 256 else -2)
+            assert fa.fa_bwd_dq_method(B, H, N, d, causal, fa.FA_FP32, need, 0) == fa.FA_DQ_RECOMPUTE
     monkeypatch.setenv("FA_DQ_MODE", "recompute")
     assert fa.fa_bwd_dq_method(1, 1, 128, 64, 1, fa.FA_BF16, 1 << 40, 0) == fa.FA_DQ_RECOMPUTE
     monkeypatch.setenv("FA_DQ_MODE", "atomic")
@@ -184,7 +183,7 @@ def bwd(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
     (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1), (dict(causal=2), -1),
-    (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1), (dict(d=80), -2), (dict(d=512), -2), (dict(d=256, dtype=fa.FA_FP32), -2),
+    (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1), (dict(d=80), -2), (dict(d=512), -2),
     (dict(dtype=7), -2),
     (dict(q=P + 8), -1), (dict(lse=P + 2), -1),
     (dict(B=1024, H=1024, N=4096, d=128), -2),
@@ -241,7 +240,7 @@ D = dense_strides(2, 3, 128, 64)
 @needs_lib
 @pytest.mark.parametrize("strides,kw,status", [
     (None, dict(q=None), -1), (None, dict(d=80), -2), (None, dict(N=0), -1), (None, dict(q=P + 8), -1),
-    (None, dict(dtype=fa.FA_FP32, d=256), -2),
+    (None, dict(dtype=fa.FA_FP32, d=512), -2),
     (_set(D * 4, 0, [D[0], D[1], -64]), {}, -1),           # negative row stride
     (_set(D * 4, 1, [D[0], D[1], 68]), {}, -1),            # k rows 136 bytes apart: not 16-byte aligned
     (_set(D * 4, 2, [D[0], 4, D[2]]), {}, -1),             # v head stride of 8 bytes
@@ -423,16 +422,16 @@ def test_tensors_of_2_pow_31_elements_are_unsupported():
 
 
 @needs_lib
-def test_head_dim_256_is_bf16_and_fp8_not_fp32():
-    """d = 256 exists for the bf16 forward and backward (with and without
-    dropout), the bf16 split-key-range forward and the two FP8 forwards; the
-    fp32 path has no d = 256 kernels."""
+def test_head_dim_256_in_every_call():
+    """d = 256 exists for the bf16 and fp32 forward and backward, the
+    dropout calls, the bf16 split-key-range forward and the two FP8
+    forwards."""
     base = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=64, d=256, causal=1, scale=0.0625, stream=None,
                 layout=fa.FA_LAYOUT_BHND)
-    assert fa.fa_fwd(**base, dtype=fa.FA_FP32) == -2
+    assert fa.fa_fwd(**dict(base, q=None), dtype=fa.FA_FP32) == -1   # d = 256 fp32 passes the shape check
     assert fa.fa_fwd(**dict(base, q=None), dtype=fa.FA_BF16) == -1   # d = 256 bf16 passes the shape check
     assert fa.fa_bwd_workspace_bytes(1, 2, 64, 256, fa.FA_BF16) > 0
-    assert fa.fa_bwd_workspace_bytes(1, 2, 64, 256, fa.FA_FP32) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 2, 64, 256, fa.FA_FP32) > 0
     assert fa.fa_fwd_dropout(**dict(base, o=None), drop_t=26, seed=1, offset=0) == -1   # shape accepted
     assert fa.fa_fwd_fp8(**dict(base, q=None), descale_q=1.0, descale_k=1.0, descale_v=1.0) == -1   # shape accepted
     # split: 64 keys are 2 tiles, fewer than the 4 a range takes at least, so one range: O and LSE

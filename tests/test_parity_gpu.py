@@ -39,9 +39,10 @@ EDGE = [(dtype, d, causal, n, m)
         for causal in (False, True)
         for n in (1, 17, 64, 129, 300)
         for m in ((fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE) if dtype == "bf16" else (fa.FA_DQ_RECOMPUTE,))]
-# head dim 256: bf16 only
+# head dim 256 (fp32: four lanes per row in the forward, eight in the backward)
 EDGE += [("bf16", 256, causal, n, m) for causal in (False, True) for n in (1, 17, 64, 129, 300)
          for m in (fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE)]
+EDGE += [("fp32", 256, causal, n, fa.FA_DQ_RECOMPUTE) for causal in (False, True) for n in (1, 17, 64, 129, 300)]
 METHOD_NAME = {fa.FA_DQ_HANDOFF: "handoff", fa.FA_DQ_RECOMPUTE: "recompute", fa.FA_DQ_ATOMIC: "atomic"}
 
 

@@ -42,7 +42,7 @@ def _compare_all(x, dtype, causal, scale, where, method=fa.FA_DQ_HANDOFF):
 
 CASES = [(dtype, d, causal, n) for dtype in ("bf16", "fp32") for d in (64, 96, 128) for causal in (False, True)
          for n in (129, 300)]
-CASES += [("bf16", 256, causal, n) for causal in (False, True) for n in (129, 300)]
+CASES += [(dtype, 256, causal, n) for dtype in ("bf16", "fp32") for causal in (False, True) for n in (129, 300)]
 
 
 @pytest.mark.parametrize("dtype,d,causal,n", CASES)

@@ -56,8 +56,7 @@ CASES = [(dtype, d, causal, n, m)
          for d in (64, 96, 128, 256)
          for causal in (False, True)
          for n in (200, 513)
-         for m in ((fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE) if dtype == "bf16" else (fa.FA_DQ_RECOMPUTE,))
-         if not (dtype == "fp32" and d == 256)]
+         for m in ((fa.FA_DQ_HANDOFF, fa.FA_DQ_RECOMPUTE) if dtype == "bf16" else (fa.FA_DQ_RECOMPUTE,))]
 
 
 @pytest.mark.parametrize("dtype,d,causal,n,method", CASES)
