@@ -247,6 +247,7 @@ BNHD = [(dtype, d, causal, n)
         for d in (64, 96, 128)
         for causal in (False, True)
         for n in (17, 300)]
+BNHD += [("fp32", 256, causal, n) for causal in (False, True) for n in (17, 300)]   # bf16: its own test
 
 
 @pytest.mark.parametrize("dtype,d,causal,n", BNHD)
@@ -409,6 +410,16 @@ def test_maximum_size_sampled_heads():
         torch.cuda.empty_cache()
     del q, k, v, do, o, lse
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_head_dim_256_larger_size(causal):
+    """The fp32 path at d = 256 (four lanes per row in the forward, eight in
+    the backward) on whole heads of 1 x 2 x 1024 x 256: 64 row blocks of the
+    backward kernels and 32 streamed tiles per row."""
+    log(f"[fp32 d256] 1x2x1024 causal={causal}")
+    x = gen.make_inputs(gen.workload("c1"), shape=(1, 2, 1024, 256), seed=25600 + int(causal))
+    _full_compare(x, "fp32", causal, 1.0 / 16.0, f"fp32 d256 1024 c{int(causal)}")
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
