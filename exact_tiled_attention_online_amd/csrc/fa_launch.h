@@ -137,16 +137,16 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            int BH, int N, int d, bool causal, float scale, bool dq_atomic, Layouts lay,
                            hipStream_t stream, const DropArgs* drop = nullptr, DsOut ds = DsOut{});
 
-// The same at d = 256 (no atomic-dQ form; plain, hand-off and dropout), from
-// its own translation unit.
+// The same at d = 256 (fa_bwd_kv256_body.h: two waves per 32-key slice);
+// plain, with the dS stores of the hand-off method and with dropout.  It has
+// no atomic-dQ form.  Dropout is passed on to launch_bwd_kv256_drop.
 hipError_t launch_bwd_kv256(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                             const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
                             Layouts lay, hipStream_t stream, const DropArgs* drop, DsOut ds);
 
-// d = 256 with dropout, except the causal kernel with the dS stores: from a
-// unit of its own, built without VGPR-form MFMA results (with them the
-// compiler's AGPR-copy rewrite crashes on these kernels, which sit at the
-// register limit).  ds.buf selects the hand-off kernel as in launch_bwd_bf16.
+// d = 256 with dropout (the same kernel body, instantiated in a unit of its
+// own so that it compiles in parallel).  ds.buf selects the form with the dS
+// stores as in launch_bwd_bf16.
 hipError_t launch_bwd_kv256_drop(const void* q, const void* k, const void* v, const void* dO, const float* nlse,
                                  const float* ndrow, void* dk, void* dv, int BH, int N, bool causal, float scale,
                                  Layouts lay, hipStream_t stream, const DropArgs& drop, DsOut ds);
